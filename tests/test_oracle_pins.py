@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself:
+sizes the pages print, hand-written layout examples, closed forms, independent
+library routines (torch's float8 / bfloat16 conversions, scipy's expit, Python's
+stable sort) and brute force on tiny inputs.  CPU only."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import synth
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _kv(name):
+    out = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#")[0].strip()
+        if line:
+            k, *v = line.split()
+            out.setdefault(k, []).append(v)
+    return out
+
+
+# ----------------------------------------------------------------------------- STQ1_0 format
+def test_stq1_patterns_exhaustive():
+    """All 32 patterns: exactly one zero and three +-1 lanes, all distinct, and every
+    (zero lane, sign triple) appears once (4 x 2^3 = 32)."""
+    seen = set()
+    for p in range(32):
+        lanes = O.stq1_pattern(p)
+        assert sorted(map(abs, lanes)) == [0, 1, 1, 1]
+        seen.add(tuple(lanes))
+    assert len(seen) == 32
+    all_patterns = set()
+    for z in range(4):
+        for signs in itertools.product((1, -1), repeat=3):
+            v = list(signs)
+            v.insert(z, 0)
+            all_patterns.add(tuple(v))
+    assert seen == all_patterns
+
+
+def test_stq1_sizes_match_pages():
+    g = {k: float(v[0][0]) for k, v in _kv("stq1_format.txt").items()}
+    z, s, d = synth.stq1_pattern_fields(11, 0, 0, 0, 64 * 3)
+    codes, scales = O.stq1_pack(z, s, d)
+    n_blk = 3
+    assert codes.size == n_blk * g["code_bytes"]
+    assert scales.nbytes == n_blk * g["scale_bytes"]
+    per_block = (codes.size + scales.nbytes) / n_blk
+    assert per_block == g["block_bytes"]
+    assert per_block * 8 / g["block_weights"] == g["bpw"]
+    assert codes.size / n_blk * 8 / g["block_weights"] == g["bpw_codes_only"]
+    assert g["groups_per_block"] * g["bits_per_group"] / 8 == g["code_bytes"]
+    assert g["patterns"] == 2 ** g["bits_per_group"] == 32
+    w = O.stq1_decode(codes, scales).reshape(-1, 4)
+    assert ((w == 0).sum(axis=1) == g["zeros_per_group"]).all()
+
+
+def test_stq1_layout_handwritten_examples():
+    ex = _kv("stq1_layout_example.txt")
+    for v in ex["pattern"]:
+        p, lanes = int(v[0]), [int(t) for t in v[1:]]
+        assert O.stq1_pattern(p) == lanes, p
+    d1 = np.array([0x3C00], dtype=np.uint16)          # fp16 1.0
+    # block where group g has pattern g % 32
+    p = np.arange(64) % 32
+    codes, _ = O.stq1_pack(p >> 3, p & 7, d1)
+    assert codes.tobytes().hex() == "".join(ex["block_pg_mod32"][0])
+    w = O.stq1_decode(codes, d1).reshape(64, 4)
+    for g in range(64):
+        assert list(w[g]) == [float(t) for t in O.stq1_pattern(g % 32)]
+    p = np.full(64, 13)
+    codes, _ = O.stq1_pack(p >> 3, p & 7, d1)
+    assert codes.tobytes().hex() == "".join(ex["block_p13"][0])
+
+
+def test_stq1_pack_decode_roundtrip_and_scale():
+    z, s, d = synth.stq1_pattern_fields(3, 0, 1, 2, 64 * 40)
+    codes, scales = O.stq1_pack(z, s, d)
+    p = O.stq1_patterns_of(codes).reshape(-1)
+    assert (p == z.astype(int) * 8 + s).all()
+    w = O.stq1_decode(codes, scales).reshape(40, 256)
+    dv = d.view(np.float16).astype(np.float64)
+    for b in range(40):
+        assert set(np.unique(np.abs(w[b]))) <= {0.0, dv[b]}
+        assert (w[b] == 0).sum() == 64
+
+
+def test_uniform_bytes_are_uniform_patterns():
+    """The generator draws uniform code bytes; every 5-bit value is a valid pattern, so
+    patterns (and zero lanes) come out uniform -- the distribution the workloads ask for."""
+    codes, _ = synth.stq1_matrix(5, 0, 0, 0, 256 * 2000)
+    p = O.stq1_patterns_of(codes).reshape(-1)
+    hist = np.bincount(p, minlength=32)
+    exp = p.size / 32
+    chi2 = ((hist - exp) ** 2 / exp).sum()
+    assert chi2 < 70, chi2          # 31 dof: p(chi2 > 70) ~ 1e-4
+    zl = np.bincount(p >> 3, minlength=4) / p.size
+    assert np.abs(zl - 0.25).max() < 0.01
+
+
+def test_flashmoe_package_bytes():
+    """Closed-form STQ1_0 matrix bytes reproduce the package's slot and sidecar sizes."""
+    g = {k: int(float(v[0][0])) if k != "gateup_avg_bpw" else float(v[0][0])
+         for k, v in _kv("flashmoe_package.txt").items()}
+    H, I = g["hidden"], g["moe_intermediate"]
+    n = H * I
+    stq = n // 256 * 42
+    assert stq == 2_064_384
+    iq2 = n // 256 * g["iq2xxs_block_bytes"]
+    assert g["iq2xxs_block_bytes"] * 8 / 256 == 2.0625
+    iq3 = n // 256 * g["iq3xxs_block_bytes"]
+    iq4 = n // 256 * g["iq4xs_block_bytes"]
+    slot = (g["stq1_gateup_layers"] * 2 * stq + g["iq2xxs_gateup_layers"] * 2 * iq2
+            + g["iq3xxs_down_layers"] * iq3 + g["iq4xs_down_layers"] * iq4)
+    assert g["stq1_gateup_layers"] + g["iq2xxs_gateup_layers"] == g["moe_layers"]
+    assert slot == g["slot_bytes"]
+    assert slot * g["routed_experts"] == g["sidecar_bytes"]
+    avg = (g["stq1_gateup_layers"] * 1.3125 + g["iq2xxs_gateup_layers"] * 2.0625) / g["moe_layers"]
+    assert round(avg, 2) == g["gateup_avg_bpw"]
+
+
+# ----------------------------------------------------------------------------- number formats
+def test_e2m1_values():
+    mags = [float(t) for t in _kv("e2m1_values.txt")["code_magnitudes"][0]]
+    v = O.e2m1_value(np.arange(16))
+    assert list(v[:8]) == mags
+    assert list(v[8:]) == [-m for m in mags]
+
+
+def test_e4m3_decode_vs_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = O.e4m3_value(np.arange(256))
+    nan = np.isnan(ref)
+    assert (np.isnan(mine) == nan).all() and nan.sum() == 2
+    assert (mine[~nan] == ref[~nan]).all()
+    assert np.nanmax(mine) == O.E4M3_MAX
+
+
+def test_ue8m0_values():
+    v = O.ue8m0_value(np.arange(256))
+    assert np.isnan(v[255])
+    assert all(v[c] == math.ldexp(1.0, c - 127) for c in range(255))
+
+
+def _e4m3_bruteforce(y):
+    """Nearest finite E4M3 value by search; ties to the even code; beyond 448 saturate."""
+    vals = O.e4m3_value(np.arange(128))[:127]      # non-negative finite values, codes 0..126
+    out = []
+    for t in np.asarray(y, dtype=np.float64).reshape(-1):
+        a = abs(t)
+        dist = np.abs(vals - a)
+        best = np.flatnonzero(dist == dist.min())
+        c = int(best[0]) if len(best) == 1 else int([b for b in best if b % 2 == 0][0])
+        if a > 448:
+            c = 126
+        out.append(c | (128 if math.copysign(1.0, t) < 0 else 0))
+    return np.array(out, dtype=np.uint8)
+
+
+def test_e4m3_encode_vs_bruteforce_and_torch():
+    # every bf16 magnitude from 2^-12 up to 512, both signs, plus exact ties
+    bits = np.arange(0x3980, 0x4400, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    vals = np.concatenate([vals, -vals, [0.0, -0.0, 2 ** -10, 3 * 2 ** -10, 17.0, 19.0, 464.0, 480.0]])
+    mine = O.e4m3_encode(vals)
+    assert (mine == _e4m3_bruteforce(vals)).all()
+    small = np.abs(vals) < 464
+    t = torch.tensor(vals[small], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (mine[small] == t).all()
+
+
+def test_mx_quantize_rule():
+    g = np.random.default_rng(0)
+    rows = [g.standard_normal(32),
+            np.zeros(32),
+            np.full(32, 2.0 ** -140),          # clamps at scale byte 0
+            np.full(32, 2.0 ** 140),           # clamps at scale byte 254
+            np.r_[256.0, g.integers(-16, 17, 31)],
+            g.standard_normal(32) * 1e-5,
+            np.r_[511.0, g.standard_normal(31)]]
+    v = np.stack(rows)
+    q, s = O.mx_quantize_e4m3(v)
+    for i, row in enumerate(v):
+        amax = np.abs(row).max()
+        if amax == 0:
+            assert s[i, 0] == 0 and (q[i] == 0).all()
+            continue
+        X = int(s[i, 0]) - 127
+        if -127 < X < 127:
+            assert 256 <= amax / 2.0 ** X < 512          # scale rule: floor(log2 amax) - 8
+        assert (q[i] == _e4m3_bruteforce(row / 2.0 ** X)).all()
+    assert s[2, 0] == 0 and s[3, 0] == 254
+    # exact integer group: 256 forces X = 0 and small integers stay exact
+    assert (O.mx_dequantize_e4m3(q[4:5], s[4:5]) == v[4]).all()
+
+
+def test_bf16_rne_vs_torch():
+    g = np.random.default_rng(1)
+    x = np.concatenate([g.standard_normal(20000).astype(np.float32),
+                        (g.standard_normal(2000) * 1e-30).astype(np.float32),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)], dtype=np.float32)])
+    ref = torch.tensor(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (O.f64_to_bf16_bits(x.astype(np.float64)) == ref).all()
+    assert (synth.f32_to_bf16_bits(x) == ref).all()       # the generator agrees too
+
+
+# ----------------------------------------------------------------------------- routing
+def test_route_bruteforce_subsets():
+    g = np.random.default_rng(2)
+    for E, k in [(6, 2), (7, 3), (5, 5), (8, 1)]:
+        logits = g.standard_normal((5, E))
+        _, ids, w = O.route(k, logits_in=logits)
+        for t in range(5):
+            best = max(itertools.combinations(range(E), k), key=lambda c: sum(logits[t, list(c)]))
+            assert set(ids[t]) == set(best)
+            assert list(ids[t]) == sorted(best, key=lambda e: -logits[t, e])
+            full = scipy.special.softmax(logits[t])
+            ref = full[ids[t]] / full[ids[t]].sum()
+            assert np.allclose(w[t], ref, rtol=1e-14, atol=0)
+            assert abs(w[t].sum() - 1) < 1e-14
+
+
+def test_route_ties_and_bias():
+    logits = np.array([[1.0, 3.0, 3.0, 0.5, 3.0]])
+    _, ids, w = O.route(3, logits_in=logits)
+    assert list(ids[0]) == [1, 2, 4]
+    assert np.allclose(w[0], 1 / 3)
+    _, ids, _ = O.route(2, logits_in=logits, bias=np.array([5.0, 0, 0, 0, 0]))
+    assert list(ids[0]) == [0, 1]
+
+
+def test_route_from_bf16_matches_bruteforce_dot():
+    x = synth.activations(0, 0, 2, 64)
+    wr = synth.router_weights(0, 0, 4, 64)
+    logits, _, _ = O.route(2, x, wr)
+    for t in range(2):
+        for e in range(4):
+            acc = 0.0
+            for h in range(64):
+                a = np.array([np.uint32(x[t, h]) << 16], dtype=np.uint32).view(np.float32)[0]
+                b = np.array([np.uint32(wr[e, h]) << 16], dtype=np.uint32).view(np.float32)[0]
+                acc += float(a) * float(b)
+            assert abs(acc - logits[t, e]) <= 1e-15 * 64
+
+
+# ----------------------------------------------------------------------------- permute
+def test_permute_vs_stable_sort():
+    g = np.random.default_rng(3)
+    for T, k, E in [(1, 8, 256), (7, 2, 8), (64, 8, 256), (5, 3, 4)]:
+        ids = np.stack([g.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        sp, off, pp = O.permute(ids, E)
+        flat = ids.reshape(-1)
+        ref = sorted(range(flat.size), key=lambda f: flat[f])     # Python's sort is stable
+        assert list(sp) == ref
+        assert list(off) == [0] + list(np.cumsum(np.bincount(flat, minlength=E)))
+        assert (sp[pp] == np.arange(flat.size)).all()
+        assert (np.diff(flat[sp]) >= 0).all()
+
+
+# ----------------------------------------------------------------------------- expert math
+def test_silu_vs_scipy():
+    g = np.linspace(-30, 30, 10001)
+    assert np.allclose(O.silu(g), g * scipy.special.expit(g), rtol=1e-15, atol=1e-300)
+
+
+def test_swiglu_bruteforce_loops():
+    g = np.random.default_rng(4)
+    K, N, n = 8, 6, 3
+    a = g.standard_normal((n, K))
+    Wg, Wu, Wd = g.standard_normal((N, K)), g.standard_normal((N, K)), g.standard_normal((K, N))
+    h, y = O.swiglu_expert(a, Wg, Wu, Wd)
+    for r in range(n):
+        hh = []
+        for i in range(N):
+            gi = sum(a[r, c] * Wg[i, c] for c in range(K))
+            ui = sum(a[r, c] * Wu[i, c] for c in range(K))
+            hh.append(gi / (1 + math.exp(-gi)) * ui)
+        assert np.allclose(h[r], hh, rtol=1e-13)
+        for o in range(K):
+            assert math.isclose(y[r, o], sum(hh[i] * Wd[o, i] for i in range(N)), rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_onehot_input_returns_ternary_column():
+    codes, scales = synth.stq1_matrix(9, 0, 0, 0, 16 * 256)
+    W = O.stq1_matrix(codes, scales, 16, 256)
+    j = 77
+    a = np.zeros((1, 256))
+    a[0, j] = 1.0
+    col = (a @ W.T)[0]
+    dv = O.fp16_to_f64(scales)
+    for r in range(16):
+        blk = (r * 256 + j) // 256
+        assert col[r] in (0.0, dv[blk], -dv[blk])
+    assert (col == 0).mean() < 0.6
+
+
+def test_mxfp4_unit_scale_integer_matmul():
+    """Scale bytes 127 and integer-valued activations: the MX gate stage equals an integer
+    matmul computed with Python ints."""
+    g = np.random.default_rng(5)
+    N, K = 5, 64
+    codes = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    W = O.mxfp4_matrix(codes, np.full((N, K // 32), 127, np.uint8), N, K)
+    assert np.all(W == np.round(W * 2) / 2)
+    act = g.integers(-16, 17, (3, K)).astype(np.float64)
+    act[:, 0] = 256.0
+    act[:, 32] = -256.0
+    q, s = O.mx_quantize_e4m3(act)
+    assert (s == 127).all()
+    a = O.mx_dequantize_e4m3(q, s)
+    assert (a == act).all()
+    got = a @ W.T
+    Wi = (W * 2).astype(np.int64).tolist()
+    for r in range(3):
+        for o in range(N):
+            ref = sum(int(act[r, c]) * Wi[o][c] for c in range(K))
+            assert got[r, o] * 2 == ref
+
+
+def test_mxfp4_nibble_order():
+    codes = np.array([[0x2A, 0x00] * 16], dtype=np.uint8)     # low nibble 0xA = -1, high 0x2 = +1
+    W = O.mxfp4_matrix(codes, np.array([[127, 127]], np.uint8), 1, 64)[0]
+    assert W[0] == -1.0 and W[1] == 1.0 and W[2] == 0.0 and W[3] == 0.0
+
+
+def test_combine_identity_single_expert():
+    g = np.random.default_rng(6)
+    y = g.standard_normal((4, 8))
+    ids = np.zeros((4, 1), dtype=np.int32)
+    sp, off, pp = O.permute(ids, 1)
+    out = O.combine(y, np.ones((4, 1)), pp)
+    assert (out == y[pp]).all()
+    w = np.array([[0.25, 0.75]] * 2)
+    yp = g.standard_normal((4, 3))
+    pp2 = np.array([2, 0, 3, 1])
+    out = O.combine(yp, w, pp2, y_shared=np.ones((2, 3)), residual=np.full((2, 3), 2.0))
+    assert np.allclose(out[0], 3 + 0.25 * yp[2] + 0.75 * yp[0])
+    assert np.allclose(out[1], 3 + 0.25 * yp[3] + 0.75 * yp[1])
+
+
+def test_rmsnorm_closed_form():
+    r = np.array([[3.0, 4.0] * 4, [1.0] * 8])
+    a = O.bf16_to_f64(O.rmsnorm_bf16(r, eps=0.0))
+    s = math.sqrt(12.5)
+    assert np.allclose(a[0], [3 / s, 4 / s] * 4, rtol=2 ** -8)
+    assert (a[1] == 1.0).all()
+    a = O.bf16_to_f64(O.rmsnorm_bf16(np.array([[1e-4] * 8]), eps=1e-6))
+    assert np.allclose(a, 1e-4 / math.sqrt(1e-8 + 1e-6), rtol=2 ** -8)
+
+
+# ----------------------------------------------------------------------------- whole layer, tiny
+def test_tiny_layer_bruteforce():
+    """Config-0 shapes: the oracle layer equals a pure-Python loop over tokens and slots
+    that decodes every weight through stq1_pattern one group at a time."""
+    c = synth.cfg(0)
+    x = synth.activations(c.seed, 0, c.T, c.H)
+    wr = synth.router_weights(c.seed, 0, c.E, c.H)
+    fam = [synth.stq1_family(c.seed, 0, m, c.E, c.I * c.H) for m in range(3)]
+    shapes = [(c.I, c.H), (c.I, c.H), (c.H, c.I)]
+
+    def get_w(e, m):
+        return O.stq1_matrix(fam[m][0][e], fam[m][1][e], *shapes[m])
+
+    res = O.moe_layer(x, c.k, get_w, "stq1", wr_bits=wr)
+    xf = O.bf16_to_f64(x)
+
+    def weight(e, m, r, col):
+        N, K = shapes[m]
+        flat = r * K + col
+        blk, within = divmod(flat, 256)
+        grp, lane = divmod(within, 4)
+        pbytes = fam[m][0][e][blk * 40:(blk + 1) * 40]
+        nib = (pbytes[grp // 2] >> (4 * (grp % 2))) & 15
+        hb = (int.from_bytes(bytes(pbytes[32:40]), "little") >> grp) & 1
+        d = float(np.array([fam[m][1][e][blk]], np.uint16).view(np.float16)[0])
+        return O.stq1_pattern(int(nib) | (hb << 4))[lane] * d
+
+    for t in range(c.T):
+        out = np.zeros(c.H)
+        for j in range(c.k):
+            e = int(res["ids"][t, j])
+            hvec = []
+            for i in range(c.I):
+                gi = sum(xf[t, q] * weight(e, 0, i, q) for q in range(c.H))
+                ui = sum(xf[t, q] * weight(e, 1, i, q) for q in range(c.H))
+                hvec.append(gi / (1 + math.exp(-gi)) * ui)
+            for o in range(c.H):
+                out[o] += res["w"][t, j] * sum(hvec[i] * weight(e, 2, o, i) for i in range(c.I))
+        assert np.allclose(res["out"][t], out, rtol=1e-10, atol=1e-12)
