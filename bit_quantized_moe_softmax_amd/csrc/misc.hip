@@ -1,0 +1,224 @@
+// Combine, RMSNorm, STQ1_0 pack/decode, MXFP4 decode and MX activation quantisation.
+#include "moe_device.h"
+
+namespace {
+
+// ---------------------------------------------------------------- combine
+// out[t] = y_shared[t] + sum_j w[t][j] * y_pairs[pair_pos[t*k+j]] (+ residual[t]).
+// The shared expert is ungated: the Flash-MoE package lists one shared expert per MoE
+// block and no gate for it.  One thread per 4 consecutive hidden elements.
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ y_pairs, const float* __restrict__ w,
+    const int32_t* __restrict__ pair_pos, const float* __restrict__ y_shared,
+    const float* residual, float* out, uint16_t* __restrict__ out_bf16, int H, int k) {
+  const int t = blockIdx.y;
+  const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (h >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (y_shared) acc = *reinterpret_cast<const float4*>(y_shared + (size_t)t * H + h);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const int pos = pair_pos[(size_t)t * k + j];
+    const float4 y = *reinterpret_cast<const float4*>(y_pairs + (size_t)pos * H + h);
+    acc.x = fmaf(wj, y.x, acc.x);
+    acc.y = fmaf(wj, y.y, acc.y);
+    acc.z = fmaf(wj, y.z, acc.z);
+    acc.w = fmaf(wj, y.w, acc.w);
+  }
+  if (residual) {
+    const float4 r = *reinterpret_cast<const float4*>(residual + (size_t)t * H + h);
+    acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+  }
+  *reinterpret_cast<float4*>(out + (size_t)t * H + h) = acc;
+  if (out_bf16) {
+    uint2 b;
+    b.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+    b.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    *reinterpret_cast<uint2*>(out_bf16 + (size_t)t * H + h) = b;
+  }
+}
+
+// ---------------------------------------------------------------- RMSNorm + bf16 cast
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ r,
+                                                      uint16_t* __restrict__ a, int H,
+                                                      float eps) {
+  __shared__ float s_part[4];
+  const int t = blockIdx.x;
+  const float* row = r + (size_t)t * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += 256) ss = fmaf(row[i], row[i], ss);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += 256)
+    a[(size_t)t * H + i] = (uint16_t)f32_to_bf16_rne(row[i] * inv);
+}
+
+// ---------------------------------------------------------------- STQ1_0 pack / decode
+// Pattern p = 8*z + s; byte i of the 32-byte nibble area = p[2i] & 15 | (p[2i+1] & 15) << 4;
+// bytes 32..39 = little-endian word with bit g = p[g] >> 4.  One wave per block.
+__global__ __launch_bounds__(256) void stq1_pack_kernel(const uint8_t* __restrict__ z,
+                                                        const uint8_t* __restrict__ sg,
+                                                        const uint16_t* __restrict__ d,
+                                                        int64_t n_blocks,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= n_blocks) return;
+  const int64_t g = b * 64 + lane;
+  const uint32_t p = ((uint32_t)(z[g] & 3) << 3) | (sg[g] & 7);
+  const uint64_t hi = __ballot((p >> 4) & 1);
+  const uint32_t nib = p & 15;
+  const uint32_t other = __shfl_xor(nib, 1, 64);
+  uint8_t* blk = codes + b * 40;
+  if ((lane & 1) == 0) blk[lane >> 1] = (uint8_t)(nib | (other << 4));
+  if (lane < 8) blk[32 + lane] = (uint8_t)(hi >> (8 * lane));
+  if (lane == 0) scales[b] = d[b];
+}
+
+// Lane j of pattern p (in units of d): the zero lane is z = p >> 3; the other lanes in
+// ascending order take the sign bits 0, 1, 2 of s = p & 7 (1 = negative).
+__device__ __forceinline__ float stq1_lane(uint32_t p, int j) {
+  const int z = p >> 3;
+  if (j == z) return 0.f;
+  const int i = j < z ? j : j - 1;
+  return ((p >> i) & 1) ? -1.f : 1.f;
+}
+
+__global__ __launch_bounds__(256) void stq1_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                           const uint16_t* __restrict__ scales,
+                                                           int64_t n_blocks,
+                                                           float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= n_blocks) return;
+  const uint8_t* blk = codes + b * 40;
+  const uint32_t nib = (blk[lane >> 1] >> ((lane & 1) * 4)) & 15;
+  const uint32_t hb = (blk[32 + (lane >> 3)] >> (lane & 7)) & 1;
+  const uint32_t p = nib | (hb << 4);
+  const float dv = fp16_to_f32(scales[b]);
+  float4 o;
+  o.x = stq1_lane(p, 0) * dv;
+  o.y = stq1_lane(p, 1) * dv;
+  o.z = stq1_lane(p, 2) * dv;
+  o.w = stq1_lane(p, 3) * dv;
+  *reinterpret_cast<float4*>(out + b * 256 + lane * 4) = o;
+}
+
+// ---------------------------------------------------------------- MXFP4 decode
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3, m = c & 1;
+  const float mag = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
+  return (c & 8) ? -mag : mag;
+}
+
+__global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t n_pairs, int K,
+                                                            float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one code byte each
+  if (i >= n_pairs) return;
+  const int64_t row = i / (K / 2);
+  const int64_t col = (i % (K / 2)) * 2;
+  const uint8_t c = codes[i];
+  const float sc = ldexpf(1.0f, (int)scales[row * (K / 32) + col / 32] - 127);
+  out[row * K + col] = e2m1_to_f32(c & 15) * sc;
+  out[row * K + col + 1] = e2m1_to_f32(c >> 4) * sc;
+}
+
+__global__ __launch_bounds__(256) void mx_quant_kernel(int64_t n_groups, const uint16_t* xb,
+                                                       const float* xf, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ sc) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= n_groups) return;
+  uint32_t bits[32];
+  if (xb) {
+    const uint4* src = reinterpret_cast<const uint4*>(xb + gi * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = src[i];
+      bits[8 * i + 0] = v.x << 16; bits[8 * i + 1] = v.x & 0xFFFF0000u;
+      bits[8 * i + 2] = v.y << 16; bits[8 * i + 3] = v.y & 0xFFFF0000u;
+      bits[8 * i + 4] = v.z << 16; bits[8 * i + 5] = v.z & 0xFFFF0000u;
+      bits[8 * i + 6] = v.w << 16; bits[8 * i + 7] = v.w & 0xFFFF0000u;
+    }
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(xf + gi * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = src[i];
+      bits[4 * i + 0] = v.x; bits[4 * i + 1] = v.y; bits[4 * i + 2] = v.z; bits[4 * i + 3] = v.w;
+    }
+  }
+  uint32_t amax = 0;   // compare magnitudes as integers (finite inputs)
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = max(amax, bits[i] & 0x7FFFFFFFu);
+  uint32_t out[8];
+  if (amax == 0) {
+    sc[gi] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = 0;
+  } else {
+    const int X = moe_mx_exp(amax);
+    sc[gi] = (uint8_t)(X + 127);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      out[i] = moe_e4m3_from_f32(bits[4 * i], X) | (moe_e4m3_from_f32(bits[4 * i + 1], X) << 8) |
+               (moe_e4m3_from_f32(bits[4 * i + 2], X) << 16) | (moe_e4m3_from_f32(bits[4 * i + 3], X) << 24);
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(q + gi * 32);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+}  // namespace
+
+hipError_t moe_launch_combine(const float* y_pairs, const float* w, const int32_t* pair_pos,
+                              const float* y_shared, const float* residual, float* out,
+                              uint16_t* out_bf16, int T, int H, int k, hipStream_t s) {
+  dim3 grid((H / 4 + 255) / 256, T);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y_pairs, w, pair_pos, y_shared,
+                     residual, out, out_bf16, H, k);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_rmsnorm(const float* r, uint16_t* a, int T, int H, float eps,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, s, r, a, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_stq1_pack(const uint8_t* z, const uint8_t* sg, const uint16_t* d,
+                                int64_t n_blocks, uint8_t* codes, uint16_t* scales,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(stq1_pack_kernel, dim3((unsigned)((n_blocks + 3) / 4)), dim3(256), 0, s, z,
+                     sg, d, n_blocks, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_stq1_dequant(const uint8_t* codes, const uint16_t* scales,
+                                   int64_t n_blocks, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(stq1_dequant_kernel, dim3((unsigned)((n_blocks + 3) / 4)), dim3(256), 0, s,
+                     codes, scales, n_blocks, out);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                    int K, float* out, hipStream_t s) {
+  const int64_t n = rows * (K / 2);
+  hipLaunchKernelGGL(mxfp4_dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     codes, scales, n, K, out);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_mx_quant(int64_t rows, int K, const uint16_t* xb, const float* xf,
+                               uint8_t* q, uint8_t* sc, hipStream_t s) {
+  const int64_t ng = rows * (K / 32);
+  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, s, ng,
+                     xb, xf, q, sc);
+  return hipGetLastError();
+}

@@ -1,0 +1,310 @@
+// C ABI of libmoe_mi355x: argument checks, workspace layout, kernel dispatch and the
+// host-side path counters.  Every entry point only enqueues work on the caller's stream.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "moe_device.h"
+
+namespace {
+
+std::atomic<uint64_t> g_counters[MOE_CNT_SLOTS];
+
+inline void bump(int slot) { g_counters[slot].fetch_add(1, std::memory_order_relaxed); }
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* v = std::getenv("MOE_MI355X_DEBUG_SYNC");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+moe_status finish(hipError_t e, hipStream_t s) {
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (debug_sync()) {
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool dims_ok(const moe_dims* d) {
+  if (!d) return false;
+  if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->k <= 0) return false;
+  if (d->E > 1024 || d->k > d->E || d->k > 32) return false;
+  if (d->H % 32 || d->I % 32) return false;
+  return true;
+}
+
+// Workspace regions: 0 h routed f32, 1 h shared f32, 2 xq, 3 xs, 4 hq, 5 hs, 6 total.
+void layout(const moe_dims* d, int fmt, int has_shared, size_t* offs) {
+  const size_t T = d->T, H = d->H, I = d->I, P = (size_t)d->T * d->k;
+  for (int i = 0; i < 7; ++i) offs[i] = (size_t)-1;
+  size_t cur = 0;
+  if (fmt == MOE_W_STQ1_0) {
+    offs[0] = cur;
+    cur = align_up(cur + P * I * sizeof(float));
+  }
+  if (has_shared) {
+    offs[1] = cur;
+    cur = align_up(cur + T * I * sizeof(float));
+  }
+  if (fmt == MOE_W_MXFP4) {
+    offs[2] = cur; cur = align_up(cur + T * H);
+    offs[3] = cur; cur = align_up(cur + T * (H / 32));
+    offs[4] = cur; cur = align_up(cur + P * I);
+    offs[5] = cur; cur = align_up(cur + P * (I / 32));
+  }
+  offs[6] = cur;
+}
+
+bool mat_ok(const moe_mat& m, bool need_scales) { return m.codes && (!need_scales || m.scales); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* moe_version(void) { return "moe_mi355x 0.1 gfx950"; }
+
+moe_status moe_get_counters(uint64_t* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < MOE_CNT_SLOTS; ++i) out[i] = g_counters[i].load(std::memory_order_relaxed);
+  return MOE_OK;
+}
+
+moe_status moe_reset_counters(void) {
+  for (int i = 0; i < MOE_CNT_SLOTS; ++i) g_counters[i].store(0, std::memory_order_relaxed);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_dims* d, const uint16_t* x_bf16, const uint16_t* wr_bf16,
+                     const float* logit_bias, const float* logits_in, float* logits_out,
+                     int32_t* topk_ids, float* topk_w, void* stream) {
+  if (!dims_ok(d) || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!logits_in && (!x_bf16 || !wr_bf16 || !logits_out)) return MOE_ERR_INVALID_ARG;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  if (!logits_in) {
+    hipError_t e = moe_launch_route_gemv(x_bf16, wr_bf16, logit_bias, logits_out, d->T, d->H,
+                                         d->E, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    bump(MOE_CNT_ROUTE_GEMV);
+    e = moe_launch_topk(logits_out, nullptr, nullptr, d->T, d->E, d->k, topk_ids, topk_w, s);
+    bump(MOE_CNT_ROUTE_TOPK);
+    return finish(e, s);
+  }
+  hipError_t e = moe_launch_topk(logits_in, logit_bias, logits_out, d->T, d->E, d->k, topk_ids,
+                                 topk_w, s);
+  bump(MOE_CNT_ROUTE_TOPK);
+  return finish(e, s);
+}
+
+moe_status moe_permute(const moe_dims* d, const int32_t* topk_ids, int32_t* sorted_pair,
+                       int32_t* expert_offsets, int32_t* pair_pos, void* stream) {
+  if (!dims_ok(d) || !topk_ids || !sorted_pair || !expert_offsets || !pair_pos)
+    return MOE_ERR_INVALID_ARG;
+  if ((int64_t)d->T * d->k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = moe_launch_permute(topk_ids, d->T * d->k, d->E, sorted_pair, expert_offsets,
+                                    pair_pos, s);
+  bump(MOE_CNT_PERMUTE);
+  return finish(e, s);
+}
+
+moe_status moe_workspace_size(const moe_dims* d, int32_t routed_fmt, int32_t has_shared,
+                              size_t* bytes) {
+  if (!dims_ok(d) || !bytes) return MOE_ERR_INVALID_ARG;
+  if (routed_fmt != MOE_W_STQ1_0 && routed_fmt != MOE_W_MXFP4) return MOE_ERR_INVALID_ARG;
+  size_t offs[7];
+  layout(d, routed_fmt, has_shared, offs);
+  *bytes = offs[6];
+  return MOE_OK;
+}
+
+moe_status moe_workspace_offsets(const moe_dims* d, int32_t routed_fmt, int32_t has_shared,
+                                 size_t* offs) {
+  if (!dims_ok(d) || !offs) return MOE_ERR_INVALID_ARG;
+  if (routed_fmt != MOE_W_STQ1_0 && routed_fmt != MOE_W_MXFP4) return MOE_ERR_INVALID_ARG;
+  layout(d, routed_fmt, has_shared, offs);
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
+                          const moe_experts* shared, const uint16_t* x_bf16,
+                          const int32_t* sorted_pair, const int32_t* expert_offsets,
+                          float* y_pairs, float* y_shared, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!dims_ok(d) || !routed || !x_bf16 || !sorted_pair || !expert_offsets || !y_pairs)
+    return MOE_ERR_INVALID_ARG;
+  const int fmt = routed->fmt;
+  if (fmt != MOE_W_STQ1_0 && fmt != MOE_W_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (!mat_ok(routed->gate, true) || !mat_ok(routed->up, true) || !mat_ok(routed->down, true))
+    return MOE_ERR_INVALID_ARG;
+  if (shared) {
+    if (shared->fmt != MOE_W_BF16 || !y_shared) return MOE_ERR_INVALID_ARG;
+    if (!mat_ok(shared->gate, false) || !mat_ok(shared->up, false) || !mat_ok(shared->down, false))
+      return MOE_ERR_INVALID_ARG;
+    if (d->H % 256 || d->I % 256) return MOE_ERR_UNSUPPORTED;
+  }
+  const int T = d->T, H = d->H, I = d->I, E = d->E, k = d->k;
+  if (fmt == MOE_W_STQ1_0) {
+    if (((int64_t)H * I) % 256) return MOE_ERR_UNSUPPORTED;
+    if (H % 256 == 0 && H / 256 > 4 * 16) return MOE_ERR_UNSUPPORTED;
+    if (I % 256 == 0 && I / 256 > 4 * 16) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
+  }
+  size_t offs[7];
+  layout(d, fmt, shared != nullptr, offs);
+  if (!ws || ws_bytes < offs[6]) return MOE_ERR_WORKSPACE;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const int P = T * k;
+
+  if (fmt == MOE_W_STQ1_0) {
+    float* h = reinterpret_cast<float*>(wsb + offs[0]);
+    FfnArgs a{};
+    a.codes0 = routed->gate.codes; a.scales0 = routed->gate.scales;
+    a.codes1 = routed->up.codes;   a.scales1 = routed->up.scales;
+    a.act = x_bf16; a.sorted_pair = sorted_pair; a.offsets = expert_offsets; a.out = h;
+    a.N = I; a.K = H; a.T = T; a.E = E; a.k = k; a.P = P;
+    hipError_t e;
+    if (H % 256 == 0) { e = moe_launch_stq_gateup(a, s); bump(MOE_CNT_STQ_GATEUP_MFMA); }
+    else { e = moe_launch_stq_generic(a, 0, s); bump(MOE_CNT_STQ_GENERIC); }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    FfnArgs b{};
+    b.codes0 = routed->down.codes; b.scales0 = routed->down.scales;
+    b.act = h; b.sorted_pair = sorted_pair; b.offsets = expert_offsets; b.out = y_pairs;
+    b.N = H; b.K = I; b.T = T; b.E = E; b.k = k; b.P = P;
+    if (I % 256 == 0) { e = moe_launch_stq_down(b, s); bump(MOE_CNT_STQ_DOWN_MFMA); }
+    else { e = moe_launch_stq_generic(b, 1, s); bump(MOE_CNT_STQ_GENERIC); }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  } else {
+    uint8_t* xq = wsb + offs[2];
+    uint8_t* xs = wsb + offs[3];
+    uint8_t* hq = wsb + offs[4];
+    uint8_t* hs = wsb + offs[5];
+    hipError_t e = moe_launch_mx_quant(T, H, x_bf16, nullptr, xq, xs, s);
+    bump(MOE_CNT_MX_QUANT);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    MxArgs a{};
+    a.wcodes0 = static_cast<const uint8_t*>(routed->gate.codes);
+    a.wscales0 = static_cast<const uint8_t*>(routed->gate.scales);
+    a.wcodes1 = static_cast<const uint8_t*>(routed->up.codes);
+    a.wscales1 = static_cast<const uint8_t*>(routed->up.scales);
+    a.aq = xq; a.as = xs; a.sorted_pair = sorted_pair; a.offsets = expert_offsets;
+    a.hq = hq; a.hs = hs; a.N = I; a.K = H; a.T = T; a.E = E; a.k = k; a.P = P;
+    e = moe_launch_mx_gateup(a, s);
+    bump(MOE_CNT_MX_GATEUP_MFMA);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    MxArgs b{};
+    b.wcodes0 = static_cast<const uint8_t*>(routed->down.codes);
+    b.wscales0 = static_cast<const uint8_t*>(routed->down.scales);
+    b.aq = hq; b.as = hs; b.sorted_pair = sorted_pair; b.offsets = expert_offsets;
+    b.y = y_pairs; b.N = H; b.K = I; b.T = T; b.E = E; b.k = k; b.P = P;
+    e = moe_launch_mx_down(b, s);
+    bump(MOE_CNT_MX_DOWN_MFMA);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+
+  if (shared) {
+    float* hsh = reinterpret_cast<float*>(wsb + offs[1]);
+    FfnArgs a{};
+    a.codes0 = shared->gate.codes; a.codes1 = shared->up.codes;
+    a.act = x_bf16; a.out = hsh; a.N = I; a.K = H; a.T = T; a.E = 1; a.k = 1; a.P = T;
+    hipError_t e = moe_launch_bf16_gateup(a, s);
+    bump(MOE_CNT_BF16_GATEUP);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    FfnArgs b{};
+    b.codes0 = shared->down.codes; b.act = hsh; b.out = y_shared;
+    b.N = H; b.K = I; b.T = T; b.E = 1; b.k = 1; b.P = T;
+    e = moe_launch_bf16_down(b, s);
+    bump(MOE_CNT_BF16_DOWN);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return finish(hipSuccess, s);
+}
+
+moe_status moe_combine(const moe_dims* d, const float* y_pairs, const float* topk_w,
+                       const int32_t* pair_pos, const float* y_shared, const float* residual,
+                       float* out_f32, uint16_t* out_bf16, void* stream) {
+  if (!dims_ok(d) || !y_pairs || !topk_w || !pair_pos || !out_f32) return MOE_ERR_INVALID_ARG;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = moe_launch_combine(y_pairs, topk_w, pair_pos, y_shared, residual, out_f32,
+                                    out_bf16, d->T, d->H, d->k, s);
+  bump(MOE_CNT_COMBINE);
+  return finish(e, s);
+}
+
+moe_status moe_stq1_pack(const uint8_t* zpos, const uint8_t* signs, const uint16_t* d_f16,
+                         int64_t n_blocks, uint8_t* codes, uint16_t* scales, void* stream) {
+  if (n_blocks < 0 || (n_blocks > 0 && (!zpos || !signs || !d_f16 || !codes || !scales)))
+    return MOE_ERR_INVALID_ARG;
+  if (n_blocks == 0) return MOE_OK;
+  if (n_blocks > (int64_t)4 * 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  return finish(moe_launch_stq1_pack(zpos, signs, d_f16, n_blocks, codes, scales, s), s);
+}
+
+moe_status moe_stq1_dequant(const uint8_t* codes, const uint16_t* scales, int64_t n_blocks,
+                            float* out, void* stream) {
+  if (n_blocks < 0 || (n_blocks > 0 && (!codes || !scales || !out))) return MOE_ERR_INVALID_ARG;
+  if (n_blocks == 0) return MOE_OK;
+  if (n_blocks > (int64_t)4 * 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  bump(MOE_CNT_DEQUANT);
+  return finish(moe_launch_stq1_dequant(codes, scales, n_blocks, out, s), s);
+}
+
+moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                             int32_t K, float* out, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 || (rows > 0 && (!codes || !scales || !out)))
+    return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (rows * (K / 2) > (int64_t)256 * 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  bump(MOE_CNT_DEQUANT);
+  return finish(moe_launch_mxfp4_dequant(codes, scales, rows, K, out, s), s);
+}
+
+moe_status moe_mx_quant_act(int64_t rows, int32_t K, const uint16_t* x_bf16, const float* x_f32,
+                            uint8_t* q, uint8_t* sc, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if ((x_bf16 == nullptr) == (x_f32 == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!q || !sc)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (rows * (K / 32) > (int64_t)256 * 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  bump(MOE_CNT_MX_QUANT);
+  return finish(moe_launch_mx_quant(rows, K, x_bf16, x_f32, q, sc, s), s);
+}
+
+moe_status moe_rmsnorm_bf16(int32_t T, int32_t H, float eps, const float* r, uint16_t* a,
+                            void* stream) {
+  if (T < 0 || H <= 0 || (T > 0 && (!r || !a)) || !(eps >= 0.f)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  bump(MOE_CNT_RMSNORM);
+  return finish(moe_launch_rmsnorm(r, a, T, H, eps, s), s);
+}
+
+}  // extern "C"

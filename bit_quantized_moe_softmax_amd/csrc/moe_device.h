@@ -1,0 +1,178 @@
+// Device-side helpers shared by the gfx950 kernels of libmoe_mi355x.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_mi355x.h"
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+#define MOE_WAVE 64
+
+// ---------------------------------------------------------------- scalar formats
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round a finite fp32 to bf16 bits, nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float fp16_to_f32(uint32_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+  return (float)v;
+}
+
+// ---------------------------------------------------------------- E4M3 encoding
+// Exact integer rounding of |v| / 2^X onto the E4M3 grid (3 mantissa bits, subnormal
+// quantum 2^-9), ties to even, saturated to 448 (code 0x7E); sign from the input.
+__device__ __forceinline__ uint32_t moe_e4m3_from_f32(uint32_t bits, int X) {
+  const uint32_t sign = (bits >> 31) << 7;
+  const uint32_t ev = (bits >> 23) & 0xFF;
+  uint32_t M = bits & 0x7FFFFF;
+  int E0;                                   // |v| = M * 2^E0
+  if (ev == 0) {
+    if (M == 0) return sign;
+    E0 = -149;
+  } else {
+    M |= 0x800000;
+    E0 = (int)ev - 150;
+  }
+  const int lg = (31 - __clz(M)) + E0 - X;  // floor(log2 |y|), y = v / 2^X
+  const int qexp = lg - 3 > -9 ? lg - 3 : -9;
+  const int sh = qexp - (E0 - X);           // y / 2^qexp = M / 2^sh
+  uint32_t R;
+  if (sh <= 0) {
+    R = M << (-sh);                         // exact (only when y is a multiple of 2^qexp)
+  } else if (sh > 25) {
+    R = 0;
+  } else {
+    const uint32_t q = M >> sh;
+    const uint32_t rem = M & ((1u << sh) - 1u);
+    const uint32_t half = 1u << (sh - 1);
+    R = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+  }
+  // value = R * 2^qexp with R <= 16
+  uint32_t code;
+  if (R == 0) {
+    code = 0;
+  } else if (qexp == -9 && R < 8) {
+    code = R;                               // subnormal
+  } else {
+    int ef = qexp + 3 + 7;                  // exponent field for R in [8, 15]
+    uint32_t m = R - 8;
+    if (R == 16) { ef += 1; m = 0; }
+    if (ef > 15 || (ef == 15 && m > 6)) code = 0x7E;   // saturate to 448
+    else code = ((uint32_t)ef << 3) | m;
+  }
+  return sign | code;
+}
+
+// MX shared exponent of a group from the bits of its largest magnitude (> 0):
+// X = floor(log2(amax)) - 8, clamped to [-127, 127]; the scale byte is X + 127.
+__device__ __forceinline__ int moe_mx_exp(uint32_t amax_bits) {
+  const uint32_t ea = amax_bits >> 23;
+  const int lg = ea ? (int)ea - 127 : (31 - __clz(amax_bits & 0x7FFFFF)) - 149;
+  const int X = lg - 8;
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+
+// The slot-th expert (in expert order) that has at least one routed pair, found by each
+// wave on its own from the expert offsets (uniform across the wave).  Returns -1 when
+// fewer experts are active.
+__device__ __forceinline__ int moe_find_active_expert(const int32_t* __restrict__ off, int E,
+                                                      int slot, int& start, int& cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int run = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int c = e < E ? off[e + 1] - off[e] : 0;
+    const uint64_t m = __ballot(c > 0);
+    const int n = __popcll(m);
+    if (slot < run + n) {
+      const int want = slot - run;
+      const uint64_t mm = __ballot(c > 0 && __popcll(m & lt) == want);
+      const int ee = base + __ffsll((unsigned long long)mm) - 1;
+      start = off[ee];
+      cnt = off[ee + 1] - start;
+      return ee;
+    }
+    run += n;
+  }
+  return -1;
+}
+
+// ---------------------------------------------------------------- launch plumbing
+#define MOE_HIP_TRY(expr)                                  \
+  do {                                                     \
+    hipError_t _e = (expr);                                \
+    if (_e != hipSuccess) return _e;                       \
+  } while (0)
+
+// Host launchers implemented by the kernel translation units.
+hipError_t moe_launch_route_gemv(const uint16_t* x, const uint16_t* wr, const float* bias,
+                                 float* logits, int T, int H, int E, hipStream_t s);
+hipError_t moe_launch_topk(const float* logits, const float* bias, float* logits_out, int T,
+                           int E, int k, int32_t* ids, float* w, hipStream_t s);
+hipError_t moe_launch_permute(const int32_t* ids, int P, int E, int32_t* sorted_pair,
+                              int32_t* offsets, int32_t* pair_pos, hipStream_t s);
+hipError_t moe_launch_combine(const float* y_pairs, const float* w, const int32_t* pair_pos,
+                              const float* y_shared, const float* residual, float* out,
+                              uint16_t* out_bf16, int T, int H, int k, hipStream_t s);
+hipError_t moe_launch_rmsnorm(const float* r, uint16_t* a, int T, int H, float eps,
+                              hipStream_t s);
+hipError_t moe_launch_stq1_pack(const uint8_t* z, const uint8_t* sg, const uint16_t* d,
+                                int64_t n_blocks, uint8_t* codes, uint16_t* scales,
+                                hipStream_t s);
+hipError_t moe_launch_stq1_dequant(const uint8_t* codes, const uint16_t* scales,
+                                   int64_t n_blocks, float* out, hipStream_t s);
+hipError_t moe_launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                    int K, float* out, hipStream_t s);
+hipError_t moe_launch_mx_quant(int64_t rows, int K, const uint16_t* xb, const float* xf,
+                               uint8_t* q, uint8_t* sc, hipStream_t s);
+
+// Decode-regime FFN (routed STQ1_0 and shared bf16) on the bf16 MFMA.
+// kind: 0 routed gate/up, 1 routed down, 2 shared gate/up, 3 shared down.
+struct FfnArgs {
+  const void* codes0;
+  const void* scales0;
+  const void* codes1;
+  const void* scales1;
+  const void* act;           // bf16 x [*, K] (gate/up) or fp32 h [*, K] (down)
+  const int32_t* sorted_pair;
+  const int32_t* offsets;
+  float* out;
+  int N, K, T, E, k, P;
+};
+hipError_t moe_launch_stq_gateup(const FfnArgs& a, hipStream_t s);
+hipError_t moe_launch_stq_down(const FfnArgs& a, hipStream_t s);
+hipError_t moe_launch_stq_generic(const FfnArgs& a, int down, hipStream_t s);
+hipError_t moe_launch_bf16_gateup(const FfnArgs& a, hipStream_t s);
+hipError_t moe_launch_bf16_down(const FfnArgs& a, hipStream_t s);
+
+// Prefill MXFP4 x FP8 grouped GEMMs on the scaled MFMA.
+struct MxArgs {
+  const uint8_t* wcodes0; const uint8_t* wscales0;   // gate or down
+  const uint8_t* wcodes1; const uint8_t* wscales1;   // up
+  const uint8_t* aq; const uint8_t* as;              // activations E4M3 + UE8M0
+  const int32_t* sorted_pair; const int32_t* offsets;
+  uint8_t* hq; uint8_t* hs;                          // gate/up output (E4M3 h)
+  float* y;                                          // down output
+  int N, K, T, E, k, P;
+};
+hipError_t moe_launch_mx_gateup(const MxArgs& a, hipStream_t s);
+hipError_t moe_launch_mx_down(const MxArgs& a, hipStream_t s);

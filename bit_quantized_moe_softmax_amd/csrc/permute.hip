@@ -1,0 +1,100 @@
+// Permute: stable counting sort of the (token, slot) pairs by expert.
+//
+// Gives each expert a contiguous run of rows, the expert-major order in which the
+// Flash-MoE runtime streams only the routed experts ("Hy4-preview Flash-MoE STQ1_0",
+// expert-major sidecar).  One workgroup of 16 waves: LDS histogram, block scan, then
+// chunks of 1024 pairs where each pair's rank among equal experts comes from wave
+// ballots (same-expert lanes found bit by bit) plus per-wave counts in LDS -- the
+// output order is fixed by the pair index, never by atomics.
+#include "moe_device.h"
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxE = 1024;
+
+__global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ ids,
+                                                           int P, int E, int nbits,
+                                                           int32_t* __restrict__ sorted_pair,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ pair_pos) {
+  __shared__ int s_cnt[kMaxE];
+  __shared__ int s_base[kMaxE];
+  __shared__ int s_wsum[kWaves];
+  __shared__ uint8_t s_wc[kWaves][kMaxE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+
+  for (int e = tid; e < E; e += kThreads) s_cnt[e] = 0;
+  __syncthreads();
+  for (int f = tid; f < P; f += kThreads) atomicAdd(&s_cnt[ids[f]], 1);
+  __syncthreads();
+
+  // exclusive scan of s_cnt[0..E) (E <= 1024: one value per thread)
+  {
+    const int c = tid < E ? s_cnt[tid] : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w2 = 0; w2 < wv; ++w2) before += s_wsum[w2];
+    const int excl = before + incl - c;
+    if (tid < E) {
+      s_base[tid] = excl;
+      offsets[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = P;
+  }
+  __syncthreads();
+
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < P; c0 += kThreads) {
+    // clear the per-wave counts of this chunk
+    for (int i = tid; i < kWaves * E; i += kThreads) s_wc[i / E][i % E] = 0;
+    __syncthreads();
+    const int f = c0 + tid;
+    const bool valid = f < P;
+    const int e = valid ? ids[f] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(valid && bit);
+      peers &= bit ? ones : ~ones;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) s_wc[wv][e] = (uint8_t)__popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int w2 = 0; w2 < wv; ++w2) pre += s_wc[w2][e];
+      const int pos = s_base[e] + pre + rank;
+      sorted_pair[pos] = f;
+      pair_pos[f] = pos;
+    }
+    __syncthreads();
+    for (int e2 = tid; e2 < E; e2 += kThreads) {
+      int s = 0;
+      for (int w2 = 0; w2 < kWaves; ++w2) s += s_wc[w2][e2];
+      s_base[e2] += s;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t moe_launch_permute(const int32_t* ids, int P, int E, int32_t* sorted_pair,
+                              int32_t* offsets, int32_t* pair_pos, hipStream_t s) {
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kThreads), 0, s, ids, P, E, nbits,
+                     sorted_pair, offsets, pair_pos);
+  return hipGetLastError();
+}

@@ -1,0 +1,243 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X (gfx950) routed-expert MoE FFN library
+ * (libmoe_mi355x.so).
+ *
+ * The library runs one Hy4-shaped MoE layer on packed low-bit expert weights: a
+ * bf16 router picks k of E routed experts per token, the routed SwiGLU experts run
+ * directly on STQ1_0 or MXFP4 weights, one bf16 shared expert runs on every token,
+ * and the outputs are combined.  Shapes follow "Hy4-preview Flash-MoE STQ1_0"
+ * (anemll), Package details table: 256 routed experts per MoE block, 8 selected
+ * per token, 1 shared expert, embedding width 6144, MoE intermediate width 2048.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is a DEVICE pointer owned by the caller.  The library never
+ *   allocates, frees or keeps any of them; it only enqueues kernels.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *   call is asynchronous on that stream; the host never waits inside a call.
+ * - Return codes report the synchronous argument checks (null pointers, shapes the
+ *   kernels do not support, short workspaces) and launch errors.  A fault inside a
+ *   kernel surfaces as MOE_ERR_HIP on a later call or at the caller's next
+ *   synchronisation.  With the environment variable MOE_MI355X_DEBUG_SYNC=1 every
+ *   call synchronises its stream and reports such faults itself.
+ * - Inputs are never written.  Outputs must not alias inputs, except that
+ *   `residual` may equal `out_f32` in moe_combine.
+ * - bf16 and fp16 values travel as their uint16_t bit patterns.
+ * - The library keeps no state between calls apart from the path counters of
+ *   moe_get_counters (atomically updated; calls on different streams are safe).
+ *
+ * Weight layouts (expert-major: expert e's matrix follows expert e-1's)
+ * -------------------------------------------------------------------
+ * STQ1_0 ("Hy4-preview-GGUF" (AngelSlim) section 3, The format; "Hy4-preview
+ * Flash-MoE STQ1_0", How the STQ1_0 packing works): 256-weight blocks of 64 groups
+ * of four weights; each group has exactly one zero and three values in {-d,+d};
+ * one binary16 scale d per block; 42 bytes per 256 weights.  Our bit layout of the
+ * 5-bit group pattern p = 8*z + s (z = zero lane 0..3, bit i of s = 1 when the i-th
+ * non-zero lane in ascending lane order is -d):
+ *   codes  : 40 bytes per block -- bytes 0..31: byte i = (p[2i] & 15) | (p[2i+1] & 15) << 4;
+ *            bytes 32..39: little-endian 64-bit word, bit g = p[g] >> 4.
+ *   scales : one uint16 (binary16 bits) per block, same block order.
+ *   Blocks run over the row-major [out][in] matrix, flattened, so a matrix of n
+ *   weights owns n/256 blocks (n % 256 == 0).
+ * MXFP4 ("Hy4-preview-SF-WFP4AFP8" (siliconflow), Quant Diff table: FP4 E2M1
+ * weights, group 32, UE8M0 scales):
+ *   codes  : [out][in/2] bytes, element 2i in the low nibble (E2M1: bit 3 sign).
+ *   scales : [out][in/32] UE8M0 bytes (value 2^(v-127)), groups along `in`.
+ * BF16 (shared expert, router): [out][in] uint16 bf16 bits.
+ * Gate and up are [I][H] (out = I, in = H); down is [H][I].
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MI355X_API __attribute__((visibility("default")))
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad or inconsistent shape            */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid request this build has no kernel for         */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than moe_workspace_size */
+  MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed         */
+} moe_status;
+
+typedef enum { MOE_W_STQ1_0 = 1, MOE_W_MXFP4 = 2, MOE_W_BF16 = 3 } moe_wfmt;
+
+/* Layer dimensions: T tokens, hidden H, expert intermediate I, E routed experts,
+ * k experts per token.  Limits: 1 <= k <= min(E, 32), E <= 1024, H % 32 == 0,
+ * I % 32 == 0; STQ1_0 needs (I*H) % 256 == 0; MXFP4 needs H % 128 == 0 and
+ * I % 128 == 0.  T == 0 is allowed and enqueues nothing. */
+typedef struct { int32_t T, H, I, E, k; } moe_dims;
+
+/* One weight family (gate, up or down) of `n` experts, expert-major. */
+typedef struct { const void* codes; const void* scales; } moe_mat;
+
+/* The three families of a set of experts (E routed experts, or 1 shared). */
+typedef struct {
+  int32_t fmt;          /* moe_wfmt of all three families                      */
+  int32_t reserved;
+  moe_mat gate, up, down;
+} moe_experts;
+
+/* Counter slots of moe_get_counters. */
+enum {
+  MOE_CNT_ROUTE_GEMV = 0,      /* router logits computed from x             */
+  MOE_CNT_ROUTE_TOPK = 1,      /* top-k launches                            */
+  MOE_CNT_PERMUTE = 2,
+  MOE_CNT_STQ_GATEUP_MFMA = 3, /* STQ1_0 fused-decode gate/up, MFMA path    */
+  MOE_CNT_STQ_DOWN_MFMA = 4,
+  MOE_CNT_STQ_GENERIC = 5,     /* STQ1_0 slow path (blocks straddling rows) */
+  MOE_CNT_MX_QUANT = 6,
+  MOE_CNT_MX_GATEUP_MFMA = 7,
+  MOE_CNT_MX_DOWN_MFMA = 8,
+  MOE_CNT_BF16_GATEUP = 9,     /* shared expert                             */
+  MOE_CNT_BF16_DOWN = 10,
+  MOE_CNT_COMBINE = 11,
+  MOE_CNT_RMSNORM = 12,
+  MOE_CNT_DEQUANT = 13,
+  MOE_CNT_BF16_GEMM = 14,      /* shared expert, large-T tiled GEMM path    */
+  MOE_CNT_SLOTS = 16
+};
+
+MOE_MI355X_API const char* moe_status_str(moe_status s);
+MOE_MI355X_API const char* moe_version(void);
+
+/* Path counters: out[MOE_CNT_SLOTS] receives how many times each kernel variant
+ * was launched since load or the last reset (host-side counts, no device work). */
+MOE_MI355X_API moe_status moe_get_counters(uint64_t* out);
+MOE_MI355X_API moe_status moe_reset_counters(void);
+
+/* ---------------------------------------------------------------------------
+ * Route.  Router logits l[t][e] = sum_h x[t][h] * Wr[e][h] (+ logit_bias[e]) in
+ * fp32 from bf16 operands (the router stays BF16: "Hy4-preview-SF-WFP4AFP8", BF16
+ * row of the Quant Diff table), then the k largest logits per token ("Hy4-preview
+ * Flash-MoE STQ1_0": 8 selected experts per token, --moe-topk 8).  The pages give
+ * no routing function; this library takes softmax over all experts, keeps the top
+ * k and renormalises, i.e. topk_w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ * over the selected slots.  Slots are ordered by descending logit, ties to the
+ * lower expert index.
+ *   x_bf16      [T][H] bf16, ignored when logits_in != NULL
+ *   wr_bf16     [E][H] bf16, ignored when logits_in != NULL
+ *   logit_bias  [E] fp32 or NULL (added to the logits in both modes)
+ *   logits_in   [T][E] fp32 or NULL: when given, the router GEMV is skipped
+ *   logits_out  [T][E] fp32 or NULL: receives the (biased) logits
+ *   topk_ids    [T][k] int32 out, topk_w [T][k] fp32 out
+ * ------------------------------------------------------------------------- */
+MOE_MI355X_API moe_status moe_route(const moe_dims* d, const uint16_t* x_bf16,
+                                    const uint16_t* wr_bf16, const float* logit_bias,
+                                    const float* logits_in, float* logits_out,
+                                    int32_t* topk_ids, float* topk_w, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Permute: group the P = T*k (token, slot) pairs by expert, stably, so each
+ * expert's rows are contiguous (the expert-major order the Flash-MoE sidecar
+ * streams).  Pair f = t*k + j.  expert_offsets[e] = number of pairs with expert
+ * below e (expert_offsets[E] = P); within one expert pairs keep increasing f;
+ * sorted_pair[pos] = f and pair_pos[f] = pos.  Deterministic (no atomics decide
+ * the order).  Any topk_ids value outside [0, E) is an error the kernel cannot
+ * report; the caller guarantees the range (moe_route produces it).
+ *   topk_ids [P] int32; sorted_pair [P], expert_offsets [E+1], pair_pos [P] int32 out
+ * ------------------------------------------------------------------------- */
+MOE_MI355X_API moe_status moe_permute(const moe_dims* d, const int32_t* topk_ids,
+                                      int32_t* sorted_pair, int32_t* expert_offsets,
+                                      int32_t* pair_pos, void* stream);
+
+/* Workspace bytes moe_expert_ffn needs for routed format `routed_fmt` with or
+ * without a shared expert (host-only, no device work). */
+MOE_MI355X_API moe_status moe_workspace_size(const moe_dims* d, int32_t routed_fmt,
+                                             int32_t has_shared, size_t* bytes);
+
+/* Byte offsets of the workspace regions, so tests can read the intermediates:
+ *   offs[0] h of the routed pairs, fp32 [P][I] (STQ1_0 path)
+ *   offs[1] h of the shared expert, fp32 [T][I]
+ *   offs[2] x as E4M3 codes [T][H]          (MXFP4 path)
+ *   offs[3] x UE8M0 scales  [T][H/32]       (MXFP4 path)
+ *   offs[4] h as E4M3 codes [P][I]          (MXFP4 path, sorted-pair order)
+ *   offs[5] h UE8M0 scales  [P][I/32]       (MXFP4 path)
+ *   offs[6] total bytes
+ * Unused regions get offset (size_t)-1. */
+MOE_MI355X_API moe_status moe_workspace_offsets(const moe_dims* d, int32_t routed_fmt,
+                                                int32_t has_shared, size_t* offs);
+
+/* ---------------------------------------------------------------------------
+ * Expert FFN.  For every routed pair at sorted position pos (token t =
+ * sorted_pair[pos] / k, expert e with expert_offsets[e] <= pos < expert_offsets[e+1]):
+ *   g = Wg[e] a_t,  u = Wu[e] a_t,  h = silu(g) * u,  y_pairs[pos] = Wd[e] h
+ * (SwiGLU expert MLP: gate_proj / up_proj / down_proj of the routed experts).
+ *   STQ1_0: a_t = bf16 x[t]; weights decoded in registers; fp32 accumulation;
+ *           h kept in fp32.
+ *   MXFP4:  a_t = x[t] MX-quantised to E4M3 with group-32 UE8M0 scales along H, and
+ *           h MX-quantised the same way along I before the down projection (every
+ *           routed-expert linear of the WFP4AFP8 recipe takes FP8 E4M3 group-32
+ *           activations); FP8 x FP4 products on the scaled MFMA, fp32 accumulation.
+ * When `shared` is non-NULL (fmt MOE_W_BF16, one expert) y_shared[t] = the same
+ * SwiGLU on bf16 weights and bf16 x[t] for every token, h kept in fp32.
+ *   x_bf16 [T][H]; sorted_pair [P]; expert_offsets [E+1] (from moe_permute)
+ *   y_pairs [P][H] fp32 out (sorted-pair order); y_shared [T][H] fp32 out or NULL
+ *   ws / ws_bytes: device workspace of at least moe_workspace_size bytes.
+ * ------------------------------------------------------------------------- */
+MOE_MI355X_API moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
+                                         const moe_experts* shared, const uint16_t* x_bf16,
+                                         const int32_t* sorted_pair,
+                                         const int32_t* expert_offsets, float* y_pairs,
+                                         float* y_shared, void* ws, size_t ws_bytes,
+                                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Combine: out[t] = y_shared[t] + sum_j topk_w[t][j] * y_pairs[pair_pos[t*k + j]]
+ * (+ residual[t]), summed in that order in fp32.  The shared expert is always on
+ * and ungated (the Flash-MoE package lists one shared expert per MoE block and no
+ * gate for it).
+ *   y_pairs [P][H]; topk_w [T][k]; pair_pos [P]; y_shared [T][H] or NULL;
+ *   residual [T][H] or NULL (may equal out_f32); out_f32 [T][H] out;
+ *   out_bf16 [T][H] out (round to nearest even) or NULL.
+ * ------------------------------------------------------------------------- */
+MOE_MI355X_API moe_status moe_combine(const moe_dims* d, const float* y_pairs,
+                                      const float* topk_w, const int32_t* pair_pos,
+                                      const float* y_shared, const float* residual,
+                                      float* out_f32, uint16_t* out_bf16, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Helpers (same conventions).
+ * ------------------------------------------------------------------------- */
+
+/* Pack STQ1_0: zpos [n_blocks*64] zero lanes (0..3), signs [n_blocks*64] sign fields
+ * (0..7, bit i = i-th non-zero lane negative), d_f16 [n_blocks] binary16 bits ->
+ * codes [n_blocks*40], scales [n_blocks].  Values outside those ranges are masked
+ * to their low bits. */
+MOE_MI355X_API moe_status moe_stq1_pack(const uint8_t* zpos, const uint8_t* signs,
+                                        const uint16_t* d_f16, int64_t n_blocks,
+                                        uint8_t* codes, uint16_t* scales, void* stream);
+
+/* Decode STQ1_0 blocks to fp32 weights out [n_blocks*256] (exact). */
+MOE_MI355X_API moe_status moe_stq1_dequant(const uint8_t* codes, const uint16_t* scales,
+                                           int64_t n_blocks, float* out, void* stream);
+
+/* Decode MXFP4 rows: codes [rows][K/2], scales [rows][K/32] -> out [rows][K] fp32 (exact). */
+MOE_MI355X_API moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales,
+                                            int64_t rows, int32_t K, float* out, void* stream);
+
+/* MX-quantise rows of K (K % 32 == 0) into E4M3 codes q [rows][K] and UE8M0 scales
+ * s [rows][K/32].  Input is either bf16 (x_bf16) or fp32 (x_f32); exactly one must be
+ * non-NULL.  Rule (OCP MX v1.0 reading): X = floor(log2(amax)) - 8 clamped to
+ * [-127, 127], scale byte X + 127; elements round to nearest even of v / 2^X,
+ * saturated to +-448; the sign bit follows the input (a negative value that rounds
+ * to zero gives 0x80); a group with amax == 0 stores scale 0 and zero codes. */
+MOE_MI355X_API moe_status moe_mx_quant_act(int64_t rows, int32_t K, const uint16_t* x_bf16,
+                                           const float* x_f32, uint8_t* q, uint8_t* s,
+                                           void* stream);
+
+/* Pre-norm for a residual stack of MoE layers: a[t] = bf16(r[t] / sqrt(mean(r[t]^2) + eps))
+ * (norm weight 1), r [T][H] fp32, a [T][H] bf16 out. */
+MOE_MI355X_API moe_status moe_rmsnorm_bf16(int32_t T, int32_t H, float eps, const float* r,
+                                           uint16_t* a, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,96 @@
+"""The C-ABI library loads, exports every symbol its header declares, and its host-side
+argument checks and workspace arithmetic behave (no device work; CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_moe_softmax_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_MI355X_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", txt)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert len(names) >= 15
+    L = M.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(M.EXPORTED)
+
+
+def test_status_and_version():
+    assert M.moe_status_str(0) == "ok"
+    assert "workspace" in M.moe_status_str(3)
+    assert "gfx950" in M.moe_version()
+
+
+def test_counters_roundtrip():
+    M.moe_reset_counters()
+    c = M.moe_get_counters()
+    assert set(c) == set(M.COUNTER_NAMES) and all(v == 0 for v in c.values())
+
+
+def test_workspace_layout():
+    d = M.Dims(T=4, H=256, I=128, E=8, k=2)
+    n = M.moe_workspace_size(d, M.MOE_W_STQ1_0, False)
+    assert n == 8 * 128 * 4                      # h of 8 pairs x 128, fp32, 256-aligned
+    offs = M.moe_workspace_offsets(d, M.MOE_W_STQ1_0, True)
+    assert offs[0] == 0 and offs[1] == 4096 and offs[2] is None and offs[6] == 4096 + 2048
+    d = M.Dims(T=4096, H=6144, I=2048, E=256, k=8)
+    offs = M.moe_workspace_offsets(d, M.MOE_W_MXFP4, True)
+    P = 4096 * 8
+    assert offs[0] is None
+    assert offs[1] == 0 and offs[2] == 4096 * 2048 * 4
+    assert offs[3] == offs[2] + 4096 * 6144
+    assert offs[4] == offs[3] + 4096 * 6144 // 32
+    assert offs[5] == offs[4] + P * 2048
+    assert offs[6] == offs[5] + P * 2048 // 32
+
+
+def _raw(name, *args):
+    return getattr(M.lib(), name)(*args)
+
+
+def test_argument_checks_need_no_gpu():
+    bad = M.Dims(T=1, H=6144, I=2048, E=256, k=40)          # k > 32
+    assert _raw("moe_route", bad.ref(), None, None, None, None, None, None, None, None) == 1
+    d = M.Dims(T=1, H=6144, I=2048, E=256, k=8)
+    # missing outputs
+    assert _raw("moe_route", d.ref(), None, None, None, None, None, None, None, None) == 1
+    assert _raw("moe_permute", d.ref(), None, None, None, None, None) == 1
+    assert _raw("moe_combine", d.ref(), None, None, None, None, None, None, None, None) == 1
+    # expert_ffn: short workspace is reported before any launch
+    routed = M.Experts(M.MOE_W_STQ1_0, (1 << 20, 1 << 20), (1 << 20, 1 << 20), (1 << 20, 1 << 20))
+    st = _raw("moe_expert_ffn", d.ref(), routed.ref(), None, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+              None, 1 << 20, ctypes.c_size_t(16), None)
+    assert st == 3
+    # unsupported MXFP4 shape (H not a multiple of 128)
+    d2 = M.Dims(T=1, H=96, I=128, E=8, k=2)
+    mx = M.Experts(M.MOE_W_MXFP4, (1 << 20, 1 << 20), (1 << 20, 1 << 20), (1 << 20, 1 << 20))
+    st = _raw("moe_expert_ffn", d2.ref(), mx.ref(), None, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+              None, 1 << 20, ctypes.c_size_t(1 << 30), None)
+    assert st == 2
+    # a shared expert must be bf16
+    sh = M.Experts(M.MOE_W_STQ1_0, (1 << 20, None), (1 << 20, None), (1 << 20, None))
+    st = _raw("moe_expert_ffn", d.ref(), routed.ref(), sh.ref(), 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+              1 << 20, 1 << 20, ctypes.c_size_t(1 << 30), None)
+    assert st == 1
+    assert _raw("moe_mx_quant_act", 4, 30, None, None, None, None, None) == 1
+    assert _raw("moe_mx_quant_act", 4, 32, 1 << 20, 1 << 20, 1 << 20, 1 << 20, None) == 1
+    assert _raw("moe_rmsnorm_bf16", 2, 64, ctypes.c_float(-1.0), 1 << 20, 1 << 20, None) == 1
+    assert _raw("moe_stq1_pack", None, None, None, -1, None, None, None) == 1
+
+
+def test_zero_tokens_enqueue_nothing():
+    d = M.Dims(T=0, H=256, I=128, E=8, k=2)
+    # T == 0 returns before touching the (fake) pointers or the GPU
+    assert _raw("moe_route", d.ref(), 8, 8, None, None, 8, 8, 8, None) == 0
+    assert _raw("moe_combine", d.ref(), 8, 8, 8, None, None, 8, None, None) == 0

@@ -1,0 +1,365 @@
+"""GPU parity of every hot-path step against the CPU oracle, through the C ABI.
+
+Bit-exact: STQ1_0 packing and decoding, MXFP4 decoding, MX activation quantisation,
+top-k ids and slot order from given logits, the permutation.  Tolerance (max |err| /
+RMS of the reference row <= 2e-3): expert outputs and the combined layer output.
+Where floating point decides an integer (top-k from x-computed logits, the FP8 codes of
+h) near-ties are allowed to differ and are counted instead."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_moe_softmax_amd as M
+import synth
+from bit_quantized_moe_softmax_amd.layer import LayerBuffers, bf16_experts, run_layer
+from oracle import moe_oracle as O
+from tests.helpers import (TOL, layer_inputs, near_tie_tokens, oracle_weights, row_err, shapes,
+                           valid_selection)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-parity]", *a, file=sys.__stderr__, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    M.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t, dtype=None):
+    a = t.detach().cpu().numpy()
+    return a.view(dtype) if dtype is not None else a
+
+
+def routed_experts(c, routed):
+    fmt = M.MOE_W_STQ1_0 if c.fmt == "stq1" else M.MOE_W_MXFP4
+    tens = [(dev(codes), dev(scales)) for codes, scales in routed]
+    return M.Experts(fmt, *tens)
+
+
+def shared_experts(shared):
+    if shared is None:
+        return None
+    return bf16_experts(*(dev(w) for w in shared))
+
+
+# ----------------------------------------------------------------------------- formats
+def test_stq1_pack_dequant_bitexact():
+    n_blk = 1237
+    say("stq1_pack/dequant n_blk", n_blk)
+    z, s, d = synth.stq1_pattern_fields(21, 0, 0, 0, n_blk * 64)
+    codes_ref, scales_ref = O.stq1_pack(z, s, d)
+    codes = torch.empty(n_blk * 40, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(n_blk, dtype=torch.int16, device="cuda")
+    M.moe_stq1_pack(dev(z), dev(s), dev(d), n_blk, codes, scales)
+    assert (host(codes) == codes_ref).all()
+    assert (host(scales, np.uint16) == scales_ref).all()
+    out = torch.empty(n_blk * 256, dtype=torch.float32, device="cuda")
+    M.moe_stq1_dequant(codes, scales, n_blk, out)
+    ref = O.stq1_decode(codes_ref, scales_ref).astype(np.float32)
+    assert (host(out).view(np.uint32) == ref.view(np.uint32)).all()
+    # uniform code bytes of a Hy4-shaped matrix
+    codes2, scales2 = synth.stq1_matrix(1, 0, 3, 2, 2048 * 6144)
+    nb = scales2.size
+    out2 = torch.empty(nb * 256, dtype=torch.float32, device="cuda")
+    M.moe_stq1_dequant(dev(codes2), dev(scales2), nb, out2)
+    ref2 = O.stq1_decode(codes2, scales2).astype(np.float32)
+    assert (host(out2).view(np.uint32) == ref2.view(np.uint32)).all()
+
+
+def test_mxfp4_dequant_bitexact():
+    rows, K = 96, 512
+    say("mxfp4_dequant", rows, K)
+    codes, scales = synth.mxfp4_matrix(3, 0, 0, 0, rows, K)
+    scales = scales.copy()
+    scales[0] = np.arange(K // 32, dtype=np.uint8) * 15 + 10     # wide exponent range
+    out = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+    M.moe_mxfp4_dequant(dev(codes), dev(scales), rows, K, out)
+    ref = O.mxfp4_matrix(codes, scales, rows, K).astype(np.float32)
+    assert (host(out).view(np.uint32) == ref.view(np.uint32)).all()
+
+
+def _mx_case_rows(K):
+    g = np.random.default_rng(7)
+    x = synth.activations(3, 0, 40, K).astype(np.uint16)
+    rows = [x]
+    e = np.zeros((8, K), dtype=np.float32)
+    e[0] = 0.0                                           # amax 0
+    e[1] = g.standard_normal(K) * 1e-30                  # tiny, bf16 subnormal range
+    e[2] = g.standard_normal(K) * 3e30                   # huge
+    e[3] = np.where(np.arange(K) % 2 == 0, 256.0, -17.0)  # exact ties after scaling
+    e[4] = g.integers(-512, 512, K).astype(np.float32) / 64.0
+    e[5] = -np.abs(g.standard_normal(K)) * 1e-3
+    e[6, ::32] = 1.0
+    e[7] = g.standard_normal(K) * 448.0
+    rows.append(synth.f32_to_bf16_bits(e))
+    return np.concatenate(rows)
+
+
+def test_mx_quant_act_bitexact_bf16_and_f32():
+    K = 512
+    xb = _mx_case_rows(K)
+    say("mx_quant_act bf16 rows", xb.shape)
+    q = torch.empty(xb.shape, dtype=torch.uint8, device="cuda")
+    s = torch.empty((xb.shape[0], K // 32), dtype=torch.uint8, device="cuda")
+    M.moe_mx_quant_act(xb.shape[0], K, dev(xb), None, q, s)
+    rq, rs = O.mx_quantize_e4m3(O.bf16_to_f64(xb))
+    assert (host(s) == rs).all()
+    assert (host(q) == rq).all()
+    g = np.random.default_rng(8)
+    xf = (g.standard_normal((33, K)) * np.exp(g.uniform(-20, 20, (33, 1)))).astype(np.float32)
+    xf[0, :5] = [1e-40, -1e-41, 0.0, -0.0, 3e-39]            # fp32 subnormals
+    say("mx_quant_act f32 rows", xf.shape)
+    q2 = torch.empty(xf.shape, dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((xf.shape[0], K // 32), dtype=torch.uint8, device="cuda")
+    M.moe_mx_quant_act(xf.shape[0], K, None, dev(xf), q2, s2)
+    rq2, rs2 = O.mx_quantize_e4m3(xf.astype(np.float64))
+    assert (host(s2) == rs2).all()
+    assert (host(q2) == rq2).all()
+
+
+# ----------------------------------------------------------------------------- routing
+@pytest.mark.parametrize("T,E,k", [(37, 256, 8), (5, 8, 2), (3, 1024, 32), (9, 64, 64 // 2), (1, 7, 7)])
+def test_topk_from_logits_bitexact(T, E, k):
+    say("topk", T, E, k)
+    g = np.random.default_rng(T * 1000 + E)
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    logits[0] = np.round(logits[0] * 2) / 2                  # many exact ties
+    bias = (g.standard_normal(E) * 0.1).astype(np.float32) if T % 2 else None
+    d = M.Dims(T, 32, 32, E, k)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lo = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    M.moe_route(d, None, None, dev(bias) if bias is not None else None, dev(logits), lo, ids, w)
+    # the biased logits are fp32 sums; the oracle takes that same fp32 value
+    lref = logits if bias is None else (logits + bias[None, :]).astype(np.float32)
+    assert (host(lo) == lref).all()
+    _, rid, rw = O.route(k, logits_in=lref.astype(np.float64))
+    assert (host(ids) == rid).all()
+    assert np.allclose(host(w), rw, rtol=1e-6, atol=0)
+
+
+def test_route_from_x():
+    c = synth.cfg(2)
+    T = 70
+    say("route gemv T", T)
+    x = synth.activations(5, 0, T, c.H)
+    wr = synth.router_weights(5, 0, c.E, c.H)
+    bias = synth.zipf_bias(5, 0, c.E)
+    d = M.Dims(T, c.H, c.I, c.E, c.k)
+    ids = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, c.k), dtype=torch.float32, device="cuda")
+    lo = torch.empty((T, c.E), dtype=torch.float32, device="cuda")
+    M.moe_route(d, dev(x), dev(wr), dev(bias), None, lo, ids, w)
+    rl, rid, rw = O.route(c.k, x, wr, bias)
+    assert np.abs(host(lo) - rl).max() < 2e-5
+    tie = near_tie_tokens(rl, c.k)
+    gi = host(ids)
+    assert (gi[~tie] == rid[~tie]).all()
+    for t in np.flatnonzero(tie):
+        assert valid_selection(rl[t], gi[t], c.k)
+    say("near-tie tokens", int(tie.sum()), "of", T)
+    ok = ~tie
+    assert np.allclose(host(w)[ok], rw[ok], rtol=2e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("T,k,E,mode", [(1, 8, 256, "rand"), (7, 2, 8, "rand"), (64, 8, 256, "zipf"),
+                                        (4096, 8, 256, "rand"), (300, 3, 4, "rand"),
+                                        (129, 8, 256, "one"), (50, 1, 1024, "rand")])
+def test_permute_bitexact(T, k, E, mode):
+    say("permute", T, k, E, mode)
+    g = np.random.default_rng(T + k + E)
+    if mode == "one":
+        ids = np.stack([np.r_[5, g.choice(np.r_[0:5, 6:E], k - 1, replace=False)] for _ in range(T)])
+    elif mode == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        ids = np.stack([g.choice(E, k, replace=False, p=p / p.sum()) for _ in range(T)])
+    else:
+        ids = np.stack([g.choice(E, k, replace=False) for _ in range(T)])
+    ids = ids.astype(np.int32)
+    d = M.Dims(T, 32, 32, E, k)
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    M.moe_permute(d, dev(ids), sp, off, pp)
+    rsp, roff, rpp = O.permute(ids, E)
+    assert (host(sp) == rsp).all() and (host(off) == roff).all() and (host(pp) == rpp).all()
+
+
+# ----------------------------------------------------------------------------- whole layers
+SMALL = {
+    "cfg0": synth.cfg(0),
+    "h512-i256-e8-top2-t37-shared": synth.LayerCfg("t", 37, 512, 256, 8, 2, True, "stq1", False, False, 1, 11),
+    "h768-i512-e16-top4-t21-zipf": synth.LayerCfg("t", 21, 768, 512, 16, 4, True, "stq1", True, False, 1, 12),
+}
+
+
+def _check_layer(c, inp, bufs, d, ref, sample=None):
+    gi = host(bufs.topk_ids)
+    tie = near_tie_tokens(ref["logits"], c.k)
+    assert (gi[~tie] == ref["ids"][~tie]).all()
+    toks = np.arange(c.T) if sample is None else np.asarray(sample)
+    out = host(bufs.out)
+    if tie.any():
+        say("near-tie tokens", np.flatnonzero(tie))
+    keep = [t for t in toks if not tie[t]]
+    err = row_err(out[keep], ref["out"][keep])
+    say("layer max row err", float(err.max()))
+    assert err.max() <= TOL
+    return err
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_stq_small(name):
+    c = SMALL[name]
+    say("layer", name)
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, shared is not None)
+    bias = dev(inp["bias"]) if inp["bias"] is not None else None
+    M.moe_reset_counters()
+    run_layer(d, bufs, dev(inp["x"]), routed, shared, wr_bf16=dev(inp["wr"]), logit_bias=bias)
+    torch.cuda.synchronize()
+    ref = O.moe_layer(inp["x"], c.k, oracle_weights(c, inp["routed"]), "stq1", wr_bits=inp["wr"],
+                      bias=inp["bias"], shared=inp["shared"])
+    _check_layer(c, inp, bufs, d, ref)
+    cnt = M.moe_get_counters()
+    if c.H % 256 == 0:
+        assert cnt["stq_gateup_mfma"] == 1
+    if c.I % 256 == 0:
+        assert cnt["stq_down_mfma"] == 1
+    # per-stage: h and y_pairs of the pairs
+    yp = host(bufs.y_pairs)
+    if (host(bufs.topk_ids) == ref["ids"]).all():
+        assert row_err(yp, ref["y_pairs"]).max() <= TOL
+        if shared is not None:
+            assert row_err(host(bufs.y_shared), ref["y_shared"]).max() <= TOL
+
+
+def test_layer_cfg1_hy4_decode():
+    c = synth.cfg(1)
+    say("layer cfg1 generate")
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, True)
+    say("layer cfg1 run")
+    run_layer(d, bufs, dev(inp["x"]), routed, shared, wr_bf16=dev(inp["wr"]))
+    torch.cuda.synchronize()
+    say("layer cfg1 oracle")
+    ref = O.moe_layer(inp["x"], c.k, oracle_weights(c, inp["routed"]), "stq1", wr_bits=inp["wr"],
+                      shared=inp["shared"])
+    _check_layer(c, inp, bufs, d, ref)
+    assert row_err(host(bufs.y_pairs), ref["y_pairs"]).max() <= TOL
+    assert row_err(host(bufs.y_shared), ref["y_shared"]).max() <= TOL
+
+
+def test_layer_cfg2_hy4_decode_zipf_sampled():
+    c = synth.cfg(2)
+    say("layer cfg2 generate")
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, True)
+    say("layer cfg2 run")
+    run_layer(d, bufs, dev(inp["x"]), routed, shared, wr_bf16=dev(inp["wr"]),
+              logit_bias=dev(inp["bias"]))
+    torch.cuda.synchronize()
+    # routing of every token, then the full layer for a sample of tokens
+    rl, rid, rw = O.route(c.k, inp["x"], inp["wr"], inp["bias"])
+    tie = near_tie_tokens(rl, c.k)
+    gi = host(bufs.topk_ids)
+    assert (gi[~tie] == rid[~tie]).all()
+    sample = [t for t in synth.sample_tokens(c.seed, c.T, 6) if not tie[t]]
+    say("layer cfg2 oracle tokens", sample, "unique experts", len(np.unique(rid)))
+    get_w = oracle_weights(c, inp["routed"])
+    ref = O.moe_layer(inp["x"][sample], c.k, get_w, "stq1", wr_bits=inp["wr"], bias=inp["bias"],
+                      shared=inp["shared"])
+    err = row_err(host(bufs.out)[sample], ref["out"])
+    say("cfg2 sampled max row err", float(err.max()))
+    assert err.max() <= TOL
+
+
+MX_SMALL = synth.LayerCfg("mx", 150, 512, 256, 8, 2, True, "mxfp4", False, True, 1, 13)
+
+
+def _mx_stage_check(c, inp, bufs, d, toks_check=None):
+    offs = M.moe_workspace_offsets(d, M.MOE_W_MXFP4, True)
+    ws = host(bufs.ws)
+    T, H, I, P = c.T, c.H, c.I, c.T * c.k
+    xq = ws[offs[2]:offs[2] + T * H].reshape(T, H)
+    xs = ws[offs[3]:offs[3] + T * H // 32].reshape(T, H // 32)
+    rq, rs = O.mx_quantize_e4m3(O.bf16_to_f64(inp["x"]))
+    assert (xq == rq).all() and (xs == rs).all()
+    hq = ws[offs[4]:offs[4] + P * I].reshape(P, I)
+    hs = ws[offs[5]:offs[5] + P * I // 32].reshape(P, I // 32)
+    # reference h from the oracle's pieces on the pairs the GPU routed
+    sp = host(bufs.sorted_pair)
+    off = host(bufs.offsets)
+    _, rid, _ = O.route(c.k, logits_in=inp["logits_in"])
+    assert (host(bufs.topk_ids) == rid).all()
+    get_w = oracle_weights(c, inp["routed"])
+    a = O.mx_dequantize_e4m3(rq, rs)
+    yp = host(bufs.y_pairs)
+    n_flip = n_tot = 0
+    worst = 0.0
+    experts = range(c.E) if toks_check is None else toks_check
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        toks = sp[lo:hi] // c.k
+        g = a[toks] @ get_w(e, 0).T
+        u = a[toks] @ get_w(e, 1).T
+        h = O.silu(g) * u
+        hq_ref, hs_ref = O.mx_quantize_e4m3(h)
+        diff = hq[lo:hi] != hq_ref
+        if diff.any():
+            vg = O.mx_dequantize_e4m3(hq[lo:hi], hs[lo:hi])
+            vr = O.mx_dequantize_e4m3(hq_ref, hs_ref)
+            step = np.abs(vr) * 2.0 ** -3 + O.ue8m0_value(hs_ref).repeat(32, axis=1) * 2.0 ** -9
+            assert (np.abs(vg - vr)[diff] <= step[diff] * 1.0001).all()
+        n_flip += int(diff.sum())
+        n_tot += diff.size
+        # down stage fed the GPU's FP8 h
+        y_ref = O.mx_dequantize_e4m3(hq[lo:hi], hs[lo:hi]) @ get_w(e, 2).T
+        worst = max(worst, float(row_err(yp[lo:hi], y_ref).max()))
+    say("mx h code flips", n_flip, "of", n_tot, "down-stage max row err", worst)
+    assert n_flip <= max(2, 1e-4 * n_tot)
+    assert worst <= TOL
+
+
+def test_mx_layer_small_stages():
+    c = MX_SMALL
+    say("mx layer small")
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_MXFP4, True)
+    run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
+    torch.cuda.synchronize()
+    _mx_stage_check(c, inp, bufs, d)
+    ref = O.moe_layer(inp["x"], c.k, oracle_weights(c, inp["routed"]), "mxfp4",
+                      logits_in=inp["logits_in"], shared=inp["shared"])
+    assert row_err(host(bufs.y_shared), ref["y_shared"]).max() <= TOL
+    say("mx end-to-end max row err (reported, FP8 re-quantisation of h is discontinuous)",
+        float(row_err(host(bufs.out), ref["out"]).max()))
