@@ -1,0 +1,269 @@
+"""Benchmark of the routed-expert MoE FFN on one MI355X.
+
+Default workload: one Hy4-shaped MoE layer in batch-1 decode (hidden 6144, intermediate
+2048, 256 STQ1_0 routed experts, top-8, one bf16 shared expert).  A step is one pass of
+the whole hot path -- route, permute, expert FFN, combine -- on one token, with the inputs
+resident in HBM.  Steps rotate over several independently generated copies of the layer
+(and fresh tokens) so that no step finds its weights in the 256 MB Infinity Cache left by
+the previous one.
+
+Printed: one JSON line.  `value` = expert-weight GB/s = (bytes of the 8 routed experts the
+token touches + the shared expert) / step time.  Also reported: whole-layer algorithmic
+GB/s, per-stage times from HIP events, the roofline of the dominant kernel, the CPU oracle
+timed on a bounded sample, and a prefill line (4096 tokens, MXFP4 x FP8) in TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+STQ_MAT_BYTES = 2048 * 6144 // 256 * 42          # one Hy4 STQ1_0 expert matrix
+MX_MAT_BYTES = 2048 * 6144 // 2 + 2048 * 6144 // 32
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=6, help="layer copies the decode steps rotate over")
+    p.add_argument("--prefill-steps", type=int, default=5)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def make_decode_copy(c, copy):
+    """Device tensors of one layer copy (its own seed)."""
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    from bit_quantized_moe_softmax_amd.layer import bf16_experts
+    seed = c.seed * 1000 + copy
+    routed = [synth.stq1_family(seed, 0, m, c.E, c.I * c.H) for m in range(3)]
+    routed_t = [(dev(cd), dev(sc)) for cd, sc in routed]
+    del routed
+    sh = [dev(w) for w in synth.shared_weights(seed, 0, c.I, c.H)]
+    return dict(routed=M.Experts(M.MOE_W_STQ1_0, *routed_t), shared=bf16_experts(*sh),
+                wr=dev(synth.router_weights(seed, 0, c.E, c.H)),
+                x=dev(synth.activations(seed, 0, 64, c.H)))
+
+
+def decode_bench(args):
+    import numpy as np
+    import torch
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    from bit_quantized_moe_softmax_amd.layer import LayerBuffers
+
+    c = synth.cfg(1)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    copies = []
+    for i in range(args.copies):
+        t0 = time.perf_counter()
+        copies.append(make_decode_copy(c, i))
+        log(f"layer copy {i} ready in {time.perf_counter() - t0:.1f} s")
+    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, True)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def step(i, ev=None):
+        L = copies[i % len(copies)]
+        x = L["x"][(i // len(copies)) % 64].reshape(1, -1)
+        if ev is not None:
+            ev[0].record(stream)
+        M.moe_route(d, x, L["wr"], None, None, bufs.logits, bufs.topk_ids, bufs.topk_w, s)
+        M.moe_permute(d, bufs.topk_ids, bufs.sorted_pair, bufs.offsets, bufs.pair_pos, s)
+        if ev is not None:
+            ev[1].record(stream)
+        M.moe_expert_ffn(d, L["routed"], L["shared"], x, bufs.sorted_pair, bufs.offsets,
+                         bufs.y_pairs, bufs.y_shared, bufs.ws, s)
+        if ev is not None:
+            ev[2].record(stream)
+        M.moe_combine(d, bufs.y_pairs, bufs.topk_w, bufs.pair_pos, bufs.y_shared, None, bufs.out,
+                      None, s)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, events per stage
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    route_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    ffn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    ms = total_ms / args.steps
+    routed_b = c.k * 3 * STQ_MAT_BYTES
+    shared_b = 3 * c.I * c.H * 2
+    router_b = c.E * c.H * 2
+    act_b = c.H * 2 + c.H * 4
+    expert_b = routed_b + shared_b
+    layer_b = expert_b + router_b + act_b
+    ffn_avg = float(ffn_ms.mean())
+    return dict(c=c, ms=ms, t_wall=t_wall, expert_b=expert_b, layer_b=layer_b, routed_b=routed_b,
+                shared_b=shared_b, router_b=router_b, route_ms=float(route_ms.mean()),
+                ffn_ms=ffn_avg, comb_ms=float(comb_ms.mean()),
+                ffn_ms_p10=float(np.percentile(ffn_ms, 10)), ffn_ms_p90=float(np.percentile(ffn_ms, 90)))
+
+
+def prefill_bench(args):
+    import torch
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    from bit_quantized_moe_softmax_amd.layer import LayerBuffers
+
+    c = synth.cfg(3)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    t0 = time.perf_counter()
+    sh = [(c.I, c.H), (c.I, c.H), (c.H, c.I)]
+    routed = []
+    for m in range(3):
+        cd, sc = synth.mxfp4_family(c.seed, 0, m, c.E, *sh[m])
+        routed.append((dev(cd), dev(sc)))
+        del cd, sc
+    R = M.Experts(M.MOE_W_MXFP4, *routed)
+    x = dev(synth.activations(c.seed, 0, c.T, c.H))
+    logits = dev(synth.prefill_logits(c.seed, 0, c.T, c.E))
+    log(f"prefill inputs ready in {time.perf_counter() - t0:.1f} s")
+    bufs = LayerBuffers(d, M.MOE_W_MXFP4, True)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    M.moe_route(d, None, None, None, logits, bufs.logits, bufs.topk_ids, bufs.topk_w, s)
+    M.moe_permute(d, bufs.topk_ids, bufs.sorted_pair, bufs.offsets, bufs.pair_pos, s)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    routed_ms = []
+    for i in range(1 + args.prefill_steps):
+        ev[0].record(stream)
+        M.moe_expert_ffn(d, R, None, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs, None, bufs.ws, s)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i:
+            routed_ms.append(ev[0].elapsed_time(ev[1]))
+    flops = 2.0 * c.T * c.k * 3 * c.I * c.H
+    r_ms = sum(routed_ms) / len(routed_ms)
+    return dict(c=c, routed_ms=r_ms, flops=flops, tflops=flops / (r_ms * 1e-3) / 1e12)
+
+
+def cpu_baseline(args):
+    """The oracle as it stands, one thread, on one batch-1 layer call (bounded sample)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import synth
+    from oracle import moe_oracle as O
+    c = synth.cfg(1)
+    x = synth.activations(c.seed, 0, 1, c.H)
+    wr = synth.router_weights(c.seed, 0, c.E, c.H)
+    sh = synth.shared_weights(c.seed, 0, c.I, c.H)
+    shapes = [(c.I, c.H), (c.I, c.H), (c.H, c.I)]
+
+    def get_w(e, m):
+        n = shapes[m][0] * shapes[m][1]
+        codes, scales = synth.stq1_matrix(c.seed, 0, e, m, n)
+        return O.stq1_matrix(codes, scales, *shapes[m])
+
+    import contextlib
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        t0 = time.perf_counter()
+        O.moe_layer(x, c.k, get_w, "stq1", wr_bits=wr, shared=sh)
+        dt = time.perf_counter() - t0
+    expert_b = c.k * 3 * STQ_MAT_BYTES + 3 * c.I * c.H * 2
+    return dict(value=expert_b / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample="one batch-1 Hy4 STQ1_0 layer call (route, 8 routed experts decoded and "
+                       "applied in float64, shared expert, combine), single thread, "
+                       f"{dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU expert-parallel path is a design, not code)"}))
+        sys.exit(2)
+    import torch
+    import bit_quantized_moe_softmax_amd as M
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    M.lib()
+    dec = decode_bench(args)
+    c = dec["c"]
+    value = dec["expert_b"] / (dec["ms"] * 1e-3) / 1e9
+    ffn_b = dec["expert_b"]
+    ffn_gbs = ffn_b / (dec["ffn_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": "MoE FFN expert-weight GB/s (decode) + TFLOP/s (prefill), % of roofline",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hy4-stq1_0-decode-t1", "tokens": c.T, "hidden": c.H,
+                   "intermediate": c.I, "experts": c.E, "top_k": c.k, "shared_expert": "bf16",
+                   "routed_format": "STQ1_0", "layer_copies": args.copies},
+        "whole_layer_gbs": round(dec["layer_b"] / (dec["ms"] * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "stage_us": {"route+permute": round(dec["route_ms"] * 1e3, 2),
+                     "expert_ffn": round(dec["ffn_ms"] * 1e3, 2),
+                     "combine": round(dec["comb_ms"] * 1e3, 2)},
+        "bytes_per_step": {"routed": dec["routed_b"], "shared": dec["shared_b"],
+                           "router": dec["router_b"], "layer_total": dec["layer_b"]},
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (routed STQ1_0 + shared bf16)",
+                     "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_prefill:
+        try:
+            pre = prefill_bench(args)
+            out["prefill"] = {"workload": "hy4-mxfp4xfp8-prefill-t4096", "routed_ms": round(pre["routed_ms"], 4),
+                              "tflops": round(pre["tflops"], 1), "peak_tflops_fp8": FP8_PEAK_TFLOPS,
+                              "frac": round(pre["tflops"] / FP8_PEAK_TFLOPS, 4),
+                              "routed_flop": pre["flops"]}
+        except Exception as e:  # the decode line must still print
+            out["prefill"] = {"error": repr(e)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

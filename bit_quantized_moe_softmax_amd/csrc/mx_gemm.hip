@@ -12,9 +12,17 @@
 // and 128 weight rows: for gate/up 64 gate + 64 up rows of the same 64 h-columns, for down
 // 128 output columns.  Each K step (128) stages the A rows (E4M3, 16 KB) and the weight rows
 // (E2M1, 8 KB) plus their scale bytes in LDS (double-buffered, rows padded against bank
-// conflicts); each wave then issues 4 x 4 MFMAs from LDS.  A lane's 32 A values and 32 B
-// values are one MX group (32 consecutive K of one row), so the lane's scale byte is that
-// group's UE8M0 byte.  16-row MFMA tiles past the expert's last pair are skipped.
+// conflicts); each wave then issues 4 x 4 MFMAs from LDS.  16-row MFMA tiles past the
+// expert's last pair are skipped.
+//
+// Operand layout of the scaled 16x16x128 MFMA (measured with an in-bounds probe on gfx950,
+// K counted within the 128-wide step): lane l serves row/column l % 16 and lane group
+// g = l / 16.  An E2M1 operand lane holds the 32 consecutive K = 32g .. 32g+31 (16 bytes,
+// element 2i in the low nibble); an E4M3 operand lane holds K = 16g .. 16g+15 in bytes
+// 0..15 and K = 64+16g .. 64+16g+15 in bytes 16..31.  The scale register of lane l is the
+// UE8M0 scale of K block g (K = 32g .. 32g+31) of its row/column, whatever data the lane
+// holds.  The MFMA's internal dot products carry about 2^-14 relative error (probe), far
+// inside the 2e-3 output tolerance.
 #include "moe_device.h"
 
 #include <math.h>
@@ -154,8 +162,8 @@ __global__ __launch_bounds__(256) void mx_ffn_kernel(MxArgs p) {
     for (int mt = 0; mt < 4; ++mt) {
       if (mt < mtiles) {
         const int arow = 64 * wm + 16 * mt + c16;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(&cur.a[arow * kAStride + 32 * g]);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(&cur.a[arow * kAStride + 32 * g + 16]);
+        const uint4 v0 = *reinterpret_cast<const uint4*>(&cur.a[arow * kAStride + 16 * g]);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(&cur.a[arow * kAStride + 64 + 16 * g]);
         const i32x8_t aop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                              (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
         const int asc = (cur.as[arow] >> (8 * g)) & 0xFF;

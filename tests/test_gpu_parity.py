@@ -343,7 +343,10 @@ def _mx_stage_check(c, inp, bufs, d, toks_check=None):
         y_ref = O.mx_dequantize_e4m3(hq[lo:hi], hs[lo:hi]) @ get_w(e, 2).T
         worst = max(worst, float(row_err(yp[lo:hi], y_ref).max()))
     say("mx h code flips", n_flip, "of", n_tot, "down-stage max row err", worst)
-    assert n_flip <= max(2, 1e-4 * n_tot)
+    # A code flips when the GPU's fp32 h and the oracle's float64 h fall on either side of an
+    # E4M3 rounding boundary.  The scaled MFMA's dot products carry ~2^-14 relative error, so
+    # with boundaries 2^-3 apart (relative) about 2 * 1e-4 / 2^-3 = 1.6e-3 of the codes may flip.
+    assert n_flip <= max(2, 2e-3 * n_tot)
     assert worst <= TOL
 
 
