@@ -74,7 +74,6 @@ def decode_bench(args):
     import torch
     import synth
     import bit_quantized_moe_softmax_amd as M
-    from bit_quantized_moe_softmax_amd.layer import LayerBuffers
 
     c = synth.cfg(1)
     d = M.Dims(c.T, c.H, c.I, c.E, c.k)
@@ -83,59 +82,81 @@ def decode_bench(args):
         t0 = time.perf_counter()
         copies.append(make_decode_copy(c, i))
         log(f"layer copy {i} ready in {time.perf_counter() - t0:.1f} s")
-    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, True)
+    f32, i32 = torch.float32, torch.int32
+    logits = torch.empty((c.T, c.E), dtype=f32, device="cuda")
+    ids = torch.empty((c.T, c.k), dtype=i32, device="cuda")
+    w = torch.empty((c.T, c.k), dtype=f32, device="cuda")
+    sp = torch.empty(d.P, dtype=i32, device="cuda")
+    off = torch.empty(c.E + 1, dtype=i32, device="cuda")
+    pp = torch.empty(d.P, dtype=i32, device="cuda")
+    yp = torch.empty((d.P, c.H), dtype=f32, device="cuda")
+    ysh = torch.empty((c.T, c.H), dtype=f32, device="cuda")
+    out = torch.empty((c.T, c.H), dtype=f32, device="cuda")
+    ws = torch.zeros(M.moe_layer_decode_workspace_size(d, True), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
 
-    def step(i, ev=None):
+    def step(i):
         L = copies[i % len(copies)]
         x = L["x"][(i // len(copies)) % 64].reshape(1, -1)
-        if ev is not None:
-            ev[0].record(stream)
-        M.moe_route(d, x, L["wr"], None, None, bufs.logits, bufs.topk_ids, bufs.topk_w, s)
-        M.moe_permute(d, bufs.topk_ids, bufs.sorted_pair, bufs.offsets, bufs.pair_pos, s)
-        if ev is not None:
-            ev[1].record(stream)
-        M.moe_expert_ffn(d, L["routed"], L["shared"], x, bufs.sorted_pair, bufs.offsets,
-                         bufs.y_pairs, bufs.y_shared, bufs.ws, s)
-        if ev is not None:
-            ev[2].record(stream)
-        M.moe_combine(d, bufs.y_pairs, bufs.topk_w, bufs.pair_pos, bufs.y_shared, None, bufs.out,
-                      None, s)
-        if ev is not None:
-            ev[3].record(stream)
+        M.moe_layer_decode(d, L["routed"], L["shared"], x, L["wr"], None, logits, ids, w, sp, off,
+                           pp, yp, ysh, None, out, None, ws, s)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: exactly `steps` steps, events per stage
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
-    route_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    ffn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    ms = total_ms / args.steps
-    routed_b = c.k * 3 * STQ_MAT_BYTES
-    shared_b = 3 * c.I * c.H * 2
+    ms = start.elapsed_time(end) / args.steps
+    # second pass with the library's per-kernel HIP events (same steps, same stream)
+    M.moe_profile_enable(True)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    prof = M.moe_profile_read()
+    M.moe_profile_enable(False)
+    # the four separate entry points on the same workload, for reference
+    from bit_quantized_moe_softmax_amd.layer import LayerBuffers
+    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    n4 = min(args.steps, 50)
+    ev0.record(stream)
+    for i in range(n4):
+        L = copies[i % len(copies)]
+        x = L["x"][(i // len(copies)) % 64].reshape(1, -1)
+        M.moe_route(d, x, L["wr"], None, None, bufs.logits, bufs.topk_ids, bufs.topk_w, s)
+        M.moe_permute(d, bufs.topk_ids, bufs.sorted_pair, bufs.offsets, bufs.pair_pos, s)
+        M.moe_expert_ffn(d, L["routed"], L["shared"], x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs,
+                         bufs.y_shared, bufs.ws, s)
+        M.moe_combine(d, bufs.y_pairs, bufs.topk_w, bufs.pair_pos, bufs.y_shared, None, bufs.out, None, s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms4 = ev0.elapsed_time(ev1) / n4
+    routed_gu_b = c.k * 2 * STQ_MAT_BYTES
+    routed_dn_b = c.k * STQ_MAT_BYTES
+    shared_gu_b = 2 * c.I * c.H * 2
+    shared_dn_b = c.I * c.H * 2
     router_b = c.E * c.H * 2
-    act_b = c.H * 2 + c.H * 4
-    expert_b = routed_b + shared_b
-    layer_b = expert_b + router_b + act_b
-    ffn_avg = float(ffn_ms.mean())
-    return dict(c=c, ms=ms, t_wall=t_wall, expert_b=expert_b, layer_b=layer_b, routed_b=routed_b,
-                shared_b=shared_b, router_b=router_b, route_ms=float(route_ms.mean()),
-                ffn_ms=ffn_avg, comb_ms=float(comb_ms.mean()),
-                ffn_ms_p10=float(np.percentile(ffn_ms, 10)), ffn_ms_p90=float(np.percentile(ffn_ms, 90)))
+    x_b = c.H * 2
+    # algorithmic bytes per launch of each kernel: weights + activations read + results written
+    kb = {
+        "decode_k1_route_shared_gateup": router_b + shared_gu_b + x_b + c.E * 4 + c.I * 4,
+        "decode_k2_gateup_shared_down": routed_gu_b + shared_dn_b + x_b + c.k * c.I * 4 + c.I * 4 + c.H * 4,
+        "decode_k3_down_combine": routed_dn_b + c.k * c.I * 4 + c.k * c.H * 4 + c.H * 4 + c.H * 4,
+    }
+    expert_b = routed_gu_b + routed_dn_b + shared_gu_b + shared_dn_b
+    layer_b = expert_b + router_b + x_b + c.H * 4
+    return dict(c=c, ms=ms, ms4=ms4, t_wall=t_wall, expert_b=expert_b, layer_b=layer_b, prof=prof,
+                kbytes=kb, routed_b=routed_gu_b + routed_dn_b, shared_b=shared_gu_b + shared_dn_b,
+                router_b=router_b)
 
 
 def prefill_bench(args):
@@ -163,17 +184,22 @@ def prefill_bench(args):
     M.moe_route(d, None, None, None, logits, bufs.logits, bufs.topk_ids, bufs.topk_w, s)
     M.moe_permute(d, bufs.topk_ids, bufs.sorted_pair, bufs.offsets, bufs.pair_pos, s)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    routed_ms = []
-    for i in range(1 + args.prefill_steps):
-        ev[0].record(stream)
+    M.moe_expert_ffn(d, R, None, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs, None, bufs.ws, s)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.prefill_steps):
         M.moe_expert_ffn(d, R, None, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs, None, bufs.ws, s)
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        if i:
-            routed_ms.append(ev[0].elapsed_time(ev[1]))
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    r_ms = ev[0].elapsed_time(ev[1]) / args.prefill_steps
+    M.moe_profile_enable(True)
+    for i in range(args.prefill_steps):
+        M.moe_expert_ffn(d, R, None, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs, None, bufs.ws, s)
+    torch.cuda.synchronize()
+    prof = M.moe_profile_read()
+    M.moe_profile_enable(False)
     flops = 2.0 * c.T * c.k * 3 * c.I * c.H
-    r_ms = sum(routed_ms) / len(routed_ms)
-    return dict(c=c, routed_ms=r_ms, flops=flops, tflops=flops / (r_ms * 1e-3) / 1e12)
+    return dict(c=c, routed_ms=r_ms, flops=flops, tflops=flops / (r_ms * 1e-3) / 1e12, prof=prof)
 
 
 def cpu_baseline(args):
@@ -222,8 +248,13 @@ def main():
     dec = decode_bench(args)
     c = dec["c"]
     value = dec["expert_b"] / (dec["ms"] * 1e-3) / 1e9
-    ffn_b = dec["expert_b"]
-    ffn_gbs = ffn_b / (dec["ffn_ms"] * 1e-3) / 1e9
+    kern = {}
+    for name, nbytes in dec["kbytes"].items():
+        us, n = dec["prof"][name]
+        kern[name] = {"avg_us": round(us, 3), "launches": n, "algorithmic_bytes": nbytes,
+                      "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None}
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    dk = kern[dom]
     out = {
         "metric": "MoE FFN expert-weight GB/s (decode) + TFLOP/s (prefill), % of roofline",
         "value": round(value, 1),
@@ -239,25 +270,36 @@ def main():
         "data": "synthetic",
         "config": {"workload": "hy4-stq1_0-decode-t1", "tokens": c.T, "hidden": c.H,
                    "intermediate": c.I, "experts": c.E, "top_k": c.k, "shared_expert": "bf16",
-                   "routed_format": "STQ1_0", "layer_copies": args.copies},
+                   "routed_format": "STQ1_0", "layer_copies": args.copies,
+                   "entry_point": "moe_layer_decode"},
         "whole_layer_gbs": round(dec["layer_b"] / (dec["ms"] * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "stage_us": {"route+permute": round(dec["route_ms"] * 1e3, 2),
-                     "expert_ffn": round(dec["ffn_ms"] * 1e3, 2),
-                     "combine": round(dec["comb_ms"] * 1e3, 2)},
+        "four_call_ms_per_step": round(dec["ms4"], 5),
+        "kernels": kern,
         "bytes_per_step": {"routed": dec["routed_b"], "shared": dec["shared_b"],
                            "router": dec["router_b"], "layer_total": dec["layer_b"]},
-        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (routed STQ1_0 + shared bf16)",
-                     "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dk["gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
     }
     if not args.no_prefill:
         try:
             pre = prefill_bench(args)
+            pc = pre["c"]
+            gu_flop = 2.0 * pc.T * pc.k * 2 * pc.I * pc.H
+            dn_flop = 2.0 * pc.T * pc.k * pc.I * pc.H
+            pk = {}
+            for name, fl in (("mx_gateup", gu_flop), ("mx_down", dn_flop), ("mx_quant", None)):
+                us, n = pre["prof"][name]
+                pk[name] = {"avg_us": round(us, 2), "launches": n,
+                            "tflops": round(fl / (us * 1e-6) / 1e12, 1) if (fl and us > 0) else None}
             out["prefill"] = {"workload": "hy4-mxfp4xfp8-prefill-t4096", "routed_ms": round(pre["routed_ms"], 4),
                               "tflops": round(pre["tflops"], 1), "peak_tflops_fp8": FP8_PEAK_TFLOPS,
                               "frac": round(pre["tflops"] / FP8_PEAK_TFLOPS, 4),
-                              "routed_flop": pre["flops"]}
+                              "routed_flop": pre["flops"], "kernels": pk,
+                              "roofline": {"bound": "mfma", "kernel": "mx_gateup",
+                                           "achieved": pk["mx_gateup"]["tflops"], "peak": FP8_PEAK_TFLOPS,
+                                           "unit": "TFLOP/s",
+                                           "frac": round((pk["mx_gateup"]["tflops"] or 0) / FP8_PEAK_TFLOPS, 4)}}
         except Exception as e:  # the decode line must still print
             out["prefill"] = {"error": repr(e)}
     if not args.no_cpu_baseline:

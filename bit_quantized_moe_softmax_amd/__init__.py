@@ -16,13 +16,17 @@ __all__ = [
     "COUNTER_NAMES", "moe_status_str", "moe_version", "moe_get_counters", "moe_reset_counters",
     "moe_route", "moe_permute", "moe_workspace_size", "moe_workspace_offsets", "moe_expert_ffn",
     "moe_combine", "moe_stq1_pack", "moe_stq1_dequant", "moe_mxfp4_dequant", "moe_mx_quant_act",
-    "moe_rmsnorm_bf16",
+    "moe_rmsnorm_bf16", "moe_layer_decode_workspace_size", "moe_layer_decode",
+    "moe_profile_enable", "moe_profile_read", "PROFILE_SLOTS",
 ]
+
+PROFILE_SLOTS = ["decode_k1_route_shared_gateup", "decode_k2_gateup_shared_down",
+                 "decode_k3_down_combine", "mx_quant", "mx_gateup", "mx_down"]
 
 MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16 = 1, 2, 3
 COUNTER_NAMES = ["route_gemv", "route_topk", "permute", "stq_gateup_mfma", "stq_down_mfma",
                  "stq_generic", "mx_quant", "mx_gateup_mfma", "mx_down_mfma", "bf16_gateup",
-                 "bf16_down", "combine", "rmsnorm", "dequant", "bf16_gemm", "reserved"]
+                 "bf16_down", "combine", "rmsnorm", "dequant", "bf16_gemm", "decode_fused"]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
@@ -62,6 +66,10 @@ _SIGS = {
     "moe_mxfp4_dequant": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
     "moe_mx_quant_act": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P]),
     "moe_rmsnorm_bf16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
+    "moe_layer_decode_workspace_size": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "moe_layer_decode": (ctypes.c_int, [_P, _P, _P] + [_P] * 15 + [ctypes.c_size_t, _P]),
+    "moe_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
+    "moe_profile_read": (ctypes.c_int, [_P, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -211,3 +219,32 @@ def moe_mx_quant_act(rows, K, x_bf16, x_f32, q, s, stream=None):
 
 def moe_rmsnorm_bf16(T, H, eps, r, a, stream=None):
     _check(lib().moe_rmsnorm_bf16(int(T), int(H), float(eps), _ptr(r), _ptr(a), _stream(stream)))
+
+
+def moe_layer_decode_workspace_size(d: Dims, has_shared: bool) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_layer_decode_workspace_size(d.ref(), int(bool(has_shared)), ctypes.byref(out)))
+    return out.value
+
+
+def moe_layer_decode(d: Dims, routed: Experts, shared, x_bf16, wr_bf16, logit_bias, logits_out,
+                     topk_ids, topk_w, sorted_pair, expert_offsets, pair_pos, y_pairs, y_shared,
+                     residual, out_f32, out_bf16, ws, stream=None):
+    _check(lib().moe_layer_decode(
+        d.ref(), routed.ref(), shared.ref() if shared is not None else None, _ptr(x_bf16),
+        _ptr(wr_bf16), _ptr(logit_bias), _ptr(logits_out), _ptr(topk_ids), _ptr(topk_w),
+        _ptr(sorted_pair), _ptr(expert_offsets), _ptr(pair_pos), _ptr(y_pairs), _ptr(y_shared),
+        _ptr(residual), _ptr(out_f32), _ptr(out_bf16), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_profile_enable(on: bool) -> None:
+    _check(lib().moe_profile_enable(int(bool(on))))
+
+
+def moe_profile_read() -> dict:
+    """{slot name: (average microseconds, launches)} of the events recorded since the last read."""
+    avg = (ctypes.c_double * 16)()
+    cnt = (ctypes.c_int64 * 16)()
+    _check(lib().moe_profile_read(ctypes.cast(avg, _P), ctypes.cast(cnt, _P)))
+    return {n: (float(avg[i]), int(cnt[i])) for i, n in enumerate(PROFILE_SLOTS)}

@@ -14,7 +14,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "misc.hip", "ffn_decode.hip", "mx_gemm.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "misc.hip", "ffn_decode.hip", "mx_gemm.hip",
+           "decode_fused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -3,6 +3,8 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "moe_device.h"
 
@@ -66,9 +68,71 @@ void layout(const moe_dims* d, int fmt, int has_shared, size_t* offs) {
 
 bool mat_ok(const moe_mat& m, bool need_scales) { return m.codes && (!need_scales || m.scales); }
 
+// ---- opt-in event profiler: per slot a pool of (begin, end) event pairs
+constexpr int kProfPool = 8192;
+struct ProfSlot {
+  std::vector<hipEvent_t> ev;   // 2 * kProfPool
+  int used = 0;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+ProfSlot g_prof[MOE_PROF_SLOTS_INTERNAL];
+
 }  // namespace
 
+bool moe_prof_on() { return g_prof_on.load(std::memory_order_relaxed); }
+
+void moe_prof_begin(int slot, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfSlot& p = g_prof[slot];
+  if (p.ev.empty() || p.used >= kProfPool) return;
+  hipEventRecord(p.ev[2 * p.used], s);
+}
+
+void moe_prof_end(int slot, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfSlot& p = g_prof[slot];
+  if (p.ev.empty() || p.used >= kProfPool) return;
+  hipEventRecord(p.ev[2 * p.used + 1], s);
+  ++p.used;
+}
+
 extern "C" {
+
+moe_status moe_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on) {
+    for (auto& p : g_prof) {
+      if (p.ev.empty()) {
+        p.ev.resize(2 * kProfPool);
+        for (auto& e : p.ev)
+          if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_HIP;
+      }
+      p.used = 0;
+    }
+  }
+  g_prof_on.store(on != 0);
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(double* avg_us, int64_t* count) {
+  if (!avg_us || !count) return MOE_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (int i = 0; i < MOE_PROF_SLOTS_INTERNAL; ++i) {
+    ProfSlot& p = g_prof[i];
+    double tot = 0.0;
+    for (int j = 0; j < p.used; ++j) {
+      if (hipEventSynchronize(p.ev[2 * j + 1]) != hipSuccess) return MOE_ERR_HIP;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, p.ev[2 * j], p.ev[2 * j + 1]) != hipSuccess) return MOE_ERR_HIP;
+      tot += ms;
+    }
+    count[i] = p.used;
+    avg_us[i] = p.used ? tot * 1e3 / p.used : 0.0;
+    p.used = 0;
+  }
+  return MOE_OK;
+}
 
 const char* moe_status_str(moe_status s) {
   switch (s) {
@@ -202,7 +266,10 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     uint8_t* xs = wsb + offs[3];
     uint8_t* hq = wsb + offs[4];
     uint8_t* hs = wsb + offs[5];
+    const bool prof = moe_prof_on();
+    if (prof) moe_prof_begin(MOE_PROF_MX_QUANT, s);
     hipError_t e = moe_launch_mx_quant(T, H, x_bf16, nullptr, xq, xs, s);
+    if (prof) moe_prof_end(MOE_PROF_MX_QUANT, s);
     bump(MOE_CNT_MX_QUANT);
     if (e != hipSuccess) return MOE_ERR_HIP;
     MxArgs a{};
@@ -212,7 +279,9 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     a.wscales1 = static_cast<const uint8_t*>(routed->up.scales);
     a.aq = xq; a.as = xs; a.sorted_pair = sorted_pair; a.offsets = expert_offsets;
     a.hq = hq; a.hs = hs; a.N = I; a.K = H; a.T = T; a.E = E; a.k = k; a.P = P;
+    if (prof) moe_prof_begin(MOE_PROF_MX_GATEUP, s);
     e = moe_launch_mx_gateup(a, s);
+    if (prof) moe_prof_end(MOE_PROF_MX_GATEUP, s);
     bump(MOE_CNT_MX_GATEUP_MFMA);
     if (e != hipSuccess) return MOE_ERR_HIP;
     MxArgs b{};
@@ -220,7 +289,9 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     b.wscales0 = static_cast<const uint8_t*>(routed->down.scales);
     b.aq = hq; b.as = hs; b.sorted_pair = sorted_pair; b.offsets = expert_offsets;
     b.y = y_pairs; b.N = H; b.K = I; b.T = T; b.E = E; b.k = k; b.P = P;
+    if (prof) moe_prof_begin(MOE_PROF_MX_DOWN, s);
     e = moe_launch_mx_down(b, s);
+    if (prof) moe_prof_end(MOE_PROF_MX_DOWN, s);
     bump(MOE_CNT_MX_DOWN_MFMA);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -241,6 +312,50 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return finish(hipSuccess, s);
+}
+
+static bool decode_fused_ok(const moe_dims* d) {
+  return d->T <= 64 && d->H % 512 == 0 && d->H <= 16384 && d->I % 256 == 0 && d->I <= 2048;
+}
+
+moe_status moe_layer_decode_workspace_size(const moe_dims* d, int32_t has_shared, size_t* bytes) {
+  if (!dims_ok(d) || !bytes) return MOE_ERR_INVALID_ARG;
+  if (!decode_fused_ok(d)) return MOE_ERR_UNSUPPORTED;
+  size_t offs[8];
+  *bytes = moe_decode_ws_layout(d->T, d->H, d->I, d->E, d->k, has_shared != 0, offs);
+  return MOE_OK;
+}
+
+moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
+                            const moe_experts* shared, const uint16_t* x_bf16,
+                            const uint16_t* wr_bf16, const float* logit_bias, float* logits_out,
+                            int32_t* topk_ids, float* topk_w, int32_t* sorted_pair,
+                            int32_t* expert_offsets, int32_t* pair_pos, float* y_pairs,
+                            float* y_shared, const float* residual, float* out_f32,
+                            uint16_t* out_bf16, void* ws, size_t ws_bytes, void* stream) {
+  if (!dims_ok(d) || !routed || !x_bf16 || !wr_bf16 || !logits_out || !topk_ids || !topk_w ||
+      !sorted_pair || !expert_offsets || !pair_pos || !y_pairs || !out_f32)
+    return MOE_ERR_INVALID_ARG;
+  if (routed->fmt != MOE_W_STQ1_0) return MOE_ERR_UNSUPPORTED;
+  if (!mat_ok(routed->gate, true) || !mat_ok(routed->up, true) || !mat_ok(routed->down, true))
+    return MOE_ERR_INVALID_ARG;
+  if (shared) {
+    if (shared->fmt != MOE_W_BF16 || !y_shared) return MOE_ERR_INVALID_ARG;
+    if (!mat_ok(shared->gate, false) || !mat_ok(shared->up, false) || !mat_ok(shared->down, false))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (!decode_fused_ok(d)) return MOE_ERR_UNSUPPORTED;
+  size_t offs[8];
+  const size_t need = moe_decode_ws_layout(d->T, d->H, d->I, d->E, d->k, shared != nullptr, offs);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = moe_launch_decode_fused(d, routed, shared, x_bf16, wr_bf16, logit_bias,
+                                         logits_out, topk_ids, topk_w, sorted_pair,
+                                         expert_offsets, pair_pos, y_pairs, y_shared, residual,
+                                         out_f32, out_bf16, ws, s);
+  bump(MOE_CNT_DECODE_FUSED);
+  return finish(e, s);
 }
 
 moe_status moe_combine(const moe_dims* d, const float* y_pairs, const float* topk_w,

@@ -101,6 +101,7 @@ enum {
   MOE_CNT_RMSNORM = 12,
   MOE_CNT_DEQUANT = 13,
   MOE_CNT_BF16_GEMM = 14,      /* shared expert, large-T tiled GEMM path    */
+  MOE_CNT_DECODE_FUSED = 15,   /* moe_layer_decode (three fused kernels)    */
   MOE_CNT_SLOTS = 16
 };
 
@@ -111,6 +112,16 @@ MOE_MI355X_API const char* moe_version(void);
  * was launched since load or the last reset (host-side counts, no device work). */
 MOE_MI355X_API moe_status moe_get_counters(uint64_t* out);
 MOE_MI355X_API moe_status moe_reset_counters(void);
+
+/* Opt-in kernel timing: while enabled the library records a HIP event pair on the launch
+ * stream around each of its main kernels (slots: 0/1/2 the three kernels of
+ * moe_layer_decode, 3/4/5 MX quantisation, MXFP4 gate/up and down GEMMs).  Enabling
+ * creates the event pools once (host objects, no device memory).  moe_profile_read waits
+ * for the recorded events, writes the average duration in microseconds and the number of
+ * launches per slot (16 slots) and clears the records.  Timing adds two event records per
+ * kernel; leave it off outside measurement. */
+MOE_MI355X_API moe_status moe_profile_enable(int32_t on);
+MOE_MI355X_API moe_status moe_profile_read(double* avg_us, int64_t* count);
 
 /* ---------------------------------------------------------------------------
  * Route.  Router logits l[t][e] = sum_h x[t][h] * Wr[e][h] (+ logit_bias[e]) in
@@ -201,6 +212,32 @@ MOE_MI355X_API moe_status moe_combine(const moe_dims* d, const float* y_pairs,
                                       const float* topk_w, const int32_t* pair_pos,
                                       const float* y_shared, const float* residual,
                                       float* out_f32, uint16_t* out_bf16, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused decode layer: the same computation as moe_route + moe_permute + moe_expert_ffn
+ * + moe_combine for STQ1_0 routed experts and an optional bf16 shared expert, in three
+ * kernels (the fused top-8 MoE operator idea of "Hy4-preview Flash-MoE STQ1_0",
+ * Important runtime choices: --slot8).  Every intermediate the four calls expose is
+ * written to the same caller buffers (logits_out, topk_ids, topk_w, sorted_pair,
+ * expert_offsets, pair_pos, y_pairs, y_shared), then out_f32 (and out_bf16 when
+ * non-NULL) = combine (+ residual; residual may equal out_f32).  The router runs from
+ * x (no logits_in).  Numerics: router logits are summed in a different order than
+ * moe_route's, so they may differ from it in the last bits; everything else follows the
+ * four-call definitions.
+ * Limits: T <= 64, H % 512 == 0, H <= 16384, I % 256 == 0, I <= 2048, k <= 32, E <= 1024.
+ * Workspace: at least moe_layer_decode_workspace_size bytes; it holds atomic counters
+ * that MUST be zero before the first call on a given workspace (e.g. clear it once after
+ * allocating it); every call leaves them zero.  Calls sharing one workspace must not
+ * overlap in time.  Returns MOE_ERR_UNSUPPORTED outside the limits.
+ * ------------------------------------------------------------------------- */
+MOE_MI355X_API moe_status moe_layer_decode_workspace_size(const moe_dims* d, int32_t has_shared,
+                                                          size_t* bytes);
+MOE_MI355X_API moe_status moe_layer_decode(
+    const moe_dims* d, const moe_experts* routed, const moe_experts* shared,
+    const uint16_t* x_bf16, const uint16_t* wr_bf16, const float* logit_bias, float* logits_out,
+    int32_t* topk_ids, float* topk_w, int32_t* sorted_pair, int32_t* expert_offsets,
+    int32_t* pair_pos, float* y_pairs, float* y_shared, const float* residual, float* out_f32,
+    uint16_t* out_bf16, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Helpers (same conventions).

@@ -366,3 +366,110 @@ def test_mx_layer_small_stages():
     assert row_err(host(bufs.y_shared), ref["y_shared"]).max() <= TOL
     say("mx end-to-end max row err (reported, FP8 re-quantisation of h is discontinuous)",
         float(row_err(host(bufs.out), ref["out"]).max()))
+
+
+# ----------------------------------------------------------------------------- fused decode layer
+FUSED = {
+    "h512-i256-e8-top2-t37-shared": synth.LayerCfg("t", 37, 512, 256, 8, 2, True, "stq1", False, False, 1, 11),
+    "h1024-i512-e16-top4-t21-zipf": synth.LayerCfg("t", 21, 1024, 512, 16, 4, True, "stq1", True, False, 1, 14),
+    "h512-i256-e40-top8-t64-noshared": synth.LayerCfg("t", 64, 512, 256, 40, 8, False, "stq1", True, False, 1, 15),
+    "h512-i256-e8-top2-t1-shared": synth.LayerCfg("t", 1, 512, 256, 8, 2, True, "stq1", False, False, 1, 16),
+}
+
+
+def run_fused(c, inp, residual=None, with_bf16=False, ws=None):
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    f32, i32 = torch.float32, torch.int32
+    o = dict(logits=torch.empty((c.T, c.E), dtype=f32, device="cuda"),
+             ids=torch.empty((c.T, c.k), dtype=i32, device="cuda"),
+             w=torch.empty((c.T, c.k), dtype=f32, device="cuda"),
+             sp=torch.empty(d.P, dtype=i32, device="cuda"),
+             off=torch.empty(c.E + 1, dtype=i32, device="cuda"),
+             pp=torch.empty(d.P, dtype=i32, device="cuda"),
+             yp=torch.empty((d.P, c.H), dtype=f32, device="cuda"),
+             ysh=torch.empty((c.T, c.H), dtype=f32, device="cuda") if shared is not None else None,
+             out=torch.empty((c.T, c.H), dtype=f32, device="cuda"),
+             obf=torch.empty((c.T, c.H), dtype=torch.int16, device="cuda") if with_bf16 else None)
+    if ws is None:
+        ws = torch.zeros(M.moe_layer_decode_workspace_size(d, shared is not None), dtype=torch.uint8,
+                         device="cuda")
+    bias = dev(inp["bias"]) if inp["bias"] is not None else None
+    M.moe_layer_decode(d, routed, shared, dev(inp["x"]), dev(inp["wr"]), bias, o["logits"], o["ids"],
+                       o["w"], o["sp"], o["off"], o["pp"], o["yp"], o["ysh"],
+                       residual, o["out"], o["obf"], ws)
+    torch.cuda.synchronize()
+    o["ws"] = ws
+    return o
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_fused_decode_small(name):
+    c = FUSED[name]
+    say("fused decode", name)
+    inp = layer_inputs(c)
+    res = synth.activations(c.seed + 100, 0, c.T, c.H).astype(np.uint16)
+    resid = O.bf16_to_f64(res).astype(np.float32)
+    M.moe_reset_counters()
+    o = run_fused(c, inp, residual=dev(resid), with_bf16=True)
+    assert M.moe_get_counters()["decode_fused"] == 1
+    ref = O.moe_layer(inp["x"], c.k, oracle_weights(c, inp["routed"]), "stq1", wr_bits=inp["wr"],
+                      bias=inp["bias"], shared=inp["shared"], residual=resid.astype(np.float64))
+    assert np.abs(host(o["logits"]) - ref["logits"]).max() < 2e-5
+    tie = near_tie_tokens(ref["logits"], c.k)
+    gi = host(o["ids"])
+    assert (gi[~tie] == ref["ids"][~tie]).all()
+    for t in np.flatnonzero(tie):
+        assert valid_selection(ref["logits"][t], gi[t], c.k)
+    # the permutation is exact for the ids the kernel chose
+    rsp, roff, rpp = O.permute(gi, c.E)
+    assert (host(o["sp"]) == rsp).all() and (host(o["off"]) == roff).all() and (host(o["pp"]) == rpp).all()
+    ok = ~tie
+    out = host(o["out"])
+    err = row_err(out[ok], ref["out"][ok])
+    say("fused max row err", float(err.max()), "near ties", int(tie.sum()))
+    assert err.max() <= TOL
+    if not tie.any():
+        assert row_err(host(o["yp"]), ref["y_pairs"]).max() <= TOL
+        if inp["shared"] is not None:
+            assert row_err(host(o["ysh"]), ref["y_shared"]).max() <= TOL
+    assert (host(o["obf"], np.uint16) == O.f64_to_bf16_bits(out.astype(np.float64))).all()
+    # the counters were left zero: a second call on the same workspace gives the same bits
+    o2 = run_fused(c, inp, residual=dev(resid), ws=o["ws"])
+    assert (host(o2["out"]).view(np.uint32) == out.view(np.uint32)).all()
+
+
+def test_fused_decode_cfg1_hy4():
+    c = synth.cfg(1)
+    say("fused decode cfg1 generate")
+    inp = layer_inputs(c)
+    o = run_fused(c, inp)
+    say("fused decode cfg1 oracle")
+    ref = O.moe_layer(inp["x"], c.k, oracle_weights(c, inp["routed"]), "stq1", wr_bits=inp["wr"],
+                      shared=inp["shared"])
+    assert (host(o["ids"]) == ref["ids"]).all()
+    err = row_err(host(o["out"]), ref["out"])
+    say("fused cfg1 max row err", float(err.max()))
+    assert err.max() <= TOL
+    assert row_err(host(o["yp"]), ref["y_pairs"]).max() <= TOL
+
+
+def test_fused_decode_cfg2_hy4_zipf_sampled():
+    c = synth.cfg(2)
+    say("fused decode cfg2 generate")
+    inp = layer_inputs(c)
+    o = run_fused(c, inp)
+    rl, rid, _ = O.route(c.k, inp["x"], inp["wr"], inp["bias"])
+    tie = near_tie_tokens(rl, c.k)
+    gi = host(o["ids"])
+    assert (gi[~tie] == rid[~tie]).all()
+    rsp, roff, rpp = O.permute(gi, c.E)
+    assert (host(o["sp"]) == rsp).all() and (host(o["pp"]) == rpp).all()
+    sample = [t for t in synth.sample_tokens(c.seed, c.T, 6) if not tie[t]]
+    say("fused cfg2 oracle tokens", sample)
+    ref = O.moe_layer(inp["x"][sample], c.k, oracle_weights(c, inp["routed"]), "stq1", wr_bits=inp["wr"],
+                      bias=inp["bias"], shared=inp["shared"])
+    err = row_err(host(o["out"])[sample], ref["out"])
+    say("fused cfg2 sampled max row err", float(err.max()))
+    assert err.max() <= TOL
