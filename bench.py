@@ -148,7 +148,7 @@ def decode_bench(args):
     x_b = c.H * 2
     # algorithmic bytes per launch of each kernel: weights + activations read + results written
     kb = {
-        "decode_k1_route_shared_gateup": router_b + shared_gu_b + x_b + c.E * 4 + c.I * 4,
+        "decode_k1_route_shared_gateup": router_b + shared_gu_b + x_b + c.I * 4,
         "decode_k2_gateup_shared_down": routed_gu_b + shared_dn_b + x_b + c.k * c.I * 4 + c.I * 4 + c.H * 4,
         "decode_k3_down_combine": routed_dn_b + c.k * c.I * 4 + c.k * c.H * 4 + c.H * 4 + c.H * 4,
     }

@@ -21,7 +21,7 @@ __all__ = [
 ]
 
 PROFILE_SLOTS = ["decode_k1_route_shared_gateup", "decode_k2_gateup_shared_down",
-                 "decode_k3_down_combine", "mx_quant", "mx_gateup", "mx_down"]
+                 "decode_k3_down_combine", "reserved3", "mx_quant", "mx_gateup", "mx_down"]
 
 MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16 = 1, 2, 3
 COUNTER_NAMES = ["route_gemv", "route_topk", "permute", "stq_gateup_mfma", "stq_down_mfma",

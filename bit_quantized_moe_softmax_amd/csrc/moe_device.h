@@ -179,14 +179,15 @@ hipError_t moe_launch_mx_gateup(const MxArgs& a, hipStream_t s);
 // Opt-in kernel timing with HIP events recorded on the launch stream around single kernels.
 enum {
   MOE_PROF_DECODE_K1 = 0, MOE_PROF_DECODE_K2 = 1, MOE_PROF_DECODE_K3 = 2,
-  MOE_PROF_MX_QUANT = 3, MOE_PROF_MX_GATEUP = 4, MOE_PROF_MX_DOWN = 5,
-  MOE_PROF_BF16_GATEUP = 6, MOE_PROF_BF16_DOWN = 7, MOE_PROF_SLOTS_INTERNAL = 16
+  MOE_PROF_MX_QUANT = 4, MOE_PROF_MX_GATEUP = 5, MOE_PROF_MX_DOWN = 6,
+  MOE_PROF_SLOTS_INTERNAL = 16
 };
 bool moe_prof_on();
 void moe_prof_begin(int slot, hipStream_t s);
 void moe_prof_end(int slot, hipStream_t s);
 
 // Fused decode layer (three kernels).
+bool moe_decode_shape_ok(int H, int I, int E);
 size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, size_t* offs);
 hipError_t moe_launch_decode_fused(const moe_dims* d, const moe_experts* routed,
                                    const moe_experts* shared, const uint16_t* x,

@@ -114,8 +114,8 @@ MOE_MI355X_API moe_status moe_get_counters(uint64_t* out);
 MOE_MI355X_API moe_status moe_reset_counters(void);
 
 /* Opt-in kernel timing: while enabled the library records a HIP event pair on the launch
- * stream around each of its main kernels (slots: 0/1/2 the three kernels of
- * moe_layer_decode, 3/4/5 MX quantisation, MXFP4 gate/up and down GEMMs).  Enabling
+ * stream around each of its main kernels (slots: 0..2 the three kernels of
+ * moe_layer_decode, 4/5/6 MX quantisation, MXFP4 gate/up and down GEMMs).  Enabling
  * creates the event pools once (host objects, no device memory).  moe_profile_read waits
  * for the recorded events, writes the average duration in microseconds and the number of
  * launches per slot (16 slots) and clears the records.  Timing adds two event records per
@@ -224,11 +224,12 @@ MOE_MI355X_API moe_status moe_combine(const moe_dims* d, const float* y_pairs,
  * x (no logits_in).  Numerics: router logits are summed in a different order than
  * moe_route's, so they may differ from it in the last bits; everything else follows the
  * four-call definitions.
- * Limits: T <= 64, H % 512 == 0, H <= 16384, I % 256 == 0, I <= 2048, k <= 32, E <= 1024.
- * Workspace: at least moe_layer_decode_workspace_size bytes; it holds atomic counters
- * that MUST be zero before the first call on a given workspace (e.g. clear it once after
- * allocating it); every call leaves them zero.  Calls sharing one workspace must not
- * overlap in time.  Returns MOE_ERR_UNSUPPORTED outside the limits.
+ * Limits: T <= 64, k <= 32, E <= 256, and (H, I) one of the compiled shapes (512, 256),
+ * (1024, 512), (2048, 1024), (4096, 2048), (6144, 2048), (8192, 2048).
+ * Workspace: at least moe_layer_decode_workspace_size bytes.  It holds one atomic ticket
+ * counter that MUST be zero before the first call on a given workspace (clear the buffer
+ * once after allocating it); every call leaves it zero.  Calls sharing one workspace must
+ * not overlap in time.  Returns MOE_ERR_UNSUPPORTED outside the limits.
  * ------------------------------------------------------------------------- */
 MOE_MI355X_API moe_status moe_layer_decode_workspace_size(const moe_dims* d, int32_t has_shared,
                                                           size_t* bytes);
