@@ -2,34 +2,45 @@
 //
 // Same computation as the four separate entry points (router in BF16, top-k with
 // renormalised softmax weights, stable permutation, SwiGLU experts on STQ1_0 weights,
-// one bf16 shared expert, ungated combine).  Work that does not depend on routing runs
-// beside the router:
-//   K1  router logits (bf16 MFMA; a workgroup sums four K chunks of 16 experts in LDS and
-//       writes one partial) beside the shared expert's gate/up + SiLU*up.  The last router
-//       workgroup to finish (atomic ticket, one release fence per router workgroup) sums
-//       the partials in a fixed order, picks the top-k, sorts the pairs by expert and writes
-//       the unit table: (expert, first pair, pairs <= 16) with each pair's token and weight;
-//   K2  routed gate/up + SiLU*up (STQ1_0 decoded in registers, bf16 MFMA) beside the shared
-//       expert's down projection;
-//   K3  routed down projection per 16-row slice of the output, every unit of the slice in
-//       one workgroup (8 waves), weighted into per-wave LDS sums and combined with the
-//       shared expert (and the residual) in a fixed order.
+// one bf16 shared expert, ungated combine), split by what each step waits for:
+//   K1  routing only: router logits (bf16 MFMA; a workgroup sums four K chunks of 16
+//       experts in LDS and writes one partial); the last router workgroup to finish (atomic
+//       ticket, one release fence per workgroup) sums the partials in a fixed order, picks
+//       the top-k, sorts the pairs by expert and writes the work lists: units of <= 16
+//       pairs of one expert (with each pair's token and weight) and half-units of <= 8.
+//       Nothing else runs beside it, so its short chain of dependent loads never queues
+//       behind bulk weight traffic;
+//   K2  every gate/up projection: routed (STQ1_0 decoded in registers, bf16 MFMA) and the
+//       shared expert's, each followed by SiLU(gate) * up;
+//   K3  every down projection and the combine, per 16-row slice of the output: the shared
+//       expert's rows and each half-unit's rows, weighted into per-wave LDS sums, then
+//       out = shared + sum over waves in a fixed order (+ residual).
 // Every sum runs in a fixed order, so results do not depend on scheduling.  The ticket
 // counter lives in the workspace: zero before the first call, left zero by every call.
-// The kernels are instantiated per (H/256, I/256) so every loop over K has a fixed trip
-// count: a wave's loads are issued without branches and stay in flight together.  Rows a
-// lane does not need (a token column past the unit's last pair) are read from a valid row
-// and zeroed by a select rather than skipped.
 //
-// MFMA layout (v_mfma_f32_16x16x32_bf16): A row = B column = lane % 16, lane group
-// g = lane / 16 supplies K-slots 8g .. 8g+7; D(4g + i, lane % 16) sits in register i.
-// K-slot -> K map: STQ1_0 K = 256 b + 64 g + 8 t + s (a lane decodes groups 16g+2t and
-// 16g+2t+1 of block b at step t from the 8 code bytes and 16 high bits it loads);
-// router K = k0 + 32 t + 8 g + s.  The routed h is stored as bf16 hi + bf16 lo (h - hi) so
-// the down projection keeps ~16 bits of h with two MFMAs (A*hi + A*lo) into one sum.
-// For up to four tokens the shared expert (plain bf16 GEMV, 75 MB of weights at Hy4
-// shape) runs on the VALU with one wave per row and every load of the row in flight;
-// beyond that it uses the MFMA with the K axis split over the workgroup's waves.
+// Memory-level order.  A wave's vector loads retire in issue order, so waiting for one
+// load waits for every load issued before it.  The weight streams are therefore the only
+// loads inside the main loops: activations (x, h) are staged into LDS once, from loads
+// issued before the first weight load, and the loops read them with LDS instructions
+// (a separate counter).  Weight code words run a fixed number of blocks ahead.
+//
+// MFMA roles (v_mfma_f32_16x16x32_bf16): the A operand carries activations (row = token
+// slot = lane % 16), the B operand carries weights (column = weight row = lane % 16); lane
+// group g = lane / 16 supplies K-slots 8g .. 8g+7 of both, and D(slot 4g + i, row) sits in
+// register i of the lane that decoded that row, so one STQ1_0 block scale per lane and
+// block applies to all four of its results.  K-slot -> K map inside a 256-weight block b at
+// MFMA step t: K = 256 b + 64 g + 8 t + s, i.e. a lane decodes groups 16g+2t and 16g+2t+1
+// from the 8 code bytes and 16 high bits it loads.  Token slots past a unit's last pair
+// read some valid row; their D rows are never used.
+// The routed h is kept as bf16 hi + bf16 lo (h - hi); in the down projection a pair takes
+// two adjacent A rows (hi, lo) of one MFMA, so ~16 bits of h cost no extra MFMA and the
+// pair's result is the sum of two D rows.  The shared h is kept the same way and enters
+// packed bf16 dot products.
+// The kernels are instantiated per (H/256, I/256) so every loop over K has a fixed trip
+// count and a wave's loads are issued without branches.  Up to kXT tokens per unit (and
+// for the shared expert) activations come from LDS and the shared expert runs on the VALU
+// (a plain bf16 GEMV: 75 MB of weights at Hy4 shape); beyond that activations are read
+// from memory block by block and the shared expert uses the MFMA.
 #include "moe_device.h"
 
 #include <math.h>
@@ -40,10 +51,17 @@ constexpr int kWG = 256;           // 4 waves
 constexpr int kNW = 4;
 constexpr int kRouterChunks = 16;  // router K chunks, 4 per workgroup
 constexpr int kRouterParts = kRouterChunks / kNW;
-constexpr int kSmallT = 4;         // shared expert on the VALU up to this many tokens
+constexpr int kXT = 4;             // tokens whose activations are staged in LDS
 constexpr int kMaxT = 64;
 constexpr int kMaxE = 256;
-constexpr int kDnWaves = 8;        // waves of a routed-down workgroup
+constexpr int kDnWaves = 8;        // waves of a down/combine workgroup
+constexpr int kHLdsPairs = 8;      // routed pairs (+ tokens) whose h fits the down kernel's LDS
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every record: loads return 0
+// Weight blocks a streaming wave keeps in flight.  HBM saturates at ~8 MB in flight across
+// the chip; more only queues, and every load issued behind the queue (the activations a
+// workgroup stages first, routing data) waits for it.  A few KB per wave x all resident
+// waves keeps the queue short.
+constexpr int kRing = 4;
 
 struct DecodeArgs {
   int T, E, k;
@@ -54,23 +72,32 @@ struct DecodeArgs {
   const uint16_t* x; const uint16_t* wr; const float* bias;
   float* logits; int32_t* ids; float* w; int32_t* sorted_pair; int32_t* offsets; int32_t* pair_pos;
   float* y_pairs; float* y_shared; const float* residual; float* out; uint16_t* out_bf16;
-  int32_t* wl;      // [0] active experts, [1] units
+  int32_t* wl;      // [0] active experts, [1] units, [2] half-units
   int32_t* ctr;     // [0] router ticket (zero between calls)
   int4* ut;         // units: {expert, first sorted position, pairs (<= 16), 0}
   int32_t* utok;    // [unit][16] token of each pair of the unit
   float* uw;        // [unit][16] routing weight of each pair of the unit
+  int32_t* hl;      // half-units: 2 * unit + half (pairs 8 half .. 8 half + 7 of the unit)
   float* rpart;     // [kRouterParts][T][E]
-  uint16_t* h_hi; uint16_t* h_lo;   // [P][I]
-  float* hs;        // shared h [T][I]
-  int n_router_wg, n_sgu_wg, n_gu_wg, n_sdn_wg;
+  uint16_t* h_hi;   // [P][I] bf16, followed at h_lo_bytes by the lo half [P][I]
+  uint32_t h_lo_bytes, h_bytes;
+  uint16_t* hs;     // shared h [T][I] bf16 hi, then [T][I] bf16 lo
+  int n_router_wg, n_sgu_wg, n_gu_wg;
+  int h_lds;        // down kernel: all routed and shared h staged in LDS
 };
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes at voff + soff (soff: a wave-uniform constant, kept out of the VGPRs).
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
-  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
 }
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -85,6 +112,15 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b, float c) {
   return dot2(a.w, b.w, c);
 }
 
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// h as bf16 hi + bf16 lo (h - hi): ~16 significant bits in two bf16 operands.
+__device__ __forceinline__ void store_hilo(uint16_t* hi_p, size_t lo_stride, float h) {
+  const uint32_t hi = f32_to_bf16_rne(h);
+  hi_p[0] = (uint16_t)hi;
+  hi_p[lo_stride] = (uint16_t)f32_to_bf16_rne(h - bf16_to_f32(hi));
+}
+
 __device__ __forceinline__ uint32_t bf16_lane(uint32_t p, int j) {
   const int z = p >> 3;
   if (j == z) return 0u;
@@ -92,15 +128,16 @@ __device__ __forceinline__ uint32_t bf16_lane(uint32_t p, int j) {
   return ((p >> i) & 1) ? 0xBF80u : 0x3F80u;
 }
 
+// 32-entry table: 5-bit STQ1_0 group pattern -> its four weights in {-1, 0, +1} as bf16.
 __device__ __forceinline__ void build_lut(uint2* lut) {
   const int t = threadIdx.x;
   if (t < 32) lut[t] = make_uint2(bf16_lane(t, 0) | (bf16_lane(t, 1) << 16),
                                   bf16_lane(t, 2) | (bf16_lane(t, 3) << 16));
 }
 
-// The 8 A operands of one STQ1_0 block (8 code bytes + 16 high bits of this lane): all 16
-// table reads are issued before any is used.
-__device__ __forceinline__ void stq_block_a(const uint2* lut, uint2 qs, uint32_t qh, bf16x8_t* av) {
+// The 8 weight operands of one STQ1_0 block (8 code bytes + 16 high bits of this lane):
+// all 16 table reads are issued before any is used.
+__device__ __forceinline__ void stq_block_w(const uint2* lut, uint2 qs, uint32_t qh, bf16x8_t* wv) {
   uint2 l[16];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -109,7 +146,29 @@ __device__ __forceinline__ void stq_block_a(const uint2* lut, uint2 qs, uint32_t
     l[2 * t + 1] = lut[(byte >> 4) | (((qh >> (2 * t + 1)) & 1u) << 4)];
   }
 #pragma unroll
-  for (int t = 0; t < 8; ++t) av[t] = as_bf16x8(make_uint4(l[2 * t].x, l[2 * t].y, l[2 * t + 1].x, l[2 * t + 1].y));
+  for (int t = 0; t < 8; ++t) wv[t] = as_bf16x8(make_uint4(l[2 * t].x, l[2 * t].y, l[2 * t + 1].x, l[2 * t + 1].y));
+}
+
+// fp16 block scales of one row: words of two, in groups of 8 blocks (16 bytes, aligned
+// when NB >= 8), fewer blocks in one smaller aligned load.
+template <int NB>
+__device__ __forceinline__ uint4 load_scale_group(const uint16_t* p, int grp) {
+  if constexpr (NB == 1) {
+    return make_uint4(*p, 0u, 0u, 0u);
+  } else if constexpr (NB == 2) {
+    return make_uint4(*reinterpret_cast<const uint32_t*>(p), 0u, 0u, 0u);
+  } else if constexpr (NB == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return make_uint4(v.x, v.y, 0u, 0u);
+  } else {
+    static_assert(NB % 8 == 0, "block count");
+    return reinterpret_cast<const uint4*>(p)[grp];
+  }
+}
+__device__ __forceinline__ float scale_of(uint4 s, int j) {
+  const int w = (j >> 1) & 3;
+  const uint32_t v = w == 0 ? s.x : (w == 1 ? s.y : (w == 2 ? s.z : s.w));
+  return fp16_to_f32((v >> (16 * (j & 1))) & 0xFFFFu);
 }
 
 __device__ __forceinline__ void wave_fence_lds() {
@@ -117,10 +176,156 @@ __device__ __forceinline__ void wave_fence_lds() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations, not for its
+// vector memory loads still in flight (the weight stream keeps running across it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Pin a block's four accumulators in registers at this point (emits no instruction):
+// sunk to the end of the unrolled loop, every block's partial sum would stay live.
+__device__ __forceinline__ void pin4(f32x4_t& acc) {
+  float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+  asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+  acc[0] = a0; acc[1] = a1; acc[2] = a2; acc[3] = a3;
+}
+
+// Stream of one STQ1_0 row tile over NB blocks: 16 weight rows (this lane's row at rp, its
+// scales at sp) against up to 16 activation rows.  issue() starts the code words of the
+// first R blocks (672 bytes per block and wave) and the first scale group; the run
+// functions decode block j while the code words of block j + R and the next scale group
+// are in flight and return sum_b d_b * (A . W_b) in the D layout.
+template <int NB, int RD = kRing>
+struct StqStream {
+  static constexpr int R = NB < RD ? NB : RD;
+  uint2 q[R];
+  uint32_t qh[R];
+  uint4 sc, sc_next;
+  const uint8_t* qp;
+  const uint8_t* hp;
+  const uint16_t* sp;
+
+  __device__ __forceinline__ void issue(const uint8_t* rp, const uint16_t* sp_) {
+    const int g = (threadIdx.x & 63) >> 4;
+    qp = rp + 8 * g;
+    hp = rp + 32 + 2 * g;
+    sp = sp_;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      q[j] = *reinterpret_cast<const uint2*>(qp + j * 40);
+      qh[j] = *reinterpret_cast<const uint16_t*>(hp + j * 40);
+    }
+    sc = load_scale_group<NB>(sp, 0);
+    sc_next = sc;
+  }
+
+  __device__ __forceinline__ void next(int j, uint2& qj, uint32_t& qhj, float& d) {
+    if (j % 8 == 0) {
+      if (j > 0) sc = sc_next;
+      if (j + 8 < NB) sc_next = load_scale_group<NB>(sp, j / 8 + 1);
+    }
+    qj = q[j % R];
+    qhj = qh[j % R];
+    if (j + R < NB) {
+      q[j % R] = *reinterpret_cast<const uint2*>(qp + (j + R) * 40);
+      qh[j % R] = *reinterpret_cast<const uint16_t*>(hp + (j + R) * 40);
+    }
+    d = scale_of(sc, j);
+  }
+
+  // A operands from LDS: row base `a_lds` (bf16 elements, this lane's token slot and K-slots
+  // already applied), K stride 1.
+  __device__ __forceinline__ f32x4_t run_lds(const uint2* lut, const uint16_t* a_lds) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      uint2 qj;
+      uint32_t qhj;
+      float d;
+      next(j, qj, qhj, d);
+      bf16x8_t wv[8];
+      stq_block_w(lut, qj, qhj, wv);
+      f32x4_t bacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        bacc = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * t)), wv[t], bacc);
+      acc[0] = fmaf(d, bacc[0], acc[0]); acc[1] = fmaf(d, bacc[1], acc[1]);
+      acc[2] = fmaf(d, bacc[2], acc[2]); acc[3] = fmaf(d, bacc[3], acc[3]);
+      pin4(acc);
+    }
+    return acc;
+  }
+
+  // A operands from memory through rsrc ra at byte offset aoff (+ 2 K); each operand is
+  // reloaded for the next block as soon as its MFMA has been issued.
+  __device__ __forceinline__ f32x4_t run_mem(const uint2* lut, rsrc_t ra, uint32_t aoff) {
+    uint4 av[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) av[t] = bload16(ra, aoff, 2 * (8 * t));
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      uint2 qj;
+      uint32_t qhj;
+      float d;
+      next(j, qj, qhj, d);
+      bf16x8_t wv[8];
+      stq_block_w(lut, qj, qhj, wv);
+      f32x4_t bacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        bacc = mfma16(as_bf16x8(av[t]), wv[t], bacc);
+        if (j + 1 < NB) av[t] = bload16(ra, aoff, 2 * (256 * (j + 1) + 8 * t));
+      }
+      acc[0] = fmaf(d, bacc[0], acc[0]); acc[1] = fmaf(d, bacc[1], acc[1]);
+      acc[2] = fmaf(d, bacc[2], acc[2]); acc[3] = fmaf(d, bacc[3], acc[3]);
+      pin4(acc);
+    }
+    return acc;
+  }
+};
+
+// Copy up to ROWS activation rows of K bf16 (row r from src_row(r)) into LDS rows of K
+// through the whole workgroup: issue() loads ROWS rows into registers (rows past `rows`
+// repeat the last one, so every load is unconditional), commit() writes the first `rows`
+// once they have arrived.
+template <int K, int NTHR, int ROWS>
+struct RowStage {
+  static constexpr int PER = (K / 8 + NTHR - 1) / NTHR;   // uint4 per thread per row
+  uint4 v[ROWS][PER];
+  template <class F>
+  __device__ __forceinline__ void issue(int rows, F src_row) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const uint4* p = reinterpret_cast<const uint4*>(src_row(r < rows ? r : rows - 1));
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        const int i = threadIdx.x + NTHR * m;
+        v[r][m] = p[K / 8 % NTHR == 0 || i < K / 8 ? i : 0];
+      }
+    }
+  }
+  __device__ __forceinline__ void commit(int rows, uint16_t* lds) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      if (r < rows) {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+          const int i = threadIdx.x + NTHR * m;
+          if (K / 8 % NTHR == 0 || i < K / 8) reinterpret_cast<uint4*>(lds + (size_t)r * K)[i] = v[r][m];
+        }
+      }
+    }
+  }
+};
+
 // ============================================================================ K1
 // Router partial for one (16 experts, 16 tokens, quarter of K): wave w takes K chunk
 // 4 q + w of 16 with every load up front; the four waves meet in LDS in order and wave 0
-// writes rpart[q][t][e].
+// writes rpart[q][t][e].  Experts and tokens past the end read as zeros.
 template <int HB>
 __device__ void router_unit(const DecodeArgs& a, int rw, float (*s_red)[4][64]) {
   constexpr int H = HB * 256, KC = H / kRouterChunks, NS = KC / 32;
@@ -133,17 +338,19 @@ __device__ void router_unit(const DecodeArgs& a, int rw, float (*s_red)[4][64]) 
   const int col = lane & 15, g = lane >> 4;
   const bool e_ok = et * 16 + col < a.E;
   const bool t_ok = tt * 16 + col < a.T;
-  const uint16_t* arow = a.wr + (size_t)(e_ok ? et * 16 + col : 0) * H + c * KC + 8 * g;
-  const uint16_t* brow = a.x + (size_t)(t_ok ? tt * 16 + col : 0) * H + c * KC + 8 * g;
+  const rsrc_t rw_r = make_rsrc(a.wr, (uint32_t)a.E * H * 2);
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2);
+  const uint32_t wo = e_ok ? 2u * ((uint32_t)(et * 16 + col) * H + c * KC + 8 * g) : kOOB;
+  const uint32_t xo = t_ok ? 2u * ((uint32_t)(tt * 16 + col) * H + c * KC + 8 * g) : kOOB;
   uint4 av[NS], bv[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    av[j] = *reinterpret_cast<const uint4*>(arow + 32 * j);
-    bv[j] = *reinterpret_cast<const uint4*>(brow + 32 * j);
+    av[j] = bload16(rw_r, wo, 2 * 32 * j);
+    bv[j] = bload16(rx, xo, 2 * 32 * j);
   }
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < NS; ++j) acc = mfma16(as_bf16x8(keep_if(e_ok, av[j])), as_bf16x8(keep_if(t_ok, bv[j])), acc);
+  for (int j = 0; j < NS; ++j) acc = mfma16(as_bf16x8(av[j]), as_bf16x8(bv[j]), acc);
 #pragma unroll
   for (int i = 0; i < 4; ++i) s_red[wave][i][lane] = acc[i];
   __syncthreads();
@@ -154,89 +361,6 @@ __device__ void router_unit(const DecodeArgs& a, int rw, float (*s_red)[4][64]) 
       const int e = et * 16 + 4 * g + i;
       const float v = ((s_red[0][i][lane] + s_red[1][i][lane]) + s_red[2][i][lane]) + s_red[3][i][lane];
       if (e < a.E) a.rpart[((size_t)q * a.T + tok) * a.E + e] = v;
-    }
-  }
-}
-
-// Shared gate/up for up to kSmallT tokens: 2 rows per workgroup, wave = (row, gate|up);
-// lane l reads the row at K = 8 l + 512 j, all loads of the row in flight at once.
-template <int HB, int IB>
-__device__ void shared_gateup_valu(const DecodeArgs& a, int sw, float (*s_gu)[2][kSmallT]) {
-  constexpr int H = HB * 256, I = IB * 256, NJ = H / 512;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rl = wave >> 1, mat = wave & 1;
-  const int row = sw * 2 + rl;
-  const uint16_t* wrow = (mat ? a.su : a.sg) + (size_t)row * H + 8 * lane;
-  uint4 wv[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) wv[j] = *reinterpret_cast<const uint4*>(wrow + 512 * j);
-  float acc[kSmallT] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < kSmallT; ++t) {
-    if (t < a.T) {
-      const uint16_t* xr = a.x + (size_t)t * H + 8 * lane;
-      uint4 xv[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) xv[j] = *reinterpret_cast<const uint4*>(xr + 512 * j);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[t] = dot8(wv[j], xv[j], acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < kSmallT; ++t) {
-    const float v = wave_sum(acc[t]);
-    if (lane == 0) s_gu[rl][mat][t] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < 2 * kSmallT) {
-    const int r = threadIdx.x / kSmallT, t = threadIdx.x % kSmallT;
-    if (t < a.T) {
-      const float gv = s_gu[r][0][t], uv = s_gu[r][1][t];
-      a.hs[(size_t)t * I + sw * 2 + r] = gv / (1.0f + expf(-gv)) * uv;
-    }
-  }
-}
-
-// Shared gate/up beyond kSmallT tokens: 16 rows x 16 tokens, the 4 waves split K.
-template <int HB, int IB>
-__device__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2][4][64]) {
-  constexpr int H = HB * 256, I = IB * 256, n_rt = I / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rt = sw % n_rt, tt = sw / n_rt;
-  const int row0 = rt * 16;
-  const int col = lane & 15, g = lane >> 4;
-  const int tok = tt * 16 + col;
-  const bool t_ok = tok < a.T;
-  const int b0 = wave * HB / kNW, b1 = (wave + 1) * HB / kNW;
-  const uint16_t* xr = a.x + (size_t)(t_ok ? tok : 0) * H;
-  const uint16_t* rg = a.sg + (size_t)(row0 + col) * H;
-  const uint16_t* ru = a.su + (size_t)(row0 + col) * H;
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  for (int b = b0; b < b1; ++b) {
-    uint4 cg[8], cu[8], cx[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int off = 256 * b + 32 * t + 8 * g;
-      cg[t] = *reinterpret_cast<const uint4*>(rg + off);
-      cu[t] = *reinterpret_cast<const uint4*>(ru + off);
-      cx[t] = *reinterpret_cast<const uint4*>(xr + off);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const bf16x8_t bx = as_bf16x8(keep_if(t_ok, cx[t]));
-      accg = mfma16(as_bf16x8(cg[t]), bx, accg);
-      accu = mfma16(as_bf16x8(cu[t]), bx, accu);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { s_red[wave][0][i][lane] = accg[i]; s_red[wave][1][i][lane] = accu[i]; }
-  __syncthreads();
-  if (wave == 0 && t_ok) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float gs = 0.f, us = 0.f;
-      for (int w = 0; w < kNW; ++w) { gs += s_red[w][0][i][lane]; us += s_red[w][1][i][lane]; }
-      a.hs[(size_t)tok * I + row0 + 4 * g + i] = gs / (1.0f + expf(-gs)) * us;
     }
   }
 }
@@ -317,61 +441,78 @@ __device__ void wave_topk(const DecodeArgs& a, int t, float* s_v, int* s_i, int*
     }
     float sum = 0.f;   // the same (expert) order in every lane
     for (int j = 0; j < k; ++j) sum += expf(s_v[j] - vmax);
+    const float wgt = expf(mv - vmax) / sum;
     a.ids[(size_t)t * k + rank] = mi;
-    a.w[(size_t)t * k + rank] = expf(mv - vmax) / sum;
+    a.w[(size_t)t * k + rank] = wgt;
     s_ids[t * k + rank] = mi;
+    s_ids[2 * kMaxT * 32 + t * k + rank] = __float_as_int(wgt);
   }
   wave_fence_lds();
 }
 
+struct FinalizeLds {
+  int ids[3 * kMaxT * 32];   // [0, P) expert of each pair; [P0, P0 + P) pairs in sorted order;
+                             // [2 P0, 2 P0 + P) weight bits of each pair (P0 = kMaxT * 32)
+  float v[kNW][32];
+  int i[kNW][32];
+  int cnt[kMaxE];
+  int base[kMaxE];
+  uint8_t wc[kNW][kMaxE];
+  int wsum[kNW * 4];
+};
 
 // Routing of all tokens by the last router workgroup (4 waves): top-k per token, stable
-// permutation of the pairs by expert (E <= 256: one expert per thread), unit table.
-__device__ void route_finalize(const DecodeArgs& a, int* s_ids, float (*s_v)[32], int (*s_i)[32],
-                               int* s_cnt, int* s_base, uint8_t (*s_wc)[kMaxE], int* s_wsum) {
+// permutation of the pairs by expert (E <= 256: one expert per thread), work lists.
+__device__ void route_finalize(const DecodeArgs& a, FinalizeLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k, T = a.T, P = T * k;
-  for (int t = wave; t < T; t += kNW) wave_topk(a, t, s_v[wave], s_i[wave], s_ids);
-  if (tid < E) s_cnt[tid] = 0;
+  constexpr int P0 = kMaxT * 32;
+  for (int t = wave; t < T; t += kNW) wave_topk(a, t, L.v[wave], L.i[wave], L.ids);
+  if (tid < E) L.cnt[tid] = 0;
   __syncthreads();
-  for (int f = tid; f < P; f += kWG) atomicAdd(&s_cnt[s_ids[f]], 1);
+  for (int f = tid; f < P; f += kWG) atomicAdd(&L.cnt[L.ids[f]], 1);
   __syncthreads();
-  const int c = tid < E ? s_cnt[tid] : 0;
-  const int nt = (c + 15) / 16;
-  int ic = c, iu = nt, ia = c > 0;
+  const int c = tid < E ? L.cnt[tid] : 0;
+  const int n16 = (c + 15) / 16, n8 = (c + 7) / 8;
+  int ic = c, iu = n16, ih = n8, ia = c > 0;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int yc = __shfl_up(ic, o, 64), yu = __shfl_up(iu, o, 64), ya = __shfl_up(ia, o, 64);
-    if (lane >= o) { ic += yc; iu += yu; ia += ya; }
+    const int yc = __shfl_up(ic, o, 64), yu = __shfl_up(iu, o, 64);
+    const int yh = __shfl_up(ih, o, 64), ya = __shfl_up(ia, o, 64);
+    if (lane >= o) { ic += yc; iu += yu; ih += yh; ia += ya; }
   }
-  if (lane == 63) { s_wsum[wave * 3] = ic; s_wsum[wave * 3 + 1] = iu; s_wsum[wave * 3 + 2] = ia; }
+  if (lane == 63) {
+    L.wsum[wave * 4] = ic; L.wsum[wave * 4 + 1] = iu; L.wsum[wave * 4 + 2] = ih; L.wsum[wave * 4 + 3] = ia;
+  }
   __syncthreads();
-  int bc = 0, bu = 0, tu = 0, ta = 0;
+  int bc = 0, bu = 0, bh = 0, tu = 0, th = 0, ta = 0;
   for (int w2 = 0; w2 < kNW; ++w2) {
-    if (w2 < wave) { bc += s_wsum[w2 * 3]; bu += s_wsum[w2 * 3 + 1]; }
-    tu += s_wsum[w2 * 3 + 1]; ta += s_wsum[w2 * 3 + 2];
+    if (w2 < wave) { bc += L.wsum[w2 * 4]; bu += L.wsum[w2 * 4 + 1]; bh += L.wsum[w2 * 4 + 2]; }
+    tu += L.wsum[w2 * 4 + 1]; th += L.wsum[w2 * 4 + 2]; ta += L.wsum[w2 * 4 + 3];
   }
   const int start = bc + ic - c;
-  const int u0 = bu + iu - nt;
+  const int u0 = bu + iu - n16;
+  const int h0 = bh + ih - n8;
   if (tid < E) {
-    s_base[tid] = start;
+    L.base[tid] = start;
     a.offsets[tid] = start;
   }
   if (tid == 0) {
     a.offsets[E] = P;
     a.wl[0] = ta;
     a.wl[1] = tu;
+    a.wl[2] = th;
   }
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
   for (int c0 = 0; c0 < P; c0 += kWG) {
-    for (int i = tid; i < kNW * kMaxE; i += kWG) s_wc[i / kMaxE][i % kMaxE] = 0;
+    for (int i = tid; i < kNW * kMaxE; i += kWG) L.wc[i / kMaxE][i % kMaxE] = 0;
     __syncthreads();
     const int f = c0 + tid;
     const bool valid = f < P;
-    const int e = valid ? s_ids[f] : 0;
+    const int e = valid ? L.ids[f] : 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -379,58 +520,48 @@ __device__ void route_finalize(const DecodeArgs& a, int* s_ids, float (*s_v)[32]
       peers &= bit ? ones : ~ones;
     }
     const int rank = __popcll(peers & lt);
-    if (valid && rank == 0) s_wc[wave][e] = (uint8_t)__popcll(peers);
+    if (valid && rank == 0) L.wc[wave][e] = (uint8_t)__popcll(peers);
     __syncthreads();
     if (valid) {
       int pre = 0;
-      for (int w2 = 0; w2 < wave; ++w2) pre += s_wc[w2][e];
-      const int pos = s_base[e] + pre + rank;
+      for (int w2 = 0; w2 < wave; ++w2) pre += L.wc[w2][e];
+      const int pos = L.base[e] + pre + rank;
       a.sorted_pair[pos] = f;
       a.pair_pos[f] = pos;
-      s_ids[kMaxT * 32 + pos] = f;     // sorted order, for the unit table below
+      L.ids[P0 + pos] = f;
     }
     __syncthreads();
     if (tid < E) {
       int s = 0;
-      for (int w2 = 0; w2 < kNW; ++w2) s += s_wc[w2][tid];
-      s_base[tid] += s;
+      for (int w2 = 0; w2 < kNW; ++w2) s += L.wc[w2][tid];
+      L.base[tid] += s;
     }
     __syncthreads();
   }
-  // unit table: unit u0 + q of expert tid covers sorted positions start + 16 q ..
+  // unit u0 + q of expert tid covers sorted positions start + 16 q .. (<= 16 pairs);
+  // half-unit h0 + r covers start + 8 r .. (<= 8 pairs), i.e. half r % 2 of unit u0 + r / 2
   if (tid < E) {
-    for (int q = 0; q < nt; ++q) {
+    for (int q = 0; q < n16; ++q) {
       const int n = min(16, c - 16 * q);
       const int p0 = start + 16 * q;
       a.ut[u0 + q] = make_int4(tid, p0, n, 0);
       for (int j = 0; j < 16; ++j) {
-        const int f = s_ids[kMaxT * 32 + p0 + (j < n ? j : 0)];
+        const int f = L.ids[P0 + p0 + (j < n ? j : 0)];
         a.utok[(u0 + q) * 16 + j] = f / k;
-        a.uw[(u0 + q) * 16 + j] = j < n ? a.w[f] : 0.f;
+        a.uw[(u0 + q) * 16 + j] = j < n ? __int_as_float(L.ids[2 * P0 + f]) : 0.f;
       }
     }
+    for (int r = 0; r < n8; ++r) a.hl[h0 + r] = 2 * (u0 + r / 2) + (r & 1);
   }
 }
 
-template <int HB, int IB>
-__global__ __launch_bounds__(kWG) void k1_router_shared(DecodeArgs a) {
-  __shared__ float s_red[kNW][2][4][64];
-  __shared__ float s_gu[2][2][kSmallT];
+
+template <int HB>
+__global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
+  __shared__ __align__(16) float s_red[kNW][4][64];
   __shared__ int s_last;
-  __shared__ int s_ids[2 * kMaxT * 32];
-  __shared__ float s_v[kNW][32];
-  __shared__ int s_i[kNW][32];
-  __shared__ int s_cnt[kMaxE];
-  __shared__ int s_base[kMaxE];
-  __shared__ uint8_t s_wc[kNW][kMaxE];
-  __shared__ int s_wsum[kNW * 3];
-  const int b = blockIdx.x;
-  if (b >= a.n_router_wg) {
-    if (a.T <= kSmallT) shared_gateup_valu<HB, IB>(a, b - a.n_router_wg, s_gu);
-    else shared_gateup_mfma<HB, IB>(a, b - a.n_router_wg, s_red);
-    return;
-  }
-  router_unit<HB>(a, b, reinterpret_cast<float(*)[4][64]>(&s_red[0][0][0][0]));
+  __shared__ FinalizeLds s_fin;
+  router_unit<HB>(a, blockIdx.x, s_red);
   if (threadIdx.x < 64) {
     __threadfence();     // wave 0 wrote this workgroup's partial: publish it device-wide
     if (threadIdx.x == 0) s_last = atomicAdd(&a.ctr[0], 1) == a.n_router_wg - 1;
@@ -438,302 +569,416 @@ __global__ __launch_bounds__(kWG) void k1_router_shared(DecodeArgs a) {
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  route_finalize(a, s_ids, s_v, s_i, s_cnt, s_base, s_wc, s_wsum);
+  route_finalize(a, s_fin);
   if (threadIdx.x == 0) a.ctr[0] = 0;
 }
 
 // ============================================================================ K2
-// Routed gate/up unit: 16 rows of I for one unit (expert, <= 16 pairs); wave = (gate|up,
-// K half), every code word of the wave's blocks loaded up front, x one block ahead.
-template <int HB, int IB>
-__device__ void routed_gateup_unit(const DecodeArgs& a, int u, const uint2* s_lut,
-                                   float (*s_sc)[HB / 2][16], float (*s_red)[4][64]) {
-  constexpr int H = HB * 256, I = IB * 256, n_rt = I / 16, NB = HB / 2;
+// Routed gate/up: a workgroup takes one unit (expert, <= 16 pairs) and 32 rows of I; wave
+// = (16-row tile, gate|up) over all of K; the gate and up waves of a tile meet in LDS and
+// the gate wave writes h = SiLU(gate) * up as bf16 hi + lo.  Units of up to kXT tokens read
+// their x rows from LDS.
+template <int HB, int IB, int XR, bool MEM>
+__device__ void routed_gateup(const DecodeArgs& a, int wi, const uint2* s_lut, uint16_t* s_x,
+                              float (*s_red)[2][4][64]) {
+  constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int un_i = u / n_rt;
-  const int4 un = a.ut[un_i];
-  const int rt = u % n_rt;
-  const int e = un.x, pos0 = un.y, ntok = un.z;
-  const int row0 = rt * 16;
   const int col = lane & 15, g = lane >> 4;
-  const int tok = a.utok[un_i * 16 + col];
-  const int mat = wave & 1, b0 = (wave >> 1) * NB;
-  const uint8_t* codes = mat ? a.uc : a.gc;
-  const uint16_t* scales = mat ? a.us : a.gs;
-  const uint8_t* rp = codes + ((size_t)e * I + row0 + col) * HB * 40 + (size_t)b0 * 40;
-  uint2 q[NB];
-  uint32_t qh[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    q[j] = *reinterpret_cast<const uint2*>(rp + j * 40 + 8 * g);
-    qh[j] = *reinterpret_cast<const uint16_t*>(rp + j * 40 + 32 + 2 * g);
-  }
-  for (int i = lane; i < NB * 16; i += 64) {
-    const int bl = i >> 4, r = i & 15;
-    s_sc[wave][bl][r] = fp16_to_f32(scales[((size_t)e * I + row0 + r) * HB + b0 + bl]);
-  }
-  const bool t_ok = col < ntok;
-  const uint16_t* xr = a.x + (size_t)tok * H + 64 * g;
-  uint4 nx[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) nx[t] = *reinterpret_cast<const uint4*>(xr + 256 * b0 + 8 * t);
-  wave_fence_lds();
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    uint4 cx[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) cx[t] = nx[t];
-    if (j + 1 < NB) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) nx[t] = *reinterpret_cast<const uint4*>(xr + 256 * (b0 + j + 1) + 8 * t);
-    }
-    bf16x8_t av[8];
-    stq_block_a(s_lut, q[j], qh[j], av);
-    f32x4_t bacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) bacc = mfma16(av[t], as_bf16x8(keep_if(t_ok, cx[t])), bacc);
-    const float4 d = *reinterpret_cast<const float4*>(&s_sc[wave][j][4 * g]);
-    acc[0] = fmaf(d.x, bacc[0], acc[0]); acc[1] = fmaf(d.y, bacc[1], acc[1]);
-    acc[2] = fmaf(d.z, bacc[2], acc[2]); acc[3] = fmaf(d.w, bacc[3], acc[3]);
+  const int un_i = wi / NTP, tp = wi % NTP;
+  const int4 un = a.ut[un_i];
+  const int e = un.x, pos0 = un.y, ntok = un.z;
+  const int mat = wave & 1, tl = wave >> 1;
+  const int row0 = (2 * tp + tl) * 16;
+  const size_t wrow = (size_t)e * I + row0 + col;
+  const uint8_t* rp = (mat ? a.uc : a.gc) + wrow * HB * 40;
+  const uint16_t* sp = (mat ? a.us : a.gs) + wrow * HB;
+  const int* toks = a.utok + un_i * 16;
+  f32x4_t acc;
+  if (!MEM || ntok <= XR) {
+    RowStage<H, kWG, XR> xs;
+    xs.issue(ntok, [&](int r) { return a.x + (size_t)toks[r] * H; });
+    StqStream<HB> st;
+    st.issue(rp, sp);
+    xs.commit(ntok, s_x);
+    lds_barrier();
+    acc = st.run_lds(s_lut, s_x + (col < ntok ? col : 0) * H + 64 * g);
+  } else if constexpr (MEM) {
+    const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2);
+    const uint32_t xo = col < ntok ? 2u * ((uint32_t)toks[col] * H + 64 * g) : kOOB;
+    StqStream<HB> st;
+    st.issue(rp, sp);
+    acc = st.run_mem(s_lut, rx, xo);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s_red[wave][i][lane] = acc[i];
+  for (int i = 0; i < 4; ++i) s_red[tl][mat][i][lane] = acc[i];
   __syncthreads();
-  if (wave == 0 && t_ok) {
-    uint32_t hi[4], lo[4];
+  if (mat == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float gs = s_red[0][i][lane] + s_red[2][i][lane];   // gate: K halves 0, 1
-      const float us = s_red[1][i][lane] + s_red[3][i][lane];   // up
-      const float h = gs / (1.0f + expf(-gs)) * us;
-      hi[i] = f32_to_bf16_rne(h);
-      lo[i] = f32_to_bf16_rne(h - bf16_to_f32(hi[i]));
+      const int slot = 4 * g + i;
+      if (slot < ntok)
+        store_hilo(a.h_hi + (size_t)(pos0 + slot) * I + row0 + col, a.h_lo_bytes / 2,
+                   silu_mul(s_red[tl][0][i][lane], s_red[tl][1][i][lane]));
     }
-    const size_t idx = (size_t)(pos0 + col) * I + row0 + 4 * g;
-    *reinterpret_cast<uint2*>(a.h_hi + idx) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-    *reinterpret_cast<uint2*>(a.h_lo + idx) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
   }
-  __syncthreads();   // s_red / s_sc are reused by the next unit
+  __syncthreads();   // s_red and the x rows are reused by the next work item
 }
 
-// Shared down for up to kSmallT tokens: wave = 4 rows of H, lane l reads K = 8 l + 512 j
-// (the last chunk is half-used when I is an odd multiple of 256).
-template <int HB, int IB>
-__device__ void shared_down_valu(const DecodeArgs& a, int sd) {
-  constexpr int H = HB * 256, I = IB * 256, NJ = (IB + 1) / 2;
+// Shared gate/up for up to kXT tokens (x rows in LDS): wave = one row of I, gate and up,
+// streamed in 16-byte chunks per lane (chunk c: K = 8 l + 512 c for lane l) with the next
+// chunk of both matrices in flight while one is reduced.
+template <int HB, int IB, int XR>
+__device__ void shared_gateup_valu(const DecodeArgs& a, int sw, uint16_t* s_x) {
+  constexpr int H = HB * 256, I = IB * 256, NJ = H / 512, RS = NJ < 2 ? NJ : 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row0 = (sd * kNW + wave) * 4;
-  const bool last_ok = (IB % 2 == 0) || lane < 32;
-  const int lcol = (IB % 2 == 0 || lane < 32) ? lane : 0;
-  uint4 wv[4][NJ];
+  const int T = a.T;
+  const int row = sw * kNW + wave;
+  RowStage<H, kWG, XR> xs;
+  xs.issue(T, [&](int r) { return a.x + (size_t)r * H; });
+  const uint16_t* gp = a.sg + (size_t)row * H + 8 * lane;
+  const uint16_t* up = a.su + (size_t)row * H + 8 * lane;
+  uint4 bg[RS], bu[RS];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int c = 0; c < RS; ++c) {
+    bg[c] = *reinterpret_cast<const uint4*>(gp + 512 * c);
+    bu[c] = *reinterpret_cast<const uint4*>(up + 512 * c);
+  }
+  xs.commit(T, s_x);
+  lds_barrier();
+  static_assert(XR <= kXT, "staged rows");
+  float ag[XR], au[XR];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int cl = j == NJ - 1 ? lcol : lane;
-      wv[r][j] = *reinterpret_cast<const uint4*>(a.sd + (size_t)(row0 + r) * I + 8 * cl + 512 * j);
+  for (int t = 0; t < XR; ++t) { ag[t] = 0.f; au[t] = 0.f; }
+#pragma unroll
+  for (int c = 0; c < NJ; ++c) {
+    const uint4 wg = bg[c % RS], wu = bu[c % RS];
+    if (c + RS < NJ) {
+      bg[c % RS] = *reinterpret_cast<const uint4*>(gp + 512 * (c + RS));
+      bu[c % RS] = *reinterpret_cast<const uint4*>(up + 512 * (c + RS));
     }
-  float acc[4][kSmallT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int t = 0; t < kSmallT; ++t) acc[r][t] = 0.f;
-#pragma unroll
-  for (int t = 0; t < kSmallT; ++t) {
-    if (t < a.T) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int cl = j == NJ - 1 ? lcol : lane;
-        const bool ok = j < NJ - 1 || last_ok;
-        const float* hp = a.hs + (size_t)t * I + 8 * cl + 512 * j;
-        float4 h0 = *reinterpret_cast<const float4*>(hp);
-        float4 h1 = *reinterpret_cast<const float4*>(hp + 4);
-        if (!ok) { h0 = make_float4(0.f, 0.f, 0.f, 0.f); h1 = h0; }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint4 wq = wv[r][j];
-          float s = acc[r][t];
-          s = fmaf(bf16_to_f32(wq.x & 0xFFFF), h0.x, s); s = fmaf(bf16_to_f32(wq.x >> 16), h0.y, s);
-          s = fmaf(bf16_to_f32(wq.y & 0xFFFF), h0.z, s); s = fmaf(bf16_to_f32(wq.y >> 16), h0.w, s);
-          s = fmaf(bf16_to_f32(wq.z & 0xFFFF), h1.x, s); s = fmaf(bf16_to_f32(wq.z >> 16), h1.y, s);
-          s = fmaf(bf16_to_f32(wq.w & 0xFFFF), h1.z, s); s = fmaf(bf16_to_f32(wq.w >> 16), h1.w, s);
-          acc[r][t] = s;
-        }
+    for (int t = 0; t < XR; ++t) {
+      if (t < T) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(s_x + t * H + 8 * lane + 512 * c);
+        ag[t] = dot8(wg, xv, ag[t]);
+        au[t] = dot8(wu, xv, au[t]);
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int t = 0; t < kSmallT; ++t) {
-      if (t < a.T) {
-        const float v = wave_sum(acc[r][t]);
-        if (lane == 0) a.y_shared[(size_t)t * H + row0 + r] = v;
-      }
+  for (int t = 0; t < XR; ++t) {
+    if (t < T) {
+      const float gs = wave_sum(ag[t]), us = wave_sum(au[t]);
+      if (lane == 0) store_hilo(a.hs + (size_t)t * I + row, (size_t)T * I, silu_mul(gs, us));
     }
+  }
 }
 
-// Shared down beyond kSmallT tokens: 16 rows x 16 tokens, the 4 waves split K = I; h is
-// split into bf16 hi + lo on the fly.
+// Shared gate/up beyond kXT tokens: 16 rows x 16 tokens, the 4 waves split K.
 template <int HB, int IB>
-__device__ void shared_down_mfma(const DecodeArgs& a, int sd, float (*s_red)[4][64]) {
-  constexpr int H = HB * 256, I = IB * 256, n_rt = H / 16;
+__device__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2][4][64]) {
+  constexpr int H = HB * 256, I = IB * 256, n_rt = I / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rt = sd % n_rt, tt = sd / n_rt;
+  const int rt = sw % n_rt, tt = sw / n_rt;
   const int row0 = rt * 16;
   const int col = lane & 15, g = lane >> 4;
   const int tok = tt * 16 + col;
   const bool t_ok = tok < a.T;
-  const int b0 = wave * IB / kNW, b1 = (wave + 1) * IB / kNW;
-  const float* hr = a.hs + (size_t)(t_ok ? tok : 0) * I;
-  const uint16_t* rd = a.sd + (size_t)(row0 + col) * I;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int b0 = wave * HB / kNW, b1 = (wave + 1) * HB / kNW;
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2);
+  const uint32_t xo = t_ok ? 2u * (uint32_t)tok * H : kOOB;
+  const uint16_t* rg = a.sg + (size_t)(row0 + col) * H;
+  const uint16_t* ru = a.su + (size_t)(row0 + col) * H;
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   for (int b = b0; b < b1; ++b) {
+    uint4 cg[8], cu[8], cx[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int off = 256 * b + 32 * t + 8 * g;
-      const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(rd + off));
-      const float4 h0 = *reinterpret_cast<const float4*>(hr + off);
-      const float4 h1 = *reinterpret_cast<const float4*>(hr + off + 4);
-      const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-      uint32_t hi[8], lo[8];
+      cg[t] = *reinterpret_cast<const uint4*>(rg + off);
+      cu[t] = *reinterpret_cast<const uint4*>(ru + off);
+      cx[t] = bload16(rx, xo, 2 * off);
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = t_ok ? hv[i] : 0.f;
-        hi[i] = f32_to_bf16_rne(v);
-        lo[i] = f32_to_bf16_rne(v - bf16_to_f32(hi[i]));
-      }
-      acc = mfma16(av, as_bf16x8(make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16))), acc);
-      acc = mfma16(av, as_bf16x8(make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16))), acc);
+    for (int t = 0; t < 8; ++t) {
+      accg = mfma16(as_bf16x8(cg[t]), as_bf16x8(cx[t]), accg);
+      accu = mfma16(as_bf16x8(cu[t]), as_bf16x8(cx[t]), accu);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s_red[wave][i][lane] = acc[i];
+  for (int i = 0; i < 4; ++i) { s_red[wave][0][i][lane] = accg[i]; s_red[wave][1][i][lane] = accu[i]; }
   __syncthreads();
   if (wave == 0 && t_ok) {
-    float y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = 0.f;
-      for (int w = 0; w < kNW; ++w) v += s_red[w][i][lane];
-      y[i] = v;
+      float gs = 0.f, us = 0.f;
+      for (int w = 0; w < kNW; ++w) { gs += s_red[w][0][i][lane]; us += s_red[w][1][i][lane]; }
+      store_hilo(a.hs + (size_t)tok * I + row0 + 4 * g + i, (size_t)a.T * I, silu_mul(gs, us));
     }
-    *reinterpret_cast<float4*>(a.y_shared + (size_t)tok * H + row0 + 4 * g) = make_float4(y[0], y[1], y[2], y[3]);
   }
 }
 
-template <int HB, int IB>
-__global__ __launch_bounds__(kWG) void k2_gateup(DecodeArgs a) {
+template <int HB, int IB, int XR, bool SMALL>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k2_gateup(DecodeArgs a) {
+  extern __shared__ __align__(16) uint16_t s_x[];   // x rows: XR x H bf16
   __shared__ uint2 s_lut[32];
-  __shared__ __align__(16) float s_sc[kNW][HB / 2][16];
-  __shared__ __align__(16) float s_red[kNW][4][64];
+  __shared__ __align__(16) float s_red[2][2][4][64];
   const int b = blockIdx.x;
-  if (b < a.n_sdn_wg) {
-    if (a.T <= kSmallT) shared_down_valu<HB, IB>(a, b);
-    else shared_down_mfma<HB, IB>(a, b, s_red);
+  if (b >= a.n_gu_wg) {
+    if constexpr (SMALL) shared_gateup_valu<HB, IB, XR>(a, b - a.n_gu_wg, s_x);
+    else shared_gateup_mfma<HB, IB>(a, b - a.n_gu_wg, reinterpret_cast<float(*)[2][4][64]>(&s_red[0][0][0][0]));
     return;
   }
   build_lut(s_lut);
   __syncthreads();
-  const int n_units = a.wl[1] * (IB * 256 / 16);
-  for (int u = b - a.n_sdn_wg; u < n_units; u += a.n_gu_wg)
-    routed_gateup_unit<HB, IB>(a, u, s_lut, s_sc, s_red);
+  const int n_items = a.wl[1] * (IB * 256 / 32);
+  for (int wi = b; wi < n_items; wi += a.n_gu_wg)
+    routed_gateup<HB, IB, XR, !SMALL>(a, wi, s_lut, s_x, s_red);
 }
 
 // ============================================================================ K3
-// One 16-row slice of the output: every unit (expert, <= 16 pairs) of the slice, spread
-// over the 8 waves; each wave adds w * y into its own LDS sums; the slice is then
-// out = y_shared + sum over waves in order (+ residual).
+// Shared down for up to kXT tokens: wave w takes rows row0 + 2w, +1, streamed in 16-byte
+// chunks per lane (chunk j: K = 8 l + 512 j for lane l; the last chunk is half-used when I
+// is an odd multiple of 256), R chunks in flight; h comes as bf16 hi + lo from `hs` (LDS or
+// memory).  Each result is added into the wave's LDS sums and written to y_shared.
 template <int HB, int IB>
-__global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
-  constexpr int H = HB * 256, I = IB * 256;
-  __shared__ uint2 s_lut[32];
-  __shared__ __align__(16) float s_sc[kDnWaves][IB][16];
-  __shared__ __align__(16) float s_acc[kDnWaves][kMaxT][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int T = a.T;
-  const int row0 = blockIdx.x * 16;
-  const int col = lane & 15, g = lane >> 4;
-  build_lut(s_lut);
-  for (int i = threadIdx.x; i < kDnWaves * T * 16; i += 64 * kDnWaves)
-    s_acc[i / (T * 16)][(i / 16) % T][i % 16] = 0.f;
-  __syncthreads();
-  const int n_units = a.wl[1];
-  for (int uu = wave; uu < n_units; uu += kDnWaves) {
-    const int4 un = a.ut[uu];
-    const int e = un.x, pos0 = un.y, ntok = un.z;
-    const int tok = a.utok[uu * 16 + col];
-    const float wt = a.uw[uu * 16 + col];
-    const uint8_t* rp = a.dc + ((size_t)e * H + row0 + col) * IB * 40;
-    uint2 q[IB];
-    uint32_t qh[IB];
+struct SharedDown {
+  static constexpr int H = HB * 256, I = IB * 256, NJ = (IB + 1) / 2, NI = 2 * NJ, R = NI < 4 ? NI : 4;
+  uint4 w[R];
+  rsrc_t rsd;
+  uint32_t rb;       // byte offset of this wave's first row at this lane's K
+  int lcol;
+  bool last_ok;
+
+  __device__ __forceinline__ uint4 load(int it) const {
+    const int j = it >> 1, r = it & 1;
+    const uint32_t cl = j == NJ - 1 ? lcol : (threadIdx.x & 63);
+    return bload16(rsd, rb + 2u * (r * I + 8 * cl), 2 * 512 * j);
+  }
+  __device__ __forceinline__ void issue(const DecodeArgs& a, int row0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    last_ok = (IB % 2 == 0) || lane < 32;
+    lcol = last_ok ? lane : 0;
+    rsd = make_rsrc(a.sd, a.sd ? (uint32_t)H * I * 2 : 0u);
+    rb = 2u * (uint32_t)(row0 + 2 * wave) * I;
 #pragma unroll
-    for (int j = 0; j < IB; ++j) {
-      q[j] = *reinterpret_cast<const uint2*>(rp + j * 40 + 8 * g);
-      qh[j] = *reinterpret_cast<const uint16_t*>(rp + j * 40 + 32 + 2 * g);
-    }
-    for (int i = lane; i < IB * 16; i += 64) {
-      const int bl = i >> 4, r = i & 15;
-      s_sc[wave][bl][r] = fp16_to_f32(a.ds[((size_t)e * H + row0 + r) * IB + bl]);
-    }
-    const bool t_ok = col < ntok;
-    const size_t hoff = (size_t)(pos0 + (t_ok ? col : 0)) * I + 64 * g;
-    const uint16_t* hh = a.h_hi + hoff;
-    const uint16_t* hl = a.h_lo + hoff;
-    uint4 nh[8], nl[8];
+    for (int it = 0; it < R; ++it) w[it] = load(it);
+  }
+  __device__ __forceinline__ void run(const DecodeArgs& a, int row0, const uint16_t* hs, float* s_acc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int T = a.T;
+    const size_t lo = (size_t)T * I;
+    float acc[2][kXT];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      nh[t] = *reinterpret_cast<const uint4*>(hh + 8 * t);
-      nl[t] = *reinterpret_cast<const uint4*>(hl + 8 * t);
-    }
-    wave_fence_lds();
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int j = 0; j < IB; ++j) {
-      uint4 ch[8], cl[8];
+      for (int t = 0; t < kXT; ++t) acc[r][t] = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) { ch[t] = nh[t]; cl[t] = nl[t]; }
-      if (j + 1 < IB) {
+    for (int it = 0; it < NI; ++it) {
+      const uint4 wv = w[it % R];
+      if (it + R < NI) w[it % R] = load(it + R);
+      const int j = it >> 1, r = it & 1;
+      const int cl = j == NJ - 1 ? lcol : lane;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          nh[t] = *reinterpret_cast<const uint4*>(hh + 256 * (j + 1) + 8 * t);
-          nl[t] = *reinterpret_cast<const uint4*>(hl + 256 * (j + 1) + 8 * t);
+      for (int t = 0; t < kXT; ++t) {
+        if (t < T) {
+          const uint16_t* hp = hs + (size_t)t * I + 8 * cl + 512 * j;
+          uint4 hh = *reinterpret_cast<const uint4*>(hp);
+          uint4 hl = *reinterpret_cast<const uint4*>(hp + lo);
+          if (j == NJ - 1 && !last_ok) { hh = make_uint4(0u, 0u, 0u, 0u); hl = hh; }
+          acc[r][t] = dot8(wv, hl, dot8(wv, hh, acc[r][t]));
         }
       }
-      bf16x8_t av[8];
-      stq_block_a(s_lut, q[j], qh[j], av);
-      f32x4_t bh = {0.f, 0.f, 0.f, 0.f}, bl = {0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int t = 0; t < kXT; ++t) {
+      if (t < T) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const float v = wave_sum(acc[r][t]);
+          if (lane == 0) {
+            const int rr = 2 * wave + r;
+            s_acc[(wave * T + t) * 16 + rr] += v;
+            a.y_shared[(size_t)t * H + row0 + rr] = v;
+          }
+        }
+      }
+    }
+  }
+};
+
+// Shared down beyond kXT tokens: 16 rows x 16-token tiles; wave w takes K blocks w, w + 8,
+// .. (A = h hi and lo rows, B = weights); the waves' partials meet in LDS (s_red) in order,
+// wave 0 writes y_shared and adds it into its own sums.
+template <int HB, int IB>
+__device__ void shared_down_mfma(const DecodeArgs& a, int row0, float* s_acc, float* s_red) {
+  constexpr int H = HB * 256, I = IB * 256;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int T = a.T;
+  const rsrc_t rh = make_rsrc(a.hs, (uint32_t)T * I * 4);
+  const uint32_t lo = 2u * (uint32_t)T * I;
+  const uint16_t* rd = a.sd + (size_t)(row0 + col) * I;
+  for (int tt = 0; tt * 16 < T; ++tt) {
+    const int tok = tt * 16 + col;
+    const uint32_t ho = tok < T ? 2u * (uint32_t)tok * I : kOOB;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int b = wave; b < IB; b += kDnWaves) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        bh = mfma16(av[t], as_bf16x8(keep_if(t_ok, ch[t])), bh);
-        bl = mfma16(av[t], as_bf16x8(keep_if(t_ok, cl[t])), bl);
+        const int off = 256 * b + 32 * t + 8 * g;
+        const bf16x8_t wv = as_bf16x8(*reinterpret_cast<const uint4*>(rd + off));
+        acc = mfma16(as_bf16x8(bload16(rh, ho, 2 * off)), wv, acc);
+        acc = mfma16(as_bf16x8(bload16(rh, ho + lo, 2 * off)), wv, acc);
       }
-      const float4 d = *reinterpret_cast<const float4*>(&s_sc[wave][j][4 * g]);
-      acc[0] = fmaf(d.x, bh[0] + bl[0], acc[0]); acc[1] = fmaf(d.y, bh[1] + bl[1], acc[1]);
-      acc[2] = fmaf(d.z, bh[2] + bl[2], acc[2]); acc[3] = fmaf(d.w, bh[3] + bl[3], acc[3]);
     }
-    if (t_ok) {
-      *reinterpret_cast<float4*>(a.y_pairs + (size_t)(pos0 + col) * H + row0 + 4 * g) =
-          make_float4(acc[0], acc[1], acc[2], acc[3]);
-      float* sa = &s_acc[wave][tok][4 * g];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = fmaf(wt, acc[i], sa[i]);
+    for (int i = 0; i < 4; ++i) s_red[(wave * 4 + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tt * 16 + 4 * g + i;
+        if (t < T) {
+          float v = 0.f;
+          for (int w = 0; w < kDnWaves; ++w) v += s_red[(w * 4 + i) * 64 + lane];
+          a.y_shared[(size_t)t * H + row0 + col] = v;
+          s_acc[t * 16 + col] += v;
+        }
+      }
     }
-    wave_fence_lds();
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < T * 16; i += 64 * kDnWaves) {
-    const int t = i >> 4, r = i & 15;
-    float v = a.y_shared ? a.y_shared[(size_t)t * H + row0 + r] : 0.f;
-    for (int w = 0; w < kDnWaves; ++w) v += s_acc[w][t][r];
-    if (a.residual) v += a.residual[(size_t)t * H + row0 + r];
-    a.out[(size_t)t * H + row0 + r] = v;
-    if (a.out_bf16) a.out_bf16[(size_t)t * H + row0 + r] = (uint16_t)f32_to_bf16_rne(v);
+    __syncthreads();
   }
 }
 
-template <int HB, int IB>
+// One 16-row slice of the output: the shared expert's rows, then every half-unit
+// (expert, <= 8 pairs) spread over the 8 waves, each wave adding w * y into its own LDS
+// sums; out = sum over waves in order (+ residual).  When all h fits (few pairs), it is
+// staged in LDS first: routed hi rows, routed lo rows, shared hi, shared lo.
+template <int HB, int IB, bool SMALL, bool HLDS>
+__global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
+  constexpr int H = HB * 256, I = IB * 256;
+  constexpr int kStage = 9;                  // uint4 per thread when h is staged
+  extern __shared__ __align__(16) float s_dyn[];  // [kDnWaves][T][16] sums, then staged h
+                                                  // or the shared partials [kDnWaves][4][64]
+  __shared__ uint2 s_lut[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, P = T * a.k;
+  const int row0 = blockIdx.x * 16;
+  const int col = lane & 15, g = lane >> 4;
+  float* s_acc = s_dyn;
+  uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn + kDnWaves * T * 16);
+  constexpr bool h_lds = HLDS;
+  // residual of this slice (T * 16 <= 1024 elements, two per thread), read up front
+  const rsrc_t rres = make_rsrc(a.residual, a.residual ? (uint32_t)T * H * 4 : 0u);
+  float rs[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int i = tid + 64 * kDnWaves * m;
+    const uint32_t o = i < T * 16 ? 4u * ((uint32_t)(i >> 4) * H + row0 + (i & 15)) : kOOB;
+    rs[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rres, o, 0, 0));
+  }
+  // staged h: uint4 i < P*I/8 from h hi, then h lo, then shared hi + lo
+  const int n_rh = P * I / 8, n_all = 2 * n_rh + T * I / 4;
+  uint4 hv[kStage];
+  if constexpr (h_lds) {
+#pragma unroll
+    for (int m = 0; m < kStage; ++m) {
+      int i = tid + 64 * kDnWaves * m;
+      i = i < n_all ? i : 0;
+      const uint4* src = i < n_rh ? reinterpret_cast<const uint4*>(a.h_hi) + i
+                       : i < 2 * n_rh ? reinterpret_cast<const uint4*>(a.h_hi + a.h_lo_bytes / 2) + (i - n_rh)
+                       : reinterpret_cast<const uint4*>(a.hs) + (i - 2 * n_rh);
+      hv[m] = *src;
+    }
+  }
+  // shared rows' weights (zeros without a shared expert)
+  SharedDown<HB, IB> sdn;
+  if constexpr (SMALL) sdn.issue(a, row0);
+  // first half-unit's code words (a wave without one streams the last half-unit's, unused)
+  const int n_half = a.wl[2];
+  StqStream<IB> st;
+  int hu = wave;
+  int ent = a.hl[hu < n_half ? hu : n_half - 1];
+  int4 un = a.ut[ent >> 1];
+  {
+    const size_t wrow = (size_t)un.x * H + row0 + col;
+    st.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
+  }
+  build_lut(s_lut);
+  for (int i = tid; i < kDnWaves * T * 16; i += 64 * kDnWaves) s_acc[i] = 0.f;
+  if constexpr (h_lds) {
+#pragma unroll
+    for (int m = 0; m < kStage; ++m) {
+      const int i = tid + 64 * kDnWaves * m;
+      if (i < n_all) reinterpret_cast<uint4*>(s_h)[i] = hv[m];
+    }
+  }
+  lds_barrier();
+  if (a.sd) {
+    if constexpr (SMALL) {
+      if constexpr (h_lds) sdn.run(a, row0, s_h + 2 * P * I, s_acc);
+      else sdn.run(a, row0, a.hs, s_acc);
+    } else {
+      shared_down_mfma<HB, IB>(a, row0, s_acc, s_dyn + kDnWaves * T * 16);
+    }
+  }
+  const rsrc_t rh = make_rsrc(a.h_hi, a.h_bytes);
+  const int sp2 = col >> 1;
+  for (; hu < n_half; hu += kDnWaves) {
+    if (hu != wave) {
+      ent = a.hl[hu];
+      un = a.ut[ent >> 1];
+      const size_t wrow = (size_t)un.x * H + row0 + col;
+      st.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
+    }
+    const int un_i = ent >> 1, half = ent & 1;
+    const int pos0 = un.y + 8 * half;
+    const int n8 = min(8, un.z - 8 * half);
+    // this lane's two result pairs (2g, 2g+1): token and routing weight
+    int tk[2];
+    float wt[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      tk[m] = a.utok[un_i * 16 + 8 * half + 2 * g + m];
+      wt[m] = a.uw[un_i * 16 + 8 * half + 2 * g + m];
+    }
+    f32x4_t acc;
+    if constexpr (h_lds) {
+      const int pr = pos0 + (sp2 < n8 ? sp2 : 0);
+      acc = st.run_lds(s_lut, s_h + (col & 1) * P * I + pr * I + 64 * g);
+    } else {
+      const uint32_t ho = sp2 < n8 ? (col & 1 ? a.h_lo_bytes : 0u) + 2u * ((uint32_t)(pos0 + sp2) * I + 64 * g) : kOOB;
+      acc = st.run_mem(s_lut, rh, ho);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int p = 2 * g + m;
+      if (p < n8) {
+        const float y = acc[2 * m] + acc[2 * m + 1];
+        a.y_pairs[(size_t)(pos0 + p) * H + row0 + col] = y;
+        float* sa = &s_acc[(wave * T + tk[m]) * 16 + col];
+        *sa = fmaf(wt[m], y, *sa);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int i = tid + 64 * kDnWaves * m;
+    if (i < T * 16) {
+      const int t = i >> 4, r = i & 15;
+      float v = 0.f;
+      for (int w = 0; w < kDnWaves; ++w) v += s_acc[(w * T + t) * 16 + r];
+      v += rs[m];
+      const size_t o = (size_t)t * H + row0 + r;
+      a.out[o] = v;
+      if (a.out_bf16) a.out_bf16[o] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
+template <int HB, int IB, int XR, bool SMALL>
 hipError_t launch_all(DecodeArgs& a, hipStream_t s) {
   constexpr int H = HB * 256, I = IB * 256;
   const int T = a.T;
@@ -741,25 +986,36 @@ hipError_t launch_all(DecodeArgs& a, hipStream_t s) {
   const int P = T * a.k;
   const int max_units = (P < a.E ? P : a.E) + (P + 15) / 16;
   a.n_router_wg = ((a.E + 15) / 16) * kRouterParts * n_tt;
-  const bool small = T <= kSmallT;
   const bool shared = a.sg != nullptr;
-  a.n_sgu_wg = shared ? (small ? I / 2 : (I / 16) * n_tt) : 0;
-  a.n_sdn_wg = shared ? (small ? H / (4 * kNW) : (H / 16) * n_tt) : 0;
+  a.n_sgu_wg = shared ? (SMALL ? I / kNW : (I / 16) * n_tt) : 0;
   const int cap = 8192;
-  const int gu = max_units * (I / 16);
+  const int gu = max_units * (I / 32);
   a.n_gu_wg = gu < cap ? gu : cap;
+  a.h_lds = P <= kHLdsPairs && SMALL && (P + T) * I <= 9 * 64 * kDnWaves * 4 ? 1 : 0;
+  const size_t lds2 = (size_t)XR * H * 2;
+  const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (a.h_lds ? (size_t)(P + T) * I * 4 : 0) +
+                      (SMALL ? 0 : (size_t)kDnWaves * 4 * 64 * 4);
   const bool prof = moe_prof_on();
   if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
-  hipLaunchKernelGGL((k1_router_shared<HB, IB>), dim3(a.n_router_wg + a.n_sgu_wg), dim3(kWG), 0, s, a);
+  hipLaunchKernelGGL((k1_route<HB>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
-  hipLaunchKernelGGL((k2_gateup<HB, IB>), dim3(a.n_sdn_wg + a.n_gu_wg), dim3(kWG), 0, s, a);
+  hipLaunchKernelGGL((k2_gateup<HB, IB, XR, SMALL>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(kWG), lds2, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
-  hipLaunchKernelGGL((k3_down_combine<HB, IB>), dim3(H / 16), dim3(64 * kDnWaves), 0, s, a);
+  if (a.h_lds) hipLaunchKernelGGL((k3_down_combine<HB, IB, SMALL, true>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  else hipLaunchKernelGGL((k3_down_combine<HB, IB, SMALL, false>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
   return hipSuccess;
+}
+
+template <int HB, int IB>
+hipError_t launch_shape(DecodeArgs& a, hipStream_t s) {
+  if (a.T == 1) return launch_all<HB, IB, 1, true>(a, s);
+  if (a.T == 2) return launch_all<HB, IB, 2, true>(a, s);
+  if (a.T <= kXT) return launch_all<HB, IB, kXT, true>(a, s);
+  return launch_all<HB, IB, kXT, false>(a, s);
 }
 
 }  // namespace
@@ -775,18 +1031,21 @@ bool moe_decode_shape_ok(int H, int I, int E) {
 
 size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, size_t* offs) {
   const size_t P = (size_t)T * k;
-  const size_t max_units = (size_t)(P < (size_t)E ? P : E) + (P + 15) / 16;
+  const size_t pe = P < (size_t)E ? P : (size_t)E;
+  const size_t max_units = pe + (P + 15) / 16;
+  const size_t max_half = pe + (P + 7) / 8;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t cur = 0;
   offs[0] = cur; cur = al(cur + 8 * sizeof(int32_t));                              // work list + ticket
   offs[1] = cur; cur = al(cur + max_units * sizeof(int4));                          // unit table
   offs[2] = cur; cur = al(cur + max_units * 16 * sizeof(int32_t));                  // unit tokens
   offs[3] = cur; cur = al(cur + max_units * 16 * sizeof(float));                    // unit weights
-  offs[4] = cur; cur = al(cur + (size_t)kRouterParts * T * E * sizeof(float));     // router partials
-  offs[5] = cur; cur = al(cur + P * I * 2);                                          // h hi
-  offs[6] = cur; cur = al(cur + P * I * 2);                                          // h lo
-  offs[7] = cur; cur = al(cur + (has_shared ? (size_t)T * I * sizeof(float) : 0));   // shared h
-  offs[8] = cur;
+  offs[4] = cur; cur = al(cur + max_half * sizeof(int32_t));                        // half-units
+  offs[5] = cur; cur = al(cur + (size_t)kRouterParts * T * E * sizeof(float));     // router partials
+  offs[6] = cur; cur = al(cur + P * I * 2);                                          // h hi
+  offs[7] = cur; cur = al(cur + P * I * 2);                                          // h lo
+  offs[8] = cur; cur = al(cur + (has_shared ? (size_t)T * I * 4 : 0));              // shared h hi, lo
+  offs[9] = cur;
   return cur;
 }
 
@@ -811,7 +1070,7 @@ hipError_t moe_launch_decode_fused(const moe_dims* d, const moe_experts* routed,
   a.sorted_pair = sorted_pair; a.offsets = offsets; a.pair_pos = pair_pos;
   a.y_pairs = y_pairs; a.y_shared = shared ? y_shared : nullptr; a.residual = residual;
   a.out = out; a.out_bf16 = out_bf16;
-  size_t offs[9];
+  size_t offs[10];
   moe_decode_ws_layout(d->T, d->H, d->I, d->E, d->k, shared != nullptr, offs);
   uint8_t* b = static_cast<uint8_t*>(ws);
   a.wl = reinterpret_cast<int32_t*>(b + offs[0]);
@@ -819,16 +1078,18 @@ hipError_t moe_launch_decode_fused(const moe_dims* d, const moe_experts* routed,
   a.ut = reinterpret_cast<int4*>(b + offs[1]);
   a.utok = reinterpret_cast<int32_t*>(b + offs[2]);
   a.uw = reinterpret_cast<float*>(b + offs[3]);
-  a.rpart = reinterpret_cast<float*>(b + offs[4]);
-  a.h_hi = reinterpret_cast<uint16_t*>(b + offs[5]);
-  a.h_lo = reinterpret_cast<uint16_t*>(b + offs[6]);
-  a.hs = reinterpret_cast<float*>(b + offs[7]);
+  a.hl = reinterpret_cast<int32_t*>(b + offs[4]);
+  a.rpart = reinterpret_cast<float*>(b + offs[5]);
+  a.h_hi = reinterpret_cast<uint16_t*>(b + offs[6]);
+  a.h_lo_bytes = (uint32_t)(offs[7] - offs[6]);
+  a.h_bytes = (uint32_t)(offs[7] - offs[6] + (size_t)d->T * d->k * d->I * 2);
+  a.hs = reinterpret_cast<uint16_t*>(b + offs[8]);
   const int hb = d->H / 256, ib = d->I / 256;
-  if (hb == 2 && ib == 1) return launch_all<2, 1>(a, s);
-  if (hb == 4 && ib == 2) return launch_all<4, 2>(a, s);
-  if (hb == 8 && ib == 4) return launch_all<8, 4>(a, s);
-  if (hb == 16 && ib == 8) return launch_all<16, 8>(a, s);
-  if (hb == 24 && ib == 8) return launch_all<24, 8>(a, s);
-  if (hb == 32 && ib == 8) return launch_all<32, 8>(a, s);
+  if (hb == 2 && ib == 1) return launch_shape<2, 1>(a, s);
+  if (hb == 4 && ib == 2) return launch_shape<4, 2>(a, s);
+  if (hb == 8 && ib == 4) return launch_shape<8, 4>(a, s);
+  if (hb == 16 && ib == 8) return launch_shape<16, 8>(a, s);
+  if (hb == 24 && ib == 8) return launch_shape<24, 8>(a, s);
+  if (hb == 32 && ib == 8) return launch_shape<32, 8>(a, s);
   return hipErrorInvalidValue;
 }
