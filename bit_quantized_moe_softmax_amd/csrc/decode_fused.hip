@@ -77,7 +77,9 @@ struct DecodeArgs {
   int4* ut;         // units: {expert, first sorted position, pairs (<= 16), 0}
   int32_t* utok;    // [unit][16] token of each pair of the unit
   float* uw;        // [unit][16] routing weight of each pair of the unit
-  int32_t* hl;      // half-units: 2 * unit + half (pairs 8 half .. 8 half + 7 of the unit)
+  int4* hl;         // half-units: {expert, first sorted position, pairs (<= 8), index of
+                    //  its first pair in utok / uw}
+  int max_half;     // capacity of hl
   float* rpart;     // [kRouterParts][T][E]
   uint16_t* h_hi;   // [P][I] bf16, followed at h_lo_bytes by the lo half [P][I]
   uint32_t h_lo_bytes, h_bytes;
@@ -149,6 +151,22 @@ __device__ __forceinline__ void stq_block_w(const uint2* lut, uint2 qs, uint32_t
   for (int t = 0; t < 8; ++t) wv[t] = as_bf16x8(make_uint4(l[2 * t].x, l[2 * t].y, l[2 * t + 1].x, l[2 * t + 1].y));
 }
 
+// The 4 weight operands of half h of one STQ1_0 block (code bytes 4h .. 4h+3 of this lane
+// and their 8 high bits): 8 table reads, all issued before any is used.
+__device__ __forceinline__ void stq_half_w(const uint2* lut, uint2 qs, uint32_t qh, int h, bf16x8_t* wv) {
+  const uint32_t w4 = h ? qs.y : qs.x;
+  const uint32_t hb = qh >> (8 * h);
+  uint2 l[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t byte = (w4 >> (8 * t)) & 0xFFu;
+    l[2 * t] = lut[(byte & 15u) | (((hb >> (2 * t)) & 1u) << 4)];
+    l[2 * t + 1] = lut[(byte >> 4) | (((hb >> (2 * t + 1)) & 1u) << 4)];
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) wv[t] = as_bf16x8(make_uint4(l[2 * t].x, l[2 * t].y, l[2 * t + 1].x, l[2 * t + 1].y));
+}
+
 // fp16 block scales of one row: words of two, in groups of 8 blocks (16 bytes, aligned
 // when NB >= 8), fewer blocks in one smaller aligned load.
 template <int NB>
@@ -171,18 +189,20 @@ __device__ __forceinline__ float scale_of(uint4 s, int j) {
   return fp16_to_f32((v >> (16 * (j & 1))) & 0xFFFFu);
 }
 
-__device__ __forceinline__ void wave_fence_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+// One wave's LDS writes made visible to its own later LDS reads: a workgroup-scope fence
+// on the LDS address space only, so vector memory loads and stores stay in flight.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations, not for its
 // vector memory loads still in flight (the weight stream keeps running across it).
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Pin a block's four accumulators in registers at this point (emits no instruction):
@@ -237,24 +257,44 @@ struct StqStream {
   }
 
   // A operands from LDS: row base `a_lds` (bf16 elements, this lane's token slot and K-slots
-  // already applied), K stride 1.
+  // already applied), K stride 1.  Software-pipelined by half blocks: the table reads of
+  // half h + 1 are in flight while the 4 MFMAs of half h run, and the two halves of a block
+  // accumulate in separate registers (two 4-deep MFMA chains).
   __device__ __forceinline__ f32x4_t run_lds(const uint2* lut, const uint16_t* a_lds) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    uint2 qj;
+    uint32_t qhj;
+    float d;
+    next(0, qj, qhj, d);
+    bf16x8_t wn[4];
+    stq_half_w(lut, qj, qhj, 0, wn);
+    f32x4_t b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      uint2 qj;
-      uint32_t qhj;
-      float d;
-      next(j, qj, qhj, d);
-      bf16x8_t wv[8];
-      stq_block_w(lut, qj, qhj, wv);
-      f32x4_t bacc = {0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < 2 * NB; ++hh) {
+      const int j = hh >> 1, h = hh & 1;
+      bf16x8_t wc[4];
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        bacc = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * t)), wv[t], bacc);
-      acc[0] = fmaf(d, bacc[0], acc[0]); acc[1] = fmaf(d, bacc[1], acc[1]);
-      acc[2] = fmaf(d, bacc[2], acc[2]); acc[3] = fmaf(d, bacc[3], acc[3]);
-      pin4(acc);
+      for (int t = 0; t < 4; ++t) wc[t] = wn[t];
+      float dj = d;
+      if (h == 0) {
+        stq_half_w(lut, qj, qhj, 1, wn);
+      } else if (j + 1 < NB) {
+        next(j + 1, qj, qhj, d);
+        stq_half_w(lut, qj, qhj, 0, wn);
+      }
+      uint4 av[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * (4 * h + t));
+      f32x4_t& bh = h ? b1 : b0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bh = mfma16(as_bf16x8(av[t]), wc[t], bh);
+      if (h == 1) {
+        acc[0] = fmaf(dj, b0[0] + b1[0], acc[0]); acc[1] = fmaf(dj, b0[1] + b1[1], acc[1]);
+        acc[2] = fmaf(dj, b0[2] + b1[2], acc[2]); acc[3] = fmaf(dj, b0[3] + b1[3], acc[3]);
+        pin4(acc);
+        b0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        b1 = b0;
+      }
     }
     return acc;
   }
@@ -327,7 +367,7 @@ struct RowStage {
 // 4 q + w of 16 with every load up front; the four waves meet in LDS in order and wave 0
 // writes rpart[q][t][e].  Experts and tokens past the end read as zeros.
 template <int HB>
-__device__ void router_unit(const DecodeArgs& a, int rw, float (*s_red)[4][64]) {
+__device__ __forceinline__ void router_unit(const DecodeArgs& a, int rw, float (*s_red)[4][64]) {
   constexpr int H = HB * 256, KC = H / kRouterChunks, NS = KC / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_et = (a.E + 15) / 16;
@@ -365,113 +405,128 @@ __device__ void router_unit(const DecodeArgs& a, int rw, float (*s_red)[4][64]) 
   }
 }
 
-// Order-preserving unsigned key of a float (larger float -> larger key; -0 as +0).
-__device__ __forceinline__ uint32_t fkey(float f) {
-  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Top-k of one token by one wave (E <= 256: four logits per lane): the k-th largest key by a
-// 32-step bitwise search with ballots, then the chosen slots ordered by (logit desc,
-// expert asc) through LDS.
-__device__ void wave_topk(const DecodeArgs& a, int t, float* s_v, int* s_i, int* s_ids) {
+// Top-k of one token by one wave (E <= 256: four logits per lane), k rounds of: the
+// largest remaining key (wave reduction), its lowest expert (ballots over the four slots),
+// that key removed.  Slots come out ordered by (logit desc, expert asc).  The k experts and
+// weights of token t land in slot order in ids_out / wbits_out (LDS); with `out` set,
+// logits, ids and weights also go to the caller's arrays.
+struct TopkIn {
+  float part[4][kRouterParts];   // router partials of this lane's four experts
+  float bias[4];
+};
+// Loads of wave_topk's inputs for token t, issued ahead of its use.
+__device__ __forceinline__ void topk_load(const DecodeArgs& a, int t, TopkIn& in) {
   const int lane = threadIdx.x & 63;
-  const int E = a.E, k = a.k;
-  float part[4][kRouterParts];
+  const int E = a.E;
+  const rsrc_t rb = make_rsrc(a.bias, a.bias ? (uint32_t)E * 4 : 0u);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = i * 64 + lane < E ? i * 64 + lane : 0;
 #pragma unroll
-    for (int c = 0; c < kRouterParts; ++c) part[i][c] = a.rpart[((size_t)c * a.T + t) * E + e];
+    for (int c = 0; c < kRouterParts; ++c) in.part[i][c] = a.rpart[((size_t)c * a.T + t) * E + e];
+    in.bias[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, i * 64 + lane < E ? 4u * (i * 64 + lane) : kOOB, 0, 0));
   }
-  float v[4];
+}
+
+// Order-preserving unsigned key of a float (larger float -> larger key, -0 as +0; every
+// finite or infinite value maps above 0) and its inverse.
+__device__ __forceinline__ uint32_t fkey(float f) {
+  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Largest value over the wave: within each row of 16 lanes by DPP (quad permutes, half and
+// full row mirrors), then across the four rows through scalar reads.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // lanes ^ 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // lanes ^ 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+__device__ __forceinline__ void wave_topk(const DecodeArgs& a, int t, const TopkIn& in, float* s_v, int* s_i,
+                                          int* ids_out, int* wbits_out, bool out) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
   uint32_t key[4];
-  bool valid[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = i * 64 + lane;
-    valid[i] = e < E;
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < kRouterParts; ++c) s += part[i][c];
-    if (a.bias && valid[i]) s += a.bias[e];
-    v[i] = s;
-    if (valid[i]) a.logits[(size_t)t * E + e] = s;
-    key[i] = valid[i] ? fkey(s) : 0u;
+    for (int c = 0; c < kRouterParts; ++c) s += in.part[i][c];
+    if (a.bias) s += in.bias[i];
+    if (out && e < E) a.logits[(size_t)t * E + e] = s;
+    key[i] = e < E ? fkey(s) : 0u;
   }
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int c = 0;
+  for (int r = 0; r < k; ++r) {
+    const uint32_t lm = max(max(key[0], key[1]), max(key[2], key[3]));
+    const uint32_t m = wave_max_u32(lm);
+    int sel = -1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c += __popcll(__ballot(valid[i] && key[i] >= cand));
-    if (c >= k) thr = cand;
-  }
-  int greater = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) greater += __popcll(__ballot(valid[i] && key[i] > thr));
-  const int need_eq = k - greater;
-  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-  int eq_before = 0, sel_before = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool eq = valid[i] && key[i] == thr;
-    const uint64_t eqm = __ballot(eq);
-    const bool sel = (valid[i] && key[i] > thr) || (eq && (eq_before + __popcll(eqm & lt)) < need_eq);
-    const uint64_t selm = __ballot(sel);
-    if (sel) {
-      const int slot = sel_before + __popcll(selm & lt);
-      s_v[slot] = v[i];
-      s_i[slot] = i * 64 + lane;
+    for (int i = 3; i >= 0; --i) {
+      const uint64_t b = __ballot(key[i] == m);
+      if (b) sel = i * 64 + __ffsll((unsigned long long)b) - 1;
     }
-    eq_before += __popcll(eqm);
-    sel_before += __popcll(selm);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = i * 64 + lane == sel ? 0u : key[i];
+    if (lane == 0) {
+      s_v[r] = fkey_value(m);
+      s_i[r] = sel;
+    }
   }
-  wave_fence_lds();
+  wave_lds_sync();
   if (lane < k) {
-    const float mv = s_v[lane];
-    const int mi = s_i[lane];
-    int rank = 0;
-    float vmax = mv;
-    for (int j = 0; j < k; ++j) {
-      const float ov = s_v[j];
-      const int oi = s_i[j];
-      rank += (ov > mv || (ov == mv && oi < mi)) ? 1 : 0;
-      vmax = fmaxf(vmax, ov);
-    }
-    float sum = 0.f;   // the same (expert) order in every lane
+    const float vmax = s_v[0];
+    float sum = 0.f;   // the same (slot) order in every lane
     for (int j = 0; j < k; ++j) sum += expf(s_v[j] - vmax);
-    const float wgt = expf(mv - vmax) / sum;
-    a.ids[(size_t)t * k + rank] = mi;
-    a.w[(size_t)t * k + rank] = wgt;
-    s_ids[t * k + rank] = mi;
-    s_ids[2 * kMaxT * 32 + t * k + rank] = __float_as_int(wgt);
+    const float wgt = expf(s_v[lane] - vmax) / sum;
+    const int mi = s_i[lane];
+    if (out) {
+      a.ids[(size_t)t * k + lane] = mi;
+      a.w[(size_t)t * k + lane] = wgt;
+    }
+    ids_out[t * k + lane] = mi;
+    wbits_out[t * k + lane] = __float_as_int(wgt);
   }
-  wave_fence_lds();
+  wave_lds_sync();
 }
 
+template <int P0>
 struct FinalizeLds {
-  int ids[3 * kMaxT * 32];   // [0, P) expert of each pair; [P0, P0 + P) pairs in sorted order;
-                             // [2 P0, 2 P0 + P) weight bits of each pair (P0 = kMaxT * 32)
+  int ids[3 * P0];           // [0, P) expert of each pair; [P0, P0 + P) pairs in sorted order;
+                             // [2 P0, 2 P0 + P) weight bits of each pair (P <= P0)
   float v[kNW][32];
   int i[kNW][32];
   int cnt[kMaxE];
   int base[kMaxE];
+  int ebase[kMaxE];          // first sorted position of each expert
+  int ubase[kMaxE];          // first unit of each expert
   uint8_t wc[kNW][kMaxE];
   int wsum[kNW * 4];
 };
 
 // Routing of all tokens by the last router workgroup (4 waves): top-k per token, stable
 // permutation of the pairs by expert (E <= 256: one expert per thread), work lists.
-__device__ void route_finalize(const DecodeArgs& a, FinalizeLds& L) {
+template <int P0>
+__device__ __forceinline__ void route_finalize(const DecodeArgs& a, FinalizeLds<P0>& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k, T = a.T, P = T * k;
-  constexpr int P0 = kMaxT * 32;
-  for (int t = wave; t < T; t += kNW) wave_topk(a, t, L.v[wave], L.i[wave], L.ids);
+  for (int t = wave; t < T; t += kNW) {
+    TopkIn in;
+    topk_load(a, t, in);
+    wave_topk(a, t, in, L.v[wave], L.i[wave], L.ids, L.ids + 2 * P0, true);
+  }
   if (tid < E) L.cnt[tid] = 0;
-  __syncthreads();
+  lds_barrier();
   for (int f = tid; f < P; f += kWG) atomicAdd(&L.cnt[L.ids[f]], 1);
-  __syncthreads();
+  lds_barrier();
   const int c = tid < E ? L.cnt[tid] : 0;
   const int n16 = (c + 15) / 16, n8 = (c + 7) / 8;
   int ic = c, iu = n16, ih = n8, ia = c > 0;
@@ -484,7 +539,7 @@ __device__ void route_finalize(const DecodeArgs& a, FinalizeLds& L) {
   if (lane == 63) {
     L.wsum[wave * 4] = ic; L.wsum[wave * 4 + 1] = iu; L.wsum[wave * 4 + 2] = ih; L.wsum[wave * 4 + 3] = ia;
   }
-  __syncthreads();
+  lds_barrier();
   int bc = 0, bu = 0, bh = 0, tu = 0, th = 0, ta = 0;
   for (int w2 = 0; w2 < kNW; ++w2) {
     if (w2 < wave) { bc += L.wsum[w2 * 4]; bu += L.wsum[w2 * 4 + 1]; bh += L.wsum[w2 * 4 + 2]; }
@@ -495,6 +550,8 @@ __device__ void route_finalize(const DecodeArgs& a, FinalizeLds& L) {
   const int h0 = bh + ih - n8;
   if (tid < E) {
     L.base[tid] = start;
+    L.ebase[tid] = start;
+    L.ubase[tid] = u0;
     a.offsets[tid] = start;
   }
   if (tid == 0) {
@@ -503,64 +560,78 @@ __device__ void route_finalize(const DecodeArgs& a, FinalizeLds& L) {
     a.wl[1] = tu;
     a.wl[2] = th;
   }
-  __syncthreads();
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-  for (int c0 = 0; c0 < P; c0 += kWG) {
-    for (int i = tid; i < kNW * kMaxE; i += kWG) L.wc[i / kMaxE][i % kMaxE] = 0;
-    __syncthreads();
-    const int f = c0 + tid;
-    const bool valid = f < P;
-    const int e = valid ? L.ids[f] : 0;
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t ones = __ballot(valid && bit);
-      peers &= bit ? ones : ~ones;
+  lds_barrier();
+  if (P <= kWG) {
+    // one thread per pair: its rank among the earlier pairs of its expert
+    if (tid < P) {
+      const int e = L.ids[tid];
+      int r = 0;
+      for (int f = 0; f < tid; ++f) r += L.ids[f] == e;
+      const int pos = L.base[e] + r;
+      a.sorted_pair[pos] = tid;
+      a.pair_pos[tid] = pos;
+      L.ids[P0 + pos] = tid;
     }
-    const int rank = __popcll(peers & lt);
-    if (valid && rank == 0) L.wc[wave][e] = (uint8_t)__popcll(peers);
-    __syncthreads();
-    if (valid) {
-      int pre = 0;
-      for (int w2 = 0; w2 < wave; ++w2) pre += L.wc[w2][e];
-      const int pos = L.base[e] + pre + rank;
-      a.sorted_pair[pos] = f;
-      a.pair_pos[f] = pos;
-      L.ids[P0 + pos] = f;
-    }
-    __syncthreads();
-    if (tid < E) {
-      int s = 0;
-      for (int w2 = 0; w2 < kNW; ++w2) s += L.wc[w2][tid];
-      L.base[tid] += s;
-    }
-    __syncthreads();
-  }
-  // unit u0 + q of expert tid covers sorted positions start + 16 q .. (<= 16 pairs);
-  // half-unit h0 + r covers start + 8 r .. (<= 8 pairs), i.e. half r % 2 of unit u0 + r / 2
-  if (tid < E) {
-    for (int q = 0; q < n16; ++q) {
-      const int n = min(16, c - 16 * q);
-      const int p0 = start + 16 * q;
-      a.ut[u0 + q] = make_int4(tid, p0, n, 0);
-      for (int j = 0; j < 16; ++j) {
-        const int f = L.ids[P0 + p0 + (j < n ? j : 0)];
-        a.utok[(u0 + q) * 16 + j] = f / k;
-        a.uw[(u0 + q) * 16 + j] = j < n ? __int_as_float(L.ids[2 * P0 + f]) : 0.f;
+  } else {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+    for (int c0 = 0; c0 < P; c0 += kWG) {
+      for (int i = tid; i < kNW * kMaxE; i += kWG) L.wc[i / kMaxE][i % kMaxE] = 0;
+      lds_barrier();
+      const int f = c0 + tid;
+      const bool valid = f < P;
+      const int e = valid ? L.ids[f] : 0;
+      uint64_t peers = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t ones = __ballot(valid && bit);
+        peers &= bit ? ones : ~ones;
       }
+      const int rank = __popcll(peers & lt);
+      if (valid && rank == 0) L.wc[wave][e] = (uint8_t)__popcll(peers);
+      lds_barrier();
+      if (valid) {
+        int pre = 0;
+        for (int w2 = 0; w2 < wave; ++w2) pre += L.wc[w2][e];
+        const int pos = L.base[e] + pre + rank;
+        a.sorted_pair[pos] = f;
+        a.pair_pos[f] = pos;
+        L.ids[P0 + pos] = f;
+      }
+      lds_barrier();
+      if (tid < E) {
+        int s2 = 0;
+        for (int w2 = 0; w2 < kNW; ++w2) s2 += L.wc[w2][tid];
+        L.base[tid] += s2;
+      }
+      lds_barrier();
     }
-    for (int r = 0; r < n8; ++r) a.hl[h0 + r] = 2 * (u0 + r / 2) + (r & 1);
+  }
+  lds_barrier();
+  // work lists: units (expert, <= 16 pairs) and half-units (<= 8 pairs); each pair writes
+  // its own token / weight slot, slots past a unit's last pair are left as they are (the
+  // readers clamp to the last pair)
+  if (tid < E) {
+    for (int q = 0; q < n16; ++q) a.ut[u0 + q] = make_int4(tid, start + 16 * q, min(16, c - 16 * q), 0);
+    for (int r = 0; r < n8; ++r)
+      a.hl[h0 + r] = make_int4(tid, start + 8 * r, min(8, c - 8 * r), (u0 + r / 2) * 16 + 8 * (r & 1));
+  }
+  for (int pos = tid; pos < P; pos += kWG) {
+    const int f = L.ids[P0 + pos];
+    const int e = L.ids[f];
+    const int rel = pos - L.ebase[e];
+    const int slot = (L.ubase[e] + rel / 16) * 16 + rel % 16;
+    a.utok[slot] = f / k;
+    a.uw[slot] = __int_as_float(L.ids[2 * P0 + f]);
   }
 }
 
-
-template <int HB>
+template <int HB, int P0>
 __global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
   __shared__ __align__(16) float s_red[kNW][4][64];
   __shared__ int s_last;
-  __shared__ FinalizeLds s_fin;
+  __shared__ FinalizeLds<P0> s_fin;
   router_unit<HB>(a, blockIdx.x, s_red);
   if (threadIdx.x < 64) {
     __threadfence();     // wave 0 wrote this workgroup's partial: publish it device-wide
@@ -573,13 +644,16 @@ __global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
   if (threadIdx.x == 0) a.ctr[0] = 0;
 }
 
+// ---------------------------------------------------------------------------- small T
+constexpr int kMaxPL = kXT * 32;   // pairs of a small-T layer (k <= 32)
+
 // ============================================================================ K2
 // Routed gate/up: a workgroup takes one unit (expert, <= 16 pairs) and 32 rows of I; wave
 // = (16-row tile, gate|up) over all of K; the gate and up waves of a tile meet in LDS and
 // the gate wave writes h = SiLU(gate) * up as bf16 hi + lo.  Units of up to kXT tokens read
 // their x rows from LDS.
 template <int HB, int IB, int XR, bool MEM>
-__device__ void routed_gateup(const DecodeArgs& a, int wi, const uint2* s_lut, uint16_t* s_x,
+__device__ __forceinline__ void routed_gateup(const DecodeArgs& a, int wi, const uint2* s_lut, uint16_t* s_x,
                               float (*s_red)[2][4][64]) {
   constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -628,7 +702,7 @@ __device__ void routed_gateup(const DecodeArgs& a, int wi, const uint2* s_lut, u
 // streamed in 16-byte chunks per lane (chunk c: K = 8 l + 512 c for lane l) with the next
 // chunk of both matrices in flight while one is reduced.
 template <int HB, int IB, int XR>
-__device__ void shared_gateup_valu(const DecodeArgs& a, int sw, uint16_t* s_x) {
+__device__ __forceinline__ void shared_gateup_valu(const DecodeArgs& a, int sw, uint16_t* s_x) {
   constexpr int H = HB * 256, I = IB * 256, NJ = H / 512, RS = NJ < 2 ? NJ : 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T;
@@ -676,7 +750,7 @@ __device__ void shared_gateup_valu(const DecodeArgs& a, int sw, uint16_t* s_x) {
 
 // Shared gate/up beyond kXT tokens: 16 rows x 16 tokens, the 4 waves split K.
 template <int HB, int IB>
-__device__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2][4][64]) {
+__device__ __forceinline__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2][4][64]) {
   constexpr int H = HB * 256, I = IB * 256, n_rt = I / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rt = sw % n_rt, tt = sw / n_rt;
@@ -718,40 +792,42 @@ __device__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2
   }
 }
 
-template <int HB, int IB, int XR, bool SMALL>
+// Large T, second kernel: routed gate/up (units of up to kXT tokens stage their x rows)
+// beside the shared expert's gate/up on the MFMA.
+template <int HB, int IB>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k2_gateup(DecodeArgs a) {
+  constexpr int XR = kXT;
   extern __shared__ __align__(16) uint16_t s_x[];   // x rows: XR x H bf16
   __shared__ uint2 s_lut[32];
   __shared__ __align__(16) float s_red[2][2][4][64];
   const int b = blockIdx.x;
   if (b >= a.n_gu_wg) {
-    if constexpr (SMALL) shared_gateup_valu<HB, IB, XR>(a, b - a.n_gu_wg, s_x);
-    else shared_gateup_mfma<HB, IB>(a, b - a.n_gu_wg, reinterpret_cast<float(*)[2][4][64]>(&s_red[0][0][0][0]));
+    shared_gateup_mfma<HB, IB>(a, b - a.n_gu_wg, reinterpret_cast<float(*)[2][4][64]>(&s_red[0][0][0][0]));
     return;
   }
   build_lut(s_lut);
   __syncthreads();
   const int n_items = a.wl[1] * (IB * 256 / 32);
   for (int wi = b; wi < n_items; wi += a.n_gu_wg)
-    routed_gateup<HB, IB, XR, !SMALL>(a, wi, s_lut, s_x, s_red);
+    routed_gateup<HB, IB, XR, true>(a, wi, s_lut, s_x, s_red);
 }
 
-// ============================================================================ K3
-// Shared down for up to kXT tokens: wave w takes rows row0 + 2w, +1, streamed in 16-byte
-// chunks per lane (chunk j: K = 8 l + 512 j for lane l; the last chunk is half-used when I
-// is an odd multiple of 256), R chunks in flight; h comes as bf16 hi + lo from `hs` (LDS or
-// memory).  Each result is added into the wave's LDS sums and written to y_shared.
-template <int HB, int IB>
+// Shared down for up to kXT tokens: wave w takes NR consecutive rows from row0 + NR w,
+// streamed in 16-byte chunks per lane (chunk j: K = 8 l + 512 j for lane l; the last chunk
+// is half-used when I is an odd multiple of 256), R chunks in flight; h comes as bf16
+// hi + lo rows from `hs` (LDS).  Writes y_shared and, with ACC, adds it into the wave's
+// combine sums (a 16-row slice: row NR w + r of the slice).
+template <int HB, int IB, int NR, bool ACC>
 struct SharedDown {
-  static constexpr int H = HB * 256, I = IB * 256, NJ = (IB + 1) / 2, NI = 2 * NJ, R = NI < 4 ? NI : 4;
+  static constexpr int H = HB * 256, I = IB * 256, NJ = (IB + 1) / 2, NI = NR * NJ, R = NI < 4 ? NI : 4;
   uint4 w[R];
   rsrc_t rsd;
-  uint32_t rb;       // byte offset of this wave's first row at this lane's K
+  uint32_t rb;       // byte offset of this wave's first row
   int lcol;
   bool last_ok;
 
   __device__ __forceinline__ uint4 load(int it) const {
-    const int j = it >> 1, r = it & 1;
+    const int j = it / NR, r = it % NR;
     const uint32_t cl = j == NJ - 1 ? lcol : (threadIdx.x & 63);
     return bload16(rsd, rb + 2u * (r * I + 8 * cl), 2 * 512 * j);
   }
@@ -760,7 +836,7 @@ struct SharedDown {
     last_ok = (IB % 2 == 0) || lane < 32;
     lcol = last_ok ? lane : 0;
     rsd = make_rsrc(a.sd, a.sd ? (uint32_t)H * I * 2 : 0u);
-    rb = 2u * (uint32_t)(row0 + 2 * wave) * I;
+    rb = 2u * (uint32_t)(row0 + NR * wave) * I;
 #pragma unroll
     for (int it = 0; it < R; ++it) w[it] = load(it);
   }
@@ -768,16 +844,16 @@ struct SharedDown {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int T = a.T;
     const size_t lo = (size_t)T * I;
-    float acc[2][kXT];
+    float acc[NR][kXT];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int t = 0; t < kXT; ++t) acc[r][t] = 0.f;
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const uint4 wv = w[it % R];
       if (it + R < NI) w[it % R] = load(it + R);
-      const int j = it >> 1, r = it & 1;
+      const int j = it / NR, r = it % NR;
       const int cl = j == NJ - 1 ? lcol : lane;
 #pragma unroll
       for (int t = 0; t < kXT; ++t) {
@@ -794,12 +870,11 @@ struct SharedDown {
     for (int t = 0; t < kXT; ++t) {
       if (t < T) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < NR; ++r) {
           const float v = wave_sum(acc[r][t]);
           if (lane == 0) {
-            const int rr = 2 * wave + r;
-            s_acc[(wave * T + t) * 16 + rr] += v;
-            a.y_shared[(size_t)t * H + row0 + rr] = v;
+            a.y_shared[(size_t)t * H + row0 + NR * wave + r] = v;
+            if constexpr (ACC) s_acc[(wave * T + t) * 16 + NR * wave + r] += v;
           }
         }
       }
@@ -807,11 +882,69 @@ struct SharedDown {
   }
 };
 
+// ============================================================================ K3
+// Routed gate/up of one work item (unit, 32 rows of I) of a small-T layer, every token's x
+// row already in LDS; as routed_gateup otherwise.
+template <int HB, int IB>
+__device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi, const uint2* s_lut,
+                                                    const uint16_t* s_x, float (*s_red)[2][4][64]) {
+  constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int un_i = wi / NTP, tp = wi % NTP;
+  const int4 un = a.ut[un_i];
+  const int e = un.x, pos0 = un.y, ntok = un.z;
+  const int mat = wave & 1, tl = wave >> 1;
+  const int row0 = (2 * tp + tl) * 16;
+  const size_t wrow = (size_t)e * I + row0 + col;
+  StqStream<HB, 8> st;
+  st.issue((mat ? a.uc : a.gc) + wrow * HB * 40, (mat ? a.us : a.gs) + wrow * HB);
+  const int tok = a.utok[un_i * 16 + (col < ntok ? col : ntok - 1)];
+  const f32x4_t acc = st.run_lds(s_lut, s_x + tok * H + 64 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_red[tl][mat][i][lane] = acc[i];
+  __syncthreads();
+  if (mat == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = 4 * g + i;
+      if (slot < ntok)
+        store_hilo(a.h_hi + (size_t)(pos0 + slot) * I + row0 + col, a.h_lo_bytes / 2,
+                   silu_mul(s_red[tl][0][i][lane], s_red[tl][1][i][lane]));
+    }
+  }
+  __syncthreads();   // s_red is reused by the next work item
+}
+
+// Small T, second kernel: routed gate/up (units from the routing tables, every token's x
+// row staged in LDS while they are read) beside the shared expert's gate/up.  Nothing in
+// it waits on a chain of dependent loads longer than one round trip.
+template <int HB, int IB, int XR>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(5))) void k2s_gateup(DecodeArgs a) {
+  constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
+  extern __shared__ __align__(16) uint16_t s_x[];   // XR x rows
+  __shared__ uint2 s_lut[32];
+  __shared__ __align__(16) float s_red[2][2][4][64];
+  const int b = blockIdx.x;
+  const int T = a.T;
+  if (b >= a.n_gu_wg) {
+    shared_gateup_valu<HB, IB, XR>(a, b - a.n_gu_wg, s_x);
+    return;
+  }
+  RowStage<H, kWG, XR> xs;
+  xs.issue(T, [&](int r) { return a.x + (size_t)r * H; });
+  build_lut(s_lut);
+  const int n_items = a.wl[1] * NTP;
+  xs.commit(T, s_x);
+  lds_barrier();
+  for (int wi = b; wi < n_items; wi += a.n_gu_wg) routed_gateup_small<HB, IB>(a, wi, s_lut, s_x, s_red);
+}
+
 // Shared down beyond kXT tokens: 16 rows x 16-token tiles; wave w takes K blocks w, w + 8,
 // .. (A = h hi and lo rows, B = weights); the waves' partials meet in LDS (s_red) in order,
 // wave 0 writes y_shared and adds it into its own sums.
 template <int HB, int IB>
-__device__ void shared_down_mfma(const DecodeArgs& a, int row0, float* s_acc, float* s_red) {
+__device__ __forceinline__ void shared_down_mfma(const DecodeArgs& a, int row0, float* s_acc, float* s_red) {
   constexpr int H = HB * 256, I = IB * 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
@@ -851,14 +984,17 @@ __device__ void shared_down_mfma(const DecodeArgs& a, int row0, float* s_acc, fl
   }
 }
 
-// One 16-row slice of the output: the shared expert's rows, then every half-unit
-// (expert, <= 8 pairs) spread over the 8 waves, each wave adding w * y into its own LDS
-// sums; out = sum over waves in order (+ residual).  When all h fits (few pairs), it is
-// staged in LDS first: routed hi rows, routed lo rows, shared hi, shared lo.
-template <int HB, int IB, bool SMALL, bool HLDS>
+// One 16-row slice of the output: the shared expert's down projection (SDN: MFMA over
+// 16-token tiles, large T; otherwise 2 rows per wave on the VALU) and every half-unit
+// (expert, <= 8 pairs) spread over the 8 waves, each wave adding its results into its own
+// LDS sums; out = sum over waves in order (+ residual).  HLDS: all h (few tokens) is staged
+// in LDS first: routed hi rows, routed lo rows, shared hi rows, shared lo rows.
+template <int HB, int IB, bool SDN, bool HLDS>
 __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   constexpr int H = HB * 256, I = IB * 256;
   constexpr int kStage = 9;                  // uint4 per thread when h is staged
+  constexpr int kLoPad = 32;                 // lo rows start 64 bytes past the hi rows' end so a
+                                             // pair's hi and lo reads fall in different banks
   extern __shared__ __align__(16) float s_dyn[];  // [kDnWaves][T][16] sums, then staged h
                                                   // or the shared partials [kDnWaves][4][64]
   __shared__ uint2 s_lut[32];
@@ -868,7 +1004,6 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   const int col = lane & 15, g = lane >> 4;
   float* s_acc = s_dyn;
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn + kDnWaves * T * 16);
-  constexpr bool h_lds = HLDS;
   // residual of this slice (T * 16 <= 1024 elements, two per thread), read up front
   const rsrc_t rres = make_rsrc(a.residual, a.residual ? (uint32_t)T * H * 4 : 0u);
   float rs[2];
@@ -878,75 +1013,72 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
     const uint32_t o = i < T * 16 ? 4u * ((uint32_t)(i >> 4) * H + row0 + (i & 15)) : kOOB;
     rs[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rres, o, 0, 0));
   }
-  // staged h: uint4 i < P*I/8 from h hi, then h lo, then shared hi + lo
+  // staged h: uint4 i < P*I/8 from h hi, then as many from h lo, then the shared h
   const int n_rh = P * I / 8, n_all = 2 * n_rh + T * I / 4;
   uint4 hv[kStage];
-  if constexpr (h_lds) {
+  if constexpr (HLDS) {
 #pragma unroll
     for (int m = 0; m < kStage; ++m) {
       int i = tid + 64 * kDnWaves * m;
       i = i < n_all ? i : 0;
-      const uint4* src = i < n_rh ? reinterpret_cast<const uint4*>(a.h_hi) + i
-                       : i < 2 * n_rh ? reinterpret_cast<const uint4*>(a.h_hi + a.h_lo_bytes / 2) + (i - n_rh)
-                       : reinterpret_cast<const uint4*>(a.hs) + (i - 2 * n_rh);
-      hv[m] = *src;
+      hv[m] = i < n_rh ? reinterpret_cast<const uint4*>(a.h_hi)[i]
+            : i < 2 * n_rh ? reinterpret_cast<const uint4*>(a.h_hi + a.h_lo_bytes / 2)[i - n_rh]
+            : reinterpret_cast<const uint4*>(a.hs)[i - 2 * n_rh];
     }
-  }
-  // shared rows' weights (zeros without a shared expert)
-  SharedDown<HB, IB> sdn;
-  if constexpr (SMALL) sdn.issue(a, row0);
-  // first half-unit's code words (a wave without one streams the last half-unit's, unused)
-  const int n_half = a.wl[2];
-  StqStream<IB> st;
-  int hu = wave;
-  int ent = a.hl[hu < n_half ? hu : n_half - 1];
-  int4 un = a.ut[ent >> 1];
-  {
-    const size_t wrow = (size_t)un.x * H + row0 + col;
-    st.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
   }
   build_lut(s_lut);
   for (int i = tid; i < kDnWaves * T * 16; i += 64 * kDnWaves) s_acc[i] = 0.f;
-  if constexpr (h_lds) {
+  // the staged rows land before any weight load is issued: otherwise they would queue
+  // behind every workgroup's weight stream
+  if constexpr (HLDS) {
 #pragma unroll
     for (int m = 0; m < kStage; ++m) {
       const int i = tid + 64 * kDnWaves * m;
-      if (i < n_all) reinterpret_cast<uint4*>(s_h)[i] = hv[m];
+      if (i < n_all) reinterpret_cast<uint4*>(s_h + (i < n_rh ? 0 : kLoPad))[i] = hv[m];
     }
+  }
+  // the shared rows' first weight chunks
+  SharedDown<HB, IB, 2, true> sdn;
+  if constexpr (!SDN) sdn.issue(a, row0);
+  // first half-unit's code words, read beside the half-unit count (a wave without a
+  // half-unit streams some valid expert's rows, unused)
+  const int n_half = a.wl[2];
+  StqStream<IB, 8> st;
+  int hu = wave;
+  int4 hent = a.hl[wave < a.max_half ? wave : a.max_half - 1];
+  {
+    const int e0 = min(max(hent.x, 0), a.E - 1);
+    const size_t wrow = (size_t)e0 * H + row0 + col;
+    st.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
   }
   lds_barrier();
   if (a.sd) {
-    if constexpr (SMALL) {
-      if constexpr (h_lds) sdn.run(a, row0, s_h + 2 * P * I, s_acc);
-      else sdn.run(a, row0, a.hs, s_acc);
-    } else {
-      shared_down_mfma<HB, IB>(a, row0, s_acc, s_dyn + kDnWaves * T * 16);
-    }
+    if constexpr (SDN) shared_down_mfma<HB, IB>(a, row0, s_acc, s_dyn + kDnWaves * T * 16);
+    else if constexpr (HLDS) sdn.run(a, row0, s_h + 2 * P * I + kLoPad, s_acc);
+    else sdn.run(a, row0, a.hs, s_acc);
   }
   const rsrc_t rh = make_rsrc(a.h_hi, a.h_bytes);
   const int sp2 = col >> 1;
   for (; hu < n_half; hu += kDnWaves) {
     if (hu != wave) {
-      ent = a.hl[hu];
-      un = a.ut[ent >> 1];
-      const size_t wrow = (size_t)un.x * H + row0 + col;
+      hent = a.hl[hu];
+      const size_t wrow = (size_t)hent.x * H + row0 + col;
       st.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
     }
-    const int un_i = ent >> 1, half = ent & 1;
-    const int pos0 = un.y + 8 * half;
-    const int n8 = min(8, un.z - 8 * half);
+    const int pos0 = hent.y, n8 = hent.z;
     // this lane's two result pairs (2g, 2g+1): token and routing weight
     int tk[2];
     float wt[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      tk[m] = a.utok[un_i * 16 + 8 * half + 2 * g + m];
-      wt[m] = a.uw[un_i * 16 + 8 * half + 2 * g + m];
+      const int p = min(2 * g + m, n8 - 1);
+      tk[m] = a.utok[hent.w + p];
+      wt[m] = a.uw[hent.w + p];
     }
     f32x4_t acc;
-    if constexpr (h_lds) {
+    if constexpr (HLDS) {
       const int pr = pos0 + (sp2 < n8 ? sp2 : 0);
-      acc = st.run_lds(s_lut, s_h + (col & 1) * P * I + pr * I + 64 * g);
+      acc = st.run_lds(s_lut, s_h + (col & 1) * (P * I + kLoPad) + pr * I + 64 * g);
     } else {
       const uint32_t ho = sp2 < n8 ? (col & 1 ? a.h_lo_bytes : 0u) + 2u * ((uint32_t)(pos0 + sp2) * I + 64 * g) : kOOB;
       acc = st.run_mem(s_lut, rh, ho);
@@ -978,8 +1110,38 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   }
 }
 
-template <int HB, int IB, int XR, bool SMALL>
-hipError_t launch_all(DecodeArgs& a, hipStream_t s) {
+// Small T: router + routing; routed + shared gate/up; routed + shared down + combine.
+template <int HB, int IB, int XR>
+hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
+  constexpr int H = HB * 256, I = IB * 256;
+  const int T = a.T;
+  const int P = T * a.k;
+  const int max_units = (P < a.E ? P : a.E) + (P + 15) / 16;
+  const bool shared = a.sg != nullptr;
+  a.n_router_wg = ((a.E + 15) / 16) * kRouterParts;
+  a.n_sgu_wg = shared ? I / kNW : 0;
+  a.n_gu_wg = max_units * (I / 32);
+  a.h_lds = (P + T) * I <= 9 * 64 * kDnWaves * 4 ? 1 : 0;
+  const size_t lds2 = (size_t)XR * H * 2;
+  const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (a.h_lds ? (size_t)(P + T) * I * 4 + 64 : 0);
+  const bool prof = moe_prof_on();
+  if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
+  hipLaunchKernelGGL((k1_route<HB, kMaxPL>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
+  hipLaunchKernelGGL((k2s_gateup<HB, IB, XR>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(kWG), lds2, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
+  if (a.h_lds) hipLaunchKernelGGL((k3_down_combine<HB, IB, false, true>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  else hipLaunchKernelGGL((k3_down_combine<HB, IB, false, false>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
+  return hipSuccess;
+}
+
+// Large T: router + routing (ticket), routed + shared gate/up, all down + combine.
+template <int HB, int IB>
+hipError_t launch_large(DecodeArgs& a, hipStream_t s) {
   constexpr int H = HB * 256, I = IB * 256;
   const int T = a.T;
   const int n_tt = (T + 15) / 16;
@@ -987,24 +1149,22 @@ hipError_t launch_all(DecodeArgs& a, hipStream_t s) {
   const int max_units = (P < a.E ? P : a.E) + (P + 15) / 16;
   a.n_router_wg = ((a.E + 15) / 16) * kRouterParts * n_tt;
   const bool shared = a.sg != nullptr;
-  a.n_sgu_wg = shared ? (SMALL ? I / kNW : (I / 16) * n_tt) : 0;
+  a.n_sgu_wg = shared ? (I / 16) * n_tt : 0;
   const int cap = 8192;
   const int gu = max_units * (I / 32);
   a.n_gu_wg = gu < cap ? gu : cap;
-  a.h_lds = P <= kHLdsPairs && SMALL && (P + T) * I <= 9 * 64 * kDnWaves * 4 ? 1 : 0;
-  const size_t lds2 = (size_t)XR * H * 2;
-  const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (a.h_lds ? (size_t)(P + T) * I * 4 : 0) +
-                      (SMALL ? 0 : (size_t)kDnWaves * 4 * 64 * 4);
+  a.h_lds = 0;
+  const size_t lds2 = (size_t)kXT * H * 2;
+  const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (size_t)kDnWaves * 4 * 64 * 4;
   const bool prof = moe_prof_on();
   if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
-  hipLaunchKernelGGL((k1_route<HB>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
+  hipLaunchKernelGGL((k1_route<HB, kMaxT * 32>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
-  hipLaunchKernelGGL((k2_gateup<HB, IB, XR, SMALL>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(kWG), lds2, s, a);
+  hipLaunchKernelGGL((k2_gateup<HB, IB>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(kWG), lds2, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
-  if (a.h_lds) hipLaunchKernelGGL((k3_down_combine<HB, IB, SMALL, true>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
-  else hipLaunchKernelGGL((k3_down_combine<HB, IB, SMALL, false>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  hipLaunchKernelGGL((k3_down_combine<HB, IB, true, false>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
   return hipSuccess;
@@ -1012,10 +1172,10 @@ hipError_t launch_all(DecodeArgs& a, hipStream_t s) {
 
 template <int HB, int IB>
 hipError_t launch_shape(DecodeArgs& a, hipStream_t s) {
-  if (a.T == 1) return launch_all<HB, IB, 1, true>(a, s);
-  if (a.T == 2) return launch_all<HB, IB, 2, true>(a, s);
-  if (a.T <= kXT) return launch_all<HB, IB, kXT, true>(a, s);
-  return launch_all<HB, IB, kXT, false>(a, s);
+  if (a.T == 1) return launch_small<HB, IB, 1>(a, s);
+  if (a.T == 2) return launch_small<HB, IB, 2>(a, s);
+  if (a.T <= kXT) return launch_small<HB, IB, kXT>(a, s);
+  return launch_large<HB, IB>(a, s);
 }
 
 }  // namespace
@@ -1040,7 +1200,7 @@ size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, s
   offs[1] = cur; cur = al(cur + max_units * sizeof(int4));                          // unit table
   offs[2] = cur; cur = al(cur + max_units * 16 * sizeof(int32_t));                  // unit tokens
   offs[3] = cur; cur = al(cur + max_units * 16 * sizeof(float));                    // unit weights
-  offs[4] = cur; cur = al(cur + max_half * sizeof(int32_t));                        // half-units
+  offs[4] = cur; cur = al(cur + max_half * sizeof(int4));                           // half-units
   offs[5] = cur; cur = al(cur + (size_t)kRouterParts * T * E * sizeof(float));     // router partials
   offs[6] = cur; cur = al(cur + P * I * 2);                                          // h hi
   offs[7] = cur; cur = al(cur + P * I * 2);                                          // h lo
@@ -1078,7 +1238,11 @@ hipError_t moe_launch_decode_fused(const moe_dims* d, const moe_experts* routed,
   a.ut = reinterpret_cast<int4*>(b + offs[1]);
   a.utok = reinterpret_cast<int32_t*>(b + offs[2]);
   a.uw = reinterpret_cast<float*>(b + offs[3]);
-  a.hl = reinterpret_cast<int32_t*>(b + offs[4]);
+  a.hl = reinterpret_cast<int4*>(b + offs[4]);
+  {
+    const int P = d->T * d->k;
+    a.max_half = (P < d->E ? P : d->E) + (P + 7) / 8;
+  }
   a.rpart = reinterpret_cast<float*>(b + offs[5]);
   a.h_hi = reinterpret_cast<uint16_t*>(b + offs[6]);
   a.h_lo_bytes = (uint32_t)(offs[7] - offs[6]);
