@@ -321,7 +321,7 @@ static bool decode_fused_ok(const moe_dims* d) {
 moe_status moe_layer_decode_workspace_size(const moe_dims* d, int32_t has_shared, size_t* bytes) {
   if (!dims_ok(d) || !bytes) return MOE_ERR_INVALID_ARG;
   if (!decode_fused_ok(d)) return MOE_ERR_UNSUPPORTED;
-  size_t offs[10];
+  size_t offs[16];
   *bytes = moe_decode_ws_layout(d->T, d->H, d->I, d->E, d->k, has_shared != 0, offs);
   return MOE_OK;
 }
@@ -345,7 +345,7 @@ moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
       return MOE_ERR_INVALID_ARG;
   }
   if (!decode_fused_ok(d)) return MOE_ERR_UNSUPPORTED;
-  size_t offs[10];
+  size_t offs[16];
   const size_t need = moe_decode_ws_layout(d->T, d->H, d->I, d->E, d->k, shared != nullptr, offs);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (d->T == 0) return MOE_OK;
