@@ -38,10 +38,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--copies", type=int, default=6, help="layer copies the decode steps rotate over")
+    p.add_argument("--copies", type=int, default=8, help="layer copies the decode steps rotate over")
     p.add_argument("--prefill-steps", type=int, default=5)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="first run a plain copy kernel (torch.neg) over this many MiB, three times, "
+                        "as the reference dispatch for the HBM byte counters")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU: summarise two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) "
+                        "of this script into a markdown table with the per-launch HBM traffic")
     return p.parse_args()
 
 
@@ -148,9 +154,14 @@ def decode_bench(args):
     x_b = c.H * 2
     # algorithmic bytes per launch of each kernel: weights + activations read + results written
     kb = {
-        "decode_k1_route_shared_gateup": router_b + shared_gu_b + x_b + c.I * 4,
-        "decode_k2_gateup_shared_down": routed_gu_b + shared_dn_b + x_b + c.k * c.I * 4 + c.I * 4 + c.H * 4,
-        "decode_k3_down_combine": routed_dn_b + c.k * c.I * 4 + c.k * c.H * 4 + c.H * 4 + c.H * 4,
+        # router GEMV + top-k + permutation: router weights, x, logits / ids / weights out
+        "decode_k1_route": router_b + x_b + c.E * 4 + c.k * 8 + (2 * c.k + c.E + 1) * 4,
+        # routed and shared gate/up: the 8 touched experts' gate/up, the shared gate/up, x in,
+        # h out (fp32 for the routed pairs and the shared expert)
+        "decode_k2_gateup": routed_gu_b + shared_gu_b + x_b + c.k * c.I * 4 + c.I * 4,
+        # routed and shared down + weighted combine: down weights, h in, y_pairs / y_shared / out
+        "decode_k3_down_combine": routed_dn_b + shared_dn_b + c.k * c.I * 4 + c.I * 4
+                                  + c.k * c.H * 4 + c.H * 4 + c.H * 4,
     }
     expert_b = routed_gu_b + routed_dn_b + shared_gu_b + shared_dn_b
     layer_b = expert_b + router_b + x_b + c.H * 4
@@ -202,6 +213,79 @@ def prefill_bench(args):
     return dict(c=c, routed_ms=r_ms, flops=flops, tflops=flops / (r_ms * 1e-3) / 1e12, prof=prof)
 
 
+TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
+    "decode_k1_route": "k1_route", "decode_k2_gateup": "k2s_gateup",
+    "decode_k3_down_combine": "k3_down_combine", "mx_gateup": "mx_gemm_kernel<true>",
+    "mx_down": "mx_gemm_kernel<false>", "copy": "neg_kernel"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hy4_t1_hbm_traffic.md")
+_DEC_SRC = "bit_quantized_moe_softmax_amd/csrc/decode_fused.hip"
+_MX_SRC = "bit_quantized_moe_softmax_amd/csrc/mx_gemm.hip"
+TRAFFIC_SOURCES = {"decode_k1_route": _DEC_SRC, "decode_k2_gateup": _DEC_SRC,
+                   "decode_k3_down_combine": _DEC_SRC, "mx_gateup": _MX_SRC, "mx_down": _MX_SRC}
+
+
+def source_hash(slot):
+    """First 16 hex digits of the sha256 of the source file that holds the slot's kernel."""
+    import hashlib
+    return hashlib.sha256(open(os.path.join(ROOT, TRAFFIC_SOURCES[slot]), "rb").read()).hexdigest()[:16]
+
+
+def pmc_summary(fetch_dir, write_dir, copy_mib):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by what the same
+    counters read for a plain copy of known size."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        acc = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                for slot, sub in TRAFFIC_KERNELS.items():
+                    if sub in r["Kernel_Name"]:
+                        acc.setdefault(slot, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    fe, nf = load(fetch_dir, "FETCH_SIZE")
+    wr, nw = load(write_dir, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    f_fac = fe["copy"] / copy_kib
+    w_fac = wr["copy"] / copy_kib
+    rows = {}
+    for slot in TRAFFIC_KERNELS:
+        if slot == "copy" or slot not in fe or slot not in wr:
+            continue
+        b = (fe[slot] / f_fac + wr[slot] / w_fac) * 1024.0
+        rows[slot] = {"fetch_kib": round(fe[slot], 1), "write_kib": round(wr[slot], 1),
+                      "dispatches": [nf[slot], nw[slot]], "traffic_bytes": round(b),
+                      "source_sha256_16": source_hash(slot)}
+    data = {"copy_mib": copy_mib,
+            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "kernels": rows}
+    print("| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | dispatches | HBM traffic B/launch (scaled) |")
+    print("|---|---|---|---|---|")
+    for slot, r in rows.items():
+        print(f"| {slot} | {r['fetch_kib']} | {r['write_kib']} | {r['dispatches'][0]} / {r['dispatches'][1]} "
+              f"| {r['traffic_bytes']} |")
+    print(f"\nCopy calibration: {copy_mib} MiB read and written by torch.neg; FETCH_SIZE reads "
+          f"{f_fac:.4f}x and WRITE_SIZE {w_fac:.4f}x the bytes moved.\n")
+    print("traffic-json: " + json.dumps(data))
+
+
+def load_traffic():
+    """Per-launch HBM traffic from the committed counter summary, or {} when the kernels' sources
+    changed after the counters were taken."""
+    try:
+        for line in open(TRAFFIC_FILE):
+            if line.startswith("traffic-json: "):
+                data = json.loads(line[len("traffic-json: "):])
+                return {k: v["traffic_bytes"] for k, v in data["kernels"].items()
+                        if v["source_sha256_16"] == source_hash(k)}
+    except OSError:
+        pass
+    return {}
+
+
 def cpu_baseline(args):
     """The oracle as it stands, one thread, on one batch-1 layer call (bounded sample)."""
     import numpy as np
@@ -217,26 +301,43 @@ def cpu_baseline(args):
     sh = synth.shared_weights(c.seed, 0, c.I, c.H)
     shapes = [(c.I, c.H), (c.I, c.H), (c.H, c.I)]
 
+    gen_s = [0.0]   # time spent generating the synthetic packed weights (not oracle work)
+
     def get_w(e, m):
         n = shapes[m][0] * shapes[m][1]
+        t = time.perf_counter()
         codes, scales = synth.stq1_matrix(c.seed, 0, e, m, n)
+        gen_s[0] += time.perf_counter() - t
         return O.stq1_matrix(codes, scales, *shapes[m])
 
     import contextlib
-    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
+    xs = synth.activations(c.seed, 1, 16, c.H)
+    n = 0
     with ctx:
         t0 = time.perf_counter()
-        O.moe_layer(x, c.k, get_w, "stq1", wr_bits=wr, shared=sh)
-        dt = time.perf_counter() - t0
+        # one layer call per token, on fresh tokens, until about 10 s of work (at most 16 calls)
+        while n < 16 and (n == 0 or time.perf_counter() - t0 < 10.0):
+            O.moe_layer(x if n == 0 else xs[n:n + 1], c.k, get_w, "stq1", wr_bits=wr, shared=sh)
+            n += 1
+        dt = (time.perf_counter() - t0 - gen_s[0]) / n
     expert_b = c.k * 3 * STQ_MAT_BYTES + 3 * c.I * c.H * 2
-    return dict(value=expert_b / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample="one batch-1 Hy4 STQ1_0 layer call (route, 8 routed experts decoded and "
-                       "applied in float64, shared expert, combine), single thread, "
-                       f"{dt:.1f} s")
+    return dict(value=expert_b / dt / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{n} batch-1 Hy4 STQ1_0 layer calls on fresh tokens (route, 8 routed experts "
+                       f"decoded and applied in float64, shared expert, combine), {cores} BLAS threads, "
+                       f"{dt:.2f} s per call without the synthetic weight generation; value = expert-weight "
+                       f"bytes per call / time per call")
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, args.calibrate_copy_mib)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the multi-GPU expert-parallel path is a design, not code)"}))
@@ -245,6 +346,15 @@ def main():
     import bit_quantized_moe_softmax_amd as M
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     M.lib()
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    traffic = load_traffic()
     dec = decode_bench(args)
     c = dec["c"]
     value = dec["expert_b"] / (dec["ms"] * 1e-3) / 1e9
@@ -279,7 +389,8 @@ def main():
         "bytes_per_step": {"routed": dec["routed_b"], "shared": dec["shared_b"],
                            "router": dec["router_b"], "layer_total": dec["layer_b"]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dk["gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(dk["gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic.get(dom), "algorithmic_bytes": dk["algorithmic_bytes"]},
     }
     if not args.no_prefill:
         try:
@@ -299,7 +410,8 @@ def main():
                               "roofline": {"bound": "mfma", "kernel": "mx_gateup",
                                            "achieved": pk["mx_gateup"]["tflops"], "peak": FP8_PEAK_TFLOPS,
                                            "unit": "TFLOP/s",
-                                           "frac": round((pk["mx_gateup"]["tflops"] or 0) / FP8_PEAK_TFLOPS, 4)}}
+                                           "frac": round((pk["mx_gateup"]["tflops"] or 0) / FP8_PEAK_TFLOPS, 4),
+                                           "traffic": traffic.get("mx_gateup")}}
         except Exception as e:  # the decode line must still print
             out["prefill"] = {"error": repr(e)}
     if not args.no_cpu_baseline:

@@ -20,7 +20,7 @@ __all__ = [
     "moe_profile_enable", "moe_profile_read", "PROFILE_SLOTS",
 ]
 
-PROFILE_SLOTS = ["decode_k1_route_shared_gateup", "decode_k2_gateup_shared_down",
+PROFILE_SLOTS = ["decode_k1_route", "decode_k2_gateup",
                  "decode_k3_down_combine", "reserved3", "mx_quant", "mx_gateup", "mx_down"]
 
 MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16 = 1, 2, 3

@@ -7,13 +7,19 @@
 // FP8 E4M3 activations (g32).  Every routed linear takes E4M3 activations, so h is
 // MX-quantised along I before the down projection.
 //
-// Tiling.  A workgroup (4 waves, 2 x 2) owns up to 128 routed pairs of one expert (the
-// pairs are contiguous in sorted order; for gate/up their x rows are gathered by token)
-// and 128 weight rows: for gate/up 64 gate + 64 up rows of the same 64 h-columns, for down
-// 128 output columns.  Each K step (128) stages the A rows (E4M3, 16 KB) and the weight rows
-// (E2M1, 8 KB) plus their scale bytes in LDS (double-buffered, rows padded against bank
-// conflicts); each wave then issues 4 x 4 MFMAs from LDS.  16-row MFMA tiles past the
-// expert's last pair are skipped.
+// Work split.  The pairs of one expert (contiguous in sorted order) are cut into M blocks
+// of at most 128 rows, evenly (150 pairs -> 75 + 75).  A job is (M block, N tile of 256
+// weight rows): for gate/up 128 gate rows + the 128 up rows of the same h-columns, for down
+// 256 output columns.  Jobs are numbered expert-major with the N tile fastest, and the jobs
+// of one XCD are one contiguous range (workgroup b runs on XCD b % 8), so the N tiles that
+// share an M block's activation rows run together behind one L2.  Every workgroup finds its
+// job from the expert offsets; the grid is sized for the most jobs any routing can make.
+//
+// Tiling.  Four waves share the M block's activation rows, staged per K step (128) in LDS
+// (double-buffered, rows padded against bank conflicts).  Each wave owns 64 weight rows and
+// keeps their E2M1 codes in registers, loaded straight from HBM three K steps ahead: every
+// weight byte is used by exactly one wave, so it never passes through LDS.  Per K step a
+// wave issues up to 8 x 4 MFMAs (16-row tiles past the block's last pair are skipped).
 //
 // Operand layout of the scaled 16x16x128 MFMA (measured with an in-bounds probe on gfx950,
 // K counted within the 128-wide step): lane l serves row/column l % 16 and lane group
@@ -29,166 +35,253 @@
 
 namespace {
 
-constexpr int kBM = 128;        // pairs per M block (a workgroup loops over its expert's blocks)
-constexpr int kBN = 128;        // weight rows per workgroup
+constexpr int kMB = 128;        // max pairs per M block
+constexpr int kMT = kMB / 16;   // 16-row MFMA tiles per M block
+constexpr int kNWave = 64;      // weight rows per wave
+constexpr int kNTile = 4 * kNWave;
 constexpr int kBK = 128;        // K per step
 constexpr int kAStride = 144;   // bytes per A row in LDS (128 + 16 pad)
-constexpr int kBStride = 80;    // bytes per B row in LDS (64 + 16 pad)
+constexpr int kXcd = 8;
+constexpr int kRing = 4;       // K steps of loads in flight (register rings)
 
-struct __align__(16) Stage {
-  uint8_t a[kBM * kAStride];
-  uint8_t b[kBN * kBStride];
-  uint32_t as[kBM];
-  uint32_t bs[kBN];
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every record: loads read 0
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// voff: per-lane byte offset; soff: a wave-uniform byte offset kept in an SGPR
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Workgroup barrier that orders LDS only: __syncthreads() also fences global memory, which
+// would wait for every weight load in flight at each K step.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct Job {
+  int e, m0, nrows, ntile;
 };
 
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int blocks_of(int cnt) { return (cnt + kMB - 1) / kMB; }
+
+// Wave 0: the job of this workgroup, or e = -1.
+__device__ Job find_job(const int32_t* __restrict__ off, int E, int NT, int lane) {
+  int total = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int nb = e < E ? blocks_of(off[e + 1] - off[e]) : 0;
+    total += __shfl(wave_incl_scan(nb, lane), 63, 64);
+  }
+  const long n_work = (long)total * NT;
+  const int x = blockIdx.x % kXcd, j = blockIdx.x / kXcd;
+  const long lo = n_work * x / kXcd, hi = n_work * (x + 1) / kXcd;
+  Job jb{-1, 0, 0, 0};
+  if (lo + j >= hi) return jb;
+  const long w = lo + j;
+  const int entry = (int)(w / NT);
+  jb.ntile = (int)(w % NT);
+  int run = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int cnt = e < E ? off[e + 1] - off[e] : 0;
+    const int nb = blocks_of(cnt);
+    const int incl = wave_incl_scan(nb, lane);
+    const int tot = __shfl(incl, 63, 64);
+    if (entry < run + tot) {
+      const bool hit = nb > 0 && run + incl - nb <= entry && entry < run + incl;
+      const uint64_t m = __ballot(hit);
+      const int L = __ffsll((unsigned long long)m) - 1;
+      const int es = base + L;
+      const int mb = entry - run - (__shfl(incl, L, 64) - __shfl(nb, L, 64));
+      const int c = __shfl(cnt, L, 64), nbs = __shfl(nb, L, 64);
+      const int r0 = (int)((long)c * mb / nbs), r1 = (int)((long)c * (mb + 1) / nbs);
+      jb.e = es;
+      jb.m0 = off[es] + r0;
+      jb.nrows = r1 - r0;
+      return jb;
+    }
+    run += tot;
+  }
+  return jb;
+}
 
 template <bool GATEUP>
-__global__ __launch_bounds__(256) void mx_ffn_kernel(MxArgs p) {
-  __shared__ Stage st[2];
-  __shared__ int s_arow[kBM];     // A source row per local pair (-1: none)
+__global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
+  __shared__ __align__(16) uint8_t s_a[2][kMB * kAStride];
+  __shared__ uint32_t s_as[2][kMB];
+  __shared__ int s_arow[kMB];
+  __shared__ Job s_job;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const int K = p.K, N = p.N;
+  const int NT = GATEUP ? N / (kNTile / 2) : (N + kNTile - 1) / kNTile;
 
-  int start, cnt;
-  const int e = moe_find_active_expert(p.offsets, p.E, blockIdx.y, start, cnt);
-  if (e < 0) return;
-  for (int m0 = blockIdx.z * kBM; m0 < cnt; m0 += kBM * gridDim.z) {
-  const int nrows = min(kBM, cnt - m0);
-  const int n0 = blockIdx.x * (GATEUP ? kBN / 2 : kBN);   // h-column base (gate/up) or out col
-
-  if (tid < kBM) {
+  if (wave == 0) {
+    const Job jb = find_job(p.offsets, p.E, NT, lane);
+    if (lane == 0) s_job = jb;
+  }
+  __syncthreads();
+  const Job jb = s_job;
+  if (jb.e < 0) return;
+  const int nrows = jb.nrows;
+  if (tid < kMB) {
     int src = -1;
     if (tid < nrows) {
-      const int pos = start + m0 + tid;
+      const int pos = jb.m0 + tid;
       src = GATEUP ? p.sorted_pair[pos] / p.k : pos;
     }
     s_arow[tid] = src;
   }
   __syncthreads();
 
-  // ---- global -> register staging assignment
-  const int ar = tid >> 1, ah = tid & 1;          // A: row, 64-byte half
-  const int br = tid >> 1, bh = tid & 1;          // B: row, 32-byte half
-  const int asrc = s_arow[ar];
-  const uint8_t* aptr = asrc >= 0 ? p.aq + (size_t)asrc * K + 64 * ah : nullptr;
-  const uint8_t* asptr = (tid < kBM && s_arow[tid] >= 0) ? p.as + (size_t)s_arow[tid] * (K / 32) : nullptr;
-  int wrow;
-  const uint8_t* bcodes;
-  const uint8_t* bscales;
-  if (GATEUP) {
-    const bool up = br >= kBN / 2;
-    wrow = n0 + (up ? br - kBN / 2 : br);
-    bcodes = up ? p.wcodes1 : p.wcodes0;
-    bscales = up ? p.wscales1 : p.wscales0;
-  } else {
-    wrow = n0 + br;
-    bcodes = p.wcodes0;
-    bscales = p.wscales0;
+  // ---- A staging: thread covers 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 i
+  const int achunk = tid & 7;
+  const rsrc_t ra_q = make_rsrc(p.aq, (uint32_t)((GATEUP ? p.T : p.P) * (size_t)K));
+  const rsrc_t ra_s = make_rsrc(p.as, (uint32_t)((GATEUP ? p.T : p.P) * (size_t)(K / 32)));
+  uint32_t aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int src = s_arow[(tid >> 3) + 32 * i];
+    aoff[i] = src >= 0 ? (uint32_t)src * K + 16 * achunk : kOOB;
   }
-  const uint8_t* bptr = bcodes + ((size_t)e * N + wrow) * (K / 2) + 32 * bh;
-  const uint8_t* bsptr = nullptr;
-  if (tid < kBN) {
-    int r2 = tid, wr2;
-    const uint8_t* bsc = p.wscales0;
-    if (GATEUP) {
-      const bool up = r2 >= kBN / 2;
-      wr2 = n0 + (up ? r2 - kBN / 2 : r2);
-      bsc = up ? p.wscales1 : p.wscales0;
-    } else {
-      wr2 = n0 + r2;
-    }
-    bsptr = bsc + ((size_t)e * N + wr2) * (K / 32);
-  }
+  const int srow = s_arow[tid & (kMB - 1)];   // threads >= kMB load a scale word they never store
+  const uint32_t asoff = srow >= 0 ? (uint32_t)srow * (K / 32) : kOOB;
 
-  uint4 ra[4], rb[2];
-  uint32_t ras = 0, rbs = 0;
-  auto gload = [&](int k0) {
+  // ---- this wave's weight rows: 4 n-tiles of 16 (gate/up: gate, gate, up, up)
+  const int g = lane >> 4, c16 = lane & 15;
+  const int col0 = GATEUP ? jb.ntile * (kNTile / 2) + 32 * wave   // first of 32 h-columns
+                          : jb.ntile * kNTile + kNWave * wave;    // first of 64 output columns
+  const bool wvalid = GATEUP || col0 < N;
+  const size_t ebytes = (size_t)N * (K / 2), escales = (size_t)N * (K / 32);
+  const rsrc_t rb0 = make_rsrc(p.wcodes0 + jb.e * ebytes, (uint32_t)ebytes);
+  const rsrc_t rs0 = make_rsrc(p.wscales0 + jb.e * escales, (uint32_t)escales);
+  const rsrc_t rb1 = GATEUP ? make_rsrc(p.wcodes1 + jb.e * ebytes, (uint32_t)ebytes) : rb0;
+  const rsrc_t rs1 = GATEUP ? make_rsrc(p.wscales1 + jb.e * escales, (uint32_t)escales) : rs0;
+  const uint32_t brow = (uint32_t)((wvalid ? col0 : 0) + c16);
+  const uint32_t boff = brow * (K / 2) + 16 * g, bsoff = brow * (K / 32);
+  // n-tile q starts qrow(q) rows after the lane's first row
+  auto qrow = [](int q) { return GATEUP ? 16 * (q & 1) : 16 * q; };
+
+  // Register rings: A(s) is loaded kRing - 1 steps before it is stored to LDS (at the end of
+  // step s - 1), B(s) kRing steps before step s uses it.  Slot of step s: s % kRing.
+  uint4 ra[kRing][4];
+  uint32_t ras[kRing];
+  auto load_a = [&](int slot, int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[slot][i] = bload16(ra_q, aoff[i], k0);
+    ras[slot] = bload4(ra_s, asoff, k0 / 32);
+  };
+  auto store_a = [&](int slot, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ra[i] = aptr ? *reinterpret_cast<const uint4*>(aptr + k0 + 16 * i) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = *reinterpret_cast<const uint4*>(bptr + k0 / 2 + 16 * i);
-    if (tid < kBM) ras = asptr ? *reinterpret_cast<const uint32_t*>(asptr + k0 / 32) : 0u;
-    if (tid < kBN) rbs = *reinterpret_cast<const uint32_t*>(bsptr + k0 / 32);
-  };
-  auto sstore = [&](Stage& s) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&s.a[ar * kAStride + 64 * ah + 16 * i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(&s.b[br * kBStride + 32 * bh + 16 * i]) = rb[i];
-    if (tid < kBM) s.as[tid] = ras;
-    if (tid < kBN) s.bs[tid] = rbs;
+      *reinterpret_cast<uint4*>(&s_a[buf][((tid >> 3) + 32 * i) * kAStride + 16 * achunk]) = ra[slot][i];
+    if (tid < kMB) s_as[buf][tid] = ras[slot];
   };
 
-  f32x4_t acc[4][4];
+  uint4 rb[kRing][4];
+  uint32_t rbs[kRing][4];
+  auto load_b = [&](int slot, int k0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 4; ++q) {
+      const bool hi = GATEUP && q >= 2;
+      rb[slot][q] = bload16(hi ? rb1 : rb0, boff, qrow(q) * (K / 2) + k0 / 2);
+      rbs[slot][q] = bload4(hi ? rs1 : rs0, bsoff, qrow(q) * (K / 32) + k0 / 32);
+    }
+  };
 
-  const int g = lane >> 4, c16 = lane & 15;
-  // weight-row (within the B tile) of each of this wave's 4 n-tiles
-  int nrow[4];
+  f32x4_t acc[kMT][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    if (GATEUP) nrow[nt] = (nt < 2 ? 0 : kBN / 2) + 32 * wn + 16 * (nt & 1) + c16;
-    else nrow[nt] = 64 * wn + 16 * nt + c16;
-  }
-  int mtiles = 0;   // valid 16-row tiles of this wave
+  for (int i = 0; i < kMT; ++i)
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-    if (64 * wm + 16 * mt < nrows) mtiles = mt + 1;
+    for (int q = 0; q < 4; ++q) acc[i][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  const int mtiles = (nrows + 15) >> 4;
 
-  const int nsteps = K / kBK;
-  gload(0);
-  sstore(st[0]);
-  __syncthreads();
-  for (int ks = 0; ks < nsteps; ++ks) {
-    Stage& cur = st[ks & 1];
-    if (ks + 1 < nsteps) gload((ks + 1) * kBK);
+  auto compute = [&](int buf, int slot) {
     i32x8_t bop[4];
     int bsc[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&cur.b[nrow[nt] * kBStride + 16 * g]);
-      bop[nt] = (i32x8_t){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      bsc[nt] = (cur.bs[nrow[nt]] >> (8 * g)) & 0xFF;
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = rb[slot][q];
+      bop[q] = (i32x8_t){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      bsc[q] = (rbs[slot][q] >> (8 * g)) & 0xFF;
     }
+    const uint8_t* sa = s_a[buf];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
       if (mt < mtiles) {
-        const int arow = 64 * wm + 16 * mt + c16;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(&cur.a[arow * kAStride + 16 * g]);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(&cur.a[arow * kAStride + 64 + 16 * g]);
+        const int arow = 16 * mt + c16;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(&sa[arow * kAStride + 16 * g]);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(&sa[arow * kAStride + 64 + 16 * g]);
         const i32x8_t aop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                              (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-        const int asc = (cur.as[arow] >> (8 * g)) & 0xFF;
+        const int asc = (s_as[buf][arow] >> (8 * g)) & 0xFF;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop, bop[nt], acc[mt][nt], 0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, asc, 0, bsc[nt]);
+        for (int q = 0; q < 4; ++q)
+          acc[mt][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop, bop[q], acc[mt][q], 0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, asc, 0, bsc[q]);
       }
     }
-    if (ks + 1 < nsteps) {
-      sstore(st[(ks + 1) & 1]);
-    }
-    __syncthreads();
+  };
+
+  // Step s: issue A(s + kRing - 1) (its slot held A(s - 1), stored to LDS a step ago), compute
+  // from LDS buffer s & 1 and B slot s % kRing, refill that B slot with B(s + kRing), then
+  // store A(s + 1) to the other LDS buffer.  Loads complete in issue order, so waiting for
+  // A(s + 1) waits for nothing issued in the last kRing - 2 steps.  Past the last step the
+  // loads repeat the last step's data, which keeps the code branch-free and the wait counts
+  // exact.
+  const int nsteps = K / kBK;
+  auto step = [&](int s, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    constexpr int AN = (SLOT + kRing - 1) % kRing, A1 = (SLOT + 1) % kRing;
+    load_a(AN, min(s + kRing - 1, nsteps - 1) * kBK);
+    if (wvalid) compute(s & 1, SLOT);
+    load_b(SLOT, min(s + kRing, nsteps - 1) * kBK);
+    if (s + 1 < nsteps) store_a(A1, (s + 1) & 1);
+    lds_barrier();
+  };
+
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    load_b(i, min(i, nsteps - 1) * kBK);
+    if (i < kRing - 1) load_a(i, min(i, nsteps - 1) * kBK);
   }
+  store_a(0, 0);
+  lds_barrier();
+  for (int s = 0; s < nsteps; s += kRing) {
+    step(s, std::integral_constant<int, 0>{});
+    if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
+    if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
+    if (s + 3 < nsteps) step(s + 3, std::integral_constant<int, 3>{});
+  }
+  if (!wvalid) return;
 
   // ---- epilogue.  D element (4*(lane/16)+i, lane%16) of each 16x16 tile is acc[..][..][i].
   if (GATEUP) {
     const int I = N;
-    const int hcol0 = n0 + 32 * wn;             // this wave's 32 h-columns = one MX group
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
       if (mt >= mtiles) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rl = 64 * wm + 16 * mt + 4 * g + i;
+        const int rl = 16 * mt + 4 * g + i;
         float h[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -199,53 +292,59 @@ __global__ __launch_bounds__(256) void mx_ffn_kernel(MxArgs p) {
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
         if (rl < nrows) {
-          const int pos = start + m0 + rl;
-          uint8_t* hrow = p.hq + (size_t)pos * I + hcol0;
+          const int pos = jb.m0 + rl;
+          uint8_t* hrow = p.hq + (size_t)pos * I + col0;
           if (amax == 0) {
             hrow[c16] = 0;
             hrow[c16 + 16] = 0;
-            if (c16 == 0) p.hs[(size_t)pos * (I / 32) + hcol0 / 32] = 0;
+            if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = 0;
           } else {
             const int X = moe_mx_exp(amax);
             hrow[c16] = (uint8_t)moe_e4m3_from_f32(__float_as_uint(h[0]), X);
             hrow[c16 + 16] = (uint8_t)moe_e4m3_from_f32(__float_as_uint(h[1]), X);
-            if (c16 == 0) p.hs[(size_t)pos * (I / 32) + hcol0 / 32] = (uint8_t)(X + 127);
+            if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = (uint8_t)(X + 127);
           }
         }
       }
     }
   } else {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
       if (mt >= mtiles) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rl = 64 * wm + 16 * mt + 4 * g + i;
+        const int rl = 16 * mt + 4 * g + i;
         if (rl < nrows) {
-          float* yrow = p.y + (size_t)(start + m0 + rl) * N + n0 + 64 * wn + c16;
+          float* yrow = p.y + (size_t)(jb.m0 + rl) * N + col0 + c16;
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) yrow[16 * nt] = acc[mt][nt][i];
+          for (int q = 0; q < 4; ++q) yrow[16 * q] = acc[mt][q][i];
         }
       }
     }
   }
-  __syncthreads();   // the next M block reuses s_arow and the stages
-  }
 }
 
-inline int expert_slots(const MxArgs& a) { return a.P < a.E ? a.P : a.E; }
+// Grid: enough workgroups for the most jobs any routing of P pairs over E experts makes
+// (sum over active experts of ceil(cnt / 128) <= min(P, E) + ceil(P / 128)), rounded up to
+// a multiple of the XCD count so that every XCD's job range fits.
+inline unsigned grid_for(const MxArgs& a, int NT) {
+  const long slots = (a.P < a.E ? a.P : a.E) + (a.P + kMB - 1) / kMB;
+  const long work = slots * NT;
+  return (unsigned)(kXcd * ((work + kXcd - 1) / kXcd));
+}
 
 }  // namespace
 
 hipError_t moe_launch_mx_gateup(const MxArgs& a, hipStream_t s) {
-  // N = I (h columns); each workgroup covers 64 h-columns (64 gate + 64 up rows)
-  dim3 grid(a.N / (kBN / 2), expert_slots(a), 1);
-  hipLaunchKernelGGL((mx_ffn_kernel<true>), grid, dim3(256), 0, s, a);
+  if (a.N % (kNTile / 2) || a.K % kBK) return hipErrorInvalidValue;
+  const int NT = a.N / (kNTile / 2);
+  hipLaunchKernelGGL((mx_gemm_kernel<true>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t moe_launch_mx_down(const MxArgs& a, hipStream_t s) {
-  dim3 grid(a.N / kBN, expert_slots(a), 1);
-  hipLaunchKernelGGL((mx_ffn_kernel<false>), grid, dim3(256), 0, s, a);
+  if (a.N % kNWave || a.K % kBK) return hipErrorInvalidValue;
+  const int NT = (a.N + kNTile - 1) / kNTile;
+  hipLaunchKernelGGL((mx_gemm_kernel<false>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

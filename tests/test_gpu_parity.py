@@ -301,8 +301,8 @@ def test_layer_cfg2_hy4_decode_zipf_sampled():
 MX_SMALL = synth.LayerCfg("mx", 150, 512, 256, 8, 2, True, "mxfp4", False, True, 1, 13)
 
 
-def _mx_stage_check(c, inp, bufs, d, toks_check=None):
-    offs = M.moe_workspace_offsets(d, M.MOE_W_MXFP4, True)
+def _mx_stage_check(c, inp, bufs, d, experts_check=None):
+    offs = M.moe_workspace_offsets(d, M.MOE_W_MXFP4, bool(c.shared))
     ws = host(bufs.ws)
     T, H, I, P = c.T, c.H, c.I, c.T * c.k
     xq = ws[offs[2]:offs[2] + T * H].reshape(T, H)
@@ -321,7 +321,7 @@ def _mx_stage_check(c, inp, bufs, d, toks_check=None):
     yp = host(bufs.y_pairs)
     n_flip = n_tot = 0
     worst = 0.0
-    experts = range(c.E) if toks_check is None else toks_check
+    experts = range(c.E) if experts_check is None else experts_check
     for e in experts:
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
@@ -348,6 +348,63 @@ def _mx_stage_check(c, inp, bufs, d, toks_check=None):
     # with boundaries 2^-3 apart (relative) about 2 * 1e-4 / 2^-3 = 1.6e-3 of the codes may flip.
     assert n_flip <= max(2, 2e-3 * n_tot)
     assert worst <= TOL
+
+
+MX_MORE = {
+    # about 300 pairs per expert: three M blocks each
+    "h512-i256-e4-top2-t600": synth.LayerCfg("mx", 600, 512, 256, 4, 2, True, "mxfp4", False, True, 1, 17),
+    # most experts idle, ragged blocks of one to two pairs
+    "h512-i384-e64-top2-t3": synth.LayerCfg("mx", 3, 512, 384, 64, 2, False, "mxfp4", False, True, 1, 18),
+    # wide down projection with a partial last N tile (H = 640 = 2.5 tiles of 256)
+    "h640-i256-e8-top2-t70": synth.LayerCfg("mx", 70, 640, 256, 8, 2, False, "mxfp4", False, True, 1, 19),
+}
+
+
+@pytest.mark.parametrize("name", list(MX_MORE))
+def test_mx_layer_blocks_and_tails(name):
+    c = MX_MORE[name]
+    say("mx layer", name)
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_MXFP4, shared is not None)
+    run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
+    torch.cuda.synchronize()
+    _mx_stage_check(c, inp, bufs, d)
+
+
+def test_mx_layer_cfg3_hy4_prefill_sampled():
+    """Full-size MXFP4 prefill (4096 tokens, 256 experts, top-8): routing, permutation and
+    activation quantisation in full; h and the down projection on the experts with the most
+    and the fewest pairs and one more; the shared expert and the combined output on sampled
+    tokens."""
+    c = synth.cfg(3)
+    say("mx cfg3 generate")
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_MXFP4, True)
+    say("mx cfg3 run")
+    run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
+    torch.cuda.synchronize()
+    _, rid, rw = O.route(c.k, logits_in=inp["logits_in"])
+    rsp, roff, rpp = O.permute(rid, c.E)
+    assert (host(bufs.sorted_pair) == rsp).all() and (host(bufs.offsets) == roff).all()
+    assert (host(bufs.pair_pos) == rpp).all()
+    cnt = np.diff(roff)
+    pick = [int(np.argmax(cnt)), int(np.argmin(np.where(cnt > 0, cnt, 1 << 30))),
+            int(synth.sample_tokens(c.seed, c.E, 1)[0])]
+    say("mx cfg3 stage check on experts", pick, "pairs", [int(cnt[e]) for e in pick])
+    _mx_stage_check(c, inp, bufs, d, experts_check=pick)
+    toks = synth.sample_tokens(c.seed, c.T, 4)
+    ysh = O.shared_expert(inp["x"][toks], *inp["shared"])
+    assert row_err(host(bufs.y_shared)[toks], ysh).max() <= TOL
+    out_ref = O.combine(host(bufs.y_pairs), rw, rpp, host(bufs.y_shared))
+    err = row_err(host(bufs.out)[toks], out_ref[toks])
+    say("mx cfg3 combine max row err on sampled tokens", float(err.max()))
+    assert err.max() <= TOL
 
 
 def test_mx_layer_small_stages():
