@@ -530,3 +530,109 @@ def test_fused_decode_cfg2_hy4_zipf_sampled():
     err = row_err(host(o["out"])[sample], ref["out"])
     say("fused cfg2 sampled max row err", float(err.max()))
     assert err.max() <= TOL
+
+
+# ----------------------------------------------------------------------------- norm, combine, chain
+def test_rmsnorm_bf16_matches_oracle():
+    g = np.random.default_rng(21)
+    T, H = 19, 6144
+    r = (g.standard_normal((T, H)) * np.exp(g.uniform(-6, 6, (T, 1)))).astype(np.float32)
+    r[3] = 0.0                                     # all-zero row: eps keeps it finite
+    say("rmsnorm", T, H)
+    a = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    M.moe_rmsnorm_bf16(T, H, 1e-6, dev(r), a)
+    got = host(a, np.uint16)
+    ref = O.rmsnorm_bf16(r.astype(np.float64))
+    # the GPU sums squares in fp32 in another order, so a value lying within an fp32 rounding
+    # of a bf16 rounding boundary may round the other way: one bf16 step at most, rarely
+    gi = got.astype(np.int32)
+    ri = ref.astype(np.int32)
+    assert (np.abs(gi - ri) <= 1).all()
+    assert (gi != ri).mean() <= 1e-3
+    assert (got[3] == 0).all()
+
+
+def test_combine_with_residual_and_bf16():
+    g = np.random.default_rng(22)
+    T, H, k = 37, 768, 4
+    P = T * k
+    yp = g.standard_normal((P, H)).astype(np.float32)
+    w = g.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    pp = g.permutation(P).astype(np.int32)
+    ysh = g.standard_normal((T, H)).astype(np.float32)
+    res = g.standard_normal((T, H)).astype(np.float32)
+    d = M.Dims(T, H, 256, 16, k)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    obf = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    M.moe_combine(d, dev(yp), dev(w), dev(pp), dev(ysh), dev(res), out, obf)
+    ref = O.combine(yp, w, pp, ysh, res)
+    got = host(out)
+    assert row_err(got, ref).max() <= 1e-6
+    assert (host(obf, np.uint16) == O.f64_to_bf16_bits(got.astype(np.float64))).all()
+    # residual may alias the output
+    r2 = dev(res)
+    M.moe_combine(d, dev(yp), dev(w), dev(pp), dev(ysh), r2, r2, None)
+    assert row_err(host(r2), ref).max() <= 1e-6
+
+
+def test_chain_cfg4_hy4_29_layers_sampled():
+    """29 STQ1_0 Hy4 layers at 16 tokens with Zipf-skewed routing, chained through
+    pre-norm residual adds: a = bf16(RMSNorm(r)), r <- r + MoE(a).  Two sampled tokens are
+    checked at every layer, teacher-forced (the oracle takes the GPU's r of that layer)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from tests.helpers import oracle_weights_regen
+    c = synth.cfg(4)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    toks = synth.sample_tokens(c.seed, c.T, 2)
+    x0 = synth.activations(c.seed, 0, c.T, c.H)
+    r = torch.from_numpy(O.bf16_to_f64(x0).astype(np.float32)).cuda()
+    r_next = torch.empty_like(r)
+    a = torch.empty((c.T, c.H), dtype=torch.int16, device="cuda")
+    f32, i32 = torch.float32, torch.int32
+    o = dict(logits=torch.empty((c.T, c.E), dtype=f32, device="cuda"),
+             ids=torch.empty((c.T, c.k), dtype=i32, device="cuda"),
+             w=torch.empty((c.T, c.k), dtype=f32, device="cuda"),
+             sp=torch.empty(d.P, dtype=i32, device="cuda"),
+             off=torch.empty(c.E + 1, dtype=i32, device="cuda"),
+             pp=torch.empty(d.P, dtype=i32, device="cuda"),
+             yp=torch.empty((d.P, c.H), dtype=f32, device="cuda"),
+             ysh=torch.empty((c.T, c.H), dtype=f32, device="cuda"))
+    ws = torch.zeros(M.moe_layer_decode_workspace_size(d, True), dtype=torch.uint8, device="cuda")
+    worst, n_tie, n_flip_a = 0.0, 0, 0
+    pool = ThreadPoolExecutor(16)
+    for layer in range(c.layers):
+        inp = layer_inputs(c, layer)
+        routed = routed_experts(c, inp["routed"])
+        shared = shared_experts(inp["shared"])
+        M.moe_rmsnorm_bf16(c.T, c.H, 1e-6, r, a)
+        M.moe_layer_decode(d, routed, shared, a, dev(inp["wr"]), dev(inp["bias"]), o["logits"],
+                           o["ids"], o["w"], o["sp"], o["off"], o["pp"], o["yp"], o["ysh"],
+                           r, r_next, None, ws)
+        torch.cuda.synchronize()
+        r_l = host(r)[toks]
+        a_l = host(a, np.uint16)[toks]
+        delta = host(r_next)[toks].astype(np.float64) - r_l
+        del routed, shared, inp
+        # the norm: teacher-forced on the GPU's r
+        a_ref = O.rmsnorm_bf16(r_l.astype(np.float64))
+        assert (np.abs(a_l.astype(np.int32) - a_ref.astype(np.int32)) <= 1).all()
+        n_flip_a += int((a_l != a_ref).sum())
+        # the MoE layer on the GPU's normed input
+        wr = synth.router_weights(c.seed, layer, c.E, c.H)
+        bias = synth.zipf_bias(c.seed, layer, c.E)
+        logits, rid, _ = O.route(c.k, a_l, wr, bias)
+        tie = near_tie_tokens(logits, c.k)
+        n_tie += int(tie.sum())
+        assert (host(o["ids"])[toks][~tie] == rid[~tie]).all()
+        regen = oracle_weights_regen(c, layer)
+        need = sorted({(int(e), m) for e in rid.ravel() for m in range(3)})
+        cache = dict(zip(need, pool.map(lambda em: regen(*em), need)))
+        ref = O.moe_layer(a_l, c.k, lambda e, m: cache[(e, m)], "stq1", wr_bits=wr, bias=bias,
+                          shared=synth.shared_weights(c.seed, layer, c.I, c.H))
+        err = row_err(delta[~tie], ref["out"][~tie]) if (~tie).any() else np.zeros(1)
+        worst = max(worst, float(err.max()))
+        say(f"chain layer {layer}: max row err {float(err.max()):.2e}, near-ties {int(tie.sum())}")
+        assert err.max() <= TOL
+        r, r_next = r_next, r
+    say("chain: worst", worst, "near-tie token-layers", n_tie, "bf16 norm flips", n_flip_a)
