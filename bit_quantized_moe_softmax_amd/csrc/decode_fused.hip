@@ -777,6 +777,106 @@ __global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
 // ---------------------------------------------------------------------------- small T
 constexpr int kMaxPL = kXT * 32;   // pairs of a small-T layer (k <= 32)
 
+// Up to kXT tokens the first kernel only computes the router partials: every routed gate/up
+// workgroup then derives the routing itself (below), so no workgroup waits on another.
+template <int HB>
+__global__ __launch_bounds__(kWG) void k1s_router(DecodeArgs a) {
+  __shared__ __align__(16) float s_red[kNW][4][64];
+  router_unit<HB>(a, blockIdx.x, s_red);
+}
+
+// Routing of up to kXT tokens inside one workgroup (LDS only): top-k per token (one wave per
+// token), the stable order of the pairs by expert, and the units (one per selected expert:
+// an expert holds at most kXT pairs).  With `out` the workgroup also writes the routing
+// outputs and the down kernel's work lists.
+struct SmallRoute {
+  float v[kNW][32];
+  int i[kNW][32];
+  int ids[kMaxPL];      // expert of pair f = t k + j
+  int wb[kMaxPL];       // routing weight bits of pair f
+  int sorted[kMaxPL];   // pair at each sorted position
+  int same[kMaxPL];     // rank of the pair at each position among its expert's pairs
+  int4 ut[kMaxPL];      // units: {expert, first position, pairs, 0}
+  int utok[kMaxPL];     // token of the pair at each position
+  int wcnt[2];
+  int n_units;
+};
+
+__device__ __forceinline__ void small_route_topk(const DecodeArgs& a, SmallRoute& R, const TopkIn& in, bool out) {
+  const int wave = threadIdx.x >> 6;
+  if (wave < a.T) wave_topk(a, wave, in, R.v[wave], R.i[wave], R.ids, R.wb, out);
+}
+
+__device__ __forceinline__ void small_route_units(const DecodeArgs& a, SmallRoute& R, bool out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = a.k, P = a.T * k, E = a.E;
+  lds_barrier();
+  if (tid < P) {
+    const int e = R.ids[tid];
+    int before = 0, same = 0;
+    for (int f = 0; f < P; ++f) {
+      const int ef = R.ids[f];
+      before += ef < e;
+      same += ef == e && f < tid;
+    }
+    const int pos = before + same;
+    R.sorted[pos] = tid;
+    R.same[pos] = same;
+    R.utok[pos] = tid / k;
+    if (out) {
+      a.sorted_pair[pos] = tid;
+      a.pair_pos[tid] = pos;
+    }
+  }
+  if (out) {
+    for (int e = tid; e <= E; e += kWG) {
+      int before = 0;
+      for (int f = 0; f < P; ++f) before += R.ids[f] < e;
+      a.offsets[e] = before;
+    }
+  }
+  lds_barrier();
+  // a unit starts at every position whose pair is its expert's first (P <= 128: two waves)
+  bool first = false;
+  uint64_t m = 0;
+  if (wave < 2) {
+    first = tid < P && R.same[tid] == 0;
+    m = __ballot(first);
+    if (lane == 0) R.wcnt[wave] = __popcll(m);
+  }
+  lds_barrier();
+  if (tid < P) {
+    const uint64_t le = ~0ull >> (63 - lane);
+    const int u = (wave ? R.wcnt[0] : 0) + __popcll(m & le) - 1;
+    const int f = R.sorted[tid];
+    const int e = R.ids[f];
+    if (first) {
+      int n = 0;
+      for (int q = tid; q < P && R.ids[R.sorted[q]] == e; ++q) ++n;
+      R.ut[u] = make_int4(e, tid, n, 0);
+      if (out) {
+        a.ut[u] = make_int4(e, tid, n, 0);
+        a.hl[u] = make_int4(e, tid, n, 16 * u);
+      }
+    }
+    if (out) {
+      const int j = R.same[tid];
+      a.utok[16 * u + j] = f / k;
+      a.uw[16 * u + j] = __int_as_float(R.wb[f]);
+    }
+  }
+  if (tid == 0) {
+    const int nu = R.wcnt[0] + (P > 64 ? R.wcnt[1] : 0);
+    R.n_units = nu;
+    if (out) {
+      a.wl[0] = nu;
+      a.wl[1] = nu;
+      a.wl[2] = nu;
+    }
+  }
+  lds_barrier();
+}
+
 // ============================================================================ K2
 // Routed gate/up: a workgroup takes one unit (expert, <= 16 pairs) and 32 rows of I; wave
 // = (16-row tile, gate|up) over all of K; the gate and up waves of a tile meet in LDS and
@@ -1017,19 +1117,20 @@ struct SharedDown {
 // row already in LDS; as routed_gateup otherwise.
 template <int HB, int IB>
 __device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi, const uint2* s_lut,
-                                                    const uint16_t* s_x, float (*s_red)[2][4][64]) {
+                                                    const uint16_t* s_x, float (*s_red)[2][4][64],
+                                                    const SmallRoute& R) {
   constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int un_i = wi / NTP, tp = wi % NTP;
-  const int4 un = a.ut[un_i];
+  const int4 un = R.ut[un_i];
   const int e = un.x, pos0 = un.y, ntok = un.z;
   const int mat = wave & 1, tl = wave >> 1;
   const int row0 = (2 * tp + tl) * 16;
   const size_t wrow = (size_t)e * I + row0 + col;
   StqStream<HB, 8> st;
   st.issue((mat ? a.uc : a.gc) + wrow * HB * 40, (mat ? a.us : a.gs) + wrow * HB);
-  const int tok = a.utok[un_i * 16 + (col < ntok ? col : ntok - 1)];
+  const int tok = R.utok[pos0 + (col < ntok ? col : ntok - 1)];
   const f32x4_t acc = st.run_lds(s_lut, s_x + tok * H + 64 * g);
 #pragma unroll
   for (int i = 0; i < 4; ++i) s_red[tl][mat][i][lane] = acc[i];
@@ -1106,6 +1207,7 @@ __global__ __launch_bounds__(F4 ? 512 : kWG) __attribute__((amdgpu_waves_per_eu(
   __shared__ __align__(16) float s_red[2][2][4][64];
   __shared__ __align__(16) float s_red4[F4 ? NTL : 1][2][64];
   __shared__ float s_hv[F4 ? 16 : 1][F4 ? 16 * NTL : 1];
+  __shared__ SmallRoute s_rt;
   const int b = blockIdx.x;
   const int T = a.T;
   if (b >= a.n_gu_wg) {
@@ -1135,13 +1237,17 @@ __global__ __launch_bounds__(F4 ? 512 : kWG) __attribute__((amdgpu_waves_per_eu(
     for (int wi = b; wi < n_items; wi += a.n_gu_wg)
       routed_gateup_e2m1<HB, IB, NTL>(a, wi, s_lut4, reinterpret_cast<const uint8_t*>(s_x), s_red4, s_hv);
   } else {
+    // router partials first, then the x rows: both in flight together
+    TopkIn in;
+    if ((int)(threadIdx.x >> 6) < T) topk_load(a, threadIdx.x >> 6, in);
     RowStage<H, kWG, XR> xs;
     xs.issue(T, [&](int r) { return a.x + (size_t)r * H; });
     build_lut(s_lut);
-    const int n_items = a.wl[1] * (I / 32);
     xs.commit(T, s_x);
-    lds_barrier();
-    for (int wi = b; wi < n_items; wi += a.n_gu_wg) routed_gateup_small<HB, IB>(a, wi, s_lut, s_x, s_red);
+    small_route_topk(a, s_rt, in, b == 0);
+    small_route_units(a, s_rt, b == 0);
+    const int n_items = s_rt.n_units * (I / 32);
+    for (int wi = b; wi < n_items; wi += a.n_gu_wg) routed_gateup_small<HB, IB>(a, wi, s_lut, s_x, s_red, s_rt);
   }
 }
 
@@ -1364,7 +1470,8 @@ hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
   const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (a.h_lds ? (size_t)hbytes + 64 : 0);
   const bool prof = moe_prof_on();
   if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
-  hipLaunchKernelGGL((k1_route<HB, kMaxPL, F4 ? 4 : 8>), dim3(a.n_router_wg + a.n_xq_wg), dim3(kWG), 0, s, a);
+  if constexpr (F4) hipLaunchKernelGGL((k1_route<HB, kMaxPL, 4>), dim3(a.n_router_wg + a.n_xq_wg), dim3(kWG), 0, s, a);
+  else hipLaunchKernelGGL((k1s_router<HB>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
   hipLaunchKernelGGL((k2s_gateup<HB, IB, XR, F4>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(NT2), lds2, s, a);

@@ -431,6 +431,11 @@ FUSED = {
     "h1024-i512-e16-top4-t21-zipf": synth.LayerCfg("t", 21, 1024, 512, 16, 4, True, "stq1", True, False, 1, 14),
     "h512-i256-e40-top8-t64-noshared": synth.LayerCfg("t", 64, 512, 256, 40, 8, False, "stq1", True, False, 1, 15),
     "h512-i256-e8-top2-t1-shared": synth.LayerCfg("t", 1, 512, 256, 8, 2, True, "stq1", False, False, 1, 16),
+    # 2..4 tokens: the per-workgroup routing path, experts shared by several tokens
+    "h512-i256-e8-top2-t4-shared": synth.LayerCfg("t", 4, 512, 256, 8, 2, True, "stq1", False, False, 1, 23),
+    "h1024-i512-e16-top4-t3-zipf": synth.LayerCfg("t", 3, 1024, 512, 16, 4, True, "stq1", True, False, 1, 24),
+    "h512-i256-e4-top4-t2-noshared": synth.LayerCfg("t", 2, 512, 256, 4, 4, False, "stq1", False, False, 1, 25),
+    "h512-i256-e64-top32-t4-shared": synth.LayerCfg("t", 4, 512, 256, 64, 32, True, "stq1", False, False, 1, 26),
 }
 
 
