@@ -101,6 +101,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// Weight streams read in whole cache lines by one load are read once per call: non-temporal
+// loads (cache policy nt) keep them from evicting what is reused from L2 -- activations,
+// routing data, h, and the kernels' code.  (Streams that touch a line through several
+// smaller loads keep normal loads: an nt line may be gone before its next touch.)
+constexpr int kNT = 2;
+__device__ __forceinline__ uint4 bload16_nt(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT));
+}
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+__device__ __forceinline__ uint4 ntload16(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
@@ -438,6 +451,124 @@ struct StqStream {
   }
 };
 
+// The same stream with the code words staged through a per-wave LDS buffer.  A wave's 16
+// weight rows are consecutive rows of one matrix, so chunk c (blocks CB c .. CB c + CB - 1
+// of every row) is 16 runs of 40 CB contiguous bytes: fetched as 16-byte pieces (fully
+// used cache lines, a quarter of the requests of per-lane 8- and 2-byte reads) two chunks
+// ahead in registers, written to LDS when their turn comes, and read from there per block.
+// LDS rows are padded so the 16 lanes reading one column group hit distinct banks.
+template <int NB>
+struct StqStreamL {
+  static constexpr int CB = NB % 4 == 0 ? 4 : 2;           // blocks per chunk (NB even)
+  static constexpr int NC = NB / CB;                       // chunks
+  static constexpr int RUN = 40 * CB;                      // bytes of one row in a chunk
+  static constexpr int PPR = RUN / 16;                     // 16-byte pieces per row run
+  static constexpr int NL = (16 * PPR + 63) / 64;          // loads per lane per chunk
+  static constexpr int CROW = CB == 4 ? 176 : 112;         // padded LDS bytes per row
+  static constexpr int BYTES = 16 * CROW;                  // LDS bytes per wave
+  static_assert(NB % 2 == 0, "whole chunks");
+  uint4 v[2][NL];
+  uint4 sc, sc_next;
+  rsrc_t tile;             // the wave's 16 rows (16 x 40 NB bytes)
+  const uint16_t* sp;
+  uint8_t* buf;            // this wave's LDS buffer
+
+  // piece m of this lane: row and byte offset inside the row run (lanes past the last
+  // piece reload piece 0 and store nothing)
+  __device__ __forceinline__ static bool piece(int m, int& row, int& off) {
+    const int pc = 64 * m + (threadIdx.x & 63);
+    const bool ok = pc < 16 * PPR;
+    const int pp = ok ? pc : 0;
+    row = pp / PPR;
+    off = 16 * (pp % PPR);
+    return ok;
+  }
+  __device__ __forceinline__ void load_chunk(int slot, int c) {
+#pragma unroll
+    for (int m = 0; m < NL; ++m) {
+      int row, off;
+      piece(m, row, off);
+      v[slot][m] = bload16_nt(tile, (uint32_t)(row * 40 * NB + off), (uint32_t)(RUN * c));
+    }
+  }
+  __device__ __forceinline__ void store_chunk(int slot) {
+#pragma unroll
+    for (int m = 0; m < NL; ++m) {
+      int row, off;
+      if (piece(m, row, off)) *reinterpret_cast<uint4*>(buf + row * CROW + off) = v[slot][m];
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint8_t* tile_, const uint16_t* sp_, uint8_t* buf_) {
+    tile = make_rsrc(tile_, 16 * 40 * NB);
+    sp = sp_;
+    buf = buf_;
+    load_chunk(0, 0);
+    if (NC > 1) load_chunk(1, 1);
+    sc = load_scale_group<NB>(sp, 0);
+    sc_next = sc;
+    store_chunk(0);
+    if (NC > 2) load_chunk(0, 2);
+  }
+
+  __device__ __forceinline__ void next(int j, uint2& qj, uint32_t& qhj, float& d) {
+    if (j % 8 == 0) {
+      if (j > 0) sc = sc_next;
+      if (j + 8 < NB) sc_next = load_scale_group<NB>(sp, j / 8 + 1);
+    }
+    if (j % CB == 0 && j > 0) {
+      const int c = j / CB;
+      store_chunk(c & 1);
+      if (c + 2 < NC) load_chunk(c & 1, c + 2);
+    }
+    const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+    const uint8_t* bp = buf + col * CROW + 40 * (j % CB);
+    qj = *reinterpret_cast<const uint2*>(bp + 8 * g);
+    qhj = *reinterpret_cast<const uint16_t*>(bp + 32 + 2 * g);
+    d = scale_of(sc, j);
+  }
+
+  // as StqStream::run_lds
+  __device__ __forceinline__ f32x4_t run_lds(const uint2* lut, const uint16_t* a_lds) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    uint2 qj;
+    uint32_t qhj;
+    float d;
+    next(0, qj, qhj, d);
+    bf16x8_t wn[4];
+    stq_half_w(lut, qj, qhj, 0, wn);
+    f32x4_t b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+#pragma unroll
+    for (int hh = 0; hh < 2 * NB; ++hh) {
+      const int j = hh >> 1, h = hh & 1;
+      bf16x8_t wc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) wc[t] = wn[t];
+      float dj = d;
+      if (h == 0) {
+        stq_half_w(lut, qj, qhj, 1, wn);
+      } else if (j + 1 < NB) {
+        next(j + 1, qj, qhj, d);
+        stq_half_w(lut, qj, qhj, 0, wn);
+      }
+      uint4 av[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * (4 * h + t));
+      f32x4_t& bh = h ? b1 : b0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bh = mfma16(as_bf16x8(av[t]), wc[t], bh);
+      if (h == 1) {
+        acc[0] = fmaf(dj, b0[0] + b1[0], acc[0]); acc[1] = fmaf(dj, b0[1] + b1[1], acc[1]);
+        acc[2] = fmaf(dj, b0[2] + b1[2], acc[2]); acc[3] = fmaf(dj, b0[3] + b1[3], acc[3]);
+        pin4(acc);
+        b0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        b1 = b0;
+      }
+    }
+    return acc;
+  }
+};
+
 // Copy up to ROWS activation rows of K bf16 (row r from src_row(r)) into LDS rows of K
 // through the whole workgroup: issue() loads ROWS rows into registers (rows past `rows`
 // repeat the last one, so every load is unconditional), commit() writes the first `rows`
@@ -495,7 +626,7 @@ __device__ __forceinline__ void router_unit(const DecodeArgs& a, int rw, float (
   uint4 av[NS], bv[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    av[j] = bload16(rw_r, wo, 2 * 32 * j);
+    av[j] = bload16_nt(rw_r, wo, 2 * 32 * j);
     bv[j] = bload16(rx, xo, 2 * 32 * j);
   }
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -944,8 +1075,8 @@ __device__ __forceinline__ void shared_gateup_valu(const DecodeArgs& a, int sw, 
   uint4 bg[RS], bu[RS];
 #pragma unroll
   for (int c = 0; c < RS; ++c) {
-    bg[c] = *reinterpret_cast<const uint4*>(gp + 512 * c);
-    bu[c] = *reinterpret_cast<const uint4*>(up + 512 * c);
+    bg[c] = ntload16(gp + 512 * c);
+    bu[c] = ntload16(up + 512 * c);
   }
   xs.commit(T, s_x);
   lds_barrier();
@@ -957,8 +1088,8 @@ __device__ __forceinline__ void shared_gateup_valu(const DecodeArgs& a, int sw, 
   for (int c = 0; c < NJ; ++c) {
     const uint4 wg = bg[c % RS], wu = bu[c % RS];
     if (c + RS < NJ) {
-      bg[c % RS] = *reinterpret_cast<const uint4*>(gp + 512 * (c + RS));
-      bu[c % RS] = *reinterpret_cast<const uint4*>(up + 512 * (c + RS));
+      bg[c % RS] = ntload16(gp + 512 * (c + RS));
+      bu[c % RS] = ntload16(up + 512 * (c + RS));
     }
 #pragma unroll
     for (int t = 0; t < XR; ++t) {
@@ -1059,7 +1190,7 @@ struct SharedDown {
   __device__ __forceinline__ uint4 load(int it) const {
     const int j = it / NR, r = it % NR;
     const uint32_t cl = j == NJ - 1 ? lcol : (threadIdx.x & 63);
-    return bload16(rsd, rb + 2u * (r * I + 8 * cl), 2 * 512 * j);
+    return bload16_nt(rsd, rb + 2u * (r * I + 8 * cl), 2 * 512 * j);
   }
   __device__ __forceinline__ void issue(const DecodeArgs& a, int row0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1118,7 +1249,7 @@ struct SharedDown {
 template <int HB, int IB>
 __device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi, const uint2* s_lut,
                                                     const uint16_t* s_x, float (*s_red)[2][4][64],
-                                                    const SmallRoute& R) {
+                                                    const SmallRoute& R, uint8_t* s_cw) {
   constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
@@ -1128,8 +1259,9 @@ __device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi,
   const int mat = wave & 1, tl = wave >> 1;
   const int row0 = (2 * tp + tl) * 16;
   const size_t wrow = (size_t)e * I + row0 + col;
-  StqStream<HB, 8> st;
-  st.issue((mat ? a.uc : a.gc) + wrow * HB * 40, (mat ? a.us : a.gs) + wrow * HB);
+  StqStreamL<HB> st;
+  st.issue((mat ? a.uc : a.gc) + (wrow - col) * HB * 40, (mat ? a.us : a.gs) + wrow * HB,
+           s_cw + wave * StqStreamL<HB>::BYTES);
   const int tok = R.utok[pos0 + (col < ntok ? col : ntok - 1)];
   const f32x4_t acc = st.run_lds(s_lut, s_x + tok * H + 64 * g);
 #pragma unroll
@@ -1197,7 +1329,7 @@ __device__ __forceinline__ void routed_gateup_e2m1(const DecodeArgs& a, int wi, 
 // row staged in LDS while they are read) beside the shared expert's gate/up.  Nothing in
 // it waits on a chain of dependent loads longer than one round trip.
 template <int HB, int IB, int XR, bool F4>
-__global__ __launch_bounds__(F4 ? 512 : kWG) __attribute__((amdgpu_waves_per_eu(F4 ? 4 : 5))) void k2s_gateup(DecodeArgs a) {
+__global__ __launch_bounds__(F4 ? 512 : kWG) __attribute__((amdgpu_waves_per_eu(4))) void k2s_gateup(DecodeArgs a) {
   constexpr int H = HB * 256, I = IB * 256, NT = F4 ? 512 : kWG, NTL = F4 ? NT / 128 : 2;
   constexpr int NTP = I / (16 * NTL);
   extern __shared__ __align__(16) uint16_t s_x[];   // XR x rows (bf16), or on the E2M1 path
@@ -1208,6 +1340,7 @@ __global__ __launch_bounds__(F4 ? 512 : kWG) __attribute__((amdgpu_waves_per_eu(
   __shared__ __align__(16) float s_red4[F4 ? NTL : 1][2][64];
   __shared__ float s_hv[F4 ? 16 : 1][F4 ? 16 * NTL : 1];
   __shared__ SmallRoute s_rt;
+  __shared__ __align__(16) uint8_t s_cw[F4 ? 16 : kNW * StqStreamL<HB>::BYTES];   // code staging
   const int b = blockIdx.x;
   const int T = a.T;
   if (b >= a.n_gu_wg) {
@@ -1247,7 +1380,8 @@ __global__ __launch_bounds__(F4 ? 512 : kWG) __attribute__((amdgpu_waves_per_eu(
     small_route_topk(a, s_rt, in, b == 0);
     small_route_units(a, s_rt, b == 0);
     const int n_items = s_rt.n_units * (I / 32);
-    for (int wi = b; wi < n_items; wi += a.n_gu_wg) routed_gateup_small<HB, IB>(a, wi, s_lut, s_x, s_red, s_rt);
+    for (int wi = b; wi < n_items; wi += a.n_gu_wg)
+      routed_gateup_small<HB, IB>(a, wi, s_lut, s_x, s_red, s_rt, s_cw);
   }
 }
 
