@@ -214,7 +214,7 @@ def prefill_bench(args):
 
 
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
-    "decode_k1_route": "k1_route", "decode_k2_gateup": "k2s_gateup",
+    "decode_k1_route": "k1s_router", "decode_k2_gateup": "k2s_gateup",
     "decode_k3_down_combine": "k3_down_combine", "mx_gateup": "mx_gemm_kernel<true>",
     "mx_down": "mx_gemm_kernel<false>", "copy": "neg_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hy4_t1_hbm_traffic.md")

@@ -103,8 +103,9 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff 
 }
 // Weight streams read in whole cache lines by one load are read once per call: non-temporal
 // loads (cache policy nt) keep them from evicting what is reused from L2 -- activations,
-// routing data, h, and the kernels' code.  (Streams that touch a line through several
-// smaller loads keep normal loads: an nt line may be gone before its next touch.)
+// routing data, h, and the kernels' code.  Streams that touch a line through several loads
+// (the STQ1_0 code words: a 40-byte block, a 160-byte run of a row, straddle lines) keep
+// normal loads: an nt line may be gone before its next touch (measured: +13 % fetched).
 constexpr int kNT = 2;
 __device__ __forceinline__ uint4 bload16_nt(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT));
@@ -488,7 +489,7 @@ struct StqStreamL {
     for (int m = 0; m < NL; ++m) {
       int row, off;
       piece(m, row, off);
-      v[slot][m] = bload16_nt(tile, (uint32_t)(row * 40 * NB + off), (uint32_t)(RUN * c));
+      v[slot][m] = bload16(tile, (uint32_t)(row * 40 * NB + off), (uint32_t)(RUN * c));
     }
   }
   __device__ __forceinline__ void store_chunk(int slot) {
