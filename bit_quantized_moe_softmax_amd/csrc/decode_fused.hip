@@ -86,11 +86,6 @@ struct DecodeArgs {
   uint16_t* hs;     // shared h [T][I] bf16 hi, then [T][I] bf16 lo
   int n_router_wg, n_sgu_wg, n_gu_wg;
   int h_lds;        // down kernel: all routed and shared h staged in LDS
-  uint8_t* xq;      // E2M1 path: [T][4][H] E4M3 parts of x
-  uint8_t* xs8;     //            [T][4][H / 32] their UE8M0 scales
-  uint8_t* hq;      //            [P][4][I] E4M3 parts of the routed h
-  uint8_t* hs8;     //            [P][4][I / 32] their scales
-  int n_xq_wg;      //            workgroups quantising x in the first kernel
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -186,68 +181,6 @@ __device__ __forceinline__ void stq_half_w(const uint2* lut, uint2 qs, uint32_t 
   for (int t = 0; t < 4; ++t) wv[t] = as_bf16x8(make_uint4(l[2 * t].x, l[2 * t].y, l[2 * t + 1].x, l[2 * t + 1].y));
 }
 
-// ---------------------------------------------------------------------------- E2M1 path
-// STQ1_0 weights are exactly -1, 0, +1, which E2M1 also represents (0xA, 0x0, 0x2): for up
-// to four tokens the routed experts run on the scaled MFMA with E2M1 weights and E4M3
-// activations.  An activation row is carried as four E4M3 parts (each the MX quantisation
-// of what the previous parts left over, ~16 significant bits in all), and a token's parts
-// take four A rows of the MFMA, so one MFMA covers 128 K of up to four tokens and the
-// parts add up inside a lane (D rows 4g .. 4g+3 = token g's parts).
-
-// The four E2M1 weights of one 5-bit STQ1_0 group pattern (weight j in bits 4j .. 4j+3).
-__device__ __forceinline__ uint32_t e2m1_group(uint32_t p) {
-  const uint32_t z = p >> 3;
-  uint32_t v = 0;
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    if (j == z) continue;
-    const uint32_t i = j < z ? j : j - 1;
-    v |= (((p >> i) & 1u) ? 0xAu : 0x2u) << (4 * j);
-  }
-  return v;
-}
-
-// 1024-entry table: a code byte (low nibbles of two consecutive patterns) with their two
-// high bits (index bits 8, 9) -> their eight E2M1 weights, first pattern in the low half.
-__device__ __forceinline__ void build_lut4(uint32_t* lut) {
-  for (uint32_t idx = threadIdx.x; idx < 1024; idx += blockDim.x) {
-    const uint32_t byte = idx & 0xFFu;
-    lut[idx] = e2m1_group((byte & 15u) | (((idx >> 8) & 1u) << 4)) |
-               (e2m1_group((byte >> 4) | (((idx >> 9) & 1u) << 4)) << 16);
-  }
-}
-
-// Exact value of an E4M3 code (no NaN codes are produced here).
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float v = e ? ldexpf((float)(8u + m), (int)e - 10) : ldexpf((float)m, -9);
-  return (c & 0x80u) ? -v : v;
-}
-
-// The four E4M3 parts of one value of a 32-element MX group, one element per lane of a
-// 32-lane half wave: part p is the MX quantisation (shared exponent from the group's
-// largest magnitude, nearest-even codes) of what parts 0 .. p-1 left.  Returns the four
-// code bytes packed (part p in byte p); the group's four scale bytes go to sc (the same in
-// every lane of the half).
-__device__ __forceinline__ uint32_t mx_parts4(float v, uint32_t& sc) {
-  uint32_t codes = 0;
-  sc = 0;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t am = __float_as_uint(v) & 0x7FFFFFFFu;
-    am = max(am, (uint32_t)__shfl_xor((int)am, 1, 64));
-    am = max(am, (uint32_t)__shfl_xor((int)am, 2, 64));
-    am = max(am, (uint32_t)__shfl_xor((int)am, 4, 64));
-    am = max(am, (uint32_t)__shfl_xor((int)am, 8, 64));
-    am = max(am, (uint32_t)__shfl_xor((int)am, 16, 64));
-    const int X = am ? moe_mx_exp(am) : -127;
-    const uint32_t c = am ? moe_e4m3_from_f32(__float_as_uint(v), X) : 0u;
-    codes |= c << (8 * p);
-    sc |= (uint32_t)(X + 127) << (8 * p);
-    v -= ldexpf(e4m3_value(c), X);
-  }
-  return codes;
-}
 
 // fp16 block scales of one row: words of two, in groups of 8 blocks (16 bytes, aligned
 // when NB >= 8), fewer blocks in one smaller aligned load.
@@ -377,48 +310,6 @@ struct StqStream {
         b0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
         b1 = b0;
       }
-    }
-    return acc;
-  }
-
-  // E2M1 weights against E4M3 activation parts from LDS: `a_row` = this lane's A row (token
-  // or pair x 4 + part, bytes, K order), `s_row` = its MX scale bytes (one per 32 K).  Per
-  // block: 8 table reads give the two 16-byte weight operands, two scaled MFMAs cover 128 K
-  // each (lane group g holds weights K = 64 g + 32 m .. + 31 of MFMA m; its A lanes hold the
-  // matching K = 64 (g / 2) + 32 m + 16 (g % 2) + 0..15 and + 128).
-  __device__ __forceinline__ f32x4_t run_e2m1(const uint32_t* lut4, const uint8_t* a_row, const uint8_t* s_row) {
-    const int g = (threadIdx.x & 63) >> 4;
-    const int c0 = 64 * (g >> 1) + 16 * (g & 1);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      uint2 qj;
-      uint32_t qhj;
-      float d;
-      next(j, qj, qhj, d);
-      uint32_t bw[2][4];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint32_t w = m ? qj.y : qj.x;
-        const uint32_t hb = qhj >> (8 * m);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) bw[m][t] = lut4[((w >> (8 * t)) & 0xFFu) | (((hb >> (2 * t)) & 3u) << 8)];
-      }
-      const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(s_row + 8 * j + 2 * g);
-      f32x4_t bacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint8_t* ap = a_row + 256 * j + 32 * m + c0;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(ap);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(ap + 128);
-        const i32x8_t aop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-        const i32x8_t bop = {(int)bw[m][0], (int)bw[m][1], (int)bw[m][2], (int)bw[m][3], 0, 0, 0, 0};
-        bacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, bacc, 0 /*A: E4M3*/, 4 /*B: E2M1*/,
-                                                               0, (int)((sc2 >> (8 * m)) & 0xFFu), 0, 127);
-      }
-      acc[0] = fmaf(d, bacc[0], acc[0]); acc[1] = fmaf(d, bacc[1], acc[1]);
-      acc[2] = fmaf(d, bacc[2], acc[2]); acc[3] = fmaf(d, bacc[3], acc[3]);
-      pin4(acc);
     }
     return acc;
   }
@@ -869,31 +760,11 @@ __device__ __forceinline__ void route_finalize(const DecodeArgs& a, FinalizeLds<
   }
 }
 
-// Quantisation of x into four E4M3 parts (E2M1 path): a half wave per 32-element group.
-template <int HB>
-__device__ __forceinline__ void x_quant(const DecodeArgs& a, int xw) {
-  constexpr int H = HB * 256, G = H / 32;
-  const int gi = xw * (kWG / 32) + (threadIdx.x >> 5), l = threadIdx.x & 31;
-  if (gi >= a.T * G) return;                      // uniform per half wave
-  const int t = gi / G, grp = gi % G;
-  uint32_t sc;
-  const uint32_t codes = mx_parts4(bf16_to_f32(a.x[(size_t)t * H + 32 * grp + l]), sc);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    a.xq[((size_t)t * 4 + p) * H + 32 * grp + l] = (uint8_t)(codes >> (8 * p));
-    if (l == 0) a.xs8[((size_t)t * 4 + p) * G + grp] = (uint8_t)(sc >> (8 * p));
-  }
-}
-
 template <int HB, int P0, int QN>
 __global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
   __shared__ __align__(16) float s_red[kNW][4][64];
   __shared__ int s_last;
   __shared__ FinalizeLds<P0> s_fin;
-  if ((int)blockIdx.x >= a.n_router_wg) {
-    x_quant<HB>(a, blockIdx.x - a.n_router_wg);
-    return;
-  }
   router_unit<HB>(a, blockIdx.x, s_red);
   if (threadIdx.x < 64) {
     __threadfence();     // wave 0 wrote this workgroup's partial: publish it device-wide
@@ -1280,97 +1151,21 @@ __device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi,
   __syncthreads();   // s_red is reused by the next work item
 }
 
-// Routed gate/up of one work item (unit, 16 NTL rows of I) on the E2M1 path: wave =
-// (16-row tile, gate|up); A rows = token x 4 + part from the staged x parts (s8: parts of
-// every token, then their scales).  Each 32 rows of h = SiLU(gate) * up of a pair form one
-// MX group of the down projection's K and are quantised here into four E4M3 parts (a half
-// wave per pair).
-template <int HB, int IB, int NTL>
-__device__ __forceinline__ void routed_gateup_e2m1(const DecodeArgs& a, int wi, const uint32_t* s_lut4,
-                                                   const uint8_t* s8, float (*s_red)[2][64],
-                                                   float (*s_hv)[16 * NTL]) {
-  constexpr int H = HB * 256, I = IB * 256, NTP = I / (16 * NTL);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int un_i = wi / NTP, tp = wi % NTP;
-  const int4 un = a.ut[un_i];
-  const int e = un.x, pos0 = un.y, ntok = un.z;
-  const int mat = wave & 1, tl = wave >> 1;
-  const int row0 = (NTL * tp + tl) * 16;
-  const size_t wrow = (size_t)e * I + row0 + col;
-  StqStream<HB, 8> st;
-  st.issue((mat ? a.uc : a.gc) + wrow * HB * 40, (mat ? a.us : a.gs) + wrow * HB);
-  const int ts = col >> 2;
-  const int tok = a.utok[un_i * 16 + (ts < ntok ? ts : ntok - 1)];
-  const int arow = 4 * tok + (col & 3);
-  const f32x4_t acc = st.run_e2m1(s_lut4, s8 + (size_t)arow * H, s8 + (size_t)4 * a.T * H + arow * (H / 32));
-  s_red[tl][mat][lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);   // token g: its four parts
-  __syncthreads();
-  if (mat == 0 && g < ntok) s_hv[g][16 * tl + col] = silu_mul(s_red[tl][0][lane], s_red[tl][1][lane]);
-  __syncthreads();
-  if (wave < NTL / 2) {
-    const int hp = lane >> 5, r = 32 * wave + (lane & 31);
-    for (int p0 = 0; p0 < ntok; p0 += 2) {
-      if (p0 + hp < ntok) {                     // uniform per half wave
-        uint32_t sc;
-        const uint32_t codes = mx_parts4(s_hv[p0 + hp][r], sc);
-        const size_t pr = (size_t)(pos0 + p0 + hp) * 4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          a.hq[(pr + q) * I + 16 * NTL * tp + r] = (uint8_t)(codes >> (8 * q));
-          if ((lane & 31) == 0) a.hs8[(pr + q) * (I / 32) + NTL * tp / 2 + wave] = (uint8_t)(sc >> (8 * q));
-        }
-      }
-    }
-  }
-  __syncthreads();   // s_red and s_hv are reused by the next work item
-}
-
-// Small T, second kernel: routed gate/up (units from the routing tables, every token's x
-// row staged in LDS while they are read) beside the shared expert's gate/up.  Nothing in
-// it waits on a chain of dependent loads longer than one round trip.
-template <int HB, int IB, int XR, bool F4>
-__global__ __launch_bounds__(F4 ? 512 : kWG) __attribute__((amdgpu_waves_per_eu(4))) void k2s_gateup(DecodeArgs a) {
-  constexpr int H = HB * 256, I = IB * 256, NT = F4 ? 512 : kWG, NTL = F4 ? NT / 128 : 2;
-  constexpr int NTP = I / (16 * NTL);
-  extern __shared__ __align__(16) uint16_t s_x[];   // XR x rows (bf16), or on the E2M1 path
-                                                    // every token's x parts and their scales
-  __shared__ uint2 s_lut[F4 ? 1 : 32];
-  __shared__ uint32_t s_lut4[F4 ? 1024 : 1];
+template <int HB, int IB, int XR>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k2s_gateup(DecodeArgs a) {
+  constexpr int H = HB * 256, I = IB * 256;
+  extern __shared__ __align__(16) uint16_t s_x[];   // XR x rows (bf16)
+  __shared__ uint2 s_lut[32];
   __shared__ __align__(16) float s_red[2][2][4][64];
-  __shared__ __align__(16) float s_red4[F4 ? NTL : 1][2][64];
-  __shared__ float s_hv[F4 ? 16 : 1][F4 ? 16 * NTL : 1];
   __shared__ SmallRoute s_rt;
-  __shared__ __align__(16) uint8_t s_cw[F4 ? 16 : kNW * StqStreamL<HB>::BYTES];   // code staging
+  __shared__ __align__(16) uint8_t s_cw[kNW * StqStreamL<HB>::BYTES];   // code staging
   const int b = blockIdx.x;
   const int T = a.T;
   if (b >= a.n_gu_wg) {
-    shared_gateup_valu<HB, IB, XR, NT>(a, b - a.n_gu_wg, s_x);
+    shared_gateup_valu<HB, IB, XR, kWG>(a, b - a.n_gu_wg, s_x);
     return;
   }
-  if constexpr (F4) {
-    // x parts (T x 4 rows of H bytes) then their scales (T x 4 rows of H / 32): 16-byte
-    // pieces, kPer per thread for one token
-    constexpr int kPer = (H / 4 + H / 128 + NT - 1) / NT;
-    const int nq = T * 4 * H / 16, ns = T * 4 * (H / 32) / 16;
-    uint4 v[kPer];
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      int i = threadIdx.x + NT * m;
-      i = i < nq + ns ? i : 0;
-      v[m] = i < nq ? reinterpret_cast<const uint4*>(a.xq)[i] : reinterpret_cast<const uint4*>(a.xs8)[i - nq];
-    }
-    build_lut4(s_lut4);
-    const int n_items = a.wl[1] * NTP;
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int i = threadIdx.x + NT * m;
-      if (i < nq + ns) reinterpret_cast<uint4*>(s_x)[i] = v[m];
-    }
-    lds_barrier();
-    for (int wi = b; wi < n_items; wi += a.n_gu_wg)
-      routed_gateup_e2m1<HB, IB, NTL>(a, wi, s_lut4, reinterpret_cast<const uint8_t*>(s_x), s_red4, s_hv);
-  } else {
+  {
     // router partials first, then the x rows: both in flight together
     TopkIn in;
     if ((int)(threadIdx.x >> 6) < T) topk_load(a, threadIdx.x >> 6, in);
@@ -1435,7 +1230,7 @@ __device__ __forceinline__ void shared_down_mfma(const DecodeArgs& a, int row0, 
 // (expert, <= 8 pairs) spread over the 8 waves, each wave adding its results into its own
 // LDS sums; out = sum over waves in order (+ residual).  HLDS: all h (few tokens) is staged
 // in LDS first: routed hi rows, routed lo rows, shared hi rows, shared lo rows.
-template <int HB, int IB, bool SDN, bool HLDS, bool F4>
+template <int HB, int IB, bool SDN, bool HLDS>
 __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   constexpr int H = HB * 256, I = IB * 256;
   constexpr int kStage = 10;                 // uint4 per thread when h is staged
@@ -1443,15 +1238,13 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
                                              // pair's hi and lo reads fall in different banks
   extern __shared__ __align__(16) float s_dyn[];  // [kDnWaves][T][16] sums, then staged h
                                                   // or the shared partials [kDnWaves][4][64]
-  __shared__ uint2 s_lut[F4 ? 1 : 32];
-  __shared__ uint32_t s_lut4[F4 ? 1024 : 1];
+  __shared__ uint2 s_lut[32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, P = T * a.k;
   const int row0 = blockIdx.x * 16;
   const int col = lane & 15, g = lane >> 4;
   float* s_acc = s_dyn;
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn + kDnWaves * T * 16);
-  uint8_t* s8 = reinterpret_cast<uint8_t*>(s_h);
   // residual of this slice (T * 16 <= 1024 elements, two per thread), read up front
   const rsrc_t rres = make_rsrc(a.residual, a.residual ? (uint32_t)T * H * 4 : 0u);
   float rs[2];
@@ -1461,9 +1254,8 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
     const uint32_t o = i < T * 16 ? 4u * ((uint32_t)(i >> 4) * H + row0 + (i & 15)) : kOOB;
     rs[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rres, o, 0, 0));
   }
-  // staged h, 16-byte pieces: bf16 path: routed hi rows, routed lo rows, shared h;
-  // E2M1 path: routed h parts, their scales, shared h
-  const int n_r0 = F4 ? P * I / 4 : P * I / 8, n_r1 = F4 ? P * I / 128 : P * I / 8;
+  // staged h, 16-byte pieces: routed hi rows, routed lo rows, shared h
+  const int n_r0 = P * I / 8, n_r1 = P * I / 8;
   const int n_all = n_r0 + n_r1 + T * I / 4;
   uint4 hv[kStage];
   if constexpr (HLDS) {
@@ -1471,19 +1263,12 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
     for (int m = 0; m < kStage; ++m) {
       int i = tid + 64 * kDnWaves * m;
       i = i < n_all ? i : 0;
-      if constexpr (F4) {
-        hv[m] = i < n_r0 ? reinterpret_cast<const uint4*>(a.hq)[i]
-              : i < n_r0 + n_r1 ? reinterpret_cast<const uint4*>(a.hs8)[i - n_r0]
-              : reinterpret_cast<const uint4*>(a.hs)[i - n_r0 - n_r1];
-      } else {
-        hv[m] = i < n_r0 ? reinterpret_cast<const uint4*>(a.h_hi)[i]
-              : i < n_r0 + n_r1 ? reinterpret_cast<const uint4*>(a.h_hi + a.h_lo_bytes / 2)[i - n_r0]
-              : reinterpret_cast<const uint4*>(a.hs)[i - n_r0 - n_r1];
-      }
+      hv[m] = i < n_r0 ? reinterpret_cast<const uint4*>(a.h_hi)[i]
+            : i < n_r0 + n_r1 ? reinterpret_cast<const uint4*>(a.h_hi + a.h_lo_bytes / 2)[i - n_r0]
+            : reinterpret_cast<const uint4*>(a.hs)[i - n_r0 - n_r1];
     }
   }
-  if constexpr (F4) build_lut4(s_lut4);
-  else build_lut(s_lut);
+  build_lut(s_lut);
   for (int i = tid; i < kDnWaves * T * 16; i += 64 * kDnWaves) s_acc[i] = 0.f;
   // the staged rows land before any weight load is issued: otherwise they would queue
   // behind every workgroup's weight stream
@@ -1491,7 +1276,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
 #pragma unroll
     for (int m = 0; m < kStage; ++m) {
       const int i = tid + 64 * kDnWaves * m;
-      if (i < n_all) reinterpret_cast<uint4*>(s_h + (F4 || i < n_r0 ? 0 : kLoPad))[i] = hv[m];
+      if (i < n_all) reinterpret_cast<uint4*>(s_h + (i < n_r0 ? 0 : kLoPad))[i] = hv[m];
     }
   }
   // the shared rows' first weight chunks
@@ -1511,7 +1296,6 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   lds_barrier();
   if (a.sd) {
     if constexpr (SDN) shared_down_mfma<HB, IB>(a, row0, s_acc, s_dyn + kDnWaves * T * 16);
-    else if constexpr (HLDS && F4) sdn.run(a, row0, reinterpret_cast<const uint16_t*>(s8 + (size_t)16 * (n_r0 + n_r1)), s_acc);
     else if constexpr (HLDS) sdn.run(a, row0, s_h + 2 * P * I + kLoPad, s_acc);
     else sdn.run(a, row0, a.hs, s_acc);
   }
@@ -1523,21 +1307,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
       st.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
     }
     const int pos0 = hent.y, nq = hent.z;
-    if constexpr (F4) {
-      // entries of <= 4 pairs: A rows pair x 4 + part; lane group g's D rows are pair g's parts
-      const int sp = col >> 2;
-      const int row = 4 * (pos0 + (sp < nq ? sp : 0)) + (col & 3);
-      const int pm = min(g, nq - 1);
-      const int tk = a.utok[hent.w + pm];
-      const float wt = a.uw[hent.w + pm];
-      const f32x4_t acc = st.run_e2m1(s_lut4, s8 + (size_t)row * I, s8 + (size_t)16 * n_r0 + row * (I / 32));
-      if (g < nq) {
-        const float y = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        a.y_pairs[(size_t)(pos0 + g) * H + row0 + col] = y;
-        float* sa = &s_acc[(wave * T + tk) * 16 + col];
-        *sa = fmaf(wt, y, *sa);
-      }
-    } else {
+    {
       // entries of <= 8 pairs: A rows (pair, hi | lo); this lane's pairs are 2g, 2g+1
       const int sp2 = col >> 1;
       int tk[2];
@@ -1585,8 +1355,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
 }
 
 // Small T: router + routing; routed + shared gate/up; routed + shared down + combine.
-// F4: the routed experts on the E2M1 path (one token).
-template <int HB, int IB, int XR, bool F4>
+template <int HB, int IB, int XR>
 hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
   constexpr int H = HB * 256, I = IB * 256;
   const int T = a.T;
@@ -1594,26 +1363,22 @@ hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
   const int max_units = P < a.E ? P : a.E;   // T <= 16: an expert's pairs fit one unit
   const bool shared = a.sg != nullptr;
   a.n_router_wg = ((a.E + 15) / 16) * kRouterParts;
-  a.n_xq_wg = F4 ? (T * (H / 32) + kWG / 32 - 1) / (kWG / 32) : 0;
-  constexpr int NT2 = F4 ? 512 : kWG;           // gate/up workgroup size
-  a.n_sgu_wg = shared ? I / (NT2 / 64) : 0;
-  a.n_gu_wg = max_units * (I / (16 * (F4 ? NT2 / 128 : 2)));
-  const int hbytes = F4 ? P * 4 * I + P * 4 * (I / 32) + T * I * 4 : (P + T) * I * 4;
+  a.n_sgu_wg = shared ? I / kNW : 0;          // one shared row (gate and up) per wave
+  a.n_gu_wg = max_units * (I / 32);           // a unit's 32 rows of I per workgroup
+  const int hbytes = (P + T) * I * 4;
   a.h_lds = hbytes <= 10 * 64 * kDnWaves * 16 ? 1 : 0;
-  const size_t lds2x = F4 ? (size_t)T * 4 * H + (size_t)T * 4 * (H / 32) : 0;
-  const size_t lds2 = (size_t)XR * H * 2 > lds2x ? (size_t)XR * H * 2 : lds2x;
+  const size_t lds2 = (size_t)XR * H * 2;
   const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (a.h_lds ? (size_t)hbytes + 64 : 0);
   const bool prof = moe_prof_on();
   if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
-  if constexpr (F4) hipLaunchKernelGGL((k1_route<HB, kMaxPL, 4>), dim3(a.n_router_wg + a.n_xq_wg), dim3(kWG), 0, s, a);
-  else hipLaunchKernelGGL((k1s_router<HB>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
+  hipLaunchKernelGGL((k1s_router<HB>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
-  hipLaunchKernelGGL((k2s_gateup<HB, IB, XR, F4>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(NT2), lds2, s, a);
+  hipLaunchKernelGGL((k2s_gateup<HB, IB, XR>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(kWG), lds2, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
-  if (a.h_lds) hipLaunchKernelGGL((k3_down_combine<HB, IB, false, true, F4>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
-  else hipLaunchKernelGGL((k3_down_combine<HB, IB, false, false, F4>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  if (a.h_lds) hipLaunchKernelGGL((k3_down_combine<HB, IB, false, true>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  else hipLaunchKernelGGL((k3_down_combine<HB, IB, false, false>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
   return hipSuccess;
@@ -1638,14 +1403,13 @@ hipError_t launch_large(DecodeArgs& a, hipStream_t s) {
   const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (size_t)kDnWaves * 4 * 64 * 4;
   const bool prof = moe_prof_on();
   if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
-  a.n_xq_wg = 0;
   hipLaunchKernelGGL((k1_route<HB, kMaxT * 32, 8>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
   hipLaunchKernelGGL((k2_gateup<HB, IB>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(kWG), lds2, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
-  hipLaunchKernelGGL((k3_down_combine<HB, IB, true, false, false>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  hipLaunchKernelGGL((k3_down_combine<HB, IB, true, false>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
   return hipSuccess;
@@ -1653,9 +1417,9 @@ hipError_t launch_large(DecodeArgs& a, hipStream_t s) {
 
 template <int HB, int IB>
 hipError_t launch_shape(DecodeArgs& a, hipStream_t s) {
-  if (a.T == 1) return launch_small<HB, IB, 1, false>(a, s);
-  if (a.T == 2) return launch_small<HB, IB, 2, false>(a, s);
-  if (a.T <= kXT) return launch_small<HB, IB, kXT, false>(a, s);
+  if (a.T == 1) return launch_small<HB, IB, 1>(a, s);
+  if (a.T == 2) return launch_small<HB, IB, 2>(a, s);
+  if (a.T <= kXT) return launch_small<HB, IB, kXT>(a, s);
   return launch_large<HB, IB>(a, s);
 }
 
@@ -1686,11 +1450,7 @@ size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, s
   offs[6] = cur; cur = al(cur + P * I * 2);                                          // h hi
   offs[7] = cur; cur = al(cur + P * I * 2);                                          // h lo
   offs[8] = cur; cur = al(cur + (has_shared ? (size_t)T * I * 4 : 0));              // shared h hi, lo
-  offs[9] = cur; cur = al(cur + (size_t)T * 4 * H);                                  // x parts
-  offs[10] = cur; cur = al(cur + (size_t)T * 4 * (H / 32));                          // x part scales
-  offs[11] = cur; cur = al(cur + P * 4 * I);                                         // h parts
-  offs[12] = cur; cur = al(cur + P * 4 * (I / 32));                                  // h part scales
-  offs[13] = cur;
+  offs[9] = cur;
   return cur;
 }
 
@@ -1733,10 +1493,6 @@ hipError_t moe_launch_decode_fused(const moe_dims* d, const moe_experts* routed,
   a.h_lo_bytes = (uint32_t)(offs[7] - offs[6]);
   a.h_bytes = (uint32_t)(offs[7] - offs[6] + (size_t)d->T * d->k * d->I * 2);
   a.hs = reinterpret_cast<uint16_t*>(b + offs[8]);
-  a.xq = b + offs[9];
-  a.xs8 = b + offs[10];
-  a.hq = b + offs[11];
-  a.hs8 = b + offs[12];
   const int hb = d->H / 256, ib = d->I / 256;
   if (hb == 2 && ib == 1) return launch_shape<2, 1>(a, s);
   if (hb == 4 && ib == 2) return launch_shape<4, 2>(a, s);
