@@ -66,6 +66,35 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Largest value over each 16-lane row of the wave (the 16 columns of one MFMA D row), by
+// DPP within the row: swaps of neighbours and pairs, then the half-row and row mirrors.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // lanes ^ 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // lanes ^ 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  return v;
+}
+
+// E4M3 code of v / 2^X, nearest-even, saturated at 448 -- the rule of moe_e4m3_from_f32,
+// branch-free for the epilogue: y = v 2^-X is exact (a power-of-two scaling), the rounding
+// quantum is 2^max(floor(log2|y|) - 3, -9) and rint() rounds the scaled magnitude to the
+// nearest integer R (ties to even); R <= 16 picks the code.
+__device__ __forceinline__ uint32_t e4m3_code(float v, int X) {
+  const float y = ldexpf(v, -X);
+  const uint32_t yb = __float_as_uint(y);
+  const uint32_t sign = (yb >> 24) & 0x80u;
+  const int e = (int)((yb >> 23) & 0xFFu) - 127;
+  const int q = max(e - 3, -9);
+  const uint32_t R = (uint32_t)rintf(ldexpf(fabsf(y), -q));
+  const bool normal = q > -9 || R >= 8;
+  const int ef = q + 10 + (int)(R >> 4);
+  const uint32_t m = R == 16 ? 0u : R - 8;
+  uint32_t code = normal ? (((uint32_t)ef << 3) | m) : R;
+  code = (ef > 15 || (ef == 15 && m > 6)) ? 0x7Eu : code;
+  return sign | code;
+}
+
 struct Job {
   int e, m0, nrows, ntile;
 };
@@ -279,18 +308,24 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
       if (mt >= mtiles) continue;
+      // the four rows of this lane group first, so their reductions overlap
+      float hh[4][2];
+      uint32_t am[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rl = 16 * mt + 4 * g + i;
-        float h[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const float gv = acc[mt][q][i], uv = acc[mt][q + 2][i];
-          h[q] = gv / (1.0f + expf(-gv)) * uv;
+          hh[i][q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
         }
-        uint32_t amax = max(__float_as_uint(h[0]) & 0x7FFFFFFFu, __float_as_uint(h[1]) & 0x7FFFFFFFu);
+        am[i] = row16_max(max(__float_as_uint(hh[i][0]) & 0x7FFFFFFFu,
+                              __float_as_uint(hh[i][1]) & 0x7FFFFFFFu));
+      }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 16 * mt + 4 * g + i;
+        const float h[2] = {hh[i][0], hh[i][1]};
+        const uint32_t amax = am[i];
         if (rl < nrows) {
           const int pos = jb.m0 + rl;
           uint8_t* hrow = p.hq + (size_t)pos * I + col0;
@@ -300,8 +335,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
             if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = 0;
           } else {
             const int X = moe_mx_exp(amax);
-            hrow[c16] = (uint8_t)moe_e4m3_from_f32(__float_as_uint(h[0]), X);
-            hrow[c16 + 16] = (uint8_t)moe_e4m3_from_f32(__float_as_uint(h[1]), X);
+            hrow[c16] = (uint8_t)e4m3_code(h[0], X);
+            hrow[c16 + 16] = (uint8_t)e4m3_code(h[1], X);
             if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = (uint8_t)(X + 127);
           }
         }
