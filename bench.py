@@ -183,13 +183,18 @@ def prefill_bench(args):
     routed = []
     for m in range(3):
         cd, sc = synth.mxfp4_family(c.seed, 0, m, c.E, *sh[m])
-        routed.append((dev(cd), dev(sc)))
-        del cd, sc
-    R = M.Experts(M.MOE_W_MXFP4, *routed)
+        dc, ds = dev(cd), dev(sc)
+        # one-time weight preparation: repack into the tiled layout the GEMMs stream
+        tc, ts = torch.empty_like(dc), torch.empty_like(ds)
+        M.moe_mxfp4_pack_tiles(dc, ds, c.E * sh[m][0], sh[m][1], tc, ts)
+        torch.cuda.synchronize()
+        routed.append((tc, ts))
+        del cd, sc, dc, ds
+    R = M.Experts(M.MOE_W_MXFP4_TILED, *routed)
     x = dev(synth.activations(c.seed, 0, c.T, c.H))
     logits = dev(synth.prefill_logits(c.seed, 0, c.T, c.E))
     log(f"prefill inputs ready in {time.perf_counter() - t0:.1f} s")
-    bufs = LayerBuffers(d, M.MOE_W_MXFP4, True)
+    bufs = LayerBuffers(d, M.MOE_W_MXFP4_TILED, True)
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
     M.moe_route(d, None, None, None, logits, bufs.logits, bufs.topk_ids, bufs.topk_w, s)
@@ -215,8 +220,8 @@ def prefill_bench(args):
 
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     "decode_k1_route": "k1s_router", "decode_k2_gateup": "k2s_gateup",
-    "decode_k3_down_combine": "k3_down_combine", "mx_gateup": "mx_gemm_kernel<true>",
-    "mx_down": "mx_gemm_kernel<false>", "copy": "neg_kernel"}
+    "decode_k3_down_combine": "k3_down_combine", "mx_gateup": "mx_gemm_kernel<true, true>",
+    "mx_down": "mx_gemm_kernel<false, true>", "copy": "neg_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hy4_t1_hbm_traffic.md")
 _DEC_SRC = "bit_quantized_moe_softmax_amd/csrc/decode_fused.hip"
 _MX_SRC = "bit_quantized_moe_softmax_amd/csrc/mx_gemm.hip"

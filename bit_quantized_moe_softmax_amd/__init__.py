@@ -13,6 +13,7 @@ import os
 
 __all__ = [
     "MoeError", "lib", "Dims", "Experts", "MOE_W_STQ1_0", "MOE_W_MXFP4", "MOE_W_BF16",
+    "MOE_W_MXFP4_TILED", "moe_mxfp4_pack_tiles",
     "COUNTER_NAMES", "moe_status_str", "moe_version", "moe_get_counters", "moe_reset_counters",
     "moe_route", "moe_permute", "moe_workspace_size", "moe_workspace_offsets", "moe_expert_ffn",
     "moe_combine", "moe_stq1_pack", "moe_stq1_dequant", "moe_mxfp4_dequant", "moe_mx_quant_act",
@@ -23,7 +24,7 @@ __all__ = [
 PROFILE_SLOTS = ["decode_k1_route", "decode_k2_gateup",
                  "decode_k3_down_combine", "reserved3", "mx_quant", "mx_gateup", "mx_down"]
 
-MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16 = 1, 2, 3
+MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16, MOE_W_MXFP4_TILED = 1, 2, 3, 4
 COUNTER_NAMES = ["route_gemv", "route_topk", "permute", "stq_gateup_mfma", "stq_down_mfma",
                  "stq_generic", "mx_quant", "mx_gateup_mfma", "mx_down_mfma", "bf16_gateup",
                  "bf16_down", "combine", "rmsnorm", "dequant", "bf16_gemm", "decode_fused"]
@@ -64,6 +65,7 @@ _SIGS = {
     "moe_stq1_pack": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P, _P, _P]),
     "moe_stq1_dequant": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P]),
     "moe_mxfp4_dequant": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
+    "moe_mxfp4_pack_tiles": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
     "moe_mx_quant_act": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P]),
     "moe_rmsnorm_bf16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
     "moe_layer_decode_workspace_size": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
@@ -210,6 +212,11 @@ def moe_stq1_dequant(codes, scales, n_blocks, out, stream=None):
 def moe_mxfp4_dequant(codes, scales, rows, K, out, stream=None):
     _check(lib().moe_mxfp4_dequant(_ptr(codes), _ptr(scales), int(rows), int(K), _ptr(out),
                                    _stream(stream)))
+
+
+def moe_mxfp4_pack_tiles(codes, scales, rows, K, tcodes, tscales, stream=None):
+    _check(lib().moe_mxfp4_pack_tiles(_ptr(codes), _ptr(scales), int(rows), int(K), _ptr(tcodes),
+                                      _ptr(tscales), _stream(stream)))
 
 
 def moe_mx_quant_act(rows, K, x_bf16, x_f32, q, s, stream=None):

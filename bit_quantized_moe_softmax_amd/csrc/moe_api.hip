@@ -57,13 +57,17 @@ void layout(const moe_dims* d, int fmt, int has_shared, size_t* offs) {
     offs[1] = cur;
     cur = align_up(cur + T * I * sizeof(float));
   }
-  if (fmt == MOE_W_MXFP4) {
+  if (fmt == MOE_W_MXFP4 || fmt == MOE_W_MXFP4_TILED) {
     offs[2] = cur; cur = align_up(cur + T * H);
     offs[3] = cur; cur = align_up(cur + T * (H / 32));
     offs[4] = cur; cur = align_up(cur + P * I);
     offs[5] = cur; cur = align_up(cur + P * (I / 32));
   }
   offs[6] = cur;
+}
+
+bool routed_fmt_ok(int fmt) {
+  return fmt == MOE_W_STQ1_0 || fmt == MOE_W_MXFP4 || fmt == MOE_W_MXFP4_TILED;
 }
 
 bool mat_ok(const moe_mat& m, bool need_scales) { return m.codes && (!need_scales || m.scales); }
@@ -195,7 +199,7 @@ moe_status moe_permute(const moe_dims* d, const int32_t* topk_ids, int32_t* sort
 moe_status moe_workspace_size(const moe_dims* d, int32_t routed_fmt, int32_t has_shared,
                               size_t* bytes) {
   if (!dims_ok(d) || !bytes) return MOE_ERR_INVALID_ARG;
-  if (routed_fmt != MOE_W_STQ1_0 && routed_fmt != MOE_W_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (!routed_fmt_ok(routed_fmt)) return MOE_ERR_INVALID_ARG;
   size_t offs[7];
   layout(d, routed_fmt, has_shared, offs);
   *bytes = offs[6];
@@ -205,7 +209,7 @@ moe_status moe_workspace_size(const moe_dims* d, int32_t routed_fmt, int32_t has
 moe_status moe_workspace_offsets(const moe_dims* d, int32_t routed_fmt, int32_t has_shared,
                                  size_t* offs) {
   if (!dims_ok(d) || !offs) return MOE_ERR_INVALID_ARG;
-  if (routed_fmt != MOE_W_STQ1_0 && routed_fmt != MOE_W_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (!routed_fmt_ok(routed_fmt)) return MOE_ERR_INVALID_ARG;
   layout(d, routed_fmt, has_shared, offs);
   return MOE_OK;
 }
@@ -218,7 +222,7 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
   if (!dims_ok(d) || !routed || !x_bf16 || !sorted_pair || !expert_offsets || !y_pairs)
     return MOE_ERR_INVALID_ARG;
   const int fmt = routed->fmt;
-  if (fmt != MOE_W_STQ1_0 && fmt != MOE_W_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (!routed_fmt_ok(fmt)) return MOE_ERR_INVALID_ARG;
   if (!mat_ok(routed->gate, true) || !mat_ok(routed->up, true) || !mat_ok(routed->down, true))
     return MOE_ERR_INVALID_ARG;
   if (shared) {
@@ -279,6 +283,7 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     a.wscales1 = static_cast<const uint8_t*>(routed->up.scales);
     a.aq = xq; a.as = xs; a.sorted_pair = sorted_pair; a.offsets = expert_offsets;
     a.hq = hq; a.hs = hs; a.N = I; a.K = H; a.T = T; a.E = E; a.k = k; a.P = P;
+    a.tiled = fmt == MOE_W_MXFP4_TILED;
     if (prof) moe_prof_begin(MOE_PROF_MX_GATEUP, s);
     e = moe_launch_mx_gateup(a, s);
     if (prof) moe_prof_end(MOE_PROF_MX_GATEUP, s);
@@ -289,6 +294,7 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     b.wscales0 = static_cast<const uint8_t*>(routed->down.scales);
     b.aq = hq; b.as = hs; b.sorted_pair = sorted_pair; b.offsets = expert_offsets;
     b.y = y_pairs; b.N = H; b.K = I; b.T = T; b.E = E; b.k = k; b.P = P;
+    b.tiled = fmt == MOE_W_MXFP4_TILED;
     if (prof) moe_prof_begin(MOE_PROF_MX_DOWN, s);
     e = moe_launch_mx_down(b, s);
     if (prof) moe_prof_end(MOE_PROF_MX_DOWN, s);
@@ -399,6 +405,24 @@ moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_
   hipStream_t s = as_stream(stream);
   bump(MOE_CNT_DEQUANT);
   return finish(moe_launch_mxfp4_dequant(codes, scales, rows, K, out, s), s);
+}
+
+moe_status moe_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                int32_t K, uint8_t* tcodes, uint8_t* tscales, void* stream) {
+  if (rows < 0 || K <= 0 || rows % 16 || K % 128) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!codes || !scales || !tcodes || !tscales) return MOE_ERR_INVALID_ARG;
+  if (((uintptr_t)codes | (uintptr_t)tcodes) % 16 || ((uintptr_t)scales | (uintptr_t)tscales) % 4)
+    return MOE_ERR_INVALID_ARG;
+  const uintptr_t nc = (uintptr_t)rows * (K / 2), ns = (uintptr_t)rows * (K / 32);
+  auto overlap = [](const void* a, uintptr_t na, const void* b, uintptr_t nb) {
+    return (uintptr_t)a < (uintptr_t)b + nb && (uintptr_t)b < (uintptr_t)a + na;
+  };
+  if (overlap(tcodes, nc, codes, nc) || overlap(tcodes, nc, scales, ns) ||
+      overlap(tscales, ns, codes, nc) || overlap(tscales, ns, scales, ns))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = as_stream(stream);
+  return finish(moe_launch_mxfp4_pack_tiles(codes, scales, rows, K, tcodes, tscales, s), s);
 }
 
 moe_status moe_mx_quant_act(int64_t rows, int32_t K, const uint16_t* x_bf16, const float* x_f32,

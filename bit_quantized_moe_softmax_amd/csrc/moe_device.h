@@ -173,8 +173,11 @@ struct MxArgs {
   uint8_t* hq; uint8_t* hs;                          // gate/up output (E4M3 h)
   float* y;                                          // down output
   int N, K, T, E, k, P;
+  int tiled;                                         // weights in the tiled MXFP4 layout
 };
 hipError_t moe_launch_mx_gateup(const MxArgs& a, hipStream_t s);
+hipError_t moe_launch_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales, long rows,
+                                       int K, uint8_t* tcodes, uint8_t* tscales, hipStream_t s);
 
 // Opt-in kernel timing with HIP events recorded on the launch stream around single kernels.
 enum {

@@ -17,9 +17,18 @@
 //
 // Tiling.  Four waves share the M block's activation rows, staged per K step (128) in LDS
 // (double-buffered, rows padded against bank conflicts).  Each wave owns 64 weight rows and
-// keeps their E2M1 codes in registers, loaded straight from HBM three K steps ahead: every
+// keeps their E2M1 codes in registers, loaded straight from HBM four K steps ahead: every
 // weight byte is used by exactly one wave, so it never passes through LDS.  Per K step a
 // wave issues up to 8 x 4 MFMAs (16-row tiles past the block's last pair are skipped).
+//
+// Weight layouts.  Row-major MXFP4 (codes [rows][K/2], scales [rows][K/32]) has each wave
+// read 64 bytes from each of 16 rows K/2 bytes apart per K step: half a cache line per row,
+// the other half a step later, which scatters the weight stream over DRAM pages.  The tiled
+// layout (moe_mxfp4_pack_tiles) stores the same bytes in the order the MFMA consumes them:
+// per 16-row tile and K step one 1 KiB block whose 16 bytes at 16 l are lane l's operand
+// (row l % 16, K bytes 16 (l / 16) .. + 15 of the step), and one 64-byte scale block (4 bytes
+// per row, byte g = scale of the step's K block g).  A wave then streams each of its tiles
+// as one contiguous run of K/2 * 16 bytes.
 //
 // Operand layout of the scaled 16x16x128 MFMA (measured with an in-bounds probe on gfx950,
 // K counted within the 128-wide step): lane l serves row/column l % 16 and lane group
@@ -151,10 +160,10 @@ __device__ Job find_job(const int32_t* __restrict__ off, int E, int NT, int lane
   return jb;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool TILED>
 __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   __shared__ __align__(16) uint8_t s_a[2][kMB * kAStride];
-  __shared__ uint32_t s_as[2][kMB];
+  __shared__ uint32_t s_as[2][256];   // entries >= kMB are written, never read
   __shared__ int s_arow[kMB];
   __shared__ Job s_job;
   const int tid = threadIdx.x;
@@ -204,8 +213,14 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   const rsrc_t rs0 = make_rsrc(p.wscales0 + jb.e * escales, (uint32_t)escales);
   const rsrc_t rb1 = GATEUP ? make_rsrc(p.wcodes1 + jb.e * ebytes, (uint32_t)ebytes) : rb0;
   const rsrc_t rs1 = GATEUP ? make_rsrc(p.wscales1 + jb.e * escales, (uint32_t)escales) : rs0;
-  const uint32_t brow = (uint32_t)((wvalid ? col0 : 0) + c16);
-  const uint32_t boff = brow * (K / 2) + 16 * g, bsoff = brow * (K / 32);
+  const uint32_t trow = (uint32_t)(wvalid ? col0 : 0);   // first row of the wave's first tile
+  const uint32_t brow = trow + c16;
+  // per-lane offsets of step 0 of the first tile; per step and tile the SGPR offset adds
+  // koff(k0) and qrow(q) rows (a tile of 16 rows is 16 rows in both layouts)
+  const uint32_t boff = TILED ? trow * (K / 2) + 16 * lane : brow * (K / 2) + 16 * g;
+  const uint32_t bsoff = TILED ? trow * (K / 32) + 4 * c16 : brow * (K / 32);
+  auto koff = [](int k0) { return TILED ? k0 * 8 : k0 / 2; };    // 1 KiB or 64 B per step
+  auto ksoff = [](int k0) { return TILED ? k0 / 2 : k0 / 32; };  // 64 B or 4 B per step
   // n-tile q starts qrow(q) rows after the lane's first row
   auto qrow = [](int q) { return GATEUP ? 16 * (q & 1) : 16 * q; };
 
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4*>(&s_a[buf][((tid >> 3) + 32 * i) * kAStride + 16 * achunk]) = ra[slot][i];
-    if (tid < kMB) s_as[buf][tid] = ras[slot];
+    s_as[buf][tid] = ras[slot];   // unconditional: keeps the load from sinking into a branch
   };
 
   uint4 rb[kRing][4];
@@ -231,8 +246,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool hi = GATEUP && q >= 2;
-      rb[slot][q] = bload16(hi ? rb1 : rb0, boff, qrow(q) * (K / 2) + k0 / 2);
-      rbs[slot][q] = bload4(hi ? rs1 : rs0, bsoff, qrow(q) * (K / 32) + k0 / 32);
+      rb[slot][q] = bload16(hi ? rb1 : rb0, boff, qrow(q) * (K / 2) + koff(k0));
+      rbs[slot][q] = bload4(hi ? rs1 : rs0, bsoff, qrow(q) * (K / 32) + ksoff(k0));
     }
   };
 
@@ -291,15 +306,24 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   for (int i = 0; i < kRing; ++i) {
     load_b(i, min(i, nsteps - 1) * kBK);
     if (i < kRing - 1) load_a(i, min(i, nsteps - 1) * kBK);
+    // keep the issue order of the steady state, whose wait counts the loop relies on
+    __builtin_amdgcn_sched_barrier(0);
   }
   store_a(0, 0);
   lds_barrier();
-  for (int s = 0; s < nsteps; s += kRing) {
+  // Whole groups of kRing steps first, with no branch between them: the compiler counts the
+  // loads in flight along every path into a wait, and a path that skipped steps would make
+  // it wait for loads issued one step earlier instead of kRing.
+  int s = 0;
+  for (; s + kRing <= nsteps; s += kRing) {
     step(s, std::integral_constant<int, 0>{});
-    if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
-    if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
-    if (s + 3 < nsteps) step(s + 3, std::integral_constant<int, 3>{});
+    step(s + 1, std::integral_constant<int, 1>{});
+    step(s + 2, std::integral_constant<int, 2>{});
+    step(s + 3, std::integral_constant<int, 3>{});
   }
+  if (s < nsteps) step(s, std::integral_constant<int, 0>{});
+  if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
+  if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
   if (!wvalid) return;
 
   // ---- epilogue.  D element (4*(lane/16)+i, lane%16) of each 16x16 tile is acc[..][..][i].
@@ -368,18 +392,60 @@ inline unsigned grid_for(const MxArgs& a, int NT) {
   return (unsigned)(kXcd * ((work + kXcd - 1) / kXcd));
 }
 
+// Row-major MXFP4 -> tiled layout.  One thread per 16-byte lane operand: tile t, K step j,
+// lane l read row 16 t + l % 16, bytes 64 j + 16 (l / 16) .. + 15; threads with l < 16 also
+// move the row's 4 scale bytes of the step.
+__global__ __launch_bounds__(256) void mx_pack_tiles_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            long rows, int K,
+                                                            uint8_t* __restrict__ tcodes,
+                                                            uint8_t* __restrict__ tscales) {
+  const int steps = K / kBK;
+  const long n = rows / 16 * steps * 64;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const int l = (int)(i & 63);
+    const long tj = i >> 6;
+    const int j = (int)(tj % steps);
+    const long t = tj / steps;
+    const long row = 16 * t + (l & 15);
+    const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + 64 * j + 16 * (l >> 4));
+    *reinterpret_cast<uint4*>(tcodes + 16 * i) = v;
+    if (l < 16) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(scales + row * (K / 32) + 4 * j);
+      *reinterpret_cast<uint32_t*>(tscales + 4 * (tj * 16 + l)) = w;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t moe_launch_mx_gateup(const MxArgs& a, hipStream_t s) {
   if (a.N % (kNTile / 2) || a.K % kBK) return hipErrorInvalidValue;
   const int NT = a.N / (kNTile / 2);
-  hipLaunchKernelGGL((mx_gemm_kernel<true>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+  if (a.tiled)
+    hipLaunchKernelGGL((mx_gemm_kernel<true, true>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<true, false>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t moe_launch_mx_down(const MxArgs& a, hipStream_t s) {
   if (a.N % kNWave || a.K % kBK) return hipErrorInvalidValue;
   const int NT = (a.N + kNTile - 1) / kNTile;
-  hipLaunchKernelGGL((mx_gemm_kernel<false>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+  if (a.tiled)
+    hipLaunchKernelGGL((mx_gemm_kernel<false, true>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<false, false>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales, long rows,
+                                       int K, uint8_t* tcodes, uint8_t* tscales, hipStream_t s) {
+  if (rows % 16 || K % kBK) return hipErrorInvalidValue;
+  const long n = rows / 16 * (K / kBK) * 64;
+  if (n == 0) return hipSuccess;
+  const long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(mx_pack_tiles_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+                     dim3(256), 0, s, codes, scales, rows, K, tcodes, tscales);
   return hipGetLastError();
 }

@@ -43,6 +43,13 @@
  * weights, group 32, UE8M0 scales):
  *   codes  : [out][in/2] bytes, element 2i in the low nibble (E2M1: bit 3 sign).
  *   scales : [out][in/32] UE8M0 bytes (value 2^(v-127)), groups along `in`.
+ * MXFP4_TILED: the MXFP4 bytes of each matrix reordered for the prefill GEMMs' matrix
+ * cores (made by moe_mxfp4_pack_tiles; same values, same size).  With R = out and
+ * S = in/128 K steps, for tile t < R/16, step j < S, lane l < 64:
+ *   codes  : bytes 1024*(t*S + j) + 16*l .. +15 = row 16t + l%16, codes bytes
+ *            64j + 16*(l/16) .. +15 of that row in the MXFP4 layout;
+ *   scales : bytes 64*(t*S + j) + 4*r .. +3 = row 16t + r, scale bytes 4j .. 4j+3.
+ *   Needs out % 16 == 0 and in % 128 == 0.
  * BF16 (shared expert, router): [out][in] uint16 bf16 bits.
  * Gate and up are [I][H] (out = I, in = H); down is [H][I].
  */
@@ -66,12 +73,12 @@ typedef enum {
   MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed         */
 } moe_status;
 
-typedef enum { MOE_W_STQ1_0 = 1, MOE_W_MXFP4 = 2, MOE_W_BF16 = 3 } moe_wfmt;
+typedef enum { MOE_W_STQ1_0 = 1, MOE_W_MXFP4 = 2, MOE_W_BF16 = 3, MOE_W_MXFP4_TILED = 4 } moe_wfmt;
 
 /* Layer dimensions: T tokens, hidden H, expert intermediate I, E routed experts,
  * k experts per token.  Limits: 1 <= k <= min(E, 32), E <= 1024, H % 32 == 0,
- * I % 32 == 0; STQ1_0 needs (I*H) % 256 == 0; MXFP4 needs H % 128 == 0 and
- * I % 128 == 0.  T == 0 is allowed and enqueues nothing. */
+ * I % 32 == 0; STQ1_0 needs (I*H) % 256 == 0; MXFP4 and MXFP4_TILED need H % 128 == 0
+ * and I % 128 == 0.  T == 0 is allowed and enqueues nothing. */
 typedef struct { int32_t T, H, I, E, k; } moe_dims;
 
 /* One weight family (gate, up or down) of `n` experts, expert-major. */
@@ -166,7 +173,7 @@ MOE_MI355X_API moe_status moe_workspace_size(const moe_dims* d, int32_t routed_f
 /* Byte offsets of the workspace regions, so tests can read the intermediates:
  *   offs[0] h of the routed pairs, fp32 [P][I] (STQ1_0 path)
  *   offs[1] h of the shared expert, fp32 [T][I]
- *   offs[2] x as E4M3 codes [T][H]          (MXFP4 path)
+ *   offs[2] x as E4M3 codes [T][H]          (MXFP4 and MXFP4_TILED paths)
  *   offs[3] x UE8M0 scales  [T][H/32]       (MXFP4 path)
  *   offs[4] h as E4M3 codes [P][I]          (MXFP4 path, sorted-pair order)
  *   offs[5] h UE8M0 scales  [P][I/32]       (MXFP4 path)
@@ -186,6 +193,8 @@ MOE_MI355X_API moe_status moe_workspace_offsets(const moe_dims* d, int32_t route
  *           h MX-quantised the same way along I before the down projection (every
  *           routed-expert linear of the WFP4AFP8 recipe takes FP8 E4M3 group-32
  *           activations); FP8 x FP4 products on the scaled MFMA, fp32 accumulation.
+ *   MXFP4_TILED: the MXFP4 computation, bit for bit, on weights in the tiled layout
+ *           (the layout the GEMMs stream fastest; the MXFP4 path reads row-major rows).
  * When `shared` is non-NULL (fmt MOE_W_BF16, one expert) y_shared[t] = the same
  * SwiGLU on bf16 weights and bf16 x[t] for every token, h kept in fp32.
  *   x_bf16 [T][H]; sorted_pair [P]; expert_offsets [E+1] (from moe_permute)
@@ -259,6 +268,16 @@ MOE_MI355X_API moe_status moe_stq1_dequant(const uint8_t* codes, const uint16_t*
 /* Decode MXFP4 rows: codes [rows][K/2], scales [rows][K/32] -> out [rows][K] fp32 (exact). */
 MOE_MI355X_API moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales,
                                             int64_t rows, int32_t K, float* out, void* stream);
+
+/* Reorder MXFP4 rows (codes [rows][K/2], scales [rows][K/32], rows % 16 == 0,
+ * K % 128 == 0) into the MXFP4_TILED layout: tcodes [rows*K/2], tscales [rows*K/32].
+ * A stack of matrices (E experts of `out` rows each) is one call with rows = E*out,
+ * since tiles never straddle a matrix when out % 16 == 0.  codes and tcodes must be
+ * 16-byte aligned, scales and tscales 4-byte aligned; outputs must not overlap the
+ * inputs.  A one-time weight preparation for MOE_W_MXFP4_TILED, not a per-step call. */
+MOE_MI355X_API moe_status moe_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales,
+                                               int64_t rows, int32_t K, uint8_t* tcodes,
+                                               uint8_t* tscales, void* stream);
 
 /* MX-quantise rows of K (K % 32 == 0) into E4M3 codes q [rows][K] and UE8M0 scales
  * s [rows][K/32].  Input is either bf16 (x_bf16) or fp32 (x_f32); exactly one must be

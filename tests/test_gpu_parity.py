@@ -45,10 +45,33 @@ def host(t, dtype=None):
     return a.view(dtype) if dtype is not None else a
 
 
-def routed_experts(c, routed):
+def routed_experts(c, routed, tiled=False):
+    """Device copies of the routed families; with tiled=True (MXFP4 only) each family is
+    repacked on the GPU into the tiled layout and the row-major copy is dropped."""
     fmt = M.MOE_W_STQ1_0 if c.fmt == "stq1" else M.MOE_W_MXFP4
     tens = [(dev(codes), dev(scales)) for codes, scales in routed]
+    if tiled:
+        assert fmt == M.MOE_W_MXFP4
+        out = []
+        for (cd, sc), (codes, _) in zip(tens, routed):
+            rows = codes.shape[0] * codes.shape[1] if codes.ndim == 3 else codes.shape[0]
+            K = 2 * codes.shape[-1]
+            tc, ts = torch.empty_like(cd), torch.empty_like(sc)
+            M.moe_mxfp4_pack_tiles(cd, sc, rows, K, tc, ts)
+            out.append((tc, ts))
+        torch.cuda.synchronize()
+        return M.Experts(M.MOE_W_MXFP4_TILED, *out)
     return M.Experts(fmt, *tens)
+
+
+def tiled_reference(codes, scales):
+    """The tiled MXFP4 layout by its definition: tile t, K step j, lane l = 16 g + r holds
+    row 16 t + r, code bytes 64 j + 16 g .. + 15; the step's scale block holds 4 bytes per row."""
+    R, KB = codes.shape
+    t, S = R // 16, KB // 64
+    tc = codes.reshape(t, 16, S, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    ts = scales.reshape(t, 16, S, 4).transpose(0, 2, 1, 3).reshape(-1)
+    return tc, ts
 
 
 def shared_experts(shared):
@@ -91,6 +114,22 @@ def test_mxfp4_dequant_bitexact():
     M.moe_mxfp4_dequant(dev(codes), dev(scales), rows, K, out)
     ref = O.mxfp4_matrix(codes, scales, rows, K).astype(np.float32)
     assert (host(out).view(np.uint32) == ref.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("rows,K", [(48, 384), (2048 * 3, 6144), (6144, 2048)])
+def test_mxfp4_pack_tiles_bitexact(rows, K):
+    say("mxfp4_pack_tiles", rows, K)
+    g = np.random.default_rng(rows + K)
+    codes = g.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    scales = g.integers(0, 256, size=(rows, K // 32), dtype=np.uint8)
+    tc = torch.empty(rows * K // 2, dtype=torch.uint8, device="cuda")
+    ts = torch.empty(rows * K // 32, dtype=torch.uint8, device="cuda")
+    M.moe_mxfp4_pack_tiles(dev(codes), dev(scales), rows, K, tc, ts)
+    rc, rs = tiled_reference(codes, scales)
+    assert (host(tc) == rc).all() and (host(ts) == rs).all()
+    # lane 17 of tile 0, step 1: row 1, code bytes 64 + 16 .. 64 + 31
+    if K >= 256:
+        assert (host(tc)[1024 + 16 * 17:1024 + 16 * 18] == codes[1, 80:96]).all()
 
 
 def _mx_case_rows(K):
@@ -360,13 +399,14 @@ MX_MORE = {
 }
 
 
+@pytest.mark.parametrize("tiled", [False, True], ids=["rowmajor", "tiled"])
 @pytest.mark.parametrize("name", list(MX_MORE))
-def test_mx_layer_blocks_and_tails(name):
+def test_mx_layer_blocks_and_tails(name, tiled):
     c = MX_MORE[name]
-    say("mx layer", name)
+    say("mx layer", name, "tiled" if tiled else "row-major")
     inp = layer_inputs(c)
     d = M.Dims(c.T, c.H, c.I, c.E, c.k)
-    routed = routed_experts(c, inp["routed"])
+    routed = routed_experts(c, inp["routed"], tiled)
     shared = shared_experts(inp["shared"])
     bufs = LayerBuffers(d, M.MOE_W_MXFP4, shared is not None)
     run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
@@ -383,7 +423,7 @@ def test_mx_layer_cfg3_hy4_prefill_sampled():
     say("mx cfg3 generate")
     inp = layer_inputs(c)
     d = M.Dims(c.T, c.H, c.I, c.E, c.k)
-    routed = routed_experts(c, inp["routed"])
+    routed = routed_experts(c, inp["routed"], tiled=True)   # the layout the prefill timing uses
     shared = shared_experts(inp["shared"])
     bufs = LayerBuffers(d, M.MOE_W_MXFP4, True)
     say("mx cfg3 run")
@@ -407,12 +447,13 @@ def test_mx_layer_cfg3_hy4_prefill_sampled():
     assert err.max() <= TOL
 
 
-def test_mx_layer_small_stages():
+@pytest.mark.parametrize("tiled", [False, True], ids=["rowmajor", "tiled"])
+def test_mx_layer_small_stages(tiled):
     c = MX_SMALL
-    say("mx layer small")
+    say("mx layer small", "tiled" if tiled else "row-major")
     inp = layer_inputs(c)
     d = M.Dims(c.T, c.H, c.I, c.E, c.k)
-    routed = routed_experts(c, inp["routed"])
+    routed = routed_experts(c, inp["routed"], tiled)
     shared = shared_experts(inp["shared"])
     bufs = LayerBuffers(d, M.MOE_W_MXFP4, True)
     run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
