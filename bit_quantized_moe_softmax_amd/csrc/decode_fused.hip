@@ -463,8 +463,8 @@ struct StqStreamL {
 
 // Copy up to ROWS activation rows of K bf16 (row r from src_row(r)) into LDS rows of K
 // through the whole workgroup: issue() loads ROWS rows into registers (rows past `rows`
-// repeat the last one, so every load is unconditional), commit() writes the first `rows`
-// once they have arrived.
+// repeat the last one, so every load is unconditional), commit() writes them once they
+// have arrived.  The LDS holds ROWS rows.
 template <int K, int NTHR, int ROWS>
 struct RowStage {
   static constexpr int PER = (K / 8 + NTHR - 1) / NTHR;   // uint4 per thread per row
@@ -481,15 +481,17 @@ struct RowStage {
       }
     }
   }
+  // Every one of the ROWS LDS rows is written (rows past `rows` get the repeated last row):
+  // with no branch around the writes the loads stay where issue() put them instead of
+  // being sunk to their first use.
   __device__ __forceinline__ void commit(int rows, uint16_t* lds) {
+    (void)rows;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      if (r < rows) {
 #pragma unroll
-        for (int m = 0; m < PER; ++m) {
-          const int i = threadIdx.x + NTHR * m;
-          if (K / 8 % NTHR == 0 || i < K / 8) reinterpret_cast<uint4*>(lds + (size_t)r * K)[i] = v[r][m];
-        }
+      for (int m = 0; m < PER; ++m) {
+        const int i = threadIdx.x + NTHR * m;
+        if (K / 8 % NTHR == 0 || i < K / 8) reinterpret_cast<uint4*>(lds + (size_t)r * K)[i] = v[r][m];
       }
     }
   }
@@ -583,7 +585,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-__device__ __forceinline__ void wave_topk(const DecodeArgs& a, int t, const TopkIn& in, float* s_v, int* s_i,
+// Router logits of this lane's four experts: the partials summed in a fixed order, plus
+// the bias.
+struct TopkSum {
+  float s[4];
+};
+__device__ __forceinline__ TopkSum topk_sums(const DecodeArgs& a, const TopkIn& in) {
+  TopkSum r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < kRouterParts; ++c) s += in.part[i][c];
+    if (a.bias) s += in.bias[i];
+    r.s[i] = s;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void wave_topk(const DecodeArgs& a, int t, const TopkSum& ls, float* s_v, int* s_i,
                                           int* ids_out, int* wbits_out, bool out) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
@@ -591,10 +611,7 @@ __device__ __forceinline__ void wave_topk(const DecodeArgs& a, int t, const Topk
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = i * 64 + lane;
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < kRouterParts; ++c) s += in.part[i][c];
-    if (a.bias) s += in.bias[i];
+    const float s = ls.s[i];
     if (out && e < E) a.logits[(size_t)t * E + e] = s;
     key[i] = e < E ? fkey(s) : 0u;
   }
@@ -654,7 +671,7 @@ __device__ __forceinline__ void route_finalize(const DecodeArgs& a, FinalizeLds<
   for (int t = wave; t < T; t += kNW) {
     TopkIn in;
     topk_load(a, t, in);
-    wave_topk(a, t, in, L.v[wave], L.i[wave], L.ids, L.ids + 2 * P0, true);
+    wave_topk(a, t, topk_sums(a, in), L.v[wave], L.i[wave], L.ids, L.ids + 2 * P0, true);
   }
   if (tid < E) L.cnt[tid] = 0;
   lds_barrier();
@@ -805,9 +822,9 @@ struct SmallRoute {
   int n_units;
 };
 
-__device__ __forceinline__ void small_route_topk(const DecodeArgs& a, SmallRoute& R, const TopkIn& in, bool out) {
+__device__ __forceinline__ void small_route_topk(const DecodeArgs& a, SmallRoute& R, const TopkSum& ls, bool out) {
   const int wave = threadIdx.x >> 6;
-  if (wave < a.T) wave_topk(a, wave, in, R.v[wave], R.i[wave], R.ids, R.wb, out);
+  if (wave < a.T) wave_topk(a, wave, ls, R.v[wave], R.i[wave], R.ids, R.wb, out);
 }
 
 __device__ __forceinline__ void small_route_units(const DecodeArgs& a, SmallRoute& R, bool out) {
@@ -832,7 +849,7 @@ __device__ __forceinline__ void small_route_units(const DecodeArgs& a, SmallRout
     }
   }
   if (out) {
-    for (int e = tid; e <= E; e += kWG) {
+    for (int e = tid; e <= E; e += (int)blockDim.x) {
       int before = 0;
       for (int f = 0; f < P; ++f) before += R.ids[f] < e;
       a.offsets[e] = before;
@@ -1166,14 +1183,18 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k
     return;
   }
   {
-    // router partials first, then the x rows: both in flight together
-    TopkIn in;
-    if ((int)(threadIdx.x >> 6) < T) topk_load(a, threadIdx.x >> 6, in);
+    // The x rows and the router partials are loaded and used in one branch-free stretch
+    // (every wave loads and sums some token's partials, only waves < T use them), so all of
+    // these loads are in flight together: a partial load placed in a branch would be sunk to
+    // its use and issued only after x had arrived.
     RowStage<H, kWG, XR> xs;
     xs.issue(T, [&](int r) { return a.x + (size_t)r * H; });
+    TopkIn in;
+    topk_load(a, min((int)(threadIdx.x >> 6), T - 1), in);
     build_lut(s_lut);
     xs.commit(T, s_x);
-    small_route_topk(a, s_rt, in, b == 0);
+    const TopkSum ls = topk_sums(a, in);
+    small_route_topk(a, s_rt, ls, b == 0);
     small_route_units(a, s_rt, b == 0);
     const int n_items = s_rt.n_units * (I / 32);
     for (int wi = b; wi < n_items; wi += a.n_gu_wg)
@@ -1257,15 +1278,18 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   // staged h, 16-byte pieces: routed hi rows, routed lo rows, shared h
   const int n_r0 = P * I / 8, n_r1 = P * I / 8;
   const int n_all = n_r0 + n_r1 + T * I / 4;
+  // h_lds is set only when the workspace holds routed hi, routed lo and shared h back to
+  // back, so the staging is one linear copy.  Branch-free: every piece is written below, so
+  // the compiler keeps all loads in flight together (a load inside a conditional write is
+  // sunk into it and waited for one at a time).  Pieces past the end reload and rewrite
+  // piece 0, the same value thread 0 writes there.
   uint4 hv[kStage];
   if constexpr (HLDS) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.h_hi);
 #pragma unroll
     for (int m = 0; m < kStage; ++m) {
-      int i = tid + 64 * kDnWaves * m;
-      i = i < n_all ? i : 0;
-      hv[m] = i < n_r0 ? reinterpret_cast<const uint4*>(a.h_hi)[i]
-            : i < n_r0 + n_r1 ? reinterpret_cast<const uint4*>(a.h_hi + a.h_lo_bytes / 2)[i - n_r0]
-            : reinterpret_cast<const uint4*>(a.hs)[i - n_r0 - n_r1];
+      const int i = tid + 64 * kDnWaves * m;
+      hv[m] = src[i < n_all ? i : 0];
     }
   }
   build_lut(s_lut);
@@ -1275,8 +1299,9 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   if constexpr (HLDS) {
 #pragma unroll
     for (int m = 0; m < kStage; ++m) {
-      const int i = tid + 64 * kDnWaves * m;
-      if (i < n_all) reinterpret_cast<uint4*>(s_h + (i < n_r0 ? 0 : kLoPad))[i] = hv[m];
+      int i = tid + 64 * kDnWaves * m;
+      i = i < n_all ? i : 0;
+      reinterpret_cast<uint4*>(s_h + (i < n_r0 ? 0 : kLoPad))[i] = hv[m];
     }
   }
   // the shared rows' first weight chunks
@@ -1366,7 +1391,10 @@ hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
   a.n_sgu_wg = shared ? I / kNW : 0;          // one shared row (gate and up) per wave
   a.n_gu_wg = max_units * (I / 32);           // a unit's 32 rows of I per workgroup
   const int hbytes = (P + T) * I * 4;
-  a.h_lds = hbytes <= 10 * 64 * kDnWaves * 16 ? 1 : 0;
+  // LDS staging of h copies routed hi, routed lo and shared h as one run
+  const bool h_run = a.h_lo_bytes == (uint32_t)P * I * 2 &&
+                     (!shared || a.hs == a.h_hi + (size_t)2 * P * I);
+  a.h_lds = h_run && hbytes <= 10 * 64 * kDnWaves * 16 ? 1 : 0;
   const size_t lds2 = (size_t)XR * H * 2;
   const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (a.h_lds ? (size_t)hbytes + 64 : 0);
   const bool prof = moe_prof_on();

@@ -477,6 +477,9 @@ FUSED = {
     "h1024-i512-e16-top4-t3-zipf": synth.LayerCfg("t", 3, 1024, 512, 16, 4, True, "stq1", True, False, 1, 24),
     "h512-i256-e4-top4-t2-noshared": synth.LayerCfg("t", 2, 512, 256, 4, 4, False, "stq1", False, False, 1, 25),
     "h512-i256-e64-top32-t4-shared": synth.LayerCfg("t", 4, 512, 256, 64, 32, True, "stq1", False, False, 1, 26),
+    # one token at H a multiple of 2048: the K-quarter table path of the gate/up kernel
+    "h2048-i1024-e16-top4-t1-shared": synth.LayerCfg("t", 1, 2048, 1024, 16, 4, True, "stq1", False, False, 1, 27),
+    "h4096-i2048-e32-top8-t1-zipf-noshared": synth.LayerCfg("t", 1, 4096, 2048, 32, 8, False, "stq1", True, False, 1, 28),
 }
 
 
