@@ -119,44 +119,53 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 
 __device__ __forceinline__ int blocks_of(int cnt) { return (cnt + kMB - 1) / kMB; }
 
-// Wave 0: the job of this workgroup, or e = -1.
-__device__ Job find_job(const int32_t* __restrict__ off, int E, int NT, int lane) {
-  int total = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    const int nb = e < E ? blocks_of(off[e + 1] - off[e]) : 0;
-    total += __shfl(wave_incl_scan(nb, lane), 63, 64);
-  }
-  const long n_work = (long)total * NT;
-  const int x = blockIdx.x % kXcd, j = blockIdx.x / kXcd;
-  const long lo = n_work * x / kXcd, hi = n_work * (x + 1) / kXcd;
-  Job jb{-1, 0, 0, 0};
-  if (lo + j >= hi) return jb;
-  const long w = lo + j;
-  const int entry = (int)(w / NT);
-  jb.ntile = (int)(w % NT);
+constexpr int kMaxE = 1024;
+
+// Per-workgroup job tables in LDS, built once: the expert offsets, and nb[e] = M blocks of
+// the experts before e (nb[E] = all blocks).
+struct JobTable {
+  int off[kMaxE + 1];
+  int nb[kMaxE + 1];
+};
+
+// Wave 0 builds the tables (the caller synchronises before use).
+__device__ void build_job_table(const int32_t* __restrict__ off, int E, JobTable& t, int lane) {
   int run = 0;
   for (int base = 0; base < E; base += 64) {
     const int e = base + lane;
-    const int cnt = e < E ? off[e + 1] - off[e] : 0;
-    const int nb = blocks_of(cnt);
+    const int o0 = e < E ? off[e] : 0, o1 = e < E ? off[e + 1] : 0;
+    const int nb = e < E ? blocks_of(o1 - o0) : 0;
     const int incl = wave_incl_scan(nb, lane);
-    const int tot = __shfl(incl, 63, 64);
-    if (entry < run + tot) {
-      const bool hit = nb > 0 && run + incl - nb <= entry && entry < run + incl;
-      const uint64_t m = __ballot(hit);
-      const int L = __ffsll((unsigned long long)m) - 1;
-      const int es = base + L;
-      const int mb = entry - run - (__shfl(incl, L, 64) - __shfl(nb, L, 64));
-      const int c = __shfl(cnt, L, 64), nbs = __shfl(nb, L, 64);
-      const int r0 = (int)((long)c * mb / nbs), r1 = (int)((long)c * (mb + 1) / nbs);
-      jb.e = es;
-      jb.m0 = off[es] + r0;
-      jb.nrows = r1 - r0;
-      return jb;
+    if (e < E) {
+      t.off[e] = o0;
+      t.nb[e + 1] = run + incl;
     }
-    run += tot;
+    run += __shfl(incl, 63, 64);
   }
+  if (lane == 0) {
+    t.off[E] = off[E];
+    t.nb[0] = 0;
+  }
+}
+
+// Job w (< all blocks x NT): the expert whose blocks hold entry w / NT, found by binary
+// search over nb (every thread, same result), and the rows of that block.
+__device__ __forceinline__ Job decode_job(const JobTable& t, int E, int NT, long w) {
+  const int entry = (int)(w / NT);
+  Job jb;
+  jb.ntile = (int)(w % NT);
+  int lo = 0, hi = E;   // the largest e with nb[e] <= entry (then nb[e + 1] > entry)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.nb[mid] <= entry) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int mb = entry - t.nb[e], nbs = t.nb[e + 1] - t.nb[e];
+  const int c = t.off[e + 1] - t.off[e];
+  const int r0 = (int)((long)c * mb / nbs), r1 = (int)((long)c * (mb + 1) / nbs);
+  jb.e = e;
+  jb.m0 = t.off[e] + r0;
+  jb.nrows = r1 - r0;
   return jb;
 }
 
@@ -165,20 +174,22 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   __shared__ __align__(16) uint8_t s_a[2][kMB * kAStride];
   __shared__ uint32_t s_as[2][256];   // entries >= kMB are written, never read
   __shared__ int s_arow[kMB];
-  __shared__ Job s_job;
+  __shared__ JobTable s_jt;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int K = p.K, N = p.N;
   const int NT = GATEUP ? N / (kNTile / 2) : (N + kNTile - 1) / kNTile;
 
-  if (wave == 0) {
-    const Job jb = find_job(p.offsets, p.E, NT, lane);
-    if (lane == 0) s_job = jb;
-  }
+  if (wave == 0) build_job_table(p.offsets, p.E, s_jt, lane);
   __syncthreads();
-  const Job jb = s_job;
-  if (jb.e < 0) return;
+  // Persistent: the jobs of XCD x are one contiguous range, taken by its workgroups in turn,
+  // so the N tiles that share an M block's activation rows run together behind one L2.
+  const long n_work = (long)s_jt.nb[p.E] * NT;
+  const int x = blockIdx.x % kXcd, slot = blockIdx.x / kXcd, nslot = gridDim.x / kXcd;
+  const long w_lo = n_work * x / kXcd, w_hi = n_work * (x + 1) / kXcd;
+  for (long w = w_lo + slot; w < w_hi; w += nslot) {
+  const Job jb = decode_job(s_jt, p.E, NT, w);
   const int nrows = jb.nrows;
   if (tid < kMB) {
     int src = -1;
@@ -324,8 +335,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   if (s < nsteps) step(s, std::integral_constant<int, 0>{});
   if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
   if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
-  if (!wvalid) return;
-
+  if (wvalid) {
   // ---- epilogue.  D element (4*(lane/16)+i, lane%16) of each 16x16 tile is acc[..][..][i].
   if (GATEUP) {
     const int I = N;
@@ -381,6 +391,9 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
       }
     }
   }
+  }   // wvalid
+  __syncthreads();   // s_arow and the LDS buffers are reused by the next job
+  }   // jobs
 }
 
 // Grid: enough workgroups for the most jobs any routing of P pairs over E experts makes
@@ -389,7 +402,18 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
 inline unsigned grid_for(const MxArgs& a, int NT) {
   const long slots = (a.P < a.E ? a.P : a.E) + (a.P + kMB - 1) / kMB;
   const long work = slots * NT;
-  return (unsigned)(kXcd * ((work + kXcd - 1) / kXcd));
+  const long most = kXcd * ((work + kXcd - 1) / kXcd);
+  // persistent: one workgroup per CU (the kernel holds one per CU), in whole XCD groups
+  static int n_cu[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (n_cu[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    n_cu[dev] = n;
+  }
+  const long per = kXcd * ((n_cu[dev] + kXcd - 1) / kXcd);
+  return (unsigned)(most < per ? most : per);
 }
 
 // Row-major MXFP4 -> tiled layout.  One thread per 16-byte lane operand: tile t, K step j,
