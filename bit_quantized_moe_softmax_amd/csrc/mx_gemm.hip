@@ -10,10 +10,12 @@
 // Work split.  The pairs of one expert (contiguous in sorted order) are cut into M blocks
 // of at most 128 rows, evenly (150 pairs -> 75 + 75).  A job is (M block, N tile of 256
 // weight rows): for gate/up 128 gate rows + the 128 up rows of the same h-columns, for down
-// 256 output columns.  Jobs are numbered expert-major with the N tile fastest, and the jobs
-// of one XCD are one contiguous range (workgroup b runs on XCD b % 8), so the N tiles that
-// share an M block's activation rows run together behind one L2.  Every workgroup finds its
-// job from the expert offsets; the grid is sized for the most jobs any routing can make.
+// 256 output columns.  Jobs are numbered expert-major, then by N tile, then by M block, and
+// the jobs of one XCD are one contiguous range (workgroup b runs on XCD b % 8): the blocks
+// of an expert that read the same weight tile run side by side, and the N tiles that share
+// an M block's activation rows run close together, behind one L2.  The kernel is
+// persistent: one workgroup per CU takes its XCD's jobs in turn, decoding each from job
+// tables built once in LDS.
 //
 // Tiling.  Four waves share the M block's activation rows, staged per K step (128) in LDS
 // (double-buffered, rows padded against bank conflicts).  Each wave owns 64 weight rows and
@@ -148,19 +150,22 @@ __device__ void build_job_table(const int32_t* __restrict__ off, int E, JobTable
   }
 }
 
-// Job w (< all blocks x NT): the expert whose blocks hold entry w / NT, found by binary
-// search over nb (every thread, same result), and the rows of that block.
+// Job w (< all blocks x NT).  Expert e owns jobs nb[e] NT .. nb[e + 1] NT - 1, ordered by N
+// tile, then M block: the blocks of one expert that read the same weight tile are
+// neighbours, run together, and the second read of the tile hits L2.  The expert is found
+// by binary search over nb (every thread, same result).
 __device__ __forceinline__ Job decode_job(const JobTable& t, int E, int NT, long w) {
-  const int entry = (int)(w / NT);
   Job jb;
-  jb.ntile = (int)(w % NT);
-  int lo = 0, hi = E;   // the largest e with nb[e] <= entry (then nb[e + 1] > entry)
+  int lo = 0, hi = E;   // the largest e with nb[e] NT <= w (then nb[e + 1] NT > w)
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (t.nb[mid] <= entry) lo = mid; else hi = mid - 1;
+    if ((long)t.nb[mid] * NT <= w) lo = mid; else hi = mid - 1;
   }
   const int e = lo;
-  const int mb = entry - t.nb[e], nbs = t.nb[e + 1] - t.nb[e];
+  const int nbs = t.nb[e + 1] - t.nb[e];
+  const int local = (int)(w - (long)t.nb[e] * NT);
+  jb.ntile = local / nbs;
+  const int mb = local % nbs;
   const int c = t.off[e + 1] - t.off[e];
   const int r0 = (int)((long)c * mb / nbs), r1 = (int)((long)c * (mb + 1) / nbs);
   jb.e = e;
