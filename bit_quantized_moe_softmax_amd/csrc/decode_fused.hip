@@ -1303,6 +1303,9 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
       i = i < n_all ? i : 0;
       reinterpret_cast<uint4*>(s_h + (i < n_r0 ? 0 : kLoPad))[i] = hv[m];
     }
+    // keep the weight loads below: hoisted above these writes, one wave's weight stream
+    // queued ahead of another wave's staging loads in the CU's in-order memory queue
+    __builtin_amdgcn_sched_barrier(0);
   }
   // the shared rows' first weight chunks
   SharedDown<HB, IB, 2, true> sdn;
