@@ -22,12 +22,14 @@ __all__ = [
 ]
 
 PROFILE_SLOTS = ["decode_k1_route", "decode_k2_gateup",
-                 "decode_k3_down_combine", "reserved3", "mx_quant", "mx_gateup", "mx_down"]
+                 "decode_k3_down_combine", "reserved3", "mx_quant", "mx_gateup", "mx_down",
+                 "stq_gateup", "stq_down", "shared_gateup", "shared_down", "act_prep"]
 
 MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16, MOE_W_MXFP4_TILED = 1, 2, 3, 4
 COUNTER_NAMES = ["route_gemv", "route_topk", "permute", "stq_gateup_mfma", "stq_down_mfma",
                  "stq_generic", "mx_quant", "mx_gateup_mfma", "mx_down_mfma", "bf16_gateup",
-                 "bf16_down", "combine", "rmsnorm", "dequant", "bf16_gemm", "decode_fused"]
+                 "bf16_down", "combine", "rmsnorm", "dequant", "bf16_gemm", "decode_fused",
+                 "stq_gemm", "rowscale"]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
@@ -154,7 +156,7 @@ def moe_version() -> str:
 
 
 def moe_get_counters() -> dict:
-    buf = (ctypes.c_uint64 * 16)()
+    buf = (ctypes.c_uint64 * len(COUNTER_NAMES))()
     _check(lib().moe_get_counters(ctypes.cast(buf, _P)))
     return {n: int(v) for n, v in zip(COUNTER_NAMES, buf)}
 

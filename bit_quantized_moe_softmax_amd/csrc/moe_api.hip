@@ -44,10 +44,33 @@ bool dims_ok(const moe_dims* d) {
   return true;
 }
 
-// Workspace regions: 0 h routed f32, 1 h shared f32, 2 xq, 3 xs, 4 hq, 5 hs, 6 total.
-void layout(const moe_dims* d, int fmt, int has_shared, size_t* offs) {
+// Token counts from which moe_expert_ffn runs the tiled prefill GEMMs instead of the
+// decode-shaped kernels: routed STQ1_0 experts, and the bf16 shared expert.
+// MOE_MI355X_PREFILL_MIN_T overrides both (measurement).
+int prefill_min_t(bool shared) {
+  static const int over = [] {
+    const char* v = std::getenv("MOE_MI355X_PREFILL_MIN_T");
+    return v ? std::atoi(v) : -1;
+  }();
+  if (over >= 0) return over;
+  return shared ? 64 : 64;
+}
+
+bool stq_gemm_ok(const moe_dims* d) {
+  return d->T >= prefill_min_t(false) && d->H % 256 == 0 && d->I % 256 == 0;
+}
+bool shared_gemm_ok(const moe_dims* d) {
+  return d->T >= prefill_min_t(true) && d->H % 256 == 0 && d->I % 256 == 0;
+}
+
+// Workspace regions: 0 h routed f32, 1 h shared f32, 2 xq, 3 xs, 4 hq, 5 hs, 6 total;
+// internal regions of the prefill GEMMs (ext): 0 x fp16 [T][H], 1 x row exponents [T],
+// 2 h as fp16 hi | lo [P][2I], 3 h row exponents [P], 4 shared h as bf16 hi | lo [T][2I].
+void layout(const moe_dims* d, int fmt, int has_shared, size_t* offs, size_t* ext = nullptr) {
   const size_t T = d->T, H = d->H, I = d->I, P = (size_t)d->T * d->k;
+  size_t e[5];
   for (int i = 0; i < 7; ++i) offs[i] = (size_t)-1;
+  for (int i = 0; i < 5; ++i) e[i] = (size_t)-1;
   size_t cur = 0;
   if (fmt == MOE_W_STQ1_0) {
     offs[0] = cur;
@@ -63,7 +86,18 @@ void layout(const moe_dims* d, int fmt, int has_shared, size_t* offs) {
     offs[4] = cur; cur = align_up(cur + P * I);
     offs[5] = cur; cur = align_up(cur + P * (I / 32));
   }
+  if (fmt == MOE_W_STQ1_0 && stq_gemm_ok(d)) {
+    e[0] = cur; cur = align_up(cur + T * H * 2);
+    e[1] = cur; cur = align_up(cur + T * 4);
+    e[2] = cur; cur = align_up(cur + P * 2 * I * 2);
+    e[3] = cur; cur = align_up(cur + P * 4);
+  }
+  if (has_shared && shared_gemm_ok(d)) {
+    e[4] = cur; cur = align_up(cur + T * 2 * I * 2);
+  }
   offs[6] = cur;
+  if (ext)
+    for (int i = 0; i < 5; ++i) ext[i] = e[i];
 }
 
 bool routed_fmt_ok(int fmt) {
@@ -239,15 +273,52 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
   } else {
     if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
   }
-  size_t offs[7];
-  layout(d, fmt, shared != nullptr, offs);
+  size_t offs[7], ext[5];
+  layout(d, fmt, shared != nullptr, offs, ext);
   if (!ws || ws_bytes < offs[6]) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   const int P = T * k;
 
-  if (fmt == MOE_W_STQ1_0) {
+  const bool prof = moe_prof_on();
+  if (fmt == MOE_W_STQ1_0 && ext[0] != (size_t)-1) {
+    // prefill: x -> fp16 rows, grouped GEMMs on the fp16 MFMA, h -> fp16 hi | lo rows
+    float* h = reinterpret_cast<float*>(wsb + offs[0]);
+    uint16_t* x16 = reinterpret_cast<uint16_t*>(wsb + ext[0]);
+    int32_t* xe = reinterpret_cast<int32_t*>(wsb + ext[1]);
+    uint16_t* h16 = reinterpret_cast<uint16_t*>(wsb + ext[2]);
+    int32_t* he = reinterpret_cast<int32_t*>(wsb + ext[3]);
+    if (prof) moe_prof_begin(MOE_PROF_ACT_PREP, s);
+    hipError_t e = moe_launch_rowscale_f16(x_bf16, nullptr, T, H, 0, x16, xe, s);
+    if (prof) moe_prof_end(MOE_PROF_ACT_PREP, s);
+    bump(MOE_CNT_ROWSCALE);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    G16Args a{};
+    a.w0 = routed->gate.codes; a.s0 = static_cast<const uint16_t*>(routed->gate.scales);
+    a.w1 = routed->up.codes;   a.s1 = static_cast<const uint16_t*>(routed->up.scales);
+    a.a = x16; a.aexp = xe; a.sorted_pair = sorted_pair; a.offsets = expert_offsets; a.out = h;
+    a.N = I; a.K = H; a.Ka = H; a.rows_a = T; a.E = E; a.k = k; a.P = P;
+    if (prof) moe_prof_begin(MOE_PROF_STQ_GATEUP, s);
+    e = moe_launch_g16_stq_gateup(a, s);
+    if (prof) moe_prof_end(MOE_PROF_STQ_GATEUP, s);
+    bump(MOE_CNT_STQ_GEMM);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (prof) moe_prof_begin(MOE_PROF_ACT_PREP, s);
+    e = moe_launch_rowscale_f16(nullptr, h, P, I, 1, h16, he, s);
+    if (prof) moe_prof_end(MOE_PROF_ACT_PREP, s);
+    bump(MOE_CNT_ROWSCALE);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    G16Args b{};
+    b.w0 = routed->down.codes; b.s0 = static_cast<const uint16_t*>(routed->down.scales);
+    b.a = h16; b.aexp = he; b.sorted_pair = sorted_pair; b.offsets = expert_offsets; b.out = y_pairs;
+    b.N = H; b.K = I; b.Ka = 2 * I; b.rows_a = P; b.E = E; b.k = k; b.P = P;
+    if (prof) moe_prof_begin(MOE_PROF_STQ_DOWN, s);
+    e = moe_launch_g16_stq_down(b, s);
+    if (prof) moe_prof_end(MOE_PROF_STQ_DOWN, s);
+    bump(MOE_CNT_STQ_GEMM);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  } else if (fmt == MOE_W_STQ1_0) {
     float* h = reinterpret_cast<float*>(wsb + offs[0]);
     FfnArgs a{};
     a.codes0 = routed->gate.codes; a.scales0 = routed->gate.scales;
@@ -270,7 +341,6 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     uint8_t* xs = wsb + offs[3];
     uint8_t* hq = wsb + offs[4];
     uint8_t* hs = wsb + offs[5];
-    const bool prof = moe_prof_on();
     if (prof) moe_prof_begin(MOE_PROF_MX_QUANT, s);
     hipError_t e = moe_launch_mx_quant(T, H, x_bf16, nullptr, xq, xs, s);
     if (prof) moe_prof_end(MOE_PROF_MX_QUANT, s);
@@ -302,7 +372,33 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
 
-  if (shared) {
+  if (shared && ext[4] != (size_t)-1) {
+    // prefill: grouped GEMMs on the bf16 MFMA (one expert owning every token)
+    float* hsh = reinterpret_cast<float*>(wsb + offs[1]);
+    uint16_t* h2 = reinterpret_cast<uint16_t*>(wsb + ext[4]);
+    G16Args a{};
+    a.w0 = shared->gate.codes; a.w1 = shared->up.codes;
+    a.a = x_bf16; a.out = hsh;
+    a.N = I; a.K = H; a.Ka = H; a.rows_a = T; a.E = 1; a.k = 1; a.P = T;
+    if (prof) moe_prof_begin(MOE_PROF_SH_GATEUP, s);
+    hipError_t e = moe_launch_g16_bf16_gateup(a, s);
+    if (prof) moe_prof_end(MOE_PROF_SH_GATEUP, s);
+    bump(MOE_CNT_BF16_GEMM);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (prof) moe_prof_begin(MOE_PROF_ACT_PREP, s);
+    e = moe_launch_split_bf16(hsh, T, I, h2, s);
+    if (prof) moe_prof_end(MOE_PROF_ACT_PREP, s);
+    bump(MOE_CNT_ROWSCALE);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    G16Args b{};
+    b.w0 = shared->down.codes; b.a = h2; b.out = y_shared;
+    b.N = H; b.K = I; b.Ka = 2 * I; b.rows_a = T; b.E = 1; b.k = 1; b.P = T;
+    if (prof) moe_prof_begin(MOE_PROF_SH_DOWN, s);
+    e = moe_launch_g16_bf16_down(b, s);
+    if (prof) moe_prof_end(MOE_PROF_SH_DOWN, s);
+    bump(MOE_CNT_BF16_GEMM);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  } else if (shared) {
     float* hsh = reinterpret_cast<float*>(wsb + offs[1]);
     FfnArgs a{};
     a.codes0 = shared->gate.codes; a.codes1 = shared->up.codes;

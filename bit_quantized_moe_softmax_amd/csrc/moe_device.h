@@ -179,10 +179,44 @@ hipError_t moe_launch_mx_gateup(const MxArgs& a, hipStream_t s);
 hipError_t moe_launch_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales, long rows,
                                        int K, uint8_t* tcodes, uint8_t* tscales, hipStream_t s);
 
+// Prefill grouped GEMMs on the 16-bit MFMA: routed STQ1_0 (fp16) and the bf16 shared expert.
+struct G16Args {
+  const void* w0; const void* w1;          // STQ1_0 codes or bf16 rows: gate (or down), up
+  const uint16_t* s0; const uint16_t* s1;  // STQ1_0 fp16 block scales
+  const uint16_t* a;                       // A rows [rows_a][Ka], fp16 (STQ1_0) or bf16
+  const int32_t* aexp;                     // STQ1_0: row scale exponents (A = row * 2^aexp)
+  const int32_t* sorted_pair;              // routed gate/up: A row of pos = sorted_pair[pos] / k
+  const int32_t* offsets;                  // [E+1]; NULL: one expert owning all P rows
+  float* out;                              // gate/up: h [P][N]; down: y [P][N]
+  int N, K, Ka, rows_a, E, k, P;
+};
+hipError_t moe_launch_g16_stq_gateup(const G16Args& a, hipStream_t s);
+hipError_t moe_launch_g16_stq_down(const G16Args& a, hipStream_t s);
+hipError_t moe_launch_g16_bf16_gateup(const G16Args& a, hipStream_t s);
+hipError_t moe_launch_g16_bf16_down(const G16Args& a, hipStream_t s);
+hipError_t moe_launch_rowscale_f16(const uint16_t* in16, const float* in32, long rows, int C,
+                                   int two, uint16_t* out, int32_t* sexp, hipStream_t s);
+hipError_t moe_launch_split_bf16(const float* h, long rows, int C, uint16_t* out, hipStream_t s);
+
+// Compute units of the current device (cached per device).
+inline int moe_cu_count() {
+  static int n_cu[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (n_cu[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    n_cu[dev] = n;
+  }
+  return n_cu[dev];
+}
+
 // Opt-in kernel timing with HIP events recorded on the launch stream around single kernels.
 enum {
   MOE_PROF_DECODE_K1 = 0, MOE_PROF_DECODE_K2 = 1, MOE_PROF_DECODE_K3 = 2,
   MOE_PROF_MX_QUANT = 4, MOE_PROF_MX_GATEUP = 5, MOE_PROF_MX_DOWN = 6,
+  MOE_PROF_STQ_GATEUP = 7, MOE_PROF_STQ_DOWN = 8, MOE_PROF_SH_GATEUP = 9, MOE_PROF_SH_DOWN = 10,
+  MOE_PROF_ACT_PREP = 11,
   MOE_PROF_SLOTS_INTERNAL = 16
 };
 bool moe_prof_on();

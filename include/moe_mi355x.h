@@ -107,9 +107,11 @@ enum {
   MOE_CNT_COMBINE = 11,
   MOE_CNT_RMSNORM = 12,
   MOE_CNT_DEQUANT = 13,
-  MOE_CNT_BF16_GEMM = 14,      /* shared expert, large-T tiled GEMM path    */
+  MOE_CNT_BF16_GEMM = 14,      /* shared expert, prefill grouped GEMM path  */
   MOE_CNT_DECODE_FUSED = 15,   /* moe_layer_decode (three fused kernels)    */
-  MOE_CNT_SLOTS = 16
+  MOE_CNT_STQ_GEMM = 16,       /* STQ1_0 prefill grouped GEMMs (fp16 MFMA)  */
+  MOE_CNT_ROWSCALE = 17,       /* activation rows to fp16 / bf16 hi + lo    */
+  MOE_CNT_SLOTS = 18
 };
 
 MOE_MI355X_API const char* moe_status_str(moe_status s);
@@ -122,7 +124,9 @@ MOE_MI355X_API moe_status moe_reset_counters(void);
 
 /* Opt-in kernel timing: while enabled the library records a HIP event pair on the launch
  * stream around each of its main kernels (slots: 0..2 the three kernels of
- * moe_layer_decode, 4/5/6 MX quantisation, MXFP4 gate/up and down GEMMs).  Enabling
+ * moe_layer_decode, 4/5/6 MX quantisation, MXFP4 gate/up and down GEMMs, 7/8 the STQ1_0
+ * prefill gate/up and down GEMMs, 9/10 the shared expert's prefill gate/up and down GEMMs,
+ * 11 the activation conversions of the prefill GEMMs).  Enabling
  * creates the event pools once (host objects, no device memory).  moe_profile_read waits
  * for the recorded events, writes the average duration in microseconds and the number of
  * launches per slot (16 slots) and clears the records.  Timing adds two event records per

@@ -52,7 +52,15 @@ def test_workspace_layout():
     assert offs[3] == offs[2] + 4096 * 6144
     assert offs[4] == offs[3] + 4096 * 6144 // 32
     assert offs[5] == offs[4] + P * 2048
-    assert offs[6] == offs[5] + P * 2048 // 32
+    # the prefill shared-expert GEMM's bf16 hi | lo copy of h closes the workspace
+    assert offs[6] == offs[5] + P * 2048 // 32 + 4096 * 2 * 2048 * 2
+    # STQ1_0 at prefill size: x and h (hi | lo) as fp16 rows with their row exponents, then the
+    # shared expert's hi | lo h (each region 256-byte aligned)
+    up = lambda v: (v + 255) // 256 * 256
+    offs = M.moe_workspace_offsets(d, M.MOE_W_STQ1_0, True)
+    assert offs[0] == 0 and offs[1] == P * 2048 * 4 and offs[2] is None
+    ext = up(4096 * 6144 * 2) + up(4096 * 4) + up(P * 2 * 2048 * 2) + up(P * 4) + up(4096 * 2 * 2048 * 2)
+    assert offs[6] == offs[1] + 4096 * 2048 * 4 + ext
 
 
 def _raw(name, *args):

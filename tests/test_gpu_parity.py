@@ -291,6 +291,106 @@ def test_layer_stq_small(name):
             assert row_err(host(bufs.y_shared), ref["y_shared"]).max() <= TOL
 
 
+STQ_PREFILL = {
+    # about 75 pairs per expert (one ragged M block each); shared expert in three M blocks
+    "h512-i256-e8-top2-t300-shared": synth.LayerCfg("p", 300, 512, 256, 8, 2, True, "stq1", False, False, 1, 21),
+    # Zipf-skewed load: a few experts with several M blocks; down output in three N tiles
+    "h768-i512-e4-top2-t400-zipf": synth.LayerCfg("p", 400, 768, 512, 4, 2, True, "stq1", True, False, 1, 22),
+    # one to a few pairs per expert, idle experts, given logits, no shared expert
+    "h256-i256-e64-top4-t64-logits": synth.LayerCfg("p", 64, 256, 256, 64, 4, False, "stq1", False, True, 1, 23),
+}
+
+
+@pytest.mark.parametrize("name", list(STQ_PREFILL))
+def test_layer_stq_prefill_gemm(name):
+    """STQ1_0 routed experts and the bf16 shared expert at prefill token counts: the tiled
+    grouped GEMMs (fp16 / bf16 MFMA) against the float64 oracle, stage by stage."""
+    c = STQ_PREFILL[name]
+    say("stq prefill layer", name)
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, shared is not None)
+    M.moe_reset_counters()
+    if c.logits_given:
+        run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
+        ref = O.moe_layer(inp["x"], c.k, oracle_weights(c, inp["routed"]), "stq1",
+                          logits_in=inp["logits_in"], shared=inp["shared"])
+    else:
+        bias = dev(inp["bias"]) if inp["bias"] is not None else None
+        run_layer(d, bufs, dev(inp["x"]), routed, shared, wr_bf16=dev(inp["wr"]), logit_bias=bias)
+        ref = O.moe_layer(inp["x"], c.k, oracle_weights(c, inp["routed"]), "stq1", wr_bits=inp["wr"],
+                          bias=inp["bias"], shared=inp["shared"])
+    torch.cuda.synchronize()
+    cnt = M.moe_get_counters()
+    assert cnt["stq_gemm"] == 2 and cnt["stq_gateup_mfma"] == 0 and cnt["stq_down_mfma"] == 0
+    assert cnt["bf16_gemm"] == (2 if shared is not None else 0) and cnt["bf16_gateup"] == 0
+    _check_layer(c, inp, bufs, d, ref)
+    if (host(bufs.topk_ids) == ref["ids"]).all():
+        offs = M.moe_workspace_offsets(d, M.MOE_W_STQ1_0, shared is not None)
+        h = host(bufs.ws)[offs[0]:offs[0] + d.P * c.I * 4].view(np.float32).reshape(d.P, c.I)
+        eh = row_err(h, ref["h"]).max()
+        ey = row_err(host(bufs.y_pairs), ref["y_pairs"]).max()
+        say("h max row err", float(eh), "y_pairs max row err", float(ey))
+        assert eh <= TOL and ey <= TOL
+        if shared is not None:
+            es = row_err(host(bufs.y_shared), ref["y_shared"]).max()
+            say("y_shared max row err", float(es))
+            assert es <= TOL
+
+
+def test_stq_prefill_hy4_t4096_sampled():
+    """Hy4-shaped STQ1_0 layer at 4096 tokens (256 experts, top-8, bf16 shared expert) on the
+    prefill GEMMs: routing and permutation in full; h and the down projection on the experts
+    with the most and the fewest pairs and one more; shared expert and combined output on
+    sampled tokens."""
+    c = synth.LayerCfg("hy4-stq1-prefill-t4096", 4096, 6144, 2048, 256, 8, True, "stq1", False, True, 1, 31)
+    say("stq prefill t4096 generate")
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, True)
+    say("stq prefill t4096 run")
+    M.moe_reset_counters()
+    run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
+    torch.cuda.synchronize()
+    cnt = M.moe_get_counters()
+    assert cnt["stq_gemm"] == 2 and cnt["bf16_gemm"] == 2
+    _, rid, rw = O.route(c.k, logits_in=inp["logits_in"])
+    rsp, roff, rpp = O.permute(rid, c.E)
+    assert (host(bufs.sorted_pair) == rsp).all() and (host(bufs.offsets) == roff).all()
+    assert (host(bufs.pair_pos) == rpp).all()
+    n = np.diff(roff)
+    pick = [int(np.argmax(n)), int(np.argmin(np.where(n > 0, n, 1 << 30))),
+            int(synth.sample_tokens(c.seed, c.E, 1)[0])]
+    say("stq prefill t4096 experts", pick, "pairs", [int(n[e]) for e in pick])
+    offs = M.moe_workspace_offsets(d, M.MOE_W_STQ1_0, True)
+    P = d.P
+    h_gpu = host(bufs.ws[offs[0]:offs[0] + P * c.I * 4]).view(np.float32).reshape(P, c.I)
+    yp = host(bufs.y_pairs)
+    get_w = oracle_weights(c, inp["routed"])
+    xf = O.bf16_to_f64(inp["x"])
+    for e in pick:
+        lo, hi = int(roff[e]), int(roff[e + 1])
+        if hi == lo:
+            continue
+        a = xf[rsp[lo:hi] // c.k]
+        h = O.silu(a @ get_w(e, 0).T) * (a @ get_w(e, 1).T)
+        eh = row_err(h_gpu[lo:hi], h).max()
+        ey = row_err(yp[lo:hi], h @ get_w(e, 2).T).max()
+        say("expert", e, "h max row err", float(eh), "y max row err", float(ey))
+        assert eh <= TOL and ey <= TOL
+    toks = synth.sample_tokens(c.seed, c.T, 4)
+    ysh = O.shared_expert(inp["x"][toks], *inp["shared"])
+    assert row_err(host(bufs.y_shared)[toks], ysh).max() <= TOL
+    out_ref = O.combine(yp, rw, rpp, host(bufs.y_shared))
+    err = row_err(host(bufs.out)[toks], out_ref[toks])
+    say("stq prefill t4096 combine max row err on sampled tokens", float(err.max()))
+    assert err.max() <= TOL
+
+
 def test_layer_cfg1_hy4_decode():
     c = synth.cfg(1)
     say("layer cfg1 generate")
