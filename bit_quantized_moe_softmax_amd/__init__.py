@@ -17,7 +17,8 @@ __all__ = [
     "COUNTER_NAMES", "moe_status_str", "moe_version", "moe_get_counters", "moe_reset_counters",
     "moe_route", "moe_permute", "moe_workspace_size", "moe_workspace_offsets", "moe_expert_ffn",
     "moe_combine", "moe_stq1_pack", "moe_stq1_dequant", "moe_mxfp4_dequant", "moe_mx_quant_act",
-    "moe_rmsnorm_bf16", "moe_layer_decode_workspace_size", "moe_layer_decode",
+    "moe_rmsnorm_bf16", "moe_layer_decode_workspace_size", "moe_layer_decode_workspace_offsets",
+    "moe_layer_decode",
     "moe_profile_enable", "moe_profile_read", "PROFILE_SLOTS",
 ]
 
@@ -71,6 +72,7 @@ _SIGS = {
     "moe_mx_quant_act": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P]),
     "moe_rmsnorm_bf16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
     "moe_layer_decode_workspace_size": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "moe_layer_decode_workspace_offsets": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "moe_layer_decode": (ctypes.c_int, [_P, _P, _P] + [_P] * 15 + [ctypes.c_size_t, _P]),
     "moe_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
     "moe_profile_read": (ctypes.c_int, [_P, _P]),
@@ -228,6 +230,12 @@ def moe_mx_quant_act(rows, K, x_bf16, x_f32, q, s, stream=None):
 
 def moe_rmsnorm_bf16(T, H, eps, r, a, stream=None):
     _check(lib().moe_rmsnorm_bf16(int(T), int(H), float(eps), _ptr(r), _ptr(a), _stream(stream)))
+
+
+def moe_layer_decode_workspace_offsets(d: Dims, has_shared: bool) -> list:
+    buf = (ctypes.c_size_t * 11)()
+    _check(lib().moe_layer_decode_workspace_offsets(d.ref(), int(bool(has_shared)), ctypes.cast(buf, _P)))
+    return [int(v) for v in buf]
 
 
 def moe_layer_decode_workspace_size(d: Dims, has_shared: bool) -> int:

@@ -86,6 +86,10 @@ struct DecodeArgs {
   uint16_t* hs;     // shared h [T][I] bf16 hi, then [T][I] bf16 lo
   int n_router_wg, n_sgu_wg, n_gu_wg;
   int h_lds;        // down kernel: all routed and shared h staged in LDS
+  // MXFP4 routed experts: E4M3 x codes [T][H] then UE8M0 scales [T][H/32] (written by K1);
+  // E4M3 h codes [P][I] then scales [P][I/32] (over the bf16 h region)
+  uint8_t* xq;
+  uint8_t* hq;
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -1382,6 +1386,306 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   }
 }
 
+// ============================================================================ MXFP4, small T
+// Routed experts in MXFP4 (E2M1 weights with UE8M0 group-32 scales) take FP8 E4M3
+// activations with group-32 scales ("Hy4-preview-SF-WFP4AFP8", Quant Diff table): x is
+// quantised once (extra K1 workgroups), h in the gate/up epilogue (a workgroup owns 32
+// consecutive h-columns, one group), and both projections run on the scaled MFMA
+// v_mfma_scale_f32_16x16x128_f8f6f4: A = E4M3 activations from LDS (row = token or pair
+// slot), B = E2M1 weight codes straight from memory (column = weight row), one scale byte
+// per lane and operand.  Operand layout (as in the MXFP4 prefill GEMMs): lane l serves row /
+// column l % 16; an E2M1 lane holds K = 32g .. 32g+31 of the 128-wide step (16 bytes), an
+// E4M3 lane K = 16g .. 16g+15 and 64+16g .. 64+16g+15, and each lane's scale is that of K
+// block g (K = 32g .. 32g+31) of its row.  The routing, the shared expert and the combine
+// are the STQ1_0 path's.
+
+// Stream of one MXFP4 16-row tile over NS K steps of 128, row-major (codes [rows][K/2],
+// scales [rows][K/32]) or tiled (per tile and step a 1 KiB code block in lane order and a
+// 64-byte scale block, 4 bytes per row).  RD steps of code words and scale words in flight.
+template <int NS, bool TILED, int RD = kRing>
+struct MxStream {
+  static constexpr int R = NS < RD ? NS : RD;
+  static constexpr int K = 128 * NS;
+  uint4 q[R];
+  uint32_t sw[R];
+  rsrc_t rc, rs;
+  uint32_t co, so;
+
+  __device__ __forceinline__ void load(int j, int slot) {
+    // tiled: each step is whole lines read once (non-temporal); row-major rows are read
+    // half a line per step
+    q[slot] = TILED ? bload16_nt(rc, co, 1024 * j) : bload16(rc, co, 64 * j);
+    sw[slot] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, TILED ? 64 * j : 4 * j, 0);
+  }
+  // codes / scales: one matrix of `rows` rows; trow: the tile's first row (a multiple of 16)
+  __device__ __forceinline__ void issue(const uint8_t* codes, const uint8_t* scales, uint32_t rows,
+                                        uint32_t trow) {
+    const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
+    rc = make_rsrc(codes, rows * (K / 2));
+    rs = make_rsrc(scales, rows * (K / 32));
+    co = TILED ? trow * (K / 2) + 16 * lane : (trow + c16) * (K / 2) + 16 * g;
+    so = TILED ? trow * (K / 32) + 4 * c16 : (trow + c16) * (K / 32);
+#pragma unroll
+    for (int j = 0; j < R; ++j) load(j, j);
+  }
+  // sum over K of this lane's A row (E4M3 codes a_q, UE8M0 scales a_s, in LDS) times the tile
+  __device__ __forceinline__ f32x4_t run_lds(const uint8_t* a_q, const uint8_t* a_s) {
+    const int g = (threadIdx.x & 63) >> 4;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const uint4 w = q[j % R];
+      const int bsc = (sw[j % R] >> (8 * g)) & 0xFF;
+      if (j + R < NS) load(j + R, j % R);
+      const uint4 v0 = *reinterpret_cast<const uint4*>(a_q + 128 * j + 16 * g);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(a_q + 128 * j + 64 + 16 * g);
+      const int asc = a_s[4 * j + g];
+      const i32x8_t aop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                           (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      const i32x8_t bop = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc, 0 /*A: E4M3*/,
+                                                             4 /*B: E2M1*/, 0, asc, 0, bsc);
+    }
+    return acc;
+  }
+};
+
+// K1 for MXFP4: the router partials, and in the workgroups past them x -> E4M3 with group-32
+// scales, one element per lane (T H is a multiple of 64, so waves past the end are whole).
+template <int HB>
+__global__ __launch_bounds__(kWG) void k1s_router_mx(DecodeArgs a) {
+  constexpr int H = HB * 256;
+  __shared__ __align__(16) float s_red[kNW][4][64];
+  if ((int)blockIdx.x < a.n_router_wg) {
+    router_unit<HB>(a, blockIdx.x, s_red);
+    return;
+  }
+  const int i = ((int)blockIdx.x - a.n_router_wg) * kWG + (int)threadIdx.x;
+  if (i >= a.T * H) return;
+  uint32_t sc;
+  const uint32_t code = moe_mx_quant_lane((uint32_t)a.x[i] << 16, &sc);
+  a.xq[i] = (uint8_t)code;
+  if ((i & 31) == 0) a.xq[(size_t)a.T * H + i / 32] = (uint8_t)sc;
+}
+
+// Routed gate/up of one work item (unit, 32 rows of I): wave = (16-row tile, gate|up); the
+// four waves meet in LDS, then threads (slot, column) form h = SiLU(gate) * up for the
+// item's 32 h-columns and quantise each slot's 32 values as one MX group.
+template <int HB, int IB, bool TILED>
+__device__ __forceinline__ void routed_gateup_mx(const DecodeArgs& a, int wi, const uint8_t* s_xq,
+                                                 float (*s_red)[2][4][64], const SmallRoute& R) {
+  constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int un_i = wi / NTP, tp = wi % NTP;
+  const int4 un = R.ut[un_i];
+  const int e = un.x, pos0 = un.y, ntok = un.z;
+  const int mat = wave & 1, tl = wave >> 1;
+  const int row0 = (2 * tp + tl) * 16;
+  const size_t eb = (size_t)I * (H / 2), es = (size_t)I * (H / 32);
+  MxStream<H / 128, TILED> st;
+  st.issue((mat ? a.uc : a.gc) + e * eb,
+           reinterpret_cast<const uint8_t*>(mat ? a.us : a.gs) + e * es, I, row0);
+  const int tok = R.utok[pos0 + (col < ntok ? col : ntok - 1)];
+  const f32x4_t acc = st.run_lds(s_xq + (size_t)tok * H, s_xq + (size_t)a.T * H + tok * (H / 32));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_red[tl][mat][i][lane] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    // thread (slot, c): h-column 32 tp + c of token slot `slot`; D(4g + i, r) of tile t2 is
+    // register i of lane 16 g + r
+    const int slot = threadIdx.x >> 5, c = threadIdx.x & 31;
+    const int t2 = c >> 4, L = 16 * (slot >> 2) + (c & 15), i = slot & 3;
+    const float h = silu_mul(s_red[t2][0][i][L], s_red[t2][1][i][L]);
+    uint32_t am = __float_as_uint(h) & 0x7FFFFFFFu;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o, 64));
+    if (slot < ntok) {
+      const size_t pos = pos0 + slot;
+      uint32_t code = 0, sc = 0;
+      if (am != 0) {
+        const int X = moe_mx_exp(am);
+        code = moe_e4m3_from_f32(__float_as_uint(h), X);
+        sc = (uint32_t)(X + 127);
+      }
+      a.hq[pos * I + 32 * tp + c] = (uint8_t)code;
+      if (c == 0) a.hq[(size_t)a.T * a.k * I + pos * (I / 32) + tp] = (uint8_t)sc;
+    }
+  }
+  __syncthreads();   // s_red is reused by the next work item
+}
+
+template <int HB, int IB, int XR, bool TILED>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k2s_gateup_mx(DecodeArgs a) {
+  constexpr int H = HB * 256, I = IB * 256;
+  extern __shared__ __align__(16) uint16_t s_x[];   // shared workgroups: XR bf16 x rows;
+                                                    // routed: E4M3 x rows, then their scales
+  __shared__ __align__(16) float s_red[2][2][4][64];
+  __shared__ SmallRoute s_rt;
+  const int b = blockIdx.x;
+  const int T = a.T;
+  if (b >= a.n_gu_wg) {
+    shared_gateup_valu<HB, IB, XR, kWG>(a, b - a.n_gu_wg, s_x);
+    return;
+  }
+  uint8_t* s_xq = reinterpret_cast<uint8_t*>(s_x);
+  {
+    // the x codes and scales (one linear run) and the router partials are loaded in one
+    // branch-free stretch: pieces past the end reload and rewrite piece 0
+    constexpr int PER = (XR * (H + H / 32) / 16 + kWG - 1) / kWG;
+    const int n16 = T * (H + H / 32) / 16;
+    const uint4* src = reinterpret_cast<const uint4*>(a.xq);
+    uint4 v[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = threadIdx.x + kWG * m;
+      v[m] = src[i < n16 ? i : 0];
+    }
+    TopkIn in;
+    topk_load(a, min((int)(threadIdx.x >> 6), T - 1), in);
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = threadIdx.x + kWG * m;
+      reinterpret_cast<uint4*>(s_xq)[i < n16 ? i : 0] = v[m];
+    }
+    const TopkSum ls = topk_sums(a, in);
+    small_route_topk(a, s_rt, ls, b == 0);
+    small_route_units(a, s_rt, b == 0);   // starts and ends with a barrier: s_xq is complete
+    const int n_items = s_rt.n_units * (I / 32);
+    for (int wi = b; wi < n_items; wi += a.n_gu_wg)
+      routed_gateup_mx<HB, IB, TILED>(a, wi, s_xq, s_red, s_rt);
+  }
+}
+
+// Down projections and combine for MXFP4 routed experts: as k3_down_combine with every
+// pair's E4M3 h codes and scales staged in LDS; an entry's pairs are A rows 0 .. nq - 1.
+template <int HB, int IB, bool TILED>
+__global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine_mx(DecodeArgs a) {
+  constexpr int H = HB * 256, I = IB * 256;
+  constexpr int kStage = 10;                 // uint4 per thread of staged h
+  extern __shared__ __align__(16) float s_dyn[];  // [kDnWaves][T][16] sums, then h codes + scales
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, P = T * a.k;
+  const int row0 = blockIdx.x * 16;
+  const int col = lane & 15, g = lane >> 4;
+  float* s_acc = s_dyn;
+  uint8_t* s_h = reinterpret_cast<uint8_t*>(s_dyn + kDnWaves * T * 16);
+  const rsrc_t rres = make_rsrc(a.residual, a.residual ? (uint32_t)T * H * 4 : 0u);
+  float rs[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int i = tid + 64 * kDnWaves * m;
+    const uint32_t o = i < T * 16 ? 4u * ((uint32_t)(i >> 4) * H + row0 + (i & 15)) : kOOB;
+    rs[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rres, o, 0, 0));
+  }
+  // staged h: P I code bytes then P I / 32 scale bytes, one linear copy (branch-free, as in
+  // k3_down_combine); the last piece may run up to 15 bytes past the scales (inside the h
+  // region of the workspace)
+  const int n_all = (P * (I + I / 32) + 15) / 16;
+  uint4 hv[kStage];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.hq);
+#pragma unroll
+    for (int m = 0; m < kStage; ++m) {
+      const int i = tid + 64 * kDnWaves * m;
+      hv[m] = src[i < n_all ? i : 0];
+    }
+  }
+  for (int i = tid; i < kDnWaves * T * 16; i += 64 * kDnWaves) s_acc[i] = 0.f;
+#pragma unroll
+  for (int m = 0; m < kStage; ++m) {
+    int i = tid + 64 * kDnWaves * m;
+    i = i < n_all ? i : 0;
+    reinterpret_cast<uint4*>(s_h)[i] = hv[m];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  SharedDown<HB, IB, 2, true> sdn;
+  sdn.issue(a, row0);
+  const int n_ent = a.wl[2];
+  const size_t eb = (size_t)H * (I / 2), es = (size_t)H * (I / 32);
+  const uint8_t* dsc = reinterpret_cast<const uint8_t*>(a.ds);
+  MxStream<I / 128, TILED> st;
+  int hu = wave;
+  int4 hent = a.hl[wave < a.max_half ? wave : a.max_half - 1];
+  {
+    const int e0 = min(max(hent.x, 0), a.E - 1);
+    st.issue(a.dc + e0 * eb, dsc + e0 * es, H, row0);
+  }
+  lds_barrier();
+  if (a.sd) sdn.run(a, row0, a.hs, s_acc);
+  for (; hu < n_ent; hu += kDnWaves) {
+    if (hu != wave) {
+      hent = a.hl[hu];
+      st.issue(a.dc + hent.x * eb, dsc + hent.x * es, H, row0);
+    }
+    const int pos0 = hent.y, nq = hent.z;
+    const int pr = pos0 + (col < nq ? col : 0);
+    const f32x4_t acc = st.run_lds(s_h + (size_t)pr * I, s_h + (size_t)P * I + pr * (I / 32));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = 4 * g + i;
+      if (p < nq) {
+        const float y = acc[i];
+        a.y_pairs[(size_t)(pos0 + p) * H + row0 + col] = y;
+        const int tk = a.utok[hent.w + p];
+        float* sa = &s_acc[(wave * T + tk) * 16 + col];
+        *sa = fmaf(a.uw[hent.w + p], y, *sa);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int i = tid + 64 * kDnWaves * m;
+    if (i < T * 16) {
+      const int t = i >> 4, r = i & 15;
+      float v = 0.f;
+      for (int w = 0; w < kDnWaves; ++w) v += s_acc[(w * T + t) * 16 + r];
+      v += rs[m];
+      const size_t o = (size_t)t * H + row0 + r;
+      a.out[o] = v;
+      if (a.out_bf16) a.out_bf16[o] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
+template <int HB, int IB, int XR, bool TILED>
+hipError_t launch_small_mx(DecodeArgs& a, hipStream_t s) {
+  constexpr int H = HB * 256, I = IB * 256;
+  const int T = a.T;
+  const int P = T * a.k;
+  const int max_units = P < a.E ? P : a.E;
+  const bool shared = a.sg != nullptr;
+  a.n_router_wg = ((a.E + 15) / 16) * kRouterParts;
+  const int n_xq_wg = (T * H + kWG - 1) / kWG;
+  a.n_sgu_wg = shared ? I / kNW : 0;
+  a.n_gu_wg = max_units * (I / 32);
+  a.h_lds = 0;
+  const size_t lds2 = (size_t)XR * H * 2;
+  const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + ((size_t)P * (I + I / 32) + 15) / 16 * 16;
+  if (((size_t)P * (I + I / 32) + 15) / 16 > (size_t)10 * 64 * kDnWaves) return hipErrorInvalidValue;
+  const bool prof = moe_prof_on();
+  if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
+  hipLaunchKernelGGL((k1s_router_mx<HB>), dim3(a.n_router_wg + n_xq_wg), dim3(kWG), 0, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
+  hipLaunchKernelGGL((k2s_gateup_mx<HB, IB, XR, TILED>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(kWG), lds2, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
+  hipLaunchKernelGGL((k3_down_combine_mx<HB, IB, TILED>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
+  return hipSuccess;
+}
+
+template <int HB, int IB, bool TILED>
+hipError_t launch_shape_mx(DecodeArgs& a, hipStream_t s) {
+  if (a.T == 1) return launch_small_mx<HB, IB, 1, TILED>(a, s);
+  if (a.T == 2) return launch_small_mx<HB, IB, 2, TILED>(a, s);
+  if (a.T <= kXT) return launch_small_mx<HB, IB, kXT, TILED>(a, s);
+  return hipErrorInvalidValue;
+}
+
 // Small T: router + routing; routed + shared gate/up; routed + shared down + combine.
 template <int HB, int IB, int XR>
 hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
@@ -1465,6 +1769,13 @@ bool moe_decode_shape_ok(int H, int I, int E) {
          (hb == 16 && ib == 8) || (hb == 24 && ib == 8) || (hb == 32 && ib == 8);
 }
 
+// MXFP4 routed experts: up to kXT tokens, every pair's E4M3 h (codes and scales) fits the
+// down kernel's LDS staging.
+bool moe_decode_mx_ok(int T, int I, int k) {
+  const long P = (long)T * k;
+  return T <= kXT && (P * (I + I / 32) + 15) / 16 <= 10L * 64 * kDnWaves;
+}
+
 size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, size_t* offs) {
   const size_t P = (size_t)T * k;
   const size_t pe = P < (size_t)E ? P : (size_t)E;
@@ -1481,7 +1792,8 @@ size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, s
   offs[6] = cur; cur = al(cur + P * I * 2);                                          // h hi
   offs[7] = cur; cur = al(cur + P * I * 2);                                          // h lo
   offs[8] = cur; cur = al(cur + (has_shared ? (size_t)T * I * 4 : 0));              // shared h hi, lo
-  offs[9] = cur;
+  offs[9] = cur; cur = al(cur + (size_t)T * (H + H / 32));                          // MXFP4: E4M3 x
+  offs[10] = cur;
   return cur;
 }
 
@@ -1524,7 +1836,19 @@ hipError_t moe_launch_decode_fused(const moe_dims* d, const moe_experts* routed,
   a.h_lo_bytes = (uint32_t)(offs[7] - offs[6]);
   a.h_bytes = (uint32_t)(offs[7] - offs[6] + (size_t)d->T * d->k * d->I * 2);
   a.hs = reinterpret_cast<uint16_t*>(b + offs[8]);
+  a.xq = b + offs[9];
+  a.hq = b + offs[6];
   const int hb = d->H / 256, ib = d->I / 256;
+  if (routed->fmt == MOE_W_MXFP4 || routed->fmt == MOE_W_MXFP4_TILED) {
+    const bool tl = routed->fmt == MOE_W_MXFP4_TILED;
+#define MOE_MX_SHAPE(HB_, IB_)                                                          \
+    if (hb == HB_ && ib == IB_)                                                         \
+      return tl ? launch_shape_mx<HB_, IB_, true>(a, s) : launch_shape_mx<HB_, IB_, false>(a, s);
+    MOE_MX_SHAPE(2, 1) MOE_MX_SHAPE(4, 2) MOE_MX_SHAPE(8, 4) MOE_MX_SHAPE(16, 8)
+    MOE_MX_SHAPE(24, 8) MOE_MX_SHAPE(32, 8)
+#undef MOE_MX_SHAPE
+    return hipErrorInvalidValue;
+  }
   if (hb == 2 && ib == 1) return launch_shape<2, 1>(a, s);
   if (hb == 4 && ib == 2) return launch_shape<4, 2>(a, s);
   if (hb == 8 && ib == 4) return launch_shape<8, 4>(a, s);

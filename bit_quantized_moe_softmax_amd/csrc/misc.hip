@@ -129,50 +129,20 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint8_t* __res
   out[row * K + col + 1] = e2m1_to_f32(c >> 4) * sc;
 }
 
-__global__ __launch_bounds__(256) void mx_quant_kernel(int64_t n_groups, const uint16_t* xb,
+// One element per lane; lanes 32q .. 32q + 31 form a group (groups never straddle rows:
+// K is a multiple of 32).  Lanes past the end load the last element and store nothing.
+__global__ __launch_bounds__(256) void mx_quant_kernel(int64_t n, const uint16_t* xb,
                                                        const float* xf, uint8_t* __restrict__ q,
                                                        uint8_t* __restrict__ sc) {
-  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gi >= n_groups) return;
-  uint32_t bits[32];
-  if (xb) {
-    const uint4* src = reinterpret_cast<const uint4*>(xb + gi * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = src[i];
-      bits[8 * i + 0] = v.x << 16; bits[8 * i + 1] = v.x & 0xFFFF0000u;
-      bits[8 * i + 2] = v.y << 16; bits[8 * i + 3] = v.y & 0xFFFF0000u;
-      bits[8 * i + 4] = v.z << 16; bits[8 * i + 5] = v.z & 0xFFFF0000u;
-      bits[8 * i + 6] = v.w << 16; bits[8 * i + 7] = v.w & 0xFFFF0000u;
-    }
-  } else {
-    const uint4* src = reinterpret_cast<const uint4*>(xf + gi * 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 v = src[i];
-      bits[4 * i + 0] = v.x; bits[4 * i + 1] = v.y; bits[4 * i + 2] = v.z; bits[4 * i + 3] = v.w;
-    }
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t j = i < n ? i : n - 1;
+  const uint32_t bits = xb ? (uint32_t)xb[j] << 16 : __float_as_uint(xf[j]);
+  uint32_t s;
+  const uint32_t code = moe_mx_quant_lane(bits, &s);
+  if (i < n) {
+    q[i] = (uint8_t)code;
+    if ((i & 31) == 0) sc[i / 32] = (uint8_t)s;
   }
-  uint32_t amax = 0;   // compare magnitudes as integers (finite inputs)
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = max(amax, bits[i] & 0x7FFFFFFFu);
-  uint32_t out[8];
-  if (amax == 0) {
-    sc[gi] = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = 0;
-  } else {
-    const int X = moe_mx_exp(amax);
-    sc[gi] = (uint8_t)(X + 127);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      out[i] = moe_e4m3_from_f32(bits[4 * i], X) | (moe_e4m3_from_f32(bits[4 * i + 1], X) << 8) |
-               (moe_e4m3_from_f32(bits[4 * i + 2], X) << 16) | (moe_e4m3_from_f32(bits[4 * i + 3], X) << 24);
-    }
-  }
-  uint4* dst = reinterpret_cast<uint4*>(q + gi * 32);
-  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
 }  // namespace
@@ -217,8 +187,10 @@ hipError_t moe_launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales,
 
 hipError_t moe_launch_mx_quant(int64_t rows, int K, const uint16_t* xb, const float* xf,
                                uint8_t* q, uint8_t* sc, hipStream_t s) {
-  const int64_t ng = rows * (K / 32);
-  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, s, ng,
+  const int64_t n = rows * K;
+  if (n == 0) return hipSuccess;
+  if ((n + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n,
                      xb, xf, q, sc);
   return hipGetLastError();
 }

@@ -428,6 +428,15 @@ moe_status moe_layer_decode_workspace_size(const moe_dims* d, int32_t has_shared
   return MOE_OK;
 }
 
+moe_status moe_layer_decode_workspace_offsets(const moe_dims* d, int32_t has_shared, size_t* offs) {
+  if (!dims_ok(d) || !offs) return MOE_ERR_INVALID_ARG;
+  if (!decode_fused_ok(d)) return MOE_ERR_UNSUPPORTED;
+  size_t o[16];
+  moe_decode_ws_layout(d->T, d->H, d->I, d->E, d->k, has_shared != 0, o);
+  for (int i = 0; i < 11; ++i) offs[i] = o[i];
+  return MOE_OK;
+}
+
 moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
                             const moe_experts* shared, const uint16_t* x_bf16,
                             const uint16_t* wr_bf16, const float* logit_bias, float* logits_out,
@@ -438,7 +447,9 @@ moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
   if (!dims_ok(d) || !routed || !x_bf16 || !wr_bf16 || !logits_out || !topk_ids || !topk_w ||
       !sorted_pair || !expert_offsets || !pair_pos || !y_pairs || !out_f32)
     return MOE_ERR_INVALID_ARG;
-  if (routed->fmt != MOE_W_STQ1_0) return MOE_ERR_UNSUPPORTED;
+  const bool mx = routed->fmt == MOE_W_MXFP4 || routed->fmt == MOE_W_MXFP4_TILED;
+  if (routed->fmt != MOE_W_STQ1_0 && !mx) return MOE_ERR_UNSUPPORTED;
+  if (mx && !moe_decode_mx_ok(d->T, d->I, d->k)) return MOE_ERR_UNSUPPORTED;
   if (!mat_ok(routed->gate, true) || !mat_ok(routed->up, true) || !mat_ok(routed->down, true))
     return MOE_ERR_INVALID_ARG;
   if (shared) {
@@ -527,7 +538,7 @@ moe_status moe_mx_quant_act(int64_t rows, int32_t K, const uint16_t* x_bf16, con
   if ((x_bf16 == nullptr) == (x_f32 == nullptr)) return MOE_ERR_INVALID_ARG;
   if (rows > 0 && (!q || !sc)) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
-  if (rows * (K / 32) > (int64_t)256 * 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
+  if ((rows * (int64_t)K + 255) / 256 > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;   // one lane per element
   hipStream_t s = as_stream(stream);
   bump(MOE_CNT_MX_QUANT);
   return finish(moe_launch_mx_quant(rows, K, x_bf16, x_f32, q, sc, s), s);

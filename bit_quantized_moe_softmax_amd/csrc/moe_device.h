@@ -81,6 +81,23 @@ __device__ __forceinline__ int moe_mx_exp(uint32_t amax_bits) {
   return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
+// Lane-parallel MX quantisation: lanes 32q .. 32q + 31 of the wave hold the 32 values of
+// one group (fp32 bit patterns, finite).  Returns this lane's E4M3 code and the group's
+// UE8M0 scale byte in *scale (scale byte 0 and zero codes for an all-zero group).
+// Every lane of the wave must call it (the group maximum is a cross-lane reduction).
+__device__ __forceinline__ uint32_t moe_mx_quant_lane(uint32_t bits, uint32_t* scale) {
+  uint32_t am = bits & 0x7FFFFFFFu;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o, 64));
+  if (am == 0) {
+    *scale = 0;
+    return 0;
+  }
+  const int X = moe_mx_exp(am);
+  *scale = (uint32_t)(X + 127);
+  return moe_e4m3_from_f32(bits, X);
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -225,6 +242,7 @@ void moe_prof_end(int slot, hipStream_t s);
 
 // Fused decode layer (three kernels).
 bool moe_decode_shape_ok(int H, int I, int E);
+bool moe_decode_mx_ok(int T, int I, int k);
 size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, size_t* offs);
 hipError_t moe_launch_decode_fused(const moe_dims* d, const moe_experts* routed,
                                    const moe_experts* shared, const uint16_t* x,

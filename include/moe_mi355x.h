@@ -228,17 +228,21 @@ MOE_MI355X_API moe_status moe_combine(const moe_dims* d, const float* y_pairs,
 
 /* ---------------------------------------------------------------------------
  * Fused decode layer: the same computation as moe_route + moe_permute + moe_expert_ffn
- * + moe_combine for STQ1_0 routed experts and an optional bf16 shared expert, in three
- * kernels (the fused top-8 MoE operator idea of "Hy4-preview Flash-MoE STQ1_0",
- * Important runtime choices: --slot8).  Every intermediate the four calls expose is
+ * + moe_combine for STQ1_0 or MXFP4 (row-major or tiled) routed experts and an optional
+ * bf16 shared expert, in three kernels (the fused top-8 MoE operator idea of "Hy4-preview
+ * Flash-MoE STQ1_0", Important runtime choices: --slot8).  Every intermediate the four calls expose is
  * written to the same caller buffers (logits_out, topk_ids, topk_w, sorted_pair,
  * expert_offsets, pair_pos, y_pairs, y_shared), then out_f32 (and out_bf16 when
  * non-NULL) = combine (+ residual; residual may equal out_f32).  The router runs from
  * x (no logits_in).  Numerics: router logits are summed in a different order than
  * moe_route's, so they may differ from it in the last bits; everything else follows the
  * four-call definitions.
+ * MXFP4 routed experts follow moe_expert_ffn's MXFP4 definition: x and h MX-quantised to
+ * E4M3 (group 32 along H, resp. I) before their projections.
  * Limits: T <= 64, k <= 32, E <= 256, and (H, I) one of the compiled shapes (512, 256),
- * (1024, 512), (2048, 1024), (4096, 2048), (6144, 2048), (8192, 2048).
+ * (1024, 512), (2048, 1024), (4096, 2048), (6144, 2048), (8192, 2048); MXFP4 routed
+ * experts also T <= 4 and T k (I + I/32) <= 81920 (every pair's FP8 h fits the down
+ * kernel's LDS).
  * Workspace: at least moe_layer_decode_workspace_size bytes.  It holds one atomic ticket
  * counter that MUST be zero before the first call on a given workspace (clear the buffer
  * once after allocating it); every call leaves it zero.  Calls sharing one workspace must
@@ -246,6 +250,15 @@ MOE_MI355X_API moe_status moe_combine(const moe_dims* d, const float* y_pairs,
  * ------------------------------------------------------------------------- */
 MOE_MI355X_API moe_status moe_layer_decode_workspace_size(const moe_dims* d, int32_t has_shared,
                                                           size_t* bytes);
+/* Byte offsets of the fused decode workspace regions, so tests can read intermediates
+ * (host-only):
+ *   offs[6] routed h: STQ1_0 bf16 hi [P][I] (lo half at offs[7]); MXFP4 E4M3 codes [P][I]
+ *           then UE8M0 scales [P][I/32], in sorted-pair order
+ *   offs[8] shared h, bf16 hi [T][I] then lo [T][I]
+ *   offs[9] MXFP4: x as E4M3 codes [T][H] then UE8M0 scales [T][H/32]
+ *   offs[10] total bytes (offs[0..5]: work lists, ticket, router partials) */
+MOE_MI355X_API moe_status moe_layer_decode_workspace_offsets(const moe_dims* d, int32_t has_shared,
+                                                             size_t* offs);
 MOE_MI355X_API moe_status moe_layer_decode(
     const moe_dims* d, const moe_experts* routed, const moe_experts* shared,
     const uint16_t* x_bf16, const uint16_t* wr_bf16, const float* logit_bias, float* logits_out,

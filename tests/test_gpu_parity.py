@@ -440,27 +440,13 @@ def test_layer_cfg2_hy4_decode_zipf_sampled():
 MX_SMALL = synth.LayerCfg("mx", 150, 512, 256, 8, 2, True, "mxfp4", False, True, 1, 13)
 
 
-def _mx_stage_check(c, inp, bufs, d, experts_check=None):
-    offs = M.moe_workspace_offsets(d, M.MOE_W_MXFP4, bool(c.shared))
-    ws = host(bufs.ws)
-    T, H, I, P = c.T, c.H, c.I, c.T * c.k
-    xq = ws[offs[2]:offs[2] + T * H].reshape(T, H)
-    xs = ws[offs[3]:offs[3] + T * H // 32].reshape(T, H // 32)
-    rq, rs = O.mx_quantize_e4m3(O.bf16_to_f64(inp["x"]))
-    assert (xq == rq).all() and (xs == rs).all()
-    hq = ws[offs[4]:offs[4] + P * I].reshape(P, I)
-    hs = ws[offs[5]:offs[5] + P * I // 32].reshape(P, I // 32)
-    # reference h from the oracle's pieces on the pairs the GPU routed
-    sp = host(bufs.sorted_pair)
-    off = host(bufs.offsets)
-    _, rid, _ = O.route(c.k, logits_in=inp["logits_in"])
-    assert (host(bufs.topk_ids) == rid).all()
-    get_w = oracle_weights(c, inp["routed"])
-    a = O.mx_dequantize_e4m3(rq, rs)
-    yp = host(bufs.y_pairs)
+def _mx_h_down_check(c, get_w, a, hq, hs, yp, sp, off, experts):
+    """h codes of the pairs the GPU routed against the oracle's MX quantisation of
+    SiLU(x W_g^T) * (x W_u^T) (a = dequantised E4M3 x), and the down projection fed the GPU's
+    FP8 h.  A code may flip where the GPU's fp32 h and the oracle's float64 h fall on either
+    side of an E4M3 rounding boundary: flips are counted and must stay one step wide."""
     n_flip = n_tot = 0
     worst = 0.0
-    experts = range(c.E) if experts_check is None else experts_check
     for e in experts:
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
@@ -478,15 +464,34 @@ def _mx_stage_check(c, inp, bufs, d, experts_check=None):
             assert (np.abs(vg - vr)[diff] <= step[diff] * 1.0001).all()
         n_flip += int(diff.sum())
         n_tot += diff.size
-        # down stage fed the GPU's FP8 h
         y_ref = O.mx_dequantize_e4m3(hq[lo:hi], hs[lo:hi]) @ get_w(e, 2).T
         worst = max(worst, float(row_err(yp[lo:hi], y_ref).max()))
     say("mx h code flips", n_flip, "of", n_tot, "down-stage max row err", worst)
-    # A code flips when the GPU's fp32 h and the oracle's float64 h fall on either side of an
-    # E4M3 rounding boundary.  The scaled MFMA's dot products carry ~2^-14 relative error, so
-    # with boundaries 2^-3 apart (relative) about 2 * 1e-4 / 2^-3 = 1.6e-3 of the codes may flip.
+    # The scaled MFMA's dot products carry ~2^-14 relative error, so with boundaries 2^-3
+    # apart (relative) about 2 * 1e-4 / 2^-3 = 1.6e-3 of the codes may flip.
     assert n_flip <= max(2, 2e-3 * n_tot)
     assert worst <= TOL
+
+
+def _mx_stage_check(c, inp, bufs, d, experts_check=None):
+    offs = M.moe_workspace_offsets(d, M.MOE_W_MXFP4, bool(c.shared))
+    ws = host(bufs.ws)
+    T, H, I, P = c.T, c.H, c.I, c.T * c.k
+    xq = ws[offs[2]:offs[2] + T * H].reshape(T, H)
+    xs = ws[offs[3]:offs[3] + T * H // 32].reshape(T, H // 32)
+    rq, rs = O.mx_quantize_e4m3(O.bf16_to_f64(inp["x"]))
+    assert (xq == rq).all() and (xs == rs).all()
+    hq = ws[offs[4]:offs[4] + P * I].reshape(P, I)
+    hs = ws[offs[5]:offs[5] + P * I // 32].reshape(P, I // 32)
+    # reference h from the oracle's pieces on the pairs the GPU routed
+    sp = host(bufs.sorted_pair)
+    off = host(bufs.offsets)
+    _, rid, _ = O.route(c.k, logits_in=inp["logits_in"])
+    assert (host(bufs.topk_ids) == rid).all()
+    get_w = oracle_weights(c, inp["routed"])
+    a = O.mx_dequantize_e4m3(rq, rs)
+    experts = range(c.E) if experts_check is None else experts_check
+    _mx_h_down_check(c, get_w, a, hq, hs, host(bufs.y_pairs), sp, off, experts)
 
 
 MX_MORE = {
@@ -583,9 +588,9 @@ FUSED = {
 }
 
 
-def run_fused(c, inp, residual=None, with_bf16=False, ws=None):
+def run_fused(c, inp, residual=None, with_bf16=False, ws=None, tiled=False):
     d = M.Dims(c.T, c.H, c.I, c.E, c.k)
-    routed = routed_experts(c, inp["routed"])
+    routed = routed_experts(c, inp["routed"], tiled)
     shared = shared_experts(inp["shared"])
     f32, i32 = torch.float32, torch.int32
     o = dict(logits=torch.empty((c.T, c.E), dtype=f32, device="cuda"),
@@ -644,6 +649,81 @@ def test_fused_decode_small(name):
     # the counters were left zero: a second call on the same workspace gives the same bits
     o2 = run_fused(c, inp, residual=dev(resid), ws=o["ws"])
     assert (host(o2["out"]).view(np.uint32) == out.view(np.uint32)).all()
+
+
+MX_FUSED = {
+    "h512-i256-e8-top2-t1-shared": synth.LayerCfg("t", 1, 512, 256, 8, 2, True, "mxfp4", False, False, 1, 41),
+    "h1024-i512-e16-top4-t3-zipf": synth.LayerCfg("t", 3, 1024, 512, 16, 4, True, "mxfp4", True, False, 1, 42),
+    "h512-i256-e64-top8-t4-shared": synth.LayerCfg("t", 4, 512, 256, 64, 8, True, "mxfp4", False, False, 1, 43),
+    # experts shared by both tokens
+    "h512-i256-e4-top4-t2-noshared": synth.LayerCfg("t", 2, 512, 256, 4, 4, False, "mxfp4", False, False, 1, 44),
+    # one pair: the staged h run (264 bytes) is not a whole number of 16-byte pieces
+    "h512-i256-e8-top1-t1-noshared": synth.LayerCfg("t", 1, 512, 256, 8, 1, False, "mxfp4", False, False, 1, 45),
+}
+
+
+def _fused_mx_check(c, inp, o, resid, experts=None):
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    T, H, I, P = c.T, c.H, c.I, d.P
+    rl, rid, _ = O.route(c.k, inp["x"], inp["wr"], inp["bias"])
+    assert np.abs(host(o["logits"]) - rl).max() < 2e-5
+    tie = near_tie_tokens(rl, c.k)
+    gi = host(o["ids"])
+    assert (gi[~tie] == rid[~tie]).all()
+    for t in np.flatnonzero(tie):
+        assert valid_selection(rl[t], gi[t], c.k)
+    rsp, roff, rpp = O.permute(gi, c.E)
+    sp, off = host(o["sp"]), host(o["off"])
+    assert (sp == rsp).all() and (off == roff).all() and (host(o["pp"]) == rpp).all()
+    offs = M.moe_layer_decode_workspace_offsets(d, inp["shared"] is not None)
+    ws = host(o["ws"])
+    xq = ws[offs[9]:offs[9] + T * H].reshape(T, H)
+    xs = ws[offs[9] + T * H:offs[9] + T * H + T * H // 32].reshape(T, H // 32)
+    rq, rs = O.mx_quantize_e4m3(O.bf16_to_f64(inp["x"]))
+    assert (xq == rq).all() and (xs == rs).all()
+    hq = ws[offs[6]:offs[6] + P * I].reshape(P, I)
+    hs = ws[offs[6] + P * I:offs[6] + P * I + P * I // 32].reshape(P, I // 32)
+    yp = host(o["yp"])
+    _mx_h_down_check(c, oracle_weights(c, inp["routed"]), O.mx_dequantize_e4m3(rq, rs), hq, hs, yp,
+                     sp, off, range(c.E) if experts is None else experts)
+    ysh = None
+    if inp["shared"] is not None:
+        ysh = host(o["ysh"])
+        assert row_err(ysh, O.shared_expert(inp["x"], *inp["shared"])).max() <= TOL
+    w = host(o["w"])
+    out_ref = O.combine(yp, w, host(o["pp"]), ysh, None if resid is None else resid.astype(np.float64))
+    err = row_err(host(o["out"]), out_ref)
+    say("fused mx combine max row err", float(err.max()))
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["rowmajor", "tiled"])
+@pytest.mark.parametrize("name", list(MX_FUSED))
+def test_fused_decode_mx_small(name, tiled):
+    """Fused decode with MXFP4 routed experts: x and h codes bit-exact / within one E4M3
+    step of the oracle on the GPU's routing, y_pairs from the GPU's h, shared expert, combine."""
+    c = MX_FUSED[name]
+    say("fused decode mx", name, "tiled" if tiled else "row-major")
+    inp = layer_inputs(c)
+    res = synth.activations(c.seed + 100, 0, c.T, c.H).astype(np.uint16)
+    resid = O.bf16_to_f64(res).astype(np.float32)
+    M.moe_reset_counters()
+    o = run_fused(c, inp, residual=dev(resid), with_bf16=True, tiled=tiled)
+    assert M.moe_get_counters()["decode_fused"] == 1
+    _fused_mx_check(c, inp, o, resid)
+    out = host(o["out"])
+    assert (host(o["obf"], np.uint16) == O.f64_to_bf16_bits(out.astype(np.float64))).all()
+    o2 = run_fused(c, inp, residual=dev(resid), ws=o["ws"], tiled=tiled)
+    assert (host(o2["out"]).view(np.uint32) == out.view(np.uint32)).all()
+
+
+def test_fused_decode_mx_hy4_t1():
+    """Hy4 shape, one token, MXFP4 (tiled) routed experts and the bf16 shared expert."""
+    c = synth.LayerCfg("hy4-mxfp4-decode-t1", 1, 6144, 2048, 256, 8, True, "mxfp4", False, False, 1, 46)
+    say("fused decode mx hy4 generate")
+    inp = layer_inputs(c)
+    o = run_fused(c, inp, tiled=True)
+    _fused_mx_check(c, inp, o, None, experts=sorted(set(host(o["ids"]).ravel().tolist())))
 
 
 def test_fused_decode_cfg1_hy4():
