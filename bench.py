@@ -10,7 +10,9 @@ the previous one.
 Printed: one JSON line.  `value` = expert-weight GB/s = (bytes of the 8 routed experts the
 token touches + the shared expert) / step time.  Also reported: whole-layer algorithmic
 GB/s, per-stage times from HIP events, the roofline of the dominant kernel, the CPU oracle
-timed on a bounded sample, and a prefill line (4096 tokens, MXFP4 x FP8) in TFLOP/s.
+timed on a bounded sample, a prefill line (4096 tokens, MXFP4 x FP8) in TFLOP/s with and
+without the shared expert, and the other format x regime pairs: STQ1_0 prefill (4096
+tokens) and MXFP4 decode (one token, fused entry point).
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+FP16_PEAK_TFLOPS = 2500.0
 STQ_MAT_BYTES = 2048 * 6144 // 256 * 42          # one Hy4 STQ1_0 expert matrix
 MX_MAT_BYTES = 2048 * 6144 // 2 + 2048 * 6144 // 32
 
@@ -42,6 +45,7 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=5)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the STQ1_0 prefill and MXFP4 decode lines")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first run a plain copy kernel (torch.neg) over this many MiB, three times, "
                         "as the reference dispatch for the HBM byte counters")
@@ -215,7 +219,129 @@ def prefill_bench(args):
     prof = M.moe_profile_read()
     M.moe_profile_enable(False)
     flops = 2.0 * c.T * c.k * 3 * c.I * c.H
-    return dict(c=c, routed_ms=r_ms, flops=flops, tflops=flops / (r_ms * 1e-3) / 1e12, prof=prof)
+    # the same layer with its bf16 shared expert (prefill grouped GEMMs on the bf16 MFMA)
+    from bit_quantized_moe_softmax_amd.layer import bf16_experts
+    sh = bf16_experts(*[dev(w) for w in synth.shared_weights(c.seed, 0, c.I, c.H)])
+    M.moe_expert_ffn(d, R, sh, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs, bufs.y_shared, bufs.ws, s)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.prefill_steps):
+        M.moe_expert_ffn(d, R, sh, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs, bufs.y_shared, bufs.ws, s)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ws_ms = ev[0].elapsed_time(ev[1]) / args.prefill_steps
+    return dict(c=c, routed_ms=r_ms, flops=flops, tflops=flops / (r_ms * 1e-3) / 1e12, prof=prof,
+                with_shared_ms=ws_ms, shared_flops=2.0 * c.T * 3 * c.I * c.H)
+
+
+def stq_prefill_bench(args):
+    """Hy4 STQ1_0 layer at 4096 tokens through moe_expert_ffn: routed experts on the fp16-MFMA
+    grouped GEMMs (weights decoded in registers) and the bf16 shared expert."""
+    import torch
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    from bit_quantized_moe_softmax_amd.layer import LayerBuffers, bf16_experts
+
+    c = synth.cfg(3)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = [synth.stq1_family(c.seed, 0, m, c.E, c.I * c.H) for m in range(3)]
+    R = M.Experts(M.MOE_W_STQ1_0, *[(dev(cd), dev(sc)) for cd, sc in routed])
+    del routed
+    sh = bf16_experts(*[dev(w) for w in synth.shared_weights(c.seed, 0, c.I, c.H)])
+    x = dev(synth.activations(c.seed, 0, c.T, c.H))
+    logits = dev(synth.prefill_logits(c.seed, 0, c.T, c.E))
+    bufs = LayerBuffers(d, M.MOE_W_STQ1_0, True)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    M.moe_route(d, None, None, None, logits, bufs.logits, bufs.topk_ids, bufs.topk_w, s)
+    M.moe_permute(d, bufs.topk_ids, bufs.sorted_pair, bufs.offsets, bufs.pair_pos, s)
+
+    def run(n, shared):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(n):
+            M.moe_expert_ffn(d, R, sh if shared else None, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs,
+                             bufs.y_shared if shared else None, bufs.ws, s)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    run(1, True)
+    r_ms = run(args.prefill_steps, False)
+    ws_ms = run(args.prefill_steps, True)
+    M.moe_profile_enable(True)
+    run(args.prefill_steps, True)
+    prof = M.moe_profile_read()
+    M.moe_profile_enable(False)
+    flops = 2.0 * c.T * c.k * 3 * c.I * c.H
+    return dict(c=c, routed_ms=r_ms, with_shared_ms=ws_ms, flops=flops, prof=prof)
+
+
+def mx_decode_bench(args):
+    """Hy4 layer with MXFP4 (tiled) routed experts, one token, through moe_layer_decode;
+    steps rotate over three layer copies so the weights are not cache-resident."""
+    import torch
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    from bit_quantized_moe_softmax_amd.layer import bf16_experts
+
+    c = synth.cfg(1)
+    d = M.Dims(1, c.H, c.I, c.E, c.k)
+    shapes = [(c.I, c.H), (c.I, c.H), (c.H, c.I)]
+    copies = []
+    for cp in range(3):
+        seed = c.seed * 1000 + 500 + cp
+        fams = []
+        for m in range(3):
+            cd, sc = synth.mxfp4_family(seed, 0, m, c.E, *shapes[m])
+            dc, ds = dev(cd), dev(sc)
+            tc, ts = torch.empty_like(dc), torch.empty_like(ds)
+            M.moe_mxfp4_pack_tiles(dc, ds, c.E * shapes[m][0], shapes[m][1], tc, ts)
+            torch.cuda.synchronize()
+            fams.append((tc, ts))
+            del cd, sc, dc, ds
+        copies.append(dict(R=M.Experts(M.MOE_W_MXFP4_TILED, *fams),
+                           sh=bf16_experts(*[dev(w) for w in synth.shared_weights(seed, 0, c.I, c.H)]),
+                           wr=dev(synth.router_weights(seed, 0, c.E, c.H)),
+                           x=dev(synth.activations(seed, 0, 64, c.H))))
+    f32, i32 = torch.float32, torch.int32
+    bufs = [torch.empty((1, c.E), dtype=f32, device="cuda"), torch.empty((1, c.k), dtype=i32, device="cuda"),
+            torch.empty((1, c.k), dtype=f32, device="cuda"), torch.empty(d.P, dtype=i32, device="cuda"),
+            torch.empty(c.E + 1, dtype=i32, device="cuda"), torch.empty(d.P, dtype=i32, device="cuda"),
+            torch.empty((d.P, c.H), dtype=f32, device="cuda"), torch.empty((1, c.H), dtype=f32, device="cuda")]
+    out = torch.empty((1, c.H), dtype=f32, device="cuda")
+    ws = torch.zeros(M.moe_layer_decode_workspace_size(d, True), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def step(i):
+        L = copies[i % 3]
+        M.moe_layer_decode(d, L["R"], L["sh"], L["x"][(i // 3) % 64].reshape(1, -1), L["wr"], None, *bufs,
+                           None, out, None, ws, s)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    M.moe_profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = M.moe_profile_read()
+    M.moe_profile_enable(False)
+    mat = c.I * c.H * 17 // 32                     # one MXFP4 expert matrix: E2M1 codes + UE8M0 scales
+    kb = {"decode_k1_route": c.E * c.H * 2 + c.H * 2 + c.H + c.H // 32,
+          "decode_k2_gateup": c.k * 2 * mat + 2 * c.I * c.H * 2 + c.H + c.H // 32 + c.k * c.I * 33 // 32 + c.I * 4,
+          "decode_k3_down_combine": c.k * mat + c.I * c.H * 2 + c.k * c.I * 33 // 32 + c.I * 4
+                                    + c.k * c.H * 4 + 2 * c.H * 4}
+    expert_b = 3 * c.k * mat + 3 * c.I * c.H * 2
+    return dict(c=c, ms=ms, prof=prof, kbytes=kb, expert_b=expert_b)
 
 
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
@@ -417,8 +543,45 @@ def main():
                                            "unit": "TFLOP/s",
                                            "frac": round((pk["mx_gateup"]["tflops"] or 0) / FP8_PEAK_TFLOPS, 4),
                                            "traffic": traffic.get("mx_gateup")}}
+            sh_ms = pre["with_shared_ms"] - pre["routed_ms"]
+            out["prefill"]["with_shared_expert"] = {
+                "layer_ms": round(pre["with_shared_ms"], 4),
+                "shared_ms": round(sh_ms, 4),
+                "shared_tflops_bf16": round(pre["shared_flops"] / (sh_ms * 1e-3) / 1e12, 1) if sh_ms > 0 else None,
+                "kernels": {n: round(pre["prof"][n][0], 2) for n in ("shared_gateup", "shared_down", "act_prep")
+                            if pre["prof"][n][1]}}
         except Exception as e:  # the decode line must still print
             out["prefill"] = {"error": repr(e)}
+    if not args.no_extra:
+        # the other format x regime pairs: STQ1_0 prefill, MXFP4 decode
+        try:
+            sp = stq_prefill_bench(args)
+            pk = {n: round(sp["prof"][n][0], 2) for n in ("stq_gateup", "stq_down", "shared_gateup",
+                                                          "shared_down", "act_prep") if sp["prof"][n][1]}
+            gu = 2.0 * sp["c"].T * sp["c"].k * 2 * sp["c"].I * sp["c"].H
+            out["stq1_0_prefill"] = {
+                "workload": "hy4-stq1_0-prefill-t4096", "routed_ms": round(sp["routed_ms"], 4),
+                "layer_ms": round(sp["with_shared_ms"], 4),
+                "tflops": round(sp["flops"] / (sp["routed_ms"] * 1e-3) / 1e12, 1),
+                "peak_tflops_fp16": FP16_PEAK_TFLOPS,
+                "frac": round(sp["flops"] / (sp["routed_ms"] * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
+                "kernels_us": pk,
+                "gateup_tflops": round(gu / (pk["stq_gateup"] * 1e-6) / 1e12, 1) if pk.get("stq_gateup") else None}
+        except Exception as e:
+            out["stq1_0_prefill"] = {"error": repr(e)}
+        try:
+            md = mx_decode_bench(args)
+            kern = {}
+            for name, nbytes in md["kbytes"].items():
+                us, n = md["prof"][name]
+                kern[name] = {"avg_us": round(us, 3), "algorithmic_bytes": nbytes,
+                              "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None}
+            gbs = md["expert_b"] / (md["ms"] * 1e-3) / 1e9
+            out["mxfp4_decode"] = {"workload": "hy4-mxfp4xfp8-decode-t1", "entry_point": "moe_layer_decode",
+                                   "us_per_step": round(md["ms"] * 1e3, 2), "expert_weight_gbs": round(gbs, 1),
+                                   "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "kernels": kern}
+        except Exception as e:
+            out["mxfp4_decode"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(out), flush=True)

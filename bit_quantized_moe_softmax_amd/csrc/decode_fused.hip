@@ -1451,7 +1451,7 @@ struct MxStream {
 };
 
 // K1 for MXFP4: the router partials, and in the workgroups past them x -> E4M3 with group-32
-// scales, one element per lane (T H is a multiple of 64, so waves past the end are whole).
+// scales, 8 elements per lane (T H / 8 is a multiple of 64, so waves past the end are whole).
 template <int HB>
 __global__ __launch_bounds__(kWG) void k1s_router_mx(DecodeArgs a) {
   constexpr int H = HB * 256;
@@ -1461,11 +1461,14 @@ __global__ __launch_bounds__(kWG) void k1s_router_mx(DecodeArgs a) {
     return;
   }
   const int i = ((int)blockIdx.x - a.n_router_wg) * kWG + (int)threadIdx.x;
-  if (i >= a.T * H) return;
-  uint32_t sc;
-  const uint32_t code = moe_mx_quant_lane((uint32_t)a.x[i] << 16, &sc);
-  a.xq[i] = (uint8_t)code;
-  if ((i & 31) == 0) a.xq[(size_t)a.T * H + i / 32] = (uint8_t)sc;
+  if (i >= a.T * H / 8) return;
+  const uint4 v = reinterpret_cast<const uint4*>(a.x)[i];
+  const uint32_t bits[8] = {v.x << 16, v.x & 0xFFFF0000u, v.y << 16, v.y & 0xFFFF0000u,
+                            v.z << 16, v.z & 0xFFFF0000u, v.w << 16, v.w & 0xFFFF0000u};
+  uint32_t codes[2];
+  const uint32_t sc = moe_mx_quant8(bits, codes);
+  reinterpret_cast<uint2*>(a.xq)[i] = make_uint2(codes[0], codes[1]);
+  if ((i & 3) == 0) a.xq[(size_t)a.T * H + i / 4] = (uint8_t)sc;
 }
 
 // Routed gate/up of one work item (unit, 32 rows of I): wave = (16-row tile, gate|up); the
@@ -1505,7 +1508,7 @@ __device__ __forceinline__ void routed_gateup_mx(const DecodeArgs& a, int wi, co
       uint32_t code = 0, sc = 0;
       if (am != 0) {
         const int X = moe_mx_exp(am);
-        code = moe_e4m3_from_f32(__float_as_uint(h), X);
+        code = moe_e4m3_code(h, X);
         sc = (uint32_t)(X + 127);
       }
       a.hq[pos * I + 32 * tp + c] = (uint8_t)code;
@@ -1657,7 +1660,7 @@ hipError_t launch_small_mx(DecodeArgs& a, hipStream_t s) {
   const int max_units = P < a.E ? P : a.E;
   const bool shared = a.sg != nullptr;
   a.n_router_wg = ((a.E + 15) / 16) * kRouterParts;
-  const int n_xq_wg = (T * H + kWG - 1) / kWG;
+  const int n_xq_wg = (T * H / 8 + kWG - 1) / kWG;
   a.n_sgu_wg = shared ? I / kNW : 0;
   a.n_gu_wg = max_units * (I / 32);
   a.h_lds = 0;

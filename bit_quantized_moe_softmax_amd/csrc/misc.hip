@@ -129,19 +129,30 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint8_t* __res
   out[row * K + col + 1] = e2m1_to_f32(c >> 4) * sc;
 }
 
-// One element per lane; lanes 32q .. 32q + 31 form a group (groups never straddle rows:
-// K is a multiple of 32).  Lanes past the end load the last element and store nothing.
-__global__ __launch_bounds__(256) void mx_quant_kernel(int64_t n, const uint16_t* xb,
+// Eight elements per lane (one 16-byte bf16 load or two fp32 loads); lanes 4q .. 4q + 3
+// form a group (groups never straddle rows: K is a multiple of 32).  Lanes past the end
+// load the last octet and store nothing (n8 is a multiple of 4, so groups stay whole).
+__global__ __launch_bounds__(256) void mx_quant_kernel(int64_t n8, const uint16_t* xb,
                                                        const float* xf, uint8_t* __restrict__ q,
                                                        uint8_t* __restrict__ sc) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t j = i < n ? i : n - 1;
-  const uint32_t bits = xb ? (uint32_t)xb[j] << 16 : __float_as_uint(xf[j]);
-  uint32_t s;
-  const uint32_t code = moe_mx_quant_lane(bits, &s);
-  if (i < n) {
-    q[i] = (uint8_t)code;
-    if ((i & 31) == 0) sc[i / 32] = (uint8_t)s;
+  const int64_t j = i < n8 ? i : n8 - 1;
+  uint32_t bits[8];
+  if (xb) {
+    const uint4 v = reinterpret_cast<const uint4*>(xb)[j];
+    bits[0] = v.x << 16; bits[1] = v.x & 0xFFFF0000u; bits[2] = v.y << 16; bits[3] = v.y & 0xFFFF0000u;
+    bits[4] = v.z << 16; bits[5] = v.z & 0xFFFF0000u; bits[6] = v.w << 16; bits[7] = v.w & 0xFFFF0000u;
+  } else {
+    const uint4 v0 = reinterpret_cast<const uint4*>(xf)[2 * j];
+    const uint4 v1 = reinterpret_cast<const uint4*>(xf)[2 * j + 1];
+    bits[0] = v0.x; bits[1] = v0.y; bits[2] = v0.z; bits[3] = v0.w;
+    bits[4] = v1.x; bits[5] = v1.y; bits[6] = v1.z; bits[7] = v1.w;
+  }
+  uint32_t codes[2];
+  const uint32_t s = moe_mx_quant8(bits, codes);
+  if (i < n8) {
+    reinterpret_cast<uint2*>(q)[i] = make_uint2(codes[0], codes[1]);
+    if ((i & 3) == 0) sc[i / 4] = (uint8_t)s;
   }
 }
 
@@ -187,10 +198,10 @@ hipError_t moe_launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales,
 
 hipError_t moe_launch_mx_quant(int64_t rows, int K, const uint16_t* xb, const float* xf,
                                uint8_t* q, uint8_t* sc, hipStream_t s) {
-  const int64_t n = rows * K;
-  if (n == 0) return hipSuccess;
-  if ((n + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n,
+  const int64_t n8 = rows * K / 8;
+  if (n8 == 0) return hipSuccess;
+  if ((n8 + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, n8,
                      xb, xf, q, sc);
   return hipGetLastError();
 }

@@ -538,7 +538,7 @@ moe_status moe_mx_quant_act(int64_t rows, int32_t K, const uint16_t* x_bf16, con
   if ((x_bf16 == nullptr) == (x_f32 == nullptr)) return MOE_ERR_INVALID_ARG;
   if (rows > 0 && (!q || !sc)) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
-  if ((rows * (int64_t)K + 255) / 256 > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;   // one lane per element
+  if ((rows * (int64_t)K / 8 + 255) / 256 > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;   // 8 elements per lane
   hipStream_t s = as_stream(stream);
   bump(MOE_CNT_MX_QUANT);
   return finish(moe_launch_mx_quant(rows, K, x_bf16, x_f32, q, sc, s), s);

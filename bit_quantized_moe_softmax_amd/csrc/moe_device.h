@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <math.h>
 
 #include "moe_mi355x.h"
 
@@ -81,21 +82,50 @@ __device__ __forceinline__ int moe_mx_exp(uint32_t amax_bits) {
   return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
-// Lane-parallel MX quantisation: lanes 32q .. 32q + 31 of the wave hold the 32 values of
-// one group (fp32 bit patterns, finite).  Returns this lane's E4M3 code and the group's
-// UE8M0 scale byte in *scale (scale byte 0 and zero codes for an all-zero group).
-// Every lane of the wave must call it (the group maximum is a cross-lane reduction).
-__device__ __forceinline__ uint32_t moe_mx_quant_lane(uint32_t bits, uint32_t* scale) {
-  uint32_t am = bits & 0x7FFFFFFFu;
+// The E4M3 code of v / 2^X by the rule of moe_e4m3_from_f32, branch-free: y = v 2^-X is
+// exact wherever the code is not zero (a power-of-two scaling), the rounding quantum is
+// 2^max(floor(log2|y|) - 3, -9), and rint() rounds the scaled magnitude to the nearest
+// integer R (ties to even); R <= 16 picks the code.  Equal to moe_e4m3_from_f32 for every
+// finite fp32 input with |v| < 2^(X + 9) (checked exhaustively on the CPU at nine X).
+__device__ __forceinline__ uint32_t moe_e4m3_code(float v, int X) {
+  const float y = ldexpf(v, -X);
+  const uint32_t yb = __float_as_uint(y);
+  const uint32_t sign = (yb >> 24) & 0x80u;
+  const int e = (int)((yb >> 23) & 0xFFu) - 127;
+  const int q = max(e - 3, -9);
+  const uint32_t R = (uint32_t)rintf(ldexpf(fabsf(y), -q));
+  const bool normal = q > -9 || R >= 8;
+  const int ef = q + 10 + (int)(R >> 4);
+  const uint32_t m = R == 16 ? 0u : R - 8;
+  uint32_t code = normal ? (((uint32_t)ef << 3) | m) : R;
+  code = (ef > 15 || (ef == 15 && m > 6)) ? 0x7Eu : code;
+  return sign | code;
+}
+
+// Lane-parallel MX quantisation of 8 consecutive values per lane (fp32 bit patterns,
+// finite): lanes 4q .. 4q + 3 of the wave hold the 32 values of one group.  Writes this
+// lane's 8 E4M3 codes (element j in byte j % 4 of word j / 4) and returns the group's UE8M0
+// scale byte (0 and zero codes for an all-zero group).  Every lane of the wave must call it
+// (the group maximum is a cross-lane reduction).
+__device__ __forceinline__ uint32_t moe_mx_quant8(const uint32_t* bits, uint32_t* codes) {
+  uint32_t am = 0;
 #pragma unroll
-  for (int o = 1; o < 32; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o, 64));
+  for (int i = 0; i < 8; ++i) am = max(am, bits[i] & 0x7FFFFFFFu);
+  am = max(am, (uint32_t)__shfl_xor((int)am, 1, 64));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 2, 64));
   if (am == 0) {
-    *scale = 0;
+    codes[0] = codes[1] = 0;
     return 0;
   }
   const int X = moe_mx_exp(am);
-  *scale = (uint32_t)(X + 127);
-  return moe_e4m3_from_f32(bits, X);
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c |= moe_e4m3_code(__uint_as_float(bits[4 * w + j]), X) << (8 * j);
+    codes[w] = c;
+  }
+  return (uint32_t)(X + 127);
 }
 
 // ---------------------------------------------------------------- wave helpers

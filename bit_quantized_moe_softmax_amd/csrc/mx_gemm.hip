@@ -64,25 +64,6 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   return v;
 }
 
-// E4M3 code of v / 2^X, nearest-even, saturated at 448 -- the rule of moe_e4m3_from_f32,
-// branch-free for the epilogue: y = v 2^-X is exact (a power-of-two scaling), the rounding
-// quantum is 2^max(floor(log2|y|) - 3, -9) and rint() rounds the scaled magnitude to the
-// nearest integer R (ties to even); R <= 16 picks the code.
-__device__ __forceinline__ uint32_t e4m3_code(float v, int X) {
-  const float y = ldexpf(v, -X);
-  const uint32_t yb = __float_as_uint(y);
-  const uint32_t sign = (yb >> 24) & 0x80u;
-  const int e = (int)((yb >> 23) & 0xFFu) - 127;
-  const int q = max(e - 3, -9);
-  const uint32_t R = (uint32_t)rintf(ldexpf(fabsf(y), -q));
-  const bool normal = q > -9 || R >= 8;
-  const int ef = q + 10 + (int)(R >> 4);
-  const uint32_t m = R == 16 ? 0u : R - 8;
-  uint32_t code = normal ? (((uint32_t)ef << 3) | m) : R;
-  code = (ef > 15 || (ef == 15 && m > 6)) ? 0x7Eu : code;
-  return sign | code;
-}
-
 template <bool GATEUP, bool TILED>
 __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   __shared__ __align__(16) uint8_t s_a[2][kMB * kAStride];
@@ -283,8 +264,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
             if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = 0;
           } else {
             const int X = moe_mx_exp(amax);
-            hrow[c16] = (uint8_t)e4m3_code(h[0], X);
-            hrow[c16 + 16] = (uint8_t)e4m3_code(h[1], X);
+            hrow[c16] = (uint8_t)moe_e4m3_code(h[0], X);
+            hrow[c16 + 16] = (uint8_t)moe_e4m3_code(h[1], X);
             if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = (uint8_t)(X + 127);
           }
         }
