@@ -345,14 +345,19 @@ def mx_decode_bench(args):
 
 
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
-    "decode_k1_route": "k1s_router", "decode_k2_gateup": "k2s_gateup",
-    "decode_k3_down_combine": "k3_down_combine", "mx_gateup": "mx_gemm_kernel<true, true>",
-    "mx_down": "mx_gemm_kernel<false, true>", "copy": "neg_kernel"}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hy4_t1_hbm_traffic.md")
+    "decode_k1_route": "k1s_router<", "decode_k2_gateup": "k2s_gateup<",
+    "decode_k3_down_combine": "k3_down_combine<", "mx_gateup": "mx_gemm_kernel<true, true>",
+    "mx_down": "mx_gemm_kernel<false, true>", "stq_gateup": "g16_kernel<0, true>",
+    "stq_down": "g16_kernel<0, false>", "mxdec_k2_gateup": "k2s_gateup_mx<",
+    "mxdec_k3_down_combine": "k3_down_combine_mx<", "copy": "neg_kernel"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hy4_layer_hbm_traffic_per_kernel.md")
 _DEC_SRC = "bit_quantized_moe_softmax_amd/csrc/decode_fused.hip"
 _MX_SRC = "bit_quantized_moe_softmax_amd/csrc/mx_gemm.hip"
+_G16_SRC = "bit_quantized_moe_softmax_amd/csrc/gemm16.hip"
 TRAFFIC_SOURCES = {"decode_k1_route": _DEC_SRC, "decode_k2_gateup": _DEC_SRC,
-                   "decode_k3_down_combine": _DEC_SRC, "mx_gateup": _MX_SRC, "mx_down": _MX_SRC}
+                   "decode_k3_down_combine": _DEC_SRC, "mx_gateup": _MX_SRC, "mx_down": _MX_SRC,
+                   "stq_gateup": _G16_SRC, "stq_down": _G16_SRC, "mxdec_k2_gateup": _DEC_SRC,
+                   "mxdec_k3_down_combine": _DEC_SRC}
 
 
 def source_hash(slot):
@@ -559,6 +564,7 @@ def main():
             pk = {n: round(sp["prof"][n][0], 2) for n in ("stq_gateup", "stq_down", "shared_gateup",
                                                           "shared_down", "act_prep") if sp["prof"][n][1]}
             gu = 2.0 * sp["c"].T * sp["c"].k * 2 * sp["c"].I * sp["c"].H
+            gu_tf = round(gu / (pk["stq_gateup"] * 1e-6) / 1e12, 1) if pk.get("stq_gateup") else None
             out["stq1_0_prefill"] = {
                 "workload": "hy4-stq1_0-prefill-t4096", "routed_ms": round(sp["routed_ms"], 4),
                 "layer_ms": round(sp["with_shared_ms"], 4),
@@ -566,7 +572,10 @@ def main():
                 "peak_tflops_fp16": FP16_PEAK_TFLOPS,
                 "frac": round(sp["flops"] / (sp["routed_ms"] * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
                 "kernels_us": pk,
-                "gateup_tflops": round(gu / (pk["stq_gateup"] * 1e-6) / 1e12, 1) if pk.get("stq_gateup") else None}
+                "roofline": {"bound": "mfma", "kernel": "stq_gateup", "achieved": gu_tf,
+                             "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round((gu_tf or 0) / FP16_PEAK_TFLOPS, 4),
+                             "traffic": traffic.get("stq_gateup")}}
         except Exception as e:
             out["stq1_0_prefill"] = {"error": repr(e)}
         try:
@@ -577,9 +586,15 @@ def main():
                 kern[name] = {"avg_us": round(us, 3), "algorithmic_bytes": nbytes,
                               "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None}
             gbs = md["expert_b"] / (md["ms"] * 1e-3) / 1e9
+            k2 = kern["decode_k2_gateup"]
             out["mxfp4_decode"] = {"workload": "hy4-mxfp4xfp8-decode-t1", "entry_point": "moe_layer_decode",
                                    "us_per_step": round(md["ms"] * 1e3, 2), "expert_weight_gbs": round(gbs, 1),
-                                   "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "kernels": kern}
+                                   "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "kernels": kern,
+                                   "roofline": {"bound": "hbm", "kernel": "decode_k2_gateup (MXFP4)",
+                                                "achieved": k2["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                "frac": round((k2["gbs"] or 0) / HBM_PEAK_GBS, 4),
+                                                "traffic": traffic.get("mxdec_k2_gateup"),
+                                                "algorithmic_bytes": k2["algorithmic_bytes"]}}
         except Exception as e:
             out["mxfp4_decode"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
