@@ -226,6 +226,90 @@ def stq1_matrix(codes, scales, N: int, K: int) -> np.ndarray:
     return stq1_decode(codes, scales, N * K).reshape(N, K)
 
 
+# -----------------------------------------------------------------------------
+# STQ1_0 encoders ("Hy4-preview-GGUF" (AngelSlim), section 3, Our encoder)
+# -----------------------------------------------------------------------------
+# A float matrix is encoded per 256-weight block of its flattened row-major order (the
+# blocks stq1_decode reads), with importance w per weight: the imatrix entry of the
+# weight's input column (column = flat index mod K), or 1 without an imatrix.
+#  * upstream: d = the block's largest magnitude; in every group the lane of smallest |x|
+#    is zeroed.
+#  * wls (the pages' encoder): alternate (i) the weighted least-squares scale
+#    d = sum(w sel x) / sum(w sel^2) for the current selection and (ii) in every group the
+#    zero at the lane of smallest incremental cost w_j (x_j^2 - (|x_j| - d)^2), 3 rounds.
+# Readings (the pages leave these open): the rounds start from the upstream zero placement;
+# a round is (i) then (ii), and a final (i) fits d to the final selection; a kept lane
+# takes the sign of x (x = 0 counts as positive); ties go to the lowest lane; a block whose
+# kept lanes all have w = 0 keeps d = amax; d is rounded to fp16 (nearest even) once, at the
+# end.
+
+STQ_ENC_ROUNDS = 3
+
+
+def _stq_blocks(x, K: int, imatrix):
+    """x and its importance as [n_blk, 64, 4] float64."""
+    x = np.asarray(x, dtype=np.float64).reshape(-1)
+    assert x.size % STQ_BLOCK == 0
+    if imatrix is None:
+        w = np.ones_like(x)
+    else:
+        w = np.asarray(imatrix, dtype=np.float64).reshape(-1)[np.arange(x.size) % K]
+    shp = (x.size // STQ_BLOCK, STQ_GROUPS, 4)
+    return x.reshape(shp), w.reshape(shp)
+
+
+def stq1_ls_scale(xb, wb, z):
+    """Weighted least-squares d of each block for zero lanes z [n_blk, 64], the kept lanes
+    carrying sign(x): sel x = |x| and sel^2 = 1 on them."""
+    kept = np.arange(4)[None, None, :] != np.asarray(z)[:, :, None]
+    num = (wb * np.abs(xb) * kept).sum(axis=(1, 2))
+    den = (wb * kept).sum(axis=(1, 2))
+    amax = np.abs(xb).max(axis=(1, 2))
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), amax)
+
+
+def stq1_zero_placement(xb, wb, d):
+    """Zero lane of every group: the smallest incremental cost w (x^2 - (|x| - d)^2) of
+    zeroing it instead of keeping it at sign(x) d (first lane on ties)."""
+    cost = wb * (xb * xb - (np.abs(xb) - np.asarray(d)[:, None, None]) ** 2)
+    return np.argmin(cost, axis=2)
+
+
+def stq1_encode_parts(x, K: int, imatrix=None, method: str = "wls", rounds: int = STQ_ENC_ROUNDS):
+    """(zero lanes [n_blk*64], sign fields [n_blk*64], d [n_blk] float64 before rounding)."""
+    xb, wb = _stq_blocks(x, K, imatrix)
+    z = np.argmin(np.abs(xb), axis=2)
+    if method == "upstream":
+        d = np.abs(xb).max(axis=(1, 2))
+    else:
+        assert method == "wls"
+        for _ in range(rounds):
+            d = stq1_ls_scale(xb, wb, z)
+            z = stq1_zero_placement(xb, wb, d)
+        d = stq1_ls_scale(xb, wb, z)
+    neg = xb < 0
+    s = np.zeros(z.shape, dtype=np.int64)
+    for zz in range(4):
+        nz = [j for j in range(4) if j != zz]
+        sz = sum(neg[:, :, j].astype(np.int64) << i for i, j in enumerate(nz))
+        s = np.where(z == zz, sz, s)
+    return z.reshape(-1).astype(np.uint8), s.reshape(-1).astype(np.uint8), d
+
+
+def stq1_encode(x, K: int, imatrix=None, method: str = "wls", rounds: int = STQ_ENC_ROUNDS):
+    """Encode a float matrix (flattened row-major, K columns) into STQ1_0 (code bytes, fp16
+    scale bits)."""
+    z, s, d = stq1_encode_parts(x, K, imatrix, method, rounds)
+    return stq1_pack(z, s, d.astype(np.float16).view(np.uint16))
+
+
+def stq1_weighted_ssd(x, K: int, codes, scales, imatrix=None):
+    """Weighted squared error sum w (x - decode)^2 of every 256-weight block."""
+    xb, wb = _stq_blocks(x, K, imatrix)
+    y = stq1_decode(codes, scales).reshape(xb.shape)
+    return (wb * (xb - y) ** 2).sum(axis=(1, 2))
+
+
 # =============================================================================
 # MXFP4 weights
 # =============================================================================

@@ -396,3 +396,119 @@ def test_tiny_layer_bruteforce():
             for o in range(c.H):
                 out[o] += res["w"][t, j] * sum(hvec[i] * weight(e, 2, o, i) for i in range(c.I))
         assert np.allclose(res["out"][t], out, rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- STQ1_0 encoders
+# "Hy4-preview-GGUF" (AngelSlim), section 3, Our encoder: the upstream encoder (d = amax,
+# zero at the smallest |x|) and the weighted least-squares one (LS scale, imatrix-weighted
+# incremental-cost zero placement, 3 alternating rounds).
+
+def _grid_block_inputs(g, n_blk):
+    """Weights already on the ternary grid: random patterns and fp16 scales, x = d * lanes."""
+    z = g.integers(0, 4, n_blk * 64)
+    s = g.integers(0, 8, n_blk * 64)
+    d = np.abs(g.standard_normal(n_blk) * 0.02).astype(np.float16)
+    d[d == 0] = np.float16(0.01)
+    lanes = np.array([O.stq1_pattern(int(p)) for p in (8 * z + s)], dtype=np.float64)
+    x = (lanes.reshape(n_blk, 256) * d.astype(np.float64)[:, None]).reshape(-1)
+    return x, z, s, d.view(np.uint16)
+
+
+@pytest.mark.parametrize("method", ["upstream", "wls"])
+def test_stq1_encode_recovers_grid_inputs(method):
+    """Inputs already on the grid (what the upstream encoder was made for: QAT weights) come
+    back exactly from both encoders, with or without an imatrix."""
+    g = np.random.default_rng(31)
+    x, z, s, d_bits = _grid_block_inputs(g, 12)
+    want = O.stq1_pack(z, s, d_bits)
+    for imat in (None, np.exp(g.standard_normal(512))):
+        codes, scales = O.stq1_encode(x, 512, imatrix=imat, method=method)
+        assert (codes == want[0]).all() and (scales == want[1]).all()
+
+
+def test_stq1_ls_scale_matches_weighted_lstsq():
+    """For a fixed selection, d minimises sum w (x - d sel)^2: numpy's least-squares solver on
+    the sqrt(w)-weighted one-column system gives the same d."""
+    g = np.random.default_rng(32)
+    K = 256
+    x = g.standard_normal(3 * 256) * 0.03
+    w = np.exp(g.standard_normal(K))
+    xb, wb = O._stq_blocks(x, K, w)
+    z = g.integers(0, 4, (3, 64))
+    d = O.stq1_ls_scale(xb, wb, z)
+    for b in range(3):
+        sel = np.sign(xb[b]) + (xb[b] == 0)
+        sel[np.arange(64), z[b]] = 0
+        a = (np.sqrt(wb[b]) * sel).reshape(-1, 1)
+        ref = np.linalg.lstsq(a, (np.sqrt(wb[b]) * xb[b]).reshape(-1), rcond=None)[0][0]
+        assert abs(d[b] - ref) <= 1e-12 * abs(ref)
+
+
+def test_stq1_zero_placement_is_the_best_zero_for_the_group():
+    """Given d, zeroing the lane of least incremental cost is the zero choice of least
+    weighted group error sum_j w_j (x_j - d q_j)^2 (q = sign(x) on kept lanes): brute force
+    over the four choices."""
+    g = np.random.default_rng(33)
+    x = g.standard_normal(2 * 256) * 0.03
+    w = np.exp(g.standard_normal(256))
+    xb, wb = O._stq_blocks(x, 256, w)
+    d = np.array([0.02, 0.05])
+    z = O.stq1_zero_placement(xb, wb, d)
+    for b in range(2):
+        for grp in range(64):
+            errs = []
+            for zz in range(4):
+                q = np.sign(xb[b, grp])
+                q[zz] = 0
+                errs.append((wb[b, grp] * (xb[b, grp] - d[b] * q) ** 2).sum())
+            assert z[b, grp] == int(np.argmin(errs))
+
+
+def test_stq1_wls_alternation_never_increases_error_and_beats_upstream():
+    """Each half-step of the alternation minimises the weighted error over its own variable,
+    so the error never rises from round to round, and the result is never worse than the
+    upstream encoder's (whose selection the first LS step starts from)."""
+    g = np.random.default_rng(34)
+    K = 512
+    # heavy-tailed rows (Student t, 3 degrees of freedom) make amax a poor scale
+    x = g.standard_t(3, 16 * 256) * 0.02
+    w = np.exp(g.standard_normal(K))
+    xb, wb = O._stq_blocks(x, K, w)
+
+    def err(z, d):
+        q = np.sign(xb) + (xb == 0)
+        q[np.arange(4)[None, None, :] == z[:, :, None]] = 0
+        return (wb * (xb - d[:, None, None] * q) ** 2).sum(axis=(1, 2))
+
+    z = np.argmin(np.abs(xb), axis=2)
+    e_up = err(z, np.abs(xb).max(axis=(1, 2)))
+    prev = e_up
+    for _ in range(O.STQ_ENC_ROUNDS):
+        d = O.stq1_ls_scale(xb, wb, z)
+        e1 = err(z, d)
+        z = O.stq1_zero_placement(xb, wb, d)
+        e2 = err(z, d)
+        assert (e1 <= prev * (1 + 1e-12)).all() and (e2 <= e1 * (1 + 1e-12)).all()
+        prev = e2
+    # the oracle's encoder is this sequence plus a final LS fit
+    zf, _, df = O.stq1_encode_parts(x, K, w, "wls")
+    assert (err(zf.reshape(-1, 64), df) <= prev * (1 + 1e-12)).all()
+    assert (err(zf.reshape(-1, 64), df) < e_up).all()
+    # and after fp16 rounding of d the packed encodings keep the order on these rows
+    cu, su = O.stq1_encode(x, K, w, "upstream")
+    cw, sw = O.stq1_encode(x, K, w, "wls")
+    assert O.stq1_weighted_ssd(x, K, cw, sw, w).sum() < 0.5 * O.stq1_weighted_ssd(x, K, cu, su, w).sum()
+
+
+def test_stq1_encode_signs_ties_and_zero_blocks():
+    """Kept lanes carry sign(x) (0 counts as positive), the first lane wins a tie for the
+    zero, and an all-zero block encodes d = 0."""
+    x = np.zeros(256)
+    x[:4] = [0.5, -0.5, 0.25, -0.25]           # tie |x| between lanes 2 and 3: lane 2 zeroed
+    x[4:8] = [0.0, 0.0, 1.0, -1.0]             # tie at 0 between lanes 0 and 1: lane 0 zeroed
+    z, s, d = O.stq1_encode_parts(x, 256, method="upstream")
+    assert z[0] == 2 and s[0] == 0b110         # kept lanes 0, 1, 3: +, -, - (bit i: i-th kept lane)
+    assert z[1] == 0 and s[1] == 0b100         # kept lanes 1, 2, 3: +0 -> +, +, -
+    assert d[0] == 1.0
+    codes, scales = O.stq1_encode(np.zeros(512), 256)
+    assert (scales == 0).all() and (O.stq1_decode(codes, scales) == 0).all()
