@@ -18,7 +18,7 @@ __all__ = [
     "moe_route", "moe_permute", "moe_workspace_size", "moe_workspace_offsets", "moe_expert_ffn",
     "moe_combine", "moe_stq1_pack", "moe_stq1_dequant", "moe_mxfp4_dequant", "moe_mx_quant_act",
     "moe_rmsnorm_bf16", "moe_layer_decode_workspace_size", "moe_layer_decode_workspace_offsets",
-    "moe_layer_decode",
+    "moe_layer_decode", "moe_stq1_encode", "MOE_STQ1_ENC_UPSTREAM", "MOE_STQ1_ENC_WLS",
     "moe_profile_enable", "moe_profile_read", "PROFILE_SLOTS",
 ]
 
@@ -73,6 +73,7 @@ _SIGS = {
     "moe_rmsnorm_bf16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
     "moe_layer_decode_workspace_size": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "moe_layer_decode_workspace_offsets": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "moe_stq1_encode": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "moe_layer_decode": (ctypes.c_int, [_P, _P, _P] + [_P] * 15 + [ctypes.c_size_t, _P]),
     "moe_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
     "moe_profile_read": (ctypes.c_int, [_P, _P]),
@@ -230,6 +231,15 @@ def moe_mx_quant_act(rows, K, x_bf16, x_f32, q, s, stream=None):
 
 def moe_rmsnorm_bf16(T, H, eps, r, a, stream=None):
     _check(lib().moe_rmsnorm_bf16(int(T), int(H), float(eps), _ptr(r), _ptr(a), _stream(stream)))
+
+
+MOE_STQ1_ENC_UPSTREAM, MOE_STQ1_ENC_WLS = 0, 1
+
+
+def moe_stq1_encode(x_f32, imatrix_f32, n_weights: int, K: int, method: int, codes, scales, stream=None):
+    """Encode a float32 matrix (flattened [N][K]) into STQ1_0 codes / fp16 scale bits."""
+    _check(lib().moe_stq1_encode(_ptr(x_f32), _ptr(imatrix_f32), n_weights, K, method, _ptr(codes),
+                                 _ptr(scales), _stream(stream)))
 
 
 def moe_layer_decode_workspace_offsets(d: Dims, has_shared: bool) -> list:

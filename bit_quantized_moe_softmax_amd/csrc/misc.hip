@@ -156,6 +156,84 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(int64_t n8, const uint16_
   }
 }
 
+// STQ1_0 encoders ("Hy4-preview-GGUF" (AngelSlim), section 3, Our encoder), one wave per
+// 256-weight block of the flattened matrix, lane l = group l (weights 4l .. 4l+3).  Importance
+// w of a weight: imatrix[flat index mod K], or 1.
+//   method 0 (upstream): d = the block's largest magnitude; zero at the smallest |x| of each
+//     group (the first lane on ties).
+//   method 1 (weighted least squares): from the upstream zero placement, 3 rounds of
+//     d = sum(w |x|) / sum(w) over the kept lanes (the LS scale with sel = sign(x)), then in
+//     every group the zero at the smallest incremental cost w d (2 |x| - d) (= w (x^2 -
+//     (|x| - d)^2)), and a final LS fit; a block whose kept lanes have no weight keeps
+//     d = amax.
+// Kept lanes take the sign of x (x = 0 counts as positive); d is rounded to fp16 (nearest
+// even) once.  Sums are wave reductions in a fixed order.
+__device__ __forceinline__ int argmin4(const float* c) {
+  int z = 0;
+  float m = c[0];
+#pragma unroll
+  for (int j = 1; j < 4; ++j)
+    if (c[j] < m) { m = c[j]; z = j; }
+  return z;
+}
+
+__global__ __launch_bounds__(256) void stq1_encode_kernel(const float* __restrict__ x,
+                                                          const float* __restrict__ imatrix,
+                                                          int64_t n_blocks, int K, int method,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= n_blocks) return;   // whole waves
+  const int64_t f0 = b * 256 + 4 * lane;
+  const float4 xv = *reinterpret_cast<const float4*>(x + f0);
+  const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+  float ax[4], w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ax[j] = fabsf(xs[j]);
+    w[j] = imatrix ? imatrix[(f0 + j) % K] : 1.0f;
+  }
+  float amax = fmaxf(fmaxf(ax[0], ax[1]), fmaxf(ax[2], ax[3]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  int z = argmin4(ax);
+  float d = amax;
+  if (method == 1) {
+    auto ls = [&]() {
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j != z) { num = fmaf(w[j], ax[j], num); den += w[j]; }
+      num = wave_sum(num);
+      den = wave_sum(den);
+      return den > 0.f ? num / den : amax;
+    };
+    for (int r = 0; r < 3; ++r) {
+      d = ls();
+      float c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = w[j] * d * (2.0f * ax[j] - d);
+      z = argmin4(c);
+    }
+    d = ls();
+  }
+  uint32_t sg = 0;
+  int i = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j != z) { sg |= (xs[j] < 0.f ? 1u : 0u) << i; ++i; }
+  const uint32_t p = ((uint32_t)z << 3) | sg;
+  const uint32_t pn = (uint32_t)__shfl_down((int)p, 1, 64);
+  uint8_t* cb = codes + b * 40;
+  if ((lane & 1) == 0) cb[lane >> 1] = (uint8_t)((p & 15u) | ((pn & 15u) << 4));
+  const uint64_t hi = __ballot((p >> 4) & 1u);
+  if (lane == 0) {
+    reinterpret_cast<uint2*>(cb + 32)[0] = make_uint2((uint32_t)hi, (uint32_t)(hi >> 32));
+    scales[b] = __builtin_bit_cast(uint16_t, (_Float16)d);
+  }
+}
+
 }  // namespace
 
 hipError_t moe_launch_combine(const float* y_pairs, const float* w, const int32_t* pair_pos,
@@ -203,5 +281,14 @@ hipError_t moe_launch_mx_quant(int64_t rows, int K, const uint16_t* xb, const fl
   if ((n8 + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, n8,
                      xb, xf, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_stq1_encode(const float* x, const float* imatrix, int64_t n_blocks, int K,
+                                  int method, uint8_t* codes, uint16_t* scales, hipStream_t s) {
+  if (n_blocks == 0) return hipSuccess;
+  if ((n_blocks + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stq1_encode_kernel, dim3((unsigned)((n_blocks + 3) / 4)), dim3(256), 0, s, x,
+                     imatrix, n_blocks, K, method, codes, scales);
   return hipGetLastError();
 }

@@ -532,6 +532,19 @@ moe_status moe_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales, int
   return finish(moe_launch_mxfp4_pack_tiles(codes, scales, rows, K, tcodes, tscales, s), s);
 }
 
+moe_status moe_stq1_encode(const float* x, const float* imatrix, int64_t n_weights, int32_t K,
+                           int32_t method, uint8_t* codes, uint16_t* scales, void* stream) {
+  if (n_weights < 0 || n_weights % 256 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (method != MOE_STQ1_ENC_UPSTREAM && method != MOE_STQ1_ENC_WLS) return MOE_ERR_INVALID_ARG;
+  if (n_weights == 0) return MOE_OK;
+  if (!x || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(codes) % 8 ||
+      reinterpret_cast<uintptr_t>(scales) % 2)
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = as_stream(stream);
+  return finish(moe_launch_stq1_encode(x, imatrix, n_weights / 256, K, method, codes, scales, s), s);
+}
+
 moe_status moe_mx_quant_act(int64_t rows, int32_t K, const uint16_t* x_bf16, const float* x_f32,
                             uint8_t* q, uint8_t* sc, void* stream) {
   if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;

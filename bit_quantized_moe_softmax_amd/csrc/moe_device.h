@@ -185,6 +185,8 @@ hipError_t moe_launch_rmsnorm(const float* r, uint16_t* a, int T, int H, float e
 hipError_t moe_launch_stq1_pack(const uint8_t* z, const uint8_t* sg, const uint16_t* d,
                                 int64_t n_blocks, uint8_t* codes, uint16_t* scales,
                                 hipStream_t s);
+hipError_t moe_launch_stq1_encode(const float* x, const float* imatrix, int64_t n_blocks, int K,
+                                  int method, uint8_t* codes, uint16_t* scales, hipStream_t s);
 hipError_t moe_launch_stq1_dequant(const uint8_t* codes, const uint16_t* scales,
                                    int64_t n_blocks, float* out, hipStream_t s);
 hipError_t moe_launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows,

@@ -278,6 +278,27 @@ MOE_MI355X_API moe_status moe_stq1_pack(const uint8_t* zpos, const uint8_t* sign
                                         const uint16_t* d_f16, int64_t n_blocks,
                                         uint8_t* codes, uint16_t* scales, void* stream);
 
+/* STQ1_0 encoders ("Hy4-preview-GGUF" (AngelSlim), section 3, Our encoder): a float
+ * matrix (flattened row-major [N][K], n_weights % 256 == 0) -> STQ1_0 blocks of 256
+ * consecutive weights.  Importance of a weight: imatrix[flat index mod K] (K > 0), or 1
+ * when imatrix is NULL.
+ *   MOE_STQ1_ENC_UPSTREAM: d = the block's largest magnitude; in each group of four the
+ *     lane of smallest |x| is zeroed (first lane on ties).
+ *   MOE_STQ1_ENC_WLS: from that zero placement, 3 rounds of (the weighted least-squares
+ *     scale d = sum(w sel x) / sum(w sel^2), then in each group the zero at the lane of
+ *     smallest incremental cost w (x^2 - (|x| - d)^2)), and a final least-squares fit of d
+ *     (d = amax when the kept lanes carry no weight).
+ * Kept lanes take the sign of x (0 counts as positive); d is rounded to fp16 once.
+ * Sums run in fp32 in a fixed order, so a zero placement at a near-tie of two lanes'
+ * costs may differ from an exact computation.
+ *   x [n_weights] fp32 (16-byte aligned); imatrix [K] fp32 (entries >= 0) or NULL;
+ *   codes [n_weights/256*40] out (8-byte aligned), scales [n_weights/256] fp16 out.
+ * A one-time weight preparation, not a per-step call. */
+enum { MOE_STQ1_ENC_UPSTREAM = 0, MOE_STQ1_ENC_WLS = 1 };
+MOE_MI355X_API moe_status moe_stq1_encode(const float* x, const float* imatrix, int64_t n_weights,
+                                          int32_t K, int32_t method, uint8_t* codes,
+                                          uint16_t* scales, void* stream);
+
 /* Decode STQ1_0 blocks to fp32 weights out [n_blocks*256] (exact). */
 MOE_MI355X_API moe_status moe_stq1_dequant(const uint8_t* codes, const uint16_t* scales,
                                            int64_t n_blocks, float* out, void* stream);

@@ -865,3 +865,82 @@ def test_chain_cfg4_hy4_29_layers_sampled():
         assert err.max() <= TOL
         r, r_next = r_next, r
     say("chain: worst", worst, "near-tie token-layers", n_tie, "bf16 norm flips", n_flip_a)
+
+
+# ----------------------------------------------------------------------------- STQ1_0 encoders
+def _encode_gpu(x, K, imat, method):
+    n = x.size
+    c = torch.empty(n // 256 * 40, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(n // 256, dtype=torch.int16, device="cuda")
+    M.moe_stq1_encode(dev(np.ascontiguousarray(x, dtype=np.float32)),
+                      None if imat is None else dev(np.ascontiguousarray(imat, dtype=np.float32)),
+                      n, K, method, c, sc)
+    torch.cuda.synchronize()
+    return host(c), host(sc).view(np.uint16)
+
+
+def _encode_inputs():
+    g = np.random.default_rng(51)
+    ties = (g.integers(-3, 4, 64 * 512) * 0.01).astype(np.float32)   # many equal |x| and zeros
+    ties[::7] = -0.0
+    return {
+        "normal-n48-k512": (g.standard_normal(48 * 512).astype(np.float32) * 0.02, 512),
+        "straddle-n64-k128": (g.standard_normal(64 * 128).astype(np.float32) * 0.02, 128),
+        "ties-n64-k512": (ties, 512),
+        "student3-n512-k6144": (g.standard_t(3, 512 * 6144).astype(np.float32) * 0.02, 6144),
+    }
+
+
+@pytest.mark.parametrize("name", ["normal-n48-k512", "straddle-n64-k128", "ties-n64-k512", "student3-n512-k6144"])
+def test_stq1_encode_upstream_bitexact(name):
+    """Upstream STQ1_0 encoder (block amax, zero at the smallest |x|): codes and scales equal
+    the oracle's bit for bit (max and comparisons are exact in any order)."""
+    x, K = _encode_inputs()[name]
+    say("stq1 encode upstream", name)
+    gc, gs = _encode_gpu(x, K, None, M.MOE_STQ1_ENC_UPSTREAM)
+    oc, osc = O.stq1_encode(x.astype(np.float64), K, method="upstream")
+    assert (gc == oc).all() and (gs == osc).all()
+
+
+@pytest.mark.parametrize("imat", [False, True], ids=["no-imatrix", "imatrix"])
+@pytest.mark.parametrize("name", ["normal-n48-k512", "straddle-n64-k128", "student3-n512-k6144"])
+def test_stq1_encode_wls_matches_oracle(name, imat):
+    """Weighted least-squares STQ1_0 encoder: the GPU sums in fp32, the oracle in float64.
+    Blocks whose zero placement matches take d within one fp16 step; a block may place a zero
+    differently only at a near-tie, so such blocks are rare and their weighted error equals
+    the oracle's to 1e-3."""
+    x, K = _encode_inputs()[name]
+    w = np.exp(np.random.default_rng(52).standard_normal(K)).astype(np.float32) if imat else None
+    say("stq1 encode wls", name, "imatrix" if imat else "")
+    gc, gs = _encode_gpu(x, K, w, M.MOE_STQ1_ENC_WLS)
+    xd = x.astype(np.float64)
+    wd = None if w is None else w.astype(np.float64)
+    oc, osc = O.stq1_encode(xd, K, imatrix=wd, method="wls")
+    same = (O.stq1_patterns_of(gc) == O.stq1_patterns_of(oc)).all(axis=1)
+    step = np.abs(gs.astype(np.int64) - osc.astype(np.int64))
+    eg = O.stq1_weighted_ssd(xd, K, gc, gs, wd)
+    eo = O.stq1_weighted_ssd(xd, K, oc, osc, wd)
+    say("blocks", same.size, "with another zero placement", int((~same).sum()),
+        "max fp16 step on matching blocks", int(step[same].max()) if same.any() else None)
+    assert (step[same] <= 1).all()
+    assert (~same).mean() <= 0.02
+    assert (np.abs(eg - eo) <= 1e-3 * eo).all()
+    # and the encoder does what it is for: far less weighted error than the upstream one
+    uc, us = O.stq1_encode(xd, K, method="upstream")
+    assert eg.sum() < 0.5 * O.stq1_weighted_ssd(xd, K, uc, us, wd).sum()
+
+
+def test_stq1_encode_grid_inputs_exact():
+    """Weights already on the ternary grid come back exactly from both GPU encoders."""
+    g = np.random.default_rng(53)
+    n_blk = 64
+    z = g.integers(0, 4, n_blk * 64)
+    s = g.integers(0, 8, n_blk * 64)
+    d = np.abs(g.standard_normal(n_blk) * 0.02).astype(np.float16)
+    d[d == 0] = np.float16(0.01)
+    lanes = np.array([O.stq1_pattern(int(p)) for p in (8 * z + s)], dtype=np.float64)
+    x = (lanes.reshape(n_blk, 256) * d.astype(np.float64)[:, None]).reshape(-1).astype(np.float32)
+    want = O.stq1_pack(z, s, d.view(np.uint16))
+    for method in (M.MOE_STQ1_ENC_UPSTREAM, M.MOE_STQ1_ENC_WLS):
+        gc, gs = _encode_gpu(x, 1024, np.exp(g.standard_normal(1024)), method)
+        assert (gc == want[0]).all() and (gs == want[1]).all()
