@@ -347,8 +347,8 @@ def mx_decode_bench(args):
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     "decode_k1_route": "k1s_router<", "decode_k2_gateup": "k2s_gateup<",
     "decode_k3_down_combine": "k3_down_combine<", "mx_gateup": "mx_gemm_kernel<true, true>",
-    "mx_down": "mx_gemm_kernel<false, true>", "stq_gateup": "g16_kernel<0, true>",
-    "stq_down": "g16_kernel<0, false>", "mxdec_k2_gateup": "k2s_gateup_mx<",
+    "mx_down": "mx_gemm_kernel<false, true>", "stq_gateup": "g16_kernel<0, true, 1>",
+    "stq_down": "g16_kernel<0, false, 2>", "mxdec_k2_gateup": "k2s_gateup_mx<",
     "mxdec_k3_down_combine": "k3_down_combine_mx<", "copy": "neg_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hy4_layer_hbm_traffic_per_kernel.md")
 _DEC_SRC = "bit_quantized_moe_softmax_amd/csrc/decode_fused.hip"

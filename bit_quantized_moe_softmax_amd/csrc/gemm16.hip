@@ -23,7 +23,7 @@
 // blocks of at most 128 rows; a job is (M block, N tile of 256 weight rows: 128 gate + the
 // 128 up rows of the same h-columns, or 256 output columns); jobs are numbered expert-major,
 // then N tile, then M block, each XCD takes one contiguous range, and one workgroup per CU
-// walks it.  Four waves share the M block's activation rows, staged per K step (64) in LDS
+// walks it (two for the down projections).  Four waves share the M block's activation rows, staged per K step (64) in LDS
 // (double-buffered); each wave owns 64 weight rows whose codes it loads from HBM into
 // registers, so weights never pass through LDS.
 //
@@ -47,8 +47,12 @@ constexpr int kNWave = 64;      // weight rows per wave
 constexpr int kNTile = 4 * kNWave;
 constexpr int kBK = 64;         // K (16-bit elements) per step
 constexpr int kAStride = 144;   // bytes per A row in LDS (128 + 16 pad)
-constexpr int kRing = 4;        // A: K steps of loads in flight
 constexpr int kRingB = 2;       // bf16 B: K steps of loads in flight
+// Workgroups per CU (WGS): with full M blocks the down GEMMs run two per CU in 256
+// registers per lane (one wave's LDS reads and barrier overlap another's MFMAs: -20 % time
+// at 4096 tokens); with blocks of a few rows they run one, with deeper load rings (two were
+// 55 % slower at 64 tokens).  The gate/up GEMMs need more registers (the SiLU epilogue, two
+// weight families) and always run one.
 
 enum { kSTQ = 0, kBF16 = 1 };
 
@@ -93,8 +97,10 @@ struct StqRaw {
   uint32_t qs0, qs1, qh, d;
 };
 
-template <int WF, bool GATEUP>
-__global__ __launch_bounds__(256, 1) void g16_kernel(G16Args p) {
+template <int WF, bool GATEUP, int WGS>
+__global__ __launch_bounds__(256, WGS) void g16_kernel(G16Args p) {
+  // A: K steps of loads in flight (fewer registers at two workgroups per CU)
+  constexpr int kRing = WGS == 1 ? 4 : 2;
   __shared__ __align__(16) uint8_t s_a[2][kMB * kAStride];
   __shared__ int s_arow[kMB];
   __shared__ int s_aexp[kMB];
@@ -193,12 +199,13 @@ __global__ __launch_bounds__(256, 1) void g16_kernel(G16Args p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool hi = GATEUP && q >= 2;
+      // the tile's row offset is wave-uniform: it goes in the scalar offset
       const uint32_t ro = qrow(q) * rstride;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(hi ? rw1 : rw0, boff + ro, 40 * b, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(hi ? rw1 : rw0, boff, ro + 40 * b, 0);
       r[q].qs0 = v[0];
       r[q].qs1 = v[1];
-      r[q].qh = __builtin_amdgcn_raw_buffer_load_b16(hi ? rw1 : rw0, bhoff + ro, 40 * b, 0);
-      r[q].d = __builtin_amdgcn_raw_buffer_load_b16(hi ? rd1 : rd0, bdoff + qrow(q) * nblk * 2, 2 * b, 0);
+      r[q].qh = __builtin_amdgcn_raw_buffer_load_b16(hi ? rw1 : rw0, bhoff, ro + 40 * b, 0);
+      r[q].d = __builtin_amdgcn_raw_buffer_load_b16(hi ? rd1 : rd0, bdoff, qrow(q) * nblk * 2 + 2 * b, 0);
     }
   };
   // B operand of tile q at K step j (0..3 within the block), sub-step t
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void g16_kernel(G16Args p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const bool hi = GATEUP && q >= 2;
-        rb[sl][t][q] = bload16(hi ? rw1 : rw0, boff + qrow(q) * rstride, 128 * ws + 64 * t);
+        rb[sl][t][q] = bload16(hi ? rw1 : rw0, boff, qrow(q) * rstride + 128 * ws + 64 * t);
       }
   };
 
@@ -237,7 +244,13 @@ __global__ __launch_bounds__(256, 1) void g16_kernel(G16Args p) {
     for (int q = 0; q < 4; ++q) acc[i][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const int mtiles = (nrows + 15) >> 4;
 
-  // MFMAs of one K step from LDS buffer `buf`: B operands from `bq(t, q)`
+  // MFMAs of one K step from LDS buffer `buf`: B operands from `bq(t, q)`.  A full M block
+  // runs straight-line code that issues four A fragment reads before their MFMAs; a partial
+  // one skips the tiles past its last row, reading each fragment just before its MFMAs.  The
+  // two are separate copies of the whole K loop (chosen once per job), so each keeps its own
+  // register pressure.
+  auto main_loop = [&](auto full_c) {
+  constexpr bool full = decltype(full_c)::value;
   auto compute = [&](int buf, auto&& bq) {
     const uint8_t* sa = s_a[buf];
 #pragma unroll
@@ -246,12 +259,26 @@ __global__ __launch_bounds__(256, 1) void g16_kernel(G16Args p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) bop[q] = bq(t, q);
       const int chunk = F16 ? 2 * g + t : 4 * t + g;
+      if constexpr (full) {
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        if (mt < mtiles) {
-          const uint4 av = *reinterpret_cast<const uint4*>(&sa[(16 * mt + c16) * kAStride + 16 * chunk]);
+        for (int hh = 0; hh < 2; ++hh) {
+          uint4 av[kMT / 2];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[mt][q] = mfma16(av, bop[q], acc[mt][q], F16);
+          for (int i = 0; i < kMT / 2; ++i)
+            av[i] = *reinterpret_cast<const uint4*>(&sa[(16 * (4 * hh + i) + c16) * kAStride + 16 * chunk]);
+#pragma unroll
+          for (int i = 0; i < kMT / 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[4 * hh + i][q] = mfma16(av[i], bop[q], acc[4 * hh + i][q], F16);
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          if (mt < mtiles) {
+            const uint4 av = *reinterpret_cast<const uint4*>(&sa[(16 * mt + c16) * kAStride + 16 * chunk]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[mt][q] = mfma16(av, bop[q], acc[mt][q], F16);
+          }
         }
       }
     }
@@ -300,6 +327,12 @@ __global__ __launch_bounds__(256, 1) void g16_kernel(G16Args p) {
     step(s + 2, std::integral_constant<int, 2>{});
     step(s + 3, std::integral_constant<int, 3>{});
   }
+  };   // main_loop
+  // the shared expert's blocks split all tokens evenly (full at 128-token multiples): its
+  // kernels keep only the straight-line loop
+  if constexpr (!F16) main_loop(std::true_type{});
+  else if (mtiles == kMT) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
 
   if (wvalid) {
     // D element (4 (lane / 16) + i, lane % 16) of each 16x16 tile is acc[..][..][i]
@@ -379,24 +412,33 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict
   }
 }
 
-inline unsigned grid_for(const G16Args& a, int NT) {
+inline unsigned grid_for(const G16Args& a, int NT, int per_cu) {
   const int E = a.offsets ? a.E : 1;
   const long slots = (a.P < E ? a.P : E) + (a.P + kMB - 1) / kMB;
   const long work = slots * NT;
   const long most = kXcd * ((work + kXcd - 1) / kXcd);
-  const long per = kXcd * ((moe_cu_count() + kXcd - 1) / kXcd);
+  const long per = per_cu * kXcd * ((moe_cu_count() + kXcd - 1) / kXcd);
   return (unsigned)(most < per ? most : per);
 }
 
 template <int WF, bool GATEUP>
 hipError_t launch(const G16Args& a, hipStream_t s) {
+  // two workgroups per CU where the pairs fill most M blocks (64 or more per expert)
+  const int E = a.offsets ? a.E : 1;
+  const bool two = !GATEUP && (long)a.P >= 64L * E;
   if (GATEUP ? a.N % (kNTile / 2) : a.N % 16) return hipErrorInvalidValue;
   if (a.K % (WF == kSTQ ? 256 : 4 * kBK) || a.Ka % (4 * kBK)) return hipErrorInvalidValue;
   if ((size_t)a.rows_a * a.Ka * 2 >= 0x80000000ull) return hipErrorInvalidValue;
   if ((size_t)a.N * a.K * 2 >= 0x80000000ull) return hipErrorInvalidValue;
   if (a.P == 0) return hipSuccess;
   const int NT = GATEUP ? a.N / (kNTile / 2) : (a.N + kNTile - 1) / kNTile;
-  hipLaunchKernelGGL((g16_kernel<WF, GATEUP>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+  if constexpr (!GATEUP) {
+    if (two) {
+      hipLaunchKernelGGL((g16_kernel<WF, false, 2>), dim3(grid_for(a, NT, 2)), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((g16_kernel<WF, GATEUP, 1>), dim3(grid_for(a, NT, 1)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
