@@ -450,6 +450,17 @@ def shared_expert(x_bits, wg_bits, wu_bits, wd_bits):
     return y
 
 
+def shared_expert_mxfp8(x_bits, wg, wu, wd):
+    """The shared expert in MXFP8 W8A8 group 32 ("Hy4-preview-SF-WFP4AFP8", Quant Diff
+    table: mlp.shared_experts.{gate,up,down}_proj MXFP8 W8A8 g32): E4M3 weights with UE8M0
+    scales per 32 along the input axis, x MX-quantised to E4M3 along H and h along I (the
+    same rule as the routed experts' activations).  wg, wu, wd are (codes, scale bytes)."""
+    a = mx_dequantize_e4m3(*mx_quantize_e4m3(bf16_to_f64(x_bits)))
+    W = [mx_dequantize_e4m3(c, sc) for c, sc in (wg, wu, wd)]
+    _, y = swiglu_expert(a, W[0], W[1], W[2], mx_h=True)
+    return y
+
+
 def combine(y_pairs, w, pair_pos, y_shared=None, residual=None):
     """out[t] = y_shared[t] + sum_j w[t, j] * y_pairs[pair_pos[t*k + j]] (+ residual).
 
@@ -473,14 +484,16 @@ def rmsnorm_bf16(r, eps: float = 1e-6):
 
 
 def moe_layer(x_bits, k, get_w, fmt, wr_bits=None, bias=None, logits_in=None,
-              shared=None, residual=None):
-    """Whole layer: route -> permute -> routed experts (+ shared) -> combine.
-    Returns a dict of every stage."""
+              shared=None, residual=None, shared_fmt: str = "bf16"):
+    """Whole layer: route -> permute -> routed experts (+ shared, bf16 or MXFP8) ->
+    combine.  Returns a dict of every stage."""
     logits, ids, w = route(k, x_bits, wr_bits, bias, logits_in)
     E = logits.shape[1]
     sp, off, pp = permute(ids, E)
     y_pairs, h = expert_ffn(x_bits, ids, sp, off, get_w, fmt)
-    y_sh = shared_expert(x_bits, *shared) if shared is not None else None
+    y_sh = None
+    if shared is not None:
+        y_sh = shared_expert(x_bits, *shared) if shared_fmt == "bf16" else shared_expert_mxfp8(x_bits, *shared)
     out = combine(y_pairs, w, pp, y_sh, residual)
     return dict(logits=logits, ids=ids, w=w, sorted_pair=sp, offsets=off, pair_pos=pp,
                 y_pairs=y_pairs, h=h, y_shared=y_sh, out=out)

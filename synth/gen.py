@@ -36,7 +36,8 @@ __all__ = [
     "fp16_abs_normal", "stq1_codes_bytes", "stq1_matrix", "stq1_family",
     "stq1_pattern_fields", "mxfp4_matrix", "mxfp4_family", "zipf_bias",
     "prefill_logits", "activations", "router_weights", "shared_weights",
-    "sample_tokens", "STQ_BLOCK", "STQ_CODE_BYTES", "MAT_GATE", "MAT_UP", "MAT_DOWN",
+    "sample_tokens", "mxfp8_matrix", "shared_weights_mxfp8",
+    "STQ_BLOCK", "STQ_CODE_BYTES", "MAT_GATE", "MAT_UP", "MAT_DOWN",
 ]
 
 STQ_BLOCK = 256          # weights per STQ1_0 block
@@ -48,6 +49,7 @@ _T_X, _T_ROUTER, _T_RANK, _T_LOGITS = 1, 2, 3, 4
 _T_STQ_CODES, _T_STQ_SCALES, _T_STQ_Z, _T_STQ_S = 10, 11, 12, 13
 _T_MX_CODES, _T_MX_SCALES = 20, 21
 _T_SHARED, _T_SAMPLE = 30, 40
+_T_SH8_CODES, _T_SH8_SCALES = 31, 32
 
 
 @dataclass(frozen=True)
@@ -209,6 +211,24 @@ def shared_weights(seed: int, layer: int, I: int, H: int):
     return (bf16_normal(seed, (_T_SHARED, layer, MAT_GATE), (I, H), 0.02),
             bf16_normal(seed, (_T_SHARED, layer, MAT_UP), (I, H), 0.02),
             bf16_normal(seed, (_T_SHARED, layer, MAT_DOWN), (H, I), 0.02))
+
+
+def mxfp8_matrix(seed: int, layer: int, mat: int, N: int, K: int):
+    """MXFP8 weights of the shared expert: E4M3 code bytes [N, K] uniform over the 254
+    finite codes, UE8M0 scale bytes [N, K/32] in 113..116 (|w| up to about 0.05)."""
+    assert K % 32 == 0
+    g = rng(seed, _T_SH8_CODES, layer, mat)
+    codes = g.integers(0, 254, (N, K), dtype=np.int16)
+    codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)   # skip 0x7F and 0xFF (NaN)
+    scales = (127 + rng(seed, _T_SH8_SCALES, layer, mat).integers(-14, -10, (N, K // 32),
+                                                                   dtype=np.int16)).astype(np.uint8)
+    return codes, scales
+
+
+def shared_weights_mxfp8(seed: int, layer: int, I: int, H: int):
+    """MXFP8 (codes, scales) of the shared expert's gate [I, H], up [I, H], down [H, I]."""
+    return (mxfp8_matrix(seed, layer, MAT_GATE, I, H), mxfp8_matrix(seed, layer, MAT_UP, I, H),
+            mxfp8_matrix(seed, layer, MAT_DOWN, H, I))
 
 
 def sample_tokens(seed: int, T: int, n: int) -> np.ndarray:

@@ -512,3 +512,42 @@ def test_stq1_encode_signs_ties_and_zero_blocks():
     assert d[0] == 1.0
     codes, scales = O.stq1_encode(np.zeros(512), 256)
     assert (scales == 0).all() and (O.stq1_decode(codes, scales) == 0).all()
+
+
+# ----------------------------------------------------------------------------- MXFP8 shared expert
+def test_mxfp8_weight_decode_vs_torch():
+    """MXFP8 weights ("Hy4-preview-SF-WFP4AFP8", Quant Diff table: shared experts MXFP8 W8A8
+    g32) decode as torch's float8_e4m3fn value times 2^(scale byte - 127), per 32 inputs."""
+    codes, scales = synth.mxfp8_matrix(5, 0, 0, 8, 64)
+    assert not ((codes == 0x7F) | (codes == 0xFF)).any()
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    ref = ref * np.exp2(scales.astype(np.float64) - 127).repeat(32, axis=1)
+    assert (O.mx_dequantize_e4m3(codes, scales) == ref).all()
+
+
+def test_mxfp8_shared_expert_is_the_swiglu_of_dequantised_operands():
+    """The W8A8 shared expert with x already on its MX grid (so quantising x changes nothing)
+    and weights decoding to small integers: gate and up are integer matmuls, checked through
+    a down projection that picks one h entry (unit weight on the grid) per output."""
+    g = np.random.default_rng(35)
+    T, H, I = 3, 64, 32
+    xv = g.integers(-7, 8, (T, H)).astype(np.float64)
+    xv[:, 0] = 7                                    # each group's max 7: scale 2^(2-8), exact
+    xv[:, 32] = 7
+    x_bits = O.f64_to_bf16_bits(xv)
+    # E4M3 codes of small integers at scale byte 127: values in {-3..3}
+    ints = g.integers(-3, 4, (I, H))
+    code_of = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44}
+    enc = np.vectorize(lambda v: code_of[abs(v)] | (0x80 if v < 0 else 0))
+    wg = (enc(ints).astype(np.uint8), np.full((I, H // 32), 127, np.uint8))
+    ints_u = g.integers(-3, 4, (I, H))
+    wu = (enc(ints_u).astype(np.uint8), np.full((I, H // 32), 127, np.uint8))
+    eye = np.zeros((I, I), dtype=np.int64)
+    eye[np.arange(I), np.arange(I)] = 1
+    wd = (enc(eye).astype(np.uint8), np.full((I, I // 32), 127, np.uint8))
+    y = O.shared_expert_mxfp8(x_bits, wg, wu, wd)[:, :I]
+    gate = (xv.astype(np.int64) @ ints.T).astype(np.float64)
+    up = (xv.astype(np.int64) @ ints_u.T).astype(np.float64)
+    h = gate / (1 + np.exp(-gate)) * up
+    hq = O.mx_dequantize_e4m3(*O.mx_quantize_e4m3(h))
+    assert np.array_equal(y, hq)
