@@ -230,8 +230,19 @@ def prefill_bench(args):
     ev[1].record(stream)
     torch.cuda.synchronize()
     ws_ms = ev[0].elapsed_time(ev[1]) / args.prefill_steps
+    # and with the recipe's own shared-expert format: MXFP8 W8A8 group 32
+    sh8 = M.Experts(M.MOE_W_MXFP8, *[(dev(cd), dev(sc)) for cd, sc in
+                                     synth.shared_weights_mxfp8(c.seed, 0, c.I, c.H)])
+    M.moe_expert_ffn(d, R, sh8, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs, bufs.y_shared, bufs.ws, s)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.prefill_steps):
+        M.moe_expert_ffn(d, R, sh8, x, bufs.sorted_pair, bufs.offsets, bufs.y_pairs, bufs.y_shared, bufs.ws, s)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    w8_ms = ev[0].elapsed_time(ev[1]) / args.prefill_steps
     return dict(c=c, routed_ms=r_ms, flops=flops, tflops=flops / (r_ms * 1e-3) / 1e12, prof=prof,
-                with_shared_ms=ws_ms, shared_flops=2.0 * c.T * 3 * c.I * c.H)
+                with_shared_ms=ws_ms, with_mxfp8_shared_ms=w8_ms, shared_flops=2.0 * c.T * 3 * c.I * c.H)
 
 
 def stq_prefill_bench(args):
@@ -555,6 +566,10 @@ def main():
                 "shared_tflops_bf16": round(pre["shared_flops"] / (sh_ms * 1e-3) / 1e12, 1) if sh_ms > 0 else None,
                 "kernels": {n: round(pre["prof"][n][0], 2) for n in ("shared_gateup", "shared_down", "act_prep")
                             if pre["prof"][n][1]}}
+            s8_ms = pre["with_mxfp8_shared_ms"] - pre["routed_ms"]
+            out["prefill"]["with_mxfp8_shared_expert"] = {
+                "layer_ms": round(pre["with_mxfp8_shared_ms"], 4), "shared_ms": round(s8_ms, 4),
+                "note": "the WFP4AFP8 recipe's formats: MXFP4 routed experts, MXFP8 W8A8 shared expert"}
         except Exception as e:  # the decode line must still print
             out["prefill"] = {"error": repr(e)}
     if not args.no_extra:

@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "MoeError", "lib", "Dims", "Experts", "MOE_W_STQ1_0", "MOE_W_MXFP4", "MOE_W_BF16",
-    "MOE_W_MXFP4_TILED", "moe_mxfp4_pack_tiles",
+    "MOE_W_MXFP4_TILED", "MOE_W_MXFP8", "moe_mxfp4_pack_tiles",
     "COUNTER_NAMES", "moe_status_str", "moe_version", "moe_get_counters", "moe_reset_counters",
     "moe_route", "moe_permute", "moe_workspace_size", "moe_workspace_offsets", "moe_expert_ffn",
     "moe_combine", "moe_stq1_pack", "moe_stq1_dequant", "moe_mxfp4_dequant", "moe_mx_quant_act",
@@ -26,11 +26,11 @@ PROFILE_SLOTS = ["decode_k1_route", "decode_k2_gateup",
                  "decode_k3_down_combine", "reserved3", "mx_quant", "mx_gateup", "mx_down",
                  "stq_gateup", "stq_down", "shared_gateup", "shared_down", "act_prep"]
 
-MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16, MOE_W_MXFP4_TILED = 1, 2, 3, 4
+MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16, MOE_W_MXFP4_TILED, MOE_W_MXFP8 = 1, 2, 3, 4, 5
 COUNTER_NAMES = ["route_gemv", "route_topk", "permute", "stq_gateup_mfma", "stq_down_mfma",
                  "stq_generic", "mx_quant", "mx_gateup_mfma", "mx_down_mfma", "bf16_gateup",
                  "bf16_down", "combine", "rmsnorm", "dequant", "bf16_gemm", "decode_fused",
-                 "stq_gemm", "rowscale"]
+                 "stq_gemm", "rowscale", "mxfp8_shared"]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 

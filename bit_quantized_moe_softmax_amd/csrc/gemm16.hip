@@ -17,7 +17,11 @@
 // error of hi), taken as two K halves against the same weight columns: about 22
 // significant bits, where one fp16 term (11 bits) leaves output errors near 1e-3 of the row
 // RMS.  The bf16 shared expert runs on the bf16 MFMA: x as it is for gate/up, and h split
-// into bf16 hi + lo for the down projection, again as two K halves (16 bits of h).
+// into bf16 hi + lo for the down projection, again as two K halves (16 bits of h).  An
+// MXFP8 (W8A8 group 32) shared expert runs on the bf16 MFMA too: its E4M3 weights times
+// their UE8M0 scale are exact in bf16 (decoded in registers by the gfx950 scaled
+// conversion), and so are its activations, which are MX-quantised (x along H, h along I)
+// into the bf16 values of their E4M3 codes before the GEMMs.
 //
 // Work split (as in the MXFP4 prefill GEMMs): the pairs of one expert are cut evenly into M
 // blocks of at most 128 rows; a job is (M block, N tile of 256 weight rows: 128 gate + the
@@ -54,7 +58,7 @@ constexpr int kRingB = 2;       // bf16 B: K steps of loads in flight
 // 55 % slower at 64 tokens).  The gate/up GEMMs need more registers (the SiLU epilogue, two
 // weight families) and always run one.
 
-enum { kSTQ = 0, kBF16 = 1 };
+enum { kSTQ = 0, kBF16 = 1, kMX8 = 2 };
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
@@ -169,15 +173,22 @@ __global__ __launch_bounds__(256, WGS) void g16_kernel(G16Args p) {
     rd0 = make_rsrc(reinterpret_cast<const uint8_t*>(p.s0) + jb.e * es, (uint32_t)es);
     rw1 = GATEUP ? make_rsrc(static_cast<const uint8_t*>(p.w1) + jb.e * eb, (uint32_t)eb) : rw0;
     rd1 = GATEUP ? make_rsrc(reinterpret_cast<const uint8_t*>(p.s1) + jb.e * es, (uint32_t)es) : rd0;
-  } else {
+  } else if (WF == kBF16) {
     rw0 = make_rsrc(p.w0, (uint32_t)(mat * 2));
     rw1 = GATEUP ? make_rsrc(p.w1, (uint32_t)(mat * 2)) : rw0;
     rd0 = rd1 = rw0;
+  } else {   // MXFP8: E4M3 codes [N][K], UE8M0 scales [N][K/32] (one expert)
+    rw0 = make_rsrc(p.w0, (uint32_t)mat);
+    rw1 = GATEUP ? make_rsrc(p.w1, (uint32_t)mat) : rw0;
+    rd0 = make_rsrc(p.s0, (uint32_t)(mat / 32));
+    rd1 = GATEUP ? make_rsrc(p.s1, (uint32_t)(mat / 32)) : rd0;
   }
   // per-lane byte offsets of the lane's row in tile 0; tile q adds qrow(q) rows
   const uint32_t brow = trow + c16;
-  const uint32_t rstride = F16 ? (uint32_t)nblk * 40 : (uint32_t)K * 2;   // bytes per weight row
-  const uint32_t boff = F16 ? brow * rstride + 8 * g : brow * rstride + 16 * g;
+  const uint32_t rstride = F16 ? (uint32_t)nblk * 40 : WF == kBF16 ? (uint32_t)K * 2 : (uint32_t)K;
+  const uint32_t boff = F16 ? brow * rstride + 8 * g : WF == kBF16 ? brow * rstride + 16 * g
+                                                                    : brow * rstride + 8 * g;
+  const uint32_t bsoff = brow * (uint32_t)(K / 32);   // MXFP8 scale bytes
   const uint32_t bhoff = brow * rstride + 32 + 2 * g;
   const uint32_t bdoff = brow * (uint32_t)nblk * 2;
 
@@ -224,7 +235,8 @@ __global__ __launch_bounds__(256, WGS) void g16_kernel(G16Args p) {
     return o;
   };
 
-  // ---- B, bf16: register ring of kRingB steps, 2 sub-steps x 4 tiles per step
+  // ---- B, bf16 or MXFP8: register ring of kRingB steps, 2 sub-steps x 4 tiles per step
+  // (MXFP8: 8 code bytes and the scale byte of their 32-block per lane)
   uint4 rb[kRingB][2][4];
   auto load_bf = [&](int sl, int s) {
     const int ws = s % kw;   // weight K step (the two K halves of hi / lo share the weights)
@@ -233,8 +245,29 @@ __global__ __launch_bounds__(256, WGS) void g16_kernel(G16Args p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const bool hi = GATEUP && q >= 2;
-        rb[sl][t][q] = bload16(hi ? rw1 : rw0, boff, qrow(q) * rstride + 128 * ws + 64 * t);
+        if constexpr (WF == kBF16) {
+          rb[sl][t][q] = bload16(hi ? rw1 : rw0, boff, qrow(q) * rstride + 128 * ws + 64 * t);
+        } else {
+          const auto c = __builtin_amdgcn_raw_buffer_load_b64(hi ? rw1 : rw0, boff,
+                                                              qrow(q) * rstride + 64 * ws + 32 * t, 0);
+          const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(hi ? rd1 : rd0, bsoff,
+                                                                  qrow(q) * (K / 32) + 2 * ws + t, 0);
+          rb[sl][t][q] = make_uint4(c[0], c[1], sb, 0u);
+        }
       }
+  };
+  // B operand from the ring entry: bf16 as loaded, MXFP8 decoded (8 codes times the scale)
+  auto bf_b = [&](const uint4& r) -> uint4 {
+    if constexpr (WF == kBF16) {
+      return r;
+    } else {
+      const float sc = moe_ue8m0_scale(r.z);
+      return make_uint4(
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, true)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, true)));
+    }
   };
 
   f32x4_t acc[kMT][4];
@@ -301,7 +334,7 @@ __global__ __launch_bounds__(256, WGS) void g16_kernel(G16Args p) {
       }
     } else {
       constexpr int BS = SLOT % kRingB;
-      if (wvalid) compute(s & 1, [&](int t, int q) { return rb[BS][t][q]; });
+      if (wvalid) compute(s & 1, [&](int t, int q) { return bf_b(rb[BS][t][q]); });
       load_bf(BS, min(s + kRingB, nsteps - 1));
     }
     if (s + 1 < nsteps) store_a(A1, (s + 1) & 1);
@@ -448,6 +481,8 @@ hipError_t moe_launch_g16_stq_gateup(const G16Args& a, hipStream_t s) { return l
 hipError_t moe_launch_g16_stq_down(const G16Args& a, hipStream_t s) { return launch<kSTQ, false>(a, s); }
 hipError_t moe_launch_g16_bf16_gateup(const G16Args& a, hipStream_t s) { return launch<kBF16, true>(a, s); }
 hipError_t moe_launch_g16_bf16_down(const G16Args& a, hipStream_t s) { return launch<kBF16, false>(a, s); }
+hipError_t moe_launch_g16_mx8_gateup(const G16Args& a, hipStream_t s) { return launch<kMX8, true>(a, s); }
+hipError_t moe_launch_g16_mx8_down(const G16Args& a, hipStream_t s) { return launch<kMX8, false>(a, s); }
 
 hipError_t moe_launch_rowscale_f16(const uint16_t* in16, const float* in32, long rows, int C,
                                    int two, uint16_t* out, int32_t* sexp, hipStream_t s) {

@@ -156,6 +156,36 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(int64_t n8, const uint16_
   }
 }
 
+// The bf16 values of the MX E4M3 quantisation of rows (group 32 along K): the codes of
+// moe_mx_quant8, decoded times 2^X by the gfx950 scaled conversion (E4M3 with 3 mantissa
+// bits times a power of two is exact in bf16).  Eight elements per lane as mx_quant_kernel.
+__global__ __launch_bounds__(256) void mx_roundtrip_kernel(int64_t n8, const uint16_t* xb,
+                                                           const float* xf,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t j = i < n8 ? i : n8 - 1;
+  uint32_t bits[8];
+  if (xb) {
+    const uint4 v = reinterpret_cast<const uint4*>(xb)[j];
+    bits[0] = v.x << 16; bits[1] = v.x & 0xFFFF0000u; bits[2] = v.y << 16; bits[3] = v.y & 0xFFFF0000u;
+    bits[4] = v.z << 16; bits[5] = v.z & 0xFFFF0000u; bits[6] = v.w << 16; bits[7] = v.w & 0xFFFF0000u;
+  } else {
+    const uint4 v0 = reinterpret_cast<const uint4*>(xf)[2 * j];
+    const uint4 v1 = reinterpret_cast<const uint4*>(xf)[2 * j + 1];
+    bits[0] = v0.x; bits[1] = v0.y; bits[2] = v0.z; bits[3] = v0.w;
+    bits[4] = v1.x; bits[5] = v1.y; bits[6] = v1.z; bits[7] = v1.w;
+  }
+  uint32_t codes[2];
+  const float sc = moe_ue8m0_scale(moe_mx_quant8(bits, codes));
+  uint32_t o[4];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    o[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], sc, false));
+    o[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], sc, true));
+  }
+  if (i < n8) reinterpret_cast<uint4*>(out)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // STQ1_0 encoders ("Hy4-preview-GGUF" (AngelSlim), section 3, Our encoder), one wave per
 // 256-weight block of the flattened matrix, lane l = group l (weights 4l .. 4l+3).  Importance
 // w of a weight: imatrix[flat index mod K], or 1.
@@ -290,5 +320,15 @@ hipError_t moe_launch_stq1_encode(const float* x, const float* imatrix, int64_t 
   if ((n_blocks + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(stq1_encode_kernel, dim3((unsigned)((n_blocks + 3) / 4)), dim3(256), 0, s, x,
                      imatrix, n_blocks, K, method, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_mx_roundtrip_bf16(int64_t rows, int K, const uint16_t* xb, const float* xf,
+                                        uint16_t* out, hipStream_t s) {
+  const int64_t n8 = rows * K / 8;
+  if (n8 == 0) return hipSuccess;
+  if ((n8 + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_roundtrip_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, n8,
+                     xb, xf, out);
   return hipGetLastError();
 }

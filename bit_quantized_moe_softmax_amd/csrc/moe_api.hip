@@ -67,12 +67,14 @@ bool shared_gemm_ok(const moe_dims* d) {
 
 // Workspace regions: 0 h routed f32, 1 h shared f32, 2 xq, 3 xs, 4 hq, 5 hs, 6 total;
 // internal regions of the prefill GEMMs (ext): 0 x fp16 [T][H], 1 x row exponents [T],
-// 2 h as fp16 hi | lo [P][2I], 3 h row exponents [P], 4 shared h as bf16 hi | lo [T][2I].
+// 2 h as fp16 hi | lo [P][2I], 3 h row exponents [P], 4 shared h as bf16 hi | lo [T][2I]
+// (MXFP8 shared expert: the bf16 values of its E4M3 h [T][I]), 5 MXFP8 shared expert: the
+// bf16 values of its E4M3 x [T][H].
 void layout(const moe_dims* d, int fmt, int has_shared, size_t* offs, size_t* ext = nullptr) {
   const size_t T = d->T, H = d->H, I = d->I, P = (size_t)d->T * d->k;
-  size_t e[5];
+  size_t e[6];
   for (int i = 0; i < 7; ++i) offs[i] = (size_t)-1;
-  for (int i = 0; i < 5; ++i) e[i] = (size_t)-1;
+  for (int i = 0; i < 6; ++i) e[i] = (size_t)-1;
   size_t cur = 0;
   if (fmt == MOE_W_STQ1_0) {
     offs[0] = cur;
@@ -94,12 +96,13 @@ void layout(const moe_dims* d, int fmt, int has_shared, size_t* offs, size_t* ex
     e[2] = cur; cur = align_up(cur + P * 2 * I * 2);
     e[3] = cur; cur = align_up(cur + P * 4);
   }
-  if (has_shared && shared_gemm_ok(d)) {
+  if (has_shared) {   // (the shared expert's format is not known here: bf16 or MXFP8)
     e[4] = cur; cur = align_up(cur + T * 2 * I * 2);
+    e[5] = cur; cur = align_up(cur + T * H * 2);
   }
   offs[6] = cur;
   if (ext)
-    for (int i = 0; i < 5; ++i) ext[i] = e[i];
+    for (int i = 0; i < 6; ++i) ext[i] = e[i];
 }
 
 bool routed_fmt_ok(int fmt) {
@@ -262,8 +265,9 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
   if (!mat_ok(routed->gate, true) || !mat_ok(routed->up, true) || !mat_ok(routed->down, true))
     return MOE_ERR_INVALID_ARG;
   if (shared) {
-    if (shared->fmt != MOE_W_BF16 || !y_shared) return MOE_ERR_INVALID_ARG;
-    if (!mat_ok(shared->gate, false) || !mat_ok(shared->up, false) || !mat_ok(shared->down, false))
+    if ((shared->fmt != MOE_W_BF16 && shared->fmt != MOE_W_MXFP8) || !y_shared) return MOE_ERR_INVALID_ARG;
+    const bool sc = shared->fmt == MOE_W_MXFP8;
+    if (!mat_ok(shared->gate, sc) || !mat_ok(shared->up, sc) || !mat_ok(shared->down, sc))
       return MOE_ERR_INVALID_ARG;
     if (d->H % 256 || d->I % 256) return MOE_ERR_UNSUPPORTED;
   }
@@ -275,7 +279,7 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
   } else {
     if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
   }
-  size_t offs[7], ext[5];
+  size_t offs[7], ext[6];
   layout(d, fmt, shared != nullptr, offs, ext);
   if (!ws || ws_bytes < offs[6]) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
@@ -374,7 +378,40 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
 
-  if (shared && ext[4] != (size_t)-1) {
+  if (shared && shared->fmt == MOE_W_MXFP8) {
+    // W8A8: x and h through their MX E4M3 values (exact in bf16), grouped GEMMs on the bf16
+    // MFMA with the E4M3 weights decoded in registers, at every token count
+    float* hsh = reinterpret_cast<float*>(wsb + offs[1]);
+    uint16_t* h2 = reinterpret_cast<uint16_t*>(wsb + ext[4]);
+    uint16_t* xr = reinterpret_cast<uint16_t*>(wsb + ext[5]);
+    if (prof) moe_prof_begin(MOE_PROF_ACT_PREP, s);
+    hipError_t e = moe_launch_mx_roundtrip_bf16(T, H, x_bf16, nullptr, xr, s);
+    if (prof) moe_prof_end(MOE_PROF_ACT_PREP, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    G16Args a{};
+    a.w0 = shared->gate.codes; a.s0 = static_cast<const uint16_t*>(shared->gate.scales);
+    a.w1 = shared->up.codes;   a.s1 = static_cast<const uint16_t*>(shared->up.scales);
+    a.a = xr; a.out = hsh;
+    a.N = I; a.K = H; a.Ka = H; a.rows_a = T; a.E = 1; a.k = 1; a.P = T;
+    if (prof) moe_prof_begin(MOE_PROF_SH_GATEUP, s);
+    e = moe_launch_g16_mx8_gateup(a, s);
+    if (prof) moe_prof_end(MOE_PROF_SH_GATEUP, s);
+    bump(MOE_CNT_MXFP8_SHARED);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (prof) moe_prof_begin(MOE_PROF_ACT_PREP, s);
+    e = moe_launch_mx_roundtrip_bf16(T, I, nullptr, hsh, h2, s);
+    if (prof) moe_prof_end(MOE_PROF_ACT_PREP, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    G16Args b{};
+    b.w0 = shared->down.codes; b.s0 = static_cast<const uint16_t*>(shared->down.scales);
+    b.a = h2; b.out = y_shared;
+    b.N = H; b.K = I; b.Ka = I; b.rows_a = T; b.E = 1; b.k = 1; b.P = T;
+    if (prof) moe_prof_begin(MOE_PROF_SH_DOWN, s);
+    e = moe_launch_g16_mx8_down(b, s);
+    if (prof) moe_prof_end(MOE_PROF_SH_DOWN, s);
+    bump(MOE_CNT_MXFP8_SHARED);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  } else if (shared && shared_gemm_ok(d)) {
     // prefill: grouped GEMMs on the bf16 MFMA (one expert owning every token)
     float* hsh = reinterpret_cast<float*>(wsb + offs[1]);
     uint16_t* h2 = reinterpret_cast<uint16_t*>(wsb + ext[4]);
@@ -455,6 +492,7 @@ moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
   if (!mat_ok(routed->gate, true) || !mat_ok(routed->up, true) || !mat_ok(routed->down, true))
     return MOE_ERR_INVALID_ARG;
   if (shared) {
+    if (shared->fmt == MOE_W_MXFP8) return MOE_ERR_UNSUPPORTED;   // four-call path only
     if (shared->fmt != MOE_W_BF16 || !y_shared) return MOE_ERR_INVALID_ARG;
     if (!mat_ok(shared->gate, false) || !mat_ok(shared->up, false) || !mat_ok(shared->down, false))
       return MOE_ERR_INVALID_ARG;

@@ -128,6 +128,11 @@ __device__ __forceinline__ uint32_t moe_mx_quant8(const uint32_t* bits, uint32_t
   return (uint32_t)(X + 127);
 }
 
+// 2^(byte - 127) as fp32 for a UE8M0 scale byte (byte 0: 2^-127, a subnormal).
+__device__ __forceinline__ float moe_ue8m0_scale(uint32_t byte) {
+  return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -246,6 +251,12 @@ hipError_t moe_launch_g16_bf16_down(const G16Args& a, hipStream_t s);
 hipError_t moe_launch_rowscale_f16(const uint16_t* in16, const float* in32, long rows, int C,
                                    int two, uint16_t* out, int32_t* sexp, hipStream_t s);
 hipError_t moe_launch_split_bf16(const float* h, long rows, int C, uint16_t* out, hipStream_t s);
+hipError_t moe_launch_g16_mx8_gateup(const G16Args& a, hipStream_t s);
+hipError_t moe_launch_g16_mx8_down(const G16Args& a, hipStream_t s);
+// Rows of bf16 (xb) or fp32 (xf) [rows][K] -> bf16 values of their MX E4M3 quantisation
+// (group 32 along K), which bf16 holds exactly.
+hipError_t moe_launch_mx_roundtrip_bf16(int64_t rows, int K, const uint16_t* xb, const float* xf,
+                                        uint16_t* out, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 inline int moe_cu_count() {

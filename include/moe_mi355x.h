@@ -73,7 +73,11 @@ typedef enum {
   MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed         */
 } moe_status;
 
-typedef enum { MOE_W_STQ1_0 = 1, MOE_W_MXFP4 = 2, MOE_W_BF16 = 3, MOE_W_MXFP4_TILED = 4 } moe_wfmt;
+typedef enum { MOE_W_STQ1_0 = 1, MOE_W_MXFP4 = 2, MOE_W_BF16 = 3, MOE_W_MXFP4_TILED = 4,
+               MOE_W_MXFP8 = 5 } moe_wfmt;
+/* MOE_W_MXFP8 (shared expert only; "Hy4-preview-SF-WFP4AFP8", Quant Diff table: the shared
+ * experts' gate/up/down are MXFP8 W8A8 group 32): codes [N][K] E4M3 bytes (0x7F / 0xFF,
+ * the NaN codes, are not valid weights), scales [N][K/32] UE8M0 bytes. */
 
 /* Layer dimensions: T tokens, hidden H, expert intermediate I, E routed experts,
  * k experts per token.  Limits: 1 <= k <= min(E, 32), E <= 1024, H % 32 == 0,
@@ -111,7 +115,8 @@ enum {
   MOE_CNT_DECODE_FUSED = 15,   /* moe_layer_decode (three fused kernels)    */
   MOE_CNT_STQ_GEMM = 16,       /* STQ1_0 prefill grouped GEMMs (fp16 MFMA)  */
   MOE_CNT_ROWSCALE = 17,       /* activation rows to fp16 / bf16 hi + lo    */
-  MOE_CNT_SLOTS = 18
+  MOE_CNT_MXFP8_SHARED = 18,   /* MXFP8 shared expert GEMMs (gate/up, down) */
+  MOE_CNT_SLOTS = 19
 };
 
 MOE_MI355X_API const char* moe_status_str(moe_status s);
@@ -199,8 +204,11 @@ MOE_MI355X_API moe_status moe_workspace_offsets(const moe_dims* d, int32_t route
  *           activations); FP8 x FP4 products on the scaled MFMA, fp32 accumulation.
  *   MXFP4_TILED: the MXFP4 computation, bit for bit, on weights in the tiled layout
  *           (the layout the GEMMs stream fastest; the MXFP4 path reads row-major rows).
- * When `shared` is non-NULL (fmt MOE_W_BF16, one expert) y_shared[t] = the same
- * SwiGLU on bf16 weights and bf16 x[t] for every token, h kept in fp32.
+ * When `shared` is non-NULL (one expert) y_shared[t] = the same SwiGLU for every token:
+ *   MOE_W_BF16: bf16 weights on bf16 x[t], h kept in fp32;
+ *   MOE_W_MXFP8: W8A8 -- x[t] MX-quantised to E4M3 along H and h along I, as for MXFP4
+ *           routed experts; E4M3 x E4M3 products (exact in the bf16 MFMA), fp32 sums.
+ *           Runs on the prefill GEMMs at every token count.
  *   x_bf16 [T][H]; sorted_pair [P]; expert_offsets [E+1] (from moe_permute)
  *   y_pairs [P][H] fp32 out (sorted-pair order); y_shared [T][H] fp32 out or NULL
  *   ws / ws_bytes: device workspace of at least moe_workspace_size bytes.
@@ -239,6 +247,8 @@ MOE_MI355X_API moe_status moe_combine(const moe_dims* d, const float* y_pairs,
  * four-call definitions.
  * MXFP4 routed experts follow moe_expert_ffn's MXFP4 definition: x and h MX-quantised to
  * E4M3 (group 32 along H, resp. I) before their projections.
+ * The shared expert must be bf16 (an MXFP8 one returns MOE_ERR_UNSUPPORTED: use the four
+ * calls).
  * Limits: T <= 64, k <= 32, E <= 256, and (H, I) one of the compiled shapes (512, 256),
  * (1024, 512), (2048, 1024), (4096, 2048), (6144, 2048), (8192, 2048); MXFP4 routed
  * experts also T <= 4 and T k (I + I/32) <= 81920 (every pair's FP8 h fits the down

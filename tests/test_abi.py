@@ -43,7 +43,9 @@ def test_workspace_layout():
     n = M.moe_workspace_size(d, M.MOE_W_STQ1_0, False)
     assert n == 8 * 128 * 4                      # h of 8 pairs x 128, fp32, 256-aligned
     offs = M.moe_workspace_offsets(d, M.MOE_W_STQ1_0, True)
-    assert offs[0] == 0 and offs[1] == 4096 and offs[2] is None and offs[6] == 4096 + 2048
+    # routed h, shared h, then the shared expert's bf16 staging of h (hi | lo, or its MXFP8
+    # values) and of x (MXFP8)
+    assert offs[0] == 0 and offs[1] == 4096 and offs[2] is None and offs[6] == 4096 + 2048 + 2048 + 2048
     d = M.Dims(T=4096, H=6144, I=2048, E=256, k=8)
     offs = M.moe_workspace_offsets(d, M.MOE_W_MXFP4, True)
     P = 4096 * 8
@@ -52,14 +54,15 @@ def test_workspace_layout():
     assert offs[3] == offs[2] + 4096 * 6144
     assert offs[4] == offs[3] + 4096 * 6144 // 32
     assert offs[5] == offs[4] + P * 2048
-    # the prefill shared-expert GEMM's bf16 hi | lo copy of h closes the workspace
-    assert offs[6] == offs[5] + P * 2048 // 32 + 4096 * 2 * 2048 * 2
+    # the shared expert's staging (h as bf16 hi | lo, x as MXFP8 values) closes the workspace
+    assert offs[6] == offs[5] + P * 2048 // 32 + 4096 * 2 * 2048 * 2 + 4096 * 6144 * 2
     # STQ1_0 at prefill size: x and h (hi | lo) as fp16 rows with their row exponents, then the
     # shared expert's hi | lo h (each region 256-byte aligned)
     up = lambda v: (v + 255) // 256 * 256
     offs = M.moe_workspace_offsets(d, M.MOE_W_STQ1_0, True)
     assert offs[0] == 0 and offs[1] == P * 2048 * 4 and offs[2] is None
-    ext = up(4096 * 6144 * 2) + up(4096 * 4) + up(P * 2 * 2048 * 2) + up(P * 4) + up(4096 * 2 * 2048 * 2)
+    ext = (up(4096 * 6144 * 2) + up(4096 * 4) + up(P * 2 * 2048 * 2) + up(P * 4) + up(4096 * 2 * 2048 * 2)
+           + up(4096 * 6144 * 2))
     assert offs[6] == offs[1] + 4096 * 2048 * 4 + ext
 
 

@@ -948,3 +948,82 @@ def test_stq1_encode_grid_inputs_exact():
     for method in (M.MOE_STQ1_ENC_UPSTREAM, M.MOE_STQ1_ENC_WLS):
         gc, gs = _encode_gpu(x, 1024, np.exp(g.standard_normal(1024)), method)
         assert (gc == want[0]).all() and (gs == want[1]).all()
+
+
+# ----------------------------------------------------------------------------- MXFP8 shared expert
+MX8_SHARED = {
+    # a few tokens: routed STQ1_0 on the decode kernels, the MXFP8 shared expert on its GEMMs
+    "stq-h512-i256-e8-top2-t5": synth.LayerCfg("s8", 5, 512, 256, 8, 2, True, "stq1", False, False, 1, 61),
+    # several M blocks of the shared expert (300 tokens: three blocks of 100), MXFP4 routed
+    "mx-h512-i256-e8-top2-t300": synth.LayerCfg("s8", 300, 512, 256, 8, 2, True, "mxfp4", False, True, 1, 62),
+    # three down N tiles, full blocks (256 tokens: two blocks of 128)
+    "stq-h768-i512-e4-top2-t256": synth.LayerCfg("s8", 256, 768, 512, 4, 2, True, "stq1", False, True, 1, 63),
+}
+
+
+def _mx8_shared_check(c, inp, bufs, d, sh8, toks=None):
+    """h of the shared expert against the oracle's SiLU(a Wg^T) * (a Wu^T) with a the MX
+    E4M3 values of x, and y_shared against the oracle's down projection of the MX E4M3
+    values of the GPU's own h (so the discontinuous requantisation is taken the same way)."""
+    fmt = M.MOE_W_STQ1_0 if c.fmt == "stq1" else M.MOE_W_MXFP4
+    offs = M.moe_workspace_offsets(d, fmt, True)
+    T, H, I = c.T, c.H, c.I
+    toks = np.arange(T) if toks is None else np.asarray(toks)
+    h_gpu = host(bufs.ws[offs[1]:offs[1] + T * I * 4]).view(np.float32).reshape(T, I)[toks]
+    a = O.mx_dequantize_e4m3(*O.mx_quantize_e4m3(O.bf16_to_f64(inp["x"][toks])))
+    Wg, Wu, Wd = [O.mx_dequantize_e4m3(cd, sc) for cd, sc in sh8]
+    h_ref = O.silu(a @ Wg.T) * (a @ Wu.T)
+    eh = row_err(h_gpu, h_ref).max()
+    y_ref = O.mx_dequantize_e4m3(*O.mx_quantize_e4m3(h_gpu.astype(np.float64))) @ Wd.T
+    ey = row_err(host(bufs.y_shared)[toks], y_ref).max()
+    say("mxfp8 shared: h max row err", float(eh), "y_shared max row err", float(ey))
+    assert eh <= TOL and ey <= TOL
+
+
+@pytest.mark.parametrize("name", list(MX8_SHARED))
+def test_shared_expert_mxfp8(name):
+    """MXFP8 W8A8 shared expert (E4M3 weights decoded with the gfx950 scaled conversion, x and
+    h MX-quantised) through moe_expert_ffn, next to STQ1_0 or MXFP4 routed experts."""
+    c = MX8_SHARED[name]
+    say("mxfp8 shared", name)
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    sh8 = synth.shared_weights_mxfp8(c.seed, 0, c.I, c.H)
+    shared = M.Experts(M.MOE_W_MXFP8, *[(dev(cd), dev(sc)) for cd, sc in sh8])
+    routed = routed_experts(c, inp["routed"])
+    fmt = M.MOE_W_STQ1_0 if c.fmt == "stq1" else M.MOE_W_MXFP4
+    bufs = LayerBuffers(d, fmt, True)
+    M.moe_reset_counters()
+    if c.logits_given:
+        run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
+    else:
+        run_layer(d, bufs, dev(inp["x"]), routed, shared, wr_bf16=dev(inp["wr"]))
+    torch.cuda.synchronize()
+    cnt = M.moe_get_counters()
+    assert cnt["mxfp8_shared"] == 2 and cnt["bf16_gateup"] == 0 and cnt["bf16_gemm"] == 0
+    _mx8_shared_check(c, inp, bufs, d, sh8)
+    out_ref = O.combine(host(bufs.y_pairs), host(bufs.topk_w), host(bufs.pair_pos), host(bufs.y_shared))
+    assert row_err(host(bufs.out), out_ref).max() <= TOL
+    # the whole layer against the oracle, printed (h requantisation is discontinuous)
+    ref = O.moe_layer(inp["x"], c.k, oracle_weights(c, inp["routed"]), c.fmt,
+                      wr_bits=None if c.logits_given else inp["wr"],
+                      logits_in=inp["logits_in"] if c.logits_given else None,
+                      shared=sh8, shared_fmt="mxfp8")
+    say("mxfp8 shared: y_shared vs the oracle end to end",
+        float(row_err(host(bufs.y_shared), ref["y_shared"]).max()))
+
+
+def test_shared_expert_mxfp8_hy4_t4096_sampled():
+    """Hy4 MXFP4 routed + MXFP8 shared layer at 4096 tokens (the WFP4AFP8 recipe's formats):
+    the shared expert checked on sampled tokens."""
+    c = synth.LayerCfg("hy4-wfp4afp8-prefill-t4096", 4096, 6144, 2048, 256, 8, True, "mxfp4", False, True, 1, 64)
+    say("mxfp8 shared t4096 generate")
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    sh8 = synth.shared_weights_mxfp8(c.seed, 0, c.I, c.H)
+    shared = M.Experts(M.MOE_W_MXFP8, *[(dev(cd), dev(sc)) for cd, sc in sh8])
+    routed = routed_experts(c, inp["routed"], tiled=True)
+    bufs = LayerBuffers(d, M.MOE_W_MXFP4, True)
+    run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
+    torch.cuda.synchronize()
+    _mx8_shared_check(c, inp, bufs, d, sh8, toks=synth.sample_tokens(c.seed, c.T, 4))
