@@ -204,6 +204,11 @@ MOE_MI355X_API moe_status moe_workspace_offsets(const moe_dims* d, int32_t route
  *           activations); FP8 x FP4 products on the scaled MFMA, fp32 accumulation.
  *   MXFP4_TILED: the MXFP4 computation, bit for bit, on weights in the tiled layout
  *           (the layout the GEMMs stream fastest; the MXFP4 path reads row-major rows).
+ * Kernels by token count: MXFP4 always runs the grouped GEMMs; STQ1_0 runs the decode-shaped
+ * kernels below 128 tokens and grouped GEMMs on the fp16 MFMA from 128 (x scaled per row by
+ * a power of two into fp16, h as fp16 hi + lo: results within the same tolerance); the bf16
+ * shared expert switches at 256 tokens.  The environment variable MOE_MI355X_PREFILL_MIN_T,
+ * read once, overrides both thresholds (measurement).
  * When `shared` is non-NULL (one expert) y_shared[t] = the same SwiGLU for every token:
  *   MOE_W_BF16: bf16 weights on bf16 x[t], h kept in fp32;
  *   MOE_W_MXFP8: W8A8 -- x[t] MX-quantised to E4M3 along H and h along I, as for MXFP4
