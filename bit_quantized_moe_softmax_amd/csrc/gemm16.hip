@@ -27,16 +27,17 @@
 // blocks of at most 128 rows; a job is (M block, N tile of 256 weight rows: 128 gate + the
 // 128 up rows of the same h-columns, or 256 output columns); jobs are numbered expert-major,
 // then N tile, then M block, each XCD takes one contiguous range, and one workgroup per CU
-// walks it (two for the down projections).  Four waves share the M block's activation rows, staged per K step (64) in LDS
-// (double-buffered); each wave owns 64 weight rows whose codes it loads from HBM into
-// registers, so weights never pass through LDS.
+// walks it (two for a down projection with 64 or more pairs per expert).  Four waves share
+// the M block's activation rows, staged per K step (64) in LDS (double-buffered); each wave
+// owns 64 weight rows whose codes it loads from HBM into registers, so weights never pass
+// through LDS.
 //
 // K order.  The MFMA lane l serves row / column l % 16 and takes 8 consecutive K-slots from
 // slot 8 (l / 16) of the 32-wide step.  The slot -> K map is ours, the same for A and B:
 //   STQ1_0: lane group g owns groups 16g .. 16g+15 of each block (8 code bytes + 16 high
 //     bits, loaded once per block); K step j (0..3) of block b and sub-step t (0, 1) take
 //     groups 16g + 4j + 2t, +1, i.e. K = 256 b + 64 g + 16 j + 8 t + (0..7).
-//   bf16: K step j, sub-step t: K = 64 j + 32 t + 8 g + (0..7).
+//   bf16 and MXFP8: K step j, sub-step t: K = 64 j + 32 t + 8 g + (0..7).
 // The A rows are staged in the same order, so each lane reads its A operand as one
 // 16-byte LDS word.
 #include "moe_device.h"

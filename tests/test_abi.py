@@ -112,6 +112,36 @@ def test_argument_checks_need_no_gpu():
         M.moe_workspace_offsets(d3, M.MOE_W_MXFP4, True)
 
 
+def test_new_entry_point_checks_need_no_gpu():
+    F = 1 << 20   # a fake device address: every call below returns before any launch
+    # STQ1_0 encoder: whole 256-weight blocks, a positive K, a known method, aligned pointers
+    enc = "moe_stq1_encode"
+    assert _raw(enc, F, None, 300, 256, 0, F, F, None) == 1             # n_weights % 256
+    assert _raw(enc, F, None, 512, 0, 0, F, F, None) == 1               # K <= 0
+    assert _raw(enc, F, None, 512, 256, 7, F, F, None) == 1             # unknown method
+    assert _raw(enc, F + 4, None, 512, 256, 1, F, F, None) == 1         # x not 16-byte aligned
+    assert _raw(enc, F, None, 512, 256, 1, F + 4, F, None) == 1         # codes not 8-byte aligned
+    assert _raw(enc, None, None, 0, 256, 1, None, None, None) == 0      # nothing to do
+    d = M.Dims(T=4, H=512, I=256, E=8, k=2)
+    routed = M.Experts(M.MOE_W_STQ1_0, (F, F), (F, F), (F, F))
+    # an MXFP8 shared expert needs its scale bytes
+    sh8 = M.Experts(M.MOE_W_MXFP8, (F, None), (F, F), (F, F))
+    assert _raw("moe_expert_ffn", d.ref(), routed.ref(), sh8.ref(), F, F, F, F, F, F,
+                ctypes.c_size_t(1 << 30), None) == 1
+    # the fused decode takes only a bf16 shared expert, and MXFP4 routed experts up to 4 tokens
+    sh8 = M.Experts(M.MOE_W_MXFP8, (F, F), (F, F), (F, F))
+    args = (F,) * 11 + (None, F, None, F, ctypes.c_size_t(1 << 30), None)
+    assert _raw("moe_layer_decode", d.ref(), routed.ref(), sh8.ref(), *args) == 2
+    mx = M.Experts(M.MOE_W_MXFP4_TILED, (F, F), (F, F), (F, F))
+    d5 = M.Dims(T=5, H=512, I=256, E=8, k=2)
+    assert _raw("moe_layer_decode", d5.ref(), mx.ref(), None, *args) == 2
+    d4 = M.Dims(T=4, H=6144, I=2048, E=256, k=32)                   # FP8 h of 128 pairs: too big
+    assert _raw("moe_layer_decode", d4.ref(), mx.ref(), None, *args) == 2
+    offs = M.moe_layer_decode_workspace_offsets(d, True)
+    assert offs[10] == M.moe_layer_decode_workspace_size(d, True)
+    assert offs[9] >= offs[8] and offs[10] - offs[9] >= d.T * (d.H + d.H // 32)
+
+
 def test_zero_tokens_enqueue_nothing():
     d = M.Dims(T=0, H=256, I=128, E=8, k=2)
     # T == 0 returns before touching the (fake) pointers or the GPU
