@@ -106,11 +106,11 @@ def decode_bench(args):
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
 
-    def step(i):
+    def step(i, st=None):
         L = copies[i % len(copies)]
         x = L["x"][(i // len(copies)) % 64].reshape(1, -1)
         M.moe_layer_decode(d, L["routed"], L["shared"], x, L["wr"], None, logits, ids, w, sp, off,
-                           pp, yp, ysh, None, out, None, ws, s)
+                           pp, yp, ysh, None, out, None, ws, s if st is None else st)
 
     for i in range(args.warmup):
         step(i)
@@ -125,6 +125,23 @@ def decode_bench(args):
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / args.steps
+    # the same steps replayed from one captured HIP graph (one step per layer copy)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream().cuda_stream
+        for i in range(len(copies)):
+            step(i, cs)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // len(copies))
+    start.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end) / (reps * len(copies))
+    del graph
     # second pass with the library's per-kernel HIP events (same steps, same stream)
     M.moe_profile_enable(True)
     for i in range(args.steps):
@@ -169,7 +186,7 @@ def decode_bench(args):
     }
     expert_b = routed_gu_b + routed_dn_b + shared_gu_b + shared_dn_b
     layer_b = expert_b + router_b + x_b + c.H * 4
-    return dict(c=c, ms=ms, ms4=ms4, t_wall=t_wall, expert_b=expert_b, layer_b=layer_b, prof=prof,
+    return dict(c=c, ms=ms, ms4=ms4, graph_ms=graph_ms, t_wall=t_wall, expert_b=expert_b, layer_b=layer_b, prof=prof,
                 kbytes=kb, routed_b=routed_gu_b + routed_dn_b, shared_b=shared_gu_b + shared_dn_b,
                 router_b=router_b)
 
@@ -532,6 +549,8 @@ def main():
         "whole_layer_gbs": round(dec["layer_b"] / (dec["ms"] * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "four_call_ms_per_step": round(dec["ms4"], 5),
+        "graph_ms_per_step": round(dec["graph_ms"], 5),
+        "graph_value": round(dec["expert_b"] / (dec["graph_ms"] * 1e-3) / 1e9, 1),
         "kernels": kern,
         "bytes_per_step": {"routed": dec["routed_b"], "shared": dec["shared_b"],
                            "router": dec["router_b"], "layer_total": dec["layer_b"]},

@@ -1027,3 +1027,51 @@ def test_shared_expert_mxfp8_hy4_t4096_sampled():
     run_layer(d, bufs, dev(inp["x"]), routed, shared, logits_in=dev(inp["logits_in"]))
     torch.cuda.synchronize()
     _mx8_shared_check(c, inp, bufs, d, sh8, toks=synth.sample_tokens(c.seed, c.T, 4))
+
+
+# ----------------------------------------------------------------------------- graph capture
+@pytest.mark.parametrize("fmt", ["stq1", "mxfp4"])
+def test_fused_decode_graph_replays(fmt):
+    """moe_layer_decode captured once into a HIP graph and replayed with new tokens copied into
+    the captured input buffer, eager work and synchronisations between the replays: every
+    replay equals the eager call on the same token, bit for bit."""
+    c = synth.LayerCfg("g", 1, 512, 256, 8, 2, True, fmt, False, False, 1, 71)
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"], tiled=(fmt == "mxfp4"))
+    shared = shared_experts(inp["shared"])
+    f32, i32 = torch.float32, torch.int32
+    bufs = [torch.empty((1, c.E), dtype=f32, device="cuda"), torch.empty((1, c.k), dtype=i32, device="cuda"),
+            torch.empty((1, c.k), dtype=f32, device="cuda"), torch.empty(d.P, dtype=i32, device="cuda"),
+            torch.empty(c.E + 1, dtype=i32, device="cuda"), torch.empty(d.P, dtype=i32, device="cuda"),
+            torch.empty((d.P, c.H), dtype=f32, device="cuda"), torch.empty((1, c.H), dtype=f32, device="cuda")]
+    out = torch.empty((1, c.H), dtype=f32, device="cuda")
+    ws = torch.zeros(M.moe_layer_decode_workspace_size(d, True), dtype=torch.uint8, device="cuda")
+    x_in = torch.empty((1, c.H), dtype=torch.int16, device="cuda")
+    wr = dev(inp["wr"])
+    tokens = dev(synth.activations(c.seed, 5, 4, c.H))
+
+    def call(stream):
+        M.moe_layer_decode(d, routed, shared, x_in, wr, None, *bufs, None, out, None, ws, stream)
+
+    x_in.copy_(tokens[0:1])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm the library's one-time set-up off the capture
+        call(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for r in range(4):
+        x_in.copy_(tokens[r:r + 1])
+        call(torch.cuda.current_stream().cuda_stream)          # eager reference
+        torch.cuda.synchronize()
+        want = out.clone()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), want.view(torch.int32)), f"replay {r} differs"
