@@ -305,6 +305,68 @@ def stq_prefill_bench(args):
     return dict(c=c, routed_ms=r_ms, with_shared_ms=ws_ms, flops=flops, prof=prof)
 
 
+def slot_bank_bench(args, slots):
+    """Hy4 STQ1_0 layer, one token, with the 256 routed experts in pinned host memory and an
+    S-slot device bank: per step route, copy the ids to the host, plan, fetch the misses
+    (host -> device), remap ids, permute, expert FFN over the slots, combine.  Host-to-device
+    traffic is part of the step (context for models larger than HBM, not the headline)."""
+    import numpy as np
+    import torch
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    from bit_quantized_moe_softmax_amd.layer import LayerBuffers, bf16_experts
+
+    c = synth.cfg(1)
+    d = M.Dims(1, c.H, c.I, c.E, c.k)
+    dS = M.Dims(1, c.H, c.I, slots, c.k)
+    fams = [synth.stq1_family(c.seed, 0, m, c.E, c.I * c.H) for m in range(3)]
+    host = [tuple(torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).pin_memory() for a in f) for f in fams]
+    del fams
+    per = []
+    for cd, sc in host:
+        per += [cd.numel() // c.E, sc.numel() // c.E]
+    slot_t = [(torch.empty(slots * per[2 * i], dtype=torch.uint8, device="cuda"),
+               torch.empty(slots * per[2 * i + 1], dtype=torch.uint8, device="cuda")) for i in range(3)]
+    host_src = M.Experts(M.MOE_W_STQ1_0, *host)
+    dev_slots = M.Experts(M.MOE_W_STQ1_0, *slot_t)
+    shared = bf16_experts(*[dev(w) for w in synth.shared_weights(c.seed, 0, c.I, c.H)])
+    wr = dev(synth.router_weights(c.seed, 0, c.E, c.H))
+    xs = dev(synth.activations(c.seed, 3, 256, c.H))
+    bank = M.SlotBank(c.E, slots, per, io_split=4)
+    b = LayerBuffers(dS, M.MOE_W_STQ1_0, True)
+    slot_of_dev = torch.empty(c.E, dtype=torch.int32, device="cuda")
+    slot_ids = torch.empty((1, c.k), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def step(i):
+        x = xs[i % 256].reshape(1, -1)
+        M.moe_route(d, x, wr, None, None, b.logits, b.topk_ids, b.topk_w, s)
+        slot_of, _ = bank.plan(b.topk_ids.cpu().numpy())
+        slot_of_dev.copy_(torch.from_numpy(slot_of), non_blocking=False)
+        bank.fetch(host_src, dev_slots, s)
+        M.moe_remap_ids(b.topk_ids, d.P, slot_of_dev, slot_ids, s)
+        M.moe_permute(dS, slot_ids, b.sorted_pair, b.offsets, b.pair_pos, s)
+        M.moe_expert_ffn(dS, dev_slots, shared, x, b.sorted_pair, b.offsets, b.y_pairs, b.y_shared, b.ws, s)
+        M.moe_combine(dS, b.y_pairs, b.topk_w, b.pair_pos, b.y_shared, None, b.out, None, s)
+
+    for i in range(8):
+        step(i)
+    torch.cuda.synchronize()
+    h0, m0 = bank.stats()
+    n = 48
+    t0 = time.perf_counter()
+    for i in range(8, 8 + n):
+        step(i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    h1, m1 = bank.stats()
+    hits, misses = h1 - h0, m1 - m0
+    moved = misses * sum(per)
+    return {"slots": slots, "us_per_step": round(dt * 1e6, 1), "hit_rate": round(hits / max(1, hits + misses), 3),
+            "host_to_device_gbs": round(moved / (dt * n) / 1e9, 1)}
+
+
 def mx_decode_bench(args):
     """Hy4 layer with MXFP4 (tiled) routed experts, one token, through moe_layer_decode;
     steps rotate over three layer copies so the weights are not cache-resident."""
@@ -631,6 +693,14 @@ def main():
                                                 "algorithmic_bytes": k2["algorithmic_bytes"]}}
         except Exception as e:
             out["mxfp4_decode"] = {"error": repr(e)}
+        try:
+            out["slot_bank_decode"] = {
+                "workload": "hy4-stq1_0-decode-t1, routed experts in pinned host memory",
+                "note": "host-to-device copies inside the step (PCIe-inclusive); random tokens, so hits "
+                        "come only from the bank holding a slot's expert by chance",
+                "runs": [slot_bank_bench(args, S) for S in (8, 96)]}
+        except Exception as e:
+            out["slot_bank_decode"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(out), flush=True)

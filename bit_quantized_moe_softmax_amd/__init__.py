@@ -18,7 +18,7 @@ __all__ = [
     "moe_route", "moe_permute", "moe_workspace_size", "moe_workspace_offsets", "moe_expert_ffn",
     "moe_combine", "moe_stq1_pack", "moe_stq1_dequant", "moe_mxfp4_dequant", "moe_mx_quant_act",
     "moe_rmsnorm_bf16", "moe_layer_decode_workspace_size", "moe_layer_decode_workspace_offsets",
-    "moe_layer_decode", "moe_stq1_encode", "MOE_STQ1_ENC_UPSTREAM", "MOE_STQ1_ENC_WLS",
+    "moe_layer_decode", "moe_stq1_encode", "SlotBank", "moe_remap_ids", "MOE_STQ1_ENC_UPSTREAM", "MOE_STQ1_ENC_WLS",
     "moe_profile_enable", "moe_profile_read", "PROFILE_SLOTS",
 ]
 
@@ -74,6 +74,12 @@ _SIGS = {
     "moe_layer_decode_workspace_size": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "moe_layer_decode_workspace_offsets": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "moe_stq1_encode": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "moe_slot_bank_create": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P]),
+    "moe_slot_bank_destroy": (ctypes.c_int, [_P]),
+    "moe_slot_bank_plan": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P]),
+    "moe_slot_bank_fetch": (ctypes.c_int, [_P, _P, _P, _P]),
+    "moe_slot_bank_stats": (ctypes.c_int, [_P, _P, _P]),
+    "moe_remap_ids": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P, _P]),
     "moe_layer_decode": (ctypes.c_int, [_P, _P, _P] + [_P] * 15 + [ctypes.c_size_t, _P]),
     "moe_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
     "moe_profile_read": (ctypes.c_int, [_P, _P]),
@@ -234,6 +240,51 @@ def moe_rmsnorm_bf16(T, H, eps, r, a, stream=None):
 
 
 MOE_STQ1_ENC_UPSTREAM, MOE_STQ1_ENC_WLS = 0, 1
+
+
+class SlotBank:
+    """Host handle of an expert slot bank (E experts, S device slots): plan() returns the
+    slot of every resident expert for a step's expert ids (a host int32 array), fetch()
+    enqueues the planned host -> device copies."""
+
+    def __init__(self, E: int, S: int, bytes_per_expert, io_split: int = 4):
+        b = (ctypes.c_uint64 * 6)(*[int(v) for v in bytes_per_expert])
+        h = ctypes.c_void_p()
+        _check(lib().moe_slot_bank_create(E, S, ctypes.cast(b, _P), io_split, ctypes.byref(h)))
+        self._h = h
+        self.E, self.S = E, S
+
+    def plan(self, ids_host):
+        import numpy as np
+        ids = np.ascontiguousarray(ids_host, dtype=np.int32).reshape(-1)
+        slot_of = np.empty(self.E, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().moe_slot_bank_plan(self._h, ids.ctypes.data, ids.size, slot_of.ctypes.data,
+                                        ctypes.byref(n)))
+        return slot_of, n.value
+
+    def fetch(self, host_src, dev_slots, stream=None):
+        _check(lib().moe_slot_bank_fetch(self._h, host_src.ref(), dev_slots.ref(), _stream(stream)))
+
+    def stats(self):
+        h, m = ctypes.c_uint64(), ctypes.c_uint64()
+        _check(lib().moe_slot_bank_stats(self._h, ctypes.byref(h), ctypes.byref(m)))
+        return h.value, m.value
+
+    def close(self):
+        if self._h:
+            lib().moe_slot_bank_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter teardown
+            pass
+
+
+def moe_remap_ids(ids, n: int, slot_of, out, stream=None) -> None:
+    _check(lib().moe_remap_ids(_ptr(ids), n, _ptr(slot_of), _ptr(out), _stream(stream)))
 
 
 def moe_stq1_encode(x_f32, imatrix_f32, n_weights: int, K: int, method: int, codes, scales, stream=None):

@@ -15,7 +15,7 @@ LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "misc.hip", "ffn_decode.hip", "mx_gemm.hip",
-           "gemm16.hip", "decode_fused.hip"]
+           "gemm16.hip", "decode_fused.hip", "slot_bank.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

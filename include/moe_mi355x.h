@@ -314,6 +314,39 @@ MOE_MI355X_API moe_status moe_stq1_encode(const float* x, const float* imatrix, 
                                           int32_t K, int32_t method, uint8_t* codes,
                                           uint16_t* scales, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Expert slot bank ("Hy4-preview Flash-MoE STQ1_0", slot-bank mode: routed experts kept
+ * expert-major outside the dense model and streamed into a fixed set of slots as the router
+ * asks for them; 8 slots is the minimum for top-8, more slots cache more experts, misses are
+ * read in bounded chunks).  For models larger than HBM: S device slots hold routed experts,
+ * filled from caller-owned (pinned) host memory.  A step:
+ *   1. moe_slot_bank_plan (host only): the step's expert ids (host array, e.g. topk_ids
+ *      copied back) -> slot_of[E] (slot of every resident expert, -1 otherwise).  Resident
+ *      experts are hits; each miss takes an empty slot, else the least recently used slot
+ *      that no expert of this step holds (lowest slot on ties).  MOE_ERR_UNSUPPORTED when the
+ *      step has more distinct experts than slots (state unchanged).
+ *   2. moe_slot_bank_fetch: enqueue the planned copies (every non-empty family buffer of each
+ *      missing expert, in io_split chunks) host -> device on `stream`.
+ *   3. moe_remap_ids: topk_ids -> slot ids on the device (slot_of uploaded by the caller), then
+ *      moe_permute / moe_expert_ffn with E = S on the slot arrays, and moe_combine as usual.
+ * bytes[6]: per-expert bytes of gate codes, gate scales, up codes, up scales, down codes,
+ * down scales (0 for a family buffer that does not exist).  host_src: all E experts
+ * (expert-major, pinned host memory); dev_slots: S experts' worth of device memory in the
+ * same layout.  The bank object is host state; it is not thread-safe. */
+typedef struct moe_slot_bank moe_slot_bank;
+MOE_MI355X_API moe_status moe_slot_bank_create(int32_t E, int32_t S, const uint64_t* bytes,
+                                               int32_t io_split, moe_slot_bank** out);
+MOE_MI355X_API moe_status moe_slot_bank_destroy(moe_slot_bank* bank);
+MOE_MI355X_API moe_status moe_slot_bank_plan(moe_slot_bank* bank, const int32_t* ids_host,
+                                             int64_t n, int32_t* slot_of_host, int32_t* n_copies);
+MOE_MI355X_API moe_status moe_slot_bank_fetch(moe_slot_bank* bank, const moe_experts* host_src,
+                                              const moe_experts* dev_slots, void* stream);
+MOE_MI355X_API moe_status moe_slot_bank_stats(const moe_slot_bank* bank, uint64_t* hits,
+                                              uint64_t* misses);
+/* ids [n] -> out [n] = slot_of[ids] (device arrays; ids must be resident in slot_of). */
+MOE_MI355X_API moe_status moe_remap_ids(const int32_t* ids, int64_t n, const int32_t* slot_of,
+                                        int32_t* out, void* stream);
+
 /* Decode STQ1_0 blocks to fp32 weights out [n_blocks*256] (exact). */
 MOE_MI355X_API moe_status moe_stq1_dequant(const uint8_t* codes, const uint16_t* scales,
                                            int64_t n_blocks, float* out, void* stream);

@@ -1075,3 +1075,54 @@ def test_fused_decode_graph_replays(fmt):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), want.view(torch.int32)), f"replay {r} differs"
+
+
+# ----------------------------------------------------------------------------- expert slot bank
+def test_slot_bank_layer_equals_direct():
+    """A layer whose 16 routed experts live in pinned host memory and run from an 8-slot
+    device bank (plan, chunked fetch, id remap, then permute / FFN / combine over the slots)
+    gives the same bits as the layer run on all 16 experts in device memory, step after step
+    with new tokens (hits and misses both occur)."""
+    E, S = 16, 8
+    c = synth.LayerCfg("sb", 4, 512, 256, E, 2, True, "stq1", False, False, 1, 81)
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, E, c.k)
+    dS = M.Dims(c.T, c.H, c.I, S, c.k)
+    routed = routed_experts(c, inp["routed"])
+    shared = shared_experts(inp["shared"])
+    wr = dev(inp["wr"])
+    fams = inp["routed"]                                    # (codes [E, n], scales [E, m]) x 3
+    host = [tuple(torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).pin_memory() for a in f) for f in fams]
+    per = []
+    for cd, sc in host:
+        per += [cd.numel() // E, sc.numel() // E]
+    slots = [(torch.empty(S * per[2 * i], dtype=torch.uint8, device="cuda"),
+              torch.empty(S * per[2 * i + 1], dtype=torch.uint8, device="cuda")) for i in range(3)]
+    host_src = M.Experts(M.MOE_W_STQ1_0, *host)
+    dev_slots = M.Experts(M.MOE_W_STQ1_0, *slots)
+    bank = M.SlotBank(E, S, per, io_split=4)
+    ref_bufs = LayerBuffers(d, M.MOE_W_STQ1_0, True)
+    sb = LayerBuffers(dS, M.MOE_W_STQ1_0, True)
+    slot_of_dev = torch.empty(E, dtype=torch.int32, device="cuda")
+    slot_ids = torch.empty((c.T, c.k), dtype=torch.int32, device="cuda")
+    tokens = synth.activations(c.seed, 9, 8 * c.T, c.H)
+    for step in range(8):
+        x = dev(tokens[step * c.T:(step + 1) * c.T])
+        ref = run_layer(d, ref_bufs, x, routed, shared, wr_bf16=wr)
+        M.moe_route(d, x, wr, None, None, sb.logits, sb.topk_ids, sb.topk_w)
+        slot_of, n_copies = bank.plan(host_t(sb.topk_ids))
+        slot_of_dev.copy_(torch.from_numpy(slot_of))
+        bank.fetch(host_src, dev_slots, torch.cuda.current_stream().cuda_stream)
+        M.moe_remap_ids(sb.topk_ids, d.P, slot_of_dev, slot_ids)
+        M.moe_permute(dS, slot_ids, sb.sorted_pair, sb.offsets, sb.pair_pos)
+        M.moe_expert_ffn(dS, dev_slots, shared, x, sb.sorted_pair, sb.offsets, sb.y_pairs, sb.y_shared, sb.ws)
+        M.moe_combine(dS, sb.y_pairs, sb.topk_w, sb.pair_pos, sb.y_shared, None, sb.out, None)
+        torch.cuda.synchronize()
+        assert torch.equal(sb.out.view(torch.int32), ref.view(torch.int32)), f"step {step}"
+    hits, misses = bank.stats()
+    say("slot bank hits", hits, "misses", misses)
+    assert hits > 0 and misses > S
+
+
+def host_t(t):
+    return t.detach().cpu().numpy()
