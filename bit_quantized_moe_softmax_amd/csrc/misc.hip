@@ -11,8 +11,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y_pairs, const float* __restrict__ w,
     const int32_t* __restrict__ pair_pos, const float* __restrict__ y_shared,
     const float* residual, float* out, uint16_t* __restrict__ out_bf16, int H, int k) {
-  const int t = blockIdx.y;
-  const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int t = blockIdx.x;   // tokens on x: the other grid dimensions stop at 65535
+  const int h = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (h >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (y_shared) acc = *reinterpret_cast<const float4*>(y_shared + (size_t)t * H + h);
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void stq1_encode_kernel(const float* __restric
 hipError_t moe_launch_combine(const float* y_pairs, const float* w, const int32_t* pair_pos,
                               const float* y_shared, const float* residual, float* out,
                               uint16_t* out_bf16, int T, int H, int k, hipStream_t s) {
-  dim3 grid((H / 4 + 255) / 256, T);
+  dim3 grid(T, (H / 4 + 255) / 256);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y_pairs, w, pair_pos, y_shared,
                      residual, out, out_bf16, H, k);
   return hipGetLastError();

@@ -65,6 +65,36 @@ bool shared_gemm_ok(const moe_dims* d) {
   return d->T >= prefill_min_t(true) && d->H % 256 == 0 && d->I % 256 == 0;
 }
 
+// Size limits of moe_expert_ffn.  The grouped GEMMs address each activation operand through
+// a buffer resource with 32-bit offsets, and an offset of 2^31 or more marks an absent row,
+// so every operand stays within 2^31 bytes: x and h, in the GEMM's input format, per family
+// (routed STQ1_0: x fp16 [T][H], h fp16 hi | lo [P][2I]; routed MXFP4: x and h E4M3 [T][H],
+// [P][I]; shared bf16 or MXFP8: x bf16 [T][H], h two bf16 [T][2I]).  The decode-shaped kernels
+// put token tiles of 8 (the generic STQ1_0 one: single tokens) on a grid dimension that stops
+// at 65535.
+constexpr int64_t kMaxOperand = (int64_t)1 << 31;
+constexpr int64_t kMaxGridYZ = 65535;
+bool ffn_size_ok(const moe_dims* d, int fmt, const moe_experts* shared) {
+  const int64_t T = d->T, H = d->H, I = d->I, P = T * d->k;
+  if (fmt == MOE_W_STQ1_0) {
+    if (stq_gemm_ok(d)) {
+      if (T * H * 2 > kMaxOperand || P * I * 4 > kMaxOperand) return false;
+    } else if (T > ((H % 256 || I % 256) ? kMaxGridYZ : 8 * kMaxGridYZ)) {
+      return false;
+    }
+  } else if (T * H > kMaxOperand || P * I > kMaxOperand) {
+    return false;
+  }
+  if (shared) {
+    if (shared->fmt == MOE_W_MXFP8 || shared_gemm_ok(d)) {
+      if (T * H * 2 > kMaxOperand || T * I * 4 > kMaxOperand) return false;
+    } else if (T > 8 * kMaxGridYZ) {
+      return false;
+    }
+  }
+  return true;
+}
+
 // Workspace regions: 0 h routed f32, 1 h shared f32, 2 xq, 3 xs, 4 hq, 5 hs, 6 total;
 // internal regions of the prefill GEMMs (ext): 0 x fp16 [T][H], 1 x row exponents [T],
 // 2 h as fp16 hi | lo [P][2I], 3 h row exponents [P], 4 shared h as bf16 hi | lo [T][2I]
@@ -206,6 +236,8 @@ moe_status moe_route(const moe_dims* d, const uint16_t* x_bf16, const uint16_t* 
                      int32_t* topk_ids, float* topk_w, void* stream) {
   if (!dims_ok(d) || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!logits_in && (!x_bf16 || !wr_bf16 || !logits_out)) return MOE_ERR_INVALID_ARG;
+  // the logits GEMV puts 8-token tiles on a grid dimension that stops at 65535
+  if (!logits_in && d->T > 8 * kMaxGridYZ) return MOE_ERR_UNSUPPORTED;
   if (d->T == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
   if (!logits_in) {
@@ -271,6 +303,7 @@ moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
       return MOE_ERR_INVALID_ARG;
     if (d->H % 256 || d->I % 256) return MOE_ERR_UNSUPPORTED;
   }
+  if (!ffn_size_ok(d, fmt, shared)) return MOE_ERR_UNSUPPORTED;
   const int T = d->T, H = d->H, I = d->I, E = d->E, k = d->k;
   if (fmt == MOE_W_STQ1_0) {
     if (((int64_t)H * I) % 256) return MOE_ERR_UNSUPPORTED;

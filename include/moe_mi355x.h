@@ -147,7 +147,8 @@ MOE_MI355X_API moe_status moe_profile_read(double* avg_us, int64_t* count);
  * no routing function; this library takes softmax over all experts, keeps the top
  * k and renormalises, i.e. topk_w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)
  * over the selected slots.  Slots are ordered by descending logit, ties to the
- * lower expert index.
+ * lower expert index.  Without logits_in, T is at most 524280 (MOE_ERR_UNSUPPORTED
+ * past it).
  *   x_bf16      [T][H] bf16, ignored when logits_in != NULL
  *   wr_bf16     [E][H] bf16, ignored when logits_in != NULL
  *   logit_bias  [E] fp32 or NULL (added to the logits in both modes)
@@ -217,6 +218,12 @@ MOE_MI355X_API moe_status moe_workspace_offsets(const moe_dims* d, int32_t route
  *   x_bf16 [T][H]; sorted_pair [P]; expert_offsets [E+1] (from moe_permute)
  *   y_pairs [P][H] fp32 out (sorted-pair order); y_shared [T][H] fp32 out or NULL
  *   ws / ws_bytes: device workspace of at least moe_workspace_size bytes.
+ * Size limits (MOE_ERR_UNSUPPORTED past them; split the tokens over several calls):
+ * every activation operand of the grouped GEMMs stays within 2^31 bytes -- routed STQ1_0
+ * 2 T H and 4 P I, routed MXFP4 T H and P I, a shared expert on the GEMMs 2 T H and 4 T I
+ * (at hidden 6144, intermediate 2048, top-8: 32768 tokens for STQ1_0, 131072 for MXFP4,
+ * 174762 for the shared expert); the decode-shaped kernels take up to 524280 tokens (the
+ * generic STQ1_0 kernel, for H or I not a multiple of 256, 65535).
  * ------------------------------------------------------------------------- */
 MOE_MI355X_API moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* routed,
                                          const moe_experts* shared, const uint16_t* x_bf16,

@@ -70,6 +70,31 @@ def _raw(name, *args):
     return getattr(M.lib(), name)(*args)
 
 
+def test_size_limits_hold_at_their_boundaries():
+    """moe_expert_ffn refuses a call whose grouped-GEMM operands pass 2^31 bytes, and moe_route
+    one with more 8-token tiles than a grid dimension holds.  A call just inside a limit stops
+    at the (deliberately short) workspace instead, so nothing is launched."""
+    w = ((1 << 20, 1 << 20),) * 3
+    stq, mx = M.Experts(M.MOE_W_STQ1_0, *w), M.Experts(M.MOE_W_MXFP4, *w)
+    bf = M.Experts(M.MOE_W_BF16, *(((1 << 20, None),) * 3))
+
+    def ffn(T, routed, shared=None, k=8):
+        d = M.Dims(T=T, H=6144, I=2048, E=256, k=k)
+        return _raw("moe_expert_ffn", d.ref(), routed.ref(), shared.ref() if shared else None,
+                    1 << 20, 1 << 20, 1 << 20, 1 << 20, (1 << 20) if shared else None, 1 << 20,
+                    ctypes.c_size_t(16), None)
+
+    # STQ1_0: h as fp16 hi | lo, 4 P I bytes = 2^31 at 32768 tokens
+    assert ffn(32768, stq) == 3 and ffn(32769, stq) == 2
+    # MXFP4: h as E4M3, P I bytes = 2^31 at 131072 tokens
+    assert ffn(131072, mx) == 3 and ffn(131073, mx) == 2
+    # a bf16 shared expert on the GEMMs: x bf16, 2 T H bytes (top-1 keeps the routed side inside)
+    assert ffn(174762, mx, bf, k=1) == 3 and ffn(174763, mx, bf, k=1) == 2
+    d = M.Dims(T=8 * 65535 + 1, H=6144, I=2048, E=256, k=8)
+    assert _raw("moe_route", d.ref(), 1 << 20, 1 << 20, None, None, 1 << 20, 1 << 20, 1 << 20,
+                None) == 2
+
+
 def test_argument_checks_need_no_gpu():
     bad = M.Dims(T=1, H=6144, I=2048, E=256, k=40)          # k > 32
     assert _raw("moe_route", bad.ref(), None, None, None, None, None, None, None, None) == 1

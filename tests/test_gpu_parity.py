@@ -809,6 +809,22 @@ def test_combine_with_residual_and_bf16():
     assert row_err(host(r2), ref).max() <= 1e-6
 
 
+def test_combine_more_tokens_than_a_y_grid_dimension():
+    """70000 tokens, more than the 65535 blocks a y or z grid dimension holds (the combine
+    puts tokens on x)."""
+    g = np.random.default_rng(23)
+    T, H, k = 70000, 64, 2
+    P = T * k
+    yp = g.standard_normal((P, H)).astype(np.float32)
+    w = g.random((T, k)).astype(np.float32)
+    pp = g.permutation(P).astype(np.int32)
+    d = M.Dims(T, H, 256, 16, k)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    M.moe_combine(d, dev(yp), dev(w), dev(pp), None, None, out, None)
+    ref = O.combine(yp, w, pp, None, None)
+    assert row_err(host(out), ref).max() <= 1e-6
+
+
 def test_chain_cfg4_hy4_29_layers_sampled():
     """29 STQ1_0 Hy4 layers at 16 tokens with Zipf-skewed routing, chained through
     pre-norm residual adds: a = bf16(RMSNorm(r)), r <- r + MoE(a).  Two sampled tokens are
