@@ -7,10 +7,12 @@
 //
 // Per step the host plans (moe_slot_bank_plan): the step's distinct experts that are resident
 // are hits; each miss takes an empty slot, else the least recently used slot that no expert of
-// this step holds (lowest slot on ties).  moe_slot_bank_fetch enqueues the planned copies
-// (every family buffer of a missing expert, cut into io_split chunks) on the caller's stream,
-// and moe_remap_ids turns the routed expert ids into slot ids on the device, so the unchanged
-// permute / expert FFN / combine calls run on the S slots as S experts.
+// this step holds (lowest slot on ties).  moe_slot_bank_fetch enqueues every planned copy not
+// yet fetched (every family buffer of a missing expert, cut into io_split chunks) on the
+// caller's stream, so a plan made twice, or a fetch that failed, loses no copy (a copy whose
+// slot a later plan reuses is dropped).  moe_remap_ids turns the routed expert ids into slot
+// ids on the device, so the unchanged permute / expert FFN / combine calls run on the S slots
+// as S experts.
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -24,7 +26,7 @@ struct moe_slot_bank {
   std::vector<int> slot_of;                  // [E] slot of each expert, -1 if not resident
   std::vector<int> expert_in;                // [S] expert in each slot, -1 if empty
   std::vector<uint64_t> last_use;            // [S] step of the last use
-  std::vector<std::pair<int, int>> pending;  // (expert, slot) copies of the last plan
+  std::vector<std::pair<int, int>> pending;  // (expert, slot) copies planned, not yet fetched
   uint64_t step = 0, hits = 0, misses = 0;
 };
 
@@ -83,8 +85,8 @@ moe_status moe_slot_bank_plan(moe_slot_bank* b, const int32_t* ids, int64_t n, i
     }
   }
   if ((int)distinct.size() > b->S) return MOE_ERR_UNSUPPORTED;   // more experts than slots
+  const uint64_t misses0 = b->misses;
   ++b->step;
-  b->pending.clear();
   for (int e : distinct)
     if (b->slot_of[e] >= 0) {
       b->last_use[b->slot_of[e]] = b->step;
@@ -100,6 +102,10 @@ moe_status moe_slot_bank_plan(moe_slot_bank* b, const int32_t* ids, int64_t n, i
         if (b->last_use[s] < b->step && (victim < 0 || b->last_use[s] < b->last_use[victim])) victim = s;
     // a victim always exists: at most S distinct experts use this step's slots
     if (b->expert_in[victim] >= 0) b->slot_of[b->expert_in[victim]] = -1;
+    // a copy into this slot planned earlier and never fetched is superseded
+    b->pending.erase(std::remove_if(b->pending.begin(), b->pending.end(),
+                                    [victim](const std::pair<int, int>& c) { return c.second == victim; }),
+                     b->pending.end());
     b->expert_in[victim] = e;
     b->slot_of[e] = victim;
     b->last_use[victim] = b->step;
@@ -107,7 +113,7 @@ moe_status moe_slot_bank_plan(moe_slot_bank* b, const int32_t* ids, int64_t n, i
     ++b->misses;
   }
   std::copy(b->slot_of.begin(), b->slot_of.end(), slot_of);
-  *n_copies = (int32_t)b->pending.size();
+  *n_copies = (int32_t)(b->misses - misses0);
   return MOE_OK;
 }
 

@@ -330,10 +330,13 @@ MOE_MI355X_API moe_status moe_stq1_encode(const float* x, const float* imatrix, 
  *   1. moe_slot_bank_plan (host only): the step's expert ids (host array, e.g. topk_ids
  *      copied back) -> slot_of[E] (slot of every resident expert, -1 otherwise).  Resident
  *      experts are hits; each miss takes an empty slot, else the least recently used slot
- *      that no expert of this step holds (lowest slot on ties).  MOE_ERR_UNSUPPORTED when the
- *      step has more distinct experts than slots (state unchanged).
- *   2. moe_slot_bank_fetch: enqueue the planned copies (every non-empty family buffer of each
- *      missing expert, in io_split chunks) host -> device on `stream`.
+ *      that no expert of this step holds (lowest slot on ties).  n_copies: the step's misses.
+ *      MOE_ERR_UNSUPPORTED when the step has more distinct experts than slots (state
+ *      unchanged).
+ *   2. moe_slot_bank_fetch: enqueue every planned copy not yet fetched (every non-empty family
+ *      buffer of each missing expert, in io_split chunks) host -> device on `stream`.  Copies
+ *      of a plan that was not followed by a fetch, or of a fetch that returned an error, stay
+ *      pending until a fetch succeeds, unless a later plan gave their slot to another expert.
  *   3. moe_remap_ids: topk_ids -> slot ids on the device (slot_of uploaded by the caller), then
  *      moe_permute / moe_expert_ffn with E = S on the slot arrays, and moe_combine as usual.
  * bytes[6]: per-expert bytes of gate codes, gate scales, up codes, up scales, down codes,

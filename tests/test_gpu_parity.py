@@ -1098,7 +1098,8 @@ def test_slot_bank_layer_equals_direct():
     """A layer whose 16 routed experts live in pinned host memory and run from an 8-slot
     device bank (plan, chunked fetch, id remap, then permute / FFN / combine over the slots)
     gives the same bits as the layer run on all 16 experts in device memory, step after step
-    with new tokens (hits and misses both occur)."""
+    with new tokens (hits and misses both occur), also when a step is planned twice before its
+    fetch."""
     E, S = 16, 8
     c = synth.LayerCfg("sb", 4, 512, 256, E, 2, True, "stq1", False, False, 1, 81)
     inp = layer_inputs(c)
@@ -1127,6 +1128,11 @@ def test_slot_bank_layer_equals_direct():
         ref = run_layer(d, ref_bufs, x, routed, shared, wr_bf16=wr)
         M.moe_route(d, x, wr, None, None, sb.logits, sb.topk_ids, sb.topk_w)
         slot_of, n_copies = bank.plan(host_t(sb.topk_ids))
+        if step % 2:
+            # planned again before the fetch: all hits now, and the first plan's copies must
+            # still be fetched
+            again, n2 = bank.plan(host_t(sb.topk_ids))
+            assert n2 == 0 and (again == slot_of).all()
         slot_of_dev.copy_(torch.from_numpy(slot_of))
         bank.fetch(host_src, dev_slots, torch.cuda.current_stream().cuda_stream)
         M.moe_remap_ids(sb.topk_ids, d.P, slot_of_dev, slot_ids)

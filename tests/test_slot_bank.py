@@ -76,3 +76,14 @@ def test_slot_bank_argument_checks():
         bank.plan(np.array([8], dtype=np.int32))   # expert id out of range
     slot_of, n = bank.plan(np.array([], dtype=np.int32))
     assert n == 0 and (slot_of == -1).all()
+
+
+def test_slot_bank_plan_again_before_fetch_is_all_hits():
+    """A step planned twice before its fetch: the second plan finds every expert resident,
+    makes no copy of its own and keeps the slots (the first plan's copies stay pending)."""
+    bank = M.SlotBank(16, 8, [100, 4, 100, 4, 100, 4])
+    ids = np.array([3, 9, 3, 12], dtype=np.int32)
+    slot_of, n = bank.plan(ids)
+    again, n2 = bank.plan(ids)
+    assert n == 3 and n2 == 0 and (again == slot_of).all()
+    assert bank.stats() == (3, 3)
