@@ -519,8 +519,8 @@ moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
   if (!dims_ok(d) || !routed || !x_bf16 || !wr_bf16 || !logits_out || !topk_ids || !topk_w ||
       !sorted_pair || !expert_offsets || !pair_pos || !y_pairs || !out_f32)
     return MOE_ERR_INVALID_ARG;
+  if (!routed_fmt_ok(routed->fmt)) return MOE_ERR_INVALID_ARG;   // as moe_expert_ffn
   const bool mx = routed->fmt == MOE_W_MXFP4 || routed->fmt == MOE_W_MXFP4_TILED;
-  if (routed->fmt != MOE_W_STQ1_0 && !mx) return MOE_ERR_UNSUPPORTED;
   if (mx && !moe_decode_mx_ok(d->T, d->I, d->k)) return MOE_ERR_UNSUPPORTED;
   if (!mat_ok(routed->gate, true) || !mat_ok(routed->up, true) || !mat_ok(routed->down, true))
     return MOE_ERR_INVALID_ARG;

@@ -162,6 +162,11 @@ def test_new_entry_point_checks_need_no_gpu():
     assert _raw("moe_layer_decode", d5.ref(), mx.ref(), None, *args) == 2
     d4 = M.Dims(T=4, H=6144, I=2048, E=256, k=32)                   # FP8 h of 128 pairs: too big
     assert _raw("moe_layer_decode", d4.ref(), mx.ref(), None, *args) == 2
+    # a routed format that is no routed format at all is an invalid argument, in both calls
+    bad = M.Experts(M.MOE_W_BF16, (F, F), (F, F), (F, F))
+    assert _raw("moe_layer_decode", d.ref(), bad.ref(), None, *args) == 1
+    assert _raw("moe_expert_ffn", d.ref(), bad.ref(), None, F, F, F, F, None, F,
+                ctypes.c_size_t(1 << 30), None) == 1
     offs = M.moe_layer_decode_workspace_offsets(d, True)
     assert offs[10] == M.moe_layer_decode_workspace_size(d, True)
     assert offs[9] >= offs[8] and offs[10] - offs[9] >= d.T * (d.H + d.H // 32)
