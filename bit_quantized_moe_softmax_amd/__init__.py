@@ -17,6 +17,7 @@ __all__ = [
     "COUNTER_NAMES", "moe_status_str", "moe_version", "moe_get_counters", "moe_reset_counters",
     "moe_route", "moe_permute", "moe_workspace_size", "moe_workspace_offsets", "moe_expert_ffn",
     "moe_combine", "moe_stq1_pack", "moe_stq1_dequant", "moe_mxfp4_dequant", "moe_mx_quant_act",
+    "moe_mx_quant_f32_hwcvt",
     "moe_rmsnorm_bf16", "moe_layer_decode_workspace_size", "moe_layer_decode_workspace_offsets",
     "moe_layer_decode", "moe_stq1_encode", "SlotBank", "moe_remap_ids", "MOE_STQ1_ENC_UPSTREAM", "MOE_STQ1_ENC_WLS",
     "moe_profile_enable", "moe_profile_read", "PROFILE_SLOTS",
@@ -70,6 +71,7 @@ _SIGS = {
     "moe_mxfp4_dequant": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
     "moe_mxfp4_pack_tiles": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
     "moe_mx_quant_act": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P]),
+    "moe_mx_quant_f32_hwcvt": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]),
     "moe_rmsnorm_bf16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
     "moe_layer_decode_workspace_size": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "moe_layer_decode_workspace_offsets": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
@@ -233,6 +235,10 @@ def moe_mxfp4_pack_tiles(codes, scales, rows, K, tcodes, tscales, stream=None):
 def moe_mx_quant_act(rows, K, x_bf16, x_f32, q, s, stream=None):
     _check(lib().moe_mx_quant_act(int(rows), int(K), _ptr(x_bf16), _ptr(x_f32), _ptr(q), _ptr(s),
                                   _stream(stream)))
+
+
+def moe_mx_quant_f32_hwcvt(rows, K, x_f32, q, s, stream=None):
+    _check(lib().moe_mx_quant_f32_hwcvt(int(rows), int(K), _ptr(x_f32), _ptr(q), _ptr(s), _stream(stream)))
 
 
 def moe_rmsnorm_bf16(T, H, eps, r, a, stream=None):

@@ -568,8 +568,10 @@ __device__ __forceinline__ void topk_load(const DecodeArgs& a, int t, TopkIn& in
 }
 
 // Order-preserving unsigned key of a float (larger float -> larger key, -0 as +0; every
-// finite or infinite value maps above 0) and its inverse.
+// finite or infinite value maps above 0; every NaN takes the largest key, so NaN ranks
+// above every number and all NaNs tie) and its inverse (a NaN key gives a NaN).
 __device__ __forceinline__ uint32_t fkey(float f) {
+  if (f != f) return 0xFFFFFFFFu;
   uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }

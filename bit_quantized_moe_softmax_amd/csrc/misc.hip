@@ -6,7 +6,8 @@ namespace {
 // ---------------------------------------------------------------- combine
 // out[t] = y_shared[t] + sum_j w[t][j] * y_pairs[pair_pos[t*k+j]] (+ residual[t]).
 // The shared expert is ungated: the Flash-MoE package lists one shared expert per MoE
-// block and no gate for it.  One thread per 4 consecutive hidden elements.
+// block and no gate for it.  One thread per 4 consecutive hidden elements.  A pair with
+// pair_pos -1 (not routed by moe_permute) contributes nothing.
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y_pairs, const float* __restrict__ w,
     const int32_t* __restrict__ pair_pos, const float* __restrict__ y_shared,
@@ -19,6 +20,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
     const int pos = pair_pos[(size_t)t * k + j];
+    if (pos < 0) continue;   // a pair moe_permute left unrouted adds nothing
     const float4 y = *reinterpret_cast<const float4*>(y_pairs + (size_t)pos * H + h);
     acc.x = fmaf(wj, y.x, acc.x);
     acc.y = fmaf(wj, y.y, acc.y);
@@ -153,6 +155,37 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(int64_t n8, const uint16_
   if (i < n8) {
     reinterpret_cast<uint2*>(q)[i] = make_uint2(codes[0], codes[1]);
     if ((i & 3) == 0) sc[i / 4] = (uint8_t)s;
+  }
+}
+
+// The MX quantisation of fp32 rows with every E4M3 code from the scaled hardware conversion
+// (moe_e4m3_pair_hw, the encoder of the MXFP4 gate/up epilogue) in place of moe_e4m3_code:
+// the same group exponent and the same output layout as mx_quant_kernel.
+__global__ __launch_bounds__(256) void mx_quant_hw_kernel(int64_t n8, const float* xf,
+                                                          uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ sc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t j = i < n8 ? i : n8 - 1;
+  const uint4 v0 = reinterpret_cast<const uint4*>(xf)[2 * j];
+  const uint4 v1 = reinterpret_cast<const uint4*>(xf)[2 * j + 1];
+  const uint32_t bits[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t am = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am = max(am, bits[e] & 0x7FFFFFFFu);
+  am = max(am, (uint32_t)__shfl_xor((int)am, 1, 64));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 2, 64));
+  uint32_t c[2] = {0u, 0u};
+  const int X = am ? moe_mx_exp(am) : -127;
+  if (am) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const float* f = reinterpret_cast<const float*>(bits + 4 * w);
+      c[w] = moe_e4m3_pair_hw(f[0], f[1], X) | (moe_e4m3_pair_hw(f[2], f[3], X) << 16);
+    }
+  }
+  if (i < n8) {
+    reinterpret_cast<uint2*>(q)[i] = make_uint2(c[0], c[1]);
+    if ((i & 3) == 0) sc[i / 4] = am ? (uint8_t)(X + 127) : (uint8_t)0;
   }
 }
 
@@ -311,6 +344,16 @@ hipError_t moe_launch_mx_quant(int64_t rows, int K, const uint16_t* xb, const fl
   if ((n8 + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, n8,
                      xb, xf, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t moe_launch_mx_quant_hw(int64_t rows, int K, const float* xf, uint8_t* q, uint8_t* sc,
+                                  hipStream_t s) {
+  const int64_t n8 = rows * K / 8;
+  if (n8 == 0) return hipSuccess;
+  if ((n8 + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_quant_hw_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, n8,
+                     xf, q, sc);
   return hipGetLastError();
 }
 

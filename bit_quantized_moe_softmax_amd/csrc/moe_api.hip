@@ -630,6 +630,16 @@ moe_status moe_mx_quant_act(int64_t rows, int32_t K, const uint16_t* x_bf16, con
   return finish(moe_launch_mx_quant(rows, K, x_bf16, x_f32, q, sc, s), s);
 }
 
+moe_status moe_mx_quant_f32_hwcvt(int64_t rows, int32_t K, const float* x_f32, uint8_t* q,
+                                  uint8_t* sc, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!x_f32 || !q || !sc)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if ((rows * (int64_t)K / 8 + 255) / 256 > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  return finish(moe_launch_mx_quant_hw(rows, K, x_f32, q, sc, s), s);
+}
+
 moe_status moe_rmsnorm_bf16(int32_t T, int32_t H, float eps, const float* r, uint16_t* a,
                             void* stream) {
   if (T < 0 || H <= 0 || (T > 0 && (!r || !a)) || !(eps >= 0.f)) return MOE_ERR_INVALID_ARG;

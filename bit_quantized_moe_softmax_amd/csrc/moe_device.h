@@ -102,6 +102,20 @@ __device__ __forceinline__ uint32_t moe_e4m3_code(float v, int X) {
   return sign | code;
 }
 
+// Two values to E4M3 codes at MX exponent X (bytes 0 and 1 of the result) with the gfx950
+// scaled hardware conversion, which divides by the scale 2^X and rounds to nearest even.
+// Inputs are clamped to +-448 2^X first: past it the conversion gives the NaN code where the
+// MX rule saturates.  Meant to equal moe_e4m3_code on each value for every exponent the MX
+// rule produces (-127 .. 119) and |v| < 2^(X+9); moe_mx_quant_f32_hwcvt exposes it so that
+// this can be checked against the integer rule on chosen values.
+__device__ __forceinline__ uint32_t moe_e4m3_pair_hw(float a, float b, int X) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const float lim = ldexpf(448.0f, X);
+  const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s){0, 0}, fminf(fmaxf(a, -lim), lim),
+                                                         fminf(fmaxf(b, -lim), lim), ldexpf(1.0f, X), false);
+  return (uint16_t)r.x;
+}
+
 // Lane-parallel MX quantisation of 8 consecutive values per lane (fp32 bit patterns,
 // finite): lanes 4q .. 4q + 3 of the wave hold the 32 values of one group.  Writes this
 // lane's 8 E4M3 codes (element j in byte j % 4 of word j / 4) and returns the group's UE8M0
@@ -198,6 +212,8 @@ hipError_t moe_launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales,
                                     int K, float* out, hipStream_t s);
 hipError_t moe_launch_mx_quant(int64_t rows, int K, const uint16_t* xb, const float* xf,
                                uint8_t* q, uint8_t* sc, hipStream_t s);
+hipError_t moe_launch_mx_quant_hw(int64_t rows, int K, const float* xf, uint8_t* q, uint8_t* sc,
+                                  hipStream_t s);
 
 // Decode-regime FFN (routed STQ1_0 and shared bf16) on the bf16 MFMA.
 // kind: 0 routed gate/up, 1 routed down, 2 shared gate/up, 3 shared down.

@@ -6,6 +6,10 @@
 // chunks of 1024 pairs where each pair's rank among equal experts comes from wave
 // ballots (same-expert lanes found bit by bit) plus per-wave counts in LDS -- the
 // output order is fixed by the pair index, never by atomics.
+// A pair whose expert id lies outside [0, E) (an expert with no slot, or a corrupted id) is
+// not routed: it gets pair_pos -1, takes no sorted position (offsets[E] counts only the
+// routed pairs), and sorted_pair is -1 from offsets[E] on.  No id is used as an index
+// before that check.
 #include "moe_device.h"
 
 namespace {
@@ -22,6 +26,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
   __shared__ int s_cnt[kMaxE];
   __shared__ int s_base[kMaxE];
   __shared__ int s_wsum[kWaves];
+  __shared__ int s_routed;
   __shared__ uint8_t s_wc[kWaves][kMaxE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -29,7 +34,10 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
 
   for (int e = tid; e < E; e += kThreads) s_cnt[e] = 0;
   __syncthreads();
-  for (int f = tid; f < P; f += kThreads) atomicAdd(&s_cnt[ids[f]], 1);
+  for (int f = tid; f < P; f += kThreads) {
+    const int e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  }
   __syncthreads();
 
   // exclusive scan of s_cnt[0..E) (E <= 1024: one value per thread)
@@ -50,9 +58,13 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
       s_base[tid] = excl;
       offsets[tid] = excl;
     }
-    if (tid == 0) offsets[E] = P;
+    if (tid == E - 1) {
+      offsets[E] = excl + c;
+      s_routed = excl + c;
+    }
   }
   __syncthreads();
+  for (int pos = s_routed + tid; pos < P; pos += kThreads) sorted_pair[pos] = -1;
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int c0 = 0; c0 < P; c0 += kThreads) {
@@ -60,8 +72,9 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     for (int i = tid; i < kWaves * E; i += kThreads) s_wc[i / E][i % E] = 0;
     __syncthreads();
     const int f = c0 + tid;
-    const bool valid = f < P;
-    const int e = valid ? ids[f] : 0;
+    const int ef = f < P ? ids[f] : -1;
+    const bool valid = ef >= 0 && ef < E;
+    const int e = valid ? ef : 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -77,6 +90,8 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
       const int pos = s_base[e] + pre + rank;
       sorted_pair[pos] = f;
       pair_pos[f] = pos;
+    } else if (f < P) {
+      pair_pos[f] = -1;
     }
     __syncthreads();
     for (int e2 = tid; e2 < E; e2 += kThreads) {

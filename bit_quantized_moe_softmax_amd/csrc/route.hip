@@ -65,8 +65,17 @@ __global__ __launch_bounds__(256) void route_gemv_kernel(const uint16_t* __restr
 
 constexpr int kMaxPerLane = 16;   // E <= 1024
 
-// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a wave arg-max
-// over (value, -index) pick the slots in descending order, ties to the lower index.
+// Order-preserving unsigned key of a logit: a larger value gives a larger key, -0 keys as
+// +0, and every NaN takes the largest key (NaN ranks above every number, all NaNs equal),
+// so the selection is a total order and every pick is a real expert index.
+__device__ __forceinline__ uint32_t logit_key(float f) {
+  if (f != f) return 0xFFFFFFFFu;
+  const uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a wave arg-max over
+// (key, -index) pick the slots in descending order, ties to the lower index.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    const float* __restrict__ bias,
                                                    float* __restrict__ logits_out, int T,
@@ -77,19 +86,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;
   const int nper = (E + 63) >> 6;
   float v[kMaxPerLane];
+  uint32_t key[kMaxPerLane];
   const float* row = logits + (size_t)t * E;
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = i * 64 + lane;
-    float val = -INFINITY;
+    float val = 0.f;
     if (i < nper && e < E) {
       val = row[e];
       if (bias) val += bias[e];
       if (logits_out) logits_out[(size_t)t * E + e] = val;
     }
     v[i] = val;
+    key[i] = logit_key(val);
   }
-  uint32_t taken = 0;
   // a lane slot is "live" when it maps to a real expert and has not been taken yet
   uint32_t live = 0;
 #pragma unroll
@@ -98,22 +108,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   float my_v = 0.f;
   int my_i = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    // candidate = (key << 32) | (~index): the largest is the largest key, then the lowest
+    // index; a lane with nothing live offers 0, below every real candidate
+    uint64_t best = 0;
+    float bv = 0.f;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
-      if (((live & ~taken) >> i) & 1u) {
-        const int e = i * 64 + lane;
-        if (v[i] > bv || (v[i] == bv && e < bi)) { bv = v[i]; bi = e; }
+      if ((live >> i) & 1u) {
+        const uint64_t c = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(i * 64 + lane);
+        if (c > best) { best = c; bv = v[i]; }
       }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t ob = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), o, 64) << 32) |
+                          (uint32_t)__shfl_xor((int)(uint32_t)best, o, 64);
       const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      if (ob > best) { best = ob; bv = ov; }
     }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const int bi = (int)~(uint32_t)best;
+    if ((bi & 63) == lane) live &= ~(1u << (bi >> 6));
     if (lane == j) { my_v = bv; my_i = bi; }
   }
   const float v0 = __shfl(my_v, 0, 64);

@@ -147,7 +147,9 @@ MOE_MI355X_API moe_status moe_profile_read(double* avg_us, int64_t* count);
  * no routing function; this library takes softmax over all experts, keeps the top
  * k and renormalises, i.e. topk_w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)
  * over the selected slots.  Slots are ordered by descending logit, ties to the
- * lower expert index.  Without logits_in, T is at most 524280 (MOE_ERR_UNSUPPORTED
+ * lower expert index.  A NaN logit ranks above every number and all NaNs tie (a NaN
+ * in x[t] makes the row NaN: experts 0 .. k-1 are selected, with NaN weights), so
+ * every id is in [0, E).  Without logits_in, T is at most 524280 (MOE_ERR_UNSUPPORTED
  * past it).
  *   x_bf16      [T][H] bf16, ignored when logits_in != NULL
  *   wr_bf16     [E][H] bf16, ignored when logits_in != NULL
@@ -167,8 +169,11 @@ MOE_MI355X_API moe_status moe_route(const moe_dims* d, const uint16_t* x_bf16,
  * streams).  Pair f = t*k + j.  expert_offsets[e] = number of pairs with expert
  * below e (expert_offsets[E] = P); within one expert pairs keep increasing f;
  * sorted_pair[pos] = f and pair_pos[f] = pos.  Deterministic (no atomics decide
- * the order).  Any topk_ids value outside [0, E) is an error the kernel cannot
- * report; the caller guarantees the range (moe_route produces it).
+ * the order).  A pair whose id lies outside [0, E) (moe_route never gives one;
+ * moe_remap_ids gives -1 for an expert without a slot) is not routed: pair_pos[f] = -1,
+ * expert_offsets[E] counts only the routed pairs, sorted_pair is -1 from
+ * expert_offsets[E] on, moe_expert_ffn never sees the pair and moe_combine adds
+ * nothing for it.  One workgroup; no workspace.
  *   topk_ids [P] int32; sorted_pair [P], expert_offsets [E+1], pair_pos [P] int32 out
  * ------------------------------------------------------------------------- */
 MOE_MI355X_API moe_status moe_permute(const moe_dims* d, const int32_t* topk_ids,
@@ -234,7 +239,8 @@ MOE_MI355X_API moe_status moe_expert_ffn(const moe_dims* d, const moe_experts* r
 
 /* ---------------------------------------------------------------------------
  * Combine: out[t] = y_shared[t] + sum_j topk_w[t][j] * y_pairs[pair_pos[t*k + j]]
- * (+ residual[t]), summed in that order in fp32.  The shared expert is always on
+ * (+ residual[t]), summed in that order in fp32; a slot with pair_pos -1 (not routed
+ * by moe_permute) adds nothing.  The shared expert is always on
  * and ungated (the Flash-MoE package lists one shared expert per MoE block and no
  * gate for it).
  *   y_pairs [P][H]; topk_w [T][k]; pair_pos [P]; y_shared [T][H] or NULL;
@@ -384,6 +390,15 @@ MOE_MI355X_API moe_status moe_mxfp4_pack_tiles(const uint8_t* codes, const uint8
 MOE_MI355X_API moe_status moe_mx_quant_act(int64_t rows, int32_t K, const uint16_t* x_bf16,
                                            const float* x_f32, uint8_t* q, uint8_t* s,
                                            void* stream);
+
+/* The same MX quantisation of fp32 rows as moe_mx_quant_act (same rule, same outputs), with
+ * every E4M3 code produced by the gfx950 scaled hardware conversion that the MXFP4 gate/up
+ * epilogue uses for h, instead of the integer-rule encoder.  A check point for that
+ * epilogue's encoder on chosen values (rounding ties, the saturating band, zeros, every group
+ * exponent); not a per-step call.  x_f32 [rows][K] (16-byte aligned), q [rows][K] and
+ * s [rows][K/32] out. */
+MOE_MI355X_API moe_status moe_mx_quant_f32_hwcvt(int64_t rows, int32_t K, const float* x_f32,
+                                                 uint8_t* q, uint8_t* s, void* stream);
 
 /* Pre-norm for a residual stack of MoE layers: a[t] = bf16(r[t] / sqrt(mean(r[t]^2) + eps))
  * (norm weight 1), r [T][H] fp32, a [T][H] bf16 out. */

@@ -342,6 +342,10 @@ def route(k: int, x_bits=None, wr_bits=None, bias=None, logits_in=None):
     them -- which equals the softmax over the k selected logits, since the full
     denominator cancels.  Order: descending logit, ties to the lower expert index.
     A per-expert bias, when given, is added to the logits before everything else.
+    A NaN logit (a NaN in the token's activations makes its whole row NaN) has no
+    place in that order; reading: NaN ranks above every number and all NaNs are
+    equal, so a NaN row selects experts 0 .. k-1, and the weights of a selection
+    holding a NaN are NaN.
 
     Returns (logits [T, E] float64, ids [T, k] int32, w [T, k] float64).
     """
@@ -355,7 +359,9 @@ def route(k: int, x_bits=None, wr_bits=None, bias=None, logits_in=None):
     ids = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float64)
     for t in range(T):
-        order = np.lexsort((np.arange(E), -logits[t]))       # by -logit, then index
+        nan = np.isnan(logits[t])
+        # NaN first, then by -logit, then by index (lexsort's last key is the primary one)
+        order = np.lexsort((np.arange(E), np.where(nan, 0.0, -logits[t]), ~nan))
         sel = order[:k]
         ids[t] = sel
         ex = np.exp(logits[t, sel] - logits[t, sel].max())
@@ -369,19 +375,26 @@ def permute(ids, E: int):
     Pair f = t*k + j.  Counting sort: offsets[e] = number of pairs whose expert is
     below e; within one expert, pairs keep increasing f.  sorted_pair[pos] = f and
     pair_pos[f] = pos.  The result is unique.
+
+    A pair whose id is not an expert (outside [0, E): the library's rule for ids it
+    cannot route) takes no position: pair_pos[f] = -1, offsets[E] counts the routed
+    pairs only, and sorted_pair holds -1 from offsets[E] on.
     """
     flat = np.asarray(ids, dtype=np.int64).reshape(-1)
     P = flat.size
     counts = np.zeros(E, dtype=np.int64)
     for f in range(P):
-        counts[flat[f]] += 1
+        if 0 <= flat[f] < E:
+            counts[flat[f]] += 1
     offsets = np.zeros(E + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
     fill = offsets[:-1].copy()
-    sorted_pair = np.empty(P, dtype=np.int64)
-    pair_pos = np.empty(P, dtype=np.int64)
+    sorted_pair = np.full(P, -1, dtype=np.int64)
+    pair_pos = np.full(P, -1, dtype=np.int64)
     for f in range(P):
         e = flat[f]
+        if not 0 <= e < E:
+            continue
         sorted_pair[fill[e]] = f
         pair_pos[f] = fill[e]
         fill[e] += 1
@@ -464,13 +477,15 @@ def shared_expert_mxfp8(x_bits, wg, wu, wd):
 def combine(y_pairs, w, pair_pos, y_shared=None, residual=None):
     """out[t] = y_shared[t] + sum_j w[t, j] * y_pairs[pair_pos[t*k + j]] (+ residual).
 
-    The pages show no gate on the shared expert, so it is added unweighted."""
+    The pages show no gate on the shared expert, so it is added unweighted.  A pair
+    that permute left unrouted (pair_pos -1) adds nothing."""
     T, k = w.shape
     H = y_pairs.shape[1]
     out = np.zeros((T, H)) if y_shared is None else np.array(y_shared, dtype=np.float64)
     for t in range(T):
         for j in range(k):
-            out[t] += w[t, j] * y_pairs[pair_pos[t * k + j]]
+            if pair_pos[t * k + j] >= 0:
+                out[t] += w[t, j] * y_pairs[pair_pos[t * k + j]]
     if residual is not None:
         out = out + residual
     return out

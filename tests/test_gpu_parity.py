@@ -5,6 +5,7 @@ top-k ids and slot order from given logits, the permutation.  Tolerance (max |er
 RMS of the reference row <= 2e-3): expert outputs and the combined layer output.
 Where floating point decides an integer (top-k from x-computed logits, the FP8 codes of
 h) near-ties are allowed to differ and are counted instead."""
+import math
 import sys
 
 import numpy as np
@@ -344,11 +345,56 @@ def test_layer_stq_prefill_gemm(name):
             assert es <= TOL
 
 
+def _stq_rows(codes_e, scales_e, K, rows):
+    """Rows `rows` of one STQ1_0 matrix with K columns (each row is K/256 whole blocks)."""
+    nb = K // 256
+    c = np.concatenate([codes_e[r * nb * 40:(r + 1) * nb * 40] for r in rows])
+    sc = np.concatenate([scales_e[r * nb:(r + 1) * nb] for r in rows])
+    return O.stq1_decode(c, sc).reshape(len(rows), K)
+
+
+def _mx_rows(codes_e, scales_e, K, rows):
+    """Rows `rows` of one row-major MXFP4 matrix with K columns."""
+    rows = np.asarray(rows)
+    return O.mxfp4_matrix(codes_e[rows], scales_e[rows], len(rows), K)
+
+
+def _expert_samples(c, off, seed):
+    """For every expert with pairs: its first and last pair (the first and last M block of a
+    split expert), two h groups of 32 columns from different gate/up N tiles (128 columns
+    each), and one output row from each down N tile (256 rows each)."""
+    g = np.random.default_rng(seed)
+    out = []
+    n_ht = c.I // 128
+    for e in range(c.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        poss = sorted({lo, hi - 1})
+        t0, t1 = g.choice(n_ht, 2, replace=False) if n_ht > 1 else (0, 0)
+        grp = [4 * t0 + int(g.integers(4)), 4 * t1 + int(g.integers(4))]
+        if grp[0] == grp[1]:
+            grp[1] = (grp[1] + 1) % (c.I // 32)
+        hcols = np.concatenate([np.arange(32 * q, 32 * q + 32) for q in grp])
+        orow = np.array([256 * t + int(g.integers(256)) for t in range(c.H // 256)])
+        out.append((e, poss, grp, hcols, orow))
+    return out
+
+
+def _sampled_err(got, ref):
+    """max |got - ref| / RMS(ref) over a sample of one row's entries."""
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = math.sqrt(float((ref * ref).mean()))
+    return float(np.abs(np.asarray(got, dtype=np.float64) - ref).max()) / max(rms, 1e-300)
+
+
 def test_stq_prefill_hy4_t4096_sampled():
     """Hy4-shaped STQ1_0 layer at 4096 tokens (256 experts, top-8, bf16 shared expert) on the
-    prefill GEMMs: routing and permutation in full; h and the down projection on the experts
-    with the most and the fewest pairs and one more; shared expert and combined output on
-    sampled tokens."""
+    prefill GEMMs: routing and permutation in full; on EVERY expert, the first and last pair
+    (both M blocks of a split expert): h on two 32-column groups from different N tiles
+    against the oracle, and the down projection of the GPU's h on one output row per N tile;
+    the combined output of sampled tokens against the oracle's own layer (its h, its y_pairs,
+    its shared expert)."""
     c = synth.LayerCfg("hy4-stq1-prefill-t4096", 4096, 6144, 2048, 256, 8, True, "stq1", False, True, 1, 31)
     say("stq prefill t4096 generate")
     inp = layer_inputs(c)
@@ -366,32 +412,37 @@ def test_stq_prefill_hy4_t4096_sampled():
     rsp, roff, rpp = O.permute(rid, c.E)
     assert (host(bufs.sorted_pair) == rsp).all() and (host(bufs.offsets) == roff).all()
     assert (host(bufs.pair_pos) == rpp).all()
-    n = np.diff(roff)
-    pick = [int(np.argmax(n)), int(np.argmin(np.where(n > 0, n, 1 << 30))),
-            int(synth.sample_tokens(c.seed, c.E, 1)[0])]
-    say("stq prefill t4096 experts", pick, "pairs", [int(n[e]) for e in pick])
     offs = M.moe_workspace_offsets(d, M.MOE_W_STQ1_0, True)
     P = d.P
     h_gpu = host(bufs.ws[offs[0]:offs[0] + P * c.I * 4]).view(np.float32).reshape(P, c.I)
     yp = host(bufs.y_pairs)
-    get_w = oracle_weights(c, inp["routed"])
     xf = O.bf16_to_f64(inp["x"])
-    for e in pick:
-        lo, hi = int(roff[e]), int(roff[e + 1])
-        if hi == lo:
-            continue
-        a = xf[rsp[lo:hi] // c.k]
-        h = O.silu(a @ get_w(e, 0).T) * (a @ get_w(e, 1).T)
-        eh = row_err(h_gpu[lo:hi], h).max()
-        ey = row_err(yp[lo:hi], h @ get_w(e, 2).T).max()
-        say("expert", e, "h max row err", float(eh), "y max row err", float(ey))
-        assert eh <= TOL and ey <= TOL
-    toks = synth.sample_tokens(c.seed, c.T, 4)
+    (gc, gs), (uc, us), (dc, ds) = inp["routed"]
+    worst_h = worst_y = 0.0
+    samples = _expert_samples(c, roff, 131)
+    for e, poss, grp, hcols, orow in samples:
+        a = xf[rsp[poss] // c.k]
+        h = O.silu(a @ _stq_rows(gc[e], gs[e], c.H, hcols).T) * (a @ _stq_rows(uc[e], us[e], c.H, hcols).T)
+        Wd = _stq_rows(dc[e], ds[e], c.I, orow)
+        for i, pos in enumerate(poss):
+            worst_h = max(worst_h, _sampled_err(h_gpu[pos, hcols], h[i]))
+            worst_y = max(worst_y, _sampled_err(yp[pos, orow], Wd @ h_gpu[pos].astype(np.float64)))
+    say("stq prefill t4096:", len(samples), "experts checked, h max err", worst_h, "down max err", worst_y)
+    assert len(samples) == int((np.diff(roff) > 0).sum())
+    assert worst_h <= TOL and worst_y <= TOL
+    # two sampled tokens through the oracle's own layer (independent of every GPU stage)
+    toks = synth.sample_tokens(c.seed, c.T, 2)
+    get_w = oracle_weights(c, inp["routed"])
     ysh = O.shared_expert(inp["x"][toks], *inp["shared"])
     assert row_err(host(bufs.y_shared)[toks], ysh).max() <= TOL
-    out_ref = O.combine(yp, rw, rpp, host(bufs.y_shared))
-    err = row_err(host(bufs.out)[toks], out_ref[toks])
-    say("stq prefill t4096 combine max row err on sampled tokens", float(err.max()))
+    out_ref = ysh.copy()
+    for i, t in enumerate(toks):
+        for j in range(c.k):
+            e = int(rid[t, j])
+            _, y = O.swiglu_expert(xf[t:t + 1], get_w(e, 0), get_w(e, 1), get_w(e, 2))
+            out_ref[i] += rw[t, j] * y[0]
+    err = row_err(host(bufs.out)[toks], out_ref)
+    say("stq prefill t4096 combined output vs the oracle's layer on tokens", list(toks), float(err.max()))
     assert err.max() <= TOL
 
 
@@ -444,6 +495,33 @@ def test_layer_cfg2_hy4_decode_zipf_sampled():
 MX_SMALL = synth.LayerCfg("mx", 150, 512, 256, 8, 2, True, "mxfp4", False, True, 1, 13)
 
 
+# FP8 requantisation of h (R11 stage ii): codes of h may differ from the oracle's by one E4M3
+# step where the scaled MFMA's reduced-precision sums (about 2^-16 of the sum of |products|,
+# measured by test_mx_scaled_mfma_accumulation_error) move a value across a rounding
+# boundary.  Measured rates, on samples of 32768 .. 307200 codes: 3.1e-4 .. 4.9e-4.  The
+# budget is twice the largest, plus a Poisson margin (three standard deviations and two codes)
+# so that configs with a few thousand codes do not fail on counting noise.
+MX_FLIP_RATE = 1e-3
+
+
+def _mx_flip_budget(n_tot):
+    mean = MX_FLIP_RATE * n_tot
+    return mean + 3.0 * math.sqrt(mean) + 2.0
+
+
+def _mx_flip_count(hq, hs, hq_ref, hs_ref):
+    """Codes of h that differ from the oracle's; each must stay within one E4M3 step of the
+    oracle's value (a flip at a rounding boundary, or an amax on either side of a power of
+    two)."""
+    diff = hq != hq_ref
+    if diff.any():
+        vg = O.mx_dequantize_e4m3(hq, hs)
+        vr = O.mx_dequantize_e4m3(hq_ref, hs_ref)
+        step = np.abs(vr) * 2.0 ** -3 + O.ue8m0_value(hs_ref).repeat(32, axis=1) * 2.0 ** -9
+        assert (np.abs(vg - vr)[diff] <= step[diff] * 1.0001).all()
+    return int(diff.sum())
+
+
 def _mx_h_down_check(c, get_w, a, hq, hs, yp, sp, off, experts):
     """h codes of the pairs the GPU routed against the oracle's MX quantisation of
     SiLU(x W_g^T) * (x W_u^T) (a = dequantised E4M3 x), and the down projection fed the GPU's
@@ -460,20 +538,13 @@ def _mx_h_down_check(c, get_w, a, hq, hs, yp, sp, off, experts):
         u = a[toks] @ get_w(e, 1).T
         h = O.silu(g) * u
         hq_ref, hs_ref = O.mx_quantize_e4m3(h)
-        diff = hq[lo:hi] != hq_ref
-        if diff.any():
-            vg = O.mx_dequantize_e4m3(hq[lo:hi], hs[lo:hi])
-            vr = O.mx_dequantize_e4m3(hq_ref, hs_ref)
-            step = np.abs(vr) * 2.0 ** -3 + O.ue8m0_value(hs_ref).repeat(32, axis=1) * 2.0 ** -9
-            assert (np.abs(vg - vr)[diff] <= step[diff] * 1.0001).all()
-        n_flip += int(diff.sum())
-        n_tot += diff.size
+        n_flip += _mx_flip_count(hq[lo:hi], hs[lo:hi], hq_ref, hs_ref)
+        n_tot += hq_ref.size
         y_ref = O.mx_dequantize_e4m3(hq[lo:hi], hs[lo:hi]) @ get_w(e, 2).T
         worst = max(worst, float(row_err(yp[lo:hi], y_ref).max()))
-    say("mx h code flips", n_flip, "of", n_tot, "down-stage max row err", worst)
-    # The scaled MFMA's dot products carry ~2^-14 relative error, so with boundaries 2^-3
-    # apart (relative) about 2 * 1e-4 / 2^-3 = 1.6e-3 of the codes may flip.
-    assert n_flip <= max(2, 2e-3 * n_tot)
+    say(f"mx h code flips {n_flip} of {n_tot} (rate {n_flip / max(1, n_tot):.2e}, budget "
+        f"{MX_FLIP_RATE:.1e}), down-stage max row err {worst:.3e}")
+    assert n_flip <= _mx_flip_budget(n_tot)
     assert worst <= TOL
 
 
@@ -525,9 +596,11 @@ def test_mx_layer_blocks_and_tails(name, tiled):
 
 def test_mx_layer_cfg3_hy4_prefill_sampled():
     """Full-size MXFP4 prefill (4096 tokens, 256 experts, top-8): routing, permutation and
-    activation quantisation in full; h and the down projection on the experts with the most
-    and the fewest pairs and one more; the shared expert and the combined output on sampled
-    tokens."""
+    activation quantisation in full; on EVERY expert, the first and last pair (both M blocks
+    of a split expert): h codes on two 32-column groups from different N tiles by the
+    stage-(ii) rule, and the down projection of the GPU's FP8 h on one output row per N tile;
+    the shared expert and the combined output of sampled tokens against the oracle's y_pairs
+    (the oracle's down projection of the GPU's FP8 h, whole rows)."""
     c = synth.cfg(3)
     say("mx cfg3 generate")
     inp = layer_inputs(c)
@@ -542,17 +615,53 @@ def test_mx_layer_cfg3_hy4_prefill_sampled():
     rsp, roff, rpp = O.permute(rid, c.E)
     assert (host(bufs.sorted_pair) == rsp).all() and (host(bufs.offsets) == roff).all()
     assert (host(bufs.pair_pos) == rpp).all()
-    cnt = np.diff(roff)
-    pick = [int(np.argmax(cnt)), int(np.argmin(np.where(cnt > 0, cnt, 1 << 30))),
-            int(synth.sample_tokens(c.seed, c.E, 1)[0])]
-    say("mx cfg3 stage check on experts", pick, "pairs", [int(cnt[e]) for e in pick])
-    _mx_stage_check(c, inp, bufs, d, experts_check=pick)
-    toks = synth.sample_tokens(c.seed, c.T, 4)
+    offs = M.moe_workspace_offsets(d, M.MOE_W_MXFP4, True)
+    ws = host(bufs.ws)
+    T, H, I, P = c.T, c.H, c.I, d.P
+    xq = ws[offs[2]:offs[2] + T * H].reshape(T, H)
+    xs = ws[offs[3]:offs[3] + T * H // 32].reshape(T, H // 32)
+    rq, rs = O.mx_quantize_e4m3(O.bf16_to_f64(inp["x"]))
+    assert (xq == rq).all() and (xs == rs).all()
+    hq = ws[offs[4]:offs[4] + P * I].reshape(P, I)
+    hs = ws[offs[5]:offs[5] + P * I // 32].reshape(P, I // 32)
+    a = O.mx_dequantize_e4m3(rq, rs)
+    yp = host(bufs.y_pairs)
+    (gc, gs), (uc, us), (dc, ds) = inp["routed"]
+    n_flip = n_tot = 0
+    worst_y = 0.0
+    samples = _expert_samples(c, roff, 133)
+    for e, poss, grp, hcols, orow in samples:
+        at = a[rsp[poss] // c.k]
+        h = O.silu(at @ _mx_rows(gc[e], gs[e], H, hcols).T) * (at @ _mx_rows(uc[e], us[e], H, hcols).T)
+        hq_ref, hs_ref = O.mx_quantize_e4m3(h)
+        hq_g = hq[poss][:, hcols]
+        hs_g = hs[poss][:, grp]
+        n_flip += _mx_flip_count(hq_g, hs_g, hq_ref, hs_ref)
+        n_tot += hq_g.size
+        hv = O.mx_dequantize_e4m3(hq[poss], hs[poss])
+        Wd = _mx_rows(dc[e], ds[e], I, orow)
+        for i, pos in enumerate(poss):
+            worst_y = max(worst_y, _sampled_err(yp[pos, orow], Wd @ hv[i]))
+    rate = n_flip / max(1, n_tot)
+    say(f"mx cfg3: {len(samples)} experts checked; h code flips {n_flip} of {n_tot} "
+        f"(rate {rate:.2e}, budget {MX_FLIP_RATE:.1e}); down-stage max err {worst_y:.3e}")
+    assert len(samples) == int((np.diff(roff) > 0).sum())
+    assert n_flip <= _mx_flip_budget(n_tot)
+    assert worst_y <= TOL
+    toks = synth.sample_tokens(c.seed, c.T, 3)
     ysh = O.shared_expert(inp["x"][toks], *inp["shared"])
     assert row_err(host(bufs.y_shared)[toks], ysh).max() <= TOL
-    out_ref = O.combine(host(bufs.y_pairs), rw, rpp, host(bufs.y_shared))
-    err = row_err(host(bufs.out)[toks], out_ref[toks])
-    say("mx cfg3 combine max row err on sampled tokens", float(err.max()))
+    get_w = oracle_weights(c, inp["routed"])
+    hv_all = {}
+    out_ref = ysh.copy()
+    for i, t in enumerate(toks):
+        for j in range(c.k):
+            pos = int(rpp[t * c.k + j])
+            e = int(rid[t, j])
+            y = O.mx_dequantize_e4m3(hq[pos:pos + 1], hs[pos:pos + 1]) @ get_w(e, 2).T
+            out_ref[i] += rw[t, j] * y[0]
+    err = row_err(host(bufs.out)[toks], out_ref)
+    say("mx cfg3 combined output vs the oracle's y_pairs on tokens", list(toks), float(err.max()))
     assert err.max() <= TOL
 
 

@@ -238,6 +238,27 @@ def test_route_ties_and_bias():
     assert list(ids[0]) == [0, 1]
 
 
+def test_route_nan_rows():
+    """A NaN logit ranks above every number and NaNs tie: the selection equals that of the row
+    with every NaN replaced by one common value above all the others (a finite case already
+    pinned above), and a selection holding a NaN gets NaN weights.  An all-NaN row (what a NaN
+    in x gives) therefore selects experts 0 .. k-1, as an all-equal row does."""
+    g = np.random.default_rng(12)
+    E, k = 12, 4
+    for nan_at in ([3], [7, 2], [0, 5, 11], list(range(E))):
+        row = g.standard_normal(E)
+        row[nan_at] = np.nan
+        repl = np.where(np.isnan(row), np.nanmax(np.append(row, 0.0)) + 1e3, row)
+        _, ids, w = O.route(k, logits_in=row[None, :])
+        _, ids_r, _ = O.route(k, logits_in=repl[None, :])
+        assert list(ids[0]) == list(ids_r[0])
+        assert np.isnan(w).all()
+        assert ((ids >= 0) & (ids < E)).all()
+    _, ids, _ = O.route(k, logits_in=np.full((1, E), np.nan))
+    _, ids0, _ = O.route(k, logits_in=np.zeros((1, E)))
+    assert list(ids[0]) == list(ids0[0]) == list(range(k))
+
+
 def test_route_from_bf16_matches_bruteforce_dot():
     x = synth.activations(0, 0, 2, 64)
     wr = synth.router_weights(0, 0, 4, 64)
@@ -264,6 +285,36 @@ def test_permute_vs_stable_sort():
         assert list(off) == [0] + list(np.cumsum(np.bincount(flat, minlength=E)))
         assert (sp[pp] == np.arange(flat.size)).all()
         assert (np.diff(flat[sp]) >= 0).all()
+
+
+def test_permute_drops_unroutable_ids():
+    """Ids outside [0, E) take no sorted position: the routed pairs are Python's stable sort
+    of the valid ids, pair_pos is -1 for the others, offsets end at the routed count and
+    sorted_pair is -1 past it."""
+    g = np.random.default_rng(13)
+    E, T, k = 6, 9, 3
+    ids = g.integers(-2, E + 2, (T, k)).astype(np.int32)
+    sp, off, pp = O.permute(ids, E)
+    flat = ids.reshape(-1)
+    valid = [f for f in range(flat.size) if 0 <= flat[f] < E]
+    ref = sorted(valid, key=lambda f: flat[f])
+    n = len(ref)
+    assert list(sp[:n]) == ref and (sp[n:] == -1).all()
+    assert off[E] == n and list(off) == [0] + list(np.cumsum(np.bincount(flat[valid], minlength=E)))
+    assert all(pp[f] == -1 for f in range(flat.size) if f not in valid)
+    assert all(sp[pp[f]] == f for f in valid)
+
+
+def test_combine_skips_unrouted_pairs():
+    """A pair with pair_pos -1 contributes exactly what a zero routing weight would."""
+    g = np.random.default_rng(14)
+    yp = g.standard_normal((5, 7))
+    w = g.random((3, 2))
+    pp = np.array([4, -1, 0, 2, -1, 3])
+    w0 = w.copy()
+    w0[0, 1] = w0[2, 0] = 0.0
+    pp0 = np.where(pp < 0, 1, pp)
+    assert np.array_equal(O.combine(yp, w, pp), O.combine(yp, w0, pp0))
 
 
 # ----------------------------------------------------------------------------- expert math
@@ -396,6 +447,94 @@ def test_tiny_layer_bruteforce():
             for o in range(c.H):
                 out[o] += res["w"][t, j] * sum(hvec[i] * weight(e, 2, o, i) for i in range(c.I))
         assert np.allclose(res["out"][t], out, rtol=1e-10, atol=1e-12)
+
+
+def _bf16_value(bits):
+    """bf16 bits -> Python float through the IEEE binary32 it is the top half of."""
+    import struct
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+def test_shared_expert_bruteforce_loops():
+    """The bf16 shared expert equals pure-Python loops over bf16 bits decoded one by one:
+    h_i = silu(sum_c x_c Wg[i,c]) * sum_c x_c Wu[i,c], y_o = sum_i h_i Wd[o,i] (gate inside
+    the SiLU, up outside it)."""
+    T, H, I = 2, 16, 8
+    x = synth.activations(40, 0, T, H)
+    wg, wu, wd = synth.shared_weights(40, 0, I, H)
+    y = O.shared_expert(x, wg, wu, wd)
+    for t in range(T):
+        xs = [_bf16_value(v) for v in x[t]]
+        h = []
+        for i in range(I):
+            gi = sum(xs[c] * _bf16_value(wg[i, c]) for c in range(H))
+            ui = sum(xs[c] * _bf16_value(wu[i, c]) for c in range(H))
+            h.append(gi / (1 + math.exp(-gi)) * ui)
+        for o in range(H):
+            ref = sum(h[i] * _bf16_value(wd[o, i]) for i in range(I))
+            assert math.isclose(y[t, o], ref, rel_tol=1e-12, abs_tol=1e-15)
+
+
+_E2M1_MAG = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _mx_brute(vals):
+    """MX E4M3 quantise-dequantise of a list whose length is a multiple of 32, by search over
+    the finite E4M3 values (torch's float8_e4m3fn decoding of all 256 codes): per group the
+    shared exponent floor(log2 amax) - 8 (math.frexp), then each v / 2^X goes to the nearest
+    value, a tie to the one with an even code, magnitudes past 448 to 448."""
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    fin = [(float(v), c) for c, v in enumerate(codes) if np.isfinite(v) and c < 128]
+    out = []
+    for g0 in range(0, len(vals), 32):
+        grp = vals[g0:g0 + 32]
+        amax = max(abs(v) for v in grp)
+        if amax == 0:
+            out += [0.0] * 32
+            continue
+        X = max(-127, min(127, math.frexp(amax)[1] - 1 - 8))
+        for v in grp:
+            y = min(abs(v) / 2.0 ** X, 448.0)
+            best = min(fin, key=lambda vc: (abs(vc[0] - y), vc[1] % 2))
+            out.append(math.copysign(best[0], v) * 2.0 ** X)
+    return out
+
+
+def test_expert_ffn_mxfp4_bruteforce():
+    """The MXFP4 branch of expert_ffn: x MX-quantised along H, gathered by sorted pair, gate
+    and up with E2M1 weights times their UE8M0 group scales, SiLU(gate) * up MX-quantised
+    along I, then down -- equal to pure-Python loops with a brute-force MX quantiser and a
+    hand-decoded E2M1 table."""
+    g = np.random.default_rng(41)
+    T, H, I, E, k = 3, 64, 32, 3, 2
+    x = synth.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    shp = [(I, H), (I, H), (H, I)]
+    fam = [(g.integers(0, 256, (E, n, kk // 2), dtype=np.uint8),
+            (127 + g.integers(-3, 2, (E, n, kk // 32))).astype(np.uint8)) for n, kk in shp]
+    ids = np.array([[0, 2], [2, 1], [0, 1]], dtype=np.int32)
+    sp, off, _ = O.permute(ids, E)
+    get_w = lambda e, m: O.mxfp4_matrix(fam[m][0][e], fam[m][1][e], *shp[m])
+    y, h = O.expert_ffn(x, ids, sp, off, get_w, "mxfp4")
+
+    def w_at(e, m, r, c):
+        code = int(fam[m][0][e][r, c // 2]) >> (4 * (c % 2)) & 15
+        mag = _E2M1_MAG[code & 7] * 2.0 ** (int(fam[m][1][e][r, c // 32]) - 127)
+        return -mag if code & 8 else mag
+
+    xq = [_mx_brute([_bf16_value(v) for v in x[t]]) for t in range(T)]
+    for e in range(E):
+        for pos in range(off[e], off[e + 1]):
+            a = xq[sp[pos] // k]
+            hv = []
+            for i in range(I):
+                gi = sum(a[c] * w_at(e, 0, i, c) for c in range(H))
+                ui = sum(a[c] * w_at(e, 1, i, c) for c in range(H))
+                hv.append(gi / (1 + math.exp(-gi)) * ui)
+            hq = _mx_brute(hv)
+            assert np.array_equal(h[pos], hq)
+            for o in range(H):
+                ref = sum(hq[i] * w_at(e, 2, o, i) for i in range(I))
+                assert math.isclose(y[pos, o], ref, rel_tol=1e-12, abs_tol=1e-15)
 
 
 # ----------------------------------------------------------------------------- STQ1_0 encoders
