@@ -434,6 +434,175 @@ def mx_decode_bench(args):
     return dict(c=c, ms=ms, prof=prof, kbytes=kb, expert_b=expert_b)
 
 
+def gpu_stq_layer(c, seed):
+    """One STQ1_0 Hy4 layer generated on the GPU from a seeded torch generator, with the
+    distributions of the synthetic workloads: uniform code bytes (= uniform over the 32
+    patterns), fp16 scales |N(0, 0.02)|, bf16 N(0, 0.02) router and shared expert."""
+    import torch
+    import bit_quantized_moe_softmax_amd as M
+    from bit_quantized_moe_softmax_amd.layer import bf16_experts
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    n_blk = c.I * c.H // 256
+    fam = []
+    for _ in range(3):
+        codes = torch.randint(0, 256, (c.E, n_blk * 40), dtype=torch.uint8, device="cuda", generator=g)
+        scales = (torch.randn((c.E, n_blk), device="cuda", generator=g).abs_() * 0.02).half().view(torch.int16)
+        fam.append((codes, scales))
+
+    def bf16(shape):
+        return (torch.randn(shape, device="cuda", generator=g) * 0.02).bfloat16().view(torch.int16)
+
+    return dict(routed=M.Experts(M.MOE_W_STQ1_0, *fam),
+                shared=bf16_experts(bf16((c.I, c.H)), bf16((c.I, c.H)), bf16((c.H, c.I))),
+                wr=bf16((c.E, c.H)))
+
+
+def decode_bufs(d, c, shared=True):
+    import torch
+    f32, i32 = torch.float32, torch.int32
+    import bit_quantized_moe_softmax_amd as M
+    return dict(logits=torch.empty((c.T, c.E), dtype=f32, device="cuda"),
+                ids=torch.empty((c.T, c.k), dtype=i32, device="cuda"),
+                w=torch.empty((c.T, c.k), dtype=f32, device="cuda"),
+                sp=torch.empty(d.P, dtype=i32, device="cuda"),
+                off=torch.empty(c.E + 1, dtype=i32, device="cuda"),
+                pp=torch.empty(d.P, dtype=i32, device="cuda"),
+                yp=torch.empty((d.P, c.H), dtype=f32, device="cuda"),
+                ysh=torch.empty((c.T, c.H), dtype=f32, device="cuda"),
+                ws=torch.zeros(M.moe_layer_decode_workspace_size(d, shared), dtype=torch.uint8, device="cuda"))
+
+
+def decode_call(M, d, L, x, bias, b, residual, out, stream):
+    M.moe_layer_decode(d, L["routed"], L["shared"], x, L["wr"], bias, b["logits"], b["ids"], b["w"],
+                       b["sp"], b["off"], b["pp"], b["yp"], b["ysh"], residual, out, None, b["ws"], stream)
+
+
+def decode_t64_bench(args):
+    """64-token decode with Zipf(1.1)-skewed routing (the batch-64 workload): one fused
+    moe_layer_decode per step over 3 GPU-generated layer copies (the step's unique experts,
+    about 0.7 GB, do not fit the 256 MB Infinity Cache, and the copies keep the shared expert
+    and router cold too).  Reports U (unique experts per step), the unique-expert bytes and
+    the whole step's algorithmic bytes as GB/s."""
+    import numpy as np
+    import torch
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    c = synth.cfg(2)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    copies = [gpu_stq_layer(c, 2000 + i) for i in range(3)]
+    xs = [dev(synth.activations(c.seed, 1 + i, c.T, c.H)) for i in range(2)]
+    bias = dev(synth.zipf_bias(c.seed, 0, c.E))
+    b = decode_bufs(d, c)
+    out = torch.empty((c.T, c.H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    # unique experts of every (copy, batch) combination the steps use
+    U = {}
+    for i in range(len(copies)):
+        for j in range(len(xs)):
+            decode_call(M, d, copies[i], xs[j], bias, b, None, out, s)
+            torch.cuda.synchronize()
+            U[(i, j)] = len(np.unique(b["ids"].cpu().numpy()))
+
+    def step(i):
+        decode_call(M, d, copies[i % 3], xs[(i // 3) % 2], bias, b, None, out, s)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    M.moe_profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = M.moe_profile_read()
+    M.moe_profile_enable(False)
+    u_avg = float(np.mean([U[(i % 3, (i // 3) % 2)] for i in range(args.steps)]))
+    expert_b = 3 * STQ_MAT_BYTES
+    shared_b = 3 * c.I * c.H * 2
+    router_b = c.E * c.H * 2
+    act_b = c.T * c.H * 2 + c.T * c.H * 4 + d.P * c.H * 4 + c.T * c.H * 4   # x, out, y_pairs, y_shared
+    unique_b = u_avg * expert_b
+    step_b = unique_b + shared_b + router_b + act_b
+    kb = {"decode_k1_route": router_b + c.T * c.H * 2 + c.T * c.E * 4,
+          "decode_k2_gateup": u_avg * 2 * STQ_MAT_BYTES + 2 * c.I * c.H * 2 + c.T * c.H * 2
+                              + (d.P + c.T) * c.I * 4,
+          "decode_k3_down_combine": u_avg * STQ_MAT_BYTES + c.I * c.H * 2 + (d.P + c.T) * c.I * 4
+                                    + d.P * c.H * 4 + 2 * c.T * c.H * 4}
+    return dict(c=c, ms=ms, U=u_avg, unique_b=unique_b, step_b=step_b, prof=prof, kbytes=kb)
+
+
+def chain_bench(args):
+    """The 29-layer STQ1_0 stack at 16 tokens (about 46 GB of packed experts resident):
+    a step runs, for every layer, RMSNorm (bf16 out) and the fused moe_layer_decode with the
+    residual add, on Zipf-skewed routing.  Every step starts from the same hidden state, so
+    every step touches the same experts; U per layer is read from the ids of an untimed pass."""
+    import numpy as np
+    import torch
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    c = synth.cfg(4)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    t0 = time.perf_counter()
+    layers = [gpu_stq_layer(c, 7000 + l) for l in range(c.layers)]
+    biases = [dev(synth.zipf_bias(c.seed, l, c.E)) for l in range(c.layers)]
+    torch.cuda.synchronize()
+    log(f"29 layers generated on the GPU in {time.perf_counter() - t0:.1f} s")
+    b = decode_bufs(d, c)
+    r0 = dev(O_bf16_to_f32(synth.activations(c.seed, 0, c.T, c.H)))
+    r = torch.empty_like(r0)
+    r2 = torch.empty_like(r0)
+    a = torch.empty((c.T, c.H), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    U = []
+
+    def step(record=False):
+        r.copy_(r0)
+        cur, nxt = r, r2
+        for l in range(c.layers):
+            M.moe_rmsnorm_bf16(c.T, c.H, 1e-6, cur, a, s)
+            decode_call(M, d, layers[l], a, biases[l], b, cur, nxt, s)
+            if record:
+                torch.cuda.synchronize()
+                U.append(len(np.unique(b["ids"].cpu().numpy())))
+            cur, nxt = nxt, cur
+
+    step(record=True)
+    for _ in range(max(1, args.warmup // 2)):
+        step()
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 2)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(n):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / n
+    expert_b = 3 * STQ_MAT_BYTES
+    # shared expert, router, and the activations: RMSNorm reads r and writes a; the layer reads
+    # a and the residual, writes out, y_shared and y_pairs
+    per_layer_fixed = 3 * c.I * c.H * 2 + c.E * c.H * 2 + c.T * c.H * (4 + 2 + 2 + 4 + 4 + 4) + d.P * c.H * 4
+    step_b = sum(u * expert_b for u in U) + c.layers * per_layer_fixed
+    del layers
+    torch.cuda.empty_cache()
+    return dict(c=c, ms=ms, U=U, step_b=step_b, steps=n)
+
+
+def O_bf16_to_f32(bits):
+    """bf16 bit patterns -> float32 (a plain reinterpretation, no arithmetic)."""
+    import numpy as np
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     "decode_k1_route": "k1s_router<", "decode_k2_gateup": "k2s_gateup<",
     "decode_k3_down_combine": "k3_down_combine<", "mx_gateup": "mx_gemm_kernel<true, true>",
@@ -512,13 +681,25 @@ def load_traffic():
     return {}
 
 
-def cpu_baseline(args):
-    """The oracle as it stands, one thread, on one batch-1 layer call (bounded sample)."""
-    import numpy as np
+def _cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _threads(n):
+    import contextlib
     try:
         from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n)
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        return contextlib.nullcontext()
+
+
+def cpu_baseline(args, threads=None, budget_s=10.0, max_calls=16):
+    """The oracle as it stands on batch-1 Hy4 STQ1_0 layer calls (fresh tokens) on the host's
+    cores (all BLAS threads, or `threads`), bounded to about budget_s of work."""
     import synth
     from oracle import moe_oracle as O
     c = synth.cfg(1)
@@ -526,7 +707,6 @@ def cpu_baseline(args):
     wr = synth.router_weights(c.seed, 0, c.E, c.H)
     sh = synth.shared_weights(c.seed, 0, c.I, c.H)
     shapes = [(c.I, c.H), (c.I, c.H), (c.H, c.I)]
-
     gen_s = [0.0]   # time spent generating the synthetic packed weights (not oracle work)
 
     def get_w(e, m):
@@ -536,27 +716,103 @@ def cpu_baseline(args):
         gen_s[0] += time.perf_counter() - t
         return O.stq1_matrix(codes, scales, *shapes[m])
 
-    import contextlib
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    ctx = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
+    cores = threads or _cores()
     xs = synth.activations(c.seed, 1, 16, c.H)
     n = 0
-    with ctx:
+    with _threads(cores):
         t0 = time.perf_counter()
-        # one layer call per token, on fresh tokens, until about 10 s of work (at most 16 calls)
-        while n < 16 and (n == 0 or time.perf_counter() - t0 < 10.0):
+        while n < max_calls and (n == 0 or time.perf_counter() - t0 - gen_s[0] < budget_s):
             O.moe_layer(x if n == 0 else xs[n:n + 1], c.k, get_w, "stq1", wr_bits=wr, shared=sh)
             n += 1
         dt = (time.perf_counter() - t0 - gen_s[0]) / n
     expert_b = c.k * 3 * STQ_MAT_BYTES + 3 * c.I * c.H * 2
     return dict(value=expert_b / dt / 1e9, unit="GB/s", cores=cores, kind="oracle",
                 sample=f"{n} batch-1 Hy4 STQ1_0 layer calls on fresh tokens (route, 8 routed experts "
-                       f"decoded and applied in float64, shared expert, combine), {cores} BLAS threads, "
-                       f"{dt:.2f} s per call without the synthetic weight generation; value = expert-weight "
-                       f"bytes per call / time per call")
+                       f"decoded and applied in float64, shared expert, combine), {cores} BLAS "
+                       f"thread{'s' if cores > 1 else ''}, {dt:.2f} s per call without the synthetic "
+                       f"weight generation; value = expert-weight bytes per call / time per call")
+
+
+def cpu_baselines_extra():
+    """Bounded samples of the oracle on the other workloads (host cores, all BLAS threads;
+    synthetic weight generation excluded): 2 tokens of the 64-token Zipf batch, a few experts
+    of the 4096-token MXFP4 prefill with all their pairs (float32 BLAS for the matmuls, as a
+    timing stand-in; parity runs in float64), and the 2 sampled tokens of the 29-layer chain
+    through one layer.  Each in the unit of its GPU line."""
+    import numpy as np
+    import synth
+    from oracle import moe_oracle as O
+    cores = _cores()
+    out = {}
+    sh = [(2048, 6144), (2048, 6144), (6144, 2048)]
+    with _threads(cores):
+        # 64-token Zipf decode: 2 tokens of the batch, GB/s of their unique experts' bytes
+        c = synth.cfg(2)
+        x = synth.activations(c.seed, 0, 2, c.H)
+        wr = synth.router_weights(c.seed, 0, c.E, c.H)
+        bias = synth.zipf_bias(c.seed, 0, c.E)
+        shw = synth.shared_weights(c.seed, 0, c.I, c.H)
+        gen = [0.0]
+
+        def stq_w(seed, layer):
+            def get_w(e, m):
+                t = time.perf_counter()
+                cd, sc = synth.stq1_matrix(seed, layer, e, m, sh[m][0] * sh[m][1])
+                gen[0] += time.perf_counter() - t
+                return O.stq1_matrix(cd, sc, *sh[m])
+            return get_w
+
+        t0 = time.perf_counter()
+        ref = O.moe_layer(x, c.k, stq_w(c.seed, 0), "stq1", wr_bits=wr, bias=bias, shared=shw)
+        dt = time.perf_counter() - t0 - gen[0]
+        U = len(np.unique(ref["ids"]))
+        b = U * 3 * STQ_MAT_BYTES + 3 * c.I * c.H * 2 + c.E * c.H * 2
+        out["decode_t64_zipf"] = dict(value=b / dt / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                                      sample=f"2 of the 64 tokens ({U} unique experts) through the whole "
+                                             f"layer in {dt:.2f} s; value = their unique-expert + shared + "
+                                             f"router bytes / time")
+        # 4096-token MXFP4 prefill: experts 0, 1 with all their pairs, fp32 matmuls
+        c = synth.cfg(3)
+        logits = synth.prefill_logits(c.seed, 0, c.T, c.E)
+        _, ids, _ = O.route(c.k, logits_in=logits)
+        sp, off, _ = O.permute(ids, c.E)
+        xall = synth.activations(c.seed, 0, c.T, c.H)
+        flop = 0.0
+        gen[0] = 0.0
+        t0 = time.perf_counter()
+        for e in (0, 1):
+            toks = sp[off[e]:off[e + 1]] // c.k
+            tg = time.perf_counter()
+            mats = [synth.mxfp4_matrix(c.seed, 0, e, m, *sh[m]) for m in range(3)]
+            gen[0] += time.perf_counter() - tg
+            W = [O.mxfp4_matrix(cd, sc, *sh[m]).astype(np.float32) for m, (cd, sc) in enumerate(mats)]
+            a = O.mx_dequantize_e4m3(*O.mx_quantize_e4m3(O.bf16_to_f64(xall[toks]))).astype(np.float32)
+            h = O.silu(a @ W[0].T) * (a @ W[1].T)
+            hq = O.mx_dequantize_e4m3(*O.mx_quantize_e4m3(h)).astype(np.float32)
+            _ = hq @ W[2].T
+            flop += 2.0 * len(toks) * 3 * c.I * c.H
+        dt = time.perf_counter() - t0 - gen[0]
+        out["mxfp4_prefill_t4096"] = dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                                          sample=f"experts 0 and 1 with all their pairs ({int(flop / (2 * 3 * c.I * c.H))} "
+                                                 f"pairs) of the 4096-token batch: MX quantisation, E2M1 decode, "
+                                                 f"float32 matmuls, in {dt:.2f} s")
+        # 29-layer chain: the 2 sampled tokens through layer 0
+        c = synth.cfg(4)
+        toks = synth.sample_tokens(c.seed, c.T, 2)
+        xr = O.bf16_to_f64(synth.activations(c.seed, 0, c.T, c.H))[toks]
+        gen[0] = 0.0
+        t0 = time.perf_counter()
+        a = O.rmsnorm_bf16(xr)
+        ref = O.moe_layer(a, c.k, stq_w(c.seed, 0), "stq1", wr_bits=synth.router_weights(c.seed, 0, c.E, c.H),
+                          bias=synth.zipf_bias(c.seed, 0, c.E), shared=synth.shared_weights(c.seed, 0, c.I, c.H),
+                          residual=xr)
+        dt = time.perf_counter() - t0 - gen[0]
+        U = len(np.unique(ref["ids"]))
+        b = U * 3 * STQ_MAT_BYTES + 3 * c.I * c.H * 2 + c.E * c.H * 2
+        out["chain_29_layers"] = dict(value=b / dt / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                                      sample=f"the 2 sampled tokens through layer 0 of 29 (RMSNorm, {U} unique "
+                                             f"experts, shared expert, residual) in {dt:.2f} s")
+    return out
 
 
 def main():
@@ -701,8 +957,47 @@ def main():
                 "runs": [slot_bank_bench(args, S) for S in (8, 96)]}
         except Exception as e:
             out["slot_bank_decode"] = {"error": repr(e)}
+    if not args.no_extra:
+        try:
+            t64 = decode_t64_bench(args)
+            kern = {}
+            for name, nbytes in t64["kbytes"].items():
+                us, n = t64["prof"][name]
+                kern[name] = {"avg_us": round(us, 3), "launches": n, "algorithmic_bytes": round(nbytes),
+                              "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None}
+            dom = max(kern, key=lambda k: kern[k]["avg_us"])
+            gbs = t64["step_b"] / (t64["ms"] * 1e-3) / 1e9
+            out["decode_t64_zipf"] = {
+                "workload": "hy4-stq1_0-decode-t64-zipf1.1", "entry_point": "moe_layer_decode",
+                "us_per_step": round(t64["ms"] * 1e3, 2), "unique_experts": round(t64["U"], 2),
+                "unique_expert_bytes": round(t64["unique_b"]), "step_bytes": round(t64["step_b"]),
+                "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "unique_expert_gbs": round(t64["unique_b"] / (t64["ms"] * 1e-3) / 1e9, 1),
+                "kernels": kern,
+                "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["gbs"], "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round((kern[dom]["gbs"] or 0) / HBM_PEAK_GBS, 4),
+                             "traffic": traffic.get("t64_" + dom), "algorithmic_bytes": kern[dom]["algorithmic_bytes"]}}
+        except Exception as e:
+            out["decode_t64_zipf"] = {"error": repr(e)}
+        try:
+            ch = chain_bench(args)
+            gbs = ch["step_b"] / (ch["ms"] * 1e-3) / 1e9
+            out["chain_29_layers"] = {
+                "workload": "hy4-stq1_0-stack29-t16-zipf1.1", "layers": ch["c"].layers, "tokens": ch["c"].T,
+                "resident_expert_bytes": ch["c"].layers * ch["c"].E * 3 * STQ_MAT_BYTES,
+                "ms_per_step": round(ch["ms"], 4), "steps": ch["steps"], "step_bytes": round(ch["step_b"]),
+                "unique_experts_per_layer": ch["U"], "gbs": round(gbs, 1),
+                "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "note": "a step = 29 x (RMSNorm + fused layer with residual) from the same hidden state"}
+        except Exception as e:
+            out["chain_29_layers"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args)
+        out["cpu_baseline_1thread"] = cpu_baseline(args, threads=1, budget_s=4.0, max_calls=1)
+        try:
+            out["cpu_baseline_other_workloads"] = cpu_baselines_extra()
+        except Exception as e:
+            out["cpu_baseline_other_workloads"] = {"error": repr(e)}
     print(json.dumps(out), flush=True)
 
 
