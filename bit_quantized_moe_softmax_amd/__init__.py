@@ -19,7 +19,7 @@ __all__ = [
     "moe_combine", "moe_stq1_pack", "moe_stq1_dequant", "moe_mxfp4_dequant", "moe_mx_quant_act",
     "moe_mx_quant_f32_hwcvt",
     "moe_rmsnorm_bf16", "moe_layer_decode_workspace_size", "moe_layer_decode_workspace_offsets",
-    "moe_layer_decode", "moe_stq1_encode", "SlotBank", "moe_remap_ids", "MOE_STQ1_ENC_UPSTREAM", "MOE_STQ1_ENC_WLS",
+    "moe_layer_decode", "moe_layer_decode_noalloc", "moe_stq1_encode", "SlotBank", "moe_remap_ids", "MOE_STQ1_ENC_UPSTREAM", "MOE_STQ1_ENC_WLS",
     "moe_profile_enable", "moe_profile_read", "PROFILE_SLOTS",
 ]
 
@@ -83,6 +83,7 @@ _SIGS = {
     "moe_slot_bank_stats": (ctypes.c_int, [_P, _P, _P]),
     "moe_remap_ids": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P, _P]),
     "moe_layer_decode": (ctypes.c_int, [_P, _P, _P] + [_P] * 15 + [ctypes.c_size_t, _P]),
+    "moe_layer_decode_noalloc": (ctypes.c_int, [_P, _P, _P] + [_P] * 15),
     "moe_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
     "moe_profile_read": (ctypes.c_int, [_P, _P]),
 }
@@ -320,6 +321,16 @@ def moe_layer_decode(d: Dims, routed: Experts, shared, x_bf16, wr_bf16, logit_bi
         _ptr(sorted_pair), _ptr(expert_offsets), _ptr(pair_pos), _ptr(y_pairs), _ptr(y_shared),
         _ptr(residual), _ptr(out_f32), _ptr(out_bf16), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_decode_noalloc(d: Dims, routed: Experts, shared, x_bf16, wr_bf16, logit_bias, logits_out,
+                             topk_ids, topk_w, sorted_pair, expert_offsets, pair_pos, y_pairs, y_shared,
+                             residual, out_f32, out_bf16, stream=None):
+    _check(lib().moe_layer_decode_noalloc(
+        d.ref(), routed.ref(), shared.ref() if shared is not None else None, _ptr(x_bf16),
+        _ptr(wr_bf16), _ptr(logit_bias), _ptr(logits_out), _ptr(topk_ids), _ptr(topk_w),
+        _ptr(sorted_pair), _ptr(expert_offsets), _ptr(pair_pos), _ptr(y_pairs), _ptr(y_shared),
+        _ptr(residual), _ptr(out_f32), _ptr(out_bf16), _stream(stream)))
 
 
 def moe_profile_enable(on: bool) -> None:

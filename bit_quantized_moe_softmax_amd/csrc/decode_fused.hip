@@ -45,6 +45,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr int kWG = 256;           // 4 waves
@@ -1773,6 +1775,44 @@ hipError_t launch_shape(DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------- static scratch
+// The workspace of moe_layer_decode_noalloc, for callers that cannot allocate: one array per
+// device, held by the loaded library until the process ends.  Host code never uses the
+// symbol's name as an address: moe_decode_static_scratch() looks up each device's own
+// address once (hipGetSymbolAddress, that device current) and keeps it.
+static __device__ __align__(256) uint8_t scratch[kDecodeStaticScratchBytes];
+
+namespace {
+
+// Zero the first n words of the workspace (the work-list header with the router ticket):
+// a kernel, not hipMemsetAsync, so a captured call replays it as a kernel node.
+__global__ __launch_bounds__(64) void clear_words_kernel(uint32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+void* moe_decode_static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+hipError_t moe_clear_decode_header(void* ws, hipStream_t s) {
+  hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(64), 0, s, static_cast<uint32_t*>(ws), 8);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------- host side
 // Shapes with a compiled instantiation: (H, I) in units of 256.

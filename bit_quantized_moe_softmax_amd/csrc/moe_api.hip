@@ -509,13 +509,14 @@ moe_status moe_layer_decode_workspace_offsets(const moe_dims* d, int32_t has_sha
   return MOE_OK;
 }
 
-moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
-                            const moe_experts* shared, const uint16_t* x_bf16,
-                            const uint16_t* wr_bf16, const float* logit_bias, float* logits_out,
-                            int32_t* topk_ids, float* topk_w, int32_t* sorted_pair,
-                            int32_t* expert_offsets, int32_t* pair_pos, float* y_pairs,
-                            float* y_shared, const float* residual, float* out_f32,
-                            uint16_t* out_bf16, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of the fused decode (both entry points); MOE_OK when the call may proceed.
+static moe_status decode_args_ok(const moe_dims* d, const moe_experts* routed,
+                                 const moe_experts* shared, const uint16_t* x_bf16,
+                                 const uint16_t* wr_bf16, const float* logits_out,
+                                 const int32_t* topk_ids, const float* topk_w,
+                                 const int32_t* sorted_pair, const int32_t* expert_offsets,
+                                 const int32_t* pair_pos, const float* y_pairs, const float* y_shared,
+                                 const float* out_f32) {
   if (!dims_ok(d) || !routed || !x_bf16 || !wr_bf16 || !logits_out || !topk_ids || !topk_w ||
       !sorted_pair || !expert_offsets || !pair_pos || !y_pairs || !out_f32)
     return MOE_ERR_INVALID_ARG;
@@ -531,6 +532,48 @@ moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
       return MOE_ERR_INVALID_ARG;
   }
   if (!decode_fused_ok(d)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_layer_decode_noalloc(const moe_dims* d, const moe_experts* routed,
+                                    const moe_experts* shared, const uint16_t* x_bf16,
+                                    const uint16_t* wr_bf16, const float* logit_bias,
+                                    float* logits_out, int32_t* topk_ids, float* topk_w,
+                                    int32_t* sorted_pair, int32_t* expert_offsets,
+                                    int32_t* pair_pos, float* y_pairs, float* y_shared,
+                                    const float* residual, float* out_f32, uint16_t* out_bf16,
+                                    void* stream) {
+  const moe_status st = decode_args_ok(d, routed, shared, x_bf16, wr_bf16, logits_out, topk_ids,
+                                       topk_w, sorted_pair, expert_offsets, pair_pos, y_pairs,
+                                       y_shared, out_f32);
+  if (st != MOE_OK) return st;
+  size_t offs[16];
+  const size_t need = moe_decode_ws_layout(d->T, d->H, d->I, d->E, d->k, shared != nullptr, offs);
+  if (need > kDecodeStaticScratchBytes) return MOE_ERR_UNSUPPORTED;
+  if (d->T == 0) return MOE_OK;
+  void* ws = moe_decode_static_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = moe_clear_decode_header(ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe_launch_decode_fused(d, routed, shared, x_bf16, wr_bf16, logit_bias, logits_out,
+                              topk_ids, topk_w, sorted_pair, expert_offsets, pair_pos, y_pairs,
+                              y_shared, residual, out_f32, out_bf16, ws, s);
+  bump(MOE_CNT_DECODE_FUSED);
+  return finish(e, s);
+}
+
+moe_status moe_layer_decode(const moe_dims* d, const moe_experts* routed,
+                            const moe_experts* shared, const uint16_t* x_bf16,
+                            const uint16_t* wr_bf16, const float* logit_bias, float* logits_out,
+                            int32_t* topk_ids, float* topk_w, int32_t* sorted_pair,
+                            int32_t* expert_offsets, int32_t* pair_pos, float* y_pairs,
+                            float* y_shared, const float* residual, float* out_f32,
+                            uint16_t* out_bf16, void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = decode_args_ok(d, routed, shared, x_bf16, wr_bf16, logits_out, topk_ids,
+                                       topk_w, sorted_pair, expert_offsets, pair_pos, y_pairs,
+                                       y_shared, out_f32);
+  if (st != MOE_OK) return st;
   size_t offs[16];
   const size_t need = moe_decode_ws_layout(d->T, d->H, d->I, d->E, d->k, shared != nullptr, offs);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;

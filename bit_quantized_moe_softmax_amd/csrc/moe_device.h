@@ -300,6 +300,12 @@ void moe_prof_begin(int slot, hipStream_t s);
 void moe_prof_end(int slot, hipStream_t s);
 
 // Fused decode layer (three kernels).
+// Bytes of the static scratch array behind moe_layer_decode_noalloc (per device).
+constexpr size_t kDecodeStaticScratchBytes = (size_t)8 << 20;
+// This device's address of that array (looked up once per device), or nullptr on failure.
+void* moe_decode_static_scratch();
+// Enqueue a kernel that zeroes the fused decode workspace's header words (the router ticket).
+hipError_t moe_clear_decode_header(void* ws, hipStream_t s);
 bool moe_decode_shape_ok(int H, int I, int E);
 bool moe_decode_mx_ok(int T, int I, int k);
 size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, size_t* offs);

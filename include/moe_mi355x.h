@@ -294,6 +294,23 @@ MOE_MI355X_API moe_status moe_layer_decode(
     int32_t* pair_pos, float* y_pairs, float* y_shared, const float* residual, float* out_f32,
     uint16_t* out_bf16, void* ws, size_t ws_bytes, void* stream);
 
+/* The same fused decode layer with no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): it calls no allocating routine and uses, as its workspace, a scratch array of
+ * 8 MiB that the library holds on every device it runs on until the process ends.  Same
+ * arguments, limits and results as moe_layer_decode (bit for bit), plus: the workspace
+ * moe_layer_decode_workspace_size reports for these dims must fit 8 MiB (at hidden 6144,
+ * intermediate 2048, top-8 every T <= 64 does), else MOE_ERR_UNSUPPORTED.  Each call first
+ * enqueues a small kernel that zeroes the scratch's ticket counter.  All calls on one device
+ * share its array: calls that overlap in time on one device (other streams, other host
+ * threads) race and give wrong results; serialise them. */
+MOE_MI355X_API moe_status moe_layer_decode_noalloc(
+    const moe_dims* d, const moe_experts* routed, const moe_experts* shared,
+    const uint16_t* x_bf16, const uint16_t* wr_bf16, const float* logit_bias, float* logits_out,
+    int32_t* topk_ids, float* topk_w, int32_t* sorted_pair, int32_t* expert_offsets,
+    int32_t* pair_pos, float* y_pairs, float* y_shared, const float* residual, float* out_f32,
+    uint16_t* out_bf16, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Helpers (same conventions).
  * ------------------------------------------------------------------------- */
