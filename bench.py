@@ -174,16 +174,25 @@ def decode_bench(args):
     router_b = c.E * c.H * 2
     x_b = c.H * 2
     # algorithmic bytes per launch of each kernel: weights + activations read + results written
+    P = c.T * c.k
     kb = {
-        # router GEMV + top-k + permutation: router weights, x, logits / ids / weights out
-        "decode_k1_route": router_b + x_b + c.E * 4 + c.k * 8 + (2 * c.k + c.E + 1) * 4,
-        # routed and shared gate/up: the 8 touched experts' gate/up, the shared gate/up, x in,
-        # h out (fp32 for the routed pairs and the shared expert)
-        "decode_k2_gateup": routed_gu_b + shared_gu_b + x_b + c.k * c.I * 4 + c.I * 4,
-        # routed and shared down + weighted combine: down weights, h in, y_pairs / y_shared / out
-        "decode_k3_down_combine": routed_dn_b + shared_dn_b + c.k * c.I * 4 + c.I * 4
-                                  + c.k * c.H * 4 + c.H * 4 + c.H * 4,
+        # router GEMV partials beside the shared gate/up: router and shared gate/up weights, x,
+        # the shared h out (bf16 hi + lo)
+        "decode_k1_route": router_b + shared_gu_b + x_b + c.T * c.I * 4,
+        # routing, routed gate/up beside the shared down: the touched experts' gate/up, the
+        # shared down weights, x and shared h in, routing outputs, routed h and y_shared out
+        "decode_k2_gateup": routed_gu_b + shared_dn_b + x_b + c.T * c.I * 4 + c.T * c.E * 4
+                            + (2 * c.k + c.E + 1) * 4 + P * c.I * 4 + c.T * c.H * 4,
+        # routed down: the touched experts' down weights, routed h in, y_pairs out
+        "decode_k3_down": routed_dn_b + P * c.I * 4 + P * c.H * 4,
+        # combine: y_pairs, y_shared, weights in, out
+        "decode_k4_combine": P * c.H * 4 + c.T * c.H * 4 + c.T * c.k * 4 + c.T * c.H * 4,
     }
+    expert_b0 = routed_gu_b + routed_dn_b + shared_gu_b + shared_dn_b
+    # the single-launch decode (up to 4 tokens): the whole layer's algorithmic bytes -- every
+    # weight, x in, out written, and the intermediates it exposes (logits, y_pairs, y_shared)
+    kb["decode_persistent"] = (expert_b0 + router_b + x_b + c.T * c.H * 4 + c.T * c.E * 4
+                               + P * c.H * 4 + c.T * c.H * 4)
     expert_b = routed_gu_b + routed_dn_b + shared_gu_b + shared_dn_b
     layer_b = expert_b + router_b + x_b + c.H * 4
     return dict(c=c, ms=ms, ms4=ms4, graph_ms=graph_ms, t_wall=t_wall, expert_b=expert_b, layer_b=layer_b, prof=prof,
@@ -426,10 +435,12 @@ def mx_decode_bench(args):
     prof = M.moe_profile_read()
     M.moe_profile_enable(False)
     mat = c.I * c.H * 17 // 32                     # one MXFP4 expert matrix: E2M1 codes + UE8M0 scales
-    kb = {"decode_k1_route": c.E * c.H * 2 + c.H * 2 + c.H + c.H // 32,
-          "decode_k2_gateup": c.k * 2 * mat + 2 * c.I * c.H * 2 + c.H + c.H // 32 + c.k * c.I * 33 // 32 + c.I * 4,
-          "decode_k3_down_combine": c.k * mat + c.I * c.H * 2 + c.k * c.I * 33 // 32 + c.I * 4
-                                    + c.k * c.H * 4 + 2 * c.H * 4}
+    # K1 router + x quantisation + shared gate/up; K2 routed gate/up + shared down; K3 routed
+    # down + combine (+ y_shared)
+    kb = {"decode_k1_route": c.E * c.H * 2 + c.H * 2 + c.H + c.H // 32 + 2 * c.I * c.H * 2 + c.I * 4,
+          "decode_k2_gateup": c.k * 2 * mat + c.I * c.H * 2 + c.H + c.H // 32 + c.I * 4
+                              + c.k * c.I * 33 // 32 + c.H * 4,
+          "decode_k3_down": c.k * mat + c.k * c.I * 33 // 32 + c.k * c.H * 4 + 2 * c.H * 4}
     expert_b = 3 * c.k * mat + 3 * c.I * c.H * 2
     return dict(c=c, ms=ms, prof=prof, kbytes=kb, expert_b=expert_b)
 
@@ -534,7 +545,7 @@ def decode_t64_bench(args):
     kb = {"decode_k1_route": router_b + c.T * c.H * 2 + c.T * c.E * 4,
           "decode_k2_gateup": u_avg * 2 * STQ_MAT_BYTES + 2 * c.I * c.H * 2 + c.T * c.H * 2
                               + (d.P + c.T) * c.I * 4,
-          "decode_k3_down_combine": u_avg * STQ_MAT_BYTES + c.I * c.H * 2 + (d.P + c.T) * c.I * 4
+          "decode_k3_down": u_avg * STQ_MAT_BYTES + c.I * c.H * 2 + (d.P + c.T) * c.I * 4
                                     + d.P * c.H * 4 + 2 * c.T * c.H * 4}
     return dict(c=c, ms=ms, U=u_avg, unique_b=unique_b, step_b=step_b, prof=prof, kbytes=kb)
 
@@ -605,7 +616,8 @@ def O_bf16_to_f32(bits):
 
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     "decode_k1_route": "k1s_router<", "decode_k2_gateup": "k2s_gateup<",
-    "decode_k3_down_combine": "k3_down_combine<", "mx_gateup": "mx_gemm_kernel<true, true>",
+    "decode_k3_down": "k3_down_pairs<", "decode_k4_combine": "combine_kernel",
+    "mx_gateup": "mx_gemm_kernel<true, true>",
     "mx_down": "mx_gemm_kernel<false, true>", "stq_gateup": "g16_kernel<0, true, 1>",
     "stq_down": "g16_kernel<0, false, 2>", "mxdec_k2_gateup": "k2s_gateup_mx<",
     "mxdec_k3_down_combine": "k3_down_combine_mx<", "copy": "neg_kernel"}
@@ -614,7 +626,8 @@ _DEC_SRC = "bit_quantized_moe_softmax_amd/csrc/decode_fused.hip"
 _MX_SRC = "bit_quantized_moe_softmax_amd/csrc/mx_gemm.hip"
 _G16_SRC = "bit_quantized_moe_softmax_amd/csrc/gemm16.hip"
 TRAFFIC_SOURCES = {"decode_k1_route": _DEC_SRC, "decode_k2_gateup": _DEC_SRC,
-                   "decode_k3_down_combine": _DEC_SRC, "mx_gateup": _MX_SRC, "mx_down": _MX_SRC,
+                   "decode_k3_down": _DEC_SRC, "decode_k4_combine": "bit_quantized_moe_softmax_amd/csrc/misc.hip",
+                   "mx_gateup": _MX_SRC, "mx_down": _MX_SRC,
                    "stq_gateup": _G16_SRC, "stq_down": _G16_SRC, "mxdec_k2_gateup": _DEC_SRC,
                    "mxdec_k3_down_combine": _DEC_SRC}
 
@@ -675,7 +688,7 @@ def load_traffic():
             if line.startswith("traffic-json: "):
                 data = json.loads(line[len("traffic-json: "):])
                 return {k: v["traffic_bytes"] for k, v in data["kernels"].items()
-                        if v["source_sha256_16"] == source_hash(k)}
+                        if k in TRAFFIC_SOURCES and v["source_sha256_16"] == source_hash(k)}
     except OSError:
         pass
     return {}
@@ -843,6 +856,8 @@ def main():
     kern = {}
     for name, nbytes in dec["kbytes"].items():
         us, n = dec["prof"][name]
+        if n == 0:
+            continue   # a kernel of the other decode structure
         kern[name] = {"avg_us": round(us, 3), "launches": n, "algorithmic_bytes": nbytes,
                       "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None}
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
@@ -963,6 +978,8 @@ def main():
             kern = {}
             for name, nbytes in t64["kbytes"].items():
                 us, n = t64["prof"][name]
+                if n == 0:
+                    continue
                 kern[name] = {"avg_us": round(us, 3), "launches": n, "algorithmic_bytes": round(nbytes),
                               "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None}
             dom = max(kern, key=lambda k: kern[k]["avg_us"])
