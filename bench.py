@@ -183,16 +183,10 @@ def decode_bench(args):
         # shared down weights, x and shared h in, routing outputs, routed h and y_shared out
         "decode_k2_gateup": routed_gu_b + shared_dn_b + x_b + c.T * c.I * 4 + c.T * c.E * 4
                             + (2 * c.k + c.E + 1) * 4 + P * c.I * 4 + c.T * c.H * 4,
-        # routed down: the touched experts' down weights, routed h in, y_pairs out
-        "decode_k3_down": routed_dn_b + P * c.I * 4 + P * c.H * 4,
-        # combine: y_pairs, y_shared, weights in, out
-        "decode_k4_combine": P * c.H * 4 + c.T * c.H * 4 + c.T * c.k * 4 + c.T * c.H * 4,
+        # routed down + combine: the touched experts' down weights, routed h and y_shared in,
+        # y_pairs and out written
+        "decode_k3_down_combine": routed_dn_b + P * c.I * 4 + c.T * c.H * 4 + P * c.H * 4 + c.T * c.H * 4,
     }
-    expert_b0 = routed_gu_b + routed_dn_b + shared_gu_b + shared_dn_b
-    # the single-launch decode (up to 4 tokens): the whole layer's algorithmic bytes -- every
-    # weight, x in, out written, and the intermediates it exposes (logits, y_pairs, y_shared)
-    kb["decode_persistent"] = (expert_b0 + router_b + x_b + c.T * c.H * 4 + c.T * c.E * 4
-                               + P * c.H * 4 + c.T * c.H * 4)
     expert_b = routed_gu_b + routed_dn_b + shared_gu_b + shared_dn_b
     layer_b = expert_b + router_b + x_b + c.H * 4
     return dict(c=c, ms=ms, ms4=ms4, graph_ms=graph_ms, t_wall=t_wall, expert_b=expert_b, layer_b=layer_b, prof=prof,
@@ -440,7 +434,7 @@ def mx_decode_bench(args):
     kb = {"decode_k1_route": c.E * c.H * 2 + c.H * 2 + c.H + c.H // 32 + 2 * c.I * c.H * 2 + c.I * 4,
           "decode_k2_gateup": c.k * 2 * mat + c.I * c.H * 2 + c.H + c.H // 32 + c.I * 4
                               + c.k * c.I * 33 // 32 + c.H * 4,
-          "decode_k3_down": c.k * mat + c.k * c.I * 33 // 32 + c.k * c.H * 4 + 2 * c.H * 4}
+          "decode_k3_down_combine": c.k * mat + c.k * c.I * 33 // 32 + c.k * c.H * 4 + 2 * c.H * 4}
     expert_b = 3 * c.k * mat + 3 * c.I * c.H * 2
     return dict(c=c, ms=ms, prof=prof, kbytes=kb, expert_b=expert_b)
 
@@ -545,7 +539,7 @@ def decode_t64_bench(args):
     kb = {"decode_k1_route": router_b + c.T * c.H * 2 + c.T * c.E * 4,
           "decode_k2_gateup": u_avg * 2 * STQ_MAT_BYTES + 2 * c.I * c.H * 2 + c.T * c.H * 2
                               + (d.P + c.T) * c.I * 4,
-          "decode_k3_down": u_avg * STQ_MAT_BYTES + c.I * c.H * 2 + (d.P + c.T) * c.I * 4
+          "decode_k3_down_combine": u_avg * STQ_MAT_BYTES + c.I * c.H * 2 + (d.P + c.T) * c.I * 4
                                     + d.P * c.H * 4 + 2 * c.T * c.H * 4}
     return dict(c=c, ms=ms, U=u_avg, unique_b=unique_b, step_b=step_b, prof=prof, kbytes=kb)
 
@@ -616,8 +610,7 @@ def O_bf16_to_f32(bits):
 
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     "decode_k1_route": "k1s_router<", "decode_k2_gateup": "k2s_gateup<",
-    "decode_k3_down": "k3_down_pairs<", "decode_k4_combine": "combine_kernel",
-    "mx_gateup": "mx_gemm_kernel<true, true>",
+    "decode_k3_down_combine": "k3_down_combine<", "mx_gateup": "mx_gemm_kernel<true, true>",
     "mx_down": "mx_gemm_kernel<false, true>", "stq_gateup": "g16_kernel<0, true, 1>",
     "stq_down": "g16_kernel<0, false, 2>", "mxdec_k2_gateup": "k2s_gateup_mx<",
     "mxdec_k3_down_combine": "k3_down_combine_mx<", "copy": "neg_kernel"}
@@ -626,8 +619,7 @@ _DEC_SRC = "bit_quantized_moe_softmax_amd/csrc/decode_fused.hip"
 _MX_SRC = "bit_quantized_moe_softmax_amd/csrc/mx_gemm.hip"
 _G16_SRC = "bit_quantized_moe_softmax_amd/csrc/gemm16.hip"
 TRAFFIC_SOURCES = {"decode_k1_route": _DEC_SRC, "decode_k2_gateup": _DEC_SRC,
-                   "decode_k3_down": _DEC_SRC, "decode_k4_combine": "bit_quantized_moe_softmax_amd/csrc/misc.hip",
-                   "mx_gateup": _MX_SRC, "mx_down": _MX_SRC,
+                   "decode_k3_down_combine": _DEC_SRC, "mx_gateup": _MX_SRC, "mx_down": _MX_SRC,
                    "stq_gateup": _G16_SRC, "stq_down": _G16_SRC, "mxdec_k2_gateup": _DEC_SRC,
                    "mxdec_k3_down_combine": _DEC_SRC}
 

@@ -58,7 +58,6 @@ constexpr int kMaxT = 64;
 constexpr int kMaxE = 256;
 constexpr int kDnWaves = 8;        // waves of a down/combine workgroup
 constexpr int kHLdsPairs = 8;      // routed pairs (+ tokens) whose h fits the down kernel's LDS
-constexpr int kMaxEntryPairs = 8;  // pairs of one down work entry (a half-unit)
 constexpr int kMaxDevices = 64;
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every record: loads return 0
 // Weight blocks a streaming wave keeps in flight.  HBM saturates at ~8 MB in flight across
@@ -92,11 +91,6 @@ struct DecodeArgs {
   int n_xq_wg;      // MXFP4: x quantisation workgroups of the first kernel
   int h_lds;        // down kernel: all routed (and, without ysh_ready, shared) h staged in LDS
   int ysh_ready;    // y_shared was written by an earlier kernel: the down kernel adds it
-  int h_cap;        // k3_down_pairs: pairs per entry its LDS regions hold (<= kMaxEntryPairs)
-  // persistent decode: first item of each kind (router, routing, shared gate/up, routed
-  // gate/up, shared down, routed down, combine), the item count, and the counters
-  int iX, iS, iU, iD, iY, iC, n_items;
-  int* pc;
   // MXFP4 routed experts: E4M3 x codes [T][H] then UE8M0 scales [T][H/32] (written by K1);
   // E4M3 h codes [P][I] then scales [P][I/32] (over the bf16 h region)
   uint8_t* xq;
@@ -361,8 +355,10 @@ struct StqStream {
 // The same stream with the code words staged through a per-wave LDS buffer.  A wave's 16
 // weight rows are consecutive rows of one matrix, so chunk c (blocks CB c .. CB c + CB - 1
 // of every row) is 16 runs of 40 CB contiguous bytes: fetched as 16-byte pieces (fully
-// used cache lines, a quarter of the requests of per-lane 8- and 2-byte reads) two chunks
+// used cache lines, a quarter of the requests of per-lane 8- and 2-byte reads) DEPTH chunks
 // ahead in registers, written to LDS when their turn comes, and read from there per block.
+// (Four or six chunks ahead measured slower at one token: 55-56 us per layer against 48 us
+// with two; the extra loads only lengthen the memory queue the routing and x loads wait in.)
 // LDS rows are padded so the 16 lanes reading one column group hit distinct banks.
 template <int NB, int DEPTH = 2>
 struct StqStreamL {
@@ -454,29 +450,14 @@ struct StqStreamL {
       for (int t = 0; t < 4; ++t) wc[t] = wn[t];
       float dj = d;
       if (h == 0) {
-#ifdef MOE_ABL_NOLUT
-#pragma unroll
-        for (int t = 0; t < 4; ++t) wn[t] = as_bf16x8(make_uint4(qj.x, qj.y ^ t, qhj, qj.x + t));
-#else
         stq_half_w(lut, qj, qhj, 1, wn);
-#endif
       } else if (j + 1 < NB) {
         next(j + 1, qj, qhj, d);
-#ifdef MOE_ABL_NOLUT
-#pragma unroll
-        for (int t = 0; t < 4; ++t) wn[t] = as_bf16x8(make_uint4(qj.x, qj.y ^ t, qhj, qj.x + t));
-#else
         stq_half_w(lut, qj, qhj, 0, wn);
-#endif
       }
       uint4 av[4];
-#ifdef MOE_ABL_NOA
-#pragma unroll
-      for (int t = 0; t < 4; ++t) av[t] = make_uint4(0x3F803F80u + j, 0x3F803F80u ^ t, h, 0x3F803F80u);
-#else
 #pragma unroll
       for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * (4 * h + t));
-#endif
       f32x4_t& bh = h ? b1 : b0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) bh = mfma16(as_bf16x8(av[t]), wc[t], bh);
@@ -532,7 +513,7 @@ struct RowStage {
 // Router partial for one (16 experts, 16 tokens, quarter of K): wave w takes K chunk
 // 4 q + w of 16 with every load up front; the four waves meet in LDS in order and wave 0
 // writes rpart[q][t][e].  Experts and tokens past the end read as zeros.
-template <int HB, bool AG = false>
+template <int HB>
 __device__ __forceinline__ void router_unit(const DecodeArgs& a, int rw, float (*s_red)[4][64]) {
   constexpr int H = HB * 256, KC = H / kRouterChunks, NS = KC / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -566,11 +547,7 @@ __device__ __forceinline__ void router_unit(const DecodeArgs& a, int rw, float (
     for (int i = 0; i < 4; ++i) {
       const int e = et * 16 + 4 * g + i;
       const float v = ((s_red[0][i][lane] + s_red[1][i][lane]) + s_red[2][i][lane]) + s_red[3][i][lane];
-      if (e < a.E) {
-        float* dst = a.rpart + ((size_t)q * a.T + tok) * a.E + e;
-        if constexpr (AG) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else *dst = v;
-      }
+      if (e < a.E) a.rpart[((size_t)q * a.T + tok) * a.E + e] = v;
     }
   }
 }
@@ -1118,7 +1095,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k
 // hi + lo rows from `hs` (LDS).  Writes y_shared and, with ACC, adds it into the wave's
 // combine sums (a 16-row slice: row NR w + r of the slice).
 // NR rows per wave; SR: row stride of the per-wave output sums in LDS.
-template <int HB, int IB, int NR, bool ACC, int SR = 16, bool AG = false>
+template <int HB, int IB, int NR, bool ACC, int SR = 16>
 struct SharedDown {
   static constexpr int H = HB * 256, I = IB * 256, NJ = (IB + 1) / 2, NI = NR * NJ, R = NI < 4 ? NI : 4;
   uint4 w[R];
@@ -1174,9 +1151,7 @@ struct SharedDown {
         for (int r = 0; r < NR; ++r) {
           const float v = wave_sum(acc[r][t]);
           if (lane == 0) {
-            float* dst = a.y_shared + (size_t)t * H + row0 + NR * wave + r;
-            if constexpr (AG) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            else *dst = v;
+            a.y_shared[(size_t)t * H + row0 + NR * wave + r] = v;
             if constexpr (ACC) s_acc[(wave * T + t) * SR + NR * wave + r] += v;
           }
         }
@@ -1230,12 +1205,9 @@ __device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi,
   const int mat = wave & 1, tl = wave >> 1;
   const int row0 = (2 * tp + tl) * 16;
   const size_t wrow = (size_t)e * I + row0 + col;
-#ifndef MOE_GU_DEPTH
-#define MOE_GU_DEPTH 2
-#endif
-  StqStreamL<HB, MOE_GU_DEPTH> st;
+  StqStreamL<HB> st;
   st.issue((mat ? a.uc : a.gc) + (wrow - col) * HB * 40, (mat ? a.us : a.gs) + wrow * HB,
-           s_cw + wave * StqStreamL<HB, MOE_GU_DEPTH>::BYTES);
+           s_cw + wave * StqStreamL<HB>::BYTES);
   const int tok = R.utok[pos0 + (col < ntok ? col : ntok - 1)];
   const f32x4_t acc = st.run_lds(s_lut, s_x + tok * H + 64 * g);
 #pragma unroll
@@ -1475,590 +1447,6 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
       a.out[o] = v;
       if (a.out_bf16) a.out_bf16[o] = (uint16_t)f32_to_bf16_rne(v);
     }
-  }
-}
-
-// Routed down projections only, one work item per (entry = one expert's run of <= cap pairs,
-// 128 output rows): the entry's h (bf16 hi rows, then lo rows) is staged in LDS -- loads
-// issued first, then the weight stream, then the LDS writes, which wait for the older h
-// loads only -- and each of the 8 waves streams one 16-row tile of the expert's down matrix
-// over all of I (every block of it in flight at once) and writes the pairs' y.  A pair takes
-// two adjacent A rows (hi, lo) of the MFMA.  The weighted combine runs in the next kernel.
-// Every workgroup stages only its own entry's h (8 KB per pair at I = 2048), where a
-// workgroup of one 16-row output slice over all pairs stages every pair's.
-template <int HB, int IB>
-__global__ __launch_bounds__(64 * kDnWaves) void k3_down_pairs(DecodeArgs a) {
-  constexpr int H = HB * 256, I = IB * 256, NSL = H / 128;
-  constexpr int kLoPad = 32;                      // lo rows 64 bytes past the hi rows' end
-  constexpr int PER = (2 * kMaxEntryPairs * I / 8 + 64 * kDnWaves - 1) / (64 * kDnWaves);
-  extern __shared__ __align__(16) uint16_t s_hd[];   // hi rows [cap][I], then lo rows
-  __shared__ uint2 s_lut[32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int ent = blockIdx.x / NSL, slice = blockIdx.x % NSL;
-  if (ent >= a.wl[2]) return;                     // uniform over the workgroup
-  const int4 hent = a.hl[ent];
-  const int e = hent.x, pos0 = hent.y, nq = hent.z;
-  const int cap = a.h_cap;                        // pairs per entry the LDS regions hold
-  const int lo_off = cap * I + kLoPad;
-  // h pieces (16 bytes): region 0 = hi rows pos0 .. pos0 + nq - 1, region 1 = lo rows;
-  // pieces past the entry's rows read nothing (offset past the buffer) and write zeros
-  const rsrc_t rh = make_rsrc(a.h_hi, a.h_bytes);
-  const int rpieces = kMaxEntryPairs * I / 8, valid = nq * I / 8;
-  uint4 hv[PER];
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int i = tid + 64 * kDnWaves * m;
-    const int reg = i / rpieces, w = i % rpieces;
-    const uint32_t o = (reg < 2 && w < valid)
-                           ? (reg ? a.h_lo_bytes : 0u) + 2u * ((uint32_t)pos0 * I + 8 * w) : kOOB;
-    hv[m] = bload16(rh, o);
-  }
-  build_lut(s_lut);
-  const int r16 = slice * 128 + wave * 16;
-  StqStream<IB, 8> st;
-  {
-    const size_t wrow = (size_t)e * H + r16 + col;
-    st.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
-  }
-  // branch-free (a load whose only use sits in a branch is sunk into it): pieces past the
-  // regions' capacity all write one spare 16-byte slot after the lo rows
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int i = tid + 64 * kDnWaves * m;
-    const int reg = i / rpieces, w = i % rpieces;
-    const int dst = (reg < 2 && w < cap * I / 8) ? reg * lo_off + 8 * w : lo_off + cap * I;
-    *reinterpret_cast<uint4*>(s_hd + dst) = hv[m];
-  }
-  lds_barrier();
-  const int sp2 = col >> 1;
-  const int pr = sp2 < nq ? sp2 : 0;
-  const f32x4_t acc = st.run_lds(s_lut, s_hd + (col & 1) * lo_off + pr * I + 64 * g);
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int p = 2 * g + m;
-    if (p < nq) a.y_pairs[(size_t)(pos0 + p) * H + r16 + col] = acc[2 * m] + acc[2 * m + 1];
-  }
-}
-
-// ============================================================================ persistent decode
-// Up to kXT tokens with STQ1_0 routed experts in ONE launch.  The layer is cut into work items
-// in an order where every item depends only on earlier ones:
-//   R  router partials, (16 experts x 16 tokens x a quarter of K) each; the workgroup that
-//      finishes the last one routes every token at once: top-k, pair order, units (one per
-//      selected expert, with its tokens)
-//   S  shared gate/up, one row of I per wave
-//   U  routed gate/up, (unit, 32 rows of I): wave = (16-row tile, gate|up)   <- the routing
-//   D  shared down, 16 output rows                                          <- every S
-//   Y  routed down, (unit, 128 output rows): 2 16-row tiles per wave        <- the unit's U
-// and the combine of each 128-row slice of the output (y_shared + sum_j w_j y_j, + residual)
-// is done by whichever Y or D item of the slice arrives last.  Workgroup b takes items
-// b, b + G, b + 2G, ... (G = the grid, sized so every workgroup is resident at once): the
-// shared expert's streams fill the time the router's short chain and the routing take, with
-// no kernel boundary between the steps.  Data handed from one item to another goes through
-// agent-coherent accesses (stores written through to memory, loads that miss the per-XCD
-// caches: cache policy sc1); a producer waits for its stores (vmcnt) before it counts, a
-// consumer polls the count (thread 0, s_sleep between polls) before it loads.  Counters sit
-// 4 KB apart (polled and counted lines shared by many workgroups serialise).  Every wait
-// gives up after a bounded number of polls and sets an abort flag every other wait checks,
-// so a wrong count can only give wrong results (NaN outputs), never a hang.  The last
-// workgroup to leave zeroes the counters for the next call.
-
-constexpr int kPcRouter = 0, kPcRoute = 1, kPcSgu = 2, kPcExit = 5, kPcAbort = 6, kPcUnit = 8;
-constexpr int kPcSlice = kPcUnit + kMaxPL;   // per 128-row output slice (H <= 8192: 64)
-constexpr int kPcCount = kPcSlice + 64;      // counters
-static_assert(kPcCount <= 256, "cleared by one workgroup of 256 threads");
-#ifndef MOE_PCSTRIDE
-#define MOE_PCSTRIDE 1024
-#endif
-#ifndef MOE_PSLEEP
-#define MOE_PSLEEP 8
-#endif
-constexpr int kPcStride = MOE_PCSTRIDE;      // words between counters
-constexpr int kPcWords = kPcCount * kPcStride;
-constexpr int kSpinLimit = (1 << 22) / MOE_PSLEEP;   // polls before a wait gives up
-constexpr int kAg = 16;                      // buffer cache policy sc1 (agent-coherent)
-
-__device__ __forceinline__ int ld_ag(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_ag(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_ag(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint4 bload16_ag(rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kAg));
-}
-__device__ __forceinline__ uint32_t bload4_ag(rsrc_t r, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kAg);
-}
-// h as bf16 hi + lo, element `i` of the hi array and i + lo_elems of the lo array (rsrc r)
-__device__ __forceinline__ void store_hilo_ag(rsrc_t r, uint32_t i, uint32_t lo_elems, float h) {
-  const uint32_t hi = f32_to_bf16_rne(h);
-  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hi, r, 2u * i, 0, kAg);
-  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(h - bf16_to_f32(hi)), r,
-                                        2u * (i + lo_elems), 0, kAg);
-}
-
-// Thread 0 polls counter idx until it reaches target (or the abort flag is set, or the poll
-// limit is reached, which sets it); the workgroup meets at a barrier.
-__device__ __forceinline__ void p_wait(int* pc, int idx, int target) {
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (ld_ag(pc + idx * kPcStride) < target) {
-      if ((n & 15) == 15 && ld_ag(pc + kPcAbort * kPcStride)) break;
-      if (++n > kSpinLimit) {
-        st_ag(pc + kPcAbort * kPcStride, 1);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(MOE_PSLEEP);
-    }
-  }
-  __syncthreads();
-}
-// Every wave's stores have completed; then thread 0 counts the item and returns the count
-// before it (to thread 0; others get -1).
-__device__ __forceinline__ int p_publish(int* pc, int idx) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  int old = -1;
-  if (threadIdx.x == 0)
-    old = __hip_atomic_fetch_add(pc + idx * kPcStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return old;
-}
-
-// Per-workgroup state kept in LDS across items: the routing (unit table with each unit's
-// tokens packed in .w, 8 bits each) once this workgroup has read it.
-struct PState {
-  int route_seen, sgu_seen, router_seen, n_units, x_staged, flag;
-  int4 ut[kMaxPL];
-};
-
-// The routing of all T tokens, by the workgroup that finished the last router item: top-k
-// per token (wave t) from the partials (agent-coherent loads), the stable pair order and the
-// units in LDS, then the outputs.  What later items read (units, pair_pos, the weights, the
-// unit count) is written agent-coherent; logits, ids, sorted_pair and offsets are outputs only.
-__device__ __forceinline__ void p_route(const DecodeArgs& a, SmallRoute& R, PState& st) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = a.T, E = a.E, k = a.k, P = T * k;
-  TopkIn in;
-  {
-    const int t = min(wave, T - 1);
-    const rsrc_t rp = make_rsrc(a.rpart, (uint32_t)kRouterParts * T * E * 4);
-    const rsrc_t rb = make_rsrc(a.bias, a.bias ? (uint32_t)E * 4 : 0u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = i * 64 + lane < E ? i * 64 + lane : 0;
-#pragma unroll
-      for (int c = 0; c < kRouterParts; ++c)
-        in.part[i][c] = __uint_as_float(bload4_ag(rp, 4u * (uint32_t)((c * T + t) * E + e)));
-      in.bias[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, i * 64 + lane < E ? 4u * (i * 64 + lane) : kOOB, 0, 0));
-    }
-  }
-  const TopkSum ls = topk_sums(a, in);
-  if (wave < T) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i * 64 + lane < E) a.logits[(size_t)wave * E + i * 64 + lane] = ls.s[i];
-  }
-  small_route_topk(a, R, ls, false);
-  small_route_units(a, R, false);
-  for (int u = tid; u < R.n_units; u += kWG) {
-    int4 v = R.ut[u];
-    int toks = 0;
-    for (int jj = 0; jj < v.z; ++jj) toks |= (R.sorted[v.y + jj] / k) << (8 * jj);
-    v.w = toks;
-    int* dst = reinterpret_cast<int*>(a.ut + u);
-    st_ag(dst, v.x); st_ag(dst + 1, v.y); st_ag(dst + 2, v.z); st_ag(dst + 3, v.w);
-  }
-  for (int f = tid; f < P; f += kWG) {
-    a.sorted_pair[f] = R.sorted[f];
-    st_ag(a.pair_pos + R.sorted[f], f);
-    a.ids[f] = R.ids[f];
-    st_ag(a.w + f, __int_as_float(R.wb[f]));
-  }
-  for (int e = tid; e <= E; e += kWG) {
-    int before = 0;
-    for (int f = 0; f < P; ++f) before += R.ids[f] < e;
-    a.offsets[e] = before;
-  }
-  if (tid == 0) st_ag(a.wl + 1, R.n_units);
-  p_publish(a.pc, kPcRoute);
-}
-
-// The routing result in this workgroup's state: one wait, then the unit count and every unit
-// entry in one round of loads (entries past the count are never used).
-__device__ __forceinline__ void p_need_route(const DecodeArgs& a, PState& st) {
-  if (!st.route_seen) {
-    p_wait(a.pc, kPcRoute, 1);
-    const int tid = threadIdx.x;
-    const int P = a.T * a.k, mu = P < a.E ? P : a.E;
-    const rsrc_t ru = make_rsrc(a.ut, (uint32_t)mu * 16);
-    const rsrc_t rw = make_rsrc(a.wl, 16);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (tid < kMaxPL) v = bload16_ag(ru, tid < mu ? 16u * tid : kOOB);
-    const int nu = (int)bload4_ag(rw, 4u);
-    if (tid < kMaxPL) st.ut[tid] = __builtin_bit_cast(int4, v);
-    if (tid == 0) {
-      st.n_units = nu;
-      st.route_seen = 1;
-    }
-    __syncthreads();
-  }
-}
-
-template <int HB, int XR>
-__device__ __forceinline__ void p_stage_x(const DecodeArgs& a, uint16_t* s_x, PState& st) {
-  constexpr int H = HB * 256;
-  if (!st.x_staged) {
-    RowStage<H, kWG, XR> xs;
-    xs.issue(a.T, [&](int r) { return a.x + (size_t)r * H; });
-    xs.commit(a.T, s_x);
-    __syncthreads();
-    if (threadIdx.x == 0) st.x_staged = 1;
-    __syncthreads();
-  }
-}
-
-// S: shared gate/up of rows 4 sw + wave (x in LDS); h as bf16 hi + lo, agent-coherent; four
-// 16-byte chunks of each matrix in flight per wave.
-template <int HB, int IB, int XR>
-__device__ __forceinline__ void p_shared_gateup(const DecodeArgs& a, int sw, const uint16_t* s_x) {
-  constexpr int H = HB * 256, I = IB * 256, NJ = H / 512, RS = NJ < 4 ? NJ : 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int T = a.T;
-  const int row = sw * kNW + wave;
-  const uint16_t* gp = a.sg + (size_t)row * H + 8 * lane;
-  const uint16_t* up = a.su + (size_t)row * H + 8 * lane;
-  uint4 bg[RS], bu[RS];
-#pragma unroll
-  for (int c = 0; c < RS; ++c) {
-    bg[c] = ntload16(gp + 512 * c);
-    bu[c] = ntload16(up + 512 * c);
-  }
-  float ag[XR], au[XR];
-#pragma unroll
-  for (int t = 0; t < XR; ++t) { ag[t] = 0.f; au[t] = 0.f; }
-#pragma unroll
-  for (int c = 0; c < NJ; ++c) {
-    const uint4 wg = bg[c % RS], wu = bu[c % RS];
-    if (c + RS < NJ) {
-      bg[c % RS] = ntload16(gp + 512 * (c + RS));
-      bu[c % RS] = ntload16(up + 512 * (c + RS));
-    }
-#pragma unroll
-    for (int t = 0; t < XR; ++t) {
-      if (t < T) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(s_x + t * H + 8 * lane + 512 * c);
-        ag[t] = dot8(wg, xv, ag[t]);
-        au[t] = dot8(wu, xv, au[t]);
-      }
-    }
-  }
-  const rsrc_t rhs = make_rsrc(a.hs, (uint32_t)T * I * 4);
-#pragma unroll
-  for (int t = 0; t < XR; ++t) {
-    if (t < T) {
-      const float gs = wave_sum(ag[t]), us = wave_sum(au[t]);
-      if (lane == 0) store_hilo_ag(rhs, (uint32_t)(t * I + row), (uint32_t)(T * I), silu_mul(gs, us));
-    }
-  }
-  p_publish(a.pc, kPcSgu);
-}
-
-// U: routed gate/up of (unit, 32 rows of I): wave = (16-row tile, gate|up); the code words
-// four chunks ahead; h agent-coherent.
-template <int HB, int IB>
-__device__ __forceinline__ void p_routed_gateup(const DecodeArgs& a, int wi, const uint2* s_lut,
-                                                const uint16_t* s_x, float (*s_red)[2][4][64],
-                                                uint8_t* s_cw, const PState& st) {
-  constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int un_i = wi / NTP, tp = wi % NTP;
-  if (un_i >= st.n_units) return;                       // uniform: no such unit
-  const int4 un = st.ut[un_i];
-  const int e = un.x, pos0 = un.y, ntok = un.z;
-  const int mat = wave & 1, tl = wave >> 1;
-  const int row0 = (2 * tp + tl) * 16;
-  const size_t wrow = (size_t)e * I + row0 + col;
-  StqStreamL<HB, 4> sl;
-  sl.issue((mat ? a.uc : a.gc) + (wrow - col) * HB * 40, (mat ? a.us : a.gs) + wrow * HB,
-           s_cw + wave * StqStreamL<HB, 4>::BYTES);
-  const int tok = (un.w >> (8 * (col < ntok ? col : ntok - 1))) & 0xFF;
-  const f32x4_t acc = sl.run_lds(s_lut, s_x + tok * H + 64 * g);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s_red[tl][mat][i][lane] = acc[i];
-  __syncthreads();
-  if (mat == 0) {
-    const rsrc_t rh = make_rsrc(a.h_hi, a.h_bytes);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = 4 * g + i;
-      if (slot < ntok)
-        store_hilo_ag(rh, (uint32_t)((pos0 + slot) * I + row0 + col), a.h_lo_bytes / 2,
-                      silu_mul(s_red[tl][0][i][lane], s_red[tl][1][i][lane]));
-    }
-  }
-  p_publish(a.pc, kPcUnit + un_i);
-}
-
-// The combine of output rows 128 sl .. 128 sl + 127 of every token, in the order of
-// moe_combine: y_shared + sum_j w_j y_j, then + residual (agent-coherent loads of what other
-// items wrote).
-template <int HB>
-__device__ __forceinline__ void p_slice_combine(const DecodeArgs& a, int sl) {
-  constexpr int H = HB * 256;
-  const int k = a.k, T = a.T;
-  const rsrc_t ry = make_rsrc(a.y_pairs, (uint32_t)T * k * H * 4);
-  const rsrc_t rs = make_rsrc(a.y_shared, a.y_shared ? (uint32_t)T * H * 4 : 0u);
-  const rsrc_t rw = make_rsrc(a.w, (uint32_t)T * k * 4);
-  const rsrc_t rp = make_rsrc(a.pair_pos, (uint32_t)T * k * 4);
-  const bool abort = ld_ag(a.pc + kPcAbort * kPcStride) != 0;
-  for (int i = threadIdx.x; i < T * 128; i += kWG) {
-    const int t = i >> 7, h = sl * 128 + (i & 127);
-    float acc = __uint_as_float(bload4_ag(rs, a.y_shared ? 4u * (uint32_t)(t * H + h) : kOOB));
-    float wj[32];
-    int pj[32];
-    for (int j = 0; j < k; ++j) {
-      wj[j] = __uint_as_float(bload4_ag(rw, 4u * (uint32_t)(t * k + j)));
-      pj[j] = (int)bload4_ag(rp, 4u * (uint32_t)(t * k + j));
-    }
-    for (int j = 0; j < k; ++j)
-      acc = fmaf(wj[j], __uint_as_float(bload4_ag(ry, 4u * ((uint32_t)pj[j] * H + h))), acc);
-    if (a.residual) acc += a.residual[(size_t)t * H + h];
-    if (abort) acc = NAN;   // a wait gave up
-    a.out[(size_t)t * H + h] = acc;
-    if (a.out_bf16) a.out_bf16[(size_t)t * H + h] = (uint16_t)f32_to_bf16_rne(acc);
-  }
-}
-
-// Arrival at output slice sl (after this item's stores); the last arrival combines it.
-template <int HB>
-__device__ __forceinline__ void p_arrive(const DecodeArgs& a, int sl, PState& st) {
-  const int old = p_publish(a.pc, kPcSlice + sl);
-  const int target = st.n_units + (a.sg ? 8 : 0);   // the units' Y items and 8 D items
-  if (threadIdx.x == 0) st.flag = old == target - 1;
-  __syncthreads();
-  if (st.flag) p_slice_combine<HB>(a, sl);
-}
-
-// D: shared down of 16 output rows (4 per wave); the shared h staged from agent-coherent
-// loads; y_shared agent-coherent.
-template <int HB, int IB, int XR>
-__device__ __forceinline__ void p_shared_down(const DecodeArgs& a, int sw, uint16_t* s_h, PState& st) {
-  constexpr int I = IB * 256;
-  constexpr int PER = (XR * I / 4 + kWG - 1) / kWG;
-  p_need_route(a, st);
-  if (!st.sgu_seen) {
-    p_wait(a.pc, kPcSgu, a.iU - a.iS);
-    if (threadIdx.x == 0) st.sgu_seen = 1;
-  }
-  const int n16 = a.T * I / 4;
-  const int row0 = sw * 16;
-  const rsrc_t rhs = make_rsrc(a.hs, (uint32_t)a.T * I * 4);
-  uint4 v[PER];
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int i = threadIdx.x + kWG * m;
-    v[m] = bload16_ag(rhs, i < n16 ? 16u * i : kOOB);
-  }
-  SharedDown<HB, IB, 4, false, 16, true> sdn;
-  sdn.issue(a, row0);
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int i = threadIdx.x + kWG * m;
-    reinterpret_cast<uint4*>(s_h)[i < n16 ? i : n16] = v[m];   // slot n16: spare
-  }
-  lds_barrier();
-  sdn.run(a, row0, s_h, nullptr);
-  p_arrive<HB>(a, row0 / 128, st);
-}
-
-// Y: routed down of (unit, 128 output rows): the unit's h (hi rows, then lo rows) staged from
-// agent-coherent loads once its gate/up items are all counted; wave = two 16-row tiles over
-// all of I, every code word of both in flight at once, one A read for both tiles' MFMAs;
-// y_pairs agent-coherent.
-template <int HB, int IB>
-__device__ __forceinline__ void p_routed_down(const DecodeArgs& a, int yi, const uint2* s_lut,
-                                              uint16_t* s_hd, PState& st) {
-  constexpr int H = HB * 256, I = IB * 256, NSL = H / 128, NTP = I / 32;
-  constexpr int kLoPad = 32;
-  constexpr int PER = (2 * kXT * I / 8 + kWG - 1) / kWG;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int u = yi / NSL, slice = yi % NSL;
-  if (u >= st.n_units) return;                    // uniform: no such unit, no arrival
-  p_wait(a.pc, kPcUnit + u, NTP);
-  const int4 un = st.ut[u];
-  const int e = un.x, pos0 = un.y, nq = un.z;
-  const int cap = a.h_cap, lo_off = cap * I + kLoPad;
-  const rsrc_t rh = make_rsrc(a.h_hi, a.h_bytes);
-  const int rpieces = kXT * I / 8, valid = nq * I / 8;
-  uint4 hv[PER];
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int i = tid + kWG * m;
-    const int reg = i / rpieces, w = i % rpieces;
-    const uint32_t o = (reg < 2 && w < valid) ? (reg ? a.h_lo_bytes : 0u) + 2u * ((uint32_t)pos0 * I + 8 * w) : kOOB;
-    hv[m] = bload16_ag(rh, o);
-  }
-  const int r0 = slice * 128 + wave * 32;         // this wave's two tiles: r0, r0 + 16
-  StqStream<IB, 8> s0, s1;
-  {
-    const size_t wrow = (size_t)e * H + r0 + col;
-    s0.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
-    s1.issue(a.dc + (wrow + 16) * IB * 40, a.ds + (wrow + 16) * IB);
-  }
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int i = tid + kWG * m;
-    const int reg = i / rpieces, w = i % rpieces;
-    const int dst = (reg < 2 && w < cap * I / 8) ? reg * lo_off + 8 * w : lo_off + cap * I;
-    *reinterpret_cast<uint4*>(s_hd + dst) = hv[m];
-  }
-  lds_barrier();
-  const int sp2 = col >> 1;
-  const int pr = sp2 < nq ? sp2 : 0;
-  const uint16_t* a_lds = s_hd + (col & 1) * lo_off + pr * I + 64 * g;
-  // both tiles per half block: one set of A reads feeds 8 MFMAs
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-#pragma unroll
-  for (int j = 0; j < IB; ++j) {
-    uint2 q0, q1;
-    uint32_t h0, h1;
-    float d0, d1;
-    s0.next(j, q0, h0, d0);
-    s1.next(j, q1, h1, d1);
-    f32x4_t b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      bf16x8_t w0[4], w1[4];
-      stq_half_w(s_lut, q0, h0, hh, w0);
-      stq_half_w(s_lut, q1, h1, hh, w1);
-      uint4 av[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * (4 * hh + t));
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        b0 = mfma16(as_bf16x8(av[t]), w0[t], b0);
-        b1 = mfma16(as_bf16x8(av[t]), w1[t], b1);
-      }
-    }
-    acc0[0] = fmaf(d0, b0[0], acc0[0]); acc0[1] = fmaf(d0, b0[1], acc0[1]);
-    acc0[2] = fmaf(d0, b0[2], acc0[2]); acc0[3] = fmaf(d0, b0[3], acc0[3]);
-    acc1[0] = fmaf(d1, b1[0], acc1[0]); acc1[1] = fmaf(d1, b1[1], acc1[1]);
-    acc1[2] = fmaf(d1, b1[2], acc1[2]); acc1[3] = fmaf(d1, b1[3], acc1[3]);
-    pin4(acc0);
-    pin4(acc1);
-  }
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int p = 2 * g + m;
-    if (p < nq) {
-      float* yr = a.y_pairs + (size_t)(pos0 + p) * H + r0 + col;
-      st_ag(yr, acc0[2 * m] + acc0[2 * m + 1]);
-      st_ag(yr + 16, acc1[2 * m] + acc1[2 * m + 1]);
-    }
-  }
-  p_arrive<HB>(a, slice, st);
-}
-
-// LDS carve-up of the persistent kernel (bytes): x rows, then one region each item kind
-// reuses (router sums / routing / routed gate/up staging / shared h / the unit's h).
-template <int HB, int IB, int XR>
-struct PLds {
-  static constexpr int H = HB * 256, I = IB * 256;
-  static constexpr size_t kX = (size_t)XR * H * 2;
-  static constexpr size_t kRoute = sizeof(SmallRoute);
-  static constexpr size_t kGu = sizeof(float) * 2 * 2 * 4 * 64 + kNW * StqStreamL<HB, 4>::BYTES;
-  static constexpr size_t kSh = (size_t)XR * I * 4 + 16;
-  static constexpr size_t kYh = ((size_t)2 * XR * I + 32 + 8) * 2;
-  static constexpr size_t m2(size_t p, size_t q) { return p > q ? p : q; }
-  static constexpr size_t kU = m2(m2(m2(4096, kRoute), m2(kGu, kSh)), kYh);
-  static constexpr size_t kBytes = kX + (kU + 15) / 16 * 16;
-};
-
-#ifdef MOE_PTRACE
-__device__ __forceinline__ uint64_t p_clock() { return __builtin_amdgcn_s_memrealtime(); }
-#endif
-
-template <int HB, int IB, int XR>
-__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void kp_decode(DecodeArgs a) {
-  using L = PLds<HB, IB, XR>;
-  extern __shared__ __align__(16) uint8_t s_dyn8[];
-  __shared__ uint2 s_lut[32];
-  __shared__ PState st;
-  uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn8);
-  uint8_t* s_u = s_dyn8 + L::kX;
-  build_lut(s_lut);
-  if (threadIdx.x == 0) {
-    st.route_seen = 0; st.sgu_seen = 0; st.router_seen = 0; st.n_units = 0; st.x_staged = 0; st.flag = 0;
-  }
-  __syncthreads();
-  const int nS = a.iU - a.iS, nU = a.iD - a.iU, nD = a.iY - a.iD, nY = a.iC - a.iY;
-  for (int it = blockIdx.x; it < a.n_items; it += gridDim.x) {
-#ifdef MOE_PTRACE
-    const uint64_t t0 = p_clock();
-#endif
-    // after the router items, the shared gate/up and routed gate/up items are interleaved in
-    // proportion, and so are the shared and routed down items: every round keeps shared
-    // streams going beside the routed chain
-    int kind, li;
-    if (it < a.iS) {
-      kind = 0; li = it;
-    } else if (it < a.iD) {
-      const int p = it - a.iS;
-      const int s0 = (int)((long)p * nS / (nS + nU)), s1 = (int)((long)(p + 1) * nS / (nS + nU));
-      if (s1 > s0) { kind = 1; li = s0; } else { kind = 2; li = p - s0; }
-    } else {
-      const int p = it - a.iD;
-      const int s0 = (int)((long)p * nD / (nD + nY)), s1 = (int)((long)(p + 1) * nD / (nD + nY));
-      if (s1 > s0) { kind = 3; li = s0; } else { kind = 4; li = p - s0; }
-    }
-    if (kind == 0) {
-      router_unit<HB, true>(a, it, reinterpret_cast<float(*)[4][64]>(s_u));
-      const int old = p_publish(a.pc, kPcRouter);
-      if (threadIdx.x == 0) st.flag = old == a.n_router_wg - 1;
-      __syncthreads();
-      if (st.flag) p_route(a, *reinterpret_cast<SmallRoute*>(s_u), st);   // the last one routes
-    } else if (kind == 1) {
-      // the shared streams start once the router's loads are done: before that they would
-      // only queue ahead of the routing's short chain
-      if (!st.router_seen) {
-        p_wait(a.pc, kPcRouter, a.n_router_wg);
-        if (threadIdx.x == 0) st.router_seen = 1;
-      }
-      p_stage_x<HB, XR>(a, s_x, st);
-      p_shared_gateup<HB, IB, XR>(a, li, s_x);
-    } else if (kind == 2) {
-      p_need_route(a, st);
-      p_stage_x<HB, XR>(a, s_x, st);
-      p_routed_gateup<HB, IB>(a, li, s_lut, s_x, reinterpret_cast<float(*)[2][4][64]>(s_u),
-                              s_u + sizeof(float) * 2 * 2 * 4 * 64, st);
-    } else if (kind == 3) {
-      p_shared_down<HB, IB, XR>(a, li, reinterpret_cast<uint16_t*>(s_u), st);
-    } else {
-      p_need_route(a, st);
-      p_routed_down<HB, IB>(a, li, s_lut, reinterpret_cast<uint16_t*>(s_u), st);
-    }
-    __syncthreads();   // the item's LDS is reused by the next one
-#ifdef MOE_PTRACE
-    if (threadIdx.x == 0) {
-      uint64_t* tr = reinterpret_cast<uint64_t*>(a.xq) + 3 * it;   // past the STQ1_0 regions
-      tr[0] = ((uint64_t)blockIdx.x << 32) | (uint32_t)it;
-      tr[1] = t0;
-      tr[2] = p_clock();
-    }
-#endif
-  }
-  if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(a.pc + kPcExit * kPcStride, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (int)gridDim.x - 1)
-      for (int i = 0; i < kPcCount; ++i) st_ag(a.pc + i * kPcStride, 0);
   }
 }
 
@@ -2378,58 +1766,6 @@ hipError_t launch_shape_mx(DecodeArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// Compute units of the current device (looked up once per device).
-int device_cus() {
-  static std::mutex mu;
-  static int cus[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  std::lock_guard<std::mutex> lk(mu);
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
-// Up to kXT tokens, STQ1_0: the persistent single-launch decode (kp_decode).
-template <int HB, int IB, int XR>
-hipError_t launch_persist(DecodeArgs& a, hipStream_t s) {
-  using L = PLds<HB, IB, XR>;
-  constexpr int H = HB * 256, I = IB * 256;
-  const int T = a.T;
-  const int P = T * a.k;
-  const int max_units = P < a.E ? P : a.E;
-  const bool shared = a.sg != nullptr;
-  if (P > kMaxPL) return hipErrorInvalidValue;
-  a.n_router_wg = ((a.E + 15) / 16) * kRouterParts;
-  if (H / 128 > 64) return hipErrorInvalidValue;      // output slices with a counter
-  a.h_cap = T;
-  a.iX = a.n_router_wg;
-  a.iS = a.n_router_wg;
-  a.iU = a.iS + (shared ? I / kNW : 0);
-  a.iD = a.iU + max_units * (I / 32);
-  a.iY = a.iD + (shared ? H / 16 : 0);
-  a.iC = a.iY + max_units * (H / 128);
-  a.n_items = a.iC;
-  a.pc = a.wl + 16;
-  // every workgroup resident at once (the items wait on each other): at most as many per CU
-  // as its LDS allows, two at most (the register budget of amdgpu_waves_per_eu(2))
-  const int cus = device_cus();
-  if (cus <= 0) return hipErrorInvalidDevice;
-  const size_t per_wg = L::kBytes + 1024;
-  const int per_cu = (int)((size_t)160 * 1024 / per_wg) < 2 ? (int)((size_t)160 * 1024 / per_wg) : 2;
-  if (per_cu < 1) return hipErrorInvalidValue;
-  const int G = a.n_items < cus * per_cu ? a.n_items : cus * per_cu;
-  const bool prof = moe_prof_on();
-  if (prof) moe_prof_begin(MOE_PROF_DECODE_P, s);
-  hipLaunchKernelGGL((kp_decode<HB, IB, XR>), dim3(G), dim3(kWG), L::kBytes, s, a);
-  MOE_HIP_TRY(hipGetLastError());
-  if (prof) moe_prof_end(MOE_PROF_DECODE_P, s);
-  return hipSuccess;
-}
-
 // Small T, split by what each piece waits for: (1) router partials + shared gate/up (x
 // only); (2) per-workgroup routing + routed gate/up, beside the shared down (shared h only);
 // (3) routed down + combine (+ y_shared, + residual).
@@ -2501,15 +1837,9 @@ hipError_t launch_large(DecodeArgs& a, hipStream_t s) {
 
 template <int HB, int IB>
 hipError_t launch_shape(DecodeArgs& a, hipStream_t s) {
-#ifdef MOE_DECODE_PERSIST
-  if (a.T == 1) return launch_persist<HB, IB, 1>(a, s);
-  if (a.T == 2) return launch_persist<HB, IB, 2>(a, s);
-  if (a.T <= kXT) return launch_persist<HB, IB, kXT>(a, s);
-#else
   if (a.T == 1) return launch_small<HB, IB, 1>(a, s);
   if (a.T == 2) return launch_small<HB, IB, 2>(a, s);
   if (a.T <= kXT) return launch_small<HB, IB, kXT>(a, s);
-#endif
   return launch_large<HB, IB>(a, s);
 }
 
@@ -2524,13 +1854,10 @@ static __device__ __align__(256) uint8_t scratch[kDecodeStaticScratchBytes];
 
 namespace {
 
-// Zero the workspace header's counters (the work-list words with the router ticket, and the
-// single-launch decode's counters): a kernel, not hipMemsetAsync, so a captured call replays
-// it as a kernel node.
-__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p) {
-  const int i = threadIdx.x;
-  if (i < 16) p[i] = 0u;                               // work lists, ticket
-  if (i < kPcCount) p[16 + i * kPcStride] = 0u;         // the single-launch decode's counters
+// Zero the workspace header (the work-list words with the router ticket): a kernel, not
+// hipMemsetAsync, so a captured call replays it as a kernel node.
+__global__ __launch_bounds__(64) void clear_words_kernel(uint32_t* p) {
+  if (threadIdx.x < 16) p[threadIdx.x] = 0u;   // work lists and the router ticket
 }
 
 std::mutex g_scratch_mu;
@@ -2551,7 +1878,7 @@ void* moe_decode_static_scratch() {
 }
 
 hipError_t moe_clear_decode_header(void* ws, hipStream_t s) {
-  hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t*>(ws));
+  hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(64), 0, s, static_cast<uint32_t*>(ws));
   return hipGetLastError();
 }
 
@@ -2578,7 +1905,7 @@ size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, s
   const size_t max_half = pe + (P + 3) / 4;     // entries of <= 8 (or <= 4) pairs
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t cur = 0;
-  offs[0] = cur; cur = al(cur + (16 + (size_t)kPcWords) * sizeof(int32_t));        // work lists, ticket, counters
+  offs[0] = cur; cur = al(cur + 16 * sizeof(int32_t));                             // work lists + ticket
   offs[1] = cur; cur = al(cur + max_units * sizeof(int4));                          // unit table
   offs[2] = cur; cur = al(cur + max_units * 16 * sizeof(int32_t));                  // unit tokens
   offs[3] = cur; cur = al(cur + max_units * 16 * sizeof(float));                    // unit weights
