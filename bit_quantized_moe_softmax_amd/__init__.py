@@ -24,7 +24,7 @@ __all__ = [
 ]
 
 PROFILE_SLOTS = ["decode_k1_route", "decode_k2_gateup",
-                 "decode_k3_down_combine", "reserved3", "mx_quant", "mx_gateup", "mx_down",
+                 "decode_k3_down_combine", "decode_k4_combine", "mx_quant", "mx_gateup", "mx_down",
                  "stq_gateup", "stq_down", "shared_gateup", "shared_down", "act_prep"]
 
 MOE_W_STQ1_0, MOE_W_MXFP4, MOE_W_BF16, MOE_W_MXFP4_TILED, MOE_W_MXFP8 = 1, 2, 3, 4, 5

@@ -46,6 +46,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace {
 
@@ -153,43 +154,59 @@ __device__ __forceinline__ uint32_t bf16_lane(uint32_t p, int j) {
   return ((p >> i) & 1) ? 0xBF80u : 0x3F80u;
 }
 
-// 32-entry table: 5-bit STQ1_0 group pattern -> its four weights in {-1, 0, +1} as bf16.
-__device__ __forceinline__ void build_lut(uint2* lut) {
+// 32-entry table: 5-bit STQ1_0 group pattern -> its four weights in {-1, 0, +1} as bf16
+// (8 bytes per entry: words 2p, 2p + 1).  Entries p and p + 16 share banks; splitting each
+// entry into two 4-byte tables (conflict-free ds_read2_b32) measured slower.
+__device__ __forceinline__ void build_lut(uint32_t* lut) {
   const int t = threadIdx.x;
-  if (t < 32) lut[t] = make_uint2(bf16_lane(t, 0) | (bf16_lane(t, 1) << 16),
-                                  bf16_lane(t, 2) | (bf16_lane(t, 3) << 16));
-}
-
-// The 8 weight operands of one STQ1_0 block (8 code bytes + 16 high bits of this lane):
-// all 16 table reads are issued before any is used.
-__device__ __forceinline__ void stq_block_w(const uint2* lut, uint2 qs, uint32_t qh, bf16x8_t* wv) {
-  uint2 l[16];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const uint32_t byte = ((t < 4 ? qs.x : qs.y) >> (8 * (t & 3))) & 0xFFu;
-    l[2 * t] = lut[(byte & 15u) | (((qh >> (2 * t)) & 1u) << 4)];
-    l[2 * t + 1] = lut[(byte >> 4) | (((qh >> (2 * t + 1)) & 1u) << 4)];
+  if (t < 32) {
+    lut[2 * t] = bf16_lane(t, 0) | (bf16_lane(t, 1) << 16);
+    lut[2 * t + 1] = bf16_lane(t, 2) | (bf16_lane(t, 3) << 16);
   }
-#pragma unroll
-  for (int t = 0; t < 8; ++t) wv[t] = as_bf16x8(make_uint4(l[2 * t].x, l[2 * t].y, l[2 * t + 1].x, l[2 * t + 1].y));
 }
 
-// The 4 weight operands of half h of one STQ1_0 block (code bytes 4h .. 4h+3 of this lane
-// and their 8 high bits): 8 table reads, all issued before any is used.
-__device__ __forceinline__ void stq_half_w(const uint2* lut, uint2 qs, uint32_t qh, int h, bf16x8_t* wv) {
-  const uint32_t w4 = h ? qs.y : qs.x;
-  const uint32_t hb = qh >> (8 * h);
+// Table byte offsets (pattern x 8) of the 8 groups of one code word qw (4 bytes: group 2t
+// is the low nibble of byte t, group 2t + 1 the high nibble) with their high bits hb (bits
+// 2t and 2t + 1), four at a time: the nibbles x 8 by masks; the high bits moved to bit 7 of
+// their bytes by one multiply (bit 2i lands on bit 8i; the stray copies fall elsewhere and
+// are masked off).  About 3 VALU instructions per lookup instead of 5.
+__device__ __forceinline__ void stq_word_offsets(uint32_t qw, uint32_t hb, uint32_t& alo, uint32_t& ahi) {
+  const uint32_t lo8 = (qw << 3) & 0x78787878u, hi8 = (qw >> 1) & 0x78787878u;
+  const uint32_t sl = __umul24(hb & 0x55u, 0x41041u) & 0x01010101u;
+  const uint32_t sh = __umul24((hb >> 1) & 0x55u, 0x41041u) & 0x01010101u;
+  alo = (sl << 7) | lo8;
+  ahi = (sh << 7) | hi8;
+}
+__device__ __forceinline__ uint2 lut_at(const uint32_t* lut, uint32_t off) {
+  return *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(lut) + off);
+}
+
+// The 4 weight operands of one code word (its 8 groups): 8 table reads, all issued before
+// any is used.
+__device__ __forceinline__ void stq_word_w(const uint32_t* lut, uint32_t qw, uint32_t hb, bf16x8_t* wv) {
+  uint32_t alo, ahi;
+  stq_word_offsets(qw, hb, alo, ahi);
   uint2 l[8];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const uint32_t byte = (w4 >> (8 * t)) & 0xFFu;
-    l[2 * t] = lut[(byte & 15u) | (((hb >> (2 * t)) & 1u) << 4)];
-    l[2 * t + 1] = lut[(byte >> 4) | (((hb >> (2 * t + 1)) & 1u) << 4)];
+    l[2 * t] = lut_at(lut, (alo >> (8 * t)) & 0xFFu);
+    l[2 * t + 1] = lut_at(lut, (ahi >> (8 * t)) & 0xFFu);
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) wv[t] = as_bf16x8(make_uint4(l[2 * t].x, l[2 * t].y, l[2 * t + 1].x, l[2 * t + 1].y));
 }
 
+// The 8 weight operands of one STQ1_0 block (8 code bytes + 16 high bits of this lane).
+__device__ __forceinline__ void stq_block_w(const uint32_t* lut, uint2 qs, uint32_t qh, bf16x8_t* wv) {
+  stq_word_w(lut, qs.x, qh, wv);
+  stq_word_w(lut, qs.y, qh >> 8, wv + 4);
+}
+
+// The 4 weight operands of half h of one STQ1_0 block (code bytes 4h .. 4h+3 of this lane
+// and their 8 high bits).
+__device__ __forceinline__ void stq_half_w(const uint32_t* lut, uint2 qs, uint32_t qh, int h, bf16x8_t* wv) {
+  stq_word_w(lut, h ? qs.y : qs.x, qh >> (8 * h), wv);
+}
 
 // fp16 block scales of one row: words of two, in groups of 8 blocks (16 bytes, aligned
 // when NB >= 8), fewer blocks in one smaller aligned load.
@@ -284,7 +301,7 @@ struct StqStream {
   // already applied), K stride 1.  Software-pipelined by half blocks: the table reads of
   // half h + 1 are in flight while the 4 MFMAs of half h run, and the two halves of a block
   // accumulate in separate registers (two 4-deep MFMA chains).
-  __device__ __forceinline__ f32x4_t run_lds(const uint2* lut, const uint16_t* a_lds) {
+  __device__ __forceinline__ f32x4_t run_lds(const uint32_t* lut, const uint16_t* a_lds) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     uint2 qj;
     uint32_t qhj;
@@ -325,7 +342,7 @@ struct StqStream {
 
   // A operands from memory through rsrc ra at byte offset aoff (+ 2 K); each operand is
   // reloaded for the next block as soon as its MFMA has been issued.
-  __device__ __forceinline__ f32x4_t run_mem(const uint2* lut, rsrc_t ra, uint32_t aoff) {
+  __device__ __forceinline__ f32x4_t run_mem(const uint32_t* lut, rsrc_t ra, uint32_t aoff) {
     uint4 av[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) av[t] = bload16(ra, aoff, 2 * (8 * t));
@@ -433,7 +450,7 @@ struct StqStreamL {
   }
 
   // as StqStream::run_lds
-  __device__ __forceinline__ f32x4_t run_lds(const uint2* lut, const uint16_t* a_lds) {
+  __device__ __forceinline__ f32x4_t run_lds(const uint32_t* lut, const uint16_t* a_lds) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     uint2 qj;
     uint32_t qhj;
@@ -676,16 +693,31 @@ struct FinalizeLds {
   int wsum[kNW * 4];
 };
 
-// Routing of all tokens by the last router workgroup (4 waves): top-k per token, stable
-// permutation of the pairs by expert (E <= 256: one expert per thread), work lists.
+// Top-k of tokens t0 .. t1 - 1 (t1 - t0 <= 16: wave w takes t0 + w + 4 i), every input load
+// issued before the first selection; writes logits, ids and weights.
+__device__ __forceinline__ void route_topk_tile(const DecodeArgs& a, int t0, int t1, float* s_v, int* s_i,
+                                                int* ids_l, int* wb_l) {
+  const int wave = threadIdx.x >> 6;
+  TopkIn in[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) topk_load(a, min(t0 + wave + kNW * i, t1 - 1), in[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + wave + kNW * i;
+    if (t < t1) wave_topk(a, t, topk_sums(a, in[i]), s_v, s_i, ids_l, wb_l, true);
+  }
+}
+
+// Stable permutation of all pairs by expert (E <= 256: one expert per thread) and the work
+// lists, from the ids and weights every tile's top-k wrote: units of <= 16 pairs of one
+// expert (with each pair's token and weight) and half-units of <= QN.
 template <int P0, int QN>
-__device__ __forceinline__ void route_finalize(const DecodeArgs& a, FinalizeLds<P0>& L) {
+__device__ __forceinline__ void route_permute(const DecodeArgs& a, FinalizeLds<P0>& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, k = a.k, T = a.T, P = T * k;
-  for (int t = wave; t < T; t += kNW) {
-    TopkIn in;
-    topk_load(a, t, in);
-    wave_topk(a, t, topk_sums(a, in), L.v[wave], L.i[wave], L.ids, L.ids + 2 * P0, true);
+  const int E = a.E, k = a.k, P = a.T * k;
+  for (int f = tid; f < P; f += kWG) {
+    L.ids[f] = a.ids[f];
+    L.ids[2 * P0 + f] = __float_as_int(a.w[f]);
   }
   if (tid < E) L.cnt[tid] = 0;
   lds_barrier();
@@ -791,21 +823,45 @@ __device__ __forceinline__ void route_finalize(const DecodeArgs& a, FinalizeLds<
   }
 }
 
-template <int HB, int P0, int QN>
+template <int HB, int IB>
+__device__ __forceinline__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2][4][64]);
+
+// Beyond kXT tokens, first kernel: router partials (workgroups 0 .. n_router_wg - 1, per
+// 16-token tile), then the shared expert's gate/up (16 rows x 16 tokens per workgroup).
+// Routing runs as a chain of two tickets, agent-scope acquire/release atomics on counters
+// in the workspace: the last router workgroup of a token tile sums that tile's partials and
+// picks its tokens' top-k (tiles in parallel); the last tile to finish sorts all pairs and
+// writes the work lists, then leaves every counter at zero for the next call.
+template <int HB, int IB, int P0, int QN>
 __global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
   __shared__ __align__(16) float s_red[kNW][4][64];
   __shared__ int s_last;
   __shared__ FinalizeLds<P0> s_fin;
-  router_unit<HB>(a, blockIdx.x, s_red);
-  if (threadIdx.x < 64) {
-    __threadfence();     // wave 0 wrote this workgroup's partial: publish it device-wide
-    if (threadIdx.x == 0) s_last = atomicAdd(&a.ctr[0], 1) == a.n_router_wg - 1;
+  const int b = blockIdx.x;
+  if (b >= a.n_router_wg) {
+    shared_gateup_mfma<HB, IB>(a, b - a.n_router_wg, reinterpret_cast<float(*)[2][4][64]>(s_fin.ids));
+    return;
   }
+  router_unit<HB>(a, b, s_red);
+  const int per_tile = kRouterParts * ((a.E + 15) / 16);
+  const int tt = b / per_tile, n_tt = (a.T + 15) / 16;
+  // wave 0 wrote this workgroup's partial: its first lane releases it with the tile ticket
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&a.ctr[1 + tt], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == per_tile - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  route_finalize<P0, QN>(a, s_fin);
-  if (threadIdx.x == 0) a.ctr[0] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // every wave reads the tile's partials
+  route_topk_tile(a, 16 * tt, min(16 * tt + 16, a.T), s_fin.v[threadIdx.x >> 6], s_fin.i[threadIdx.x >> 6],
+                  s_fin.ids, s_fin.ids + 2 * P0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // every wave's ids and weights
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&a.ctr[0], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == n_tt - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  route_permute<P0, QN>(a, s_fin);
+  if ((int)threadIdx.x <= n_tt) a.ctr[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------------------------- small T
@@ -925,56 +981,6 @@ __device__ __forceinline__ void small_route_units(const DecodeArgs& a, SmallRout
 }
 
 // ============================================================================ K2
-// Routed gate/up: a workgroup takes one unit (expert, <= 16 pairs) and 32 rows of I; wave
-// = (16-row tile, gate|up) over all of K; the gate and up waves of a tile meet in LDS and
-// the gate wave writes h = SiLU(gate) * up as bf16 hi + lo.  Units of up to kXT tokens read
-// their x rows from LDS.
-template <int HB, int IB, int XR, bool MEM>
-__device__ __forceinline__ void routed_gateup(const DecodeArgs& a, int wi, const uint2* s_lut, uint16_t* s_x,
-                              float (*s_red)[2][4][64]) {
-  constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int un_i = wi / NTP, tp = wi % NTP;
-  const int4 un = a.ut[un_i];
-  const int e = un.x, pos0 = un.y, ntok = un.z;
-  const int mat = wave & 1, tl = wave >> 1;
-  const int row0 = (2 * tp + tl) * 16;
-  const size_t wrow = (size_t)e * I + row0 + col;
-  const uint8_t* rp = (mat ? a.uc : a.gc) + wrow * HB * 40;
-  const uint16_t* sp = (mat ? a.us : a.gs) + wrow * HB;
-  const int* toks = a.utok + un_i * 16;
-  f32x4_t acc;
-  if (!MEM || ntok <= XR) {
-    RowStage<H, kWG, XR> xs;
-    xs.issue(ntok, [&](int r) { return a.x + (size_t)toks[r] * H; });
-    StqStream<HB> st;
-    st.issue(rp, sp);
-    xs.commit(ntok, s_x);
-    lds_barrier();
-    acc = st.run_lds(s_lut, s_x + (col < ntok ? col : 0) * H + 64 * g);
-  } else if constexpr (MEM) {
-    const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2);
-    const uint32_t xo = col < ntok ? 2u * ((uint32_t)toks[col] * H + 64 * g) : kOOB;
-    StqStream<HB> st;
-    st.issue(rp, sp);
-    acc = st.run_mem(s_lut, rx, xo);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s_red[tl][mat][i][lane] = acc[i];
-  __syncthreads();
-  if (mat == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = 4 * g + i;
-      if (slot < ntok)
-        store_hilo(a.h_hi + (size_t)(pos0 + slot) * I + row0 + col, a.h_lo_bytes / 2,
-                   silu_mul(s_red[tl][0][i][lane], s_red[tl][1][i][lane]));
-    }
-  }
-  __syncthreads();   // s_red and the x rows are reused by the next work item
-}
-
 // Shared gate/up for up to kXT tokens (x rows in LDS): wave = one row of I, gate and up,
 // streamed in 16-byte chunks per lane (chunk c: K = 8 l + 512 c for lane l) with the next
 // chunk of both matrices in flight while one is reduced.
@@ -1025,10 +1031,12 @@ __device__ __forceinline__ void shared_gateup_valu(const DecodeArgs& a, int sw, 
   }
 }
 
-// Shared gate/up beyond kXT tokens: 16 rows x 16 tokens, the 4 waves split K.
+// Shared gate/up beyond kXT tokens: 16 rows x 16 tokens, the 4 waves split K (A = weight
+// rows, B = token columns).  Each wave's next block is in flight while one is multiplied;
+// blocks past the wave's share read as zeros (buffer loads out of range) and add nothing.
 template <int HB, int IB>
 __device__ __forceinline__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2][4][64]) {
-  constexpr int H = HB * 256, I = IB * 256, n_rt = I / 16;
+  constexpr int H = HB * 256, I = IB * 256, n_rt = I / 16, NBW = (HB + kNW - 1) / kNW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rt = sw % n_rt, tt = sw / n_rt;
   const int row0 = rt * 16;
@@ -1037,23 +1045,29 @@ __device__ __forceinline__ void shared_gateup_mfma(const DecodeArgs& a, int sw, 
   const bool t_ok = tok < a.T;
   const int b0 = wave * HB / kNW, b1 = (wave + 1) * HB / kNW;
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2);
-  const uint32_t xo = t_ok ? 2u * (uint32_t)tok * H : kOOB;
-  const uint16_t* rg = a.sg + (size_t)(row0 + col) * H;
-  const uint16_t* ru = a.su + (size_t)(row0 + col) * H;
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  for (int b = b0; b < b1; ++b) {
-    uint4 cg[8], cu[8], cx[8];
+  const rsrc_t rg = make_rsrc(a.sg, (uint32_t)I * H * 2), ru = make_rsrc(a.su, (uint32_t)I * H * 2);
+  const uint32_t xo = 2u * (uint32_t)tok * H, wo = 2u * (uint32_t)(row0 + col) * H;
+  uint4 c[2][3][8];   // [slot][gate, up, x][step]
+  auto load = [&](int m, uint4 (*cs)[8]) {
+    const int b = b0 + m;
+    const bool ok = b < b1;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int off = 256 * b + 32 * t + 8 * g;
-      cg[t] = *reinterpret_cast<const uint4*>(rg + off);
-      cu[t] = *reinterpret_cast<const uint4*>(ru + off);
-      cx[t] = bload16(rx, xo, 2 * off);
+      const uint32_t off = 2u * (256 * b + 32 * t + 8 * g);
+      cs[0][t] = bload16(rg, ok ? wo + off : kOOB);
+      cs[1][t] = bload16(ru, ok ? wo + off : kOOB);
+      cs[2][t] = bload16(rx, ok && t_ok ? xo + off : kOOB);
     }
+  };
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  load(0, c[0]);
+#pragma unroll
+  for (int m = 0; m < NBW; ++m) {
+    if (m + 1 < NBW) load(m + 1, c[(m + 1) & 1]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      accg = mfma16(as_bf16x8(cg[t]), as_bf16x8(cx[t]), accg);
-      accu = mfma16(as_bf16x8(cu[t]), as_bf16x8(cx[t]), accu);
+      accg = mfma16(as_bf16x8(c[m & 1][0][t]), as_bf16x8(c[m & 1][2][t]), accg);
+      accu = mfma16(as_bf16x8(c[m & 1][1][t]), as_bf16x8(c[m & 1][2][t]), accu);
     }
   }
 #pragma unroll
@@ -1069,24 +1083,367 @@ __device__ __forceinline__ void shared_gateup_mfma(const DecodeArgs& a, int sw, 
   }
 }
 
-// Large T, second kernel: routed gate/up (units of up to kXT tokens stage their x rows)
-// beside the shared expert's gate/up on the MFMA.
-template <int HB, int IB>
-__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k2_gateup(DecodeArgs a) {
-  constexpr int XR = kXT;
-  extern __shared__ __align__(16) uint16_t s_x[];   // x rows: XR x H bf16
-  __shared__ uint2 s_lut[32];
-  __shared__ __align__(16) float s_red[2][2][4][64];
-  const int b = blockIdx.x;
-  if (b >= a.n_gu_wg) {
-    shared_gateup_mfma<HB, IB>(a, b - a.n_gu_wg, reinterpret_cast<float(*)[2][4][64]>(&s_red[0][0][0][0]));
-    return;
+// ============================================================================ large T
+// Beyond kXT tokens the routed projections run in persistent workgroups of 8 waves over a
+// list of work items (unit of <= 16 pairs, slice of 128 weight rows: 16 per wave); each
+// workgroup takes a contiguous range of the list, so its items mostly share a unit and
+// the list is split evenly whatever the routing.
+constexpr int kLW = 512;
+constexpr int kLNW = kLW / 64;
+constexpr int kSlice = 16 * kLNW;
+
+// Work split of a persistent grid of G workgroups: workgroup b takes the heavy items
+// b, b + G, b + 2 G, .. of n_heavy (each costing W light ones), then the contiguous range
+// [i0, i1) of the n light items that brings its share of the total cost closest to its even
+// share (the ranges are monotone in b and cover every light item exactly once).
+__device__ __forceinline__ void light_range(int b, int G, int n, int n_heavy, int W, int& i0, int& i1) {
+  const long C = (long)n + (long)W * n_heavy;
+  const int full = n_heavy / G, rem = n_heavy % G;
+  auto end = [&](int bb) {   // end of workgroup bb's light range
+    if (bb < 0) return 0L;
+    const long heavy = (long)W * ((long)(bb + 1) * full + min(bb + 1, rem));
+    const long e = C * (bb + 1) / G - heavy;
+    return e < 0 ? 0L : (e > n ? (long)n : e);
+  };
+  i0 = (int)end(b - 1);
+  i1 = b == G - 1 ? n : (int)end(b);
+}
+
+// Large-T gate/up: the x rows of a half-unit (<= 8 tokens) in LDS, row r at byte r XROW
+// (H bf16 + 16 bytes of padding, so the rows one MFMA operand read touches start in
+// different banks); staged once per half-unit, every load issued before the first write.
+template <int HB>
+__device__ __forceinline__ void stage_x_large(const DecodeArgs& a, const int* toks, int n, uint8_t* s_x) {
+  constexpr int H = HB * 256, XROW = 2 * H + 16, PR = H / 8, PER = (8 * PR + kLW - 1) / kLW;
+  constexpr int PASS = PER < 12 ? PER : 12;
+  const int tid = threadIdx.x;
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2);
+#pragma unroll
+  for (int m0 = 0; m0 < PER; m0 += PASS) {
+    uint4 v[PASS];
+#pragma unroll
+    for (int m = 0; m < PASS; ++m) {
+      const int idx = tid + kLW * (m0 + m), r = idx / PR, pc = idx % PR;
+      const bool ok = m0 + m < PER && r < n;
+      v[m] = bload16(rx, ok ? 2u * (uint32_t)toks[ok ? r : 0] * H + 16u * pc : kOOB);
+    }
+#pragma unroll
+    for (int m = 0; m < PASS; ++m) {
+      const int idx = tid + kLW * (m0 + m), r = idx / PR, pc = idx % PR;
+      if (m0 + m < PER && r < 8) *reinterpret_cast<uint4*>(s_x + r * XROW + 16 * pc) = v[m];
+    }
   }
+}
+
+// One item of the large-T gate/up: wave w multiplies the half-unit's staged x rows (A) with
+// rows slice * 128 + 16 w .. + 15 of the expert's gate and up matrices (B, STQ1_0 decoded
+// through the table, RD blocks in flight) over all of K, then writes h = SiLU(gate) * up as
+// bf16 hi + lo.  No workgroup barrier inside: every wave streams on its own.
+template <int HB, int IB, int RD>
+__device__ __forceinline__ void routed_gateup_large(const DecodeArgs& a, int e, int pos0, int ntok, int slice,
+                                                    const uint32_t* s_lut, const uint8_t* s_x) {
+  constexpr int H = HB * 256, I = IB * 256, XROW = 2 * H + 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int row0 = slice * kSlice + 16 * wave;
+  const size_t wrow = (size_t)e * I + row0 + col;
+  StqStream<HB, RD> sg, su;
+  sg.issue(a.gc + wrow * HB * 40, a.gs + wrow * HB);
+  su.issue(a.uc + wrow * HB * 40, a.us + wrow * HB);
+  const uint8_t* xa = s_x + (col < ntok ? col : 0) * XROW + 128 * g;   // this lane's A operand
+  f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
+#pragma unroll
+  for (int j = 0; j < HB; ++j) {
+    uint4 av[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) av[t] = *reinterpret_cast<const uint4*>(xa + 512 * j + 16 * t);
+    uint2 qg, qu;
+    uint32_t hg, hu;
+    float dg, du;
+    sg.next(j, qg, hg, dg);
+    su.next(j, qu, hu, du);
+    bf16x8_t wg[8], wu[8];
+    stq_block_w(s_lut, qg, hg, wg);
+    stq_block_w(s_lut, qu, hu, wu);
+    f32x4_t bg = {0.f, 0.f, 0.f, 0.f}, bu = bg;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      bg = mfma16(as_bf16x8(av[t]), wg[t], bg);
+      bu = mfma16(as_bf16x8(av[t]), wu[t], bu);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { ag[i] = fmaf(dg, bg[i], ag[i]); au[i] = fmaf(du, bu[i], au[i]); }
+    pin4(ag);
+    pin4(au);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = 4 * g + i;
+    if (slot < ntok)
+      store_hilo(a.h_hi + (size_t)(pos0 + slot) * I + row0 + col, a.h_lo_bytes / 2, silu_mul(ag[i], au[i]));
+  }
+}
+
+// Large T, second kernel: the routed gate/up items (half-unit, 128 rows of I), persistent
+// workgroups over contiguous ranges of the item list; x is restaged when the half-unit
+// changes.
+template <int HB, int IB>
+__global__ __launch_bounds__(kLW) void k2l_gateup(DecodeArgs a) {
+  constexpr int I = IB * 256, NS = I / kSlice;
+  static_assert(I % kSlice == 0, "slices");
+  __shared__ uint32_t s_lut[64];                  // first: table offsets fit the offset field
+  extern __shared__ __align__(16) uint8_t s_xl[];  // 8 x rows
   build_lut(s_lut);
-  __syncthreads();
-  const int n_items = a.wl[1] * (IB * 256 / 32);
-  for (int wi = b; wi < n_items; wi += a.n_gu_wg)
-    routed_gateup<HB, IB, XR, true>(a, wi, s_lut, s_x, s_red);
+  int i0, i1;
+  light_range(blockIdx.x, gridDim.x, a.wl[2] * NS, 0, 1, i0, i1);
+  int staged = -1;
+  int4 hu = make_int4(0, 0, 0, 0);
+  for (int i = i0; i < i1; ++i) {
+    const int h = i / NS;
+    if (h != staged) {
+      hu = a.hl[h];
+      __syncthreads();   // every wave is done with the previous rows
+      stage_x_large<HB>(a, a.utok + hu.w, hu.z, s_xl);
+      __syncthreads();
+      staged = h;
+    }
+    routed_gateup_large<HB, IB, kRing>(a, hu.x, hu.y, hu.z, i % NS, s_lut, s_xl);
+  }
+}
+
+// Large-T down: the A operand of a unit (or of a 16-token tile of the shared expert) as two
+// 16-row halves in LDS: pairs 8q .. 8q+7 in half q, pair p's bf16 hi row as A row
+// 2 (p - 8q) and its lo row as 2 (p - 8q) + 1; rows of I bf16 + 16 bytes of padding.  Rows
+// `first` .. `first` + n - 1 of the hi rows at byte 0 of rh (lo rows at lo_bytes); rows past
+// n are zero.  All loads are issued before the first write.
+template <int IB>
+__device__ __forceinline__ void stage_h_large(rsrc_t rh, uint32_t lo_bytes, int first, int n, uint8_t* s_h) {
+  constexpr int I = IB * 256, HROW = 2 * I + 16, PR = I / 8, PER = 2 * 16 * PR / kLW;
+  constexpr int PASS = PER < 8 ? PER : 8;   // loads in flight per thread and pass
+  static_assert((2 * 16 * PR) % kLW == 0 && PER % PASS == 0, "pieces");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int m0 = 0; m0 < PER; m0 += PASS) {
+    uint4 v[PASS];
+#pragma unroll
+    for (int m = 0; m < PASS; ++m) {
+      const int idx = tid + kLW * (m0 + m);
+      const int q = idx / (16 * PR), r = (idx / PR) % 16, pc = idx % PR;
+      const int p = 8 * q + (r >> 1);
+      v[m] = bload16(rh, p < n ? (r & 1 ? lo_bytes : 0u) + 2u * (uint32_t)(first + p) * I + 16u * pc : kOOB);
+    }
+#pragma unroll
+    for (int m = 0; m < PASS; ++m) {
+      const int idx = tid + kLW * (m0 + m);
+      const int q = idx / (16 * PR), r = (idx / PR) % 16, pc = idx % PR;
+      *reinterpret_cast<uint4*>(s_h + (16 * q + r) * HROW + 16 * pc) = v[m];
+    }
+  }
+}
+
+// One shared-expert down item: tokens 16 tt .. 16 tt + 15 (staged A) times rows slice * 128 +
+// 16 w .. + 15 of the bf16 down matrix (B, one block ahead in registers); writes y_shared.
+template <int HB, int IB>
+__device__ __forceinline__ void shared_down_item(const DecodeArgs& a, int tt, int slice, const uint8_t* s_h) {
+  constexpr int H = HB * 256, I = IB * 256, HROW = 2 * I + 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int row = slice * kSlice + 16 * wave + col;
+  const rsrc_t rw = make_rsrc(a.sd, (uint32_t)H * I * 2);
+  const uint32_t wo = 2u * (uint32_t)row * I;
+  uint4 w[2][8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) w[0][t] = bload16(rw, wo + 2u * (64 * g + 8 * t));
+  const uint8_t* a0 = s_h + col * HROW + 128 * g;
+  const uint8_t* a1 = a0 + 16 * HROW;
+  f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    if (j + 1 < IB) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) w[(j + 1) & 1][t] = bload16(rw, wo + 2u * (256 * (j + 1) + 64 * g + 8 * t));
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(a0 + 512 * j + 16 * t);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(a1 + 512 * j + 16 * t);
+      c0 = mfma16(as_bf16x8(x0), as_bf16x8(w[j & 1][t]), c0);
+      c1 = mfma16(as_bf16x8(x1), as_bf16x8(w[j & 1][t]), c1);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int t0 = 16 * tt + 2 * g + m;
+    if (t0 < a.T) a.y_shared[(size_t)t0 * H + row] = c0[2 * m] + c0[2 * m + 1];
+    if (t0 + 8 < a.T) a.y_shared[(size_t)(t0 + 8) * H + row] = c1[2 * m] + c1[2 * m + 1];
+  }
+}
+
+// The STQ1_0 down rows of one item in flight: all NB (<= 8) blocks of this lane's row (code
+// words and high bits) and its scale group.  Loads of an absent item read as zeros.
+template <int NB>
+struct DownRing {
+  uint2 q[NB];
+  uint32_t qh[NB];
+  uint4 sc;
+  __device__ __forceinline__ void load_scales(rsrc_t rs, uint32_t so) {
+    if constexpr (NB == 1) {
+      sc = make_uint4(__builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0), 0u, 0u, 0u);
+    } else if constexpr (NB == 2) {
+      sc = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0), 0u, 0u, 0u);
+    } else if constexpr (NB == 4) {
+      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0));
+      sc = make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+      static_assert(NB == 8, "one scale group");
+      sc = bload16(rs, so);
+    }
+  }
+  // block j of the row starting at byte `row` of the codes: this lane's 8 code bytes (group
+  // g) and its 16 high bits
+  __device__ __forceinline__ void load_block(rsrc_t rc, uint32_t row, int j) {
+    const int g = (threadIdx.x & 63) >> 4;
+    q[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, row + 8 * g, 40 * j, 0));
+    qh[j] = __builtin_amdgcn_raw_buffer_load_b16(rc, row + 32 + 2 * g, 40 * j, 0);
+  }
+};
+
+// One routed down item: the unit's staged h (A; NH halves) times rows r16 .. r16 + 15 of its
+// expert's down matrix (B, from the ring; the next item's blocks are loaded as this item's
+// are consumed, at code offset nco / scale offset nso); writes y_pairs.
+template <int HB, int IB, int NH>
+__device__ __forceinline__ void routed_down_item(const DecodeArgs& a, int pos0, int npairs, int r16,
+                                                 DownRing<IB>& ring, rsrc_t rc, rsrc_t rs, uint32_t nco,
+                                                 uint32_t nso, const uint32_t* s_lut, const uint8_t* s_h) {
+  constexpr int H = HB * 256, I = IB * 256, HROW = 2 * I + 16;
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  const uint4 sc = ring.sc;
+  ring.load_scales(rs, nso);
+  const uint8_t* a0 = s_h + col * HROW + 128 * g;
+  f32x4_t acc[NH];
+#pragma unroll
+  for (int q = 0; q < NH; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    const uint2 qj = ring.q[j];
+    const uint32_t qhj = ring.qh[j];
+    ring.load_block(rc, nco, j);
+    bf16x8_t wv[8];
+    stq_block_w(s_lut, qj, qhj, wv);
+    // two MFMA chains per half (even and odd steps)
+    f32x4_t b[2][NH];
+#pragma unroll
+    for (int q = 0; q < NH; ++q) { b[0][q] = f32x4_t{0.f, 0.f, 0.f, 0.f}; b[1][q] = b[0][q]; }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int q = 0; q < NH; ++q) {
+        const uint4 x = *reinterpret_cast<const uint4*>(a0 + q * 16 * HROW + 512 * j + 16 * t);
+        b[t & 1][q] = mfma16(as_bf16x8(x), wv[t], b[t & 1][q]);
+      }
+    }
+    const float d = scale_of(sc, j);
+#pragma unroll
+    for (int q = 0; q < NH; ++q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[q][i] = fmaf(d, b[0][q][i] + b[1][q][i], acc[q][i]);
+      pin4(acc[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NH; ++q) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int p = 8 * q + 2 * g + m;
+      if (p < npairs) a.y_pairs[(size_t)(pos0 + p) * H + r16 + col] = acc[q][2 * m] + acc[q][2 * m + 1];
+    }
+  }
+}
+
+// Large T, third kernel: the shared expert's down items (16-token tile, 128 rows: each
+// weighs about 12 routed items -- bf16 against 42/256 bytes per weight -- so they are dealt
+// round-robin, at most one or two per workgroup) and the routed down items (contiguous
+// ranges), persistent workgroups.  A unit's (or tile's) h is staged once per change.
+constexpr int kSharedItemWeight = 12;
+template <int HB, int IB>
+__global__ __launch_bounds__(kLW) void k3l_down(DecodeArgs a) {
+  constexpr int H = HB * 256, I = IB * 256, NS = H / kSlice;
+  static_assert(H % kSlice == 0, "slices");
+  extern __shared__ __align__(16) uint8_t s_h[];   // 32 A rows of 2 I + 16 bytes
+  __shared__ uint32_t s_lut[64];
+  const int wave = threadIdx.x >> 6, col = threadIdx.x & 15;
+  const int T = a.T;
+  const int n_sh = a.sd ? ((T + 15) / 16) * NS : 0;
+  const int n_units = a.wl[1];
+  int i0, i1;
+  light_range(blockIdx.x, gridDim.x, n_units * NS, n_sh, kSharedItemWeight, i0, i1);
+  build_lut(s_lut);
+  if (n_sh) {
+    const rsrc_t rhs = make_rsrc(a.hs, (uint32_t)T * I * 4);
+    int staged = -1;
+    for (int si = blockIdx.x; si < n_sh; si += gridDim.x) {
+      const int tt = si / NS;
+      if (tt != staged) {
+        __syncthreads();   // every wave is done with the previous tile
+        stage_h_large<IB>(rhs, (uint32_t)T * I * 2, 16 * tt, min(16, T - 16 * tt), s_h);
+        __syncthreads();
+        staged = tt;
+      }
+      shared_down_item<HB, IB>(a, tt, si % NS, s_h);
+    }
+  }
+  int i = i0;
+  if (i >= i1) return;
+  const rsrc_t rh = make_rsrc(a.h_hi, a.h_bytes);
+  const rsrc_t rc = make_rsrc(a.dc, (uint32_t)((size_t)a.E * H * IB * 40));
+  const rsrc_t rs = make_rsrc(a.ds, (uint32_t)((size_t)a.E * H * IB * 2));
+  auto code_off = [&](int e, int slice) {   // this lane's down row of expert e, item slice
+    return (uint32_t)(((size_t)e * H + slice * kSlice + 16 * wave + col) * IB * 40);
+  };
+  auto scale_off = [&](int e, int slice) {
+    return (uint32_t)(((size_t)e * H + slice * kSlice + 16 * wave + col) * IB * 2);
+  };
+  int u = i / NS;
+  int4 un = a.ut[u];
+  int4 un_next = a.ut[min(u + 1, n_units - 1)];
+  DownRing<IB> ring;
+  {
+    const int sl = i % NS;
+    const uint32_t co = code_off(un.x, sl);
+#pragma unroll
+    for (int j = 0; j < IB; ++j) ring.load_block(rc, co, j);
+    ring.load_scales(rs, scale_off(un.x, sl));
+  }
+  // one unit's items at a time, the unit's half count fixed for the inner loop
+  while (i < i1) {
+    const int ui = i / NS;
+    if (ui != u) {       // the next unit of the range
+      u = ui;
+      un = un_next;
+      un_next = a.ut[min(u + 1, n_units - 1)];
+    }
+    __syncthreads();
+    stage_h_large<IB>(rh, a.h_lo_bytes, un.y, un.z, s_h);
+    __syncthreads();
+    const int iend = min(i1, (u + 1) * NS);
+    auto run = [&](auto nh_tag) {
+      constexpr int NHC = decltype(nh_tag)::value;
+      for (; i < iend; ++i) {
+        const int slice = i % NS;
+        uint32_t nco = kOOB, nso = kOOB;
+        if (i + 1 < i1) {
+          const bool same = slice + 1 < NS;
+          const int e2 = same ? un.x : un_next.x;
+          const int s2 = same ? slice + 1 : 0;
+          nco = code_off(e2, s2);
+          nso = scale_off(e2, s2);
+        }
+        routed_down_item<HB, IB, NHC>(a, un.y, un.z, slice * kSlice + 16 * wave, ring, rc, rs, nco, nso, s_lut, s_h);
+      }
+    };
+    if (un.z > 8) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+  }
 }
 
 // Shared down for up to kXT tokens: wave w takes NR consecutive rows from row0 + NR w,
@@ -1191,9 +1548,10 @@ __device__ __forceinline__ void shared_down_small(const DecodeArgs& a, int sw, u
 
 // ============================================================================ K3
 // Routed gate/up of one work item (unit, 32 rows of I) of a small-T layer, every token's x
-// row already in LDS; as routed_gateup otherwise.
+// row already in LDS: wave = (16-row tile, gate|up) over all of K; the gate and up waves of
+// a tile meet in LDS and the gate wave writes h = SiLU(gate) * up as bf16 hi + lo.
 template <int HB, int IB>
-__device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi, const uint2* s_lut,
+__device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi, const uint32_t* s_lut,
                                                     const uint16_t* s_x, float (*s_red)[2][4][64],
                                                     const SmallRoute& R, uint8_t* s_cw) {
   constexpr int H = HB * 256, I = IB * 256, NTP = I / 32;
@@ -1230,7 +1588,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k
   constexpr int H = HB * 256, I = IB * 256;
   static_assert(2 * I <= H, "the shared h (T rows of I fp32) fits the x staging (T rows of H bf16)");
   extern __shared__ __align__(16) uint16_t s_x[];   // XR x rows (bf16), or the shared h
-  __shared__ uint2 s_lut[32];
+  __shared__ uint32_t s_lut[64];
   __shared__ __align__(16) float s_red[2][2][4][64];
   __shared__ SmallRoute s_rt;
   __shared__ __align__(16) uint8_t s_cw[kNW * StqStreamL<HB>::BYTES];   // code staging
@@ -1260,52 +1618,8 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 }
 
-// Shared down beyond kXT tokens: 16 rows x 16-token tiles; wave w takes K blocks w, w + 8,
-// .. (A = h hi and lo rows, B = weights); the waves' partials meet in LDS (s_red) in order,
-// wave 0 writes y_shared and adds it into its own sums.
-template <int HB, int IB>
-__device__ __forceinline__ void shared_down_mfma(const DecodeArgs& a, int row0, float* s_acc, float* s_red) {
-  constexpr int H = HB * 256, I = IB * 256;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int T = a.T;
-  const rsrc_t rh = make_rsrc(a.hs, (uint32_t)T * I * 4);
-  const uint32_t lo = 2u * (uint32_t)T * I;
-  const uint16_t* rd = a.sd + (size_t)(row0 + col) * I;
-  for (int tt = 0; tt * 16 < T; ++tt) {
-    const int tok = tt * 16 + col;
-    const uint32_t ho = tok < T ? 2u * (uint32_t)tok * I : kOOB;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int b = wave; b < IB; b += kDnWaves) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int off = 256 * b + 32 * t + 8 * g;
-        const bf16x8_t wv = as_bf16x8(*reinterpret_cast<const uint4*>(rd + off));
-        acc = mfma16(as_bf16x8(bload16(rh, ho, 2 * off)), wv, acc);
-        acc = mfma16(as_bf16x8(bload16(rh, ho + lo, 2 * off)), wv, acc);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_red[(wave * 4 + i) * 64 + lane] = acc[i];
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tt * 16 + 4 * g + i;
-        if (t < T) {
-          float v = 0.f;
-          for (int w = 0; w < kDnWaves; ++w) v += s_red[(w * 4 + i) * 64 + lane];
-          a.y_shared[(size_t)t * H + row0 + col] = v;
-          s_acc[t * 16 + col] += v;
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// One 16-row slice of the output: the shared expert's down projection (SDN: MFMA over
-// 16-token tiles, large T; otherwise 2 rows per wave on the VALU) and every half-unit
+// Up to kXT tokens, one 16-row slice of the output: the shared expert's down projection (2
+// rows per wave on the VALU, unless YSH) and every half-unit
 // (expert, <= 8 pairs) spread over the 8 waves, each wave adding its results into its own
 // LDS sums; out = sum over waves in order (+ residual).  HLDS: all h (few tokens) is staged
 // in LDS first: routed hi rows, routed lo rows, shared hi rows, shared lo rows.
@@ -1313,10 +1627,9 @@ __device__ __forceinline__ void shared_down_mfma(const DecodeArgs& a, int row0, 
 // work items, one per 16-row tile.
 // YSH: the shared expert's down projection already ran (second kernel); the combine adds
 // y_shared from memory (and h holds the routed pairs only).
-template <int HB, int IB, bool SDN, bool HLDS, int RW = 16, bool YSH = false>
+template <int HB, int IB, bool HLDS, int RW = 16, bool YSH = false>
 __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
-  static_assert(RW % 16 == 0 && (!SDN || RW == 16), "rows per workgroup");
-  static_assert(!(SDN && YSH), "one place for the shared down");
+  static_assert(RW % 16 == 0, "rows per workgroup");
   constexpr int NTL = RW / 16;
   constexpr int H = HB * 256, I = IB * 256;
   constexpr int kStage = 10;                 // uint4 per thread when h is staged
@@ -1324,7 +1637,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
                                              // pair's hi and lo reads fall in different banks
   extern __shared__ __align__(16) float s_dyn[];  // [kDnWaves][T][16] sums, then staged h
                                                   // or the shared partials [kDnWaves][4][64]
-  __shared__ uint2 s_lut[32];
+  __shared__ uint32_t s_lut[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, P = T * a.k;
   const int row0 = blockIdx.x * RW;
@@ -1376,7 +1689,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   }
   // the shared rows' first weight chunks
   SharedDown<HB, IB, RW / 8, true, RW> sdn;
-  if constexpr (!SDN && !YSH) sdn.issue(a, row0);
+  if constexpr (!YSH) sdn.issue(a, row0);
   // first work item's code words, read beside the entry count (a wave without an item
   // streams some valid expert's rows, unused)
   const int n_ent = a.wl[2];
@@ -1390,8 +1703,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   }
   lds_barrier();
   if (!YSH && a.sd) {
-    if constexpr (SDN) shared_down_mfma<HB, IB>(a, row0, s_acc, s_dyn + kDnWaves * T * 16);
-    else if constexpr (HLDS) sdn.run(a, row0, s_h + 2 * P * I + kLoPad, s_acc);
+    if constexpr (HLDS) sdn.run(a, row0, s_h + 2 * P * I + kLoPad, s_acc);
     else sdn.run(a, row0, a.hs, s_acc);
   }
   const rsrc_t rh = make_rsrc(a.h_hi, a.h_bytes);
@@ -1797,41 +2109,55 @@ hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k2s_gateup<HB, IB, XR>), dim3(a.n_gu_wg + n_sdn_wg), dim3(kWG), lds2, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
-  if (a.h_lds) hipLaunchKernelGGL((k3_down_combine<HB, IB, false, true, RW, true>), dim3(H / RW), dim3(64 * kDnWaves), lds3, s, a);
-  else hipLaunchKernelGGL((k3_down_combine<HB, IB, false, false, RW, true>), dim3(H / RW), dim3(64 * kDnWaves), lds3, s, a);
+  if (a.h_lds) hipLaunchKernelGGL((k3_down_combine<HB, IB, true, RW, true>), dim3(H / RW), dim3(64 * kDnWaves), lds3, s, a);
+  else hipLaunchKernelGGL((k3_down_combine<HB, IB, false, RW, true>), dim3(H / RW), dim3(64 * kDnWaves), lds3, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
   return hipSuccess;
 }
 
-// Large T: router + routing (ticket), routed + shared gate/up, all down + combine.
+// Compute units of the current device (persistent grids: one workgroup per CU).
+int device_cus() {
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Large T: (1) router + routing (tickets) beside the shared gate/up; (2) routed gate/up
+// items; (3) shared and routed down items; (4) combine (+ y_shared, + residual).
 template <int HB, int IB>
 hipError_t launch_large(DecodeArgs& a, hipStream_t s) {
-  constexpr int H = HB * 256, I = IB * 256;
+  constexpr int I = IB * 256;
   const int T = a.T;
   const int n_tt = (T + 15) / 16;
-  const int P = T * a.k;
-  const int max_units = (P < a.E ? P : a.E) + (P + 15) / 16;
   a.n_router_wg = ((a.E + 15) / 16) * kRouterParts * n_tt;
   const bool shared = a.sg != nullptr;
   a.n_sgu_wg = shared ? (I / 16) * n_tt : 0;
-  const int cap = 8192;
-  const int gu = max_units * (I / 32);
-  a.n_gu_wg = gu < cap ? gu : cap;
   a.h_lds = 0;
-  const size_t lds2 = (size_t)kXT * H * 2;
-  const size_t lds3 = (size_t)kDnWaves * T * 16 * 4 + (size_t)kDnWaves * 4 * 64 * 4;
+  a.ysh_ready = 0;
+  const int cus = device_cus();
+  const size_t lds2 = (size_t)8 * (2 * HB * 256 + 16);
+  const size_t lds3 = (size_t)32 * (2 * I + 16);
   const bool prof = moe_prof_on();
   if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
-  hipLaunchKernelGGL((k1_route<HB, kMaxT * 32, 8>), dim3(a.n_router_wg), dim3(kWG), 0, s, a);
+  hipLaunchKernelGGL((k1_route<HB, IB, kMaxT * 32, 8>), dim3(a.n_router_wg + a.n_sgu_wg), dim3(kWG), 0, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
-  hipLaunchKernelGGL((k2_gateup<HB, IB>), dim3(a.n_gu_wg + a.n_sgu_wg), dim3(kWG), lds2, s, a);
+  hipLaunchKernelGGL((k2l_gateup<HB, IB>), dim3(cus), dim3(kLW), lds2, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
-  hipLaunchKernelGGL((k3_down_combine<HB, IB, true, false>), dim3(H / 16), dim3(64 * kDnWaves), lds3, s, a);
+  hipLaunchKernelGGL((k3l_down<HB, IB>), dim3(cus), dim3(kLW), lds3, s, a);
   MOE_HIP_TRY(hipGetLastError());
-  if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K3, s); moe_prof_begin(MOE_PROF_DECODE_K4, s); }
+  MOE_HIP_TRY(moe_launch_combine(a.y_pairs, a.w, a.pair_pos, a.y_shared, a.residual, a.out, a.out_bf16,
+                                 T, HB * 256, a.k, s));
+  if (prof) moe_prof_end(MOE_PROF_DECODE_K4, s);
   return hipSuccess;
 }
 

@@ -289,7 +289,7 @@ inline int moe_cu_count() {
 
 // Opt-in kernel timing with HIP events recorded on the launch stream around single kernels.
 enum {
-  MOE_PROF_DECODE_K1 = 0, MOE_PROF_DECODE_K2 = 1, MOE_PROF_DECODE_K3 = 2,
+  MOE_PROF_DECODE_K1 = 0, MOE_PROF_DECODE_K2 = 1, MOE_PROF_DECODE_K3 = 2, MOE_PROF_DECODE_K4 = 3,
   MOE_PROF_MX_QUANT = 4, MOE_PROF_MX_GATEUP = 5, MOE_PROF_MX_DOWN = 6,
   MOE_PROF_STQ_GATEUP = 7, MOE_PROF_STQ_DOWN = 8, MOE_PROF_SH_GATEUP = 9, MOE_PROF_SH_DOWN = 10,
   MOE_PROF_ACT_PREP = 11,

@@ -128,7 +128,9 @@ MOE_MI355X_API moe_status moe_get_counters(uint64_t* out);
 MOE_MI355X_API moe_status moe_reset_counters(void);
 
 /* Opt-in kernel timing: while enabled the library records a HIP event pair on the launch
- * stream around each of its main kernels (slots: 0..2 the three kernels of moe_layer_decode, 4/5/6 MX quantisation, MXFP4 gate/up and down GEMMs, 7/8 the STQ1_0
+ * stream around each of its main kernels (slots: 0..3 the kernels of moe_layer_decode -- routing,
+ * gate/up, down, and beyond 4 tokens the separate combine --, 4/5/6 MX quantisation, MXFP4
+ * gate/up and down GEMMs, 7/8 the STQ1_0
  * prefill gate/up and down GEMMs, 9/10 the shared expert's prefill gate/up and down GEMMs,
  * 11 the activation conversions of the prefill GEMMs).  Enabling
  * creates the event pools once (host objects, no device memory).  moe_profile_read waits

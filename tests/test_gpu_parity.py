@@ -689,6 +689,12 @@ FUSED = {
     "h512-i256-e8-top2-t37-shared": synth.LayerCfg("t", 37, 512, 256, 8, 2, True, "stq1", False, False, 1, 11),
     "h1024-i512-e16-top4-t21-zipf": synth.LayerCfg("t", 21, 1024, 512, 16, 4, True, "stq1", True, False, 1, 14),
     "h512-i256-e40-top8-t64-noshared": synth.LayerCfg("t", 64, 512, 256, 40, 8, False, "stq1", True, False, 1, 15),
+    # beyond 4 tokens: every expert takes all 64 tokens (four full units each, two 8-pair
+    # halves per unit in the down items; four shared token tiles); the smallest large batch;
+    # two token tiles, the second of one token
+    "h512-i256-e4-top4-t64-shared": synth.LayerCfg("t", 64, 512, 256, 4, 4, True, "stq1", False, False, 1, 17),
+    "h512-i256-e16-top8-t5-shared": synth.LayerCfg("t", 5, 512, 256, 16, 8, True, "stq1", False, False, 1, 18),
+    "h2048-i1024-e16-top4-t17-zipf": synth.LayerCfg("t", 17, 2048, 1024, 16, 4, True, "stq1", True, False, 1, 19),
     "h512-i256-e8-top2-t1-shared": synth.LayerCfg("t", 1, 512, 256, 8, 2, True, "stq1", False, False, 1, 16),
     # 2..4 tokens: the per-workgroup routing path, experts shared by several tokens
     "h512-i256-e8-top2-t4-shared": synth.LayerCfg("t", 4, 512, 256, 8, 2, True, "stq1", False, False, 1, 23),
