@@ -679,12 +679,70 @@ __device__ __forceinline__ void wave_topk(const DecodeArgs& a, int t, const Topk
   wave_lds_sync();
 }
 
+// Top-k of up to four tokens by one wave (token q valid for q < nq), the four selection
+// chains interleaved round by round: each round's wave reduction and lane search is a
+// chain of dependent DPP, readlane and scalar steps, and four independent chains keep the
+// SIMD busy where one leaves it waiting.  Per token as wave_topk; token q's slots land in
+// s_v[q] / s_i[q], its ids and weight bits at tq[q] k + slot of ids_out / wbits_out.
+__device__ __forceinline__ void wave_topk4(const DecodeArgs& a, const int* tq, int nq, const TopkSum* ls,
+                                           float (*s_v)[32], int (*s_i)[32], int* ids_out, int* wbits_out) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
+  uint32_t key[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[q][i] = i * 64 + lane < E ? fkey(ls[q].s[i]) : 0u;
+  }
+  for (int r = 0; r < k; ++r) {
+    uint32_t m[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = wave_max_u32(max(max(key[q][0], key[q][1]), max(key[q][2], key[q][3])));
+    int sel[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sel[q] = -1;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        const uint64_t b = __ballot(key[q][i] == m[q]);
+        if (b) sel[q] = i * 64 + __ffsll((unsigned long long)b) - 1;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[q][i] = i * 64 + lane == sel[q] ? 0u : key[q][i];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s_v[q][r] = fkey_value(m[q]);
+        s_i[q][r] = sel[q];
+      }
+    }
+  }
+  wave_lds_sync();
+  if (lane < k) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < nq) {
+        const float vmax = s_v[q][0];
+        float sum = 0.f;   // the same (slot) order in every lane
+        for (int j = 0; j < k; ++j) sum += expf(s_v[q][j] - vmax);
+        ids_out[tq[q] * k + lane] = s_i[q][lane];
+        wbits_out[tq[q] * k + lane] = __float_as_int(expf(s_v[q][lane] - vmax) / sum);
+      }
+    }
+  }
+  wave_lds_sync();
+}
+
 template <int P0>
 struct FinalizeLds {
   int ids[3 * P0];           // [0, P) expert of each pair; [P0, P0 + P) pairs in sorted order;
                              // [2 P0, 2 P0 + P) weight bits of each pair (P <= P0)
-  float v[kNW][32];
-  int i[kNW][32];
+  float v[kNW][4][32];
+  int i[kNW][4][32];
   int cnt[kMaxE];
   int base[kMaxE];
   int ebase[kMaxE];          // first sorted position of each expert
@@ -693,18 +751,39 @@ struct FinalizeLds {
   int wsum[kNW * 4];
 };
 
-// Top-k of tokens t0 .. t1 - 1 (t1 - t0 <= 16: wave w takes t0 + w + 4 i), every input load
-// issued before the first selection; writes logits, ids and weights.
-__device__ __forceinline__ void route_topk_tile(const DecodeArgs& a, int t0, int t1, float* s_v, int* s_i,
+// Top-k of tokens t0 .. t1 - 1 (t1 - t0 <= 16: wave w takes t0 + w + 4 i, the four at once),
+// every input load issued before the first selection; writes logits, ids and weights.
+__device__ __forceinline__ void route_topk_tile(const DecodeArgs& a, int t0, int t1, float (*s_v)[32], int (*s_i)[32],
                                                 int* ids_l, int* wb_l) {
   const int wave = threadIdx.x >> 6;
   TopkIn in[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) topk_load(a, min(t0 + wave + kNW * i, t1 - 1), in[i]);
+  int tq[4], nq = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t = t0 + wave + kNW * i;
-    if (t < t1) wave_topk(a, t, topk_sums(a, in[i]), s_v, s_i, ids_l, wb_l, true);
+    tq[i] = t0 + wave + kNW * i;
+    nq += tq[i] < t1;
+    topk_load(a, min(tq[i], t1 - 1), in[i]);
+  }
+  // Every sum before the first selection and every store after the last: a memory
+  // operation in flight during the selection rounds (whose registers the rounds reuse)
+  // makes each round wait for it.
+  TopkSum ls[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ls[i] = topk_sums(a, in[i]);
+  wave_topk4(a, tq, nq, ls, s_v, s_i, ids_l, wb_l);
+  const int lane = threadIdx.x & 63, E = a.E, k = a.k;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tq[i];
+    if (t < t1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q * 64 + lane < E) a.logits[(size_t)t * E + q * 64 + lane] = ls[i].s[q];
+      if (lane < k) {
+        a.ids[(size_t)t * k + lane] = ids_l[t * k + lane];
+        a.w[(size_t)t * k + lane] = __int_as_float(wb_l[t * k + lane]);
+      }
+    }
   }
 }
 
@@ -823,23 +902,99 @@ __device__ __forceinline__ void route_permute(const DecodeArgs& a, FinalizeLds<P
   }
 }
 
-template <int HB, int IB>
-__device__ __forceinline__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2][4][64]);
+// Shared gate/up beyond kXT tokens, beside the routing chain of the first kernel: rows
+// 16 rt .. 16 rt + 15 of the bf16 gate and up matrices (A) for up to MT token tiles (B = x
+// columns), the 4 waves splitting K.  A block's weights are loaded once for all tiles and
+// every tile's x operand of the block at once; up to two tiles, the next block's weights
+// are in flight meanwhile (four tiles' operands leave no registers for them).  The waves'
+// partials meet in LDS in wave order, one tile at a time.
+template <int HB, int IB, int MT>
+__device__ __forceinline__ void shared_gateup_k1(const DecodeArgs& a, int rt, float (*s_red)[2][4][64]) {
+  constexpr int H = HB * 256, I = IB * 256, NBW = (HB + kNW - 1) / kNW;
+  constexpr bool PREF = MT <= 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int T = a.T, n_tt = (T + 15) / 16;
+  const int b0 = wave * HB / kNW, b1 = (wave + 1) * HB / kNW;
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)T * H * 2);
+  const rsrc_t rg = make_rsrc(a.sg, (uint32_t)I * H * 2), ru = make_rsrc(a.su, (uint32_t)I * H * 2);
+  const uint32_t wo = 2u * (uint32_t)(16 * rt + col) * H;
+  auto load_w = [&](int m, uint4 (*w)[8]) {
+    const int bk = b0 + m;
+    const bool ok = bk < b1;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t off = 2u * (256 * bk + 64 * g + 8 * t);
+      w[0][t] = bload16(rg, ok ? wo + off : kOOB);
+      w[1][t] = bload16(ru, ok ? wo + off : kOOB);
+    }
+  };
+  auto load_x = [&](int m, int tt, uint4* xv) {
+    const int bk = b0 + m, tok = 16 * tt + col;
+    const bool ok = bk < b1 && tok < T;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xv[t] = bload16(rx, ok ? 2u * ((uint32_t)tok * H + 256 * bk + 64 * g + 8 * t) : kOOB);
+  };
+  f32x4_t acc[MT][2];
+#pragma unroll
+  for (int tt = 0; tt < MT; ++tt) { acc[tt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f}; acc[tt][1] = acc[tt][0]; }
+  uint4 w[PREF ? 2 : 1][2][8];
+  if (PREF) load_w(0, w[0]);
+#pragma unroll
+  for (int m = 0; m < NBW; ++m) {
+    uint4 xv[MT][8];
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt) load_x(m, tt, xv[tt]);   // tiles past the last read zeros
+    if (PREF) {
+      if (m + 1 < NBW) load_w(m + 1, w[(m + 1) & 1]);
+    } else {
+      load_w(m, w[0]);
+    }
+    const int ws = PREF ? (m & 1) : 0;
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt) {
+      if (tt < n_tt) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          acc[tt][0] = mfma16(as_bf16x8(w[ws][0][t]), as_bf16x8(xv[tt][t]), acc[tt][0]);
+          acc[tt][1] = mfma16(as_bf16x8(w[ws][1][t]), as_bf16x8(xv[tt][t]), acc[tt][1]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < MT; ++tt) {
+    if (tt < n_tt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { s_red[wave][0][i][lane] = acc[tt][0][i]; s_red[wave][1][i][lane] = acc[tt][1][i]; }
+      __syncthreads();
+      const int tok = 16 * tt + col;
+      if (wave == 0 && tok < T) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float gs = 0.f, us = 0.f;
+          for (int w2 = 0; w2 < kNW; ++w2) { gs += s_red[w2][0][i][lane]; us += s_red[w2][1][i][lane]; }
+          store_hilo(a.hs + (size_t)tok * I + 16 * rt + 4 * g + i, (size_t)T * I, silu_mul(gs, us));
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
 
-// Beyond kXT tokens, first kernel: router partials (workgroups 0 .. n_router_wg - 1, per
-// 16-token tile), then the shared expert's gate/up (16 rows x 16 tokens per workgroup).
-// Routing runs as a chain of two tickets, agent-scope acquire/release atomics on counters
-// in the workspace: the last router workgroup of a token tile sums that tile's partials and
-// picks its tokens' top-k (tiles in parallel); the last tile to finish sorts all pairs and
-// writes the work lists, then leaves every counter at zero for the next call.
-template <int HB, int IB, int P0, int QN>
+// Beyond kXT tokens, first kernel: the shared expert's gate/up (workgroups n_router_wg ..)
+// beside the routing -- router partials (per 16-token tile), then a chain of two tickets, agent-scope acquire/release atomics on counters in the workspace:
+// the last router workgroup of a token tile sums that tile's partials and picks its tokens'
+// top-k (tiles in parallel); the last tile to finish sorts all pairs and writes the work
+// lists, then leaves every counter at zero for the next call.
+template <int HB, int IB, int MT, int P0, int QN>
 __global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
   __shared__ __align__(16) float s_red[kNW][4][64];
   __shared__ int s_last;
   __shared__ FinalizeLds<P0> s_fin;
   const int b = blockIdx.x;
   if (b >= a.n_router_wg) {
-    shared_gateup_mfma<HB, IB>(a, b - a.n_router_wg, reinterpret_cast<float(*)[2][4][64]>(s_fin.ids));
+    shared_gateup_k1<HB, IB, MT>(a, b - a.n_router_wg, reinterpret_cast<float(*)[2][4][64]>(s_fin.ids));
     return;
   }
   router_unit<HB>(a, b, s_red);
@@ -1031,58 +1186,6 @@ __device__ __forceinline__ void shared_gateup_valu(const DecodeArgs& a, int sw, 
   }
 }
 
-// Shared gate/up beyond kXT tokens: 16 rows x 16 tokens, the 4 waves split K (A = weight
-// rows, B = token columns).  Each wave's next block is in flight while one is multiplied;
-// blocks past the wave's share read as zeros (buffer loads out of range) and add nothing.
-template <int HB, int IB>
-__device__ __forceinline__ void shared_gateup_mfma(const DecodeArgs& a, int sw, float (*s_red)[2][4][64]) {
-  constexpr int H = HB * 256, I = IB * 256, n_rt = I / 16, NBW = (HB + kNW - 1) / kNW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rt = sw % n_rt, tt = sw / n_rt;
-  const int row0 = rt * 16;
-  const int col = lane & 15, g = lane >> 4;
-  const int tok = tt * 16 + col;
-  const bool t_ok = tok < a.T;
-  const int b0 = wave * HB / kNW, b1 = (wave + 1) * HB / kNW;
-  const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2);
-  const rsrc_t rg = make_rsrc(a.sg, (uint32_t)I * H * 2), ru = make_rsrc(a.su, (uint32_t)I * H * 2);
-  const uint32_t xo = 2u * (uint32_t)tok * H, wo = 2u * (uint32_t)(row0 + col) * H;
-  uint4 c[2][3][8];   // [slot][gate, up, x][step]
-  auto load = [&](int m, uint4 (*cs)[8]) {
-    const int b = b0 + m;
-    const bool ok = b < b1;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t off = 2u * (256 * b + 32 * t + 8 * g);
-      cs[0][t] = bload16(rg, ok ? wo + off : kOOB);
-      cs[1][t] = bload16(ru, ok ? wo + off : kOOB);
-      cs[2][t] = bload16(rx, ok && t_ok ? xo + off : kOOB);
-    }
-  };
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  load(0, c[0]);
-#pragma unroll
-  for (int m = 0; m < NBW; ++m) {
-    if (m + 1 < NBW) load(m + 1, c[(m + 1) & 1]);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      accg = mfma16(as_bf16x8(c[m & 1][0][t]), as_bf16x8(c[m & 1][2][t]), accg);
-      accu = mfma16(as_bf16x8(c[m & 1][1][t]), as_bf16x8(c[m & 1][2][t]), accu);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { s_red[wave][0][i][lane] = accg[i]; s_red[wave][1][i][lane] = accu[i]; }
-  __syncthreads();
-  if (wave == 0 && t_ok) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float gs = 0.f, us = 0.f;
-      for (int w = 0; w < kNW; ++w) { gs += s_red[w][0][i][lane]; us += s_red[w][1][i][lane]; }
-      store_hilo(a.hs + (size_t)tok * I + row0 + 4 * g + i, (size_t)a.T * I, silu_mul(gs, us));
-    }
-  }
-}
-
 // ============================================================================ large T
 // Beyond kXT tokens the routed projections run in persistent workgroups of 8 waves over a
 // list of work items (unit of <= 16 pairs, slice of 128 weight rows: 16 per wave); each
@@ -1093,16 +1196,16 @@ constexpr int kLNW = kLW / 64;
 constexpr int kSlice = 16 * kLNW;
 
 // Work split of a persistent grid of G workgroups: workgroup b takes the heavy items
-// b, b + G, b + 2 G, .. of n_heavy (each costing W light ones), then the contiguous range
-// [i0, i1) of the n light items that brings its share of the total cost closest to its even
-// share (the ranges are monotone in b and cover every light item exactly once).
-__device__ __forceinline__ void light_range(int b, int G, int n, int n_heavy, int W, int& i0, int& i1) {
-  const long C = (long)n + (long)W * n_heavy;
+// b, b + G, b + 2 G, .. of n_heavy (each costing WH), then the contiguous range [i0, i1) of
+// the n light items (each costing WL) that brings its share of the total cost closest to
+// its even share (the ranges are monotone in b and cover every light item exactly once).
+__device__ __forceinline__ void light_range(int b, int G, int n, int n_heavy, int WL, int WH, int& i0, int& i1) {
+  const long C = (long)WL * n + (long)WH * n_heavy;
   const int full = n_heavy / G, rem = n_heavy % G;
   auto end = [&](int bb) {   // end of workgroup bb's light range
     if (bb < 0) return 0L;
-    const long heavy = (long)W * ((long)(bb + 1) * full + min(bb + 1, rem));
-    const long e = C * (bb + 1) / G - heavy;
+    const long heavy = (long)WH * ((long)(bb + 1) * full + min(bb + 1, rem));
+    const long e = (C * (bb + 1) / G - heavy) / WL;
     return e < 0 ? 0L : (e > n ? (long)n : e);
   };
   i0 = (int)end(b - 1);
@@ -1112,9 +1215,9 @@ __device__ __forceinline__ void light_range(int b, int G, int n, int n_heavy, in
 // Large-T gate/up: the x rows of a half-unit (<= 8 tokens) in LDS, row r at byte r XROW
 // (H bf16 + 16 bytes of padding, so the rows one MFMA operand read touches start in
 // different banks); staged once per half-unit, every load issued before the first write.
-template <int HB>
+template <int HB, int NTHR>
 __device__ __forceinline__ void stage_x_large(const DecodeArgs& a, const int* toks, int n, uint8_t* s_x) {
-  constexpr int H = HB * 256, XROW = 2 * H + 16, PR = H / 8, PER = (8 * PR + kLW - 1) / kLW;
+  constexpr int H = HB * 256, XROW = 2 * H + 16, PR = H / 8, PER = (8 * PR + NTHR - 1) / NTHR;
   constexpr int PASS = PER < 12 ? PER : 12;
   const int tid = threadIdx.x;
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * H * 2);
@@ -1123,33 +1226,34 @@ __device__ __forceinline__ void stage_x_large(const DecodeArgs& a, const int* to
     uint4 v[PASS];
 #pragma unroll
     for (int m = 0; m < PASS; ++m) {
-      const int idx = tid + kLW * (m0 + m), r = idx / PR, pc = idx % PR;
+      const int idx = tid + NTHR * (m0 + m), r = idx / PR, pc = idx % PR;
       const bool ok = m0 + m < PER && r < n;
       v[m] = bload16(rx, ok ? 2u * (uint32_t)toks[ok ? r : 0] * H + 16u * pc : kOOB);
     }
 #pragma unroll
     for (int m = 0; m < PASS; ++m) {
-      const int idx = tid + kLW * (m0 + m), r = idx / PR, pc = idx % PR;
+      const int idx = tid + NTHR * (m0 + m), r = idx / PR, pc = idx % PR;
       if (m0 + m < PER && r < 8) *reinterpret_cast<uint4*>(s_x + r * XROW + 16 * pc) = v[m];
     }
   }
 }
 
 // One item of the large-T gate/up: wave w multiplies the half-unit's staged x rows (A) with
-// rows slice * 128 + 16 w .. + 15 of the expert's gate and up matrices (B, STQ1_0 decoded
-// through the table, RD blocks in flight) over all of K, then writes h = SiLU(gate) * up as
-// bf16 hi + lo.  No workgroup barrier inside: every wave streams on its own.
-template <int HB, int IB, int RD>
+// rows slice * 128 + 16 w .. + 15 of the expert's gate and up matrices (B, STQ1_0 code
+// words staged through the wave's LDS buffers in whole 16-byte row runs, decoded through
+// the table) over all of K, then writes h = SiLU(gate) * up as bf16 hi + lo.  No workgroup
+// barrier inside: every wave streams on its own.
+template <int HB, int IB, int NWV>
 __device__ __forceinline__ void routed_gateup_large(const DecodeArgs& a, int e, int pos0, int ntok, int slice,
-                                                    const uint32_t* s_lut, const uint8_t* s_x) {
+                                                    const uint32_t* s_lut, const uint8_t* s_x, uint8_t* s_cw) {
   constexpr int H = HB * 256, I = IB * 256, XROW = 2 * H + 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
-  const int row0 = slice * kSlice + 16 * wave;
-  const size_t wrow = (size_t)e * I + row0 + col;
-  StqStream<HB, RD> sg, su;
-  sg.issue(a.gc + wrow * HB * 40, a.gs + wrow * HB);
-  su.issue(a.uc + wrow * HB * 40, a.us + wrow * HB);
+  const int row0 = slice * 16 * NWV + 16 * wave;
+  const size_t wrow = (size_t)e * I + row0;   // the wave's first row
+  StqStreamL<HB> sg, su;
+  sg.issue(a.gc + wrow * HB * 40, a.gs + (wrow + col) * HB, s_cw + (2 * wave) * StqStreamL<HB>::BYTES);
+  su.issue(a.uc + wrow * HB * 40, a.us + (wrow + col) * HB, s_cw + (2 * wave + 1) * StqStreamL<HB>::BYTES);
   const uint8_t* xa = s_x + (col < ntok ? col : 0) * XROW + 128 * g;   // this lane's A operand
   f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
 #pragma unroll
@@ -1184,18 +1288,25 @@ __device__ __forceinline__ void routed_gateup_large(const DecodeArgs& a, int e, 
   }
 }
 
-// Large T, second kernel: the routed gate/up items (half-unit, 128 rows of I), persistent
-// workgroups over contiguous ranges of the item list; x is restaged when the half-unit
-// changes.
+// Waves of a large-T gate/up workgroup: 8, or 4 where 8 x rows and 8 waves' code staging
+// would not fit the 160 KB of LDS (H above 6144).
+__host__ __device__ constexpr int k2l_waves(int HB) { return HB > 24 ? 4 : 8; }
+__host__ __device__ constexpr size_t k2l_lds_x(int HB) { return (size_t)8 * (2 * HB * 256 + 16); }
+
+// Large T, second kernel: the routed gate/up items (half-unit, 16 rows per wave of I),
+// persistent workgroups over contiguous ranges of the item list; x is restaged when the
+// half-unit changes.
 template <int HB, int IB>
 __global__ __launch_bounds__(kLW) void k2l_gateup(DecodeArgs a) {
-  constexpr int I = IB * 256, NS = I / kSlice;
-  static_assert(I % kSlice == 0, "slices");
+  constexpr int I = IB * 256, NWV = k2l_waves(HB), NS = I / (16 * NWV);
+  static_assert(I % (16 * NWV) == 0, "slices");
+  static_assert(k2l_lds_x(HB) + 2 * NWV * StqStreamL<HB>::BYTES + 256 <= 160 * 1024, "LDS");
   __shared__ uint32_t s_lut[64];                  // first: table offsets fit the offset field
+  __shared__ __align__(16) uint8_t s_cw[2 * NWV * StqStreamL<HB>::BYTES];   // code staging
   extern __shared__ __align__(16) uint8_t s_xl[];  // 8 x rows
   build_lut(s_lut);
   int i0, i1;
-  light_range(blockIdx.x, gridDim.x, a.wl[2] * NS, 0, 1, i0, i1);
+  light_range(blockIdx.x, gridDim.x, a.wl[2] * NS, 0, 1, 1, i0, i1);
   int staged = -1;
   int4 hu = make_int4(0, 0, 0, 0);
   for (int i = i0; i < i1; ++i) {
@@ -1203,11 +1314,11 @@ __global__ __launch_bounds__(kLW) void k2l_gateup(DecodeArgs a) {
     if (h != staged) {
       hu = a.hl[h];
       __syncthreads();   // every wave is done with the previous rows
-      stage_x_large<HB>(a, a.utok + hu.w, hu.z, s_xl);
+      stage_x_large<HB, 64 * NWV>(a, a.utok + hu.w, hu.z, s_xl);
       __syncthreads();
       staged = h;
     }
-    routed_gateup_large<HB, IB, kRing>(a, hu.x, hu.y, hu.z, i % NS, s_lut, s_xl);
+    routed_gateup_large<HB, IB, NWV>(a, hu.x, hu.y, hu.z, i % NS, s_lut, s_xl, s_cw);
   }
 }
 
@@ -1376,7 +1487,7 @@ __global__ __launch_bounds__(kLW) void k3l_down(DecodeArgs a) {
   const int n_sh = a.sd ? ((T + 15) / 16) * NS : 0;
   const int n_units = a.wl[1];
   int i0, i1;
-  light_range(blockIdx.x, gridDim.x, n_units * NS, n_sh, kSharedItemWeight, i0, i1);
+  light_range(blockIdx.x, gridDim.x, n_units * NS, n_sh, 1, kSharedItemWeight, i0, i1);
   build_lut(s_lut);
   if (n_sh) {
     const rsrc_t rhs = make_rsrc(a.hs, (uint32_t)T * I * 4);
@@ -2137,19 +2248,21 @@ hipError_t launch_large(DecodeArgs& a, hipStream_t s) {
   const int T = a.T;
   const int n_tt = (T + 15) / 16;
   a.n_router_wg = ((a.E + 15) / 16) * kRouterParts * n_tt;
-  const bool shared = a.sg != nullptr;
-  a.n_sgu_wg = shared ? (I / 16) * n_tt : 0;
+  a.n_sgu_wg = a.sg ? I / 16 : 0;
   a.h_lds = 0;
   a.ysh_ready = 0;
   const int cus = device_cus();
-  const size_t lds2 = (size_t)8 * (2 * HB * 256 + 16);
+  const size_t lds2 = k2l_lds_x(HB);
   const size_t lds3 = (size_t)32 * (2 * I + 16);
   const bool prof = moe_prof_on();
   if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
-  hipLaunchKernelGGL((k1_route<HB, IB, kMaxT * 32, 8>), dim3(a.n_router_wg + a.n_sgu_wg), dim3(kWG), 0, s, a);
+  const dim3 g1(a.n_router_wg + a.n_sgu_wg);
+  if (n_tt == 1) hipLaunchKernelGGL((k1_route<HB, IB, 1, kMaxT * 32, 8>), g1, dim3(kWG), 0, s, a);
+  else if (n_tt == 2) hipLaunchKernelGGL((k1_route<HB, IB, 2, kMaxT * 32, 8>), g1, dim3(kWG), 0, s, a);
+  else hipLaunchKernelGGL((k1_route<HB, IB, kMaxT / 16, kMaxT * 32, 8>), g1, dim3(kWG), 0, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
-  hipLaunchKernelGGL((k2l_gateup<HB, IB>), dim3(cus), dim3(kLW), lds2, s, a);
+  hipLaunchKernelGGL((k2l_gateup<HB, IB>), dim3(cus), dim3(64 * k2l_waves(HB)), lds2, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
   hipLaunchKernelGGL((k3l_down<HB, IB>), dim3(cus), dim3(kLW), lds3, s, a);

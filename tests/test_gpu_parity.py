@@ -695,6 +695,9 @@ FUSED = {
     "h512-i256-e4-top4-t64-shared": synth.LayerCfg("t", 64, 512, 256, 4, 4, True, "stq1", False, False, 1, 17),
     "h512-i256-e16-top8-t5-shared": synth.LayerCfg("t", 5, 512, 256, 16, 8, True, "stq1", False, False, 1, 18),
     "h2048-i1024-e16-top4-t17-zipf": synth.LayerCfg("t", 17, 2048, 1024, 16, 4, True, "stq1", True, False, 1, 19),
+    # the widest supported H beyond 4 tokens (gate/up workgroups of 4 waves: 8 x rows of
+    # 16 KB and 8 waves' code staging would not fit the LDS together)
+    "h8192-i2048-e8-top2-t9-shared": synth.LayerCfg("t", 9, 8192, 2048, 8, 2, True, "stq1", False, False, 1, 20),
     "h512-i256-e8-top2-t1-shared": synth.LayerCfg("t", 1, 512, 256, 8, 2, True, "stq1", False, False, 1, 16),
     # 2..4 tokens: the per-workgroup routing path, experts shared by several tokens
     "h512-i256-e8-top2-t4-shared": synth.LayerCfg("t", 4, 512, 256, 8, 2, True, "stq1", False, False, 1, 23),
