@@ -536,11 +536,13 @@ def decode_t64_bench(args):
     act_b = c.T * c.H * 2 + c.T * c.H * 4 + d.P * c.H * 4 + c.T * c.H * 4   # x, out, y_pairs, y_shared
     unique_b = u_avg * expert_b
     step_b = unique_b + shared_b + router_b + act_b
-    kb = {"decode_k1_route": router_b + c.T * c.H * 2 + c.T * c.E * 4,
-          "decode_k2_gateup": u_avg * 2 * STQ_MAT_BYTES + 2 * c.I * c.H * 2 + c.T * c.H * 2
-                              + (d.P + c.T) * c.I * 4,
+    # beyond 4 tokens: K1 = router + routing beside the shared gate/up; K2 = routed gate/up;
+    # K3 = shared and routed down (writes y_shared, y_pairs); K4 = combine
+    kb = {"decode_k1_route": router_b + c.T * c.H * 2 + c.T * c.E * 4 + 2 * c.I * c.H * 2 + c.T * c.I * 4,
+          "decode_k2_gateup": u_avg * 2 * STQ_MAT_BYTES + c.T * c.H * 2 + d.P * c.I * 4,
           "decode_k3_down_combine": u_avg * STQ_MAT_BYTES + c.I * c.H * 2 + (d.P + c.T) * c.I * 4
-                                    + d.P * c.H * 4 + 2 * c.T * c.H * 4}
+                                    + d.P * c.H * 4 + c.T * c.H * 4,
+          "decode_k4_combine": d.P * c.H * 4 + 2 * c.T * c.H * 4}
     return dict(c=c, ms=ms, U=u_avg, unique_b=unique_b, step_b=step_b, prof=prof, kbytes=kb)
 
 
