@@ -24,6 +24,10 @@ CFLAGS = [
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # loops marked for full unrolling stay unrolled at every instantiated shape (the largest
+    # decode shapes exceed the default size limit; a rolled loop indexes its register arrays
+    # through scratch memory)
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

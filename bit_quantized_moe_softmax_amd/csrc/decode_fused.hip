@@ -339,34 +339,6 @@ struct StqStream {
     }
     return acc;
   }
-
-  // A operands from memory through rsrc ra at byte offset aoff (+ 2 K); each operand is
-  // reloaded for the next block as soon as its MFMA has been issued.
-  __device__ __forceinline__ f32x4_t run_mem(const uint32_t* lut, rsrc_t ra, uint32_t aoff) {
-    uint4 av[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) av[t] = bload16(ra, aoff, 2 * (8 * t));
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      uint2 qj;
-      uint32_t qhj;
-      float d;
-      next(j, qj, qhj, d);
-      bf16x8_t wv[8];
-      stq_block_w(lut, qj, qhj, wv);
-      f32x4_t bacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        bacc = mfma16(as_bf16x8(av[t]), wv[t], bacc);
-        if (j + 1 < NB) av[t] = bload16(ra, aoff, 2 * (256 * (j + 1) + 8 * t));
-      }
-      acc[0] = fmaf(d, bacc[0], acc[0]); acc[1] = fmaf(d, bacc[1], acc[1]);
-      acc[2] = fmaf(d, bacc[2], acc[2]); acc[3] = fmaf(d, bacc[3], acc[3]);
-      pin4(acc);
-    }
-    return acc;
-  }
 };
 
 // The same stream with the code words staged through a per-wave LDS buffer.  A wave's 16
@@ -1484,7 +1456,7 @@ __global__ __launch_bounds__(kLW) void k3l_down(DecodeArgs a) {
   __shared__ uint32_t s_lut[64];
   const int wave = threadIdx.x >> 6, col = threadIdx.x & 15;
   const int T = a.T;
-  const int n_sh = a.sd ? ((T + 15) / 16) * NS : 0;
+  const int n_sh = a.sd && !a.ysh_ready ? ((T + 15) / 16) * NS : 0;
   const int n_units = a.wl[1];
   int i0, i1;
   light_range(blockIdx.x, gridDim.x, n_units * NS, n_sh, 1, kSharedItemWeight, i0, i1);
@@ -1729,25 +1701,20 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 }
 
-// Up to kXT tokens, one 16-row slice of the output: the shared expert's down projection (2
-// rows per wave on the VALU, unless YSH) and every half-unit
+// One token (its routed h fits the LDS), one RW-row slice of the output: every half-unit
 // (expert, <= 8 pairs) spread over the 8 waves, each wave adding its results into its own
-// LDS sums; out = sum over waves in order (+ residual).  HLDS: all h (few tokens) is staged
-// in LDS first: routed hi rows, routed lo rows, shared hi rows, shared lo rows.
-// RW output rows per workgroup (every workgroup stages all of h); a routed entry is RW / 16
-// work items, one per 16-row tile.
-// YSH: the shared expert's down projection already ran (second kernel); the combine adds
-// y_shared from memory (and h holds the routed pairs only).
-template <int HB, int IB, bool HLDS, int RW = 16, bool YSH = false>
+// LDS sums; out = y_shared (written by the second kernel) + sum over waves in order
+// (+ residual).  All routed h is staged in LDS first (hi rows, then lo rows); a routed
+// entry is RW / 16 work items, one per 16-row tile.
+template <int HB, int IB, int RW = 16>
 __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   static_assert(RW % 16 == 0, "rows per workgroup");
   constexpr int NTL = RW / 16;
   constexpr int H = HB * 256, I = IB * 256;
-  constexpr int kStage = 10;                 // uint4 per thread when h is staged
+  constexpr int kStage = 10;                 // uint4 per thread of staged h
   constexpr int kLoPad = 32;                 // lo rows start 64 bytes past the hi rows' end so a
                                              // pair's hi and lo reads fall in different banks
-  extern __shared__ __align__(16) float s_dyn[];  // [kDnWaves][T][16] sums, then staged h
-                                                  // or the shared partials [kDnWaves][4][64]
+  extern __shared__ __align__(16) float s_dyn[];  // [kDnWaves][T][RW] sums, then staged h
   __shared__ uint32_t s_lut[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, P = T * a.k;
@@ -1755,27 +1722,25 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   const int col = lane & 15, g = lane >> 4;
   float* s_acc = s_dyn;
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn + kDnWaves * T * RW);
-  // residual of this slice (T * RW <= 1024 elements, two per thread), read up front
+  // residual and y_shared of this slice (T * RW <= 1024 elements, two per thread), read up front
   const rsrc_t rres = make_rsrc(a.residual, a.residual ? (uint32_t)T * H * 4 : 0u);
-  const rsrc_t rysh = make_rsrc(a.y_shared, YSH && a.y_shared ? (uint32_t)T * H * 4 : 0u);
+  const rsrc_t rysh = make_rsrc(a.y_shared, a.y_shared ? (uint32_t)T * H * 4 : 0u);
   float rs[2], ys[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int i = tid + 64 * kDnWaves * m;
     const uint32_t o = i < T * RW ? 4u * ((uint32_t)(i / RW) * H + row0 + (i % RW)) : kOOB;
     rs[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rres, o, 0, 0));
-    ys[m] = YSH ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rysh, o, 0, 0)) : 0.f;
+    ys[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rysh, o, 0, 0));
   }
-  // staged h, 16-byte pieces: routed hi rows, routed lo rows, shared h (not with YSH)
-  const int n_r0 = P * I / 8, n_r1 = P * I / 8;
-  const int n_all = n_r0 + n_r1 + (YSH ? 0 : T * I / 4);
-  // h_lds is set only when the workspace holds routed hi, routed lo and shared h back to
-  // back, so the staging is one linear copy.  Branch-free: every piece is written below, so
-  // the compiler keeps all loads in flight together (a load inside a conditional write is
-  // sunk into it and waited for one at a time).  Pieces past the end reload and rewrite
-  // piece 0, the same value thread 0 writes there.
+  // staged h, 16-byte pieces: routed hi rows, then routed lo rows (the workspace holds them
+  // back to back, so the staging is one linear copy).  Branch-free: every piece is written
+  // below, so the compiler keeps all loads in flight together (a load inside a conditional
+  // write is sunk into it and waited for one at a time).  Pieces past the end reload and
+  // rewrite piece 0, the same value thread 0 writes there.
+  const int n_r0 = P * I / 8, n_all = 2 * n_r0;
   uint4 hv[kStage];
-  if constexpr (HLDS) {
+  {
     const uint4* src = reinterpret_cast<const uint4*>(a.h_hi);
 #pragma unroll
     for (int m = 0; m < kStage; ++m) {
@@ -1787,20 +1752,15 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
   for (int i = tid; i < kDnWaves * T * RW; i += 64 * kDnWaves) s_acc[i] = 0.f;
   // the staged rows land before any weight load is issued: otherwise they would queue
   // behind every workgroup's weight stream
-  if constexpr (HLDS) {
 #pragma unroll
-    for (int m = 0; m < kStage; ++m) {
-      int i = tid + 64 * kDnWaves * m;
-      i = i < n_all ? i : 0;
-      reinterpret_cast<uint4*>(s_h + (i < n_r0 ? 0 : kLoPad))[i] = hv[m];
-    }
-    // keep the weight loads below: hoisted above these writes, one wave's weight stream
-    // queued ahead of another wave's staging loads in the CU's in-order memory queue
-    __builtin_amdgcn_sched_barrier(0);
+  for (int m = 0; m < kStage; ++m) {
+    int i = tid + 64 * kDnWaves * m;
+    i = i < n_all ? i : 0;
+    reinterpret_cast<uint4*>(s_h + (i < n_r0 ? 0 : kLoPad))[i] = hv[m];
   }
-  // the shared rows' first weight chunks
-  SharedDown<HB, IB, RW / 8, true, RW> sdn;
-  if constexpr (!YSH) sdn.issue(a, row0);
+  // keep the weight loads below: hoisted above these writes, one wave's weight stream
+  // queued ahead of another wave's staging loads in the CU's in-order memory queue
+  __builtin_amdgcn_sched_barrier(0);
   // first work item's code words, read beside the entry count (a wave without an item
   // streams some valid expert's rows, unused)
   const int n_ent = a.wl[2];
@@ -1813,11 +1773,6 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
     st.issue(a.dc + wrow * IB * 40, a.ds + wrow * IB);
   }
   lds_barrier();
-  if (!YSH && a.sd) {
-    if constexpr (HLDS) sdn.run(a, row0, s_h + 2 * P * I + kLoPad, s_acc);
-    else sdn.run(a, row0, a.hs, s_acc);
-  }
-  const rsrc_t rh = make_rsrc(a.h_hi, a.h_bytes);
   for (; it < n_ent * NTL; it += kDnWaves) {
     const int r16 = row0 + 16 * (it % NTL);   // first output row of this item's tile
     if (it != wave) {
@@ -1837,14 +1792,8 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
         tk[m] = a.utok[hent.w + p];
         wt[m] = a.uw[hent.w + p];
       }
-      f32x4_t acc;
-      if constexpr (HLDS) {
-        const int pr = pos0 + (sp2 < nq ? sp2 : 0);
-        acc = st.run_lds(s_lut, s_h + (col & 1) * (P * I + kLoPad) + pr * I + 64 * g);
-      } else {
-        const uint32_t ho = sp2 < nq ? (col & 1 ? a.h_lo_bytes : 0u) + 2u * ((uint32_t)(pos0 + sp2) * I + 64 * g) : kOOB;
-        acc = st.run_mem(s_lut, rh, ho);
-      }
+      const int pr = pos0 + (sp2 < nq ? sp2 : 0);
+      const f32x4_t acc = st.run_lds(s_lut, s_h + (col & 1) * (P * I + kLoPad) + pr * I + 64 * g);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int p = 2 * g + m;
@@ -1863,7 +1812,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
     const int i = tid + 64 * kDnWaves * m;
     if (i < T * RW) {
       const int t = i / RW, r = i % RW;
-      float v = ys[m];   // y_shared (YSH), else 0: the shared term is in the waves' sums
+      float v = ys[m];   // y_shared (0 without a shared expert)
       for (int w = 0; w < kDnWaves; ++w) v += s_acc[(w * T + t) * RW + r];
       v += rs[m];
       const size_t o = (size_t)t * H + row0 + r;
@@ -2137,7 +2086,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine_mx(DecodeArgs a
     const int i = tid + 64 * kDnWaves * m;
     if (i < T * 16) {
       const int t = i >> 4, r = i & 15;
-      float v = ys[m];   // y_shared (YSH), else 0: the shared term is in the waves' sums
+      float v = ys[m];   // y_shared (0 without a shared expert)
       for (int w = 0; w < kDnWaves; ++w) v += s_acc[(w * T + t) * 16 + r];
       v += rs[m];
       const size_t o = (size_t)t * H + row0 + r;
@@ -2145,6 +2094,19 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine_mx(DecodeArgs a
       if (a.out_bf16) a.out_bf16[o] = (uint16_t)f32_to_bf16_rne(v);
     }
   }
+}
+
+// Compute units of the current device (persistent grids: one workgroup per CU).
+int device_cus() {
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <int HB, int IB, int XR, bool TILED>
@@ -2211,7 +2173,7 @@ hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
   // output rows per down workgroup (each stages all of h): 32 halves the staging but
   // leaves 192 workgroups for 256 CUs, and K3 measured 21.5 us against 20.4 us with 16
   constexpr int RW = 16;
-  const size_t lds3 = (size_t)kDnWaves * T * RW * 4 + (a.h_lds ? (size_t)hbytes + 64 : 0);
+  const size_t lds3 = (size_t)kDnWaves * T * RW * 4 + (size_t)hbytes + 64;
   const bool prof = moe_prof_on();
   if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
   hipLaunchKernelGGL((k1s_router<HB, IB, XR>), dim3(a.n_router_wg + a.n_sgu_wg), dim3(kWG), lds1, s, a);
@@ -2220,24 +2182,21 @@ hipError_t launch_small(DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k2s_gateup<HB, IB, XR>), dim3(a.n_gu_wg + n_sdn_wg), dim3(kWG), lds2, s, a);
   MOE_HIP_TRY(hipGetLastError());
   if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
-  if (a.h_lds) hipLaunchKernelGGL((k3_down_combine<HB, IB, true, RW, true>), dim3(H / RW), dim3(64 * kDnWaves), lds3, s, a);
-  else hipLaunchKernelGGL((k3_down_combine<HB, IB, false, RW, true>), dim3(H / RW), dim3(64 * kDnWaves), lds3, s, a);
-  MOE_HIP_TRY(hipGetLastError());
-  if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
-  return hipSuccess;
-}
-
-// Compute units of the current device (persistent grids: one workgroup per CU).
-int device_cus() {
-  static int cus[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+  if (a.h_lds) {
+    hipLaunchKernelGGL((k3_down_combine<HB, IB, RW>), dim3(H / RW), dim3(64 * kDnWaves), lds3, s, a);
+    MOE_HIP_TRY(hipGetLastError());
+    if (prof) moe_prof_end(MOE_PROF_DECODE_K3, s);
+    return hipSuccess;
   }
-  return cus[dev];
+  // h beyond the LDS (more than one token at Hy4 shape): the item-list down kernel (the
+  // shared down already ran), then the combine
+  hipLaunchKernelGGL((k3l_down<HB, IB>), dim3(device_cus()), dim3(kLW), (size_t)32 * (2 * I + 16), s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K3, s); moe_prof_begin(MOE_PROF_DECODE_K4, s); }
+  MOE_HIP_TRY(moe_launch_combine(a.y_pairs, a.w, a.pair_pos, a.y_shared, a.residual, a.out, a.out_bf16,
+                                 T, H, a.k, s));
+  if (prof) moe_prof_end(MOE_PROF_DECODE_K4, s);
+  return hipSuccess;
 }
 
 // Large T: (1) router + routing (tickets) beside the shared gate/up; (2) routed gate/up
