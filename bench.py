@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the STQ1_0 prefill and MXFP4 decode lines")
+    p.add_argument("--no-chain", action="store_true",
+                   help="skip the 29-layer chain line (byte-counter runs: its kernels share names "
+                        "with the 64-token decode's)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first run a plain copy kernel (torch.neg) over this many MiB, three times, "
                         "as the reference dispatch for the HBM byte counters")
@@ -615,7 +618,11 @@ TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     "decode_k3_down_combine": "k3_down_combine<", "mx_gateup": "mx_gemm_kernel<true, true>",
     "mx_down": "mx_gemm_kernel<false, true>", "stq_gateup": "g16_kernel<0, true, 1>",
     "stq_down": "g16_kernel<0, false, 2>", "mxdec_k2_gateup": "k2s_gateup_mx<",
-    "mxdec_k3_down_combine": "k3_down_combine_mx<", "copy": "neg_kernel"}
+    "mxdec_k3_down_combine": "k3_down_combine_mx<",
+    # the 64-token decode (its K2 / K3 kernels are also the 16-token chain's: byte-counter runs
+    # pass --no-chain so that only the 64-token dispatches are averaged)
+    "t64_decode_k1_route": "k1_route<24, 8, 4,", "t64_decode_k2_gateup": "k2l_gateup<24, 8>",
+    "t64_decode_k3_down_combine": "k3l_down<24, 8>", "copy": "neg_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hy4_layer_hbm_traffic_per_kernel.md")
 _DEC_SRC = "bit_quantized_moe_softmax_amd/csrc/decode_fused.hip"
 _MX_SRC = "bit_quantized_moe_softmax_amd/csrc/mx_gemm.hip"
@@ -623,13 +630,20 @@ _G16_SRC = "bit_quantized_moe_softmax_amd/csrc/gemm16.hip"
 TRAFFIC_SOURCES = {"decode_k1_route": _DEC_SRC, "decode_k2_gateup": _DEC_SRC,
                    "decode_k3_down_combine": _DEC_SRC, "mx_gateup": _MX_SRC, "mx_down": _MX_SRC,
                    "stq_gateup": _G16_SRC, "stq_down": _G16_SRC, "mxdec_k2_gateup": _DEC_SRC,
-                   "mxdec_k3_down_combine": _DEC_SRC}
+                   "mxdec_k3_down_combine": _DEC_SRC, "t64_decode_k1_route": _DEC_SRC,
+                   "t64_decode_k2_gateup": _DEC_SRC, "t64_decode_k3_down_combine": _DEC_SRC}
 
 
 def source_hash(slot):
-    """First 16 hex digits of the sha256 of the source file that holds the slot's kernel."""
+    """First 16 hex digits of the sha256 of the source file that holds the slot's kernel, with
+    its comments and blank lines removed (an edit of a comment does not change the kernel)."""
     import hashlib
-    return hashlib.sha256(open(os.path.join(ROOT, TRAFFIC_SOURCES[slot]), "rb").read()).hexdigest()[:16]
+    import re
+    src = open(os.path.join(ROOT, TRAFFIC_SOURCES[slot]), encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def pmc_summary(fetch_dir, write_dir, copy_mib):
@@ -990,6 +1004,7 @@ def main():
                              "traffic": traffic.get("t64_" + dom), "algorithmic_bytes": kern[dom]["algorithmic_bytes"]}}
         except Exception as e:
             out["decode_t64_zipf"] = {"error": repr(e)}
+    if not args.no_extra and not args.no_chain:
         try:
             ch = chain_bench(args)
             gbs = ch["step_b"] / (ch["ms"] * 1e-3) / 1e9

@@ -1,22 +1,33 @@
-// Fused decode-regime MoE layer: route -> permute -> expert FFN -> combine in three kernels.
+// Fused decode-regime MoE layer: route -> permute -> expert FFN -> combine in three or four
+// kernels.
 //
 // Same computation as the four separate entry points (router in BF16, top-k with
 // renormalised softmax weights, stable permutation, SwiGLU experts on STQ1_0 weights,
-// one bf16 shared expert, ungated combine), split by what each step waits for:
-//   K1  routing only: router logits (bf16 MFMA; a workgroup sums four K chunks of 16
-//       experts in LDS and writes one partial); the last router workgroup to finish (atomic
-//       ticket, one release fence per workgroup) sums the partials in a fixed order, picks
-//       the top-k, sorts the pairs by expert and writes the work lists: units of <= 16
-//       pairs of one expert (with each pair's token and weight) and half-units of <= 8.
-//       Nothing else runs beside it, so its short chain of dependent loads never queues
-//       behind bulk weight traffic;
-//   K2  every gate/up projection: routed (STQ1_0 decoded in registers, bf16 MFMA) and the
-//       shared expert's, each followed by SiLU(gate) * up;
-//   K3  every down projection and the combine, per 16-row slice of the output: the shared
-//       expert's rows and each half-unit's rows, weighted into per-wave LDS sums, then
-//       out = shared + sum over waves in a fixed order (+ residual).
+// one bf16 shared expert, ungated combine), split by what each step waits for.
+// Up to kXT tokens:
+//   K1  router partials (bf16 MFMA; a workgroup sums four K chunks of 16 experts in LDS
+//       and writes one partial), beside the shared expert's gate/up (VALU dot products);
+//   K2  every routed workgroup sums the partials and derives the whole routing in its own
+//       LDS (top-k, stable pair order, units), so no workgroup waits on another; then the
+//       routed gate/up (STQ1_0 decoded in registers, bf16 MFMA) with SiLU(gate) * up,
+//       beside the shared down;
+//   K3  one token: every routed down projection and the combine per 16-row slice of the
+//       output, weighted into per-wave LDS sums, out = y_shared + sum over waves in a fixed
+//       order (+ residual).  Two to four tokens (their h exceeds the LDS): the item-list
+//       down kernel below, then the separate combine.
+// Beyond kXT tokens (up to kMaxT):
+//   K1  router partials per 16-token tile and two tickets (agent-scope atomics on counters
+//       in the workspace): the last router workgroup of a tile picks that tile's top-k, the
+//       last tile sorts all pairs and writes the work lists; the shared expert's gate/up
+//       (bf16 MFMA, one weight read for every token tile) runs beside it;
+//   K2  persistent workgroups, one per CU, over the list of routed gate/up items (half-unit
+//       of <= 8 pairs x 128 rows of I), x rows staged per half-unit;
+//   K3  persistent workgroups over the shared down items (16-token tile x 128 rows) and the
+//       routed down items (unit of <= 16 pairs x 128 rows), h staged per unit; writes
+//       y_pairs and y_shared;
+//   K4  the combine (+ residual).
 // Every sum runs in a fixed order, so results do not depend on scheduling.  The ticket
-// counter lives in the workspace: zero before the first call, left zero by every call.
+// counters live in the workspace: zero before the first call, left zero by every call.
 //
 // Memory-level order.  A wave's vector loads retire in issue order, so waiting for one
 // load waits for every load issued before it.  The weight streams are therefore the only
@@ -34,13 +45,13 @@
 // read some valid row; their D rows are never used.
 // The routed h is kept as bf16 hi + bf16 lo (h - hi); in the down projection a pair takes
 // two adjacent A rows (hi, lo) of one MFMA, so ~16 bits of h cost no extra MFMA and the
-// pair's result is the sum of two D rows.  The shared h is kept the same way and enters
-// packed bf16 dot products.
+// pair's result is the sum of two D rows.  The shared h is kept the same way: up to kXT
+// tokens it enters packed bf16 dot products, beyond that the MFMA as the routed h does.
 // The kernels are instantiated per (H/256, I/256) so every loop over K has a fixed trip
-// count and a wave's loads are issued without branches.  Up to kXT tokens per unit (and
-// for the shared expert) activations come from LDS and the shared expert runs on the VALU
-// (a plain bf16 GEMV: 75 MB of weights at Hy4 shape); beyond that activations are read
-// from memory block by block and the shared expert uses the MFMA.
+// count and a wave's loads are issued without branches.  Up to kXT tokens every x row sits
+// in LDS and the shared expert runs on the VALU (a plain bf16 GEMV: 75 MB of weights at
+// Hy4 shape); beyond that the x rows of a half-unit and the h rows of a unit are staged
+// in LDS per work item and the shared expert uses the MFMA.
 #include "moe_device.h"
 
 #include <math.h>
@@ -955,10 +966,11 @@ __device__ __forceinline__ void shared_gateup_k1(const DecodeArgs& a, int rt, fl
 }
 
 // Beyond kXT tokens, first kernel: the shared expert's gate/up (workgroups n_router_wg ..)
-// beside the routing -- router partials (per 16-token tile), then a chain of two tickets, agent-scope acquire/release atomics on counters in the workspace:
-// the last router workgroup of a token tile sums that tile's partials and picks its tokens'
-// top-k (tiles in parallel); the last tile to finish sorts all pairs and writes the work
-// lists, then leaves every counter at zero for the next call.
+// beside the routing -- router partials (per 16-token tile), then a chain of two tickets
+// (agent-scope acquire/release atomics on counters in the workspace): the last router
+// workgroup of a token tile sums that tile's partials and picks its tokens' top-k (tiles in
+// parallel); the last tile to finish sorts all pairs and writes the work lists, then leaves
+// every counter at zero for the next call.
 template <int HB, int IB, int MT, int P0, int QN>
 __global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
   __shared__ __align__(16) float s_red[kNW][4][64];
@@ -1160,9 +1172,10 @@ __device__ __forceinline__ void shared_gateup_valu(const DecodeArgs& a, int sw, 
 
 // ============================================================================ large T
 // Beyond kXT tokens the routed projections run in persistent workgroups of 8 waves over a
-// list of work items (unit of <= 16 pairs, slice of 128 weight rows: 16 per wave); each
-// workgroup takes a contiguous range of the list, so its items mostly share a unit and
-// the list is split evenly whatever the routing.
+// list of work items (gate/up: half-unit of <= 8 pairs; down: unit of <= 16 pairs; each
+// with a slice of 128 weight rows, 16 per wave); each workgroup takes a contiguous range of
+// the list, so its items mostly share a (half-)unit and the list is split evenly whatever
+// the routing.
 constexpr int kLW = 512;
 constexpr int kLNW = kLW / 64;
 constexpr int kSlice = 16 * kLNW;
@@ -2255,7 +2268,7 @@ namespace {
 // Zero the workspace header (the work-list words with the router ticket): a kernel, not
 // hipMemsetAsync, so a captured call replays it as a kernel node.
 __global__ __launch_bounds__(64) void clear_words_kernel(uint32_t* p) {
-  if (threadIdx.x < 16) p[threadIdx.x] = 0u;   // work lists and the router ticket
+  if (threadIdx.x < 16) p[threadIdx.x] = 0u;   // work lists and the ticket counters
 }
 
 std::mutex g_scratch_mu;

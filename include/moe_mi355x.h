@@ -112,7 +112,7 @@ enum {
   MOE_CNT_RMSNORM = 12,
   MOE_CNT_DEQUANT = 13,
   MOE_CNT_BF16_GEMM = 14,      /* shared expert, prefill grouped GEMM path  */
-  MOE_CNT_DECODE_FUSED = 15,   /* moe_layer_decode (three fused kernels)    */
+  MOE_CNT_DECODE_FUSED = 15,   /* moe_layer_decode (fused kernels)          */
   MOE_CNT_STQ_GEMM = 16,       /* STQ1_0 prefill grouped GEMMs (fp16 MFMA)  */
   MOE_CNT_ROWSCALE = 17,       /* activation rows to fp16 / bf16 hi + lo    */
   MOE_CNT_MXFP8_SHARED = 18,   /* MXFP8 shared expert GEMMs (gate/up, down) */
@@ -272,9 +272,10 @@ MOE_MI355X_API moe_status moe_combine(const moe_dims* d, const float* y_pairs,
  * (1024, 512), (2048, 1024), (4096, 2048), (6144, 2048), (8192, 2048); MXFP4 routed
  * experts also T <= 4 and T k (I + I/32) <= 81920 (every pair's FP8 h fits the down
  * kernel's LDS).
- * Workspace: at least moe_layer_decode_workspace_size bytes.  It holds one atomic ticket
- * counter that MUST be zero before the first call on a given workspace (clear the buffer
- * once after allocating it); every call leaves it zero.  Calls sharing one workspace must
+ * Workspace: at least moe_layer_decode_workspace_size bytes.  It holds atomic ticket
+ * counters (used beyond 4 tokens: one per 16-token tile and one for the permutation) that
+ * MUST be zero before the first call on a given workspace (clear the buffer once after
+ * allocating it); every call leaves them zero.  Calls sharing one workspace must
  * not overlap in time.  Returns MOE_ERR_UNSUPPORTED outside the limits.
  * ------------------------------------------------------------------------- */
 MOE_MI355X_API moe_status moe_layer_decode_workspace_size(const moe_dims* d, int32_t has_shared,
@@ -285,7 +286,7 @@ MOE_MI355X_API moe_status moe_layer_decode_workspace_size(const moe_dims* d, int
  *           then UE8M0 scales [P][I/32], in sorted-pair order
  *   offs[8] shared h, bf16 hi [T][I] then lo [T][I]
  *   offs[9] MXFP4: x as E4M3 codes [T][H] then UE8M0 scales [T][H/32]
- *   offs[10] total bytes (offs[0..5]: work lists, ticket, router partials) */
+ *   offs[10] total bytes (offs[0..5]: work lists, ticket counters, router partials) */
 MOE_MI355X_API moe_status moe_layer_decode_workspace_offsets(const moe_dims* d, int32_t has_shared,
                                                              size_t* offs);
 MOE_MI355X_API moe_status moe_layer_decode(
@@ -302,7 +303,7 @@ MOE_MI355X_API moe_status moe_layer_decode(
  * arguments, limits and results as moe_layer_decode (bit for bit), plus: the workspace
  * moe_layer_decode_workspace_size reports for these dims must fit 8 MiB (at hidden 6144,
  * intermediate 2048, top-8 every T <= 64 does), else MOE_ERR_UNSUPPORTED.  Each call first
- * enqueues a small kernel that zeroes the scratch's ticket counter.  All calls on one device
+ * enqueues a small kernel that zeroes the scratch's ticket counters.  All calls on one device
  * share its array: calls that overlap in time on one device (other streams, other host
  * threads) race and give wrong results; serialise them. */
 MOE_MI355X_API moe_status moe_layer_decode_noalloc(
