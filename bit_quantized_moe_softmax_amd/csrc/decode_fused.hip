@@ -41,8 +41,11 @@
 // register i of the lane that decoded that row, so one STQ1_0 block scale per lane and
 // block applies to all four of its results.  K-slot -> K map inside a 256-weight block b at
 // MFMA step t: K = 256 b + 64 g + 8 t + s, i.e. a lane decodes groups 16g+2t and 16g+2t+1
-// from the 8 code bytes and 16 high bits it loads.  Token slots past a unit's last pair
-// read some valid row; their D rows are never used.
+// from the 8 code bytes and 16 high bits it loads.  Lanes whose token slot lies past a
+// unit's last pair skip their A reads (exec-masked LDS loads) and keep zeros: their D rows
+// are never used.  (At one token this removes 15/16 of the A-operand LDS traffic but did not
+// change the layer time: the gate/up stream is bound by its per-block dependency chain --
+// code word, table offsets, table reads, MFMAs -- not by LDS bandwidth.)
 // The routed h is kept as bf16 hi + bf16 lo (h - hi); in the down projection a pair takes
 // two adjacent A rows (hi, lo) of one MFMA, so ~16 bits of h cost no extra MFMA and the
 // pair's result is the sum of two D rows.  The shared h is kept the same way: up to kXT
@@ -165,28 +168,32 @@ __device__ __forceinline__ uint32_t bf16_lane(uint32_t p, int j) {
   return ((p >> i) & 1) ? 0xBF80u : 0x3F80u;
 }
 
-// 32-entry table: 5-bit STQ1_0 group pattern -> its four weights in {-1, 0, +1} as bf16
-// (8 bytes per entry: words 2p, 2p + 1).  Entries p and p + 16 share banks; splitting each
-// entry into two 4-byte tables (conflict-free ds_read2_b32) measured slower.
+// 32-entry table: 5-bit STQ1_0 group pattern p -> its four weights in {-1, 0, +1} as bf16,
+// 8 bytes per entry at byte 16 (p & 15) + 8 (p >> 4), i.e. words 4 (p & 15) + 2 (p >> 4)
+// and the next (the two patterns that share a nibble sit side by side, so a nibble times 16
+// and the high bit times 8 form the offset).  Splitting each entry into two 4-byte tables
+// (conflict-free ds_read2_b32) measured slower.
 __device__ __forceinline__ void build_lut(uint32_t* lut) {
   const int t = threadIdx.x;
   if (t < 32) {
-    lut[2 * t] = bf16_lane(t, 0) | (bf16_lane(t, 1) << 16);
-    lut[2 * t + 1] = bf16_lane(t, 2) | (bf16_lane(t, 3) << 16);
+    const int w = 4 * (t & 15) + 2 * (t >> 4);
+    lut[w] = bf16_lane(t, 0) | (bf16_lane(t, 1) << 16);
+    lut[w + 1] = bf16_lane(t, 2) | (bf16_lane(t, 3) << 16);
   }
 }
 
-// Table byte offsets (pattern x 8) of the 8 groups of one code word qw (4 bytes: group 2t
-// is the low nibble of byte t, group 2t + 1 the high nibble) with their high bits hb (bits
-// 2t and 2t + 1), four at a time: the nibbles x 8 by masks; the high bits moved to bit 7 of
-// their bytes by one multiply (bit 2i lands on bit 8i; the stray copies fall elsewhere and
-// are masked off).  About 3 VALU instructions per lookup instead of 5.
+// Table byte offsets of the 8 groups of one code word qw (4 bytes: group 2t is the low
+// nibble of byte t, group 2t + 1 the high nibble) with their high bits hb (bits 2t and
+// 2t + 1), four at a time: the nibbles x 16 by masks (the high nibbles are in place); the
+// high bits moved to bit 3 of their bytes by one 24-bit multiply (bit 2i lands on bit
+// 8i + 3; the stray products fall on bits that are masked off).  About 3 VALU instructions
+// per lookup, all at full rate.
 __device__ __forceinline__ void stq_word_offsets(uint32_t qw, uint32_t hb, uint32_t& alo, uint32_t& ahi) {
-  const uint32_t lo8 = (qw << 3) & 0x78787878u, hi8 = (qw >> 1) & 0x78787878u;
-  const uint32_t sl = __umul24(hb & 0x55u, 0x41041u) & 0x01010101u;
-  const uint32_t sh = __umul24((hb >> 1) & 0x55u, 0x41041u) & 0x01010101u;
-  alo = (sl << 7) | lo8;
-  ahi = (sh << 7) | hi8;
+  const uint32_t lo8 = (qw << 4) & 0xF0F0F0F0u, hi8 = qw & 0xF0F0F0F0u;
+  const uint32_t sl = __umul24(hb & 0x55u, 0x208208u) & 0x08080808u;
+  const uint32_t sh = __umul24((hb >> 1) & 0x55u, 0x208208u) & 0x08080808u;
+  alo = sl | lo8;
+  ahi = sh | hi8;
 }
 __device__ __forceinline__ uint2 lut_at(const uint32_t* lut, uint32_t off) {
   return *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(lut) + off);
@@ -309,10 +316,11 @@ struct StqStream {
   }
 
   // A operands from LDS: row base `a_lds` (bf16 elements, this lane's token slot and K-slots
-  // already applied), K stride 1.  Software-pipelined by half blocks: the table reads of
-  // half h + 1 are in flight while the 4 MFMAs of half h run, and the two halves of a block
-  // accumulate in separate registers (two 4-deep MFMA chains).
-  __device__ __forceinline__ f32x4_t run_lds(const uint32_t* lut, const uint16_t* a_lds) {
+  // already applied), K stride 1; lanes with a_on false read nothing and feed zeros.
+  // Software-pipelined by half blocks: the table reads of half h + 1 are in flight while the
+  // 4 MFMAs of half h run, and the two halves of a block accumulate in separate registers
+  // (two 4-deep MFMA chains).
+  __device__ __forceinline__ f32x4_t run_lds(const uint32_t* lut, const uint16_t* a_lds, bool a_on = true) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     uint2 qj;
     uint32_t qhj;
@@ -321,6 +329,7 @@ struct StqStream {
     bf16x8_t wn[4];
     stq_half_w(lut, qj, qhj, 0, wn);
     f32x4_t b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+    uint4 av[4] = {};
 #pragma unroll
     for (int hh = 0; hh < 2 * NB; ++hh) {
       const int j = hh >> 1, h = hh & 1;
@@ -334,9 +343,10 @@ struct StqStream {
         next(j + 1, qj, qhj, d);
         stq_half_w(lut, qj, qhj, 0, wn);
       }
-      uint4 av[4];
+      if (a_on) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * (4 * h + t));
+        for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * (4 * h + t));
+      }
       f32x4_t& bh = h ? b1 : b0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) bh = mfma16(as_bf16x8(av[t]), wc[t], bh);
@@ -433,7 +443,7 @@ struct StqStreamL {
   }
 
   // as StqStream::run_lds
-  __device__ __forceinline__ f32x4_t run_lds(const uint32_t* lut, const uint16_t* a_lds) {
+  __device__ __forceinline__ f32x4_t run_lds(const uint32_t* lut, const uint16_t* a_lds, bool a_on = true) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     uint2 qj;
     uint32_t qhj;
@@ -442,6 +452,7 @@ struct StqStreamL {
     bf16x8_t wn[4];
     stq_half_w(lut, qj, qhj, 0, wn);
     f32x4_t b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+    uint4 av[4] = {};
 #pragma unroll
     for (int hh = 0; hh < 2 * NB; ++hh) {
       const int j = hh >> 1, h = hh & 1;
@@ -455,9 +466,10 @@ struct StqStreamL {
         next(j + 1, qj, qhj, d);
         stq_half_w(lut, qj, qhj, 0, wn);
       }
-      uint4 av[4];
+      if (a_on) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * (4 * h + t));
+        for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const uint4*>(a_lds + 256 * j + 8 * (4 * h + t));
+      }
       f32x4_t& bh = h ? b1 : b0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) bh = mfma16(as_bf16x8(av[t]), wc[t], bh);
@@ -1239,13 +1251,16 @@ __device__ __forceinline__ void routed_gateup_large(const DecodeArgs& a, int e, 
   StqStreamL<HB> sg, su;
   sg.issue(a.gc + wrow * HB * 40, a.gs + (wrow + col) * HB, s_cw + (2 * wave) * StqStreamL<HB>::BYTES);
   su.issue(a.uc + wrow * HB * 40, a.us + (wrow + col) * HB, s_cw + (2 * wave + 1) * StqStreamL<HB>::BYTES);
-  const uint8_t* xa = s_x + (col < ntok ? col : 0) * XROW + 128 * g;   // this lane's A operand
+  const uint8_t* xa = s_x + col * XROW + 128 * g;   // this lane's A operand
+  const bool a_on = col < ntok;   // token slots past the half-unit keep zeros, no LDS reads
   f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
+  uint4 av[8] = {};
 #pragma unroll
   for (int j = 0; j < HB; ++j) {
-    uint4 av[8];
+    if (a_on) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) av[t] = *reinterpret_cast<const uint4*>(xa + 512 * j + 16 * t);
+      for (int t = 0; t < 8; ++t) av[t] = *reinterpret_cast<const uint4*>(xa + 512 * j + 16 * t);
+    }
     uint2 qg, qu;
     uint32_t hg, hu;
     float dg, du;
@@ -1663,7 +1678,7 @@ __device__ __forceinline__ void routed_gateup_small(const DecodeArgs& a, int wi,
   st.issue((mat ? a.uc : a.gc) + (wrow - col) * HB * 40, (mat ? a.us : a.gs) + wrow * HB,
            s_cw + wave * StqStreamL<HB>::BYTES);
   const int tok = R.utok[pos0 + (col < ntok ? col : ntok - 1)];
-  const f32x4_t acc = st.run_lds(s_lut, s_x + tok * H + 64 * g);
+  const f32x4_t acc = st.run_lds(s_lut, s_x + tok * H + 64 * g, col < ntok);
 #pragma unroll
   for (int i = 0; i < 4; ++i) s_red[tl][mat][i][lane] = acc[i];
   __syncthreads();
@@ -1806,7 +1821,7 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
         wt[m] = a.uw[hent.w + p];
       }
       const int pr = pos0 + (sp2 < nq ? sp2 : 0);
-      const f32x4_t acc = st.run_lds(s_lut, s_h + (col & 1) * (P * I + kLoPad) + pr * I + 64 * g);
+      const f32x4_t acc = st.run_lds(s_lut, s_h + (col & 1) * (P * I + kLoPad) + pr * I + 64 * g, sp2 < nq);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int p = 2 * g + m;
