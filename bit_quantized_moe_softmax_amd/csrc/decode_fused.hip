@@ -977,18 +977,26 @@ __device__ __forceinline__ void shared_gateup_k1(const DecodeArgs& a, int rt, fl
   }
 }
 
+template <int HB>
+__device__ __forceinline__ void quant_x8(const DecodeArgs& a, int i);
+
 // Beyond kXT tokens, first kernel: the shared expert's gate/up (workgroups n_router_wg ..)
-// beside the routing -- router partials (per 16-token tile), then a chain of two tickets
-// (agent-scope acquire/release atomics on counters in the workspace): the last router
-// workgroup of a token tile sums that tile's partials and picks its tokens' top-k (tiles in
-// parallel); the last tile to finish sorts all pairs and writes the work lists, then leaves
-// every counter at zero for the next call.
+// and, with MXFP4 routed experts, x -> E4M3 (the n_xq_wg workgroups after those) beside the
+// routing -- router partials (per 16-token tile), then a chain of two tickets (agent-scope
+// acquire/release atomics on counters in the workspace): the last router workgroup of a
+// token tile sums that tile's partials and picks its tokens' top-k (tiles in parallel); the
+// last tile to finish sorts all pairs and writes the work lists, then leaves every counter
+// at zero for the next call.
 template <int HB, int IB, int MT, int P0, int QN>
 __global__ __launch_bounds__(kWG) void k1_route(DecodeArgs a) {
   __shared__ __align__(16) float s_red[kNW][4][64];
   __shared__ int s_last;
   __shared__ FinalizeLds<P0> s_fin;
   const int b = blockIdx.x;
+  if (b >= a.n_router_wg + a.n_sgu_wg) {
+    quant_x8<HB>(a, (b - a.n_router_wg - a.n_sgu_wg) * kWG + (int)threadIdx.x);
+    return;
+  }
   if (b >= a.n_router_wg) {
     shared_gateup_k1<HB, IB, MT>(a, b - a.n_router_wg, reinterpret_cast<float(*)[2][4][64]>(s_fin.ids));
     return;
@@ -1892,18 +1900,23 @@ struct MxStream {
 #pragma unroll
     for (int j = 0; j < R; ++j) load(j, j);
   }
-  // sum over K of this lane's A row (E4M3 codes a_q, UE8M0 scales a_s, in LDS) times the tile
-  __device__ __forceinline__ f32x4_t run_lds(const uint8_t* a_q, const uint8_t* a_s) {
+  // sum over K of this lane's A row (E4M3 codes a_q, UE8M0 scales a_s, in LDS) times the tile;
+  // lanes with a_on false read nothing and feed zero codes (their D rows are unused)
+  __device__ __forceinline__ f32x4_t run_lds(const uint8_t* a_q, const uint8_t* a_s, bool a_on = true) {
     const int g = (threadIdx.x & 63) >> 4;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    uint4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
+    int asc = 0;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const uint4 w = q[j % R];
       const int bsc = (sw[j % R] >> (8 * g)) & 0xFF;
       if (j + R < NS) load(j + R, j % R);
-      const uint4 v0 = *reinterpret_cast<const uint4*>(a_q + 128 * j + 16 * g);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(a_q + 128 * j + 64 + 16 * g);
-      const int asc = a_s[4 * j + g];
+      if (a_on) {
+        v0 = *reinterpret_cast<const uint4*>(a_q + 128 * j + 16 * g);
+        v1 = *reinterpret_cast<const uint4*>(a_q + 128 * j + 64 + 16 * g);
+        asc = a_s[4 * j + g];
+      }
       const i32x8_t aop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                            (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
       const i32x8_t bop = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
@@ -1914,8 +1927,23 @@ struct MxStream {
   }
 };
 
+// x -> E4M3 with group-32 scales, 8 elements (index i of T H / 8) per lane; the four lanes of
+// a group meet by shuffles (T H / 8 is a multiple of 64, so waves past the end are whole).
+template <int HB>
+__device__ __forceinline__ void quant_x8(const DecodeArgs& a, int i) {
+  constexpr int H = HB * 256;
+  if (i >= a.T * H / 8) return;
+  const uint4 v = reinterpret_cast<const uint4*>(a.x)[i];
+  const uint32_t bits[8] = {v.x << 16, v.x & 0xFFFF0000u, v.y << 16, v.y & 0xFFFF0000u,
+                            v.z << 16, v.z & 0xFFFF0000u, v.w << 16, v.w & 0xFFFF0000u};
+  uint32_t codes[2];
+  const uint32_t sc = moe_mx_quant8(bits, codes);
+  reinterpret_cast<uint2*>(a.xq)[i] = make_uint2(codes[0], codes[1]);
+  if ((i & 3) == 0) a.xq[(size_t)a.T * H + i / 4] = (uint8_t)sc;
+}
+
 // K1 for MXFP4: the router partials, and in the workgroups past them x -> E4M3 with group-32
-// scales, 8 elements per lane (T H / 8 is a multiple of 64, so waves past the end are whole).
+// scales, 8 elements per lane.
 template <int HB, int IB, int XR>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k1s_router_mx(DecodeArgs a) {
   constexpr int H = HB * 256;
@@ -1930,15 +1958,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k
     shared_gateup_valu<HB, IB, XR, kWG>(a, b - a.n_router_wg - a.n_xq_wg, s_x);
     return;
   }
-  const int i = (b - a.n_router_wg) * kWG + (int)threadIdx.x;
-  if (i >= a.T * H / 8) return;
-  const uint4 v = reinterpret_cast<const uint4*>(a.x)[i];
-  const uint32_t bits[8] = {v.x << 16, v.x & 0xFFFF0000u, v.y << 16, v.y & 0xFFFF0000u,
-                            v.z << 16, v.z & 0xFFFF0000u, v.w << 16, v.w & 0xFFFF0000u};
-  uint32_t codes[2];
-  const uint32_t sc = moe_mx_quant8(bits, codes);
-  reinterpret_cast<uint2*>(a.xq)[i] = make_uint2(codes[0], codes[1]);
-  if ((i & 3) == 0) a.xq[(size_t)a.T * H + i / 4] = (uint8_t)sc;
+  quant_x8<HB>(a, (b - a.n_router_wg) * kWG + (int)threadIdx.x);
 }
 
 // Routed gate/up of one work item (unit, 32 rows of I): wave = (16-row tile, gate|up); the
@@ -2124,6 +2144,215 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine_mx(DecodeArgs a
   }
 }
 
+// ---------------------------------------------------------------------------- MXFP4, large T
+// Beyond kXT tokens with MXFP4 routed experts.  A unit's E4M3 x rows (<= 16; 6.2 KB each at
+// Hy4 shape) fit the LDS together, so the gate/up items are (unit, 64 rows of I): 8 waves =
+// 4 row tiles x (gate, up), every expert's gate/up weights read once per unit (no half-units).
+// The down items are (unit, 128 rows of H) on the unit's staged E4M3 h; the shared expert's
+// down items and the combine are the STQ1_0 path's.
+constexpr int kMxGuRows = 64;
+constexpr int kMxSharedItemWeight = 4;   // a bf16 shared down item against an MXFP4 one
+
+// E4M3 x rows of a unit in LDS: row s (pair s, token toks[s]) at byte s XR (XR = H + 16: the
+// 16 lanes of one operand read start in different banks), its scales at 16 XR + s SR (SR =
+// H / 32 + 16).  Rows past n read zeros; every load is issued before the first write.
+template <int HB>
+__device__ __forceinline__ void stage_xq_large(const DecodeArgs& a, const int* toks, int n, uint8_t* s_x) {
+  constexpr int H = HB * 256, XR = H + 16, SR = H / 32 + 16;
+  constexpr int PC = H / 16, PS = H / 32 / 16;   // 16-byte pieces of a code row, of a scale row
+  constexpr int NP = 16 * (PC + PS), PER = (NP + kLW - 1) / kLW;
+  const int tid = threadIdx.x;
+  const rsrc_t rx = make_rsrc(a.xq, (uint32_t)a.T * (H + H / 32));
+  uint4 v[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + kLW * m;
+    const bool code = idx < 16 * PC;
+    const int r = code ? idx / PC : (idx - 16 * PC) / PS;
+    const int pc = code ? idx % PC : (idx - 16 * PC) % PS;
+    const bool ok = idx < NP && r < n;
+    const uint32_t tok = ok ? (uint32_t)toks[r] : 0u;
+    const uint32_t o = code ? tok * H + 16u * pc : (uint32_t)a.T * H + tok * (H / 32) + 16u * pc;
+    v[m] = bload16(rx, ok ? o : kOOB);
+  }
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + kLW * m;
+    if (idx < NP) {
+      const bool code = idx < 16 * PC;
+      const int r = code ? idx / PC : (idx - 16 * PC) / PS;
+      const int pc = code ? idx % PC : (idx - 16 * PC) % PS;
+      *reinterpret_cast<uint4*>(s_x + (code ? r * XR : 16 * XR + r * SR) + 16 * pc) = v[m];
+    }
+  }
+}
+
+// One gate/up item: unit (expert e, first sorted position pos0, npairs) x rows 64 sl .. +63
+// of I.  Wave w streams row tile w / 2 of gate (w even) or up (w odd) against the staged x
+// rows; the waves meet in LDS, then threads (slot, column) form h = SiLU(gate) * up for the
+// item's 64 h-columns and quantise each slot's two 32-column groups.
+template <int HB, int IB, bool TILED>
+__device__ __forceinline__ void routed_gateup_mx_large(const DecodeArgs& a, int e, int pos0, int npairs, int sl,
+                                                       const uint8_t* s_x, float (*s_red)[2][4][64]) {
+  constexpr int H = HB * 256, I = IB * 256, XR = H + 16, SR = H / 32 + 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
+  const int tl = wave >> 1, mat = wave & 1;
+  const size_t eb = (size_t)I * (H / 2), es = (size_t)I * (H / 32);
+  MxStream<H / 128, TILED> st;
+  st.issue((mat ? a.uc : a.gc) + e * eb, reinterpret_cast<const uint8_t*>(mat ? a.us : a.gs) + e * es, I,
+           kMxGuRows * sl + 16 * tl);
+  const f32x4_t acc = st.run_lds(s_x + col * XR, s_x + 16 * XR + col * SR, col < npairs);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_red[tl][mat][i][lane] = acc[i];
+  __syncthreads();
+  const int slot = threadIdx.x >> 5, c = threadIdx.x & 31;   // 16 slots x 32 columns
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    // h-column 64 sl + 32 q + c of token slot `slot`: D(4 g + i, r) of tile t2 is register i
+    // of lane 16 g + r
+    const int cc = 32 * q + c, t2 = cc >> 4, L = 16 * (slot >> 2) + (cc & 15), i = slot & 3;
+    const float h = silu_mul(s_red[t2][0][i][L], s_red[t2][1][i][L]);
+    uint32_t am = __float_as_uint(h) & 0x7FFFFFFFu;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o, 64));
+    if (slot < npairs) {
+      const size_t pos = pos0 + slot;
+      uint32_t code = 0, sc = 0;
+      if (am != 0) {
+        const int X = moe_mx_exp(am);
+        code = moe_e4m3_code(h, X);
+        sc = (uint32_t)(X + 127);
+      }
+      a.hq[pos * I + kMxGuRows * sl + cc] = (uint8_t)code;
+      if (c == 0) a.hq[(size_t)a.T * a.k * I + pos * (I / 32) + 2 * sl + q] = (uint8_t)sc;
+    }
+  }
+  __syncthreads();   // s_red is reused by the next item
+}
+
+// Large T, MXFP4, second kernel: persistent workgroups over contiguous ranges of the gate/up
+// items; x is restaged when the unit changes.
+template <int HB, int IB, bool TILED>
+__global__ __launch_bounds__(kLW) void k2l_gateup_mx(DecodeArgs a) {
+  constexpr int I = IB * 256, NS = I / kMxGuRows;
+  static_assert(I % kMxGuRows == 0, "slices");
+  __shared__ __align__(16) float s_red[4][2][4][64];
+  extern __shared__ __align__(16) uint8_t s_xm[];   // 16 E4M3 x rows, then their scales
+  int i0, i1;
+  light_range(blockIdx.x, gridDim.x, a.wl[1] * NS, 0, 1, 1, i0, i1);
+  int staged = -1;
+  int4 un = make_int4(0, 0, 0, 0);
+  for (int i = i0; i < i1; ++i) {
+    const int u = i / NS;
+    if (u != staged) {
+      un = a.ut[u];
+      __syncthreads();   // every wave is done with the previous rows
+      stage_xq_large<HB>(a, a.utok + 16 * u, un.z, s_xm);
+      __syncthreads();
+      staged = u;
+    }
+    routed_gateup_mx_large<HB, IB, TILED>(a, un.x, un.y, un.z, i % NS, s_xm, s_red);
+  }
+}
+
+// E4M3 h rows of a unit in LDS: pair s's codes at byte s HR (HR = I + 16), its scales at
+// 16 HR + s HS (HS = I / 32 + 16); rows past n read zeros.
+template <int IB>
+__device__ __forceinline__ void stage_hq_large(const DecodeArgs& a, int first, int n, uint8_t* s_h) {
+  constexpr int I = IB * 256, HR = I + 16, HS = I / 32 + 16;
+  constexpr int PC = I / 16, PS = (I / 32 + 15) / 16;
+  constexpr int NP = 16 * (PC + PS), PER = (NP + kLW - 1) / kLW;
+  const int tid = threadIdx.x;
+  const uint32_t P = (uint32_t)a.T * a.k;
+  const rsrc_t rh = make_rsrc(a.hq, P * (I + I / 32));
+  uint4 v[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + kLW * m;
+    const bool code = idx < 16 * PC;
+    const int r = code ? idx / PC : (idx - 16 * PC) / PS;
+    const int pc = code ? idx % PC : (idx - 16 * PC) % PS;
+    const bool ok = idx < NP && r < n;
+    const uint32_t pos = (uint32_t)(first + r);
+    const uint32_t o = code ? pos * I + 16u * pc : P * I + pos * (I / 32) + 16u * pc;
+    v[m] = bload16(rh, ok ? o : kOOB);
+  }
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + kLW * m;
+    if (idx < NP) {
+      const bool code = idx < 16 * PC;
+      const int r = code ? idx / PC : (idx - 16 * PC) / PS;
+      const int pc = code ? idx % PC : (idx - 16 * PC) % PS;
+      *reinterpret_cast<uint4*>(s_h + (code ? r * HR : 16 * HR + r * HS) + 16 * pc) = v[m];
+    }
+  }
+}
+
+// Large T, MXFP4, third kernel: as k3l_down (the shared expert's down items dealt round-robin
+// first, then contiguous ranges of routed items) with MXFP4 routed down items: unit x rows
+// slice * 128 + 16 w .. + 15 of H per wave, the next item's first K steps in flight while an
+// item runs.
+template <int HB, int IB, bool TILED>
+__global__ __launch_bounds__(kLW) void k3l_down_mx(DecodeArgs a) {
+  constexpr int H = HB * 256, I = IB * 256, NS = H / kSlice, HR = I + 16, HS = I / 32 + 16;
+  static_assert(H % kSlice == 0, "slices");
+  extern __shared__ __align__(16) uint8_t s_h[];   // shared tiles: 32 bf16 A rows; routed: E4M3 h
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
+  const int T = a.T;
+  const int n_sh = a.sd ? ((T + 15) / 16) * NS : 0;
+  const int n_units = a.wl[1];
+  int i0, i1;
+  light_range(blockIdx.x, gridDim.x, n_units * NS, n_sh, 1, kMxSharedItemWeight, i0, i1);
+  if (n_sh) {
+    const rsrc_t rhs = make_rsrc(a.hs, (uint32_t)T * I * 4);
+    int staged = -1;
+    for (int si = blockIdx.x; si < n_sh; si += gridDim.x) {
+      const int tt = si / NS;
+      if (tt != staged) {
+        __syncthreads();   // every wave is done with the previous tile
+        stage_h_large<IB>(rhs, (uint32_t)T * I * 2, 16 * tt, min(16, T - 16 * tt), s_h);
+        __syncthreads();
+        staged = tt;
+      }
+      shared_down_item<HB, IB>(a, tt, si % NS, s_h);
+    }
+  }
+  int i = i0;
+  if (i >= i1) return;
+  const size_t eb = (size_t)H * (I / 2), es = (size_t)H * (I / 32);
+  const uint8_t* dsc = reinterpret_cast<const uint8_t*>(a.ds);
+  int u = -1;
+  int4 un = make_int4(0, 0, 0, 0);
+  MxStream<I / 128, TILED> st;
+  {
+    const int4 u0 = a.ut[i / NS];
+    st.issue(a.dc + u0.x * eb, dsc + u0.x * es, H, (i % NS) * kSlice + 16 * wave);
+  }
+  for (; i < i1; ++i) {
+    if (i / NS != u) {   // the next unit of the range
+      u = i / NS;
+      un = a.ut[u];
+      __syncthreads();
+      stage_hq_large<IB>(a, un.y, un.z, s_h);
+      __syncthreads();
+    }
+    MxStream<I / 128, TILED> nx = st;
+    if (i + 1 < i1) {
+      const int4 un2 = (i + 1) / NS == u ? un : a.ut[(i + 1) / NS];
+      nx.issue(a.dc + un2.x * eb, dsc + un2.x * es, H, ((i + 1) % NS) * kSlice + 16 * wave);
+    }
+    const f32x4_t acc = st.run_lds(s_h + col * HR, s_h + 16 * HR + col * HS, col < un.z);
+    const int r16 = (i % NS) * kSlice + 16 * wave;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = 4 * g + j;
+      if (p < un.z) a.y_pairs[(size_t)(un.y + p) * H + r16 + col] = acc[j];
+    }
+    st = nx;
+  }
+}
+
 // Compute units of the current device (persistent grids: one workgroup per CU).
 int device_cus() {
   static int cus[kMaxDevices] = {};
@@ -2171,12 +2400,48 @@ hipError_t launch_small_mx(DecodeArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
+// Large T, MXFP4: (1) router + routing (tickets) beside the shared gate/up and x -> E4M3;
+// (2) routed gate/up items (h -> E4M3); (3) shared and routed down items; (4) combine.
+template <int HB, int IB, bool TILED>
+hipError_t launch_large_mx(DecodeArgs& a, hipStream_t s) {
+  constexpr int H = HB * 256, I = IB * 256;
+  const int T = a.T;
+  const int n_tt = (T + 15) / 16;
+  a.n_router_wg = ((a.E + 15) / 16) * kRouterParts * n_tt;
+  a.n_sgu_wg = a.sg ? I / 16 : 0;
+  a.n_xq_wg = (T * H / 8 + kWG - 1) / kWG;
+  a.h_lds = 0;
+  a.ysh_ready = 0;
+  const int cus = device_cus();
+  const size_t lds2 = (size_t)16 * (H + 16) + (size_t)16 * (H / 32 + 16);
+  size_t lds3 = (size_t)16 * (I + 16) + (size_t)16 * (I / 32 + 16);
+  if (a.sd && (size_t)32 * (2 * I + 16) > lds3) lds3 = (size_t)32 * (2 * I + 16);
+  const bool prof = moe_prof_on();
+  if (prof) moe_prof_begin(MOE_PROF_DECODE_K1, s);
+  const dim3 g1(a.n_router_wg + a.n_sgu_wg + a.n_xq_wg);
+  if (n_tt == 1) hipLaunchKernelGGL((k1_route<HB, IB, 1, kMaxT * 32, 8>), g1, dim3(kWG), 0, s, a);
+  else if (n_tt == 2) hipLaunchKernelGGL((k1_route<HB, IB, 2, kMaxT * 32, 8>), g1, dim3(kWG), 0, s, a);
+  else hipLaunchKernelGGL((k1_route<HB, IB, kMaxT / 16, kMaxT * 32, 8>), g1, dim3(kWG), 0, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K1, s); moe_prof_begin(MOE_PROF_DECODE_K2, s); }
+  hipLaunchKernelGGL((k2l_gateup_mx<HB, IB, TILED>), dim3(cus), dim3(kLW), lds2, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K2, s); moe_prof_begin(MOE_PROF_DECODE_K3, s); }
+  hipLaunchKernelGGL((k3l_down_mx<HB, IB, TILED>), dim3(cus), dim3(kLW), lds3, s, a);
+  MOE_HIP_TRY(hipGetLastError());
+  if (prof) { moe_prof_end(MOE_PROF_DECODE_K3, s); moe_prof_begin(MOE_PROF_DECODE_K4, s); }
+  MOE_HIP_TRY(moe_launch_combine(a.y_pairs, a.w, a.pair_pos, a.y_shared, a.residual, a.out, a.out_bf16,
+                                 T, H, a.k, s));
+  if (prof) moe_prof_end(MOE_PROF_DECODE_K4, s);
+  return hipSuccess;
+}
+
 template <int HB, int IB, bool TILED>
 hipError_t launch_shape_mx(DecodeArgs& a, hipStream_t s) {
   if (a.T == 1) return launch_small_mx<HB, IB, 1, TILED>(a, s);
   if (a.T == 2) return launch_small_mx<HB, IB, 2, TILED>(a, s);
   if (a.T <= kXT) return launch_small_mx<HB, IB, kXT, TILED>(a, s);
-  return hipErrorInvalidValue;
+  return launch_large_mx<HB, IB, TILED>(a, s);
 }
 
 // Small T, split by what each piece waits for: (1) router partials + shared gate/up (x
@@ -2317,11 +2582,12 @@ bool moe_decode_shape_ok(int H, int I, int E) {
          (hb == 16 && ib == 8) || (hb == 24 && ib == 8) || (hb == 32 && ib == 8);
 }
 
-// MXFP4 routed experts: up to kXT tokens, every pair's E4M3 h (codes and scales) fits the
-// down kernel's LDS staging.
+// MXFP4 routed experts: up to kXT tokens every pair's E4M3 h (codes and scales) must fit the
+// down kernel's LDS staging; beyond, up to kMaxT tokens, h is staged per unit.
 bool moe_decode_mx_ok(int T, int I, int k) {
   const long P = (long)T * k;
-  return T <= kXT && (P * (I + I / 32) + 15) / 16 <= 10L * 64 * kDnWaves;
+  if (T > kXT) return T <= kMaxT;
+  return (P * (I + I / 32) + 15) / 16 <= 10L * 64 * kDnWaves;
 }
 
 size_t moe_decode_ws_layout(int T, int H, int I, int E, int k, int has_shared, size_t* offs) {

@@ -270,8 +270,8 @@ MOE_MI355X_API moe_status moe_combine(const moe_dims* d, const float* y_pairs,
  * calls).
  * Limits: T <= 64, k <= 32, E <= 256, and (H, I) one of the compiled shapes (512, 256),
  * (1024, 512), (2048, 1024), (4096, 2048), (6144, 2048), (8192, 2048); MXFP4 routed
- * experts also T <= 4 and T k (I + I/32) <= 81920 (every pair's FP8 h fits the down
- * kernel's LDS).
+ * experts at T <= 4 also T k (I + I/32) <= 81920 (every pair's FP8 h fits the small-batch
+ * down kernel's LDS; beyond 4 tokens h is staged per unit of <= 16 pairs).
  * Workspace: at least moe_layer_decode_workspace_size bytes.  It holds atomic ticket
  * counters (used beyond 4 tokens: one per 16-token tile and one for the permutation) that
  * MUST be zero before the first call on a given workspace (clear the buffer once after

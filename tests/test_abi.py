@@ -153,13 +153,14 @@ def test_new_entry_point_checks_need_no_gpu():
     sh8 = M.Experts(M.MOE_W_MXFP8, (F, None), (F, F), (F, F))
     assert _raw("moe_expert_ffn", d.ref(), routed.ref(), sh8.ref(), F, F, F, F, F, F,
                 ctypes.c_size_t(1 << 30), None) == 1
-    # the fused decode takes only a bf16 shared expert, and MXFP4 routed experts up to 4 tokens
+    # the fused decode takes only a bf16 shared expert, and MXFP4 routed experts up to 64 tokens
+    # (up to 4 only while every pair's FP8 h fits the small-batch down kernel)
     sh8 = M.Experts(M.MOE_W_MXFP8, (F, F), (F, F), (F, F))
     args = (F,) * 11 + (None, F, None, F, ctypes.c_size_t(1 << 30), None)
     assert _raw("moe_layer_decode", d.ref(), routed.ref(), sh8.ref(), *args) == 2
     mx = M.Experts(M.MOE_W_MXFP4_TILED, (F, F), (F, F), (F, F))
-    d5 = M.Dims(T=5, H=512, I=256, E=8, k=2)
-    assert _raw("moe_layer_decode", d5.ref(), mx.ref(), None, *args) == 2
+    d65 = M.Dims(T=65, H=512, I=256, E=8, k=2)
+    assert _raw("moe_layer_decode", d65.ref(), mx.ref(), None, *args) == 2
     d4 = M.Dims(T=4, H=6144, I=2048, E=256, k=32)                   # FP8 h of 128 pairs: too big
     assert _raw("moe_layer_decode", d4.ref(), mx.ref(), None, *args) == 2
     # a routed format that is no routed format at all is an invalid argument, in both calls

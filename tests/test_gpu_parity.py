@@ -781,6 +781,11 @@ MX_FUSED = {
     "h512-i256-e4-top4-t2-noshared": synth.LayerCfg("t", 2, 512, 256, 4, 4, False, "mxfp4", False, False, 1, 44),
     # one pair: the staged h run (264 bytes) is not a whole number of 16-byte pieces
     "h512-i256-e8-top1-t1-noshared": synth.LayerCfg("t", 1, 512, 256, 8, 1, False, "mxfp4", False, False, 1, 45),
+    # beyond four tokens: the item-list kernels (one token tile; two with Zipf routing and
+    # experts over 16 pairs, split into several units; three tiles, every expert in 10 units)
+    "h512-i256-e16-top4-t9-shared": synth.LayerCfg("t", 9, 512, 256, 16, 4, True, "mxfp4", False, False, 1, 47),
+    "h1024-i512-e32-top8-t17-zipf": synth.LayerCfg("t", 17, 1024, 512, 32, 8, True, "mxfp4", True, False, 1, 48),
+    "h512-i256-e8-top2-t40-noshared": synth.LayerCfg("t", 40, 512, 256, 8, 2, False, "mxfp4", False, False, 1, 49),
 }
 
 
@@ -846,6 +851,22 @@ def test_fused_decode_mx_hy4_t1():
     inp = layer_inputs(c)
     o = run_fused(c, inp, tiled=True)
     _fused_mx_check(c, inp, o, None, experts=sorted(set(host(o["ids"]).ravel().tolist())))
+
+
+def test_fused_decode_mx_hy4_t64_zipf():
+    """Hy4 shape, 64 tokens with Zipf(1.1) routing, MXFP4 (tiled) routed experts and the bf16
+    shared expert: routing, permutation and x codes in full; h codes and the down stage on the
+    experts with the most and the fewest pairs plus one more; shared expert and combine in full."""
+    c = synth.LayerCfg("hy4-mxfp4-decode-t64-zipf", 64, 6144, 2048, 256, 8, True, "mxfp4", True, False, 1, 50)
+    say("fused decode mx hy4 t64 generate")
+    inp = layer_inputs(c)
+    o = run_fused(c, inp, tiled=True)
+    ids = host(o["ids"]).ravel()
+    cnt = np.bincount(ids, minlength=c.E)
+    used = np.flatnonzero(cnt)
+    pick = sorted({int(used[np.argmax(cnt[used])]), int(used[np.argmin(cnt[used])]), int(used[len(used) // 2])})
+    say("fused decode mx hy4 t64 experts", pick, "pairs", cnt[pick].tolist())
+    _fused_mx_check(c, inp, o, None, experts=pick)
 
 
 def test_fused_decode_cfg1_hy4():
