@@ -549,6 +549,113 @@ def decode_t64_bench(args):
     return dict(c=c, ms=ms, U=u_avg, unique_b=unique_b, step_b=step_b, prof=prof, kbytes=kb)
 
 
+def gpu_mx_layer(c, seed):
+    """One Hy4 layer with MXFP4 routed experts in the tiled layout, generated on the GPU from a
+    seeded torch generator with the synthetic workloads' distributions: uniform E2M1 code bytes,
+    UE8M0 scale bytes uniform over 127 + {-8 .. -4}, bf16 N(0, 0.02) router and shared expert."""
+    import torch
+    import bit_quantized_moe_softmax_amd as M
+    from bit_quantized_moe_softmax_amd.layer import bf16_experts
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    fam = []
+    for rows, K in ((c.I, c.H), (c.I, c.H), (c.H, c.I)):
+        codes = torch.randint(0, 256, (c.E * rows, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+        scales = torch.randint(119, 124, (c.E * rows, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+        tc, ts = torch.empty_like(codes), torch.empty_like(scales)
+        M.moe_mxfp4_pack_tiles(codes, scales, c.E * rows, K, tc, ts)
+        torch.cuda.synchronize()
+        del codes, scales
+        fam.append((tc, ts))
+
+    def bf16(shape):
+        return (torch.randn(shape, device="cuda", generator=g) * 0.02).bfloat16().view(torch.int16)
+
+    return dict(routed=M.Experts(M.MOE_W_MXFP4_TILED, *fam),
+                shared=bf16_experts(bf16((c.I, c.H)), bf16((c.I, c.H)), bf16((c.H, c.I))),
+                wr=bf16((c.E, c.H)))
+
+
+def mx_decode_t64_bench(args):
+    """64-token decode with Zipf(1.1) routing and MXFP4 (tiled) routed experts: the fused
+    moe_layer_decode over 3 GPU-generated layer copies (about 2 GB of unique experts per step),
+    and the same steps through the four separate calls (route, permute, expert FFN on the
+    grouped GEMMs, combine) for comparison."""
+    import numpy as np
+    import torch
+    import synth
+    import bit_quantized_moe_softmax_amd as M
+    c = synth.cfg(2)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    copies = [gpu_mx_layer(c, 5000 + i) for i in range(3)]
+    xs = [dev(synth.activations(c.seed, 1 + i, c.T, c.H)) for i in range(2)]
+    bias = dev(synth.zipf_bias(c.seed, 0, c.E))
+    b = decode_bufs(d, c)
+    out = torch.empty((c.T, c.H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    U = {}
+    for i in range(len(copies)):
+        for j in range(len(xs)):
+            decode_call(M, d, copies[i], xs[j], bias, b, None, out, s)
+            torch.cuda.synchronize()
+            U[(i, j)] = len(np.unique(b["ids"].cpu().numpy()))
+
+    def step(i):
+        decode_call(M, d, copies[i % 3], xs[(i // 3) % 2], bias, b, None, out, s)
+
+    def timed(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for i in range(n):
+            fn(i)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms = timed(step, args.steps)
+    M.moe_profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = M.moe_profile_read()
+    M.moe_profile_enable(False)
+    # the four separate calls on the same inputs
+    ws4 = torch.zeros(M.moe_workspace_size(d, M.MOE_W_MXFP4_TILED, True), dtype=torch.uint8, device="cuda")
+
+    def step4(i):
+        L, x = copies[i % 3], xs[(i // 3) % 2]
+        M.moe_route(d, x, L["wr"], bias, None, b["logits"], b["ids"], b["w"], s)
+        M.moe_permute(d, b["ids"], b["sp"], b["off"], b["pp"], s)
+        M.moe_expert_ffn(d, L["routed"], L["shared"], x, b["sp"], b["off"], b["yp"], b["ysh"], ws4, s)
+        M.moe_combine(d, b["yp"], b["w"], b["pp"], b["ysh"], None, out, None, s)
+
+    n4 = max(3, args.steps // 4)
+    for i in range(3):
+        step4(i)
+    torch.cuda.synchronize()
+    ms4 = timed(step4, n4)
+    u_avg = float(np.mean([U[(i % 3, (i // 3) % 2)] for i in range(args.steps)]))
+    P = d.P
+    xq_b = c.T * (c.H + c.H // 32)
+    hq_b = P * (c.I + c.I // 32)
+    shared_b = 3 * c.I * c.H * 2
+    router_b = c.E * c.H * 2
+    unique_b = u_avg * 3 * MX_MAT_BYTES
+    step_b = unique_b + shared_b + router_b + c.T * c.H * 2 + c.T * c.H * 4 + P * c.H * 4 + c.T * c.H * 4
+    kb = {"decode_k1_route": router_b + c.T * c.H * 2 + c.T * c.E * 4 + 2 * c.I * c.H * 2 + c.T * c.I * 4 + xq_b,
+          "decode_k2_gateup": u_avg * 2 * MX_MAT_BYTES + xq_b + hq_b,
+          "decode_k3_down_combine": u_avg * MX_MAT_BYTES + c.I * c.H * 2 + c.T * c.I * 4 + hq_b
+                                    + P * c.H * 4 + c.T * c.H * 4,
+          "decode_k4_combine": P * c.H * 4 + 2 * c.T * c.H * 4}
+    del copies
+    torch.cuda.empty_cache()
+    return dict(c=c, ms=ms, ms4=ms4, U=u_avg, unique_b=unique_b, step_b=step_b, prof=prof, kbytes=kb)
+
+
 def chain_bench(args):
     """The 29-layer STQ1_0 stack at 16 tokens (about 46 GB of packed experts resident):
     a step runs, for every layer, RMSNorm (bf16 out) and the fused moe_layer_decode with the
@@ -622,7 +729,8 @@ TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     # the 64-token decode (its K2 / K3 kernels are also the 16-token chain's: byte-counter runs
     # pass --no-chain so that only the 64-token dispatches are averaged)
     "t64_decode_k1_route": "k1_route<24, 8, 4,", "t64_decode_k2_gateup": "k2l_gateup<24, 8>",
-    "t64_decode_k3_down_combine": "k3l_down<24, 8>", "copy": "neg_kernel"}
+    "t64_decode_k3_down_combine": "k3l_down<24, 8>", "mx64_decode_k2_gateup": "k2l_gateup_mx<24, 8, true>",
+    "mx64_decode_k3_down_combine": "k3l_down_mx<24, 8, true>", "copy": "neg_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hy4_layer_hbm_traffic_per_kernel.md")
 _DEC_SRC = "bit_quantized_moe_softmax_amd/csrc/decode_fused.hip"
 _MX_SRC = "bit_quantized_moe_softmax_amd/csrc/mx_gemm.hip"
@@ -631,7 +739,8 @@ TRAFFIC_SOURCES = {"decode_k1_route": _DEC_SRC, "decode_k2_gateup": _DEC_SRC,
                    "decode_k3_down_combine": _DEC_SRC, "mx_gateup": _MX_SRC, "mx_down": _MX_SRC,
                    "stq_gateup": _G16_SRC, "stq_down": _G16_SRC, "mxdec_k2_gateup": _DEC_SRC,
                    "mxdec_k3_down_combine": _DEC_SRC, "t64_decode_k1_route": _DEC_SRC,
-                   "t64_decode_k2_gateup": _DEC_SRC, "t64_decode_k3_down_combine": _DEC_SRC}
+                   "t64_decode_k2_gateup": _DEC_SRC, "t64_decode_k3_down_combine": _DEC_SRC,
+                   "mx64_decode_k2_gateup": _DEC_SRC, "mx64_decode_k3_down_combine": _DEC_SRC}
 
 
 def source_hash(slot):
@@ -1004,6 +1113,30 @@ def main():
                              "traffic": traffic.get("t64_" + dom), "algorithmic_bytes": kern[dom]["algorithmic_bytes"]}}
         except Exception as e:
             out["decode_t64_zipf"] = {"error": repr(e)}
+    if not args.no_extra:
+        try:
+            m64 = mx_decode_t64_bench(args)
+            kern = {}
+            for name, nbytes in m64["kbytes"].items():
+                us, n = m64["prof"][name]
+                if n == 0:
+                    continue
+                kern[name] = {"avg_us": round(us, 3), "launches": n, "algorithmic_bytes": round(nbytes),
+                              "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None}
+            dom = max(kern, key=lambda k: kern[k]["avg_us"])
+            gbs = m64["step_b"] / (m64["ms"] * 1e-3) / 1e9
+            out["mxfp4_decode_t64_zipf"] = {
+                "workload": "hy4-mxfp4xfp8-decode-t64-zipf1.1", "entry_point": "moe_layer_decode",
+                "us_per_step": round(m64["ms"] * 1e3, 2), "unique_experts": round(m64["U"], 2),
+                "unique_expert_bytes": round(m64["unique_b"]), "step_bytes": round(m64["step_b"]),
+                "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "four_call_us_per_step": round(m64["ms4"] * 1e3, 2),
+                "kernels": kern,
+                "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["gbs"], "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round((kern[dom]["gbs"] or 0) / HBM_PEAK_GBS, 4),
+                             "traffic": traffic.get("mx64_" + dom), "algorithmic_bytes": kern[dom]["algorithmic_bytes"]}}
+        except Exception as e:
+            out["mxfp4_decode_t64_zipf"] = {"error": repr(e)}
     if not args.no_extra and not args.no_chain:
         try:
             ch = chain_bench(args)
