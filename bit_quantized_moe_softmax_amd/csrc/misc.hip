@@ -41,6 +41,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }
 
 // ---------------------------------------------------------------- RMSNorm + bf16 cast
+// One workgroup per row.  Rows of up to 8192 floats (H % 4 == 0): every thread loads its M
+// float4 pieces (piece tid + 256 m) at once, keeps them in registers for the scaling, and the
+// row is read once; other rows take the strided loop.
+template <int M>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ r,
                                                       uint16_t* __restrict__ a, int H,
                                                       float eps) {
@@ -48,14 +52,40 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const int t = blockIdx.x;
   const float* row = r + (size_t)t * H;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += 256) ss = fmaf(row[i], row[i], ss);
+  float4 v[M > 0 ? M : 1];
+  if constexpr (M > 0) {
+    const int n4 = H / 4;
+    const float4* row4 = reinterpret_cast<const float4*>(row);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int i = threadIdx.x + 256 * m;
+      v[m] = i < n4 ? row4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      ss = fmaf(v[m].x, v[m].x, fmaf(v[m].y, v[m].y, fmaf(v[m].z, v[m].z, fmaf(v[m].w, v[m].w, ss))));
+  } else {
+    for (int i = threadIdx.x; i < H; i += 256) ss = fmaf(row[i], row[i], ss);
+  }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int i = threadIdx.x; i < H; i += 256)
-    a[(size_t)t * H + i] = (uint16_t)f32_to_bf16_rne(row[i] * inv);
+  if constexpr (M > 0) {
+    const int n4 = H / 4;
+    uint2* a4 = reinterpret_cast<uint2*>(a + (size_t)t * H);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int i = threadIdx.x + 256 * m;
+      if (i < n4)
+        a4[i] = make_uint2(f32_to_bf16_rne(v[m].x * inv) | (f32_to_bf16_rne(v[m].y * inv) << 16),
+                           f32_to_bf16_rne(v[m].z * inv) | (f32_to_bf16_rne(v[m].w * inv) << 16));
+    }
+  } else {
+    for (int i = threadIdx.x; i < H; i += 256)
+      a[(size_t)t * H + i] = (uint16_t)f32_to_bf16_rne(row[i] * inv);
+  }
 }
 
 // ---------------------------------------------------------------- STQ1_0 pack / decode
@@ -310,7 +340,14 @@ hipError_t moe_launch_combine(const float* y_pairs, const float* w, const int32_
 
 hipError_t moe_launch_rmsnorm(const float* r, uint16_t* a, int T, int H, float eps,
                               hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, s, r, a, H, eps);
+  const bool vec = H % 4 == 0 && H <= 8192 && reinterpret_cast<uintptr_t>(r) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a) % 8 == 0;
+  const int m = vec ? (H / 4 + 255) / 256 : 0;
+  if (m == 0) hipLaunchKernelGGL(rmsnorm_kernel<0>, dim3(T), dim3(256), 0, s, r, a, H, eps);
+  else if (m <= 2) hipLaunchKernelGGL(rmsnorm_kernel<2>, dim3(T), dim3(256), 0, s, r, a, H, eps);
+  else if (m <= 4) hipLaunchKernelGGL(rmsnorm_kernel<4>, dim3(T), dim3(256), 0, s, r, a, H, eps);
+  else if (m <= 6) hipLaunchKernelGGL(rmsnorm_kernel<6>, dim3(T), dim3(256), 0, s, r, a, H, eps);
+  else hipLaunchKernelGGL(rmsnorm_kernel<8>, dim3(T), dim3(256), 0, s, r, a, H, eps);
   return hipGetLastError();
 }
 
