@@ -46,9 +46,9 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the STQ1_0 prefill and MXFP4 decode lines")
-    p.add_argument("--no-chain", action="store_true",
-                   help="skip the 29-layer chain line (byte-counter runs: its kernels share names "
-                        "with the 64-token decode's)")
+    p.add_argument("--counter-run", action="store_true",
+                   help="byte-counter runs: skip the work whose kernels share names with another "
+                        "line's (the 29-layer chain, the MXFP4 64-token line's four-call comparison)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first run a plain copy kernel (torch.neg) over this many MiB, three times, "
                         "as the reference dispatch for the HBM byte counters")
@@ -633,11 +633,13 @@ def mx_decode_t64_bench(args):
         M.moe_expert_ffn(d, L["routed"], L["shared"], x, b["sp"], b["off"], b["yp"], b["ysh"], ws4, s)
         M.moe_combine(d, b["yp"], b["w"], b["pp"], b["ysh"], None, out, None, s)
 
-    n4 = max(3, args.steps // 4)
-    for i in range(3):
-        step4(i)
-    torch.cuda.synchronize()
-    ms4 = timed(step4, n4)
+    ms4 = float("nan")
+    if not getattr(args, "counter_run", False):
+        n4 = max(3, args.steps // 4)
+        for i in range(3):
+            step4(i)
+        torch.cuda.synchronize()
+        ms4 = timed(step4, n4)
     u_avg = float(np.mean([U[(i % 3, (i // 3) % 2)] for i in range(args.steps)]))
     P = d.P
     xq_b = c.T * (c.H + c.H // 32)
@@ -726,8 +728,8 @@ TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     "mx_down": "mx_gemm_kernel<false, true>", "stq_gateup": "g16_kernel<0, true, 1>",
     "stq_down": "g16_kernel<0, false, 2>", "mxdec_k2_gateup": "k2s_gateup_mx<",
     "mxdec_k3_down_combine": "k3_down_combine_mx<",
-    # the 64-token decode (its K2 / K3 kernels are also the 16-token chain's: byte-counter runs
-    # pass --no-chain so that only the 64-token dispatches are averaged)
+    # the 64-token decode (its K2 / K3 kernels are also the 16-token chain's, and its K1 the
+    # MXFP4 64-token layer's: byte-counter runs pass --counter-run, which skips the chain)
     "t64_decode_k1_route": "k1_route<24, 8, 4,", "t64_decode_k2_gateup": "k2l_gateup<24, 8>",
     "t64_decode_k3_down_combine": "k3l_down<24, 8>", "mx64_decode_k2_gateup": "k2l_gateup_mx<24, 8, true>",
     "mx64_decode_k3_down_combine": "k3l_down_mx<24, 8, true>", "copy": "neg_kernel"}
@@ -1130,14 +1132,14 @@ def main():
                 "us_per_step": round(m64["ms"] * 1e3, 2), "unique_experts": round(m64["U"], 2),
                 "unique_expert_bytes": round(m64["unique_b"]), "step_bytes": round(m64["step_b"]),
                 "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                "four_call_us_per_step": round(m64["ms4"] * 1e3, 2),
+                "four_call_us_per_step": round(m64["ms4"] * 1e3, 2) if m64["ms4"] == m64["ms4"] else None,
                 "kernels": kern,
                 "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["gbs"], "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round((kern[dom]["gbs"] or 0) / HBM_PEAK_GBS, 4),
                              "traffic": traffic.get("mx64_" + dom), "algorithmic_bytes": kern[dom]["algorithmic_bytes"]}}
         except Exception as e:
             out["mxfp4_decode_t64_zipf"] = {"error": repr(e)}
-    if not args.no_extra and not args.no_chain:
+    if not args.no_extra and not args.counter_run:
         try:
             ch = chain_bench(args)
             gbs = ch["step_b"] / (ch["ms"] * 1e-3) / 1e9
