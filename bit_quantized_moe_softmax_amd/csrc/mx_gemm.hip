@@ -21,7 +21,9 @@
 // (double-buffered, rows padded against bank conflicts).  Each wave owns 64 weight rows and
 // keeps their E2M1 codes in registers, loaded straight from HBM four K steps ahead: every
 // weight byte is used by exactly one wave, so it never passes through LDS.  Per K step a
-// wave issues up to 8 x 4 MFMAs (16-row tiles past the block's last pair are skipped).
+// wave issues up to 8 x 4 MFMAs (16-row tiles past the block's last pair are skipped; in the
+// down GEMM a full block runs a branch-free copy of the K loop, each tile's A fragment read
+// one tile ahead).
 //
 // Weight layouts.  Row-major MXFP4 (codes [rows][K/2], scales [rows][K/32]) has each wave
 // read 64 bytes from each of 16 rows K/2 bytes apart per K step: half a cache line per row,
@@ -165,7 +167,11 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
     for (int q = 0; q < 4; ++q) acc[i][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const int mtiles = (nrows + 15) >> 4;
 
-  auto compute = [&](int buf, int slot) {
+  // MTC = kMT: a full M block, the tile loop without branches, so the A-fragment reads of the
+  // next tiles can be issued ahead of the current tile's MFMAs; MTC = 0: the job's tile count
+  // at run time (tiles past the block's last row skipped)
+  auto compute = [&](int buf, int slot, auto mtc) {
+    constexpr int MTC = decltype(mtc)::value;
     i32x8_t bop[4];
     int bsc[4];
 #pragma unroll
@@ -175,6 +181,31 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
       bsc[q] = (rbs[slot][q] >> (8 * g)) & 0xFF;
     }
     const uint8_t* sa = s_a[buf];
+    auto afrag = [&](int mt, i32x8_t& aop, int& asc) {
+      const int arow = 16 * mt + c16;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(&sa[arow * kAStride + 16 * g]);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(&sa[arow * kAStride + 64 + 16 * g]);
+      aop = (i32x8_t){(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      asc = (s_as[buf][arow] >> (8 * g)) & 0xFF;
+    };
+    if constexpr (MTC == kMT) {
+      // tile mt + 1's fragment read is issued before tile mt's MFMAs, and no further ahead
+      i32x8_t an;
+      int ascn;
+      afrag(0, an, ascn);
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const i32x8_t aop = an;
+        const int asc = ascn;
+        if (mt + 1 < kMT) afrag(mt + 1, an, ascn);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[mt][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop, bop[q], acc[mt][q], 0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, asc, 0, bsc[q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
       if (mt < mtiles) {
@@ -199,15 +230,16 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   // loads repeat the last step's data, which keeps the code branch-free and the wait counts
   // exact.
   const int nsteps = K / kBK;
-  auto step = [&](int s, auto slot_c) {
+  auto step = [&](int s, auto slot_c, auto mtc) {
     constexpr int SLOT = decltype(slot_c)::value;
     constexpr int AN = (SLOT + kRing - 1) % kRing, A1 = (SLOT + 1) % kRing;
     load_a(AN, min(s + kRing - 1, nsteps - 1) * kBK);
-    if (wvalid) compute(s & 1, SLOT);
+    if (wvalid) compute(s & 1, SLOT, mtc);
     load_b(SLOT, min(s + kRing, nsteps - 1) * kBK);
     if (s + 1 < nsteps) store_a(A1, (s + 1) & 1);
     lds_barrier();
   };
+  auto kloop = [&](auto mtc) {
 
 #pragma unroll
   for (int i = 0; i < kRing; ++i) {
@@ -223,14 +255,19 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   // it wait for loads issued one step earlier instead of kRing.
   int s = 0;
   for (; s + kRing <= nsteps; s += kRing) {
-    step(s, std::integral_constant<int, 0>{});
-    step(s + 1, std::integral_constant<int, 1>{});
-    step(s + 2, std::integral_constant<int, 2>{});
-    step(s + 3, std::integral_constant<int, 3>{});
+    step(s, std::integral_constant<int, 0>{}, mtc);
+    step(s + 1, std::integral_constant<int, 1>{}, mtc);
+    step(s + 2, std::integral_constant<int, 2>{}, mtc);
+    step(s + 3, std::integral_constant<int, 3>{}, mtc);
   }
-  if (s < nsteps) step(s, std::integral_constant<int, 0>{});
-  if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
-  if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
+  if (s < nsteps) step(s, std::integral_constant<int, 0>{}, mtc);
+  if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{}, mtc);
+  if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{}, mtc);
+  };
+  // a full M block of the down GEMM runs a straight-line copy of the K loop (a job's tile
+  // count is uniform over the workgroup); in the gate/up GEMM that copy spilled registers
+  if (!GATEUP && mtiles == kMT) kloop(std::integral_constant<int, kMT>{});
+  else kloop(std::integral_constant<int, 0>{});
   if (wvalid) {
   // ---- epilogue.  D element (4*(lane/16)+i, lane%16) of each 16x16 tile is acc[..][..][i].
   if (GATEUP) {
