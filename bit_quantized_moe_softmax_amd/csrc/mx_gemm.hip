@@ -47,6 +47,8 @@
 #include "gemm_jobs.h"
 
 #include <math.h>
+#include <cstdlib>
+#include <cstring>
 
 namespace {
 
@@ -330,14 +332,312 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
   }   // jobs
 }
 
+// ---------------------------------------------------------------------------------------
+// The same GEMM with the activation tile moved from HBM straight into LDS (buffer loads with
+// the LDS flag, 16 bytes per lane) instead of through a register ring and LDS stores.  Each
+// K step's tile lands in LDS in the MFMA's operand order: per 16-row tile mt and half h one
+// 1 KiB block whose 16 bytes at 16 l are lane l's A bytes (row 16 mt + l % 16, K bytes
+// 64 h + 16 (l / 16) .. + 15 of the step), so every fragment read is one conflict-free
+// 1 KiB ds_read_b128.  The scale words follow, 32 rows per wave (rows 32 w + l % 32; lanes
+// 32..63 repeat them so every lane's load is unconditional).  Without the A ring a wave
+// fits 256 registers and two workgroups share a CU: one workgroup's LDS reads, barrier and
+// job set-up overlap the other's MFMAs.
+//
+// Three LDS buffers: step s computes from buffer s % 3 while the tiles of steps s + 1 and
+// s + 2 are in flight, so a tile has two steps to arrive (one was not enough: the rows come
+// from L2 or the Infinity Cache, about a step's time away).  The tile loads are written in
+// inline asm, out of the compiler's sight: it treats every LDS-DMA load as a pending write
+// to any LDS address and would wait for the newest one before each LDS read, which leaves
+// one step of lead whatever the ring depth.  The waits are therefore explicit: vector
+// memory loads complete in issue order, and after the tile of step s only the weight loads
+// of step s - 1 (kBLoads) and the tile of step s + 1 (kDmaLoads) are issued, so step s
+// waits for vmcnt kBLoads + kDmaLoads and then meets the other waves at a barrier (their
+// parts of the tile), with an acquire fence on LDS only (a release fence would wait for
+// every load in flight).  Loads past the last step repeat it, so these counts never change.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS-DMA buffer loads: lane l's 16 (or 4) bytes at voff + soff land at LDS byte
+// lds + 16 l (or 4 l).  lds is wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+
+constexpr int kBLoads = 8;      // weight loads per wave and step: 4 code pieces + 4 scale words
+constexpr int kRingD = 3;       // K steps of tiles and of weight loads in flight per wave
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <bool GATEUP, bool TILED, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_dma_kernel(MxArgs p) {
+  constexpr int TPW = kMT / NW;        // 16-row A tiles this wave loads
+  constexpr int RPW = kMB / NW;        // A rows whose scale words this wave loads
+  constexpr int NTW = NW * kNWave;     // weight rows per job
+  constexpr int NDMA = 2 * TPW + 1;    // LDS-DMA loads per wave and step
+  __shared__ __align__(16) uint8_t s_a[kRingD][kMB * kBK];   // [buf][mt][half][lane] 16 B
+  __shared__ __align__(16) uint32_t s_as[kRingD][NW][64];    // [buf][wave][lane]
+  __shared__ int s_arow[kMB];
+  __shared__ JobTable s_jt;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = p.K, N = p.N;
+  const int NT = GATEUP ? (N + NTW / 2 - 1) / (NTW / 2) : (N + NTW - 1) / NTW;
+
+  if (wave == 0) build_job_table(p.offsets, p.E, s_jt, lane);
+  __syncthreads();
+  const long n_work = (long)s_jt.nb[p.E] * NT;
+  const int x = blockIdx.x % kXcd, slot = blockIdx.x / kXcd, nslot = gridDim.x / kXcd;
+  const long w_lo = n_work * x / kXcd, w_hi = n_work * (x + 1) / kXcd;
+  for (long w = w_lo + slot; w < w_hi; w += nslot) {
+  const Job jb = decode_job(s_jt, p.E, NT, w);
+  const int nrows = jb.nrows;
+  if (tid < kMB) {
+    int src = -1;
+    if (tid < nrows) {
+      const int pos = jb.m0 + tid;
+      src = GATEUP ? p.sorted_pair[pos] / p.k : pos;
+    }
+    s_arow[tid] = src;
+  }
+  __syncthreads();
+
+  // ---- A: this wave loads tiles TPW wave .. TPW wave + TPW - 1 (both halves) and the
+  // scale words of rows RPW wave .. RPW wave + RPW - 1
+  const int g = lane >> 4, c16 = lane & 15;
+  const rsrc_t ra_q = make_rsrc(p.aq, (uint32_t)((GATEUP ? p.T : p.P) * (size_t)K));
+  const rsrc_t ra_s = make_rsrc(p.as, (uint32_t)((GATEUP ? p.T : p.P) * (size_t)(K / 32)));
+  uint32_t voff[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int src = s_arow[16 * (TPW * wave + i) + c16];
+    voff[i] = src >= 0 ? (uint32_t)src * K + 16 * g : kOOB;
+  }
+  const int ssrc = s_arow[RPW * wave + (lane % RPW)];
+  const uint32_t vsoff = ssrc >= 0 ? (uint32_t)ssrc * (K / 32) : kOOB;
+  auto dma_a = [&](int buf, int k0) {
+    const uint32_t sq = (uint32_t)__builtin_amdgcn_readfirstlane(k0);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        dma16(ra_q, lds_addr(&s_a[buf][((TPW * wave + i) * 2 + h) * 1024]), voff[i], sq + 64 * h);
+    dma4(ra_s, lds_addr(&s_as[buf][wave][0]), vsoff, sq / 32);
+  };
+
+  // ---- this wave's weight rows: 4 n-tiles of 16 (gate/up: gate, gate, up, up)
+  const int col0 = GATEUP ? jb.ntile * (NTW / 2) + 32 * wave
+                          : jb.ntile * NTW + kNWave * wave;
+  // (always true for gate/up, whose N is a multiple of the tile; kept a run-time test there
+  // too: the branch keeps the compiler from scheduling the unrolled steps into each other,
+  // which spilled)
+  const bool wvalid = col0 < N;
+  const size_t ebytes = (size_t)N * (K / 2), escales = (size_t)N * (K / 32);
+  const rsrc_t rb0 = make_rsrc(p.wcodes0 + jb.e * ebytes, (uint32_t)ebytes);
+  const rsrc_t rs0 = make_rsrc(p.wscales0 + jb.e * escales, (uint32_t)escales);
+  const rsrc_t rb1 = GATEUP ? make_rsrc(p.wcodes1 + jb.e * ebytes, (uint32_t)ebytes) : rb0;
+  const rsrc_t rs1 = GATEUP ? make_rsrc(p.wscales1 + jb.e * escales, (uint32_t)escales) : rs0;
+  const uint32_t trow = (uint32_t)(wvalid ? col0 : 0);
+  const uint32_t brow = trow + c16;
+  const uint32_t boff = TILED ? trow * (K / 2) + 16 * lane : brow * (K / 2) + 16 * g;
+  const uint32_t bsoff = TILED ? trow * (K / 32) + 4 * c16 : brow * (K / 32);
+  auto koff = [](int k0) { return TILED ? k0 * 8 : k0 / 2; };
+  auto ksoff = [](int k0) { return TILED ? k0 / 2 : k0 / 32; };
+  auto qrow = [](int q) { return GATEUP ? 16 * (q & 1) : 16 * q; };
+
+  uint4 rb[kRingD][4];
+  uint32_t rbs[kRingD][4];
+  auto load_b = [&](int slot, int k0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool hi = GATEUP && q >= 2;
+      rb[slot][q] = bload16(hi ? rb1 : rb0, boff, qrow(q) * (K / 2) + koff(k0));
+      rbs[slot][q] = bload4(hi ? rs1 : rs0, bsoff, qrow(q) * (K / 32) + ksoff(k0));
+    }
+  };
+
+  f32x4_t acc[kMT][4];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[i][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  const int mtiles = (nrows + 15) >> 4;
+
+  auto compute = [&](int buf, int slot, auto mtc) {
+    constexpr int MTC = decltype(mtc)::value;
+    i32x8_t bop[4];
+    int bsc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = rb[slot][q];
+      bop[q] = (i32x8_t){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      bsc[q] = (rbs[slot][q] >> (8 * g)) & 0xFF;
+    }
+    const uint8_t* sa = s_a[buf];
+    auto afrag = [&](int mt, i32x8_t& aop, int& asc) {
+      const uint4 v0 = reinterpret_cast<const uint4*>(sa + (2 * mt) * 1024)[lane];
+      const uint4 v1 = reinterpret_cast<const uint4*>(sa + (2 * mt + 1) * 1024)[lane];
+      aop = (i32x8_t){(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      const int arow = 16 * mt + c16;
+      asc = (s_as[buf][arow / RPW][arow % RPW] >> (8 * g)) & 0xFF;
+    };
+    // MTC tiles, known at compile time: tile mt + 1's fragment read is issued before tile
+    // mt's MFMAs, and no further ahead
+    i32x8_t an;
+    int ascn;
+    afrag(0, an, ascn);
+#pragma unroll
+    for (int mt = 0; mt < MTC; ++mt) {
+      const i32x8_t aop = an;
+      const int asc = ascn;
+      if (mt + 1 < MTC) afrag(mt + 1, an, ascn);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[mt][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            aop, bop[q], acc[mt][q], 0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, asc, 0, bsc[q]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int nsteps = K / kBK;
+  // Step s: wait for this wave's part of tile s, meet the other waves, compute from buffer
+  // s % kRingD and weight slot s % kRingD, refill that slot with step s + kRingD, then load
+  // tile s + 2 into buffer (s + 2) % kRingD (read last at step s - 1, before the barrier).
+  auto step = [&](int s, auto slot_c, auto mtc) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    if (s == 0) wait_vmcnt<NDMA>();   // behind tile 0: tile 1
+    else wait_vmcnt<kBLoads + NDMA>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
+    if (wvalid) compute(SLOT, SLOT, mtc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(SLOT, min(s + kRingD, nsteps - 1) * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a((SLOT + 2) % kRingD, min(s + 2, nsteps - 1) * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto kloop = [&](auto mtc) {
+#pragma unroll
+    for (int i = 0; i < kRingD; ++i) {
+      load_b(i, min(i, nsteps - 1) * kBK);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dma_a(0, 0);
+    dma_a(1, min(1, nsteps - 1) * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+    int s = 0;
+    for (; s + kRingD <= nsteps; s += kRingD)
+      static_for<0, kRingD>([&](auto i) { step(s + i, i, mtc); });
+    static_for<0, kRingD - 1>([&](auto i) { if (s + i < nsteps) step(s + i, i, mtc); });
+  };
+  // one straight-line copy of the K loop per tile count (the count is uniform over the
+  // workgroup): a tile loop with a branch per tile keeps the compiler from reading the
+  // fragments ahead and spills at 256 registers
+  switch (mtiles) {
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
+    case 6: kloop(std::integral_constant<int, 6>{}); break;
+    case 7: kloop(std::integral_constant<int, 7>{}); break;
+    default: kloop(std::integral_constant<int, 8>{}); break;
+  }
+  if (wvalid) {
+  if (GATEUP) {
+    const int I = N;
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      if (mt >= mtiles) continue;
+      float hh[4][2];
+      uint32_t am[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float gv = acc[mt][q][i], uv = acc[mt][q + 2][i];
+          hh[i][q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+        }
+        am[i] = row16_max(max(__float_as_uint(hh[i][0]) & 0x7FFFFFFFu,
+                              __float_as_uint(hh[i][1]) & 0x7FFFFFFFu));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 16 * mt + 4 * g + i;
+        const uint32_t amax = am[i];
+        if (rl < nrows) {
+          const int pos = jb.m0 + rl;
+          uint8_t* hrow = p.hq + (size_t)pos * I + col0;
+          if (amax == 0) {
+            hrow[c16] = 0;
+            hrow[c16 + 16] = 0;
+            if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = 0;
+          } else {
+            const int X = moe_mx_exp(amax);
+            const uint32_t q = moe_e4m3_pair_hw(hh[i][0], hh[i][1], X);
+            hrow[c16] = (uint8_t)q;
+            hrow[c16 + 16] = (uint8_t)(q >> 8);
+            if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = (uint8_t)(X + 127);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      if (mt >= mtiles) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 16 * mt + 4 * g + i;
+        if (rl < nrows) {
+          float* yrow = p.y + (size_t)(jb.m0 + rl) * N + col0 + c16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) yrow[16 * q] = acc[mt][q][i];
+        }
+      }
+    }
+  }
+  }   // wvalid
+  // The waits of the K loop count every weight load, including those past the last step,
+  // whose data no MFMA uses: this opaque use keeps the compiler from dropping them as dead
+  // (it waits for them here, where the barrier below waits for every load anyway).
+#pragma unroll
+  for (int i = 0; i < kRingD; ++i) {
+    uint32_t f = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f ^= rb[i][q].x ^ rb[i][q].y ^ rb[i][q].z ^ rb[i][q].w ^ rbs[i][q];
+    asm volatile("" ::"v"(f));
+  }
+  __syncthreads();   // s_arow and the LDS buffers are reused by the next job
+  }   // jobs
+}
+
 // Grid: enough workgroups for the most jobs any routing of P pairs over E experts makes
 // (sum over active experts of ceil(cnt / 128) <= min(P, E) + ceil(P / 128)), rounded up to
 // a multiple of the XCD count so that every XCD's job range fits.
-inline unsigned grid_for(const MxArgs& a, int NT) {
+inline unsigned grid_for(const MxArgs& a, int NT, int per_cu = 1) {
   const long slots = (a.P < a.E ? a.P : a.E) + (a.P + kMB - 1) / kMB;
   const long work = slots * NT;
   const long most = kXcd * ((work + kXcd - 1) / kXcd);
-  // persistent: one workgroup per CU (the kernel holds one per CU), in whole XCD groups
+  // persistent: per_cu workgroups per CU (as many as the kernel holds), in whole XCD groups
   static int n_cu[16] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
@@ -346,7 +646,7 @@ inline unsigned grid_for(const MxArgs& a, int NT) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     n_cu[dev] = n;
   }
-  const long per = kXcd * ((n_cu[dev] + kXcd - 1) / kXcd);
+  const long per = kXcd * ((per_cu * n_cu[dev] + kXcd - 1) / kXcd);
   return (unsigned)(most < per ? most : per);
 }
 
@@ -377,23 +677,50 @@ __global__ __launch_bounds__(256) void mx_pack_tiles_kernel(const uint8_t* __res
 
 }  // namespace
 
+// MOE_MI355X_MX_GEMM=regs selects the register-staged kernel (one workgroup per CU) for
+// comparison; the default is the LDS-DMA kernel (two per CU).
+static bool mx_use_regs() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = std::getenv("MOE_MI355X_MX_GEMM");
+    v = (e && std::strcmp(e, "regs") == 0) ? 1 : 0;
+  }
+  return v == 1;
+}
+
+#ifndef MOE_MX_NW
+#define MOE_MX_NW 8
+#endif
+constexpr int kNW = MOE_MX_NW;   // waves per workgroup of the LDS-DMA kernel
+
+template <bool GATEUP>
+static void launch_mx(const MxArgs& a, hipStream_t s) {
+  if (mx_use_regs()) {
+    const int NT = GATEUP ? a.N / (kNTile / 2) : (a.N + kNTile - 1) / kNTile;
+    if (a.tiled)
+      hipLaunchKernelGGL((mx_gemm_kernel<GATEUP, true>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((mx_gemm_kernel<GATEUP, false>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+    return;
+  }
+  constexpr int NTW = kNW * kNWave;
+  const int NT = GATEUP ? (a.N + NTW / 2 - 1) / (NTW / 2) : (a.N + NTW - 1) / NTW;
+  const unsigned grid = grid_for(a, NT, 8 / kNW);
+  if (a.tiled)
+    hipLaunchKernelGGL((mx_gemm_dma_kernel<GATEUP, true, kNW>), dim3(grid), dim3(64 * kNW), 0, s, a);
+  else
+    hipLaunchKernelGGL((mx_gemm_dma_kernel<GATEUP, false, kNW>), dim3(grid), dim3(64 * kNW), 0, s, a);
+}
+
 hipError_t moe_launch_mx_gateup(const MxArgs& a, hipStream_t s) {
   if (a.N % (kNTile / 2) || a.K % kBK) return hipErrorInvalidValue;
-  const int NT = a.N / (kNTile / 2);
-  if (a.tiled)
-    hipLaunchKernelGGL((mx_gemm_kernel<true, true>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((mx_gemm_kernel<true, false>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+  launch_mx<true>(a, s);
   return hipGetLastError();
 }
 
 hipError_t moe_launch_mx_down(const MxArgs& a, hipStream_t s) {
   if (a.N % kNWave || a.K % kBK) return hipErrorInvalidValue;
-  const int NT = (a.N + kNTile - 1) / kNTile;
-  if (a.tiled)
-    hipLaunchKernelGGL((mx_gemm_kernel<false, true>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((mx_gemm_kernel<false, false>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
+  launch_mx<false>(a, s);
   return hipGetLastError();
 }
 
