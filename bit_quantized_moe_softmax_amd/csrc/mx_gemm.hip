@@ -8,31 +8,32 @@
 // MX-quantised along I before the down projection.
 //
 // Work split.  The pairs of one expert (contiguous in sorted order) are cut into M blocks
-// of at most 128 rows, evenly (150 pairs -> 75 + 75).  A job is (M block, N tile of 256
-// weight rows): for gate/up 128 gate rows + the 128 up rows of the same h-columns, for down
-// 256 output columns.  Jobs are numbered expert-major, then by N tile, then by M block, and
+// of at most 128 rows, evenly (150 pairs -> 75 + 75).  A job is (M block, N tile of 512
+// weight rows): for gate/up 256 gate rows + the 256 up rows of the same h-columns, for down
+// 512 output columns.  Jobs are numbered expert-major, then by N tile, then by M block, and
 // the jobs of one XCD are one contiguous range (workgroup b runs on XCD b % 8): the blocks
 // of an expert that read the same weight tile run side by side, and the N tiles that share
 // an M block's activation rows run close together, behind one L2.  The kernel is
-// persistent: one workgroup per CU takes its XCD's jobs in turn, decoding each from job
-// tables built once in LDS.
+// persistent: one workgroup of eight waves per CU takes its XCD's jobs in turn, decoding
+// each from job tables built once in LDS.
 //
-// Tiling.  Four waves share the M block's activation rows, staged per K step (128) in LDS
-// (double-buffered, rows padded against bank conflicts).  Each wave owns 64 weight rows and
-// keeps their E2M1 codes in registers, loaded straight from HBM four K steps ahead: every
-// weight byte is used by exactly one wave, so it never passes through LDS.  Per K step a
-// wave issues up to 8 x 4 MFMAs (16-row tiles past the block's last pair are skipped; in the
-// down GEMM a full block runs a branch-free copy of the K loop, each tile's A fragment read
-// one tile ahead).
+// Tiling.  The eight waves share the M block's activation rows, staged per K step (128) in
+// LDS; each wave owns 64 weight rows and keeps their E2M1 codes in registers, loaded
+// straight from HBM three K steps ahead: every weight byte is used by exactly one wave, so
+// it never passes through LDS.  Per K step a wave issues (tiles of the block) x 4 MFMAs;
+// the tile count is uniform over a job, and each count has its own straight-line copy of
+// the K loop in which tile t + 1's A fragment is read before tile t's MFMAs.  With 128
+// accumulators and no staging registers a wave fits 256 registers, two waves per SIMD.
 //
 // Weight layouts.  Row-major MXFP4 (codes [rows][K/2], scales [rows][K/32]) has each wave
-// read 64 bytes from each of 16 rows K/2 bytes apart per K step: half a cache line per row,
-// the other half a step later, which scatters the weight stream over DRAM pages.  The tiled
-// layout (moe_mxfp4_pack_tiles) stores the same bytes in the order the MFMA consumes them:
-// per 16-row tile and K step one 1 KiB block whose 16 bytes at 16 l are lane l's operand
-// (row l % 16, K bytes 16 (l / 16) .. + 15 of the step), and one 64-byte scale block (4 bytes
-// per row, byte g = scale of the step's K block g).  A wave then streams each of its tiles
-// as one contiguous run of K/2 * 16 bytes.
+// read 64 bytes from each of 16 rows K/2 bytes apart per K step and n-tile: half a cache
+// line per row, the other half a step later, which scatters the weight stream over DRAM
+// pages.  The tiled layout (moe_mxfp4_pack_tiles) stores the same bytes in the order the
+// MFMA consumes them: per 64-row group and K step one 4 KiB run of four 1 KiB tile blocks
+// whose 16 bytes at 16 l are lane l's operand (row l % 16 of the tile, K bytes 16 (l / 16)
+// .. + 15 of the step), and one 256-byte scale block whose 32-bit word l holds the four
+// tiles' scales of lane l.  A down wave then streams one contiguous 4 KiB run and one
+// scale word per step (gate/up: 2 KiB of each matrix, two scale words).
 //
 // Operand layout of the scaled 16x16x128 MFMA (measured with an in-bounds probe on gfx950,
 // K counted within the 128-wide step): lane l serves row/column l % 16 and lane group
@@ -47,17 +48,12 @@
 #include "gemm_jobs.h"
 
 #include <math.h>
-#include <cstdlib>
-#include <cstring>
 
 namespace {
 
 constexpr int kMT = kMB / 16;   // 16-row MFMA tiles per M block
 constexpr int kNWave = 64;      // weight rows per wave
-constexpr int kNTile = 4 * kNWave;
 constexpr int kBK = 128;        // K per step
-constexpr int kAStride = 144;   // bytes per A row in LDS (128 + 16 pad)
-constexpr int kRing = 4;       // K steps of loads in flight (register rings)
 
 // Largest value over each 16-lane row of the wave (the 16 columns of one MFMA D row), by
 // DPP within the row: swaps of neighbours and pairs, then the half-row and row mirrors.
@@ -69,291 +65,28 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   return v;
 }
 
-template <bool GATEUP, bool TILED>
-__global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxArgs p) {
-  __shared__ __align__(16) uint8_t s_a[2][kMB * kAStride];
-  __shared__ uint32_t s_as[2][256];   // entries >= kMB are written, never read
-  __shared__ int s_arow[kMB];
-  __shared__ JobTable s_jt;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int K = p.K, N = p.N;
-  const int NT = GATEUP ? N / (kNTile / 2) : (N + kNTile - 1) / kNTile;
-
-  if (wave == 0) build_job_table(p.offsets, p.E, s_jt, lane);
-  __syncthreads();
-  // Persistent: the jobs of XCD x are one contiguous range, taken by its workgroups in turn,
-  // so the N tiles that share an M block's activation rows run together behind one L2.
-  const long n_work = (long)s_jt.nb[p.E] * NT;
-  const int x = blockIdx.x % kXcd, slot = blockIdx.x / kXcd, nslot = gridDim.x / kXcd;
-  const long w_lo = n_work * x / kXcd, w_hi = n_work * (x + 1) / kXcd;
-  for (long w = w_lo + slot; w < w_hi; w += nslot) {
-  const Job jb = decode_job(s_jt, p.E, NT, w);
-  const int nrows = jb.nrows;
-  if (tid < kMB) {
-    int src = -1;
-    if (tid < nrows) {
-      const int pos = jb.m0 + tid;
-      src = GATEUP ? p.sorted_pair[pos] / p.k : pos;
-    }
-    s_arow[tid] = src;
-  }
-  __syncthreads();
-
-  // ---- A staging: thread covers 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 i
-  const int achunk = tid & 7;
-  const rsrc_t ra_q = make_rsrc(p.aq, (uint32_t)((GATEUP ? p.T : p.P) * (size_t)K));
-  const rsrc_t ra_s = make_rsrc(p.as, (uint32_t)((GATEUP ? p.T : p.P) * (size_t)(K / 32)));
-  uint32_t aoff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int src = s_arow[(tid >> 3) + 32 * i];
-    aoff[i] = src >= 0 ? (uint32_t)src * K + 16 * achunk : kOOB;
-  }
-  const int srow = s_arow[tid & (kMB - 1)];   // threads >= kMB load a scale word they never store
-  const uint32_t asoff = srow >= 0 ? (uint32_t)srow * (K / 32) : kOOB;
-
-  // ---- this wave's weight rows: 4 n-tiles of 16 (gate/up: gate, gate, up, up)
-  const int g = lane >> 4, c16 = lane & 15;
-  const int col0 = GATEUP ? jb.ntile * (kNTile / 2) + 32 * wave   // first of 32 h-columns
-                          : jb.ntile * kNTile + kNWave * wave;    // first of 64 output columns
-  const bool wvalid = GATEUP || col0 < N;
-  const size_t ebytes = (size_t)N * (K / 2), escales = (size_t)N * (K / 32);
-  const rsrc_t rb0 = make_rsrc(p.wcodes0 + jb.e * ebytes, (uint32_t)ebytes);
-  const rsrc_t rs0 = make_rsrc(p.wscales0 + jb.e * escales, (uint32_t)escales);
-  const rsrc_t rb1 = GATEUP ? make_rsrc(p.wcodes1 + jb.e * ebytes, (uint32_t)ebytes) : rb0;
-  const rsrc_t rs1 = GATEUP ? make_rsrc(p.wscales1 + jb.e * escales, (uint32_t)escales) : rs0;
-  const uint32_t trow = (uint32_t)(wvalid ? col0 : 0);   // first row of the wave's first tile
-  const uint32_t brow = trow + c16;
-  // per-lane offsets of step 0 of the first tile; per step and tile the SGPR offset adds
-  // koff(k0) and qrow(q) rows (a tile of 16 rows is 16 rows in both layouts)
-  const uint32_t boff = TILED ? trow * (K / 2) + 16 * lane : brow * (K / 2) + 16 * g;
-  const uint32_t bsoff = TILED ? trow * (K / 32) + 4 * c16 : brow * (K / 32);
-  auto koff = [](int k0) { return TILED ? k0 * 8 : k0 / 2; };    // 1 KiB or 64 B per step
-  auto ksoff = [](int k0) { return TILED ? k0 / 2 : k0 / 32; };  // 64 B or 4 B per step
-  // n-tile q starts qrow(q) rows after the lane's first row
-  auto qrow = [](int q) { return GATEUP ? 16 * (q & 1) : 16 * q; };
-
-  // Register rings: A(s) is loaded kRing - 1 steps before it is stored to LDS (at the end of
-  // step s - 1), B(s) kRing steps before step s uses it.  Slot of step s: s % kRing.
-  uint4 ra[kRing][4];
-  uint32_t ras[kRing];
-  auto load_a = [&](int slot, int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[slot][i] = bload16(ra_q, aoff[i], k0);
-    ras[slot] = bload4(ra_s, asoff, k0 / 32);
-  };
-  auto store_a = [&](int slot, int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&s_a[buf][((tid >> 3) + 32 * i) * kAStride + 16 * achunk]) = ra[slot][i];
-    s_as[buf][tid] = ras[slot];   // unconditional: keeps the load from sinking into a branch
-  };
-
-  uint4 rb[kRing][4];
-  uint32_t rbs[kRing][4];
-  auto load_b = [&](int slot, int k0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool hi = GATEUP && q >= 2;
-      rb[slot][q] = bload16(hi ? rb1 : rb0, boff, qrow(q) * (K / 2) + koff(k0));
-      rbs[slot][q] = bload4(hi ? rs1 : rs0, bsoff, qrow(q) * (K / 32) + ksoff(k0));
-    }
-  };
-
-  f32x4_t acc[kMT][4];
-#pragma unroll
-  for (int i = 0; i < kMT; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[i][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  const int mtiles = (nrows + 15) >> 4;
-
-  // MTC = kMT: a full M block, the tile loop without branches, so the A-fragment reads of the
-  // next tiles can be issued ahead of the current tile's MFMAs; MTC = 0: the job's tile count
-  // at run time (tiles past the block's last row skipped)
-  auto compute = [&](int buf, int slot, auto mtc) {
-    constexpr int MTC = decltype(mtc)::value;
-    i32x8_t bop[4];
-    int bsc[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = rb[slot][q];
-      bop[q] = (i32x8_t){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      bsc[q] = (rbs[slot][q] >> (8 * g)) & 0xFF;
-    }
-    const uint8_t* sa = s_a[buf];
-    auto afrag = [&](int mt, i32x8_t& aop, int& asc) {
-      const int arow = 16 * mt + c16;
-      const uint4 v0 = *reinterpret_cast<const uint4*>(&sa[arow * kAStride + 16 * g]);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(&sa[arow * kAStride + 64 + 16 * g]);
-      aop = (i32x8_t){(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      asc = (s_as[buf][arow] >> (8 * g)) & 0xFF;
-    };
-    if constexpr (MTC == kMT) {
-      // tile mt + 1's fragment read is issued before tile mt's MFMAs, and no further ahead
-      i32x8_t an;
-      int ascn;
-      afrag(0, an, ascn);
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const i32x8_t aop = an;
-        const int asc = ascn;
-        if (mt + 1 < kMT) afrag(mt + 1, an, ascn);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc[mt][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop, bop[q], acc[mt][q], 0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, asc, 0, bsc[q]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      return;
-    }
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-      if (mt < mtiles) {
-        const int arow = 16 * mt + c16;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(&sa[arow * kAStride + 16 * g]);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(&sa[arow * kAStride + 64 + 16 * g]);
-        const i32x8_t aop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                             (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-        const int asc = (s_as[buf][arow] >> (8 * g)) & 0xFF;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc[mt][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop, bop[q], acc[mt][q], 0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, asc, 0, bsc[q]);
-      }
-    }
-  };
-
-  // Step s: issue A(s + kRing - 1) (its slot held A(s - 1), stored to LDS a step ago), compute
-  // from LDS buffer s & 1 and B slot s % kRing, refill that B slot with B(s + kRing), then
-  // store A(s + 1) to the other LDS buffer.  Loads complete in issue order, so waiting for
-  // A(s + 1) waits for nothing issued in the last kRing - 2 steps.  Past the last step the
-  // loads repeat the last step's data, which keeps the code branch-free and the wait counts
-  // exact.
-  const int nsteps = K / kBK;
-  auto step = [&](int s, auto slot_c, auto mtc) {
-    constexpr int SLOT = decltype(slot_c)::value;
-    constexpr int AN = (SLOT + kRing - 1) % kRing, A1 = (SLOT + 1) % kRing;
-    load_a(AN, min(s + kRing - 1, nsteps - 1) * kBK);
-    if (wvalid) compute(s & 1, SLOT, mtc);
-    load_b(SLOT, min(s + kRing, nsteps - 1) * kBK);
-    if (s + 1 < nsteps) store_a(A1, (s + 1) & 1);
-    lds_barrier();
-  };
-  auto kloop = [&](auto mtc) {
-
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) {
-    load_b(i, min(i, nsteps - 1) * kBK);
-    if (i < kRing - 1) load_a(i, min(i, nsteps - 1) * kBK);
-    // keep the issue order of the steady state, whose wait counts the loop relies on
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  store_a(0, 0);
-  lds_barrier();
-  // Whole groups of kRing steps first, with no branch between them: the compiler counts the
-  // loads in flight along every path into a wait, and a path that skipped steps would make
-  // it wait for loads issued one step earlier instead of kRing.
-  int s = 0;
-  for (; s + kRing <= nsteps; s += kRing) {
-    step(s, std::integral_constant<int, 0>{}, mtc);
-    step(s + 1, std::integral_constant<int, 1>{}, mtc);
-    step(s + 2, std::integral_constant<int, 2>{}, mtc);
-    step(s + 3, std::integral_constant<int, 3>{}, mtc);
-  }
-  if (s < nsteps) step(s, std::integral_constant<int, 0>{}, mtc);
-  if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{}, mtc);
-  if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{}, mtc);
-  };
-  // a full M block of the down GEMM runs a straight-line copy of the K loop (a job's tile
-  // count is uniform over the workgroup); in the gate/up GEMM that copy spilled registers
-  if (!GATEUP && mtiles == kMT) kloop(std::integral_constant<int, kMT>{});
-  else kloop(std::integral_constant<int, 0>{});
-  if (wvalid) {
-  // ---- epilogue.  D element (4*(lane/16)+i, lane%16) of each 16x16 tile is acc[..][..][i].
-  if (GATEUP) {
-    const int I = N;
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-      if (mt >= mtiles) continue;
-      // the four rows of this lane group first, so their reductions overlap
-      float hh[4][2];
-      uint32_t am[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float gv = acc[mt][q][i], uv = acc[mt][q + 2][i];
-          hh[i][q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-        }
-        am[i] = row16_max(max(__float_as_uint(hh[i][0]) & 0x7FFFFFFFu,
-                              __float_as_uint(hh[i][1]) & 0x7FFFFFFFu));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rl = 16 * mt + 4 * g + i;
-        const float h[2] = {hh[i][0], hh[i][1]};
-        const uint32_t amax = am[i];
-        if (rl < nrows) {
-          const int pos = jb.m0 + rl;
-          uint8_t* hrow = p.hq + (size_t)pos * I + col0;
-          if (amax == 0) {
-            hrow[c16] = 0;
-            hrow[c16 + 16] = 0;
-            if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = 0;
-          } else {
-            const int X = moe_mx_exp(amax);
-            const uint32_t q = moe_e4m3_pair_hw(h[0], h[1], X);
-            hrow[c16] = (uint8_t)q;
-            hrow[c16 + 16] = (uint8_t)(q >> 8);
-            if (c16 == 0) p.hs[(size_t)pos * (I / 32) + col0 / 32] = (uint8_t)(X + 127);
-          }
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-      if (mt >= mtiles) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rl = 16 * mt + 4 * g + i;
-        if (rl < nrows) {
-          float* yrow = p.y + (size_t)(jb.m0 + rl) * N + col0 + c16;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) yrow[16 * q] = acc[mt][q][i];
-        }
-      }
-    }
-  }
-  }   // wvalid
-  __syncthreads();   // s_arow and the LDS buffers are reused by the next job
-  }   // jobs
-}
-
 // ---------------------------------------------------------------------------------------
-// The same GEMM with the activation tile moved from HBM straight into LDS (buffer loads with
-// the LDS flag, 16 bytes per lane) instead of through a register ring and LDS stores.  Each
-// K step's tile lands in LDS in the MFMA's operand order: per 16-row tile mt and half h one
-// 1 KiB block whose 16 bytes at 16 l are lane l's A bytes (row 16 mt + l % 16, K bytes
-// 64 h + 16 (l / 16) .. + 15 of the step), so every fragment read is one conflict-free
-// 1 KiB ds_read_b128.  The scale words follow, 32 rows per wave (rows 32 w + l % 32; lanes
-// 32..63 repeat them so every lane's load is unconditional).  Without the A ring a wave
-// fits 256 registers and two workgroups share a CU: one workgroup's LDS reads, barrier and
-// job set-up overlap the other's MFMAs.
+// Activation staging.  A K step's tile (128 rows x 128 E4M3 bytes) goes from memory straight
+// into LDS (buffer loads with the LDS flag, 16 bytes per lane), in the MFMA's operand order:
+// per 16-row tile mt and half h one 1 KiB block whose 16 bytes at 16 l are lane l's A bytes
+// (row 16 mt + l % 16, K bytes 64 h + 16 (l / 16) .. + 15 of the step), so every fragment
+// read is one conflict-free 1 KiB ds_read_b128.  Wave w loads tile w (both halves) and the
+// scale words of rows 16 w .. 16 w + 15 (lanes repeat them so every lane's load is
+// unconditional).  No register ring or LDS store is involved.
 //
 // Three LDS buffers: step s computes from buffer s % 3 while the tiles of steps s + 1 and
-// s + 2 are in flight, so a tile has two steps to arrive (one was not enough: the rows come
-// from L2 or the Infinity Cache, about a step's time away).  The tile loads are written in
-// inline asm, out of the compiler's sight: it treats every LDS-DMA load as a pending write
-// to any LDS address and would wait for the newest one before each LDS read, which leaves
-// one step of lead whatever the ring depth.  The waits are therefore explicit: vector
-// memory loads complete in issue order, and after the tile of step s only the weight loads
-// of step s - 1 (kBLoads) and the tile of step s + 1 (kDmaLoads) are issued, so step s
-// waits for vmcnt kBLoads + kDmaLoads and then meets the other waves at a barrier (their
-// parts of the tile), with an acquire fence on LDS only (a release fence would wait for
-// every load in flight).  Loads past the last step repeat it, so these counts never change.
+// s + 2 are in flight, so a tile has two steps to arrive (the rows come from L2 or the
+// Infinity Cache, about a step's time away).  The tile loads are written in inline asm, out
+// of the compiler's sight: it treats every LDS-DMA load as a pending write to any LDS
+// address and would wait for the newest one before each LDS read, which leaves one step of
+// lead whatever the ring depth.  The waits are therefore explicit: vector memory loads
+// complete in issue order, and after the tile of step s only the weight loads of step
+// s - 1 and the tile of step s + 1 are issued, so step s waits for vmcnt (weight loads +
+// tile loads per step) and then meets the other waves at a barrier (their parts of the
+// tile), with an acquire fence on LDS only (a release fence would wait for every load in
+// flight).  Loads past the last step repeat it, so these counts never change, and an opaque
+// use at the end of each job keeps the compiler from dropping those repeated weight loads
+// as dead.  The inline asm sets M0, which nothing else in these kernels uses.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt field");
@@ -374,7 +107,6 @@ __device__ __forceinline__ void dma4(rsrc_t r, uint32_t lds, uint32_t voff, uint
                :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 
-constexpr int kBLoads = 8;      // weight loads per wave and step: 4 code pieces + 4 scale words
 constexpr int kRingD = 3;       // K steps of tiles and of weight loads in flight per wave
 
 template <int I, int N, class F>
@@ -386,7 +118,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <bool GATEUP, bool TILED, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_dma_kernel(MxArgs p) {
+__global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_kernel(MxArgs p) {
   constexpr int TPW = kMT / NW;        // 16-row A tiles this wave loads
   constexpr int RPW = kMB / NW;        // A rows whose scale words this wave loads
   constexpr int NTW = NW * kNWave;     // weight rows per job
@@ -455,22 +187,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_dma_kernel(MxArgs p) 
   const rsrc_t rb1 = GATEUP ? make_rsrc(p.wcodes1 + jb.e * ebytes, (uint32_t)ebytes) : rb0;
   const rsrc_t rs1 = GATEUP ? make_rsrc(p.wscales1 + jb.e * escales, (uint32_t)escales) : rs0;
   const uint32_t trow = (uint32_t)(wvalid ? col0 : 0);
-  const uint32_t brow = trow + c16;
-  const uint32_t boff = TILED ? trow * (K / 2) + 16 * lane : brow * (K / 2) + 16 * g;
-  const uint32_t bsoff = TILED ? trow * (K / 32) + 4 * c16 : brow * (K / 32);
-  auto koff = [](int k0) { return TILED ? k0 * 8 : k0 / 2; };
-  auto ksoff = [](int k0) { return TILED ? k0 / 2 : k0 / 32; };
-  auto qrow = [](int q) { return GATEUP ? 16 * (q & 1) : 16 * q; };
+  // Tiled: the wave's tiles lie in the 64-row group of trow (gate/up: tiles q0, q0 + 1 of
+  // each matrix; down: all four), a K step of the group is 4 KiB of codes at 4096 per step
+  // and the lane's scale word of the step holds the group's four tiles' scales.
+  // Row-major: lane row trow + c16 (+ 16 per n-tile), 64 bytes and one scale word per step.
+  const int q0 = TILED && GATEUP ? (int)(trow & 63) / 16 : 0;
+  const uint32_t gbase = trow & ~63u;
+  const uint32_t boff = TILED ? gbase * (K / 2) + 16 * lane : (trow + c16) * (K / 2) + 16 * g;
+  const uint32_t bsoff = TILED ? gbase * (K / 32) + 4 * lane : (trow + c16) * (K / 32);
+  // n-tile q: its tile within the group (tiled) or its first row after the lane's (row-major)
+  auto qtile = [&](int q) { return GATEUP ? q0 + (q & 1) : q; };
+  auto qoff = [&](int q, int k0) {
+    return TILED ? 32 * k0 + 1024 * qtile(q) : (GATEUP ? 16 * (q & 1) : 16 * q) * (K / 2) + k0 / 2;
+  };
+  constexpr int NSW = TILED ? (GATEUP ? 2 : 1) : 4;   // scale words per wave and step
+  constexpr int NBL = 4 + NSW;                        // weight loads per wave and step
 
   uint4 rb[kRingD][4];
-  uint32_t rbs[kRingD][4];
+  uint32_t rbs[kRingD][NSW];
   auto load_b = [&](int slot, int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool hi = GATEUP && q >= 2;
-      rb[slot][q] = bload16(hi ? rb1 : rb0, boff, qrow(q) * (K / 2) + koff(k0));
-      rbs[slot][q] = bload4(hi ? rs1 : rs0, bsoff, qrow(q) * (K / 32) + ksoff(k0));
+    for (int q = 0; q < 4; ++q)
+      rb[slot][q] = bload16(GATEUP && q >= 2 ? rb1 : rb0, boff, qoff(q, k0));
+#pragma unroll
+    for (int m = 0; m < NSW; ++m) {
+      const bool hi = GATEUP && (TILED ? m == 1 : m >= 2);
+      const uint32_t so = TILED ? 2 * k0 : (GATEUP ? 16 * (m & 1) : 16 * m) * (K / 32) + k0 / 32;
+      rbs[slot][m] = bload4(hi ? rs1 : rs0, bsoff, so);
     }
+  };
+  // the UE8M0 scale of n-tile q for this lane (row c16, K block g of the step)
+  auto bscale = [&](int slot, int q) {
+    return TILED ? (int)((rbs[slot][GATEUP ? q >> 1 : 0] >> (8 * qtile(q))) & 0xFF)
+                 : (int)((rbs[slot][q] >> (8 * g)) & 0xFF);
   };
 
   f32x4_t acc[kMT][4];
@@ -488,7 +237,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_dma_kernel(MxArgs p) 
     for (int q = 0; q < 4; ++q) {
       const uint4 v = rb[slot][q];
       bop[q] = (i32x8_t){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      bsc[q] = (rbs[slot][q] >> (8 * g)) & 0xFF;
+      bsc[q] = bscale(slot, q);
     }
     const uint8_t* sa = s_a[buf];
     auto afrag = [&](int mt, i32x8_t& aop, int& asc) {
@@ -523,7 +272,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_dma_kernel(MxArgs p) 
   auto step = [&](int s, auto slot_c, auto mtc) {
     constexpr int SLOT = decltype(slot_c)::value;
     if (s == 0) wait_vmcnt<NDMA>();   // behind tile 0: tile 1
-    else wait_vmcnt<kBLoads + NDMA>();
+    else wait_vmcnt<NBL + NDMA>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     __builtin_amdgcn_sched_barrier(0);
@@ -623,7 +372,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_dma_kernel(MxArgs p) 
   for (int i = 0; i < kRingD; ++i) {
     uint32_t f = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) f ^= rb[i][q].x ^ rb[i][q].y ^ rb[i][q].z ^ rb[i][q].w ^ rbs[i][q];
+    for (int q = 0; q < 4; ++q) f ^= rb[i][q].x ^ rb[i][q].y ^ rb[i][q].z ^ rb[i][q].w;
+#pragma unroll
+    for (int m = 0; m < NSW; ++m) f ^= rbs[i][m];
     asm volatile("" ::"v"(f));
   }
   __syncthreads();   // s_arow and the LDS buffers are reused by the next job
@@ -650,70 +401,52 @@ inline unsigned grid_for(const MxArgs& a, int NT, int per_cu = 1) {
   return (unsigned)(most < per ? most : per);
 }
 
-// Row-major MXFP4 -> tiled layout.  One thread per 16-byte lane operand: tile t, K step j,
-// lane l read row 16 t + l % 16, bytes 64 j + 16 (l / 16) .. + 15; threads with l < 16 also
-// move the row's 4 scale bytes of the step.
+// Row-major MXFP4 -> tiled layout.  One thread per 16-byte lane operand: group u, K step
+// j, tile q, lane l = 16 g + r read row 64 u + 16 q + r, code bytes 64 j + 16 g .. + 15;
+// the threads of tile 0 also gather their scale word, byte q' from row 64 u + 16 q' + r.
 __global__ __launch_bounds__(256) void mx_pack_tiles_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales,
                                                             long rows, int K,
                                                             uint8_t* __restrict__ tcodes,
                                                             uint8_t* __restrict__ tscales) {
   const int steps = K / kBK;
-  const long n = rows / 16 * steps * 64;
+  const long n = rows / 64 * steps * 256;
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-    const int l = (int)(i & 63);
-    const long tj = i >> 6;
-    const int j = (int)(tj % steps);
-    const long t = tj / steps;
-    const long row = 16 * t + (l & 15);
-    const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + 64 * j + 16 * (l >> 4));
+    const int l = (int)(i & 63), q = (int)((i >> 6) & 3);
+    const long uj = i >> 8;
+    const int j = (int)(uj % steps);
+    const long u = uj / steps;
+    const int r = l & 15, g = l >> 4;
+    const long row = 64 * u + 16 * q + r;
+    const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + 64 * j + 16 * g);
     *reinterpret_cast<uint4*>(tcodes + 16 * i) = v;
-    if (l < 16) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(scales + row * (K / 32) + 4 * j);
-      *reinterpret_cast<uint32_t*>(tscales + 4 * (tj * 16 + l)) = w;
+    if (q == 0) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        w |= (uint32_t)scales[(64 * u + 16 * qq + r) * (K / 32) + 4 * j + g] << (8 * qq);
+      *reinterpret_cast<uint32_t*>(tscales + 256 * uj + 4 * l) = w;
     }
   }
 }
 
 }  // namespace
 
-// MOE_MI355X_MX_GEMM=regs selects the register-staged kernel (one workgroup per CU) for
-// comparison; the default is the LDS-DMA kernel (two per CU).
-static bool mx_use_regs() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = std::getenv("MOE_MI355X_MX_GEMM");
-    v = (e && std::strcmp(e, "regs") == 0) ? 1 : 0;
-  }
-  return v == 1;
-}
-
-#ifndef MOE_MX_NW
-#define MOE_MX_NW 8
-#endif
-constexpr int kNW = MOE_MX_NW;   // waves per workgroup of the LDS-DMA kernel
+constexpr int kNW = 8;   // waves per workgroup
 
 template <bool GATEUP>
 static void launch_mx(const MxArgs& a, hipStream_t s) {
-  if (mx_use_regs()) {
-    const int NT = GATEUP ? a.N / (kNTile / 2) : (a.N + kNTile - 1) / kNTile;
-    if (a.tiled)
-      hipLaunchKernelGGL((mx_gemm_kernel<GATEUP, true>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((mx_gemm_kernel<GATEUP, false>), dim3(grid_for(a, NT)), dim3(256), 0, s, a);
-    return;
-  }
   constexpr int NTW = kNW * kNWave;
   const int NT = GATEUP ? (a.N + NTW / 2 - 1) / (NTW / 2) : (a.N + NTW - 1) / NTW;
   const unsigned grid = grid_for(a, NT, 8 / kNW);
   if (a.tiled)
-    hipLaunchKernelGGL((mx_gemm_dma_kernel<GATEUP, true, kNW>), dim3(grid), dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((mx_gemm_kernel<GATEUP, true, kNW>), dim3(grid), dim3(64 * kNW), 0, s, a);
   else
-    hipLaunchKernelGGL((mx_gemm_dma_kernel<GATEUP, false, kNW>), dim3(grid), dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((mx_gemm_kernel<GATEUP, false, kNW>), dim3(grid), dim3(64 * kNW), 0, s, a);
 }
 
 hipError_t moe_launch_mx_gateup(const MxArgs& a, hipStream_t s) {
-  if (a.N % (kNTile / 2) || a.K % kBK) return hipErrorInvalidValue;
+  if (a.N % 128 || a.K % kBK) return hipErrorInvalidValue;
   launch_mx<true>(a, s);
   return hipGetLastError();
 }
@@ -726,8 +459,8 @@ hipError_t moe_launch_mx_down(const MxArgs& a, hipStream_t s) {
 
 hipError_t moe_launch_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales, long rows,
                                        int K, uint8_t* tcodes, uint8_t* tscales, hipStream_t s) {
-  if (rows % 16 || K % kBK) return hipErrorInvalidValue;
-  const long n = rows / 16 * (K / kBK) * 64;
+  if (rows % 64 || K % kBK) return hipErrorInvalidValue;
+  const long n = rows / 64 * (K / kBK) * 256;
   if (n == 0) return hipSuccess;
   const long blocks = (n + 255) / 256;
   hipLaunchKernelGGL(mx_pack_tiles_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
