@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first run a plain copy kernel (torch.neg) over this many MiB, three times, "
                         "as the reference dispatch for the HBM byte counters")
+    p.add_argument("--trace-summary", metavar="TRACE_DIR",
+                   help="print the per-kernel time table of a rocprofv3 --kernel-trace run and exit")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: summarise two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) "
                         "of this script into a markdown table with the per-launch HBM traffic")
@@ -724,8 +726,8 @@ def O_bf16_to_f32(bits):
 
 TRAFFIC_KERNELS = {  # profile slot -> substring of the HIP kernel name
     "decode_k1_route": "k1s_router<", "decode_k2_gateup": "k2s_gateup<",
-    "decode_k3_down_combine": "k3_down_combine<", "mx_gateup": "mx_gemm_kernel<true, true>",
-    "mx_down": "mx_gemm_kernel<false, true>", "stq_gateup": "g16_kernel<0, true, 1>",
+    "decode_k3_down_combine": "k3_down_combine<", "mx_gateup": "mx_gemm_kernel<true, true, 8>",
+    "mx_down": "mx_gemm_kernel<false, true, 8>", "stq_gateup": "g16_kernel<0, true, 1>",
     "stq_down": "g16_kernel<0, false, 2>", "mxdec_k2_gateup": "k2s_gateup_mx<",
     "mxdec_k3_down_combine": "k3_down_combine_mx<",
     # the 64-token decode (its K2 / K3 kernels are also the 16-token chain's, and its K1 the
@@ -797,6 +799,59 @@ def pmc_summary(fetch_dir, write_dir, copy_mib):
     print(f"\nCopy calibration: {copy_mib} MiB read and written by torch.neg; FETCH_SIZE reads "
           f"{f_fac:.4f}x and WRITE_SIZE {w_fac:.4f}x the bytes moved.\n")
     print("traffic-json: " + json.dumps(data))
+
+
+def trace_summary(trace_dir):
+    """Per-kernel dispatch times (microseconds) from the kernel_trace.csv of a rocprofv3
+    --kernel-trace run of this script.  Kernel names keep their template arguments; torch's own
+    kernels are shown by their base name.  The MX grouped GEMMs and x quantisation that the
+    64-token MXFP4 line runs through the separate entry points (an x quantisation over 64
+    tokens precedes them) are listed apart, and the large-T decode kernels are also split by
+    the k1_route instantiation that precedes them (one per workload)."""
+    import csv
+    import glob
+    import re
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def short(name):
+        n = re.sub(r"^void ", "", name)
+        n = re.sub(r"\(anonymous namespace\)::", "", n)
+        if n.startswith("at::") or "native::" in n:
+            return re.sub(r"<.*", "", n.split("(")[0]) + " (torch)"
+        return re.sub(r"\(.*\)$", "", n).strip()
+
+    stats, by_wl = {}, {}
+    small_mx, k1 = False, None
+    total = 0.0
+    for r in rows:
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        total += us
+        n = short(r["Kernel_Name"])
+        if n.startswith("mx_quant_kernel"):
+            small_mx = int(r["Grid_Size_X"]) < 65536
+        label = n
+        if (n.startswith("mx_gemm_kernel") or n.startswith("mx_quant_kernel")) and small_mx:
+            label = n + " [64-token four-call comparison]"
+        stats.setdefault(label, []).append(us)
+        if n.startswith("k1_route"):
+            k1 = n
+        if k1 and re.match(r"(k1_route|k2l_gateup|k3l_down|combine_kernel)", n):
+            by_wl.setdefault((k1, n), []).append(us)
+        if not re.match(r"(k1_route|k2l_gateup|k3l_down|combine_kernel|rmsnorm_kernel)", n):
+            k1 = None
+    print("| kernel | calls | avg us | min us | max us | % of GPU time |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+              f"{100.0 * sum(v) / total:.2f} |")
+    print("\nLarge-T kernels by workload (the k1_route instantiation that precedes them):\n")
+    print("| after | kernel | calls | avg us | min us |")
+    print("|---|---|---:|---:|---:|")
+    for (a, k), v in sorted(by_wl.items()):
+        print(f"| {a} | {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} |")
 
 
 def load_traffic():
@@ -949,6 +1004,9 @@ def cpu_baselines_extra():
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, args.calibrate_copy_mib)
         return

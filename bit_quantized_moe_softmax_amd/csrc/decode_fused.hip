@@ -1872,9 +1872,8 @@ __global__ __launch_bounds__(64 * kDnWaves) void k3_down_combine(DecodeArgs a) {
 // are the STQ1_0 path's.
 
 // Stream of one MXFP4 16-row tile over NS K steps of 128, row-major (codes [rows][K/2],
-// scales [rows][K/32]) or tiled (per 64-row group and step a 4 KiB run of four 1 KiB tile
-// blocks in lane order and a 256-byte scale block whose word l holds lane l's scale of each
-// of the four tiles).  RD steps of code words and scale words in flight.
+// scales [rows][K/32]) or tiled (per tile and step a 1 KiB code block in lane order and a
+// 64-byte scale block, 4 bytes per row).  RD steps of code words and scale words in flight.
 template <int NS, bool TILED, int RD = kRing>
 struct MxStream {
   static constexpr int R = NS < RD ? NS : RD;
@@ -1883,13 +1882,12 @@ struct MxStream {
   uint32_t sw[R];
   rsrc_t rc, rs;
   uint32_t co, so;
-  int ssh;   // bit position of this lane's scale byte in its scale word
 
   __device__ __forceinline__ void load(int j, int slot) {
     // tiled: each step is whole lines read once (non-temporal); row-major rows are read
     // half a line per step
-    q[slot] = TILED ? bload16_nt(rc, co, 4096 * j) : bload16(rc, co, 64 * j);
-    sw[slot] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, TILED ? 256 * j : 4 * j, 0);
+    q[slot] = TILED ? bload16_nt(rc, co, 1024 * j) : bload16(rc, co, 64 * j);
+    sw[slot] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, TILED ? 64 * j : 4 * j, 0);
   }
   // codes / scales: one matrix of `rows` rows; trow: the tile's first row (a multiple of 16)
   __device__ __forceinline__ void issue(const uint8_t* codes, const uint8_t* scales, uint32_t rows,
@@ -1897,10 +1895,8 @@ struct MxStream {
     const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
     rc = make_rsrc(codes, rows * (K / 2));
     rs = make_rsrc(scales, rows * (K / 32));
-    const uint32_t gbase = trow & ~63u;   // the tile's 64-row group (tiled)
-    co = TILED ? gbase * (K / 2) + 1024 * ((trow & 63) / 16) + 16 * lane : (trow + c16) * (K / 2) + 16 * g;
-    so = TILED ? gbase * (K / 32) + 4 * lane : (trow + c16) * (K / 32);
-    ssh = TILED ? 8 * (int)((trow & 63) / 16) : 8 * g;
+    co = TILED ? trow * (K / 2) + 16 * lane : (trow + c16) * (K / 2) + 16 * g;
+    so = TILED ? trow * (K / 32) + 4 * c16 : (trow + c16) * (K / 32);
 #pragma unroll
     for (int j = 0; j < R; ++j) load(j, j);
   }
@@ -1914,7 +1910,7 @@ struct MxStream {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const uint4 w = q[j % R];
-      const int bsc = (sw[j % R] >> ssh) & 0xFF;
+      const int bsc = (sw[j % R] >> (8 * g)) & 0xFF;
       if (j + R < NS) load(j + R, j % R);
       if (a_on) {
         v0 = *reinterpret_cast<const uint4*>(a_q + 128 * j + 16 * g);

@@ -632,7 +632,7 @@ moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_
 
 moe_status moe_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                 int32_t K, uint8_t* tcodes, uint8_t* tscales, void* stream) {
-  if (rows < 0 || K <= 0 || rows % 64 || K % 128) return MOE_ERR_INVALID_ARG;
+  if (rows < 0 || K <= 0 || rows % 16 || K % 128) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
   if (!codes || !scales || !tcodes || !tscales) return MOE_ERR_INVALID_ARG;
   if (((uintptr_t)codes | (uintptr_t)tcodes) % 16 || ((uintptr_t)scales | (uintptr_t)tscales) % 4)

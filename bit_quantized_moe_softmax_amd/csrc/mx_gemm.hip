@@ -29,11 +29,10 @@
 // read 64 bytes from each of 16 rows K/2 bytes apart per K step and n-tile: half a cache
 // line per row, the other half a step later, which scatters the weight stream over DRAM
 // pages.  The tiled layout (moe_mxfp4_pack_tiles) stores the same bytes in the order the
-// MFMA consumes them: per 64-row group and K step one 4 KiB run of four 1 KiB tile blocks
-// whose 16 bytes at 16 l are lane l's operand (row l % 16 of the tile, K bytes 16 (l / 16)
-// .. + 15 of the step), and one 256-byte scale block whose 32-bit word l holds the four
-// tiles' scales of lane l.  A down wave then streams one contiguous 4 KiB run and one
-// scale word per step (gate/up: 2 KiB of each matrix, two scale words).
+// MFMA consumes them: per 16-row tile and K step one 1 KiB code block whose 16 bytes at
+// 16 l are lane l's operand (row l % 16, K bytes 16 (l / 16) .. + 15 of the step), and one
+// 64-byte scale block (4 bytes per row, byte g = scale of the step's K block g).  A wave
+// then streams each of its tiles as one contiguous run of K/2 * 16 bytes.
 //
 // Operand layout of the scaled 16x16x128 MFMA (measured with an in-bounds probe on gfx950,
 // K counted within the 128-wide step): lane l serves row/column l % 16 and lane group
@@ -187,40 +186,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_kernel(MxArgs p) {
   const rsrc_t rb1 = GATEUP ? make_rsrc(p.wcodes1 + jb.e * ebytes, (uint32_t)ebytes) : rb0;
   const rsrc_t rs1 = GATEUP ? make_rsrc(p.wscales1 + jb.e * escales, (uint32_t)escales) : rs0;
   const uint32_t trow = (uint32_t)(wvalid ? col0 : 0);
-  // Tiled: the wave's tiles lie in the 64-row group of trow (gate/up: tiles q0, q0 + 1 of
-  // each matrix; down: all four), a K step of the group is 4 KiB of codes at 4096 per step
-  // and the lane's scale word of the step holds the group's four tiles' scales.
-  // Row-major: lane row trow + c16 (+ 16 per n-tile), 64 bytes and one scale word per step.
-  const int q0 = TILED && GATEUP ? (int)(trow & 63) / 16 : 0;
-  const uint32_t gbase = trow & ~63u;
-  const uint32_t boff = TILED ? gbase * (K / 2) + 16 * lane : (trow + c16) * (K / 2) + 16 * g;
-  const uint32_t bsoff = TILED ? gbase * (K / 32) + 4 * lane : (trow + c16) * (K / 32);
-  // n-tile q: its tile within the group (tiled) or its first row after the lane's (row-major)
-  auto qtile = [&](int q) { return GATEUP ? q0 + (q & 1) : q; };
-  auto qoff = [&](int q, int k0) {
-    return TILED ? 32 * k0 + 1024 * qtile(q) : (GATEUP ? 16 * (q & 1) : 16 * q) * (K / 2) + k0 / 2;
-  };
-  constexpr int NSW = TILED ? (GATEUP ? 2 : 1) : 4;   // scale words per wave and step
-  constexpr int NBL = 4 + NSW;                        // weight loads per wave and step
+  const uint32_t brow = trow + c16;
+  // per-lane offsets of step 0 of the first tile; per step and n-tile the SGPR offset adds
+  // the step (1 KiB tiled, 64 B row-major) and the n-tile's first row (16 rows in both)
+  const uint32_t boff = TILED ? trow * (K / 2) + 16 * lane : brow * (K / 2) + 16 * g;
+  const uint32_t bsoff = TILED ? trow * (K / 32) + 4 * c16 : brow * (K / 32);
+  auto qrow = [](int q) { return GATEUP ? 16 * (q & 1) : 16 * q; };
+  auto qoff = [&](int q, int k0) { return qrow(q) * (K / 2) + (TILED ? 8 * k0 : k0 / 2); };
+  auto qsoff = [&](int q, int k0) { return qrow(q) * (K / 32) + (TILED ? k0 / 2 : k0 / 32); };
+  constexpr int NBL = 8;   // weight loads per wave and step: 4 code pieces + 4 scale words
 
   uint4 rb[kRingD][4];
-  uint32_t rbs[kRingD][NSW];
+  uint32_t rbs[kRingD][4];
   auto load_b = [&](int slot, int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      rb[slot][q] = bload16(GATEUP && q >= 2 ? rb1 : rb0, boff, qoff(q, k0));
-#pragma unroll
-    for (int m = 0; m < NSW; ++m) {
-      const bool hi = GATEUP && (TILED ? m == 1 : m >= 2);
-      const uint32_t so = TILED ? 2 * k0 : (GATEUP ? 16 * (m & 1) : 16 * m) * (K / 32) + k0 / 32;
-      rbs[slot][m] = bload4(hi ? rs1 : rs0, bsoff, so);
+    for (int q = 0; q < 4; ++q) {
+      const bool hi = GATEUP && q >= 2;
+      rb[slot][q] = bload16(hi ? rb1 : rb0, boff, qoff(q, k0));
+      rbs[slot][q] = bload4(hi ? rs1 : rs0, bsoff, qsoff(q, k0));
     }
   };
   // the UE8M0 scale of n-tile q for this lane (row c16, K block g of the step)
-  auto bscale = [&](int slot, int q) {
-    return TILED ? (int)((rbs[slot][GATEUP ? q >> 1 : 0] >> (8 * qtile(q))) & 0xFF)
-                 : (int)((rbs[slot][q] >> (8 * g)) & 0xFF);
-  };
+  auto bscale = [&](int slot, int q) { return (int)((rbs[slot][q] >> (8 * g)) & 0xFF); };
 
   f32x4_t acc[kMT][4];
 #pragma unroll
@@ -372,9 +359,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_kernel(MxArgs p) {
   for (int i = 0; i < kRingD; ++i) {
     uint32_t f = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) f ^= rb[i][q].x ^ rb[i][q].y ^ rb[i][q].z ^ rb[i][q].w;
-#pragma unroll
-    for (int m = 0; m < NSW; ++m) f ^= rbs[i][m];
+    for (int q = 0; q < 4; ++q) f ^= rb[i][q].x ^ rb[i][q].y ^ rb[i][q].z ^ rb[i][q].w ^ rbs[i][q];
     asm volatile("" ::"v"(f));
   }
   __syncthreads();   // s_arow and the LDS buffers are reused by the next job
@@ -401,31 +386,27 @@ inline unsigned grid_for(const MxArgs& a, int NT, int per_cu = 1) {
   return (unsigned)(most < per ? most : per);
 }
 
-// Row-major MXFP4 -> tiled layout.  One thread per 16-byte lane operand: group u, K step
-// j, tile q, lane l = 16 g + r read row 64 u + 16 q + r, code bytes 64 j + 16 g .. + 15;
-// the threads of tile 0 also gather their scale word, byte q' from row 64 u + 16 q' + r.
+// Row-major MXFP4 -> tiled layout.  One thread per 16-byte lane operand: tile t, K step j,
+// lane l read row 16 t + l % 16, bytes 64 j + 16 (l / 16) .. + 15; threads with l < 16 also
+// move the row's 4 scale bytes of the step.
 __global__ __launch_bounds__(256) void mx_pack_tiles_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales,
                                                             long rows, int K,
                                                             uint8_t* __restrict__ tcodes,
                                                             uint8_t* __restrict__ tscales) {
   const int steps = K / kBK;
-  const long n = rows / 64 * steps * 256;
+  const long n = rows / 16 * steps * 64;
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-    const int l = (int)(i & 63), q = (int)((i >> 6) & 3);
-    const long uj = i >> 8;
-    const int j = (int)(uj % steps);
-    const long u = uj / steps;
-    const int r = l & 15, g = l >> 4;
-    const long row = 64 * u + 16 * q + r;
-    const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + 64 * j + 16 * g);
+    const int l = (int)(i & 63);
+    const long tj = i >> 6;
+    const int j = (int)(tj % steps);
+    const long t = tj / steps;
+    const long row = 16 * t + (l & 15);
+    const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + 64 * j + 16 * (l >> 4));
     *reinterpret_cast<uint4*>(tcodes + 16 * i) = v;
-    if (q == 0) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        w |= (uint32_t)scales[(64 * u + 16 * qq + r) * (K / 32) + 4 * j + g] << (8 * qq);
-      *reinterpret_cast<uint32_t*>(tscales + 256 * uj + 4 * l) = w;
+    if (l < 16) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(scales + row * (K / 32) + 4 * j);
+      *reinterpret_cast<uint32_t*>(tscales + 4 * (tj * 16 + l)) = w;
     }
   }
 }
@@ -459,8 +440,8 @@ hipError_t moe_launch_mx_down(const MxArgs& a, hipStream_t s) {
 
 hipError_t moe_launch_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales, long rows,
                                        int K, uint8_t* tcodes, uint8_t* tscales, hipStream_t s) {
-  if (rows % 64 || K % kBK) return hipErrorInvalidValue;
-  const long n = rows / 64 * (K / kBK) * 256;
+  if (rows % 16 || K % kBK) return hipErrorInvalidValue;
+  const long n = rows / 16 * (K / kBK) * 64;
   if (n == 0) return hipSuccess;
   const long blocks = (n + 255) / 256;
   hipLaunchKernelGGL(mx_pack_tiles_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),

@@ -43,16 +43,13 @@
  * weights, group 32, UE8M0 scales):
  *   codes  : [out][in/2] bytes, element 2i in the low nibble (E2M1: bit 3 sign).
  *   scales : [out][in/32] UE8M0 bytes (value 2^(v-127)), groups along `in`.
- * MXFP4_TILED: the MXFP4 bytes of each matrix reordered for the matrix cores (made by
- * moe_mxfp4_pack_tiles; same values, same size).  Rows go in groups of 64 (four 16-row
- * tiles).  With R = out and S = in/128 K steps, for group u < R/64, step j < S, tile
- * q < 4 of the group, lane l < 64 (l = 16 g + r):
- *   codes  : bytes 4096*(u*S + j) + 1024*q + 16*l .. +15 = row 64u + 16q + r, code bytes
- *            64j + 16g .. +15 of that row in the MXFP4 layout;
- *   scales : byte 256*(u*S + j) + 4*l + q = scale byte 4j + g of row 64u + 16q + r.
- *   So a group's K step is one 4 KiB run of the four tiles' MFMA operands, and lane l's
- *   32-bit word of the step's scale block holds its four tiles' scales.
- *   Needs out % 64 == 0 and in % 128 == 0.
+ * MXFP4_TILED: the MXFP4 bytes of each matrix reordered for the prefill GEMMs' matrix
+ * cores (made by moe_mxfp4_pack_tiles; same values, same size).  With R = out and
+ * S = in/128 K steps, for tile t < R/16, step j < S, lane l < 64:
+ *   codes  : bytes 1024*(t*S + j) + 16*l .. +15 = row 16t + l%16, codes bytes
+ *            64j + 16*(l/16) .. +15 of that row in the MXFP4 layout;
+ *   scales : bytes 64*(t*S + j) + 4*r .. +3 = row 16t + r, scale bytes 4j .. 4j+3.
+ *   Needs out % 16 == 0 and in % 128 == 0.
  * BF16 (shared expert, router): [out][in] uint16 bf16 bits.
  * Gate and up are [I][H] (out = I, in = H); down is [H][I].
  */
@@ -393,10 +390,10 @@ MOE_MI355X_API moe_status moe_stq1_dequant(const uint8_t* codes, const uint16_t*
 MOE_MI355X_API moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales,
                                             int64_t rows, int32_t K, float* out, void* stream);
 
-/* Reorder MXFP4 rows (codes [rows][K/2], scales [rows][K/32], rows % 64 == 0,
+/* Reorder MXFP4 rows (codes [rows][K/2], scales [rows][K/32], rows % 16 == 0,
  * K % 128 == 0) into the MXFP4_TILED layout: tcodes [rows*K/2], tscales [rows*K/32].
  * A stack of matrices (E experts of `out` rows each) is one call with rows = E*out,
- * since row groups never straddle a matrix when out % 64 == 0.  codes and tcodes must be
+ * since tiles never straddle a matrix when out % 16 == 0.  codes and tcodes must be
  * 16-byte aligned, scales and tscales 4-byte aligned; outputs must not overlap the
  * inputs.  A one-time weight preparation for MOE_W_MXFP4_TILED, not a per-step call. */
 MOE_MI355X_API moe_status moe_mxfp4_pack_tiles(const uint8_t* codes, const uint8_t* scales,

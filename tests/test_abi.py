@@ -125,11 +125,11 @@ def test_argument_checks_need_no_gpu():
     assert _raw("moe_stq1_pack", None, None, None, -1, None, None, None) == 1
     # tiled MXFP4 repack: shape, alignment and overlap checks come before any launch
     pk = "moe_mxfp4_pack_tiles"
-    assert _raw(pk, 1 << 20, 1 << 21, 32, 128, 1 << 22, 1 << 23, None) == 1     # rows % 64
-    assert _raw(pk, 1 << 20, 1 << 21, 64, 96, 1 << 22, 1 << 23, None) == 1      # K % 128
-    assert _raw(pk, (1 << 20) + 8, 1 << 21, 64, 128, 1 << 22, 1 << 23, None) == 1  # codes align
-    assert _raw(pk, 1 << 20, (1 << 21) + 2, 64, 128, 1 << 22, 1 << 23, None) == 1  # scales align
-    assert _raw(pk, 1 << 20, 1 << 21, 64, 128, (1 << 20) + 1024, 1 << 23, None) == 1  # overlap
+    assert _raw(pk, 1 << 20, 1 << 21, 24, 128, 1 << 22, 1 << 23, None) == 1     # rows % 16
+    assert _raw(pk, 1 << 20, 1 << 21, 32, 96, 1 << 22, 1 << 23, None) == 1      # K % 128
+    assert _raw(pk, (1 << 20) + 8, 1 << 21, 32, 128, 1 << 22, 1 << 23, None) == 1  # codes align
+    assert _raw(pk, 1 << 20, (1 << 21) + 2, 32, 128, 1 << 22, 1 << 23, None) == 1  # scales align
+    assert _raw(pk, 1 << 20, 1 << 21, 32, 128, (1 << 20) + 1024, 1 << 23, None) == 1  # overlap
     assert _raw(pk, None, None, 0, 128, None, None, None) == 0                   # nothing to do
     # the tiled format shares the MXFP4 workspace layout
     d3 = M.Dims(T=64, H=512, I=256, E=8, k=2)

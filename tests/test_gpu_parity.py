@@ -66,13 +66,12 @@ def routed_experts(c, routed, tiled=False):
 
 
 def tiled_reference(codes, scales):
-    """The tiled MXFP4 layout by its definition: row group u (64 rows), K step j, tile q of
-    the group, lane l = 16 g + r holds row 64 u + 16 q + r, code bytes 64 j + 16 g .. + 15;
-    byte 4 l + q of the step's scale block is scale byte 4 j + g of that row."""
+    """The tiled MXFP4 layout by its definition: tile t, K step j, lane l = 16 g + r holds
+    row 16 t + r, code bytes 64 j + 16 g .. + 15; the step's scale block holds 4 bytes per row."""
     R, KB = codes.shape
-    u, S = R // 64, KB // 64
-    tc = codes.reshape(u, 4, 16, S, 4, 16).transpose(0, 3, 1, 4, 2, 5).reshape(-1)
-    ts = scales.reshape(u, 4, 16, S, 4).transpose(0, 3, 4, 2, 1).reshape(-1)
+    t, S = R // 16, KB // 64
+    tc = codes.reshape(t, 16, S, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    ts = scales.reshape(t, 16, S, 4).transpose(0, 2, 1, 3).reshape(-1)
     return tc, ts
 
 
@@ -118,7 +117,7 @@ def test_mxfp4_dequant_bitexact():
     assert (host(out).view(np.uint32) == ref.view(np.uint32)).all()
 
 
-@pytest.mark.parametrize("rows,K", [(64, 384), (192, 128), (2048 * 3, 6144), (6144, 2048)])
+@pytest.mark.parametrize("rows,K", [(48, 384), (2048 * 3, 6144), (6144, 2048)])
 def test_mxfp4_pack_tiles_bitexact(rows, K):
     say("mxfp4_pack_tiles", rows, K)
     g = np.random.default_rng(rows + K)
@@ -129,12 +128,9 @@ def test_mxfp4_pack_tiles_bitexact(rows, K):
     M.moe_mxfp4_pack_tiles(dev(codes), dev(scales), rows, K, tc, ts)
     rc, rs = tiled_reference(codes, scales)
     assert (host(tc) == rc).all() and (host(ts) == rs).all()
-    # lane 17 of tile 2 of group 0, step 1: row 33, code bytes 64 + 16 .. 64 + 31; its scale
-    # word's byte 2 is scale byte 4 + 1 of that row
+    # lane 17 of tile 0, step 1: row 1, code bytes 64 + 16 .. 64 + 31
     if K >= 256:
-        o = 4096 + 1024 * 2 + 16 * 17
-        assert (host(tc)[o:o + 16] == codes[33, 80:96]).all()
-        assert host(ts)[256 + 4 * 17 + 2] == scales[33, 5]
+        assert (host(tc)[1024 + 16 * 17:1024 + 16 * 18] == codes[1, 80:96]).all()
 
 
 def _mx_case_rows(K):
