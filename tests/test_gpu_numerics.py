@@ -94,7 +94,7 @@ def test_permute_unroutable_ids_bitexact():
     """Ids outside [0, E) (-1 from the slot bank for an expert without a slot, E, large
     values) are dropped by the permutation exactly as the oracle drops them."""
     g = np.random.default_rng(62)
-    for T, k, E in [(37, 8, 256), (5, 2, 8), (300, 4, 16)]:
+    for T, k, E in [(37, 8, 256), (5, 2, 8), (300, 4, 16), (2048, 8, 256)]:   # the last chunk-parallel
         ids = g.integers(0, E, (T, k)).astype(np.int32)
         bad = g.random((T, k)) < 0.2
         ids[bad] = g.choice(np.array([-1, -7, E, E + 5, 1 << 20], dtype=np.int32), bad.sum())

@@ -217,9 +217,14 @@ def test_route_from_x():
     assert np.allclose(host(w)[ok], rw[ok], rtol=2e-5, atol=1e-7)
 
 
+# from 8192 pairs (and chunks of 1024 x E <= pairs) the permutation runs chunk-parallel:
+# 4096 x 8, 4100 x 8 (a ragged last chunk, Zipf load) and 8192 x 1 take that path, 1100 x 8
+# with E = 1024 (9 chunks x 1024 > 8800 pairs) the single-workgroup one
 @pytest.mark.parametrize("T,k,E,mode", [(1, 8, 256, "rand"), (7, 2, 8, "rand"), (64, 8, 256, "zipf"),
                                         (4096, 8, 256, "rand"), (300, 3, 4, "rand"),
-                                        (129, 8, 256, "one"), (50, 1, 1024, "rand")])
+                                        (129, 8, 256, "one"), (50, 1, 1024, "rand"),
+                                        (4100, 8, 512, "zipf"), (8192, 1, 8, "rand"),
+                                        (1100, 8, 1024, "rand")])
 def test_permute_bitexact(T, k, E, mode):
     say("permute", T, k, E, mode)
     g = np.random.default_rng(T + k + E)
