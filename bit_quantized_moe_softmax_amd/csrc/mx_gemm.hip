@@ -66,12 +66,12 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
 
 // ---------------------------------------------------------------------------------------
 // Activation staging.  A K step's tile (128 rows x 128 E4M3 bytes) goes from memory straight
-// into LDS (buffer loads with the LDS flag, 16 bytes per lane), in the MFMA's operand order:
-// per 16-row tile mt and half h one 1 KiB block whose 16 bytes at 16 l are lane l's A bytes
-// (row 16 mt + l % 16, K bytes 64 h + 16 (l / 16) .. + 15 of the step), so every fragment
-// read is one conflict-free 1 KiB ds_read_b128.  Wave w loads tile w (both halves) and the
-// scale words of rows 16 w .. 16 w + 15 (lanes repeat them so every lane's load is
-// unconditional).  No register ring or LDS store is involved.
+// into LDS (buffer loads with the LDS flag, 16 bytes per lane, whole 128-byte rows: 8 rows
+// per load), without a register ring or LDS stores.  Row r's 16-byte chunk c lands at
+// 128 r + 16 (c ^ (r % 8)), so a fragment read (lane l: row l % 16 of its tile, chunks
+// l / 16 and 4 + l / 16) spreads over the LDS banks.  Wave w loads tile w and the scale
+// words of rows 16 w .. 16 w + 15 (lanes repeat them so every lane's load is unconditional).
+// Whole rows per load measured 3-4 % faster than 16 rows x 64 bytes in MFMA operand order.
 //
 // Three LDS buffers: step s computes from buffer s % 3 while the tiles of steps s + 1 and
 // s + 2 are in flight, so a tile has two steps to arrive (the rows come from L2 or the
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_kernel(MxArgs p) {
   constexpr int RPW = kMB / NW;        // A rows whose scale words this wave loads
   constexpr int NTW = NW * kNWave;     // weight rows per job
   constexpr int NDMA = 2 * TPW + 1;    // LDS-DMA loads per wave and step
-  __shared__ __align__(16) uint8_t s_a[kRingD][kMB * kBK];   // [buf][mt][half][lane] 16 B
+  __shared__ __align__(16) uint8_t s_a[kRingD][kMB * kBK];   // [buf][row][chunk ^ row % 8] 16 B
   __shared__ __align__(16) uint32_t s_as[kRingD][NW][64];    // [buf][wave][lane]
   __shared__ int s_arow[kMB];
   __shared__ JobTable s_jt;
@@ -150,26 +150,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_kernel(MxArgs p) {
   }
   __syncthreads();
 
-  // ---- A: this wave loads tiles TPW wave .. TPW wave + TPW - 1 (both halves) and the
-  // scale words of rows RPW wave .. RPW wave + RPW - 1
+  // ---- A: this wave loads tiles TPW wave .. TPW wave + TPW - 1 (8 rows of 128 bytes per
+  // load) and the scale words of rows RPW wave .. RPW wave + RPW - 1
   const int g = lane >> 4, c16 = lane & 15;
   const rsrc_t ra_q = make_rsrc(p.aq, (uint32_t)((GATEUP ? p.T : p.P) * (size_t)K));
   const rsrc_t ra_s = make_rsrc(p.as, (uint32_t)((GATEUP ? p.T : p.P) * (size_t)(K / 32)));
-  uint32_t voff[TPW];
+  uint32_t voff[2 * TPW];   // load i: lane j takes row 8 i + j / 8, chunk (j % 8) ^ (j / 8)
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int src = s_arow[16 * (TPW * wave + i) + c16];
-    voff[i] = src >= 0 ? (uint32_t)src * K + 16 * g : kOOB;
+  for (int i = 0; i < 2 * TPW; ++i) {
+    const int src = s_arow[16 * TPW * wave + 8 * i + (lane >> 3)];
+    voff[i] = src >= 0 ? (uint32_t)src * K + 16 * ((lane & 7) ^ (lane >> 3)) : kOOB;
   }
   const int ssrc = s_arow[RPW * wave + (lane % RPW)];
   const uint32_t vsoff = ssrc >= 0 ? (uint32_t)ssrc * (K / 32) : kOOB;
   auto dma_a = [&](int buf, int k0) {
     const uint32_t sq = (uint32_t)__builtin_amdgcn_readfirstlane(k0);
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        dma16(ra_q, lds_addr(&s_a[buf][((TPW * wave + i) * 2 + h) * 1024]), voff[i], sq + 64 * h);
+    for (int i = 0; i < 2 * TPW; ++i)
+      dma16(ra_q, lds_addr(&s_a[buf][(16 * TPW * wave + 8 * i) * 128]), voff[i], sq);
     dma4(ra_s, lds_addr(&s_as[buf][wave][0]), vsoff, sq / 32);
   };
 
@@ -228,8 +226,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mx_gemm_kernel(MxArgs p) {
     }
     const uint8_t* sa = s_a[buf];
     auto afrag = [&](int mt, i32x8_t& aop, int& asc) {
-      const uint4 v0 = reinterpret_cast<const uint4*>(sa + (2 * mt) * 1024)[lane];
-      const uint4 v1 = reinterpret_cast<const uint4*>(sa + (2 * mt + 1) * 1024)[lane];
+      // row 16 mt + c16, K bytes 16 g and 64 + 16 g of the step (chunks g and 4 + g, stored
+      // at chunk ^ (row % 8))
+      const uint8_t* rp = sa + (16 * mt + c16) * 128;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(rp + 16 * (g ^ (c16 & 7)));
+      const uint4 v1 = *reinterpret_cast<const uint4*>(rp + 16 * ((4 + g) ^ (c16 & 7)));
       aop = (i32x8_t){(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
       const int arow = 16 * mt + c16;
       asc = (s_as[buf][arow / RPW][arow % RPW] >> (8 * g)) & 0xFF;
