@@ -23,7 +23,7 @@
 // conversion), and so are its activations, which are MX-quantised (x along H, h along I)
 // into the bf16 values of their E4M3 codes before the GEMMs.
 //
-// Work split (as in the MXFP4 prefill GEMMs): the pairs of one expert are cut evenly into M
+// Work split (as in the first MXFP4 prefill GEMMs): the pairs of one expert are cut evenly into M
 // blocks of at most 128 rows; a job is (M block, N tile of 256 weight rows: 128 gate + the
 // 128 up rows of the same h-columns, or 256 output columns); jobs are numbered expert-major,
 // then N tile, then M block, each XCD takes one contiguous range, and one workgroup per CU
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, WGS) void g16_kernel(G16Args p) {
   const uint32_t bhoff = brow * rstride + 32 + 2 * g;
   const uint32_t bdoff = brow * (uint32_t)nblk * 2;
 
-  // ---- A: register ring, stored to LDS one step ahead (as in the MXFP4 GEMM)
+  // ---- A: register ring, stored to LDS one step ahead
   uint4 ra_[kRing][4];
   auto load_a = [&](int sl, int s) {
 #pragma unroll
