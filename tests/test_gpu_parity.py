@@ -1237,6 +1237,54 @@ def test_fused_decode_graph_replays(fmt):
         assert torch.equal(out.view(torch.int32), want.view(torch.int32)), f"replay {r} differs"
 
 
+@pytest.mark.parametrize("fmt", ["stq1", "mxfp4"])
+def test_prefill_layer_graph_replays(fmt):
+    """The four calls of a prefill layer (router GEMV and top-k from x, the chunk-parallel
+    permutation of 8200 pairs, the grouped GEMMs of the routed and the shared expert, combine)
+    captured once into a HIP graph and replayed with new tokens copied into the captured
+    input, eager calls and synchronisations between the replays: every replay equals the
+    eager layer on the same tokens, bit for bit (routing, permutation and output)."""
+    c = synth.LayerCfg("gp", 4100, 512, 256, 16, 2, True, fmt, True, False, 1, 72)
+    say("prefill graph replays", fmt, "T", c.T)
+    inp = layer_inputs(c)
+    d = M.Dims(c.T, c.H, c.I, c.E, c.k)
+    routed = routed_experts(c, inp["routed"], tiled=(fmt == "mxfp4"))
+    shared = shared_experts(inp["shared"])
+    bufs = LayerBuffers(d, M.MOE_W_MXFP4 if fmt == "mxfp4" else M.MOE_W_STQ1_0, True)
+    wr, bias = dev(inp["wr"]), dev(inp["bias"])
+    x_in = torch.empty((c.T, c.H), dtype=torch.int16, device="cuda")
+    tokens = [dev(synth.activations(c.seed, 10 + r, c.T, c.H)) for r in range(3)]
+
+    def call(stream):
+        run_layer(d, bufs, x_in, routed, shared, wr_bf16=wr, logit_bias=bias, stream=stream)
+
+    x_in.copy_(tokens[0])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm the library's one-time set-up off the capture
+        call(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for r in range(3):
+        x_in.copy_(tokens[r])
+        call(torch.cuda.current_stream().cuda_stream)          # eager reference
+        torch.cuda.synchronize()
+        want = [t.clone() for t in (bufs.topk_ids, bufs.sorted_pair, bufs.offsets, bufs.out)]
+        bufs.out.zero_()
+        bufs.sorted_pair.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (bufs.topk_ids, bufs.sorted_pair, bufs.offsets, bufs.out)
+        for name, a, b in zip(("ids", "sorted_pair", "offsets", "out"), got, want):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"replay {r}: {name} differs"
+    assert not torch.equal(want[3], torch.zeros_like(want[3]))
+
+
 # ----------------------------------------------------------------------------- expert slot bank
 def test_slot_bank_layer_equals_direct():
     """A layer whose 16 routed experts live in pinned host memory and run from an 8-slot
