@@ -559,7 +559,11 @@ __device__ __forceinline__ void router_unit(const DecodeArgs& a, int rw, float (
     for (int i = 0; i < 4; ++i) {
       const int e = et * 16 + 4 * g + i;
       const float v = ((s_red[0][i][lane] + s_red[1][i][lane]) + s_red[2][i][lane]) + s_red[3][i][lane];
-      if (e < a.E) a.rpart[((size_t)q * a.T + tok) * a.E + e] = v;
+      // agent-coherent stores (written through past this XCD's L2): the workgroup that sums
+      // the partials may run on another XCD, and a release would write back the whole L2
+      if (e < a.E)
+        __hip_atomic_store(&a.rpart[((size_t)q * a.T + tok) * a.E + e], v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -775,8 +779,11 @@ __device__ __forceinline__ void route_topk_tile(const DecodeArgs& a, int t0, int
       for (int q = 0; q < 4; ++q)
         if (q * 64 + lane < E) a.logits[(size_t)t * E + q * 64 + lane] = ls[i].s[q];
       if (lane < k) {
-        a.ids[(size_t)t * k + lane] = ids_l[t * k + lane];
-        a.w[(size_t)t * k + lane] = __int_as_float(wb_l[t * k + lane]);
+        // agent-coherent: the workgroup that permutes all pairs may run on another XCD
+        __hip_atomic_store(&a.ids[(size_t)t * k + lane], ids_l[t * k + lane], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.w[(size_t)t * k + lane], __int_as_float(wb_l[t * k + lane]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -981,11 +988,13 @@ __device__ __forceinline__ void quant_x8(const DecodeArgs& a, int i);
 
 // Beyond kXT tokens, first kernel: the shared expert's gate/up (workgroups n_router_wg ..)
 // and, with MXFP4 routed experts, x -> E4M3 (the n_xq_wg workgroups after those) beside the
-// routing -- router partials (per 16-token tile), then a chain of two tickets (agent-scope
-// acquire/release atomics on counters in the workspace): the last router workgroup of a
-// token tile sums that tile's partials and picks its tokens' top-k (tiles in parallel); the
-// last tile to finish sorts all pairs and writes the work lists, then leaves every counter
-// at zero for the next call.
+// routing -- router partials (per 16-token tile), then a chain of two tickets (relaxed
+// agent-scope atomics on counters in the workspace, taken once the data they hand over,
+// written with agent-coherent stores, has completed; the taker invalidates with an acquire
+// fence): the last router workgroup of a token tile sums that tile's partials and picks its
+// tokens' top-k (tiles in parallel); the last tile to finish sorts all pairs and writes the
+// work lists, then leaves every counter at zero for the next call.  With one tile the first
+// ticket's taker goes straight on to the permutation.
 template <int HB, int IB, int MT, int P0, int QN>
 // (the register budget of one wave per SIMD: the shared gate/up at four token tiles holds
 // about 280 registers; measured 3.5 us faster at 64 tokens than without the weight prefetch)
@@ -1005,9 +1014,14 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   router_unit<HB>(a, b, s_red);
   const int per_tile = kRouterParts * ((a.E + 15) / 16);
   const int tt = b / per_tile, n_tt = (a.T + 15) / 16;
-  // wave 0 wrote this workgroup's partial: its first lane releases it with the tile ticket
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(&a.ctr[1 + tt], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == per_tile - 1;
+  // wave 0 wrote this workgroup's partial with agent-coherent stores: once they have
+  // completed (vmcnt 0), its first lane takes the tile ticket with a relaxed atomic.  (An
+  // acquire-release ticket would write back this XCD's whole L2 first, once per workgroup.)
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    s_last = __hip_atomic_fetch_add(&a.ctr[1 + tt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == per_tile - 1;
+  }
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // every wave reads the tile's partials
@@ -1021,10 +1035,12 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if ((int)threadIdx.x <= n_tt) a.ctr[threadIdx.x] = 0;
     return;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // every wave's ids and weights
+  // every wave's ids and weights (agent-coherent stores) complete before the relaxed ticket
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(&a.ctr[0], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == n_tt - 1;
+    s_last = __hip_atomic_fetch_add(&a.ctr[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_tt - 1;
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
