@@ -911,11 +911,11 @@ __device__ __forceinline__ void route_permute(const DecodeArgs& a, FinalizeLds<P
 // Shared gate/up beyond kXT tokens, beside the routing chain of the first kernel: rows
 // 16 rt .. 16 rt + 15 of the bf16 gate and up matrices (A) for up to MT token tiles (B = x
 // columns), the 4 waves splitting K.  A block's weights are loaded once for all tiles and
-// every tile's x operand of the block at once, while the next block's weights are in flight
-// (at four tiles more than 256 registers: the first kernel is given one wave per SIMD's
-// budget).  The waves' partials meet in LDS in wave order, one tile at a time.
+// every tile's x operand of the block at once, while the next block's weights are in flight.
+// Tiles tt0 .. tt0 + MT - 1: at four tiles two workgroups of two tiles share each row tile.
+// The waves' partials meet in LDS in wave order, one tile at a time.
 template <int HB, int IB, int MT>
-__device__ __forceinline__ void shared_gateup_k1(const DecodeArgs& a, int rt, float (*s_red)[2][4][64]) {
+__device__ __forceinline__ void shared_gateup_k1(const DecodeArgs& a, int rt, int tt0, float (*s_red)[2][4][64]) {
   constexpr int H = HB * 256, I = IB * 256, NBW = (HB + kNW - 1) / kNW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
@@ -935,7 +935,7 @@ __device__ __forceinline__ void shared_gateup_k1(const DecodeArgs& a, int rt, fl
     }
   };
   auto load_x = [&](int m, int tt, uint4* xv) {
-    const int bk = b0 + m, tok = 16 * tt + col;
+    const int bk = b0 + m, tok = 16 * (tt0 + tt) + col;
     const bool ok = bk < b1 && tok < T;
 #pragma unroll
     for (int t = 0; t < 8; ++t) xv[t] = bload16(rx, ok ? 2u * ((uint32_t)tok * H + 256 * bk + 64 * g + 8 * t) : kOOB);
@@ -954,7 +954,7 @@ __device__ __forceinline__ void shared_gateup_k1(const DecodeArgs& a, int rt, fl
     const int ws = m & 1;
 #pragma unroll
     for (int tt = 0; tt < MT; ++tt) {
-      if (tt < n_tt) {
+      if (tt0 + tt < n_tt) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           acc[tt][0] = mfma16(as_bf16x8(w[ws][0][t]), as_bf16x8(xv[tt][t]), acc[tt][0]);
@@ -965,11 +965,11 @@ __device__ __forceinline__ void shared_gateup_k1(const DecodeArgs& a, int rt, fl
   }
 #pragma unroll
   for (int tt = 0; tt < MT; ++tt) {
-    if (tt < n_tt) {
+    if (tt0 + tt < n_tt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) { s_red[wave][0][i][lane] = acc[tt][0][i]; s_red[wave][1][i][lane] = acc[tt][1][i]; }
       __syncthreads();
-      const int tok = 16 * tt + col;
+      const int tok = 16 * (tt0 + tt) + col;
       if (wave == 0 && tok < T) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -996,8 +996,8 @@ __device__ __forceinline__ void quant_x8(const DecodeArgs& a, int i);
 // work lists, then leaves every counter at zero for the next call.  With one tile the first
 // ticket's taker goes straight on to the permutation.
 template <int HB, int IB, int MT, int P0, int QN>
-// (the register budget of one wave per SIMD: the shared gate/up at four token tiles holds
-// about 280 registers; measured 3.5 us faster at 64 tokens than without the weight prefetch)
+// (the register budget of one wave per SIMD, which the shared gate/up's weight prefetch may
+// use)
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1, 1))) void k1_route(DecodeArgs a) {
   __shared__ __align__(16) float s_red[kNW][4][64];
   __shared__ int s_last;
@@ -1008,7 +1008,13 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return;
   }
   if (b >= a.n_router_wg) {
-    shared_gateup_k1<HB, IB, MT>(a, b - a.n_router_wg, reinterpret_cast<float(*)[2][4][64]>(s_fin.ids));
+    // four token tiles: two workgroups per 16 weight rows, each with two tiles (the pair runs
+    // on one XCD, 128 workgroups apart, so the second weight read mostly hits L2)
+    const int r = b - a.n_router_wg;
+    if constexpr (MT == 4)
+      shared_gateup_k1<HB, IB, 2>(a, r % (IB * 16), 2 * (r / (IB * 16)), reinterpret_cast<float(*)[2][4][64]>(s_fin.ids));
+    else
+      shared_gateup_k1<HB, IB, MT>(a, r, 0, reinterpret_cast<float(*)[2][4][64]>(s_fin.ids));
     return;
   }
   router_unit<HB>(a, b, s_red);
@@ -2433,7 +2439,7 @@ hipError_t launch_large_mx(DecodeArgs& a, hipStream_t s) {
   const int T = a.T;
   const int n_tt = (T + 15) / 16;
   a.n_router_wg = ((a.E + 15) / 16) * kRouterParts * n_tt;
-  a.n_sgu_wg = a.sg ? I / 16 : 0;
+  a.n_sgu_wg = a.sg ? I / 16 * (n_tt > 2 ? 2 : 1) : 0;   // two per row tile at four tiles
   a.n_xq_wg = (T * H / 8 + kWG - 1) / kWG;
   a.h_lds = 0;
   a.ysh_ready = 0;
@@ -2525,7 +2531,7 @@ hipError_t launch_large(DecodeArgs& a, hipStream_t s) {
   const int T = a.T;
   const int n_tt = (T + 15) / 16;
   a.n_router_wg = ((a.E + 15) / 16) * kRouterParts * n_tt;
-  a.n_sgu_wg = a.sg ? I / 16 : 0;
+  a.n_sgu_wg = a.sg ? I / 16 * (n_tt > 2 ? 2 : 1) : 0;   // two per row tile at four tiles
   a.h_lds = 0;
   a.ysh_ready = 0;
   const int cus = device_cus();
